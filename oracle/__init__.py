@@ -1,0 +1,180 @@
+"""Python view of the plain C oracle (``vqm_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  The oracle is the yardstick the HIP library is held
+against; only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU
+baseline leg may import this package.  It shares no code with the HIP path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vqm_oracle.c")
+_LIB = os.path.join(_HERE, "libvqm_oracle.so")
+
+# Contraction off and no fast-math: every fp32 product and the single
+# rounding of each decimated sample must be what the C source says.
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+          "-Wall", "-Wextra", "-Werror"]
+
+
+def build(cc: str = "gcc") -> str:
+    """Compile the oracle into ``oracle/libvqm_oracle.so`` (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run([cc, *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    """Load the oracle library, building it first if it is absent.
+
+    ``VQM_ORACLE_LIB`` names another build of the same source to load instead
+    (the mutation test points it at deliberately broken copies).
+    """
+    global _lib
+    if _lib is None:
+        path = os.environ.get("VQM_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        L = ctypes.CDLL(path)
+        vp, ip, fp, dp = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+        L.vqm_oracle_scale.argtypes = [ip, ip]
+        L.vqm_oracle_scale.restype = ip
+        L.vqm_oracle_tap.argtypes = [ip]
+        L.vqm_oracle_tap.restype = ctypes.c_float
+        L.vqm_oracle_decimated_dim.argtypes = [ip, ip]
+        L.vqm_oracle_decimated_dim.restype = ip
+        L.vqm_oracle_sample_plane.argtypes = [vp, ip, ip, ip, fp]
+        L.vqm_oracle_decimate.argtypes = [vp, ip, ip, ip, ip, fp]
+        L.vqm_oracle_ssim_planes.argtypes = [fp, fp, ip, ip, dp, dp]
+        L.vqm_oracle_ssim.argtypes = [vp, vp, ip, ip, ip, dp]
+        L.vqm_oracle_msssim_level_maps.argtypes = [fp, fp, ip, ip, dp, dp, dp]
+        L.vqm_oracle_downsample.argtypes = [fp, ip, ip, fp]
+        L.vqm_oracle_msssim.argtypes = [vp, vp, ip, ip, ip, dp, dp]
+        for name in ("vqm_oracle_sample_plane", "vqm_oracle_decimate", "vqm_oracle_ssim_planes",
+                     "vqm_oracle_ssim", "vqm_oracle_msssim_level_maps", "vqm_oracle_downsample",
+                     "vqm_oracle_msssim"):
+            getattr(L, name).restype = ip
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    def __init__(self, rc: int, what: str):
+        super().__init__(f"{what} failed with {rc} ({os.strerror(-rc) if rc < 0 else rc})")
+        self.rc = rc
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _raw(a, bpc):
+    dt = np.uint8 if bpc == 8 else np.uint16
+    a = np.ascontiguousarray(a)
+    if a.dtype != dt:
+        raise TypeError(f"bpc {bpc} needs {np.dtype(dt).name} samples, got {a.dtype}")
+    return a
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise OracleError(rc, what)
+
+
+def scale(w: int, h: int) -> int:
+    return lib().vqm_oracle_scale(int(w), int(h))
+
+
+def tap(s: int) -> np.float32:
+    return np.float32(lib().vqm_oracle_tap(int(s)))
+
+
+def decimated_dim(n: int, s: int) -> int:
+    return lib().vqm_oracle_decimated_dim(int(n), int(s))
+
+
+def sample_plane(raw: np.ndarray, bpc: int) -> np.ndarray:
+    raw = _raw(raw, bpc)
+    h, w = raw.shape
+    out = np.empty((h, w), np.float32)
+    _check(lib().vqm_oracle_sample_plane(_ptr(raw), w, h, bpc, _ptr(out)), "sample_plane")
+    return out
+
+
+def decimate(raw: np.ndarray, bpc: int, s: int) -> np.ndarray:
+    raw = _raw(raw, bpc)
+    h, w = raw.shape
+    out = np.empty((decimated_dim(h, s), decimated_dim(w, s)), np.float32)
+    _check(lib().vqm_oracle_decimate(_ptr(raw), w, h, bpc, int(s), _ptr(out)), "decimate")
+    return out
+
+
+def ssim_planes(ref: np.ndarray, dis: np.ndarray, want_map: bool = False):
+    ref = np.ascontiguousarray(ref, np.float32)
+    dis = np.ascontiguousarray(dis, np.float32)
+    h, w = ref.shape
+    score = ctypes.c_double()
+    m = np.empty((max(h - 10, 0), max(w - 10, 0)), np.float64) if want_map else None
+    _check(lib().vqm_oracle_ssim_planes(_ptr(ref), _ptr(dis), w, h, ctypes.byref(score),
+                                        _ptr(m) if want_map else None), "ssim_planes")
+    return (score.value, m) if want_map else score.value
+
+
+def ssim(ref: np.ndarray, dis: np.ndarray, bpc: int) -> float:
+    ref, dis = _raw(ref, bpc), _raw(dis, bpc)
+    h, w = ref.shape
+    score = ctypes.c_double()
+    _check(lib().vqm_oracle_ssim(_ptr(ref), _ptr(dis), w, h, bpc, ctypes.byref(score)), "ssim")
+    return score.value
+
+
+def ssim_rc(ref: np.ndarray, dis: np.ndarray, w: int, h: int, bpc: int) -> int:
+    """Return code of the oracle's float_ssim for the given (possibly bad) arguments."""
+    score = ctypes.c_double()
+    return lib().vqm_oracle_ssim(_ptr(ref), _ptr(dis), w, h, bpc, ctypes.byref(score))
+
+
+def msssim_level_maps(ref: np.ndarray, dis: np.ndarray):
+    ref = np.ascontiguousarray(ref, np.float32)
+    dis = np.ascontiguousarray(dis, np.float32)
+    h, w = ref.shape
+    shp = (h - 10, w - 10)
+    l, c, s = (np.empty(shp, np.float64) for _ in range(3))
+    _check(lib().vqm_oracle_msssim_level_maps(_ptr(ref), _ptr(dis), w, h, _ptr(l), _ptr(c),
+                                              _ptr(s)), "msssim_level_maps")
+    return l, c, s
+
+
+def downsample(plane: np.ndarray) -> np.ndarray:
+    plane = np.ascontiguousarray(plane, np.float32)
+    h, w = plane.shape
+    out = np.empty((h // 2, w // 2), np.float32)
+    _check(lib().vqm_oracle_downsample(_ptr(plane), w, h, _ptr(out)), "downsample")
+    return out
+
+
+def msssim(ref: np.ndarray, dis: np.ndarray, bpc: int, want_lcs: bool = False):
+    ref, dis = _raw(ref, bpc), _raw(dis, bpc)
+    h, w = ref.shape
+    score = ctypes.c_double()
+    lcs = np.empty(15, np.float64)
+    _check(lib().vqm_oracle_msssim(_ptr(ref), _ptr(dis), w, h, bpc, ctypes.byref(score),
+                                   _ptr(lcs)), "msssim")
+    return (score.value, lcs) if want_lcs else score.value
+
+
+def msssim_rc(ref: np.ndarray, dis: np.ndarray, w: int, h: int, bpc: int) -> int:
+    score = ctypes.c_double()
+    return lib().vqm_oracle_msssim(_ptr(ref), _ptr(dis), w, h, bpc, ctypes.byref(score), None)

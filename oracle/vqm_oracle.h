@@ -1,0 +1,113 @@
+/*
+ * vqm_oracle.h — plain, slow, single-threaded CPU definition of per-frame
+ * float_ssim and 5-scale MS-SSIM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the yardstick the HIP path is
+ * held against.  Only the tests, the smoke check and the benchmark's CPU
+ * baseline leg may load it; the product path never calls it, and it shares no
+ * code, header, table or constant with the HIP library.
+ *
+ * Sources (page title, section):
+ *   [ADR-1405] "ADR-1405: float_ssim_hip decimates on the device,
+ *              bit-identical to the CPU" — Context, Decision 1–4,
+ *              Alternatives considered, Consequences.
+ *   [R-1363]   "Research-1363: Device-resident ssimulacra2 and a single-wait
+ *              MS-SSIM on SYCL" — Findings 4 and 6.
+ *
+ * Numerics: exact where the method is exact (decimation, pyramid); fp64
+ * everywhere else, except the fp32 steps the pages fix (the tap weight, the
+ * window products and the single rounding of each decimated sample).  Built
+ * with -O2 -std=c11 -ffp-contract=off on x86-64 (FLT_EVAL_METHOD == 0).
+ *
+ * Readings of points the pages leave open are listed with each function.
+ * Every function returns 0 or a negative errno (-EINVAL, -ENOTSUP, -ENOMEM).
+ *
+ * Pins (what each part is checked against, outside this library):
+ *   scale rule        — the sizes the ADR prints (1 below 384 px, 4 at 1080p,
+ *                       8 at 2160p) and 481 -> 2.
+ *   tap               — exact rational 1/s^2 rounded to fp32.
+ *   decimation        — an exact-rational (Fraction) brute force; the
+ *                       power-of-two closed form; the ADR's fp32-accumulation
+ *                       negative control (scales 3,5,6,7,9,10 differ, 2,4,8 do
+ *                       not); the exactness bound at scale 128.
+ *   ssim              — identity (exactly 1), the constant-plane closed form,
+ *                       a 50-digit mpmath evaluation on 11x11..13x17 planes,
+ *                       scipy.ndimage.correlate moments, argument symmetry.
+ *   ms-ssim           — identity, the constant-plane closed form L5^b5, the
+ *                       pyramid's exactness, mean(l*c*s) at level 1 equal to
+ *                       float_ssim at scale 1, a checkerboard that vanishes
+ *                       under 2x2 averaging (isolates level 1 and its
+ *                       exponent), and a pixel-replicated frame whose levels
+ *                       2..5 equal the original's levels 1..4.
+ */
+#ifndef VQM_ORACLE_H
+#define VQM_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Decimation factor: max(1, round(min(w, h) / 256)), real division, round
+ * half away from zero. [ADR-1405] Context. */
+int vqm_oracle_scale(int w, int h);
+
+/* Box tap weight 1.0f / (scale * scale), formed in fp32. [ADR-1405] Decision 1. */
+float vqm_oracle_tap(int scale);
+
+/* Decimated extent of one dimension: ceil(n / scale) — one output per
+ * sampled position x*scale < n (reading: the page names iqa_decimate_dim()
+ * without its formula). Returns -EINVAL for n <= 0 or scale <= 0. */
+int vqm_oracle_decimated_dim(int n, int scale);
+
+/* Sample value v = raw * 2^-(bpc-8), i.e. every bit depth mapped onto the
+ * 8-bit range (reading: exact in fp32; keeps the 2^-52 window sum below
+ * 2^60).  raw: uint8_t when bpc == 8, else uint16_t; w*h samples. */
+int vqm_oracle_sample_plane(const void *raw, int w, int h, int bpc, float *out);
+
+/* Exact box low-pass and decimate of one plane. [ADR-1405] Context and
+ * Decision 1: output (X, Y) sums, over offsets -scale/2 .. scale-1-scale/2
+ * in both directions with half-sample symmetric edges, the fp32 products
+ * v * tap; the sum is exact (here a C double, exact for scale <= 128) and is
+ * rounded once to fp32.  out: ceil(w/s) x ceil(h/s) floats, row-major,
+ * tightly packed.  Any scale >= 1 is accepted (the exactness guarantee, and
+ * so bit-identity with other exact methods, holds to 128). */
+int vqm_oracle_decimate(const void *raw, int w, int h, int bpc, int scale, float *out);
+
+/* SSIM of two fp32 planes (w x h) with the 11x11 Gaussian (sigma 1.5,
+ * normalised), "valid" region only: map (w-10) x (h-10).  Moments as direct
+ * 2-D weighted sums in fp64.  Per pixel
+ *   ((2 mx my + C1)(2 sxy + C2)) / ((mx^2 + my^2 + C1)(sxx + syy + C2)),
+ * C1 = (0.01*255)^2, C2 = (0.03*255)^2; score = fp64 sequential mean.
+ * map (optional, may be NULL): (w-10)*(h-10) doubles.
+ * Returns -ENOTSUP when w < 11 or h < 11. [ADR-1405] Context, Decision 4. */
+int vqm_oracle_ssim_planes(const float *ref, const float *dis, int w, int h,
+                           double *score, double *map);
+
+/* float_ssim of one raw frame pair: scale, gate (-ENOTSUP when scale > 128 or
+ * a decimated side < 11), sample, decimate, SSIM. [ADR-1405] Context,
+ * Decision 1 and 4. */
+int vqm_oracle_ssim(const void *ref, const void *dis, int w, int h, int bpc, double *score);
+
+/* One MS-SSIM level: per-pixel luminance, contrast and structure maps over
+ * the valid region ((w-10) x (h-10) doubles each; any may be NULL), with
+ * sigma = sqrt(max(var, 0)) and C3 = C2 / 2. */
+int vqm_oracle_msssim_level_maps(const float *ref, const float *dis, int w, int h,
+                                 double *l, double *c, double *s);
+
+/* 2x2 mean in fp32, ((a + b) + (c + d)) * 0.25f, output floor(w/2) x floor(h/2). */
+int vqm_oracle_downsample(const float *in, int w, int h, float *out);
+
+/* 5-scale MS-SSIM at full resolution (no decimation first):
+ *   MS = L5^b5 * prod_{j=1..5} C_j^b_j * S_j^b_j,
+ *   b = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333},
+ * L_j, C_j, S_j the valid-region means of level j.  NaN when any C_j or S_j
+ * is <= 0.  Gate: -ENOTSUP when floor(w/16) < 11 or floor(h/16) < 11.
+ * lcs (optional, may be NULL): 15 doubles, L_1..L_5, C_1..C_5, S_1..S_5.
+ * [R-1363] Finding 6 (per-scale l/c/s spans). */
+int vqm_oracle_msssim(const void *ref, const void *dis, int w, int h, int bpc,
+                      double *score, double *lcs);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
