@@ -1,0 +1,226 @@
+"""Throughput of per-frame float_ssim at 3840x2160 on one MI355X.
+
+One step = one pass of the whole scoring path (upload-free: decimate, SSIM
+map, fixed-tree reduction, 8-byte result, one host wait per frame) over the
+workload's 50 distinct device-resident frame pairs (1.66 GB, larger than the
+256 MB last-level cache, so every frame comes from HBM).  Frames are
+submitted through the C ABI with a lag: frame f is collected after frame
+f + lag is submitted, so the GPU never idles on the host, and every frame
+still costs exactly one wait.
+
+Prints one JSON line (see the keys below).  ``--workload`` picks another of
+the five synthetic workloads; the default is the 2160p 10-bit float_ssim one.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                    # MI355X HBM3E, GB/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3          # MI355X fp32 vector (packed FMA), TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def covered_extent(n: int, s: int) -> int:
+    """Raw samples along one side that some decimation window reads."""
+    dn = -(-n // s)
+    return min(n, s * (dn - 1) + s - s // 2)
+
+
+def algorithmic_bytes(wl, s: int) -> int:
+    """Raw bytes the method must read once per frame pair (both planes)."""
+    bps = 1 if wl.bpc == 8 else 2
+    if wl.metric == "ms_ssim":
+        return 2 * wl.w * wl.h * bps
+    return 2 * covered_extent(wl.w, s) * covered_extent(wl.h, s) * bps
+
+
+def run_pass(ctxs, frames, metric, bpc, lag, collect_all=True):
+    """Submit every frame once, collecting with the given lag; return scores."""
+    import collections
+    pending = collections.deque()
+    scores = []
+    for f, (r, d) in enumerate(frames):
+        c = ctxs[f % len(ctxs)]
+        if metric == "ms_ssim":
+            c.vqm_msssim_submit(r, d, bpc)
+        else:
+            c.vqm_ssim_submit(r, d, bpc)
+        pending.append(c)
+        while len(pending) > lag:
+            scores.append(pending.popleft().vqm_collect())
+    while pending:
+        scores.append(pending.popleft().vqm_collect())
+    return scores
+
+
+def cpu_baseline(host, wl, budget_s: float):
+    """The oracle as it stands, one thread, over the workload's frames in order
+    (cycling), until about ``budget_s`` seconds of oracle time are spent."""
+    import oracle
+    fn = oracle.msssim if wl.metric == "ms_ssim" else oracle.ssim
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        r, d = host[n % len(host)]
+        fn(r, d, wl.bpc)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 4 * len(host):
+            break
+    return {"value": round(n / el, 3), "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} frame pairs of {wl.name} (frames 0..{min(n, len(host)) - 1}, cycling), "
+                      f"one thread, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4, help="workload number 1..5")
+    ap.add_argument("--streams", type=int, default=2, help="contexts/streams frames rotate over")
+    ap.add_argument("--lag", type=int, default=0, help="frames in flight before a collect (0: 2*streams)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0: skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build scores on one GPU; --gpus {args.gpus} is not supported "
+              "(frames shard across GPUs with no collective; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from full_reference_video_amd import synth, vqm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    src = synth.FrameSource(args.workload)
+    s = vqm.vqm_ssim_scale(wl.w, wl.h) if wl.metric == "float_ssim" else 1
+    log(f"generating {wl.frames} frame pairs of {wl.name}")
+    host = [src.pair(t) for t in range(wl.frames)]
+    dev = []
+    for r, d in host:
+        tr = torch.from_numpy(r.view(np.int16) if r.dtype == np.uint16 else r).cuda()
+        td = torch.from_numpy(d.view(np.int16) if d.dtype == np.uint16 else d).cuda()
+        dev.append((tr, td))
+    torch.cuda.synchronize()
+
+    streams = [torch.cuda.Stream() for _ in range(args.streams)]
+    ctxs = [vqm.Context(0, st) for st in streams]
+    lag = args.lag if args.lag > 0 else min(2 * args.streams, args.streams * vqm.VQM_MAX_IN_FLIGHT)
+
+    log(f"warmup {args.warmup} passes")
+    ref_scores = None
+    for _ in range(args.warmup):
+        sc = run_pass(ctxs, dev, wl.metric, wl.bpc, lag)
+        if ref_scores is None:
+            ref_scores = sc
+        elif sc != ref_scores:
+            raise RuntimeError("scores changed between passes")
+    torch.cuda.synchronize()
+
+    log(f"timed {args.steps} passes over {wl.frames} frames, {args.streams} streams, lag {lag}")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        sc = run_pass(ctxs, dev, wl.metric, wl.bpc, lag)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    if ref_scores is not None and sc != ref_scores:
+        raise RuntimeError("scores changed between passes")
+    frames = args.steps * wl.frames
+    fps = frames / el
+
+    # Per-kernel durations from HIP events on each context's stream.
+    log("kernel timing pass")
+    for c in ctxs:
+        c.vqm_ctx_set_timing(True)
+    tsteps = max(1, min(args.steps, 10))
+    for _ in range(tsteps):
+        run_pass(ctxs, dev, wl.metric, wl.bpc, lag)
+    kt = {}
+    for cls, name in ((vqm.VQM_KERNEL_DECIMATE, "decimate"), (vqm.VQM_KERNEL_SSIM, "ssim_map"),
+                      (vqm.VQM_KERNEL_MSSSIM_LEVEL1, "ms_level1"),
+                      (vqm.VQM_KERNEL_MSSSIM_COARSE, "ms_levels2_5")):
+        ms = n = 0
+        for c in ctxs:
+            a, b = c.vqm_ctx_kernel_time(cls)
+            ms += a
+            n += b
+        if n:
+            kt[name] = {"avg_us": 1000.0 * ms / n, "launches": n}
+    for c in ctxs:
+        c.vqm_ctx_set_timing(False)
+
+    alg = algorithmic_bytes(wl, s)
+    if wl.metric == "float_ssim" and "decimate" in kt:
+        avg_s = kt["decimate"]["avg_us"] * 1e-6
+        achieved = alg / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decimate_pow2", "bytes_per_launch": alg}
+    elif wl.metric == "float_ssim":
+        avg_s = kt["ssim_map"]["avg_us"] * 1e-6
+        achieved = alg / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "ssim_map", "bytes_per_launch": alg}
+    else:
+        # MS-SSIM level 1 is VALU-bound: flops of the separable moments and
+        # the l/c/s terms per valid map pixel (see the design notes).
+        mw, mh = wl.w - 10, wl.h - 10
+        flops = 2.0 * (3 * wl.w * (wl.h) / 2 + 55.0 * (mh + 10) * mw + 55.0 * mh * mw) + 40.0 * mh * mw
+        avg_s = kt["ms_level1"]["avg_us"] * 1e-6
+        achieved = flops / avg_s / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "ms_level (level 1)", "flops_per_launch": flops}
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log("oracle timing on the host")
+        cpu = cpu_baseline(host, wl, args.cpu_budget)
+
+    out = {
+        "metric": "frames/sec and achieved HBM GB/s (% of peak), float_ssim at 3840x2160"
+                  if wl.index == 4 else f"frames/sec, {wl.name}",
+        "value": round(fps, 1),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1000.0 * el / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "w": wl.w, "h": wl.h, "bpc": wl.bpc, "frames_per_step": wl.frames,
+                   "scale": s, "streams": args.streams, "lag": lag,
+                   "path_GBps": round(alg * fps / 1e9, 1)},
+        "kernels": kt,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    for c in ctxs:
+        c.close()
+
+
+if __name__ == "__main__":
+    main()

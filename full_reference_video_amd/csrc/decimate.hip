@@ -1,0 +1,290 @@
+// decimate.hip — exact box low-pass and decimate for gfx950.
+//
+// "ADR-1405: float_ssim_hip decimates on the device, bit-identical to the
+// CPU", Context and Decision 1: output (X, Y) of a plane is the window at
+// (X*s + i, Y*s + j), i, j in [-s/2, s-1-s/2], half-sample symmetric edges,
+// of the fp32 products v * tap (tap = 1.0f/(s*s) formed on the host), summed
+// exactly and rounded once to fp32.  The exact sum is an integer number of
+// 2^-52 units: every product is a multiple of 2^-45 and the window sum stays
+// below 2^8, so it fits an int64 for s <= 128 with no fp64 anywhere.
+//
+// Two kernels compute that same integer:
+//
+//  * decimate_general — any s <= 128: each product is formed in fp32 and its
+//    exact value is turned into 2^-52 units from its exponent and
+//    significand, then added as a uint64.
+//
+//  * decimate_pow2 — s = 2^k, where tap = 2^-2k and every product is exact,
+//    so the units of a product are raw * 2^(52 - 2k - (bpc-8)): a constant
+//    shift of the raw integer.  The shift is hoisted out of the window sum,
+//    which becomes a plain integer sum of raw samples (v_sad_u8/v_sad_u16 add
+//    four or two samples per instruction), rounded once to fp32 and scaled by
+//    the exact power of two.  This is the HBM-bound path of the 1080p and
+//    2160p frames.
+//
+// Layout of decimate_pow2 (one workgroup per output row Y, or several for
+// very wide rows): a thread owns an aligned group of G = max(s, 16/sizeof(T))
+// raw columns, i.e. CPT = G/s whole chunks [X*s, X*s + s), and reads them with
+// 128-bit non-temporal loads for each of the s raw rows of the window band —
+// every raw sample of the frame is read once.  Window X covers the high half
+// of chunk X-1 and the low half of chunk X, so a thread keeps the two half
+// sums per chunk and takes the high half of the chunk before its first one
+// from the previous lane (a cross-lane shuffle), the previous wave (LDS), or,
+// at the left edge, the mirror of its own low half.
+#include "vqm_kernels.h"
+
+namespace vqm {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Half-sample symmetric extension (-1 -> 0, n -> n-1), repeated as often as
+// needed: the periodic even extension with period 2n.  No loop.
+__device__ __forceinline__ int mirror(int i, int n) {
+    if (i >= 0 && i < n) return i;
+    const int p = 2 * n;
+    int m = i % p;
+    if (m < 0) m += p;
+    return m < n ? m : p - 1 - m;
+}
+
+// ------------------------------------------------------------ general path
+
+// Exact value of the fp32 product raw * tap, scaled by 2^-(bpc-8), as an
+// integer count of 2^-52 units.  q = raw * tap is normal and >= 2^-14 for
+// s <= 128, so its exponent field e >= 113 and the shift e - 90 - bpc >= 7.
+__device__ __forceinline__ uint64_t product_units(uint32_t raw, float tap, int shift_base) {
+    const float q = (float)raw * tap;  // one fp32 rounding; contraction is off
+    const uint32_t bits = __float_as_uint(q);
+    if (bits == 0u) return 0ull;
+    const uint64_t m = (uint64_t)((bits & 0x7fffffu) | 0x800000u);
+    const int e = (int)(bits >> 23);
+    return m << (e + shift_base);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void decimate_general(
+    const T *__restrict__ ref, const T *__restrict__ dis, int w, int h, int bpc, int s, float tap,
+    int dec_w, int dec_h, float *__restrict__ out_ref, float *__restrict__ out_dis, int opitch) {
+    const int X = blockIdx.x * 64 + (threadIdx.x & 63);
+    const int Y = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (X >= dec_w || Y >= dec_h) return;
+    const int lo = -(s / 2);
+    const int shift_base = -90 - bpc;
+    uint64_t ar = 0, ad = 0;
+    for (int j = 0; j < s; ++j) {
+        const size_t row = (size_t)mirror(Y * s + lo + j, h) * (size_t)w;
+        for (int i = 0; i < s; ++i) {
+            const int xx = mirror(X * s + lo + i, w);
+            ar += product_units(ref[row + xx], tap, shift_base);
+            ad += product_units(dis[row + xx], tap, shift_base);
+        }
+    }
+    // One rounding to fp32 (the sum has at most 53 significant bits), then an
+    // exact scaling by 2^-52.
+    const size_t o = (size_t)Y * opitch + X;
+    out_ref[o] = (float)ar * 0x1p-52f;
+    out_dis[o] = (float)ad * 0x1p-52f;
+}
+
+// ------------------------------------------------------------ power-of-two path
+
+template <typename T> struct Samples;
+template <> struct Samples<uint8_t> {
+    static constexpr int per_word = 4;
+    // sum of the four bytes of w (those outside `mask` zeroed) plus acc
+    __device__ static uint32_t add(uint32_t w, uint32_t acc) { return __builtin_amdgcn_sad_u8(w, 0u, acc); }
+};
+template <> struct Samples<uint16_t> {
+    static constexpr int per_word = 2;
+    __device__ static uint32_t add(uint32_t w, uint32_t acc) { return __builtin_amdgcn_sad_u16(w, 0u, acc); }
+};
+
+// Bit mask selecting samples [e0, e1) of a 32-bit word of T samples.
+template <typename T>
+__host__ __device__ constexpr uint32_t sample_mask(int e0, int e1) {
+    uint32_t m = 0;
+    for (int e = e0; e < e1; ++e) m |= (uint32_t)((1ull << (8 * sizeof(T))) - 1) << (8 * sizeof(T) * e);
+    return m;
+}
+
+// Add the samples of word `q` of vector `v` (within the thread's group) into
+// the half sums of the chunks they belong to.  Everything but `word` is a
+// compile-time constant after unrolling.
+template <typename T, int S, int CPT>
+__device__ __forceinline__ void add_word(uint32_t word, int g0, uint32_t (&lo)[CPT], uint32_t (&hi)[CPT]) {
+    constexpr int SPW = Samples<T>::per_word;
+    constexpr int HALF = S / 2;
+    if constexpr (HALF >= SPW) {
+        const int k = g0 / S;
+        if ((g0 % S) >= HALF) hi[k] = Samples<T>::add(word, hi[k]);
+        else lo[k] = Samples<T>::add(word, lo[k]);
+    } else {
+        // A word spans several half-chunks: split it by masks.
+#pragma unroll
+        for (int e0 = 0; e0 < SPW; e0 += HALF) {
+            const int g = g0 + e0;
+            const int k = g / S;
+            const uint32_t part = word & sample_mask<T>(e0, e0 + HALF);
+            if ((g % S) >= HALF) hi[k] = Samples<T>::add(part, hi[k]);
+            else lo[k] = Samples<T>::add(part, lo[k]);
+        }
+    }
+}
+
+template <typename T, int S>
+__global__ __launch_bounds__(1024) void decimate_pow2(
+    const T *__restrict__ ref, const T *__restrict__ dis, int w, int h, int dec_w, float post,
+    float *__restrict__ out_ref, float *__restrict__ out_dis, int opitch) {
+    constexpr int SPW = Samples<T>::per_word;  // samples per 32-bit word
+    constexpr int V = 4 * SPW;                 // samples per 128-bit load
+    constexpr int G = S > V ? S : V;           // raw columns per thread
+    constexpr int NV = G / V;                  // 128-bit loads per thread per row
+    constexpr int CPT = G / S;                 // chunks (outputs) per thread
+    constexpr int HALF = S / 2;
+
+    const int Y = blockIdx.y;
+    const int grp = blockIdx.x * blockDim.x + threadIdx.x;
+    const int c0 = grp * G;
+
+    uint32_t lr[CPT], hr[CPT], ld[CPT], hd[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) lr[k] = hr[k] = ld[k] = hd[k] = 0u;
+
+    constexpr int kRowUnroll = S <= 16 ? S : 4;
+#pragma unroll kRowUnroll
+    for (int r = 0; r < S; ++r) {
+        const size_t row = (size_t)mirror(Y * S - HALF + r, h) * (size_t)w + (size_t)c0;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+            // w is a multiple of V, so a vector is wholly inside or outside
+            // the row; vectors outside hold only unused samples.
+            if (c0 + v * V < w) {
+                a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ref + row + v * V));
+                b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(dis + row + v * V));
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                add_word<T, S, CPT>(a[q], v * V + q * SPW, lr, hr);
+                add_word<T, S, CPT>(b[q], v * V + q * SPW, ld, hd);
+            }
+        }
+    }
+
+    // High half of the chunk just before this thread's first chunk.
+    uint32_t pr = __shfl_up(hr[CPT - 1], 1, 64);
+    uint32_t pd = __shfl_up(hd[CPT - 1], 1, 64);
+    __shared__ uint32_t xr[16], xd[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 63) {
+        xr[wave] = hr[CPT - 1];
+        xd[wave] = hd[CPT - 1];
+    }
+    __syncthreads();
+    if (lane == 0) {
+        if (wave > 0) {
+            pr = xr[wave - 1];
+            pd = xd[wave - 1];
+        } else if (grp == 0) {
+            // Left edge: columns -s/2..-1 mirror onto 0..s/2-1, the low half.
+            pr = lr[0];
+            pd = ld[0];
+        } else {
+            // The previous group belongs to another workgroup: read the s/2
+            // columns [c0 - s/2, c0) of the s rows again (one lane only).
+            pr = pd = 0u;
+            for (int r = 0; r < S; ++r) {
+                const size_t row = (size_t)mirror(Y * S - HALF + r, h) * (size_t)w;
+                for (int c = c0 - HALF; c < c0; ++c) {
+                    pr += ref[row + c];
+                    pd += dis[row + c];
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int X = grp * CPT + k;
+        if (X < dec_w) {
+            const uint32_t tr = (k == 0 ? pr : hr[k - 1]) + lr[k];
+            const uint32_t td = (k == 0 ? pd : hd[k - 1]) + ld[k];
+            // One rounding (exact below 2^24), then the exact power of two.
+            const size_t o = (size_t)Y * opitch + X;
+            out_ref[o] = (float)tr * post;
+            out_dis[o] = (float)td * post;
+        }
+    }
+}
+
+template <typename T, int S>
+hipError_t launch_pow2(const void *ref, const void *dis, int w, int h, int bpc, int dec_w, int dec_h,
+                       float *out_ref, float *out_dis, int opitch, hipStream_t stream) {
+    constexpr int SPW = Samples<T>::per_word;
+    constexpr int V = 4 * SPW;
+    constexpr int G = S > V ? S : V;
+    constexpr int CPT = G / S;
+    int k = 0;
+    while ((1 << k) < S) ++k;
+    const float post = ldexpf(1.0f, -(2 * k + bpc - 8));
+    const int threads = (dec_w + CPT - 1) / CPT;
+    int block = ((threads + 63) / 64) * 64;
+    if (block > 1024) block = 1024;
+    const dim3 grid((threads + block - 1) / block, dec_h);
+    hipLaunchKernelGGL((decimate_pow2<T, S>), grid, dim3(block), 0, stream,
+                       static_cast<const T *>(ref), static_cast<const T *>(dis), w, h, dec_w, post,
+                       out_ref, out_dis, opitch);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_pow2_any(int s, const void *ref, const void *dis, int w, int h, int bpc, int dec_w,
+                           int dec_h, float *out_ref, float *out_dis, int opitch, hipStream_t stream) {
+    switch (s) {
+    case 2: return launch_pow2<T, 2>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+    case 4: return launch_pow2<T, 4>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+    case 8: return launch_pow2<T, 8>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+    case 16: return launch_pow2<T, 16>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+    case 32: return launch_pow2<T, 32>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+    case 64: return launch_pow2<T, 64>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+    case 128: return launch_pow2<T, 128>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool decimate_fast_path(const void *ref, const void *dis, int w, int h, int bpc, int s) {
+    (void)h;
+    if (s < 2 || s > 128 || (s & (s - 1)) != 0) return false;
+    const int V = bpc == 8 ? 16 : 8;
+    if (w % V != 0) return false;
+    if (((uintptr_t)ref | (uintptr_t)dis) & 15u) return false;
+    const int dec_w = (w + s - 1) / s;
+    // the last window's right half must lie inside the row (no right mirror)
+    if (w - s * (dec_w - 1) < s / 2) return false;
+    return true;
+}
+
+hipError_t launch_decimate(const void *ref, const void *dis, int w, int h, int bpc, int s, float tap,
+                           float *out_ref, float *out_dis, int dec_w, int dec_h, int opitch,
+                           hipStream_t stream) {
+    if (decimate_fast_path(ref, dis, w, h, bpc, s)) {
+        if (bpc == 8)
+            return launch_pow2_any<uint8_t>(s, ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+        return launch_pow2_any<uint16_t>(s, ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+    }
+    const dim3 grid((dec_w + 63) / 64, (dec_h + 3) / 4);
+    if (bpc == 8)
+        hipLaunchKernelGGL(decimate_general<uint8_t>, grid, dim3(256), 0, stream,
+                           static_cast<const uint8_t *>(ref), static_cast<const uint8_t *>(dis), w, h,
+                           bpc, s, tap, dec_w, dec_h, out_ref, out_dis, opitch);
+    else
+        hipLaunchKernelGGL(decimate_general<uint16_t>, grid, dim3(256), 0, stream,
+                           static_cast<const uint16_t *>(ref), static_cast<const uint16_t *>(dis), w,
+                           h, bpc, s, tap, dec_w, dec_h, out_ref, out_dis, opitch);
+    return hipGetLastError();
+}
+
+}  // namespace vqm

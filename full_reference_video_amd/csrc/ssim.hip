@@ -1,0 +1,109 @@
+// ssim.hip — fused 11x11 Gaussian moments, SSIM map and fixed-tree mean.
+//
+// "ADR-1405: float_ssim_hip decimates on the device, bit-identical to the
+// CPU", Context and Decision 3–4: on the decimated planes (or on the raw
+// samples directly at scale 1) the 11x11 Gaussian local means, variances and
+// covariance give a per-pixel SSIM term over the valid region, whose mean is
+// the frame score; one read-back per frame.
+// "Research-1363: Device-resident ssimulacra2 and a single-wait MS-SSIM on
+// SYCL", Finding 4: the sum runs through a fixed tree — a fixed pixel subset
+// per work-item, a tree per work-group, one group over the partials — so the
+// result depends only on the plane size.
+//
+// One workgroup per TW x TH tile of the map.  The tile's (TW+10) x (TH+10)
+// input window of both planes is staged in LDS, the horizontal 11-tap pass
+// writes five moment planes to LDS, and the vertical pass forms the moments
+// of each map pixel and its SSIM term in fp32 (with the mid-scale offset
+// removed first, so E[x^2] - mu^2 cancels less).  Each thread adds its map
+// pixels in fp64; the workgroup sum goes to a partials array, and the last
+// workgroup to arrive (an atomic ticket) sums the partials in index order
+// and writes the mean straight into the pinned host result slot.
+#include "ssim_common.h"
+
+namespace vqm {
+namespace {
+
+constexpr int kTW = 64, kTH = 8, kNT = 256;
+
+template <int TW, int TH, int NT, typename TIn>
+__global__ __launch_bounds__(NT) void ssim_map(const TIn *__restrict__ ref, const TIn *__restrict__ dis,
+                                               int pitch, int W, int H, float unit, Taps taps,
+                                               ReduceTarget rt) {
+    constexpr int IW = TW + 10, IH = TH + 10;
+    __shared__ float sx[IH * IW], sy[IH * IW];
+    __shared__ float hmx[IH * TW], hmy[IH * TW], hxx[IH * TW], hyy[IH * TW], hxy[IH * TW];
+    __shared__ double red[1][NT / 64];
+    __shared__ int is_last;
+
+    const int MW = W - 10, MH = H - 10;
+    const int x0 = blockIdx.x * TW, y0 = blockIdx.y * TH;
+
+    stage_tile<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
+    __syncthreads();
+    horizontal_moments<TW, TH, NT>(sx, sy, taps, hmx, hmy, hxx, hyy, hxy);
+    __syncthreads();
+
+    double acc[1] = {0.0};
+    for (int i = threadIdx.x; i < TH * TW; i += NT) {
+        const int r = i / TW, c = i - r * TW;
+        if (x0 + c < MW && y0 + r < MH) {
+            float mx, my, xx, yy, xy;
+            vertical_moments<TW>(hmx, hmy, hxx, hyy, hxy, taps, r, c, mx, my, xx, yy, xy);
+            const float sxx = xx - mx * mx;
+            const float syy = yy - my * my;
+            const float sxy = xy - mx * my;
+            const float ux = mx + kMomentOffset;
+            const float uy = my + kMomentOffset;
+            // Numerator and denominator as mirror images (contraction is
+            // off), so identical planes give exactly 1.
+            const float num = (ux * uy + ux * uy + kC1) * (sxy + sxy + kC2);
+            const float den = (ux * ux + uy * uy + kC1) * (sxx + syy + kC2);
+            acc[0] += (double)(num / den);
+        }
+    }
+
+    block_sum<NT, 1>(acc, red);
+    const int nb = gridDim.x * gridDim.y;
+    const int slot = blockIdx.y * gridDim.x + blockIdx.x;
+    if (!publish_and_elect<NT, 1>(acc, rt.partials, nb, slot, rt.ticket, &is_last)) return;
+
+    double tot[1];
+    finish_spans<NT, 1>(rt.partials, nb, rt.ticket, tot, red);
+    if (threadIdx.x == 0) {
+        *rt.result = tot[0] / ((double)MW * (double)MH);
+        __threadfence_system();
+    }
+}
+
+}  // namespace
+
+int ssim_partials(int W, int H) {
+    return ((W - 10 + kTW - 1) / kTW) * ((H - 10 + kTH - 1) / kTH);
+}
+
+hipError_t launch_ssim(const void *ref, const void *dis, InKind kind, int pitch, int W, int H,
+                       float unit, const Taps &taps, ReduceTarget rt, hipStream_t stream) {
+    const dim3 grid((W - 10 + kTW - 1) / kTW, (H - 10 + kTH - 1) / kTH);
+    switch (kind) {
+    case IN_F32:
+        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, float>), grid, dim3(kNT), 0, stream,
+                           static_cast<const float *>(ref), static_cast<const float *>(dis), pitch, W,
+                           H, unit, taps, rt);
+        break;
+    case IN_U8:
+        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, uint8_t>), grid, dim3(kNT), 0, stream,
+                           static_cast<const uint8_t *>(ref), static_cast<const uint8_t *>(dis), pitch,
+                           W, H, unit, taps, rt);
+        break;
+    case IN_U16:
+        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, uint16_t>), grid, dim3(kNT), 0, stream,
+                           static_cast<const uint16_t *>(ref), static_cast<const uint16_t *>(dis),
+                           pitch, W, H, unit, taps, rt);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace vqm

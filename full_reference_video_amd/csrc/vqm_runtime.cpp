@@ -1,0 +1,713 @@
+// vqm_runtime.cpp — the C ABI of include/vqm.h: argument checks and the gate,
+// contexts with a FIFO of in-flight frame slots, one upload per frame, the
+// kernel launches, the one wait per frame, and the last-error message.
+//
+// "ADR-1405: float_ssim_hip decimates on the device, bit-identical to the
+// CPU", Decision 4: the gate refuses only what the method does not define
+// (scale > 128, decimated plane below 11 x 11) and runs on the host before
+// any HIP call.  "Research-1369: SYCL psnr_hvs, motion_v2 and psnr at 4K",
+// §4–§5 and §7: pageable input goes through pinned staging with one DMA per
+// plane; a slot is reused only after the frame that used it was collected
+// (so no upload overwrites data a kernel still reads); scratch is keyed by
+// the frame geometry and rebuilt when it changes.
+#include "vqm.h"
+
+#include <errno.h>
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "vqm_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int rc, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return rc;
+}
+
+#define HIP_TRY(call)                                                                              \
+    do {                                                                                           \
+        hipError_t e_ = (call);                                                                    \
+        if (e_ != hipSuccess) return fail(-EIO, "%s: %s", #call, hipGetErrorString(e_));           \
+    } while (0)
+
+#define HIP_TRY_ALLOC(call)                                                                        \
+    do {                                                                                           \
+        hipError_t e_ = (call);                                                                    \
+        if (e_ == hipErrorOutOfMemory || e_ == hipErrorMemoryAllocation)                           \
+            return fail(-ENOMEM, "%s: %s", #call, hipGetErrorString(e_));                          \
+        if (e_ != hipSuccess) return fail(-EIO, "%s: %s", #call, hipGetErrorString(e_));           \
+    } while (0)
+
+enum Kind { KIND_NONE = 0, KIND_SSIM = 1, KIND_MSSSIM = 2 };
+
+constexpr int kLevels = 5;
+constexpr int kWin = 11;
+
+int scale_of(int w, int h) {
+    const int m = w < h ? w : h;
+    const int s = (int)round((double)m / 256.0);
+    return s < 1 ? 1 : s;
+}
+
+int check_args(const void *ref, const void *dis, int w, int h, int bpc) {
+    if (!ref || !dis) return fail(-EINVAL, "NULL plane pointer");
+    if (w <= 0 || h <= 0) return fail(-EINVAL, "frame size %dx%d is not positive", w, h);
+    if ((long long)w * (long long)h > 0x7fffffffLL) return fail(-EINVAL, "frame %dx%d too large", w, h);
+    if (bpc < 8 || bpc > 16) return fail(-EINVAL, "bpc %d outside 8..16", bpc);
+    return 0;
+}
+
+int gate_ssim(int w, int h, int bpc, int *s_out, int *dw_out, int *dh_out) {
+    if (w <= 0 || h <= 0) return fail(-EINVAL, "frame size %dx%d is not positive", w, h);
+    if ((long long)w * (long long)h > 0x7fffffffLL) return fail(-EINVAL, "frame %dx%d too large", w, h);
+    if (bpc < 8 || bpc > 16) return fail(-EINVAL, "bpc %d outside 8..16", bpc);
+    const int s = scale_of(w, h);
+    const int dw = (w + s - 1) / s, dh = (h + s - 1) / s;
+    if (s > 128) return fail(-ENOTSUP, "float_ssim: scale %d exceeds 128 for %dx%d", s, w, h);
+    if (dw < kWin || dh < kWin)
+        return fail(-ENOTSUP, "float_ssim: decimated plane %dx%d is smaller than the 11x11 window", dw, dh);
+    if (s_out) *s_out = s;
+    if (dw_out) *dw_out = dw;
+    if (dh_out) *dh_out = dh;
+    return 0;
+}
+
+int gate_msssim(int w, int h) {
+    if (w / 16 < kWin || h / 16 < kWin)
+        return fail(-ENOTSUP, "MS-SSIM: level 5 of %dx%d (%dx%d) is smaller than the 11x11 window", w, h,
+                    w / 16, h / 16);
+    return 0;
+}
+
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// Normalised 11-tap Gaussian, sigma 1.5, rounded to fp32.
+vqm::Taps make_taps() {
+    double g[11], sum = 0.0;
+    for (int k = 0; k < 11; ++k) {
+        const double d = k - 5;
+        g[k] = exp(-d * d / (2.0 * 1.5 * 1.5));
+        sum += g[k];
+    }
+    vqm::Taps t;
+    for (int k = 0; k < 11; ++k) t.g[k] = (float)(g[k] / sum);
+    return t;
+}
+
+struct Geometry {
+    int kind = KIND_NONE, w = 0, h = 0, bpc = 0;
+    int s = 1, dw = 0, dh = 0, dpitch = 0;         // float_ssim
+    int lw[kLevels] = {}, lh[kLevels] = {}, lpitch[kLevels] = {};  // MS-SSIM
+    bool operator==(const Geometry &o) const {
+        return kind == o.kind && w == o.w && h == o.h && bpc == o.bpc && s == o.s;
+    }
+    size_t sample_bytes() const { return bpc == 8 ? 1 : 2; }
+    size_t plane_bytes() const { return (size_t)w * (size_t)h * sample_bytes(); }
+};
+
+Geometry make_geometry(int kind, int w, int h, int bpc) {
+    Geometry g;
+    g.kind = kind;
+    g.w = w;
+    g.h = h;
+    g.bpc = bpc;
+    if (kind == KIND_SSIM) {
+        g.s = scale_of(w, h);
+        g.dw = (w + g.s - 1) / g.s;
+        g.dh = (h + g.s - 1) / g.s;
+        g.dpitch = round_up(g.dw, 64);
+    } else {
+        int lw = w, lh = h;
+        for (int j = 0; j < kLevels; ++j) {
+            g.lw[j] = lw;
+            g.lh[j] = lh;
+            g.lpitch[j] = j == 0 ? w : round_up(lw, 64);
+            lw /= 2;
+            lh /= 2;
+        }
+    }
+    return g;
+}
+
+// Device scratch and host result slot of one frame in flight.
+struct Slot {
+    Geometry geo;
+    void *dev_in = nullptr;         // device copy of host input: ref then dis
+    size_t dev_in_bytes = 0;
+    void *staging = nullptr;        // pinned host staging for pageable input
+    size_t staging_bytes = 0;
+    float *planes = nullptr;        // decimated planes or pyramid levels 2..5
+    size_t planes_bytes = 0;
+    double *partials = nullptr;
+    size_t partials_count = 0;
+    unsigned *tickets = nullptr;    // kLevels + 1 counters, zero at rest
+    double *lcs_dev = nullptr;      // 15 doubles
+    double *result_host = nullptr;  // pinned: score + 15 means
+    double *result_dev = nullptr;   // its device-visible address
+    hipEvent_t done = nullptr;
+    int kind = KIND_NONE;
+
+    // offsets (in floats) of the planes inside `planes`
+    size_t off_ref[kLevels] = {}, off_dis[kLevels] = {};
+    size_t span[kLevels] = {};      // partials offset of each MS level
+
+    void release() {
+        if (dev_in) (void)hipFree(dev_in);
+        if (staging) (void)hipHostFree(staging);
+        if (planes) (void)hipFree(planes);
+        if (partials) (void)hipFree(partials);
+        if (tickets) (void)hipFree(tickets);
+        if (lcs_dev) (void)hipFree(lcs_dev);
+        if (result_host) (void)hipHostFree(result_host);
+        if (done) (void)hipEventDestroy(done);
+        *this = Slot();
+    }
+};
+
+struct TimedLaunch {
+    hipEvent_t start, stop;
+    int cls;
+};
+
+}  // namespace
+
+struct vqm_ctx {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    bool own_stream = false;
+    vqm::Taps taps;
+    Slot slots[VQM_MAX_IN_FLIGHT];
+    int head = 0, count = 0;
+    bool timing = false;
+    std::vector<TimedLaunch> timed;      // recorded, not yet read
+    std::vector<hipEvent_t> event_pool;  // free timing events
+    double time_ms[4] = {0, 0, 0, 0};
+    int launches[4] = {0, 0, 0, 0};
+};
+
+namespace {
+
+int ensure_device(vqm_ctx *ctx) {
+    int cur = -1;
+    HIP_TRY(hipGetDevice(&cur));
+    if (cur != ctx->device) HIP_TRY(hipSetDevice(ctx->device));
+    return 0;
+}
+
+// Size (or rebuild) a slot's scratch for geometry g.  The slot is idle.
+int prepare_slot(Slot &sl, const Geometry &g) {
+    if (sl.done != nullptr && sl.geo == g) return 0;
+    sl.release();
+    sl.geo = g;
+    HIP_TRY(hipEventCreateWithFlags(&sl.done, hipEventDisableTiming));
+    size_t floats = 0, partials = 0;
+    if (g.kind == KIND_SSIM) {
+        const size_t plane = (size_t)g.dpitch * (size_t)g.dh;
+        sl.off_ref[0] = 0;
+        sl.off_dis[0] = plane;
+        floats = 2 * plane;
+        partials = (size_t)vqm::ssim_partials(g.dw, g.dh);
+    } else {
+        for (int j = 1; j < kLevels; ++j) {
+            const size_t plane = (size_t)g.lpitch[j] * (size_t)g.lh[j];
+            sl.off_ref[j] = floats;
+            sl.off_dis[j] = floats + plane;
+            floats += 2 * plane;
+        }
+        for (int j = 0; j < kLevels; ++j) {
+            sl.span[j] = partials;
+            partials += 3 * (size_t)vqm::ms_partials(g.lw[j], g.lh[j]);
+        }
+    }
+    sl.planes_bytes = floats * sizeof(float);
+    HIP_TRY_ALLOC(hipMalloc(&sl.planes, sl.planes_bytes));
+    sl.partials_count = partials;
+    HIP_TRY_ALLOC(hipMalloc(&sl.partials, partials * sizeof(double)));
+    HIP_TRY_ALLOC(hipMalloc(&sl.tickets, (kLevels + 1) * sizeof(unsigned)));
+    HIP_TRY(hipMemset(sl.tickets, 0, (kLevels + 1) * sizeof(unsigned)));
+    HIP_TRY_ALLOC(hipMalloc(&sl.lcs_dev, 15 * sizeof(double)));
+    HIP_TRY_ALLOC(hipHostMalloc(&sl.result_host, 16 * sizeof(double), hipHostMallocMapped | hipHostMallocCoherent));
+    HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void **>(&sl.result_dev), sl.result_host, 0));
+    return 0;
+}
+
+enum PtrKind { PTR_PAGEABLE, PTR_PINNED, PTR_DEVICE };
+
+int classify(const void *p, int device, PtrKind *out) {
+    hipPointerAttribute_t a;
+    memset(&a, 0, sizeof a);
+    hipError_t e = hipPointerGetAttributes(&a, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // pageable memory is reported as an error
+        *out = PTR_PAGEABLE;
+        return 0;
+    }
+    switch (a.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+        if (a.device != device)
+            return fail(-EINVAL, "plane is device memory of device %d, context is on %d", a.device, device);
+        *out = PTR_DEVICE;
+        return 0;
+    case hipMemoryTypeHost:
+        *out = PTR_PINNED;
+        return 0;
+    default:
+        *out = PTR_PAGEABLE;
+        return 0;
+    }
+}
+
+// Make both planes readable by kernels on ctx's stream: device input is used
+// in place; host input is sent with one DMA (pageable input is first copied
+// into pinned staging, which is free because the slot is idle).
+int upload(vqm_ctx *ctx, Slot &sl, const void *ref, const void *dis, const void **dref,
+           const void **ddis) {
+    PtrKind kr, kd;
+    int rc = classify(ref, ctx->device, &kr);
+    if (rc) return rc;
+    rc = classify(dis, ctx->device, &kd);
+    if (rc) return rc;
+    if (kr == PTR_DEVICE && kd == PTR_DEVICE) {
+        *dref = ref;
+        *ddis = dis;
+        return 0;
+    }
+    const size_t pb = sl.geo.plane_bytes();
+    if (sl.dev_in_bytes < 2 * pb) {
+        if (sl.dev_in) (void)hipFree(sl.dev_in);
+        sl.dev_in = nullptr;
+        sl.dev_in_bytes = 0;
+        HIP_TRY_ALLOC(hipMalloc(&sl.dev_in, 2 * pb));
+        sl.dev_in_bytes = 2 * pb;
+    }
+    char *din = static_cast<char *>(sl.dev_in);
+    const void *src[2] = {ref, dis};
+    const PtrKind kind[2] = {kr, kd};
+    const void *dst[2] = {din, din + pb};
+    if (kr == PTR_PAGEABLE || kd == PTR_PAGEABLE) {
+        if (sl.staging_bytes < 2 * pb) {
+            if (sl.staging) (void)hipHostFree(sl.staging);
+            sl.staging = nullptr;
+            sl.staging_bytes = 0;
+            HIP_TRY_ALLOC(hipHostMalloc(&sl.staging, 2 * pb, hipHostMallocDefault));
+            sl.staging_bytes = 2 * pb;
+        }
+    }
+    char *stg = static_cast<char *>(sl.staging);
+    if (kr == PTR_PAGEABLE && kd == PTR_PAGEABLE) {
+        memcpy(stg, ref, pb);
+        memcpy(stg + pb, dis, pb);
+        HIP_TRY(hipMemcpyAsync(din, stg, 2 * pb, hipMemcpyHostToDevice, ctx->stream));
+    } else {
+        for (int i = 0; i < 2; ++i) {
+            if (kind[i] == PTR_DEVICE) {
+                HIP_TRY(hipMemcpyAsync(const_cast<void *>(dst[i]), src[i], pb, hipMemcpyDeviceToDevice, ctx->stream));
+            } else if (kind[i] == PTR_PINNED) {
+                HIP_TRY(hipMemcpyAsync(const_cast<void *>(dst[i]), src[i], pb, hipMemcpyHostToDevice, ctx->stream));
+            } else {
+                memcpy(stg + i * pb, src[i], pb);
+                HIP_TRY(hipMemcpyAsync(const_cast<void *>(dst[i]), stg + i * pb, pb, hipMemcpyHostToDevice,
+                                       ctx->stream));
+            }
+        }
+    }
+    *dref = din;
+    *ddis = din + pb;
+    return 0;
+}
+
+int timing_begin(vqm_ctx *ctx, TimedLaunch *tl, int cls) {
+    if (!ctx->timing) return 0;
+    for (int i = 0; i < 2; ++i) {
+        hipEvent_t e;
+        if (!ctx->event_pool.empty()) {
+            e = ctx->event_pool.back();
+            ctx->event_pool.pop_back();
+        } else {
+            HIP_TRY(hipEventCreate(&e));
+        }
+        (i == 0 ? tl->start : tl->stop) = e;
+    }
+    tl->cls = cls;
+    HIP_TRY(hipEventRecord(tl->start, ctx->stream));
+    return 0;
+}
+
+int timing_end(vqm_ctx *ctx, TimedLaunch *tl) {
+    if (!ctx->timing) return 0;
+    HIP_TRY(hipEventRecord(tl->stop, ctx->stream));
+    ctx->timed.push_back(*tl);
+    return 0;
+}
+
+int drain_timing(vqm_ctx *ctx) {
+    if (ctx->timed.empty()) return 0;
+    HIP_TRY(hipStreamSynchronize(ctx->stream));
+    for (const TimedLaunch &t : ctx->timed) {
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, t.start, t.stop));
+        ctx->time_ms[t.cls] += ms;
+        ctx->launches[t.cls] += 1;
+        ctx->event_pool.push_back(t.start);
+        ctx->event_pool.push_back(t.stop);
+    }
+    ctx->timed.clear();
+    return 0;
+}
+
+#define LAUNCH_TIMED(ctx, cls, launch_expr)                                                        \
+    do {                                                                                           \
+        TimedLaunch tl_;                                                                           \
+        int rc_ = timing_begin(ctx, &tl_, cls);                                                    \
+        if (rc_) return rc_;                                                                       \
+        hipError_t e_ = (launch_expr);                                                             \
+        if (e_ != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e_));       \
+        rc_ = timing_end(ctx, &tl_);                                                               \
+        if (rc_) return rc_;                                                                       \
+    } while (0)
+
+// float_ssim on device-readable planes into slot sl.  `decimate_only` stops
+// after the decimation (debug export).
+int enqueue_ssim(vqm_ctx *ctx, Slot &sl, const void *ref, const void *dis, bool decimate_only) {
+    const Geometry &g = sl.geo;
+    float *dref = sl.planes + sl.off_ref[0];
+    float *ddis = sl.planes + sl.off_dis[0];
+    const float unit = ldexpf(1.0f, -(g.bpc - 8));
+    const void *in_r = ref, *in_d = dis;
+    vqm::InKind kind = g.bpc == 8 ? vqm::IN_U8 : vqm::IN_U16;
+    int pitch = g.w;
+    if (g.s > 1 || decimate_only) {
+        const float tap = 1.0f / (float)(g.s * g.s);  // formed on the host
+        LAUNCH_TIMED(ctx, VQM_KERNEL_DECIMATE,
+                     vqm::launch_decimate(ref, dis, g.w, g.h, g.bpc, g.s, tap, dref, ddis, g.dw, g.dh,
+                                          g.dpitch, ctx->stream));
+        in_r = dref;
+        in_d = ddis;
+        kind = vqm::IN_F32;
+        pitch = g.dpitch;
+    }
+    if (decimate_only) return 0;
+    vqm::ReduceTarget rt{sl.partials, sl.tickets, sl.result_dev};
+    LAUNCH_TIMED(ctx, VQM_KERNEL_SSIM,
+                 vqm::launch_ssim(in_r, in_d, kind, pitch, g.dw, g.dh, unit, ctx->taps, rt, ctx->stream));
+    return 0;
+}
+
+int enqueue_msssim(vqm_ctx *ctx, Slot &sl, const void *ref, const void *dis) {
+    const Geometry &g = sl.geo;
+    const float unit = ldexpf(1.0f, -(g.bpc - 8));
+    for (int j = 0; j < kLevels; ++j) {
+        const void *in_r = j == 0 ? ref : static_cast<const void *>(sl.planes + sl.off_ref[j]);
+        const void *in_d = j == 0 ? dis : static_cast<const void *>(sl.planes + sl.off_dis[j]);
+        const vqm::InKind kind = j == 0 ? (g.bpc == 8 ? vqm::IN_U8 : vqm::IN_U16) : vqm::IN_F32;
+        vqm::MsLevelTarget t;
+        t.partials = sl.partials + sl.span[j];
+        t.ticket = sl.tickets + j;
+        t.lcs_dev = sl.lcs_dev;
+        t.result = sl.result_dev;
+        t.next_ref = j + 1 < kLevels ? sl.planes + sl.off_ref[j + 1] : nullptr;
+        t.next_dis = j + 1 < kLevels ? sl.planes + sl.off_dis[j + 1] : nullptr;
+        t.next_pitch = j + 1 < kLevels ? g.lpitch[j + 1] : 0;
+        LAUNCH_TIMED(ctx, j == 0 ? VQM_KERNEL_MSSSIM_LEVEL1 : VQM_KERNEL_MSSSIM_COARSE,
+                     vqm::launch_ms_level(in_r, in_d, kind, g.lpitch[j], g.lw[j], g.lh[j],
+                                          j == 0 ? unit : 1.0f, ctx->taps, j, t, ctx->stream));
+    }
+    return 0;
+}
+
+int submit(vqm_ctx *ctx, int kind, const void *ref, const void *dis, int w, int h, int bpc) {
+    if (!ctx) return fail(-EINVAL, "NULL context");
+    int rc = check_args(ref, dis, w, h, bpc);
+    if (rc) return rc;
+    if (kind == KIND_SSIM) {
+        rc = gate_ssim(w, h, bpc, nullptr, nullptr, nullptr);
+    } else {
+        rc = gate_msssim(w, h);
+    }
+    if (rc) return rc;
+    if (ctx->count >= VQM_MAX_IN_FLIGHT) return fail(-EAGAIN, "%d frames already in flight", ctx->count);
+    rc = ensure_device(ctx);
+    if (rc) return rc;
+    Slot &sl = ctx->slots[(ctx->head + ctx->count) % VQM_MAX_IN_FLIGHT];
+    rc = prepare_slot(sl, make_geometry(kind, w, h, bpc));
+    if (rc) return rc;
+    for (int i = 0; i < 16; ++i) sl.result_host[i] = NAN;
+    const void *dref = nullptr, *ddis = nullptr;
+    rc = upload(ctx, sl, ref, dis, &dref, &ddis);
+    if (rc) return rc;
+    rc = kind == KIND_SSIM ? enqueue_ssim(ctx, sl, dref, ddis, false) : enqueue_msssim(ctx, sl, dref, ddis);
+    if (rc) return rc;
+    HIP_TRY(hipEventRecord(sl.done, ctx->stream));
+    sl.kind = kind;
+    ctx->count += 1;
+    return 0;
+}
+
+int collect(vqm_ctx *ctx, double *score, double *lcs) {
+    if (!ctx) return fail(-EINVAL, "NULL context");
+    if (!score) return fail(-EINVAL, "NULL score pointer");
+    if (ctx->count == 0) return fail(-EAGAIN, "no frame in flight");
+    int rc = ensure_device(ctx);
+    if (rc) return rc;
+    Slot &sl = ctx->slots[ctx->head];
+    HIP_TRY(hipEventSynchronize(sl.done));  // the one wait of this frame
+    ctx->head = (ctx->head + 1) % VQM_MAX_IN_FLIGHT;
+    ctx->count -= 1;
+    *score = sl.result_host[0];
+    if (lcs && sl.kind == KIND_MSSSIM) memcpy(lcs, sl.result_host + 1, 15 * sizeof(double));
+    return 0;
+}
+
+int create(int device, void *stream, vqm_ctx **out) {
+    if (!out) return fail(-EINVAL, "NULL output pointer");
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n == 0) {
+        (void)hipGetLastError();
+        return fail(-ENODEV, "no HIP device (%s)", hipGetErrorString(e));
+    }
+    if (device < 0 || device >= n) return fail(-EINVAL, "device %d outside 0..%d", device, n - 1);
+    std::unique_ptr<vqm_ctx> ctx(new vqm_ctx());
+    ctx->device = device;
+    ctx->taps = make_taps();
+    int rc = ensure_device(ctx.get());
+    if (rc) return rc;
+    if (stream) {
+        ctx->stream = static_cast<hipStream_t>(stream);
+        int sdev = -1;
+        if (hipStreamGetDevice(ctx->stream, &sdev) == hipSuccess && sdev != device)
+            return fail(-EINVAL, "stream belongs to device %d, context is on %d", sdev, device);
+        (void)hipGetLastError();
+    } else {
+        HIP_TRY(hipStreamCreateWithFlags(&ctx->stream, hipStreamNonBlocking));
+        ctx->own_stream = true;
+    }
+    *out = ctx.release();
+    return 0;
+}
+
+void destroy(vqm_ctx *ctx) {
+    if (!ctx) return;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(ctx->device);
+    (void)hipStreamSynchronize(ctx->stream);
+    for (Slot &s : ctx->slots) s.release();
+    for (const TimedLaunch &t : ctx->timed) {
+        (void)hipEventDestroy(t.start);
+        (void)hipEventDestroy(t.stop);
+    }
+    for (hipEvent_t e : ctx->event_pool) (void)hipEventDestroy(e);
+    if (ctx->own_stream) (void)hipStreamDestroy(ctx->stream);
+    if (cur >= 0) (void)hipSetDevice(cur);
+    delete ctx;
+}
+
+// Per-thread implicit contexts of the blocking calls, one per device.  They
+// live until the process ends: tearing them down from a thread-exit
+// destructor could run after the HIP runtime itself has been torn down.
+struct ImplicitContexts {
+    std::map<int, vqm_ctx *> by_device;
+};
+thread_local ImplicitContexts g_implicit;
+
+int implicit_ctx(vqm_ctx **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(-ENODEV, "no HIP device (%s)", hipGetErrorString(e));
+    }
+    auto it = g_implicit.by_device.find(dev);
+    if (it != g_implicit.by_device.end()) {
+        *out = it->second;
+        return 0;
+    }
+    vqm_ctx *ctx = nullptr;
+    int rc = create(dev, nullptr, &ctx);
+    if (rc) return rc;
+    g_implicit.by_device[dev] = ctx;
+    *out = ctx;
+    return 0;
+}
+
+int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, double *score, double *lcs) {
+    if (!score) return fail(-EINVAL, "NULL score pointer");
+    int rc = check_args(ref, dis, w, h, bpc);
+    if (rc) return rc;
+    rc = kind == KIND_SSIM ? gate_ssim(w, h, bpc, nullptr, nullptr, nullptr) : gate_msssim(w, h);
+    if (rc) return rc;
+    vqm_ctx *ctx = nullptr;
+    rc = implicit_ctx(&ctx);
+    if (rc) return rc;
+    // The implicit context never holds frames between calls.
+    rc = submit(ctx, kind, ref, dis, w, h, bpc);
+    if (rc) return rc;
+    double s = 0.0;
+    double l[15];
+    rc = collect(ctx, &s, l);
+    if (rc) return rc;
+    *score = s;
+    if (lcs) memcpy(lcs, l, sizeof l);
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vqm_abi_version(void) { return VQM_ABI_VERSION; }
+
+int vqm_ssim_scale(int w, int h) {
+    if (w <= 0 || h <= 0) return 0;
+    return scale_of(w, h);
+}
+
+int vqm_ssim_geometry(int w, int h, int bpc, int *scale, int *dec_w, int *dec_h) {
+    return gate_ssim(w, h, bpc, scale, dec_w, dec_h);
+}
+
+int vqm_ssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score) {
+    return blocking(KIND_SSIM, ref, dis, w, h, bpc, score, nullptr);
+}
+
+int vqm_msssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score) {
+    return blocking(KIND_MSSSIM, ref, dis, w, h, bpc, score, nullptr);
+}
+
+int vqm_msssim_frame_lcs(const void *ref, const void *dis, int w, int h, int bpc, double *score,
+                         double *lcs) {
+    if (!lcs) return fail(-EINVAL, "NULL lcs pointer");
+    return blocking(KIND_MSSSIM, ref, dis, w, h, bpc, score, lcs);
+}
+
+int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out) { return create(device, hip_stream, out); }
+
+void vqm_ctx_destroy(vqm_ctx *ctx) { destroy(ctx); }
+
+int vqm_ssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc) {
+    return submit(ctx, KIND_SSIM, ref, dis, w, h, bpc);
+}
+
+int vqm_msssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc) {
+    return submit(ctx, KIND_MSSSIM, ref, dis, w, h, bpc);
+}
+
+int vqm_collect(vqm_ctx *ctx, double *score, double *lcs) { return collect(ctx, score, lcs); }
+
+int vqm_in_flight(const vqm_ctx *ctx) { return ctx ? ctx->count : 0; }
+
+int vqm_ctx_set_timing(vqm_ctx *ctx, int enable) {
+    if (!ctx) return fail(-EINVAL, "NULL context");
+    int rc = ensure_device(ctx);
+    if (rc) return rc;
+    rc = drain_timing(ctx);
+    if (rc) return rc;
+    for (int i = 0; i < 4; ++i) {
+        ctx->time_ms[i] = 0.0;
+        ctx->launches[i] = 0;
+    }
+    ctx->timing = enable != 0;
+    return 0;
+}
+
+int vqm_ctx_kernel_time(vqm_ctx *ctx, int kernel_class, double *total_ms, int *launches) {
+    if (!ctx) return fail(-EINVAL, "NULL context");
+    if (kernel_class < 0 || kernel_class > 3) return fail(-EINVAL, "kernel class %d", kernel_class);
+    int rc = ensure_device(ctx);
+    if (rc) return rc;
+    rc = drain_timing(ctx);
+    if (rc) return rc;
+    if (total_ms) *total_ms = ctx->time_ms[kernel_class];
+    if (launches) *launches = ctx->launches[kernel_class];
+    return 0;
+}
+
+int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc, int scale,
+                       float *out_ref, float *out_dis) {
+    if (!ctx || !out_ref || !out_dis) return fail(-EINVAL, "NULL argument");
+    int rc = check_args(ref, dis, w, h, bpc);
+    if (rc) return rc;
+    if (scale == 0) {
+        rc = gate_ssim(w, h, bpc, nullptr, nullptr, nullptr);
+        if (rc) return rc;
+    } else if (scale < 1 || scale > 128) {
+        return fail(-EINVAL, "scale %d outside 1..128", scale);
+    }
+    if (ctx->count >= VQM_MAX_IN_FLIGHT) return fail(-EAGAIN, "%d frames already in flight", ctx->count);
+    rc = ensure_device(ctx);
+    if (rc) return rc;
+    Slot &sl = ctx->slots[(ctx->head + ctx->count) % VQM_MAX_IN_FLIGHT];
+    Geometry g = make_geometry(KIND_SSIM, w, h, bpc);
+    if (scale != 0 && scale != g.s) {
+        // A forced scale is part of the slot's geometry key, so the next
+        // automatic-scale frame rebuilds the slot.
+        g.s = scale;
+        g.dw = (w + scale - 1) / scale;
+        g.dh = (h + scale - 1) / scale;
+        g.dpitch = round_up(g.dw, 64);
+    }
+    rc = prepare_slot(sl, g);
+    if (rc) return rc;
+    const void *dref = nullptr, *ddis = nullptr;
+    rc = upload(ctx, sl, ref, dis, &dref, &ddis);
+    if (rc) return rc;
+    rc = enqueue_ssim(ctx, sl, dref, ddis, true);
+    if (rc) return rc;
+    HIP_TRY(hipMemcpy2DAsync(out_ref, g.dw * sizeof(float), sl.planes + sl.off_ref[0], g.dpitch * sizeof(float),
+                             g.dw * sizeof(float), g.dh, hipMemcpyDeviceToHost, ctx->stream));
+    HIP_TRY(hipMemcpy2DAsync(out_dis, g.dw * sizeof(float), sl.planes + sl.off_dis[0], g.dpitch * sizeof(float),
+                             g.dw * sizeof(float), g.dh, hipMemcpyDeviceToHost, ctx->stream));
+    HIP_TRY(hipStreamSynchronize(ctx->stream));
+    return 0;
+}
+
+int vqm_debug_pyramid(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc, int level,
+                      float *out_ref, float *out_dis) {
+    if (!ctx || !out_ref || !out_dis) return fail(-EINVAL, "NULL argument");
+    if (level < 2 || level > kLevels) return fail(-EINVAL, "pyramid level %d outside 2..5", level);
+    int rc = check_args(ref, dis, w, h, bpc);
+    if (rc) return rc;
+    rc = gate_msssim(w, h);
+    if (rc) return rc;
+    if (ctx->count >= VQM_MAX_IN_FLIGHT) return fail(-EAGAIN, "%d frames already in flight", ctx->count);
+    rc = ensure_device(ctx);
+    if (rc) return rc;
+    Slot &sl = ctx->slots[(ctx->head + ctx->count) % VQM_MAX_IN_FLIGHT];
+    rc = prepare_slot(sl, make_geometry(KIND_MSSSIM, w, h, bpc));
+    if (rc) return rc;
+    const void *dref = nullptr, *ddis = nullptr;
+    rc = upload(ctx, sl, ref, dis, &dref, &ddis);
+    if (rc) return rc;
+    rc = enqueue_msssim(ctx, sl, dref, ddis);
+    if (rc) return rc;
+    const Geometry &g = sl.geo;
+    const int j = level - 1;
+    HIP_TRY(hipMemcpy2DAsync(out_ref, g.lw[j] * sizeof(float), sl.planes + sl.off_ref[j], g.lpitch[j] * sizeof(float),
+                             g.lw[j] * sizeof(float), g.lh[j], hipMemcpyDeviceToHost, ctx->stream));
+    HIP_TRY(hipMemcpy2DAsync(out_dis, g.lw[j] * sizeof(float), sl.planes + sl.off_dis[j], g.lpitch[j] * sizeof(float),
+                             g.lw[j] * sizeof(float), g.lh[j], hipMemcpyDeviceToHost, ctx->stream));
+    HIP_TRY(hipStreamSynchronize(ctx->stream));
+    return 0;
+}
+
+const char *vqm_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,250 @@
+"""Thin ctypes binding of ``libvqm.so`` (the C ABI of ``include/vqm.h``).
+
+Argument marshalling only: every step of the scoring runs in the HIP library.
+The names match the C entry points.  Planes may be numpy arrays (host memory)
+or torch tensors (host, pinned host or device memory): uint8 samples when
+``bpc == 8``, 16-bit samples otherwise (numpy uint16; torch int16/uint16
+tensors are passed by their bytes).  Shapes are ``(h, w)``, C-contiguous.
+
+If the library has not been built this module raises on first use; there is
+no fallback path.
+"""
+
+from __future__ import annotations
+
+import collections
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvqm.so")
+
+VQM_MAX_IN_FLIGHT = 4
+VQM_MSSSIM_LCS = 15
+VQM_KERNEL_DECIMATE = 0
+VQM_KERNEL_SSIM = 1
+VQM_KERNEL_MSSSIM_LEVEL1 = 2
+VQM_KERNEL_MSSSIM_COARSE = 3
+
+
+class VqmError(RuntimeError):
+    """A negative errno returned by the library, with its message."""
+
+    def __init__(self, rc: int, where: str, msg: str):
+        name = os.strerror(-rc) if rc < 0 else str(rc)
+        super().__init__(f"{where}: {rc} ({name}): {msg}")
+        self.rc = rc
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "or python -m full_reference_video_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        c_int, c_void_p, c_double_p = ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)
+        c_int_p = ctypes.POINTER(ctypes.c_int)
+        L.vqm_abi_version.restype = c_int
+        L.vqm_ssim_scale.argtypes = [c_int, c_int]
+        L.vqm_ssim_geometry.argtypes = [c_int, c_int, c_int, c_int_p, c_int_p, c_int_p]
+        for n in ("vqm_ssim_frame", "vqm_msssim_frame"):
+            getattr(L, n).argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_double_p]
+        L.vqm_msssim_frame_lcs.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_double_p, c_double_p]
+        L.vqm_ctx_create.argtypes = [c_int, c_void_p, ctypes.POINTER(c_void_p)]
+        L.vqm_ctx_destroy.argtypes = [c_void_p]
+        L.vqm_ctx_destroy.restype = None
+        for n in ("vqm_ssim_submit", "vqm_msssim_submit"):
+            getattr(L, n).argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int]
+        L.vqm_collect.argtypes = [c_void_p, c_double_p, c_double_p]
+        L.vqm_in_flight.argtypes = [c_void_p]
+        L.vqm_ctx_set_timing.argtypes = [c_void_p, c_int]
+        L.vqm_ctx_kernel_time.argtypes = [c_void_p, c_int, c_double_p, c_int_p]
+        L.vqm_debug_decimate.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                                         c_void_p, c_void_p]
+        L.vqm_debug_pyramid.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                                        c_void_p, c_void_p]
+        L.vqm_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def vqm_last_error() -> str:
+    return lib().vqm_last_error().decode()
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise VqmError(rc, where, vqm_last_error())
+
+
+def _plane(a, bpc: int):
+    """(pointer, w, h, keepalive) of a plane; checks shape, layout and sample size."""
+    want = 1 if bpc == 8 else 2
+    if isinstance(a, np.ndarray):
+        if a.ndim != 2 or not a.flags.c_contiguous:
+            raise ValueError("plane must be a C-contiguous 2-D array")
+        if a.itemsize != want:
+            raise TypeError(f"bpc {bpc} needs {want}-byte samples, got {a.dtype}")
+        return a.ctypes.data, a.shape[1], a.shape[0], a
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        torch = None
+    if torch is not None and isinstance(a, torch.Tensor):
+        if a.dim() != 2 or not a.is_contiguous():
+            raise ValueError("plane must be a contiguous 2-D tensor")
+        if a.element_size() != want:
+            raise TypeError(f"bpc {bpc} needs {want}-byte samples, got {a.dtype}")
+        return a.data_ptr(), a.shape[1], a.shape[0], a
+    raise TypeError(f"unsupported plane type {type(a)!r}")
+
+
+def _pair(ref, dis, bpc):
+    pr, w, h, kr = _plane(ref, bpc)
+    pd, w2, h2, kd = _plane(dis, bpc)
+    if (w, h) != (w2, h2):
+        raise ValueError(f"ref is {w}x{h} but dis is {w2}x{h2}")
+    return pr, pd, w, h, (kr, kd)
+
+
+def vqm_abi_version() -> int:
+    return lib().vqm_abi_version()
+
+
+def vqm_ssim_scale(w: int, h: int) -> int:
+    return lib().vqm_ssim_scale(int(w), int(h))
+
+
+def vqm_ssim_geometry(w: int, h: int, bpc: int):
+    s, dw, dh = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().vqm_ssim_geometry(int(w), int(h), int(bpc), ctypes.byref(s), ctypes.byref(dw),
+                                   ctypes.byref(dh)), "vqm_ssim_geometry")
+    return s.value, dw.value, dh.value
+
+
+def vqm_ssim_frame(ref, dis, bpc: int) -> float:
+    pr, pd, w, h, _ = _pair(ref, dis, bpc)
+    score = ctypes.c_double()
+    _check(lib().vqm_ssim_frame(pr, pd, w, h, int(bpc), ctypes.byref(score)), "vqm_ssim_frame")
+    return score.value
+
+
+def vqm_msssim_frame(ref, dis, bpc: int) -> float:
+    pr, pd, w, h, _ = _pair(ref, dis, bpc)
+    score = ctypes.c_double()
+    _check(lib().vqm_msssim_frame(pr, pd, w, h, int(bpc), ctypes.byref(score)), "vqm_msssim_frame")
+    return score.value
+
+
+def vqm_msssim_frame_lcs(ref, dis, bpc: int):
+    pr, pd, w, h, _ = _pair(ref, dis, bpc)
+    score = ctypes.c_double()
+    lcs = np.empty(VQM_MSSSIM_LCS, np.float64)
+    _check(lib().vqm_msssim_frame_lcs(pr, pd, w, h, int(bpc), ctypes.byref(score),
+                                      lcs.ctypes.data_as(ctypes.POINTER(ctypes.c_double))),
+           "vqm_msssim_frame_lcs")
+    return score.value, lcs
+
+
+def _stream_handle(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    handle = getattr(stream, "cuda_stream", None)  # torch.cuda.Stream on ROCm
+    if handle is None:
+        raise TypeError(f"unsupported stream {stream!r}")
+    return int(handle)
+
+
+class Context:
+    """A ``vqm_ctx``: one device, one stream, up to VQM_MAX_IN_FLIGHT frames in flight."""
+
+    def __init__(self, device: int = 0, stream=None):
+        self._h = ctypes.c_void_p()
+        _check(lib().vqm_ctx_create(int(device), _stream_handle(stream), ctypes.byref(self._h)),
+               "vqm_ctx_create")
+        # Inputs of frames in flight stay referenced until collected (pinned
+        # or device planes are read after submit returns).
+        self._inflight = collections.deque()
+
+    def close(self):
+        if self._h:
+            lib().vqm_ctx_destroy(self._h)
+            self._h = ctypes.c_void_p()
+            self._inflight.clear()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def vqm_ssim_submit(self, ref, dis, bpc: int):
+        pr, pd, w, h, keep = _pair(ref, dis, bpc)
+        _check(lib().vqm_ssim_submit(self._h, pr, pd, w, h, int(bpc)), "vqm_ssim_submit")
+        self._inflight.append(keep)
+
+    def vqm_msssim_submit(self, ref, dis, bpc: int):
+        pr, pd, w, h, keep = _pair(ref, dis, bpc)
+        _check(lib().vqm_msssim_submit(self._h, pr, pd, w, h, int(bpc)), "vqm_msssim_submit")
+        self._inflight.append(keep)
+
+    def vqm_collect(self, want_lcs: bool = False):
+        score = ctypes.c_double()
+        lcs = np.full(VQM_MSSSIM_LCS, np.nan)
+        _check(lib().vqm_collect(self._h, ctypes.byref(score),
+                                 lcs.ctypes.data_as(ctypes.POINTER(ctypes.c_double))), "vqm_collect")
+        if self._inflight:
+            self._inflight.popleft()
+        return (score.value, lcs) if want_lcs else score.value
+
+    def vqm_in_flight(self) -> int:
+        return lib().vqm_in_flight(self._h)
+
+    def vqm_ctx_set_timing(self, enable: bool):
+        _check(lib().vqm_ctx_set_timing(self._h, 1 if enable else 0), "vqm_ctx_set_timing")
+
+    def vqm_ctx_kernel_time(self, kernel_class: int):
+        ms, n = ctypes.c_double(), ctypes.c_int()
+        _check(lib().vqm_ctx_kernel_time(self._h, int(kernel_class), ctypes.byref(ms), ctypes.byref(n)),
+               "vqm_ctx_kernel_time")
+        return ms.value, n.value
+
+    def vqm_debug_decimate(self, ref, dis, bpc: int, scale: int = 0):
+        pr, pd, w, h, _ = _pair(ref, dis, bpc)
+        if scale == 0:
+            _, dw, dh = vqm_ssim_geometry(w, h, bpc)
+        else:
+            dw, dh = -(-w // scale), -(-h // scale)
+        out_r = np.empty((dh, dw), np.float32)
+        out_d = np.empty((dh, dw), np.float32)
+        _check(lib().vqm_debug_decimate(self._h, pr, pd, w, h, int(bpc), int(scale), out_r.ctypes.data,
+                                        out_d.ctypes.data), "vqm_debug_decimate")
+        return out_r, out_d
+
+    def vqm_debug_pyramid(self, ref, dis, bpc: int, level: int):
+        pr, pd, w, h, _ = _pair(ref, dis, bpc)
+        lw, lh = w >> (level - 1), h >> (level - 1)
+        out_r = np.empty((lh, lw), np.float32)
+        out_d = np.empty((lh, lw), np.float32)
+        _check(lib().vqm_debug_pyramid(self._h, pr, pd, w, h, int(bpc), int(level), out_r.ctypes.data,
+                                       out_d.ctypes.data), "vqm_debug_pyramid")
+        return out_r, out_d
+
+
+def vqm_ctx_create(device: int = 0, stream=None) -> Context:
+    return Context(device, stream)

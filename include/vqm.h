@@ -1,0 +1,188 @@
+/*
+ * vqm.h — C ABI of the MI355X (gfx950) per-frame float_ssim / MS-SSIM library.
+ *
+ * Sources (page title, section):
+ *   [ADR-1405] "ADR-1405: float_ssim_hip decimates on the device,
+ *              bit-identical to the CPU" — Context, Decision 1–4.
+ *   [R-1363]   "Research-1363: Device-resident ssimulacra2 and a single-wait
+ *              MS-SSIM on SYCL" — Findings 4 and 6.
+ *   [ADR-1357] "ADR-1357: Run the SYCL CAMBI extractor entirely on the
+ *              device" — Decision (one small result block read back per frame).
+ *   [R-1369]   "Research-1369: SYCL psnr_hvs, motion_v2 and psnr at 4K" —
+ *              §4 (pinned staging), §5 (slot fence), §7 (bit depths, sticky
+ *              geometry).
+ *
+ * Conventions for every call:
+ *   - Return 0 on success or a negative errno; never abort.  On error the
+ *     output arguments are left untouched and vqm_last_error() holds a
+ *     message for the calling thread.
+ *       -EINVAL   NULL pointer; w or h <= 0; w*h above 2^31 - 1; bpc outside
+ *                 8..16; an unusable stream or device index.
+ *       -ENOTSUP  the frame is outside what the method defines: float_ssim
+ *                 with scale > 128 or a decimated side < 11; MS-SSIM with
+ *                 floor(w/16) < 11 or floor(h/16) < 11.  Checked on the host
+ *                 before any HIP call ([ADR-1405] Decision 4).
+ *       -ENOMEM   device or pinned-host allocation failed.
+ *       -ENODEV   no HIP device.
+ *       -EIO      a HIP runtime error (the message names it).
+ *       -EAGAIN   vqm_collect with no frame in flight; a submit with
+ *                 VQM_MAX_IN_FLIGHT frames already in flight.
+ *   - Planes are row-major and tightly packed (stride = w samples): uint8_t
+ *     samples when bpc == 8, native-endian uint16_t with the value in the low
+ *     bits when 9 <= bpc <= 16.  Samples above 2^bpc - 1 violate the
+ *     contract: the call still returns and touches no memory outside its
+ *     buffers, but the score is unspecified.
+ *   - A plane pointer may be host pageable memory, host pinned memory
+ *     (hipHostMalloc) or device memory on the context's device; the library
+ *     tells them apart with hipPointerGetAttributes.  Pageable input is
+ *     copied into pinned staging and sent with one DMA per plane; pinned
+ *     input is sent directly; device input is read in place ([R-1369] §4).
+ *   - The caller owns every buffer it passes.  The library owns its device
+ *     scratch, pinned staging and result slots.
+ *
+ * Numerics:
+ *   - Every bit depth is mapped onto the 8-bit scale, v = raw * 2^-(bpc-8),
+ *     so the SSIM constants use L = 255.
+ *   - float_ssim: scale s = max(1, round(min(w,h)/256)); each plane is
+ *     low-passed with an s x s box of fp32 weight 1.0f/(s*s) (formed on the
+ *     host) and decimated to ceil(w/s) x ceil(h/s); every window sum is exact
+ *     (an integer in units of 2^-52) and rounded once to fp32 — bit-identical
+ *     to the plain definition; then the 11x11 Gaussian (sigma 1.5) SSIM map
+ *     over the valid region, reduced to one double by a fixed-shape tree
+ *     whose order depends only on the plane size ([ADR-1405] Context,
+ *     Decision 1; [R-1363] Finding 4).
+ *   - MS-SSIM: five levels at full resolution, level j+1 the exact 2x2 mean
+ *     of level j; per level the means of luminance, contrast and structure
+ *     (C3 = C2/2); MS = L5^b5 * prod_j (C_j S_j)^b_j with
+ *     b = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333}; NaN when any C_j or S_j
+ *     is <= 0.  All five levels and the combine are enqueued at once and the
+ *     host waits once per frame ([R-1363] Finding 6).
+ *   - Scores are bitwise repeatable for the same input on the same device.
+ */
+#ifndef VQM_H
+#define VQM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VQM_ABI_VERSION 1
+
+/* Exported symbols (the library is built with hidden default visibility). */
+#if defined(__GNUC__)
+#define VQM_API __attribute__((visibility("default")))
+#else
+#define VQM_API
+#endif
+
+/* Frames a context holds in flight between submit and collect. */
+#define VQM_MAX_IN_FLIGHT 4
+
+/* Number of per-level means vqm_msssim_frame_lcs returns: L_1..L_5,
+ * C_1..C_5, S_1..S_5 ([R-1363] Finding 6, enable_lcs). */
+#define VQM_MSSSIM_LCS 15
+
+/* ABI version of the loaded library (VQM_ABI_VERSION it was built with). */
+VQM_API int vqm_abi_version(void);
+
+/* Decimation factor max(1, round(min(w, h) / 256)) with real division and
+ * ties away from zero ([ADR-1405] Context).  Pure host arithmetic; 0 when w
+ * or h <= 0. */
+VQM_API int vqm_ssim_scale(int w, int h);
+
+/* Size of the decimated plane of a w x h frame (ceil(w/s) x ceil(h/s)) and
+ * whether float_ssim accepts the frame: returns 0, or -EINVAL / -ENOTSUP as
+ * vqm_ssim_frame would, without touching the GPU.  Any output may be NULL. */
+VQM_API int vqm_ssim_geometry(int w, int h, int bpc, int *scale, int *dec_w, int *dec_h);
+
+/* float_ssim of one frame pair, blocking.  Uses a per-thread implicit context
+ * on the current HIP device with a library-owned stream; one upload (unless
+ * the planes are already on the device), one device wait, one 8-byte result.
+ * *score receives the mean SSIM. */
+VQM_API int vqm_ssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score);
+
+/* 5-scale MS-SSIM of one frame pair, blocking; as vqm_ssim_frame. */
+VQM_API int vqm_msssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score);
+
+/* MS-SSIM plus the 15 per-level means (lcs: VQM_MSSSIM_LCS doubles, in the
+ * order L_1..L_5, C_1..C_5, S_1..S_5). */
+VQM_API int vqm_msssim_frame_lcs(const void *ref, const void *dis, int w, int h, int bpc,
+                         double *score, double *lcs);
+
+/* ---- explicit contexts: caller-chosen device and stream, pipelined ---- */
+
+typedef struct vqm_ctx vqm_ctx;
+
+/* Create a context on HIP device `device`.  `hip_stream` is a hipStream_t
+ * on that device to enqueue on (e.g. torch.cuda.current_stream().cuda_stream),
+ * or NULL for a library-owned non-blocking stream.  The stream must outlive
+ * the context.  A context is not thread-safe: use one per thread. */
+VQM_API int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out);
+
+/* Wait for the context's frames, then free everything it owns.  NULL is a
+ * no-op. */
+VQM_API void vqm_ctx_destroy(vqm_ctx *ctx);
+
+/* Enqueue one float_ssim frame (upload if needed, decimate, SSIM map,
+ * fixed-tree reduction) and return without waiting.  Host pageable input is
+ * copied before the call returns; pinned or device input must stay unchanged
+ * until the matching vqm_collect.  Frames of different sizes may follow one
+ * another: scratch is keyed by (w, h, bpc) and rebuilt when it changes. */
+VQM_API int vqm_ssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc);
+
+/* Enqueue one MS-SSIM frame (all five levels and the combine). */
+VQM_API int vqm_msssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc);
+
+/* Wait for the oldest frame in flight (the one device wait of that frame)
+ * and return its score.  lcs (may be NULL) receives the 15 per-level means
+ * when the frame was an MS-SSIM frame; for a float_ssim frame it is left
+ * untouched. */
+VQM_API int vqm_collect(vqm_ctx *ctx, double *score, double *lcs);
+
+/* Number of frames in flight. */
+VQM_API int vqm_in_flight(const vqm_ctx *ctx);
+
+/* ---- measurement and inspection ---- */
+
+/* Turn per-kernel timing on or off: while on, every decimation, SSIM and
+ * MS-SSIM level kernel is bracketed by HIP events on the context's stream.
+ * Switching clears the accumulated times. */
+VQM_API int vqm_ctx_set_timing(vqm_ctx *ctx, int enable);
+
+/* Kernel classes reported by vqm_ctx_kernel_time. */
+enum vqm_kernel_class {
+    VQM_KERNEL_DECIMATE = 0,
+    VQM_KERNEL_SSIM = 1,
+    VQM_KERNEL_MSSSIM_LEVEL1 = 2,
+    VQM_KERNEL_MSSSIM_COARSE = 3
+};
+
+/* Total milliseconds and launch count of one kernel class since timing was
+ * switched on.  Waits for the context's stream.  Either output may be NULL. */
+VQM_API int vqm_ctx_kernel_time(vqm_ctx *ctx, int kernel_class, double *total_ms, int *launches);
+
+/* Decimate one frame pair on the device with the float_ssim decimation
+ * kernels and copy the two fp32 planes back (ceil(w/scale) x ceil(h/scale)
+ * floats each, tightly packed).  scale = 0 picks the automatic scale and
+ * applies the float_ssim gate, exactly as vqm_ssim_submit does; scale in
+ * 1..128 forces that factor (the decimated plane may then be any size >= 1).
+ * At scale 1 the planes are the sample values v.  Blocking.  For the
+ * bit-exactness tests ([ADR-1405] Decision 2). */
+VQM_API int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc,
+                               int scale, float *out_ref, float *out_dis);
+
+/* Build the MS-SSIM pyramid on the device exactly as vqm_msssim_submit does
+ * and copy level `level` (2..5, size floor(w/2^(level-1)) x
+ * floor(h/2^(level-1))) of both planes back as fp32, tightly packed.  Level 1
+ * is never materialised (its kernel reads the raw samples).  Blocking.  For
+ * the bit-exactness tests of the pyramid. */
+VQM_API int vqm_debug_pyramid(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc,
+                      int level, float *out_ref, float *out_dis);
+
+/* Message of the last failed call on this thread ("" if none). */
+VQM_API const char *vqm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI library (no GPU needed).
+
+The library loads without a GPU, exports every entry point ``include/vqm.h``
+declares, and its host-only logic — the scale rule, the geometry and the gate,
+argument errors — answers before any HIP call.
+"""
+
+import ctypes
+import errno
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from full_reference_video_amd import vqm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vqm.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"VQM_API\s+[\w\s\*]*?\b(vqm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for must in ("vqm_ssim_frame", "vqm_msssim_frame", "vqm_ctx_create", "vqm_ssim_submit",
+                 "vqm_msssim_submit", "vqm_collect", "vqm_last_error", "vqm_debug_decimate"):
+        assert must in names
+    assert len(names) >= 17
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(vqm.LIB_PATH)
+    missing = [n for n in declared_symbols() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_names_match_the_abi():
+    for n in declared_symbols():
+        if n in ("vqm_ctx_destroy",):
+            continue
+        assert hasattr(vqm, n) or hasattr(vqm.Context, n), n
+
+
+def test_abi_version():
+    assert vqm.vqm_abi_version() == 1
+
+
+def test_scale_rule_matches_oracle():
+    for w in list(range(1, 2000, 7)) + [3839, 3840, 7680, 32895, 32896]:
+        for h in (1, 255, 383, 384, 481, 640, 1080, 2160, 4320, 32896):
+            assert vqm.vqm_ssim_scale(w, h) == oracle.scale(w, h), (w, h)
+    assert vqm.vqm_ssim_scale(0, 100) == 0
+
+
+@pytest.mark.parametrize("w,h,s,dw,dh", [(576, 324, 1, 576, 324), (853, 481, 2, 427, 241),
+                                         (1920, 1080, 4, 480, 270), (3840, 2160, 8, 480, 270)])
+def test_geometry_of_the_workloads(w, h, s, dw, dh):
+    assert vqm.vqm_ssim_geometry(w, h, 10) == (s, dw, dh)
+    assert (oracle.decimated_dim(w, s), oracle.decimated_dim(h, s)) == (dw, dh)
+
+
+def _rc(fn, *args):
+    try:
+        fn(*args)
+    except vqm.VqmError as e:
+        return e.rc
+    return 0
+
+
+def test_gate_agrees_with_oracle_without_a_gpu():
+    # The gate answers -ENOTSUP before any HIP call, so this runs on the CPU.
+    z = np.zeros(16, np.uint16)
+    for (w, h) in [(10, 200), (200, 10), (11, 11), (12, 30), (2815, 2815), (2816, 2816),
+                   (32896, 32896), (32895, 100), (3000, 43)]:
+        s = oracle.scale(w, h)
+        refused = s > 128 or oracle.decimated_dim(w, s) < 11 or oracle.decimated_dim(h, s) < 11
+        got = vqm.lib().vqm_ssim_geometry(w, h, 10, None, None, None)
+        assert got == (-errno.ENOTSUP if refused else 0), (w, h, got)
+        if refused:  # the oracle's gate also answers before reading the planes
+            assert oracle.ssim_rc(z, z, w, h, 10) == -errno.ENOTSUP
+
+
+def test_argument_errors_before_any_hip_call():
+    L = vqm.lib()
+    a = np.zeros((20, 20), np.uint8)
+    s = ctypes.c_double(123.0)
+    p = a.ctypes.data
+    assert L.vqm_ssim_frame(None, p, 20, 20, 8, ctypes.byref(s)) == -errno.EINVAL
+    assert L.vqm_ssim_frame(p, p, 0, 20, 8, ctypes.byref(s)) == -errno.EINVAL
+    assert L.vqm_ssim_frame(p, p, 20, 20, 7, ctypes.byref(s)) == -errno.EINVAL
+    assert L.vqm_ssim_frame(p, p, 20, 20, 17, ctypes.byref(s)) == -errno.EINVAL
+    assert L.vqm_ssim_frame(p, p, 65536, 65536, 8, ctypes.byref(s)) == -errno.EINVAL
+    assert L.vqm_ssim_frame(p, p, 20, 20, 8, None) == -errno.EINVAL
+    assert L.vqm_ssim_frame(p, p, 10, 20, 8, ctypes.byref(s)) == -errno.ENOTSUP
+    assert L.vqm_msssim_frame(p, p, 175, 400, 8, ctypes.byref(s)) == -errno.ENOTSUP
+    assert s.value == 123.0  # untouched on error
+    assert "11x11" in vqm.vqm_last_error()
+    assert L.vqm_collect(None, ctypes.byref(s), None) == -errno.EINVAL
+    assert L.vqm_ssim_submit(None, p, p, 20, 20, 8) == -errno.EINVAL
+
+
+def test_binding_checks_sample_size_and_shape():
+    a8 = np.zeros((20, 20), np.uint8)
+    a16 = np.zeros((20, 20), np.uint16)
+    with pytest.raises(TypeError):
+        vqm.vqm_ssim_frame(a8, a8, 10)
+    with pytest.raises(TypeError):
+        vqm.vqm_ssim_frame(a16, a16, 8)
+    with pytest.raises(ValueError):
+        vqm.vqm_ssim_frame(a8, np.zeros((20, 21), np.uint8), 8)
+    with pytest.raises(ValueError):
+        vqm.vqm_ssim_frame(a8[:, ::2], a8[:, ::2], 8)
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK),
+                    reason="a GPU is present")
+def test_no_device_is_enodev():
+    a = np.zeros((400, 400), np.uint8)
+    assert _rc(vqm.vqm_ssim_frame, a, a, 8) == -errno.ENODEV
+    assert _rc(vqm.Context, 0, None) == -errno.ENODEV

@@ -1,0 +1,286 @@
+"""Parity of the HIP path with the oracle, on an MI355X.
+
+Bars: decimated planes and MS-SSIM pyramid planes bit-exact; every per-frame
+score within 5e-5 of the oracle ("ADR-1405: float_ssim_hip decimates on the
+device, bit-identical to the CPU", Context); scores bitwise repeatable.
+Every call goes through the C ABI (``full_reference_video_amd.vqm``).
+"""
+
+import errno
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from full_reference_video_amd import synth, vqm
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def ctx(torch_cuda):
+    c = vqm.Context(0)
+    yield c
+    c.close()
+
+
+def bits(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+def to_dev(torch, a):
+    t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+    return t.cuda()
+
+
+# ------------------------------------------------------------ decimation
+
+@pytest.mark.parametrize("c", [2, 3, 4])
+def test_decimate_bit_exact_on_workload_frames(ctx, c):
+    src = synth.FrameSource(c)
+    s = oracle.scale(src.w, src.h)
+    for t in (0, 1, src.workload.frames - 1):
+        ref, dis = src.pair(t)
+        say(f"decimate config {c} frame {t} {src.w}x{src.h} bpc {src.bpc} s {s}")
+        gr, gd = ctx.vqm_debug_decimate(ref, dis, src.bpc)
+        assert np.array_equal(bits(gr), bits(oracle.decimate(ref, src.bpc, s)))
+        assert np.array_equal(bits(gd), bits(oracle.decimate(dis, src.bpc, s)))
+
+
+SCALES = list(range(1, 17)) + [31, 64, 127, 128]
+
+
+@pytest.mark.parametrize("s", SCALES)
+def test_decimate_bit_exact_forced_scale(ctx, s):
+    # Fast-path friendly widths (multiples of 16 samples, bottom rows that
+    # mirror) and odd sizes (the general kernel), every depth.
+    sizes = [(max(16, s) * 12, s * 12 + 1), (s * 11 + 3, s * 11 + 5)]
+    for bpc in (8, 9, 10, 11, 12, 16):
+        for (w, h) in sizes:
+            ref = synth.random_planes(s * 1000 + bpc, w, h, bpc)
+            dis = synth.random_planes(s * 1000 + bpc + 7, w, h, bpc)
+            say(f"decimate s {s} bpc {bpc} {w}x{h}")
+            gr, gd = ctx.vqm_debug_decimate(ref, dis, bpc, s)
+            assert np.array_equal(bits(gr), bits(oracle.decimate(ref, bpc, s))), (s, bpc, w, h)
+            assert np.array_equal(bits(gd), bits(oracle.decimate(dis, bpc, s))), (s, bpc, w, h)
+
+
+@pytest.mark.parametrize("bpc,s,w,h", [(16, 2, 8320, 30), (8, 2, 16512, 24), (16, 4, 16384, 48),
+                                       (8, 8, 2048, 100)])
+def test_decimate_wide_rows_span_several_workgroups(ctx, bpc, s, w, h):
+    ref = synth.random_planes(w + bpc, w, h, bpc)
+    dis = synth.random_planes(w + bpc + 1, w, h, bpc)
+    say(f"decimate wide s {s} bpc {bpc} {w}x{h}")
+    gr, gd = ctx.vqm_debug_decimate(ref, dis, bpc, s)
+    assert np.array_equal(bits(gr), bits(oracle.decimate(ref, bpc, s)))
+    assert np.array_equal(bits(gd), bits(oracle.decimate(dis, bpc, s)))
+
+
+def test_decimate_extreme_values(ctx):
+    for bpc in (8, 10, 16):
+        for kind in ("max", "zero", "checker"):
+            for s in (2, 3, 8):
+                w, h = 16 * s * 11, 13 * s
+                p = synth.random_planes(0, w, h, bpc, kind)
+                say(f"decimate extreme {kind} s {s} bpc {bpc}")
+                gr, _ = ctx.vqm_debug_decimate(p, p, bpc, s)
+                assert np.array_equal(bits(gr), bits(oracle.decimate(p, bpc, s)))
+
+
+# ------------------------------------------------------------ float_ssim
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4])
+def test_ssim_workload_frames_within_tolerance(ctx, c):
+    src = synth.FrameSource(c)
+    frames = sorted({0, 1, src.workload.frames // 2, src.workload.frames - 1})
+    for t in frames:
+        ref, dis = src.pair(t)
+        say(f"ssim config {c} frame {t}")
+        want = oracle.ssim(ref, dis, src.bpc)
+        got = vqm.vqm_ssim_frame(ref, dis, src.bpc)
+        assert abs(got - want) <= TOL, (c, t, got, want)
+
+
+@pytest.mark.parametrize("w,h,bpc", [(300, 200, 8), (400, 300, 10), (700, 500, 12), (853, 481, 9),
+                                     (1000, 1000, 11), (1283, 767, 16), (1666, 1001, 10),
+                                     (2000, 1200, 8), (4000, 2000, 12)])
+def test_ssim_ragged_sizes_and_depths(ctx, w, h, bpc):
+    src = synth.FrameSource(4, w=w, h=h, bpc=bpc)
+    ref, dis = src.pair(5)
+    say(f"ssim {w}x{h} bpc {bpc} s {oracle.scale(w, h)}")
+    want = oracle.ssim(ref, dis, bpc)
+    ctx.vqm_ssim_submit(ref, dis, bpc)
+    got = ctx.vqm_collect()
+    assert abs(got - want) <= TOL, (w, h, bpc, got, want)
+
+
+def test_ssim_minimum_plane(ctx):
+    # the smallest accepted decimated plane: one map pixel
+    for (w, h) in [(11, 11), (11, 40), (40, 11)]:
+        src = synth.FrameSource(1, w=w, h=h)
+        ref, dis = src.pair(0)
+        say(f"ssim minimum {w}x{h}")
+        assert abs(vqm.vqm_ssim_frame(ref, dis, 8) - oracle.ssim(ref, dis, 8)) <= TOL
+
+
+def test_ssim_identity_is_exactly_one(ctx):
+    for c in (1, 2, 3, 4):
+        src = synth.FrameSource(c)
+        ref, _ = src.pair(0)
+        say(f"ssim identity config {c}")
+        assert vqm.vqm_ssim_frame(ref, ref, src.bpc) == 1.0
+
+
+@pytest.mark.parametrize("a,b", [(0, 0), (10, 200), (128, 129), (255, 0)])
+def test_ssim_constant_planes(ctx, a, b):
+    for (w, h, bpc) in [(300, 200, 8), (1920, 1080, 10)]:
+        full = (1 << bpc) - 1
+        dt = np.uint8 if bpc == 8 else np.uint16
+        ref = np.full((h, w), round(a * full / 255), dt)
+        dis = np.full((h, w), round(b * full / 255), dt)
+        say(f"ssim constant {a} {b} {w}x{h}")
+        assert abs(vqm.vqm_ssim_frame(ref, dis, bpc) - oracle.ssim(ref, dis, bpc)) <= TOL
+
+
+def test_ssim_repeatable_across_pointer_kinds_and_streams(torch_cuda):
+    torch = torch_cuda
+    src = synth.FrameSource(4)
+    ref, dis = src.pair(3)
+    say("ssim pointer kinds")
+    base = vqm.vqm_ssim_frame(ref, dis, 10)
+    pin_r = torch.from_numpy(ref.view(np.int16)).pin_memory()
+    pin_d = torch.from_numpy(dis.view(np.int16)).pin_memory()
+    dev_r, dev_d = to_dev(torch, ref), to_dev(torch, dis)
+    assert vqm.vqm_ssim_frame(pin_r, pin_d, 10) == base
+    assert vqm.vqm_ssim_frame(dev_r, dev_d, 10) == base
+    assert vqm.vqm_ssim_frame(pin_r, dis, 10) == base       # mixed kinds
+    s = torch.cuda.Stream()
+    with vqm.Context(0, s) as c:
+        for _ in range(3):
+            c.vqm_ssim_submit(dev_r, dev_d, 10)
+        assert [c.vqm_collect() for _ in range(3)] == [base] * 3
+    assert abs(base - oracle.ssim(ref, dis, 10)) <= TOL
+
+
+def test_ssim_geometry_changes_between_frames(ctx):
+    # A context that alternates sizes must rebuild its scratch every time.
+    a = synth.FrameSource(2).pair(0)
+    b = synth.FrameSource(3).pair(0)
+    c = synth.FrameSource(1).pair(0)
+    want = [oracle.ssim(*a, 12), oracle.ssim(*b, 8), oracle.ssim(*c, 8)]
+    say("ssim sticky geometry")
+    got = []
+    for _ in range(2):
+        ctx.vqm_ssim_submit(*a, 12)
+        ctx.vqm_ssim_submit(*b, 8)
+        ctx.vqm_ssim_submit(*c, 8)
+        got += [ctx.vqm_collect() for _ in range(3)]
+    for i, g in enumerate(got):
+        assert abs(g - want[i % 3]) <= TOL
+    assert got[:3] == got[3:]
+
+
+def test_pipelined_submit_collect_and_flow_control(ctx):
+    src = synth.FrameSource(3)
+    pairs = [src.pair(t) for t in range(6)]
+    say("ssim pipelined")
+    want = [vqm.vqm_ssim_frame(r, d, 8) for (r, d) in pairs]
+    for r, d in pairs[:vqm.VQM_MAX_IN_FLIGHT]:
+        ctx.vqm_ssim_submit(r, d, 8)
+    with pytest.raises(vqm.VqmError) as e:
+        ctx.vqm_ssim_submit(*pairs[4], 8)
+    assert e.value.rc == -errno.EAGAIN
+    got = [ctx.vqm_collect()]
+    for r, d in pairs[4:]:
+        ctx.vqm_ssim_submit(r, d, 8)
+        got.append(ctx.vqm_collect())
+    while ctx.vqm_in_flight():
+        got.append(ctx.vqm_collect())
+    assert got == want
+    with pytest.raises(vqm.VqmError) as e:
+        ctx.vqm_collect()
+    assert e.value.rc == -errno.EAGAIN
+
+
+def test_gate_on_gpu(ctx):
+    z = np.zeros((10, 400), np.uint8)
+    with pytest.raises(vqm.VqmError) as e:
+        vqm.vqm_ssim_frame(z, z, 8)
+    assert e.value.rc == -errno.ENOTSUP
+    z = np.zeros((170, 400), np.uint8)
+    with pytest.raises(vqm.VqmError) as e:
+        ctx.vqm_msssim_submit(z, z, 8)
+    assert e.value.rc == -errno.ENOTSUP
+
+
+# ------------------------------------------------------------ MS-SSIM
+
+def test_msssim_workload_frame(ctx):
+    src = synth.FrameSource(5)
+    ref, dis = src.pair(0)
+    say("msssim config 5 frame 0")
+    want, want_lcs = oracle.msssim(ref, dis, 8, want_lcs=True)
+    got, lcs = vqm.vqm_msssim_frame_lcs(ref, dis, 8)
+    assert abs(got - want) <= TOL, (got, want)
+    assert np.all(np.abs(lcs - want_lcs) <= TOL)
+
+
+@pytest.mark.parametrize("w,h,bpc", [(176, 176, 8), (640, 360, 8), (400, 352, 10), (723, 389, 12),
+                                     (1001, 703, 16), (1920, 1080, 8)])
+def test_msssim_sizes_and_depths(ctx, w, h, bpc):
+    src = synth.FrameSource(5, w=w, h=h, bpc=bpc)
+    ref, dis = src.pair(1)
+    say(f"msssim {w}x{h} bpc {bpc}")
+    want, want_lcs = oracle.msssim(ref, dis, bpc, want_lcs=True)
+    ctx.vqm_msssim_submit(ref, dis, bpc)
+    got, lcs = ctx.vqm_collect(want_lcs=True)
+    assert abs(got - want) <= TOL, (got, want)
+    assert np.all(np.abs(lcs - want_lcs) <= TOL)
+
+
+@pytest.mark.parametrize("w,h,bpc", [(640, 360, 8), (723, 389, 12), (1001, 703, 16)])
+def test_msssim_pyramid_bit_exact(ctx, w, h, bpc):
+    src = synth.FrameSource(5, w=w, h=h, bpc=bpc)
+    ref, dis = src.pair(2)
+    xr, xd = oracle.sample_plane(ref, bpc), oracle.sample_plane(dis, bpc)
+    for level in range(2, 6):
+        xr, xd = oracle.downsample(xr), oracle.downsample(xd)
+        say(f"pyramid {w}x{h} bpc {bpc} level {level}")
+        gr, gd = ctx.vqm_debug_pyramid(ref, dis, bpc, level)
+        assert np.array_equal(bits(gr), bits(xr))
+        assert np.array_equal(bits(gd), bits(xd))
+
+
+def test_msssim_identity(ctx):
+    src = synth.FrameSource(5, w=960, h=540)
+    ref, _ = src.pair(0)
+    say("msssim identity")
+    score, lcs = vqm.vqm_msssim_frame_lcs(ref, ref, 8)
+    assert abs(score - 1.0) <= 1e-6
+    assert np.all(lcs[:10] == 1.0)  # luminance and contrast are mirror images
+
+
+def test_msssim_repeatable(ctx):
+    src = synth.FrameSource(5, w=1280, h=720)
+    ref, dis = src.pair(4)
+    say("msssim repeatable")
+    a = vqm.vqm_msssim_frame(ref, dis, 8)
+    for _ in range(3):
+        ctx.vqm_msssim_submit(ref, dis, 8)
+    assert [ctx.vqm_collect() for _ in range(3)] == [a] * 3
