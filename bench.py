@@ -46,18 +46,23 @@ def algorithmic_bytes(wl, s: int) -> int:
     return 2 * covered_extent(wl.w, s) * covered_extent(wl.h, s) * bps
 
 
-def run_pass(ctxs, frames, metric, bpc, lag, collect_all=True):
-    """Submit every frame once, collecting with the given lag; return scores."""
+def run_pass(ctxs, frames, metric, bpc, batch, lag):
+    """Submit every frame once in batches of `batch`, rotating over the
+    contexts, and collect each frame (one wait each) once more than `lag`
+    frames are in flight; return the scores in frame order."""
     import collections
     pending = collections.deque()
     scores = []
-    for f, (r, d) in enumerate(frames):
-        c = ctxs[f % len(ctxs)]
+    for k, f0 in enumerate(range(0, len(frames), batch)):
+        c = ctxs[k % len(ctxs)]
+        chunk = frames[f0:f0 + batch]
+        refs = [r for r, _ in chunk]
+        diss = [d for _, d in chunk]
         if metric == "ms_ssim":
-            c.vqm_msssim_submit(r, d, bpc)
+            c.vqm_msssim_submit_batch(refs, diss, bpc)
         else:
-            c.vqm_ssim_submit(r, d, bpc)
-        pending.append(c)
+            c.vqm_ssim_submit_batch(refs, diss, bpc)
+        pending.extend([c] * len(chunk))
         while len(pending) > lag:
             scores.append(pending.popleft().vqm_collect())
     while pending:
@@ -90,8 +95,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="workload number 1..5")
-    ap.add_argument("--streams", type=int, default=2, help="contexts/streams frames rotate over")
-    ap.add_argument("--lag", type=int, default=0, help="frames in flight before a collect (0: 2*streams)")
+    ap.add_argument("--streams", type=int, default=1, help="contexts/streams batches rotate over")
+    ap.add_argument("--batch", type=int, default=4, help="frames per submit (and per kernel launch)")
+    ap.add_argument("--lag", type=int, default=0,
+                    help="frames in flight before a collect (0: 2*batch, capped by the in-flight slots)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0: skip)")
     args = ap.parse_args()
 
@@ -123,22 +130,25 @@ def main():
 
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
     ctxs = [vqm.Context(0, st) for st in streams]
-    lag = args.lag if args.lag > 0 else min(2 * args.streams, args.streams * vqm.VQM_MAX_IN_FLIGHT)
+    lag = args.lag if args.lag > 0 else min(2 * args.batch, args.streams * vqm.VQM_MAX_IN_FLIGHT - args.batch)
+    if lag + args.batch > args.streams * vqm.VQM_MAX_IN_FLIGHT:
+        raise SystemExit(f"lag {lag} + batch {args.batch} exceeds the in-flight slots")
 
     log(f"warmup {args.warmup} passes")
     ref_scores = None
     for _ in range(args.warmup):
-        sc = run_pass(ctxs, dev, wl.metric, wl.bpc, lag)
+        sc = run_pass(ctxs, dev, wl.metric, wl.bpc, args.batch, lag)
         if ref_scores is None:
             ref_scores = sc
         elif sc != ref_scores:
             raise RuntimeError("scores changed between passes")
     torch.cuda.synchronize()
 
-    log(f"timed {args.steps} passes over {wl.frames} frames, {args.streams} streams, lag {lag}")
+    log(f"timed {args.steps} passes over {wl.frames} frames, batch {args.batch}, {args.streams} streams, "
+        f"lag {lag}")
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        sc = run_pass(ctxs, dev, wl.metric, wl.bpc, lag)
+        sc = run_pass(ctxs, dev, wl.metric, wl.bpc, args.batch, lag)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     if ref_scores is not None and sc != ref_scores:
@@ -152,39 +162,38 @@ def main():
         c.vqm_ctx_set_timing(True)
     tsteps = max(1, min(args.steps, 10))
     for _ in range(tsteps):
-        run_pass(ctxs, dev, wl.metric, wl.bpc, lag)
+        run_pass(ctxs, dev, wl.metric, wl.bpc, args.batch, lag)
     kt = {}
     for cls, name in ((vqm.VQM_KERNEL_DECIMATE, "decimate"), (vqm.VQM_KERNEL_SSIM, "ssim_map"),
                       (vqm.VQM_KERNEL_MSSSIM_LEVEL1, "ms_level1"),
                       (vqm.VQM_KERNEL_MSSSIM_COARSE, "ms_levels2_5")):
-        ms = n = 0
+        ms = n = nf = 0
         for c in ctxs:
-            a, b = c.vqm_ctx_kernel_time(cls)
+            a, b, fr = c.vqm_ctx_kernel_time(cls)
             ms += a
             n += b
+            nf += fr
         if n:
-            kt[name] = {"avg_us": 1000.0 * ms / n, "launches": n}
+            kt[name] = {"avg_us": 1000.0 * ms / n, "launches": n, "frames_per_launch": nf / n}
     for c in ctxs:
         c.vqm_ctx_set_timing(False)
 
     alg = algorithmic_bytes(wl, s)
-    if wl.metric == "float_ssim" and "decimate" in kt:
-        avg_s = kt["decimate"]["avg_us"] * 1e-6
-        achieved = alg / avg_s / 1e9
+    if wl.metric == "float_ssim":
+        name = "decimate" if "decimate" in kt else "ssim_map"
+        per_launch = alg * kt[name]["frames_per_launch"]
+        avg_s = kt[name]["avg_us"] * 1e-6
+        achieved = per_launch / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "decimate_pow2", "bytes_per_launch": alg}
-    elif wl.metric == "float_ssim":
-        avg_s = kt["ssim_map"]["avg_us"] * 1e-6
-        achieved = alg / avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "ssim_map", "bytes_per_launch": alg}
+                "kernel": "decimate_pow2" if name == "decimate" else "ssim_map",
+                "bytes_per_launch": int(per_launch)}
     else:
         # MS-SSIM level 1 is VALU-bound: flops of the separable moments and
         # the l/c/s terms per valid map pixel (see the design notes).
         mw, mh = wl.w - 10, wl.h - 10
         flops = 2.0 * (3 * wl.w * (wl.h) / 2 + 55.0 * (mh + 10) * mw + 55.0 * mh * mw) + 40.0 * mh * mw
+        flops *= kt["ms_level1"]["frames_per_launch"]
         avg_s = kt["ms_level1"]["avg_us"] * 1e-6
         achieved = flops / avg_s / 1e12
         roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
@@ -211,7 +220,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "w": wl.w, "h": wl.h, "bpc": wl.bpc, "frames_per_step": wl.frames,
-                   "scale": s, "streams": args.streams, "lag": lag,
+                   "scale": s, "batch": args.batch, "streams": args.streams, "lag": lag,
                    "path_GBps": round(alg * fps / 1e9, 1)},
         "kernels": kt,
         "roofline": roof,

@@ -17,20 +17,22 @@
 //  * decimate_pow2 — s = 2^k, where tap = 2^-2k and every product is exact,
 //    so the units of a product are raw * 2^(52 - 2k - (bpc-8)): a constant
 //    shift of the raw integer.  The shift is hoisted out of the window sum,
-//    which becomes a plain integer sum of raw samples (v_sad_u8/v_sad_u16 add
-//    four or two samples per instruction), rounded once to fp32 and scaled by
-//    the exact power of two.  This is the HBM-bound path of the 1080p and
-//    2160p frames.
+//    which becomes a plain integer sum of raw samples (v_sad_u8 / v_sad_u16
+//    add four or two samples per instruction), rounded once to fp32 and
+//    scaled by the exact power of two.  This is the HBM-bound path of the
+//    1080p and 2160p frames.
 //
-// Layout of decimate_pow2 (one workgroup per output row Y, or several for
-// very wide rows): a thread owns an aligned group of G = max(s, 16/sizeof(T))
-// raw columns, i.e. CPT = G/s whole chunks [X*s, X*s + s), and reads them with
-// 128-bit non-temporal loads for each of the s raw rows of the window band —
-// every raw sample of the frame is read once.  Window X covers the high half
-// of chunk X-1 and the low half of chunk X, so a thread keeps the two half
-// sums per chunk and takes the high half of the chunk before its first one
-// from the previous lane (a cross-lane shuffle), the previous wave (LDS), or,
-// at the left edge, the mirror of its own low half.
+// Layout of decimate_pow2.  Chunk k of a row is the s raw columns
+// [k*s, k*s + s); window X covers the high half of chunk X-1 and the low half
+// of chunk X.  A lane owns one aligned group of G = max(s, 16/sizeof(T))
+// columns (CPT = G/s chunks) and reads it with 128-bit non-temporal loads for
+// each of the s rows of the window band, so a wave reads contiguous,
+// 16-byte-aligned kilobytes.  The high half of the chunk before a lane's
+// first chunk comes from the previous lane (one cross-lane shift).  To make
+// every wave self-contained, wave v's lanes hold groups 63v-1 .. 63v+62: lane
+// 0 re-reads the last group of the previous wave (1/64 extra, which the XCD
+// remap keeps in the same L2) and outputs nothing.  At the left edge lane 0
+// of wave 0 stands in for group -1 with the mirror of chunk 0's low half.
 #include "vqm_kernels.h"
 
 namespace vqm {
@@ -63,9 +65,11 @@ __device__ __forceinline__ uint64_t product_units(uint32_t raw, float tap, int s
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void decimate_general(
-    const T *__restrict__ ref, const T *__restrict__ dis, int w, int h, int bpc, int s, float tap,
-    int dec_w, int dec_h, float *__restrict__ out_ref, float *__restrict__ out_dis, int opitch) {
+__global__ __launch_bounds__(256) void decimate_general(DecimateBatch b, int w, int h, int bpc, int s,
+                                                        float tap, int dec_w, int dec_h, int opitch) {
+    const DecimateFrame &fr = b.f[blockIdx.z];
+    const T *__restrict__ ref = static_cast<const T *>(fr.ref);
+    const T *__restrict__ dis = static_cast<const T *>(fr.dis);
     const int X = blockIdx.x * 64 + (threadIdx.x & 63);
     const int Y = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (X >= dec_w || Y >= dec_h) return;
@@ -83,8 +87,8 @@ __global__ __launch_bounds__(256) void decimate_general(
     // One rounding to fp32 (the sum has at most 53 significant bits), then an
     // exact scaling by 2^-52.
     const size_t o = (size_t)Y * opitch + X;
-    out_ref[o] = (float)ar * 0x1p-52f;
-    out_dis[o] = (float)ad * 0x1p-52f;
+    fr.out_ref[o] = (float)ar * 0x1p-52f;
+    fr.out_dis[o] = (float)ad * 0x1p-52f;
 }
 
 // ------------------------------------------------------------ power-of-two path
@@ -92,11 +96,12 @@ __global__ __launch_bounds__(256) void decimate_general(
 template <typename T> struct Samples;
 template <> struct Samples<uint8_t> {
     static constexpr int per_word = 4;
-    // sum of the four bytes of w (those outside `mask` zeroed) plus acc
+    // sum of the four bytes of w, plus acc
     __device__ static uint32_t add(uint32_t w, uint32_t acc) { return __builtin_amdgcn_sad_u8(w, 0u, acc); }
 };
 template <> struct Samples<uint16_t> {
     static constexpr int per_word = 2;
+    // sum of the two halves of w, plus acc
     __device__ static uint32_t add(uint32_t w, uint32_t acc) { return __builtin_amdgcn_sad_u16(w, 0u, acc); }
 };
 
@@ -108,9 +113,9 @@ __host__ __device__ constexpr uint32_t sample_mask(int e0, int e1) {
     return m;
 }
 
-// Add the samples of word `q` of vector `v` (within the thread's group) into
-// the half sums of the chunks they belong to.  Everything but `word` is a
-// compile-time constant after unrolling.
+// Add the samples of a word whose first sample is column g0 of the lane's
+// group into the half sums of the chunks they belong to.  Everything but
+// `word` is a compile-time constant after unrolling.
 template <typename T, int S, int CPT>
 __device__ __forceinline__ void add_word(uint32_t word, int g0, uint32_t (&lo)[CPT], uint32_t (&hi)[CPT]) {
     constexpr int SPW = Samples<T>::per_word;
@@ -132,20 +137,33 @@ __device__ __forceinline__ void add_word(uint32_t word, int g0, uint32_t (&lo)[C
     }
 }
 
+template <typename T, int S> struct Pow2Shape {
+    static constexpr int SPW = Samples<T>::per_word;  // samples per 32-bit word
+    static constexpr int V = 4 * SPW;                 // samples per 128-bit load
+    static constexpr int G = S > V ? S : V;           // raw columns per lane
+    static constexpr int NV = G / V;                  // 128-bit loads per lane per row
+    static constexpr int CPT = G / S;                 // chunks (outputs) per lane
+};
+
+constexpr int kPow2Waves = 1;  // waves per workgroup
+
 template <typename T, int S>
-__global__ __launch_bounds__(1024) void decimate_pow2(
-    const T *__restrict__ ref, const T *__restrict__ dis, int w, int h, int dec_w, float post,
-    float *__restrict__ out_ref, float *__restrict__ out_dis, int opitch) {
-    constexpr int SPW = Samples<T>::per_word;  // samples per 32-bit word
-    constexpr int V = 4 * SPW;                 // samples per 128-bit load
-    constexpr int G = S > V ? S : V;           // raw columns per thread
-    constexpr int NV = G / V;                  // 128-bit loads per thread per row
-    constexpr int CPT = G / S;                 // chunks (outputs) per thread
+__global__ __launch_bounds__(64 * kPow2Waves) void decimate_pow2(DecimateBatch b, int w, int h, int dec_w,
+                                                                 float post, int opitch) {
+    using Sh = Pow2Shape<T, S>;
+    constexpr int V = Sh::V, NV = Sh::NV, CPT = Sh::CPT, G = Sh::G;
     constexpr int HALF = S / 2;
 
-    const int Y = blockIdx.y;
-    const int grp = blockIdx.x * blockDim.x + threadIdx.x;
-    const int c0 = grp * G;
+    int bx, Y, bz;
+    xcd_block(bx, Y, bz);
+    const DecimateFrame &fr = b.f[bz];
+    const T *__restrict__ ref = static_cast<const T *>(fr.ref);
+    const T *__restrict__ dis = static_cast<const T *>(fr.dis);
+
+    const int lane = threadIdx.x & 63;
+    const int wv = bx * kPow2Waves + (threadIdx.x >> 6);
+    const int g = 63 * wv + lane - 1;  // this lane's group; -1 stands for the left mirror
+    const int c0 = (g < 0 ? 0 : g) * G;
 
     uint32_t lr[CPT], hr[CPT], ld[CPT], hd[CPT];
 #pragma unroll
@@ -157,133 +175,103 @@ __global__ __launch_bounds__(1024) void decimate_pow2(
         const size_t row = (size_t)mirror(Y * S - HALF + r, h) * (size_t)w + (size_t)c0;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+            u32x4 a = {0u, 0u, 0u, 0u}, d = {0u, 0u, 0u, 0u};
             // w is a multiple of V, so a vector is wholly inside or outside
             // the row; vectors outside hold only unused samples.
             if (c0 + v * V < w) {
                 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ref + row + v * V));
-                b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(dis + row + v * V));
+                d = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(dis + row + v * V));
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                add_word<T, S, CPT>(a[q], v * V + q * SPW, lr, hr);
-                add_word<T, S, CPT>(b[q], v * V + q * SPW, ld, hd);
+                add_word<T, S, CPT>(a[q], v * V + q * Sh::SPW, lr, hr);
+                add_word<T, S, CPT>(d[q], v * V + q * Sh::SPW, ld, hd);
             }
         }
     }
-
-    // High half of the chunk just before this thread's first chunk.
-    uint32_t pr = __shfl_up(hr[CPT - 1], 1, 64);
-    uint32_t pd = __shfl_up(hd[CPT - 1], 1, 64);
-    __shared__ uint32_t xr[16], xd[16];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 63) {
-        xr[wave] = hr[CPT - 1];
-        xd[wave] = hd[CPT - 1];
+    if (g < 0) {
+        // Columns -s/2..-1 mirror onto 0..s/2-1: the low half of chunk 0.
+        hr[CPT - 1] = lr[0];
+        hd[CPT - 1] = ld[0];
     }
-    __syncthreads();
-    if (lane == 0) {
-        if (wave > 0) {
-            pr = xr[wave - 1];
-            pd = xd[wave - 1];
-        } else if (grp == 0) {
-            // Left edge: columns -s/2..-1 mirror onto 0..s/2-1, the low half.
-            pr = lr[0];
-            pd = ld[0];
-        } else {
-            // The previous group belongs to another workgroup: read the s/2
-            // columns [c0 - s/2, c0) of the s rows again (one lane only).
-            pr = pd = 0u;
-            for (int r = 0; r < S; ++r) {
-                const size_t row = (size_t)mirror(Y * S - HALF + r, h) * (size_t)w;
-                for (int c = c0 - HALF; c < c0; ++c) {
-                    pr += ref[row + c];
-                    pd += dis[row + c];
-                }
-            }
-        }
-    }
-
+    // High half of the chunk just before this lane's first chunk.
+    const uint32_t pr = __shfl_up(hr[CPT - 1], 1, 64);
+    const uint32_t pd = __shfl_up(hd[CPT - 1], 1, 64);
+    if (lane == 0) return;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-        const int X = grp * CPT + k;
+        const int X = g * CPT + k;
         if (X < dec_w) {
             const uint32_t tr = (k == 0 ? pr : hr[k - 1]) + lr[k];
             const uint32_t td = (k == 0 ? pd : hd[k - 1]) + ld[k];
-            // One rounding (exact below 2^24), then the exact power of two.
+            // One rounding (the only one: sums below 2^24 are exact), then
+            // the exact power of two.
             const size_t o = (size_t)Y * opitch + X;
-            out_ref[o] = (float)tr * post;
-            out_dis[o] = (float)td * post;
+            fr.out_ref[o] = (float)tr * post;
+            fr.out_dis[o] = (float)td * post;
         }
     }
 }
 
 template <typename T, int S>
-hipError_t launch_pow2(const void *ref, const void *dis, int w, int h, int bpc, int dec_w, int dec_h,
-                       float *out_ref, float *out_dis, int opitch, hipStream_t stream) {
-    constexpr int SPW = Samples<T>::per_word;
-    constexpr int V = 4 * SPW;
-    constexpr int G = S > V ? S : V;
-    constexpr int CPT = G / S;
+hipError_t launch_pow2(const DecimateBatch &b, int n, int w, int h, int bpc, int dec_w, int dec_h,
+                       int opitch, hipStream_t stream) {
+    using Sh = Pow2Shape<T, S>;
     int k = 0;
     while ((1 << k) < S) ++k;
     const float post = ldexpf(1.0f, -(2 * k + bpc - 8));
-    const int threads = (dec_w + CPT - 1) / CPT;
-    int block = ((threads + 63) / 64) * 64;
-    if (block > 1024) block = 1024;
-    const dim3 grid((threads + block - 1) / block, dec_h);
-    hipLaunchKernelGGL((decimate_pow2<T, S>), grid, dim3(block), 0, stream,
-                       static_cast<const T *>(ref), static_cast<const T *>(dis), w, h, dec_w, post,
-                       out_ref, out_dis, opitch);
+    const int groups = (dec_w + Sh::CPT - 1) / Sh::CPT;  // groups holding outputs
+    const int waves = (groups + 62) / 63;
+    const dim3 grid((waves + kPow2Waves - 1) / kPow2Waves, dec_h, n);
+    hipLaunchKernelGGL((decimate_pow2<T, S>), grid, dim3(64 * kPow2Waves), 0, stream, b, w, h, dec_w, post,
+                       opitch);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_pow2_any(int s, const void *ref, const void *dis, int w, int h, int bpc, int dec_w,
-                           int dec_h, float *out_ref, float *out_dis, int opitch, hipStream_t stream) {
+hipError_t launch_pow2_any(int s, const DecimateBatch &b, int n, int w, int h, int bpc, int dec_w, int dec_h,
+                           int opitch, hipStream_t stream) {
     switch (s) {
-    case 2: return launch_pow2<T, 2>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
-    case 4: return launch_pow2<T, 4>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
-    case 8: return launch_pow2<T, 8>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
-    case 16: return launch_pow2<T, 16>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
-    case 32: return launch_pow2<T, 32>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
-    case 64: return launch_pow2<T, 64>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
-    case 128: return launch_pow2<T, 128>(ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+    case 2: return launch_pow2<T, 2>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
+    case 4: return launch_pow2<T, 4>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
+    case 8: return launch_pow2<T, 8>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
+    case 16: return launch_pow2<T, 16>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
+    case 32: return launch_pow2<T, 32>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
+    case 64: return launch_pow2<T, 64>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
+    case 128: return launch_pow2<T, 128>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-bool decimate_fast_path(const void *ref, const void *dis, int w, int h, int bpc, int s) {
+bool decimate_fast_path(const DecimateBatch &b, int n, int w, int h, int bpc, int s) {
     (void)h;
     if (s < 2 || s > 128 || (s & (s - 1)) != 0) return false;
     const int V = bpc == 8 ? 16 : 8;
     if (w % V != 0) return false;
-    if (((uintptr_t)ref | (uintptr_t)dis) & 15u) return false;
+    for (int i = 0; i < n; ++i)
+        if (((uintptr_t)b.f[i].ref | (uintptr_t)b.f[i].dis) & 15u) return false;
     const int dec_w = (w + s - 1) / s;
     // the last window's right half must lie inside the row (no right mirror)
     if (w - s * (dec_w - 1) < s / 2) return false;
     return true;
 }
 
-hipError_t launch_decimate(const void *ref, const void *dis, int w, int h, int bpc, int s, float tap,
-                           float *out_ref, float *out_dis, int dec_w, int dec_h, int opitch,
-                           hipStream_t stream) {
-    if (decimate_fast_path(ref, dis, w, h, bpc, s)) {
-        if (bpc == 8)
-            return launch_pow2_any<uint8_t>(s, ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
-        return launch_pow2_any<uint16_t>(s, ref, dis, w, h, bpc, dec_w, dec_h, out_ref, out_dis, opitch, stream);
+hipError_t launch_decimate(const DecimateBatch &b, int n, int w, int h, int bpc, int s, float tap, int dec_w,
+                           int dec_h, int opitch, hipStream_t stream) {
+    if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
+    if (decimate_fast_path(b, n, w, h, bpc, s)) {
+        if (bpc == 8) return launch_pow2_any<uint8_t>(s, b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
+        return launch_pow2_any<uint16_t>(s, b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
     }
-    const dim3 grid((dec_w + 63) / 64, (dec_h + 3) / 4);
+    const dim3 grid((dec_w + 63) / 64, (dec_h + 3) / 4, n);
     if (bpc == 8)
-        hipLaunchKernelGGL(decimate_general<uint8_t>, grid, dim3(256), 0, stream,
-                           static_cast<const uint8_t *>(ref), static_cast<const uint8_t *>(dis), w, h,
-                           bpc, s, tap, dec_w, dec_h, out_ref, out_dis, opitch);
+        hipLaunchKernelGGL(decimate_general<uint8_t>, grid, dim3(256), 0, stream, b, w, h, bpc, s, tap, dec_w,
+                           dec_h, opitch);
     else
-        hipLaunchKernelGGL(decimate_general<uint16_t>, grid, dim3(256), 0, stream,
-                           static_cast<const uint16_t *>(ref), static_cast<const uint16_t *>(dis), w,
-                           h, bpc, s, tap, dec_w, dec_h, out_ref, out_dis, opitch);
+        hipLaunchKernelGGL(decimate_general<uint16_t>, grid, dim3(256), 0, stream, b, w, h, bpc, s, tap, dec_w,
+                           dec_h, opitch);
     return hipGetLastError();
 }
 

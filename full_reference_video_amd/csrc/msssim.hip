@@ -3,8 +3,9 @@
 // "Research-1363: Device-resident ssimulacra2 and a single-wait MS-SSIM on
 // SYCL", Finding 6: every scale gets its own span of partial sums, so all
 // scales are enqueued at once and the host waits once per frame.  Here the
-// combine runs on the device too, so one 8-byte score (plus the 15 per-level
-// means) is the whole read-back.
+// spans are summed and combined on the device too (one finish workgroup per
+// frame, each span in index order), so one 8-byte score (plus the 15
+// per-level means) is the whole read-back.
 //
 // Level j of the pyramid is the full-resolution sample plane for j = 1 and the
 // exact 2x2 mean ((a + b) + (c + d)) * 0.25f of level j-1 after that.  Per
@@ -30,17 +31,21 @@ constexpr int kTW = 64, kTH = 16, kNT = 256;
 __constant__ double kBeta[5] = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333};
 
 template <int TW, int TH, int NT, typename TIn>
-__global__ __launch_bounds__(NT) void ms_level(const TIn *__restrict__ ref, const TIn *__restrict__ dis,
-                                               int pitch, int W, int H, float unit, Taps taps, int level,
-                                               MsLevelTarget t) {
+__global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int H, int next_pitch, float unit,
+                                               Taps taps) {
     constexpr int IW = TW + 10, IH = TH + 10;
     __shared__ float sx[IH * IW], sy[IH * IW];
     __shared__ float hmx[IH * TW], hmy[IH * TW], hxx[IH * TW], hyy[IH * TW], hxy[IH * TW];
     __shared__ double red[3][NT / 64];
-    __shared__ int is_last;
+
+    int bx, by, bz;
+    xcd_block(bx, by, bz);
+    const MsFrame &t = b.f[bz];
+    const TIn *ref = static_cast<const TIn *>(t.ref);
+    const TIn *dis = static_cast<const TIn *>(t.dis);
 
     const int MW = W - 10, MH = H - 10;
-    const int x0 = blockIdx.x * TW, y0 = blockIdx.y * TH;
+    const int x0 = bx * TW, y0 = by * TH;
 
     stage_tile<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
     __syncthreads();
@@ -49,21 +54,21 @@ __global__ __launch_bounds__(NT) void ms_level(const TIn *__restrict__ ref, cons
     // staged (offset) samples.  Every step is exact, so adding the offset
     // back gives the same bits as averaging the plain samples.
     if (t.next_ref != nullptr) {
-        const int xe = (blockIdx.x == gridDim.x - 1) ? W : x0 + TW;
-        const int ye = (blockIdx.y == gridDim.y - 1) ? H : y0 + TH;
+        const int xe = (bx == (int)gridDim.x - 1) ? W : x0 + TW;
+        const int ye = (by == (int)gridDim.y - 1) ? H : y0 + TH;
         const int nx0 = x0 / 2, ny0 = y0 / 2;
         const int nxe = min(xe / 2, W / 2), nye = min(ye / 2, H / 2);
         const int nw = nxe - nx0, nh = nye - ny0;
         for (int i = threadIdx.x; i < nw * nh; i += NT) {
             const int r = i / nw, c = i - r * nw;
             const int lr = 2 * r, lc = 2 * c;  // tile-local position of the block
-            const float a = sx[lr * IW + lc], b = sx[lr * IW + lc + 1];
-            const float cc = sx[(lr + 1) * IW + lc], d = sx[(lr + 1) * IW + lc + 1];
-            const float e = sy[lr * IW + lc], f = sy[lr * IW + lc + 1];
-            const float g = sy[(lr + 1) * IW + lc], hh = sy[(lr + 1) * IW + lc + 1];
-            const size_t o = (size_t)(ny0 + r) * (size_t)t.next_pitch + (size_t)(nx0 + c);
-            t.next_ref[o] = ((a + b) + (cc + d)) * 0.25f + kMomentOffset;
-            t.next_dis[o] = ((e + f) + (g + hh)) * 0.25f + kMomentOffset;
+            const float x00 = sx[lr * IW + lc], x01 = sx[lr * IW + lc + 1];
+            const float x10 = sx[(lr + 1) * IW + lc], x11 = sx[(lr + 1) * IW + lc + 1];
+            const float y00 = sy[lr * IW + lc], y01 = sy[lr * IW + lc + 1];
+            const float y10 = sy[(lr + 1) * IW + lc], y11 = sy[(lr + 1) * IW + lc + 1];
+            const size_t o = (size_t)(ny0 + r) * (size_t)next_pitch + (size_t)(nx0 + c);
+            t.next_ref[o] = ((x00 + x01) + (x10 + x11)) * 0.25f + kMomentOffset;
+            t.next_dis[o] = ((y00 + y01) + (y10 + y11)) * 0.25f + kMomentOffset;
         }
     }
 
@@ -94,40 +99,41 @@ __global__ __launch_bounds__(NT) void ms_level(const TIn *__restrict__ ref, cons
     }
 
     block_sum<NT, 3>(acc, red);
-    const int nb = gridDim.x * gridDim.y;
-    const int slot = blockIdx.y * gridDim.x + blockIdx.x;
-    if (!publish_and_elect<NT, 3>(acc, t.partials, nb, slot, t.ticket, &is_last)) return;
-
-    double tot[3];
-    finish_spans<NT, 3>(t.partials, nb, t.ticket, tot, red);
     if (threadIdx.x == 0) {
-        const double n = (double)MW * (double)MH;
-        const double L = tot[0] / n, C = tot[1] / n, S = tot[2] / n;
-        t.lcs_dev[level] = L;
-        t.lcs_dev[5 + level] = C;
-        t.lcs_dev[10 + level] = S;
-        if (level == 4) {
-            // Earlier levels' means were written by earlier launches on the
-            // same stream.
-            double lcs[15];
-            for (int j = 0; j < 15; ++j) lcs[j] = load_agent(t.lcs_dev + j);
-            lcs[4] = L;
-            lcs[9] = C;
-            lcs[14] = S;
-            double ms = pow(lcs[4], kBeta[4]);
-            for (int j = 0; j < 5; ++j) {
-                const double cj = lcs[5 + j], sj = lcs[10 + j];
-                if (!(cj > 0.0) || !(sj > 0.0)) {
-                    ms = __longlong_as_double(0x7ff8000000000000ll);
-                    break;
-                }
-                ms *= pow(cj, kBeta[j]) * pow(sj, kBeta[j]);
-            }
-            t.result[0] = ms;
-            for (int j = 0; j < 15; ++j) t.result[1 + j] = lcs[j];
-            __threadfence_system();
-        }
+        const int nb = gridDim.x * gridDim.y;
+        const int slot = by * gridDim.x + bx;
+        t.partials[slot] = acc[0];
+        t.partials[nb + slot] = acc[1];
+        t.partials[2 * nb + slot] = acc[2];
     }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void ms_finish(MsFinishBatch b, MsLevels lv) {
+    __shared__ double red[3][NT / 64];
+    const MsFinishFrame &fr = b.f[blockIdx.x];
+    double lcs[15];
+    for (int j = 0; j < 5; ++j) {
+        double tot[3];
+        sum_spans<NT, 3>(fr.partials + lv.offset[j], lv.nb[j], (size_t)lv.nb[j], tot, red);
+        __syncthreads();  // red[] is reused by the next level
+        lcs[j] = tot[0] / lv.count[j];
+        lcs[5 + j] = tot[1] / lv.count[j];
+        lcs[10 + j] = tot[2] / lv.count[j];
+    }
+    if (threadIdx.x != 0) return;
+    double ms = pow(lcs[4], kBeta[4]);
+    for (int j = 0; j < 5; ++j) {
+        const double cj = lcs[5 + j], sj = lcs[10 + j];
+        if (!(cj > 0.0) || !(sj > 0.0)) {
+            ms = __longlong_as_double(0x7ff8000000000000ll);
+            break;
+        }
+        ms *= pow(cj, kBeta[j]) * pow(sj, kBeta[j]);
+    }
+    fr.result[0] = ms;
+    for (int j = 0; j < 15; ++j) fr.result[1 + j] = lcs[j];
+    __threadfence_system();
 }
 
 }  // namespace
@@ -136,29 +142,32 @@ int ms_partials(int W, int H) {
     return ((W - 10 + kTW - 1) / kTW) * ((H - 10 + kTH - 1) / kTH);
 }
 
-hipError_t launch_ms_level(const void *ref, const void *dis, InKind kind, int pitch, int W, int H,
-                           float unit, const Taps &taps, int level, MsLevelTarget t,
-                           hipStream_t stream) {
-    const dim3 grid((W - 10 + kTW - 1) / kTW, (H - 10 + kTH - 1) / kTH);
+hipError_t launch_ms_level(const MsBatch &b, int n, InKind kind, int pitch, int W, int H, int next_pitch,
+                           float unit, const Taps &taps, hipStream_t stream) {
+    if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
+    const dim3 grid((W - 10 + kTW - 1) / kTW, (H - 10 + kTH - 1) / kTH, n);
     switch (kind) {
     case IN_F32:
-        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, float>), grid, dim3(kNT), 0, stream,
-                           static_cast<const float *>(ref), static_cast<const float *>(dis), pitch, W,
-                           H, unit, taps, level, t);
+        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, float>), grid, dim3(kNT), 0, stream, b, pitch, W, H, next_pitch,
+                           unit, taps);
         break;
     case IN_U8:
-        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, uint8_t>), grid, dim3(kNT), 0, stream,
-                           static_cast<const uint8_t *>(ref), static_cast<const uint8_t *>(dis), pitch,
-                           W, H, unit, taps, level, t);
+        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, uint8_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H,
+                           next_pitch, unit, taps);
         break;
     case IN_U16:
-        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, uint16_t>), grid, dim3(kNT), 0, stream,
-                           static_cast<const uint16_t *>(ref), static_cast<const uint16_t *>(dis),
-                           pitch, W, H, unit, taps, level, t);
+        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, uint16_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H,
+                           next_pitch, unit, taps);
         break;
     default:
         return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_ms_finish(const MsFinishBatch &b, int n, const MsLevels &lv, hipStream_t stream) {
+    if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(ms_finish<256>, dim3(n), dim3(256), 0, stream, b, lv);
     return hipGetLastError();
 }
 

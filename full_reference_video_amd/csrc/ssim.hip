@@ -15,9 +15,9 @@
 // writes five moment planes to LDS, and the vertical pass forms the moments
 // of each map pixel and its SSIM term in fp32 (with the mid-scale offset
 // removed first, so E[x^2] - mu^2 cancels less).  Each thread adds its map
-// pixels in fp64; the workgroup sum goes to a partials array, and the last
-// workgroup to arrive (an atomic ticket) sums the partials in index order
-// and writes the mean straight into the pinned host result slot.
+// pixels in fp64; the workgroup sum goes to a partials array, and a finish
+// kernel (one workgroup per frame) sums the partials in index order and
+// writes the mean straight into the pinned host result slot.
 #include "ssim_common.h"
 
 namespace vqm {
@@ -26,17 +26,20 @@ namespace {
 constexpr int kTW = 64, kTH = 8, kNT = 256;
 
 template <int TW, int TH, int NT, typename TIn>
-__global__ __launch_bounds__(NT) void ssim_map(const TIn *__restrict__ ref, const TIn *__restrict__ dis,
-                                               int pitch, int W, int H, float unit, Taps taps,
-                                               ReduceTarget rt) {
+__global__ __launch_bounds__(NT) void ssim_map(SsimBatch b, int pitch, int W, int H, float unit, Taps taps) {
     constexpr int IW = TW + 10, IH = TH + 10;
     __shared__ float sx[IH * IW], sy[IH * IW];
     __shared__ float hmx[IH * TW], hmy[IH * TW], hxx[IH * TW], hyy[IH * TW], hxy[IH * TW];
     __shared__ double red[1][NT / 64];
-    __shared__ int is_last;
+
+    int bx, by, bz;
+    xcd_block(bx, by, bz);
+    const SsimFrame &fr = b.f[bz];
+    const TIn *ref = static_cast<const TIn *>(fr.ref);
+    const TIn *dis = static_cast<const TIn *>(fr.dis);
 
     const int MW = W - 10, MH = H - 10;
-    const int x0 = blockIdx.x * TW, y0 = blockIdx.y * TH;
+    const int x0 = bx * TW, y0 = by * TH;
 
     stage_tile<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
     __syncthreads();
@@ -63,14 +66,19 @@ __global__ __launch_bounds__(NT) void ssim_map(const TIn *__restrict__ ref, cons
     }
 
     block_sum<NT, 1>(acc, red);
-    const int nb = gridDim.x * gridDim.y;
-    const int slot = blockIdx.y * gridDim.x + blockIdx.x;
-    if (!publish_and_elect<NT, 1>(acc, rt.partials, nb, slot, rt.ticket, &is_last)) return;
+    if (threadIdx.x == 0) fr.partials[by * gridDim.x + bx] = acc[0];
+}
 
+// One workgroup per frame: the fixed-tree sum of the frame's partials, the
+// mean, and its 8-byte write to the pinned host result slot.
+template <int NT>
+__global__ __launch_bounds__(NT) void ssim_finish(SsimBatch b, int nb, double count) {
+    __shared__ double red[1][NT / 64];
+    const SsimFrame &fr = b.f[blockIdx.x];
     double tot[1];
-    finish_spans<NT, 1>(rt.partials, nb, rt.ticket, tot, red);
+    sum_spans<NT, 1>(fr.partials, nb, 0, tot, red);
     if (threadIdx.x == 0) {
-        *rt.result = tot[0] / ((double)MW * (double)MH);
+        *fr.result = tot[0] / count;
         __threadfence_system();
     }
 }
@@ -81,28 +89,28 @@ int ssim_partials(int W, int H) {
     return ((W - 10 + kTW - 1) / kTW) * ((H - 10 + kTH - 1) / kTH);
 }
 
-hipError_t launch_ssim(const void *ref, const void *dis, InKind kind, int pitch, int W, int H,
-                       float unit, const Taps &taps, ReduceTarget rt, hipStream_t stream) {
-    const dim3 grid((W - 10 + kTW - 1) / kTW, (H - 10 + kTH - 1) / kTH);
+hipError_t launch_ssim(const SsimBatch &b, int n, InKind kind, int pitch, int W, int H, float unit,
+                       const Taps &taps, hipStream_t stream) {
+    if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
+    const dim3 grid((W - 10 + kTW - 1) / kTW, (H - 10 + kTH - 1) / kTH, n);
     switch (kind) {
     case IN_F32:
-        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, float>), grid, dim3(kNT), 0, stream,
-                           static_cast<const float *>(ref), static_cast<const float *>(dis), pitch, W,
-                           H, unit, taps, rt);
+        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, float>), grid, dim3(kNT), 0, stream, b, pitch, W, H, unit, taps);
         break;
     case IN_U8:
-        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, uint8_t>), grid, dim3(kNT), 0, stream,
-                           static_cast<const uint8_t *>(ref), static_cast<const uint8_t *>(dis), pitch,
-                           W, H, unit, taps, rt);
+        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, uint8_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H, unit, taps);
         break;
     case IN_U16:
-        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, uint16_t>), grid, dim3(kNT), 0, stream,
-                           static_cast<const uint16_t *>(ref), static_cast<const uint16_t *>(dis),
-                           pitch, W, H, unit, taps, rt);
+        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, uint16_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H, unit,
+                           taps);
         break;
     default:
         return hipErrorInvalidValue;
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const double count = (double)(W - 10) * (double)(H - 10);
+    hipLaunchKernelGGL(ssim_finish<256>, dim3(n), dim3(256), 0, stream, b, (int)(grid.x * grid.y), count);
     return hipGetLastError();
 }
 

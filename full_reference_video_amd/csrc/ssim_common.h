@@ -1,6 +1,15 @@
 // ssim_common.h — device helpers shared by the SSIM-map and MS-SSIM level
 // kernels (library-private): tile staging, the separable 11-tap moments, and
 // the fixed-shape reductions.
+//
+// The reduction has two launches: every map workgroup writes its own fixed-
+// tree partial to a partials array indexed by its tile, and a finish kernel
+// with one workgroup per frame sums the partials in index order ("Research-
+// 1363: Device-resident ssimulacra2 and a single-wait MS-SSIM on SYCL",
+// Finding 4: a work-group tree, then one group over the partials).  A
+// last-workgroup-arrives ticket would save the launch, but on gfx950 each
+// device-scope release/acquire around it writes back and invalidates the
+// XCD's L2, which costs several times the map itself.
 #pragma once
 
 #include "vqm_kernels.h"
@@ -30,14 +39,6 @@ __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;
-}
-
-// Coherent (device-scope) access to values other workgroups wrote.
-__device__ __forceinline__ double load_agent(const double *p) {
-    unsigned long long bits =
-        __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p), __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_AGENT);
-    return __longlong_as_double((long long)bits);
 }
 
 // Stage the (TH + 10) x (TW + 10) input tile of both planes at (x0, y0),
@@ -111,7 +112,8 @@ __device__ __forceinline__ void vertical_moments(const float *hmx, const float *
 }
 
 // Workgroup sum of NV doubles per thread in a fixed shape: wave butterflies,
-// then the waves in index order.  Valid in thread 0 only.
+// then the waves in index order.  Valid in thread 0 only.  `red` may be
+// reused after the next __syncthreads.
 template <int NT, int NV>
 __device__ __forceinline__ void block_sum(double (&v)[NV], double (*red)[NT / 64]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -131,39 +133,21 @@ __device__ __forceinline__ void block_sum(double (&v)[NV], double (*red)[NT / 64
     }
 }
 
-// Publish this workgroup's NV partial sums at `slot` of NV spans of `nb`
-// partials each, and tell whether this workgroup arrived last.  The ticket
-// is an acq_rel device-scope counter; the last arrival resets it to zero.
+// In a one-workgroup-per-frame finish kernel: sum each of NV spans of `nb`
+// partials (span j at partials + j * stride) in a fixed shape — thread t
+// takes partials t, t + NT, ... in index order, then block_sum.  The
+// partials were written by an earlier kernel on the same stream, so the
+// kernel boundary has made them visible.  Thread 0 holds the totals.
 template <int NT, int NV>
-__device__ __forceinline__ bool publish_and_elect(const double (&v)[NV], double *partials, int nb,
-                                                  int slot, unsigned *ticket, int *is_last) {
-    if (threadIdx.x == 0) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) partials[(size_t)j * nb + slot] = v[j];
-        __threadfence();
-        const unsigned prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        *is_last = (prev == (unsigned)(nb - 1));
-    }
-    __syncthreads();
-    return *is_last != 0;
-}
-
-// In the last workgroup: sum each span of nb partials in a fixed shape (each
-// thread a fixed strided subset in index order, then block_sum).  Thread 0
-// holds the totals and resets the ticket.
-template <int NT, int NV>
-__device__ __forceinline__ void finish_spans(const double *partials, int nb, unsigned *ticket,
-                                             double (&tot)[NV], double (*red)[NT / 64]) {
-    __threadfence();
+__device__ __forceinline__ void sum_spans(const double *partials, int nb, size_t stride, double (&tot)[NV],
+                                          double (*red)[NT / 64]) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         double t = 0.0;
-        for (int i = threadIdx.x; i < nb; i += NT) t += load_agent(partials + (size_t)j * nb + i);
+        for (int i = threadIdx.x; i < nb; i += NT) t += partials[(size_t)j * stride + i];
         tot[j] = t;
     }
-    __syncthreads();  // red[] is reused
     block_sum<NT, NV>(tot, red);
-    if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace vqm

@@ -2,12 +2,19 @@
 //
 // The runtime (vqm_runtime.cpp) validates every argument, sizes the scratch
 // and owns the streams; these launchers only compute grids and enqueue.
+//
+// Every launcher takes a batch of 1..kMaxBatch frames of the same geometry:
+// one launch processes all of them (blockIdx.z, after the XCD remap, picks
+// the frame).  A lone 2160p frame leaves a couple of microseconds of launch
+// ramp-up and drain per kernel that a batch of frames shares.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace vqm {
+
+constexpr int kMaxBatch = 8;
 
 // The 11 taps of the normalised Gaussian (sigma 1.5) in fp32.
 struct Taps {
@@ -24,54 +31,96 @@ constexpr float kMomentOffset = 128.0f;
 
 // ---------------------------------------------------------------- decimation
 
-// Whether the vectorised power-of-two decimation kernel handles this frame
-// (otherwise the general kernel runs; both are exact).
-bool decimate_fast_path(const void *ref, const void *dis, int w, int h, int bpc, int s);
+struct DecimateFrame {
+    const void *ref, *dis;       // raw planes, w x h, tightly packed
+    float *out_ref, *out_dis;    // dec_w x dec_h, row pitch opitch floats
+};
+struct DecimateBatch {
+    DecimateFrame f[kMaxBatch];
+};
 
-// Box low-pass and decimate both planes: out_* are dec_w x dec_h floats with
-// a row pitch of `opitch` floats.  `tap` = 1.0f/(s*s) formed by the caller.
-hipError_t launch_decimate(const void *ref, const void *dis, int w, int h, int bpc, int s,
-                           float tap, float *out_ref, float *out_dis, int dec_w, int dec_h,
-                           int opitch, hipStream_t stream);
+// Whether the vectorised power-of-two kernel handles these frames
+// (otherwise the general kernel runs; both compute the same exact sums).
+bool decimate_fast_path(const DecimateBatch &b, int n, int w, int h, int bpc, int s);
+
+// Box low-pass and decimate both planes of n frames.  `tap` = 1.0f/(s*s)
+// formed by the caller.
+hipError_t launch_decimate(const DecimateBatch &b, int n, int w, int h, int bpc, int s, float tap,
+                           int dec_w, int dec_h, int opitch, hipStream_t stream);
 
 // ---------------------------------------------------------------- SSIM map
 
-// Device-side state of one reduction: one partial per workgroup, a ticket
-// counter that is zero at rest, and where the final value goes.
-struct ReduceTarget {
-    double *partials;     // >= ssim_partials(...) doubles
-    unsigned *ticket;     // one counter, zero between launches
-    double *result;       // device-visible pointer to the score (pinned host)
+struct SsimFrame {
+    const void *ref, *dis;       // planes with row pitch `pitch` samples
+    double *partials;            // >= ssim_partials(W, H) doubles
+    double *result;              // device-visible address of the score (pinned host)
+};
+struct SsimBatch {
+    SsimFrame f[kMaxBatch];
 };
 
-// Number of partial sums the SSIM-map kernel writes for a W x H plane.
+// Number of partial sums the SSIM-map kernel writes per frame.
 int ssim_partials(int W, int H);
 
 // Fused 11x11 Gaussian moments + SSIM map + fixed-tree mean over the valid
-// (W-10) x (H-10) region of two planes with row pitch `pitch` samples.
-// Raw planes (IN_U8 / IN_U16) are scaled by `unit` = 2^-(bpc-8).
-hipError_t launch_ssim(const void *ref, const void *dis, InKind kind, int pitch, int W, int H,
-                       float unit, const Taps &taps, ReduceTarget rt, hipStream_t stream);
+// (W-10) x (H-10) region, for n frames: the map kernel (one partial per
+// workgroup) and the finish kernel (one workgroup per frame).  Raw planes
+// (IN_U8 / IN_U16) are scaled by `unit` = 2^-(bpc-8).
+hipError_t launch_ssim(const SsimBatch &b, int n, InKind kind, int pitch, int W, int H, float unit,
+                       const Taps &taps, hipStream_t stream);
 
 // ---------------------------------------------------------------- MS-SSIM
 
-struct MsLevelTarget {
-    double *partials;     // 3 * ms_partials(W, H) doubles (l, c, s spans)
-    unsigned *ticket;     // one counter per level, zero at rest
-    double *lcs_dev;      // 15 doubles: L1..L5, C1..C5, S1..S5 (device)
-    double *result;       // score + 15 means, device-visible pinned host (last level)
-    float *next_ref;      // floor(W/2) x floor(H/2) plane, pitch next_pitch; NULL at level 5
-    float *next_dis;
-    int next_pitch;
+struct MsFrame {
+    const void *ref, *dis;       // level planes with row pitch `pitch`
+    double *partials;            // this level's 3 spans (l, c, s) of ms_partials(W, H) doubles
+    float *next_ref, *next_dis;  // floor(W/2) x floor(H/2), pitch next_pitch; NULL at level 5
+};
+struct MsBatch {
+    MsFrame f[kMaxBatch];
 };
 
 int ms_partials(int W, int H);
 
-// One MS-SSIM level `level` (0..4): moments and l/c/s means of the valid
-// region, plus the exact 2x2 mean of the level into the next plane.  The
-// last level also combines the 15 means into the score.
-hipError_t launch_ms_level(const void *ref, const void *dis, InKind kind, int pitch, int W, int H,
-                           float unit, const Taps &taps, int level, MsLevelTarget t,
-                           hipStream_t stream);
+// One MS-SSIM level of n frames: moments and the l/c/s partial sums of the
+// valid region, plus the exact 2x2 mean of the level into the next plane.
+hipError_t launch_ms_level(const MsBatch &b, int n, InKind kind, int pitch, int W, int H, int next_pitch,
+                           float unit, const Taps &taps, hipStream_t stream);
+
+struct MsFinishFrame {
+    const double *partials;      // base of the frame's partials (all levels)
+    double *result;              // score + 15 means, device-visible pinned host
+};
+struct MsFinishBatch {
+    MsFinishFrame f[kMaxBatch];
+};
+// Where each level's spans sit in a frame's partials.
+struct MsLevels {
+    int nb[5];                   // partials per span
+    long long offset[5];         // first double of the level's 3 spans
+    double count[5];             // valid map pixels of the level
+};
+
+// One workgroup per frame: the 15 per-level means from the level spans in a
+// fixed tree, and the combined score.
+hipError_t launch_ms_finish(const MsFinishBatch &b, int n, const MsLevels &lv, hipStream_t stream);
+
+// ---------------------------------------------------------------- shared
+
+// XCD-aware block order.  The dispatcher hands consecutive workgroups of a
+// grid to the eight XCDs in turn; remapping the linear id so that each XCD
+// gets one contiguous range of logical blocks keeps neighbouring tiles (which
+// share halo lines) on the same XCD and its L2.
+__device__ __forceinline__ void xcd_block(int &bx, int &by, int &bz) {
+    const int nx = gridDim.x, ny = gridDim.y;
+    const int n = nx * ny * gridDim.z;
+    const int L = ((int)blockIdx.z * ny + (int)blockIdx.y) * nx + (int)blockIdx.x;
+    const int per = n / 8;
+    int Lp = L;
+    if (L < per * 8) Lp = (L % 8) * per + L / 8;
+    bx = Lp % nx;
+    by = (Lp / nx) % ny;
+    bz = Lp / (nx * ny);
+}
 
 }  // namespace vqm

@@ -26,6 +26,8 @@
 
 #include "vqm_kernels.h"
 
+static_assert(VQM_MAX_BATCH == vqm::kMaxBatch, "batch limits of the ABI and the kernels differ");
+
 namespace {
 
 thread_local std::string g_err;
@@ -156,8 +158,6 @@ struct Slot {
     size_t planes_bytes = 0;
     double *partials = nullptr;
     size_t partials_count = 0;
-    unsigned *tickets = nullptr;    // kLevels + 1 counters, zero at rest
-    double *lcs_dev = nullptr;      // 15 doubles
     double *result_host = nullptr;  // pinned: score + 15 means
     double *result_dev = nullptr;   // its device-visible address
     hipEvent_t done = nullptr;
@@ -172,8 +172,6 @@ struct Slot {
         if (staging) (void)hipHostFree(staging);
         if (planes) (void)hipFree(planes);
         if (partials) (void)hipFree(partials);
-        if (tickets) (void)hipFree(tickets);
-        if (lcs_dev) (void)hipFree(lcs_dev);
         if (result_host) (void)hipHostFree(result_host);
         if (done) (void)hipEventDestroy(done);
         *this = Slot();
@@ -183,6 +181,7 @@ struct Slot {
 struct TimedLaunch {
     hipEvent_t start, stop;
     int cls;
+    int frames;
 };
 
 }  // namespace
@@ -199,6 +198,7 @@ struct vqm_ctx {
     std::vector<hipEvent_t> event_pool;  // free timing events
     double time_ms[4] = {0, 0, 0, 0};
     int launches[4] = {0, 0, 0, 0};
+    int frames[4] = {0, 0, 0, 0};
 };
 
 namespace {
@@ -239,9 +239,6 @@ int prepare_slot(Slot &sl, const Geometry &g) {
     HIP_TRY_ALLOC(hipMalloc(&sl.planes, sl.planes_bytes));
     sl.partials_count = partials;
     HIP_TRY_ALLOC(hipMalloc(&sl.partials, partials * sizeof(double)));
-    HIP_TRY_ALLOC(hipMalloc(&sl.tickets, (kLevels + 1) * sizeof(unsigned)));
-    HIP_TRY(hipMemset(sl.tickets, 0, (kLevels + 1) * sizeof(unsigned)));
-    HIP_TRY_ALLOC(hipMalloc(&sl.lcs_dev, 15 * sizeof(double)));
     HIP_TRY_ALLOC(hipHostMalloc(&sl.result_host, 16 * sizeof(double), hipHostMallocMapped | hipHostMallocCoherent));
     HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void **>(&sl.result_dev), sl.result_host, 0));
     return 0;
@@ -300,7 +297,7 @@ int upload(vqm_ctx *ctx, Slot &sl, const void *ref, const void *dis, const void 
     char *din = static_cast<char *>(sl.dev_in);
     const void *src[2] = {ref, dis};
     const PtrKind kind[2] = {kr, kd};
-    const void *dst[2] = {din, din + pb};
+    void *dst[2] = {din, din + pb};
     if (kr == PTR_PAGEABLE || kd == PTR_PAGEABLE) {
         if (sl.staging_bytes < 2 * pb) {
             if (sl.staging) (void)hipHostFree(sl.staging);
@@ -318,13 +315,12 @@ int upload(vqm_ctx *ctx, Slot &sl, const void *ref, const void *dis, const void 
     } else {
         for (int i = 0; i < 2; ++i) {
             if (kind[i] == PTR_DEVICE) {
-                HIP_TRY(hipMemcpyAsync(const_cast<void *>(dst[i]), src[i], pb, hipMemcpyDeviceToDevice, ctx->stream));
+                HIP_TRY(hipMemcpyAsync(dst[i], src[i], pb, hipMemcpyDeviceToDevice, ctx->stream));
             } else if (kind[i] == PTR_PINNED) {
-                HIP_TRY(hipMemcpyAsync(const_cast<void *>(dst[i]), src[i], pb, hipMemcpyHostToDevice, ctx->stream));
+                HIP_TRY(hipMemcpyAsync(dst[i], src[i], pb, hipMemcpyHostToDevice, ctx->stream));
             } else {
                 memcpy(stg + i * pb, src[i], pb);
-                HIP_TRY(hipMemcpyAsync(const_cast<void *>(dst[i]), stg + i * pb, pb, hipMemcpyHostToDevice,
-                                       ctx->stream));
+                HIP_TRY(hipMemcpyAsync(dst[i], stg + i * pb, pb, hipMemcpyHostToDevice, ctx->stream));
             }
         }
     }
@@ -333,7 +329,7 @@ int upload(vqm_ctx *ctx, Slot &sl, const void *ref, const void *dis, const void 
     return 0;
 }
 
-int timing_begin(vqm_ctx *ctx, TimedLaunch *tl, int cls) {
+int timing_begin(vqm_ctx *ctx, TimedLaunch *tl, int cls, int frames) {
     if (!ctx->timing) return 0;
     for (int i = 0; i < 2; ++i) {
         hipEvent_t e;
@@ -346,6 +342,7 @@ int timing_begin(vqm_ctx *ctx, TimedLaunch *tl, int cls) {
         (i == 0 ? tl->start : tl->stop) = e;
     }
     tl->cls = cls;
+    tl->frames = frames;
     HIP_TRY(hipEventRecord(tl->start, ctx->stream));
     return 0;
 }
@@ -365,6 +362,7 @@ int drain_timing(vqm_ctx *ctx) {
         HIP_TRY(hipEventElapsedTime(&ms, t.start, t.stop));
         ctx->time_ms[t.cls] += ms;
         ctx->launches[t.cls] += 1;
+        ctx->frames[t.cls] += t.frames;
         ctx->event_pool.push_back(t.start);
         ctx->event_pool.push_back(t.stop);
     }
@@ -372,10 +370,10 @@ int drain_timing(vqm_ctx *ctx) {
     return 0;
 }
 
-#define LAUNCH_TIMED(ctx, cls, launch_expr)                                                        \
+#define LAUNCH_TIMED(ctx, cls, frames, launch_expr)                                                \
     do {                                                                                           \
         TimedLaunch tl_;                                                                           \
-        int rc_ = timing_begin(ctx, &tl_, cls);                                                    \
+        int rc_ = timing_begin(ctx, &tl_, cls, frames);                                            \
         if (rc_) return rc_;                                                                       \
         hipError_t e_ = (launch_expr);                                                             \
         if (e_ != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e_));       \
@@ -383,80 +381,129 @@ int drain_timing(vqm_ctx *ctx) {
         if (rc_) return rc_;                                                                       \
     } while (0)
 
-// float_ssim on device-readable planes into slot sl.  `decimate_only` stops
-// after the decimation (debug export).
-int enqueue_ssim(vqm_ctx *ctx, Slot &sl, const void *ref, const void *dis, bool decimate_only) {
-    const Geometry &g = sl.geo;
-    float *dref = sl.planes + sl.off_ref[0];
-    float *ddis = sl.planes + sl.off_dis[0];
+// float_ssim of n frames in slots sl[0..n-1] (same geometry) whose planes
+// are device-readable at in_r[i], in_d[i].  `decimate_only` stops after the
+// decimation (debug export).
+int enqueue_ssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r, const void *const *in_d,
+                 bool decimate_only) {
+    const Geometry &g = sl[0]->geo;
     const float unit = ldexpf(1.0f, -(g.bpc - 8));
-    const void *in_r = ref, *in_d = dis;
+    vqm::SsimBatch sb;
+    memset(&sb, 0, sizeof sb);
     vqm::InKind kind = g.bpc == 8 ? vqm::IN_U8 : vqm::IN_U16;
     int pitch = g.w;
     if (g.s > 1 || decimate_only) {
+        vqm::DecimateBatch db;
+        memset(&db, 0, sizeof db);
+        for (int i = 0; i < n; ++i) {
+            db.f[i].ref = in_r[i];
+            db.f[i].dis = in_d[i];
+            db.f[i].out_ref = sl[i]->planes + sl[i]->off_ref[0];
+            db.f[i].out_dis = sl[i]->planes + sl[i]->off_dis[0];
+        }
         const float tap = 1.0f / (float)(g.s * g.s);  // formed on the host
-        LAUNCH_TIMED(ctx, VQM_KERNEL_DECIMATE,
-                     vqm::launch_decimate(ref, dis, g.w, g.h, g.bpc, g.s, tap, dref, ddis, g.dw, g.dh,
-                                          g.dpitch, ctx->stream));
-        in_r = dref;
-        in_d = ddis;
+        LAUNCH_TIMED(ctx, VQM_KERNEL_DECIMATE, n,
+                     vqm::launch_decimate(db, n, g.w, g.h, g.bpc, g.s, tap, g.dw, g.dh, g.dpitch, ctx->stream));
+        for (int i = 0; i < n; ++i) {
+            sb.f[i].ref = db.f[i].out_ref;
+            sb.f[i].dis = db.f[i].out_dis;
+        }
         kind = vqm::IN_F32;
         pitch = g.dpitch;
+    } else {
+        for (int i = 0; i < n; ++i) {
+            sb.f[i].ref = in_r[i];
+            sb.f[i].dis = in_d[i];
+        }
     }
     if (decimate_only) return 0;
-    vqm::ReduceTarget rt{sl.partials, sl.tickets, sl.result_dev};
-    LAUNCH_TIMED(ctx, VQM_KERNEL_SSIM,
-                 vqm::launch_ssim(in_r, in_d, kind, pitch, g.dw, g.dh, unit, ctx->taps, rt, ctx->stream));
+    for (int i = 0; i < n; ++i) {
+        sb.f[i].partials = sl[i]->partials;
+        sb.f[i].result = sl[i]->result_dev;
+    }
+    LAUNCH_TIMED(ctx, VQM_KERNEL_SSIM, n,
+                 vqm::launch_ssim(sb, n, kind, pitch, g.dw, g.dh, unit, ctx->taps, ctx->stream));
     return 0;
 }
 
-int enqueue_msssim(vqm_ctx *ctx, Slot &sl, const void *ref, const void *dis) {
-    const Geometry &g = sl.geo;
+int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r, const void *const *in_d) {
+    const Geometry &g = sl[0]->geo;
     const float unit = ldexpf(1.0f, -(g.bpc - 8));
     for (int j = 0; j < kLevels; ++j) {
-        const void *in_r = j == 0 ? ref : static_cast<const void *>(sl.planes + sl.off_ref[j]);
-        const void *in_d = j == 0 ? dis : static_cast<const void *>(sl.planes + sl.off_dis[j]);
+        vqm::MsBatch mb;
+        memset(&mb, 0, sizeof mb);
+        for (int i = 0; i < n; ++i) {
+            Slot &s = *sl[i];
+            vqm::MsFrame &f = mb.f[i];
+            f.ref = j == 0 ? in_r[i] : static_cast<const void *>(s.planes + s.off_ref[j]);
+            f.dis = j == 0 ? in_d[i] : static_cast<const void *>(s.planes + s.off_dis[j]);
+            f.partials = s.partials + s.span[j];
+            f.next_ref = j + 1 < kLevels ? s.planes + s.off_ref[j + 1] : nullptr;
+            f.next_dis = j + 1 < kLevels ? s.planes + s.off_dis[j + 1] : nullptr;
+        }
         const vqm::InKind kind = j == 0 ? (g.bpc == 8 ? vqm::IN_U8 : vqm::IN_U16) : vqm::IN_F32;
-        vqm::MsLevelTarget t;
-        t.partials = sl.partials + sl.span[j];
-        t.ticket = sl.tickets + j;
-        t.lcs_dev = sl.lcs_dev;
-        t.result = sl.result_dev;
-        t.next_ref = j + 1 < kLevels ? sl.planes + sl.off_ref[j + 1] : nullptr;
-        t.next_dis = j + 1 < kLevels ? sl.planes + sl.off_dis[j + 1] : nullptr;
-        t.next_pitch = j + 1 < kLevels ? g.lpitch[j + 1] : 0;
-        LAUNCH_TIMED(ctx, j == 0 ? VQM_KERNEL_MSSSIM_LEVEL1 : VQM_KERNEL_MSSSIM_COARSE,
-                     vqm::launch_ms_level(in_r, in_d, kind, g.lpitch[j], g.lw[j], g.lh[j],
-                                          j == 0 ? unit : 1.0f, ctx->taps, j, t, ctx->stream));
+        const int next_pitch = j + 1 < kLevels ? g.lpitch[j + 1] : 0;
+        LAUNCH_TIMED(ctx, j == 0 ? VQM_KERNEL_MSSSIM_LEVEL1 : VQM_KERNEL_MSSSIM_COARSE, n,
+                     vqm::launch_ms_level(mb, n, kind, g.lpitch[j], g.lw[j], g.lh[j], next_pitch,
+                                          j == 0 ? unit : 1.0f, ctx->taps, ctx->stream));
     }
+    vqm::MsFinishBatch fb;
+    memset(&fb, 0, sizeof fb);
+    for (int i = 0; i < n; ++i) {
+        fb.f[i].partials = sl[i]->partials;
+        fb.f[i].result = sl[i]->result_dev;
+    }
+    vqm::MsLevels lv;
+    for (int j = 0; j < kLevels; ++j) {
+        lv.nb[j] = vqm::ms_partials(g.lw[j], g.lh[j]);
+        lv.offset[j] = (long long)sl[0]->span[j];
+        lv.count[j] = (double)(g.lw[j] - 10) * (double)(g.lh[j] - 10);
+    }
+    const hipError_t e = vqm::launch_ms_finish(fb, n, lv, ctx->stream);
+    if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
     return 0;
 }
 
-int submit(vqm_ctx *ctx, int kind, const void *ref, const void *dis, int w, int h, int bpc) {
+int gate(int kind, int w, int h, int bpc) {
+    return kind == KIND_SSIM ? gate_ssim(w, h, bpc, nullptr, nullptr, nullptr) : gate_msssim(w, h);
+}
+
+// Enqueue n frames of one geometry as one batch: every frame gets the next
+// free slot, its own upload, result and completion event; the kernels
+// process the whole batch per launch.
+int submit(vqm_ctx *ctx, int kind, const void *const *refs, const void *const *diss, int n, int w, int h,
+           int bpc) {
     if (!ctx) return fail(-EINVAL, "NULL context");
-    int rc = check_args(ref, dis, w, h, bpc);
-    if (rc) return rc;
-    if (kind == KIND_SSIM) {
-        rc = gate_ssim(w, h, bpc, nullptr, nullptr, nullptr);
-    } else {
-        rc = gate_msssim(w, h);
+    if (!refs || !diss) return fail(-EINVAL, "NULL plane array");
+    if (n < 1 || n > VQM_MAX_BATCH) return fail(-EINVAL, "batch of %d frames outside 1..%d", n, VQM_MAX_BATCH);
+    for (int i = 0; i < n; ++i) {
+        int rc = check_args(refs[i], diss[i], w, h, bpc);
+        if (rc) return rc;
     }
+    int rc = gate(kind, w, h, bpc);
     if (rc) return rc;
-    if (ctx->count >= VQM_MAX_IN_FLIGHT) return fail(-EAGAIN, "%d frames already in flight", ctx->count);
+    if (ctx->count + n > VQM_MAX_IN_FLIGHT)
+        return fail(-EAGAIN, "%d frames in flight, %d more would exceed %d", ctx->count, n, VQM_MAX_IN_FLIGHT);
     rc = ensure_device(ctx);
     if (rc) return rc;
-    Slot &sl = ctx->slots[(ctx->head + ctx->count) % VQM_MAX_IN_FLIGHT];
-    rc = prepare_slot(sl, make_geometry(kind, w, h, bpc));
+    const Geometry geo = make_geometry(kind, w, h, bpc);
+    Slot *sl[VQM_MAX_BATCH];
+    const void *in_r[VQM_MAX_BATCH], *in_d[VQM_MAX_BATCH];
+    for (int i = 0; i < n; ++i) {
+        sl[i] = &ctx->slots[(ctx->head + ctx->count + i) % VQM_MAX_IN_FLIGHT];
+        rc = prepare_slot(*sl[i], geo);
+        if (rc) return rc;
+        for (int k = 0; k < 16; ++k) sl[i]->result_host[k] = NAN;
+        rc = upload(ctx, *sl[i], refs[i], diss[i], &in_r[i], &in_d[i]);
+        if (rc) return rc;
+    }
+    rc = kind == KIND_SSIM ? enqueue_ssim(ctx, sl, n, in_r, in_d, false) : enqueue_msssim(ctx, sl, n, in_r, in_d);
     if (rc) return rc;
-    for (int i = 0; i < 16; ++i) sl.result_host[i] = NAN;
-    const void *dref = nullptr, *ddis = nullptr;
-    rc = upload(ctx, sl, ref, dis, &dref, &ddis);
-    if (rc) return rc;
-    rc = kind == KIND_SSIM ? enqueue_ssim(ctx, sl, dref, ddis, false) : enqueue_msssim(ctx, sl, dref, ddis);
-    if (rc) return rc;
-    HIP_TRY(hipEventRecord(sl.done, ctx->stream));
-    sl.kind = kind;
-    ctx->count += 1;
+    for (int i = 0; i < n; ++i) {
+        HIP_TRY(hipEventRecord(sl[i]->done, ctx->stream));
+        sl[i]->kind = kind;
+    }
+    ctx->count += n;
     return 0;
 }
 
@@ -552,13 +599,13 @@ int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, 
     if (!score) return fail(-EINVAL, "NULL score pointer");
     int rc = check_args(ref, dis, w, h, bpc);
     if (rc) return rc;
-    rc = kind == KIND_SSIM ? gate_ssim(w, h, bpc, nullptr, nullptr, nullptr) : gate_msssim(w, h);
+    rc = gate(kind, w, h, bpc);
     if (rc) return rc;
     vqm_ctx *ctx = nullptr;
     rc = implicit_ctx(&ctx);
     if (rc) return rc;
     // The implicit context never holds frames between calls.
-    rc = submit(ctx, kind, ref, dis, w, h, bpc);
+    rc = submit(ctx, kind, &ref, &dis, 1, w, h, bpc);
     if (rc) return rc;
     double s = 0.0;
     double l[15];
@@ -566,6 +613,22 @@ int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, 
     if (rc) return rc;
     *score = s;
     if (lcs) memcpy(lcs, l, sizeof l);
+    return 0;
+}
+
+// One frame into the next free slot for the debug exports (synchronous; the
+// slot is not counted as in flight).
+int debug_slot(vqm_ctx *ctx, const Geometry &g, const void *ref, const void *dis, Slot **sl_out,
+               const void **dref, const void **ddis) {
+    if (ctx->count >= VQM_MAX_IN_FLIGHT) return fail(-EAGAIN, "%d frames already in flight", ctx->count);
+    int rc = ensure_device(ctx);
+    if (rc) return rc;
+    Slot &sl = ctx->slots[(ctx->head + ctx->count) % VQM_MAX_IN_FLIGHT];
+    rc = prepare_slot(sl, g);
+    if (rc) return rc;
+    rc = upload(ctx, sl, ref, dis, dref, ddis);
+    if (rc) return rc;
+    *sl_out = &sl;
     return 0;
 }
 
@@ -603,11 +666,21 @@ int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out) { return create(
 void vqm_ctx_destroy(vqm_ctx *ctx) { destroy(ctx); }
 
 int vqm_ssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc) {
-    return submit(ctx, KIND_SSIM, ref, dis, w, h, bpc);
+    return submit(ctx, KIND_SSIM, &ref, &dis, 1, w, h, bpc);
 }
 
 int vqm_msssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc) {
-    return submit(ctx, KIND_MSSSIM, ref, dis, w, h, bpc);
+    return submit(ctx, KIND_MSSSIM, &ref, &dis, 1, w, h, bpc);
+}
+
+int vqm_ssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n, int w, int h,
+                          int bpc) {
+    return submit(ctx, KIND_SSIM, refs, dis, n, w, h, bpc);
+}
+
+int vqm_msssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n, int w, int h,
+                            int bpc) {
+    return submit(ctx, KIND_MSSSIM, refs, dis, n, w, h, bpc);
 }
 
 int vqm_collect(vqm_ctx *ctx, double *score, double *lcs) { return collect(ctx, score, lcs); }
@@ -623,12 +696,13 @@ int vqm_ctx_set_timing(vqm_ctx *ctx, int enable) {
     for (int i = 0; i < 4; ++i) {
         ctx->time_ms[i] = 0.0;
         ctx->launches[i] = 0;
+        ctx->frames[i] = 0;
     }
     ctx->timing = enable != 0;
     return 0;
 }
 
-int vqm_ctx_kernel_time(vqm_ctx *ctx, int kernel_class, double *total_ms, int *launches) {
+int vqm_ctx_kernel_time(vqm_ctx *ctx, int kernel_class, double *total_ms, int *launches, int *frames) {
     if (!ctx) return fail(-EINVAL, "NULL context");
     if (kernel_class < 0 || kernel_class > 3) return fail(-EINVAL, "kernel class %d", kernel_class);
     int rc = ensure_device(ctx);
@@ -637,6 +711,7 @@ int vqm_ctx_kernel_time(vqm_ctx *ctx, int kernel_class, double *total_ms, int *l
     if (rc) return rc;
     if (total_ms) *total_ms = ctx->time_ms[kernel_class];
     if (launches) *launches = ctx->launches[kernel_class];
+    if (frames) *frames = ctx->frames[kernel_class];
     return 0;
 }
 
@@ -651,10 +726,6 @@ int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, in
     } else if (scale < 1 || scale > 128) {
         return fail(-EINVAL, "scale %d outside 1..128", scale);
     }
-    if (ctx->count >= VQM_MAX_IN_FLIGHT) return fail(-EAGAIN, "%d frames already in flight", ctx->count);
-    rc = ensure_device(ctx);
-    if (rc) return rc;
-    Slot &sl = ctx->slots[(ctx->head + ctx->count) % VQM_MAX_IN_FLIGHT];
     Geometry g = make_geometry(KIND_SSIM, w, h, bpc);
     if (scale != 0 && scale != g.s) {
         // A forced scale is part of the slot's geometry key, so the next
@@ -664,16 +735,15 @@ int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, in
         g.dh = (h + scale - 1) / scale;
         g.dpitch = round_up(g.dw, 64);
     }
-    rc = prepare_slot(sl, g);
-    if (rc) return rc;
+    Slot *sl = nullptr;
     const void *dref = nullptr, *ddis = nullptr;
-    rc = upload(ctx, sl, ref, dis, &dref, &ddis);
+    rc = debug_slot(ctx, g, ref, dis, &sl, &dref, &ddis);
     if (rc) return rc;
-    rc = enqueue_ssim(ctx, sl, dref, ddis, true);
+    rc = enqueue_ssim(ctx, &sl, 1, &dref, &ddis, true);
     if (rc) return rc;
-    HIP_TRY(hipMemcpy2DAsync(out_ref, g.dw * sizeof(float), sl.planes + sl.off_ref[0], g.dpitch * sizeof(float),
+    HIP_TRY(hipMemcpy2DAsync(out_ref, g.dw * sizeof(float), sl->planes + sl->off_ref[0], g.dpitch * sizeof(float),
                              g.dw * sizeof(float), g.dh, hipMemcpyDeviceToHost, ctx->stream));
-    HIP_TRY(hipMemcpy2DAsync(out_dis, g.dw * sizeof(float), sl.planes + sl.off_dis[0], g.dpitch * sizeof(float),
+    HIP_TRY(hipMemcpy2DAsync(out_dis, g.dw * sizeof(float), sl->planes + sl->off_dis[0], g.dpitch * sizeof(float),
                              g.dw * sizeof(float), g.dh, hipMemcpyDeviceToHost, ctx->stream));
     HIP_TRY(hipStreamSynchronize(ctx->stream));
     return 0;
@@ -687,23 +757,20 @@ int vqm_debug_pyramid(vqm_ctx *ctx, const void *ref, const void *dis, int w, int
     if (rc) return rc;
     rc = gate_msssim(w, h);
     if (rc) return rc;
-    if (ctx->count >= VQM_MAX_IN_FLIGHT) return fail(-EAGAIN, "%d frames already in flight", ctx->count);
-    rc = ensure_device(ctx);
-    if (rc) return rc;
-    Slot &sl = ctx->slots[(ctx->head + ctx->count) % VQM_MAX_IN_FLIGHT];
-    rc = prepare_slot(sl, make_geometry(KIND_MSSSIM, w, h, bpc));
-    if (rc) return rc;
+    const Geometry g = make_geometry(KIND_MSSSIM, w, h, bpc);
+    Slot *sl = nullptr;
     const void *dref = nullptr, *ddis = nullptr;
-    rc = upload(ctx, sl, ref, dis, &dref, &ddis);
+    rc = debug_slot(ctx, g, ref, dis, &sl, &dref, &ddis);
     if (rc) return rc;
-    rc = enqueue_msssim(ctx, sl, dref, ddis);
+    rc = enqueue_msssim(ctx, &sl, 1, &dref, &ddis);
     if (rc) return rc;
-    const Geometry &g = sl.geo;
     const int j = level - 1;
-    HIP_TRY(hipMemcpy2DAsync(out_ref, g.lw[j] * sizeof(float), sl.planes + sl.off_ref[j], g.lpitch[j] * sizeof(float),
-                             g.lw[j] * sizeof(float), g.lh[j], hipMemcpyDeviceToHost, ctx->stream));
-    HIP_TRY(hipMemcpy2DAsync(out_dis, g.lw[j] * sizeof(float), sl.planes + sl.off_dis[j], g.lpitch[j] * sizeof(float),
-                             g.lw[j] * sizeof(float), g.lh[j], hipMemcpyDeviceToHost, ctx->stream));
+    HIP_TRY(hipMemcpy2DAsync(out_ref, g.lw[j] * sizeof(float), sl->planes + sl->off_ref[j],
+                             g.lpitch[j] * sizeof(float), g.lw[j] * sizeof(float), g.lh[j], hipMemcpyDeviceToHost,
+                             ctx->stream));
+    HIP_TRY(hipMemcpy2DAsync(out_dis, g.lw[j] * sizeof(float), sl->planes + sl->off_dis[j],
+                             g.lpitch[j] * sizeof(float), g.lw[j] * sizeof(float), g.lh[j], hipMemcpyDeviceToHost,
+                             ctx->stream));
     HIP_TRY(hipStreamSynchronize(ctx->stream));
     return 0;
 }

@@ -21,7 +21,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvqm.so")
 
-VQM_MAX_IN_FLIGHT = 4
+VQM_MAX_IN_FLIGHT = 16
+VQM_MAX_BATCH = 8
 VQM_MSSSIM_LCS = 15
 VQM_KERNEL_DECIMATE = 0
 VQM_KERNEL_SSIM = 1
@@ -62,10 +63,13 @@ def lib() -> ctypes.CDLL:
         L.vqm_ctx_destroy.restype = None
         for n in ("vqm_ssim_submit", "vqm_msssim_submit"):
             getattr(L, n).argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int]
+        for n in ("vqm_ssim_submit_batch", "vqm_msssim_submit_batch"):
+            getattr(L, n).argtypes = [c_void_p, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int,
+                                      c_int, c_int, c_int]
         L.vqm_collect.argtypes = [c_void_p, c_double_p, c_double_p]
         L.vqm_in_flight.argtypes = [c_void_p]
         L.vqm_ctx_set_timing.argtypes = [c_void_p, c_int]
-        L.vqm_ctx_kernel_time.argtypes = [c_void_p, c_int, c_double_p, c_int_p]
+        L.vqm_ctx_kernel_time.argtypes = [c_void_p, c_int, c_double_p, c_int_p, c_int_p]
         L.vqm_debug_decimate.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                          c_void_p, c_void_p]
         L.vqm_debug_pyramid.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
@@ -203,6 +207,33 @@ class Context:
         _check(lib().vqm_msssim_submit(self._h, pr, pd, w, h, int(bpc)), "vqm_msssim_submit")
         self._inflight.append(keep)
 
+    def _batch(self, fn, name, refs, diss, bpc):
+        if len(refs) != len(diss):
+            raise ValueError("refs and dis differ in length")
+        n = len(refs)
+        if not 1 <= n <= VQM_MAX_BATCH:
+            raise ValueError(f"batch of {n} frames outside 1..{VQM_MAX_BATCH}")
+        pr = (ctypes.c_void_p * n)()
+        pd = (ctypes.c_void_p * n)()
+        keep = []
+        w = h = None
+        for i, (r, d) in enumerate(zip(refs, diss)):
+            a, b, fw, fh, k = _pair(r, d, bpc)
+            if w is None:
+                w, h = fw, fh
+            elif (fw, fh) != (w, h):
+                raise ValueError("frames of one batch must share their size")
+            pr[i], pd[i] = a, b
+            keep.append(k)
+        _check(fn(self._h, pr, pd, n, w, h, int(bpc)), name)
+        self._inflight.extend(keep)
+
+    def vqm_ssim_submit_batch(self, refs, diss, bpc: int):
+        self._batch(lib().vqm_ssim_submit_batch, "vqm_ssim_submit_batch", refs, diss, bpc)
+
+    def vqm_msssim_submit_batch(self, refs, diss, bpc: int):
+        self._batch(lib().vqm_msssim_submit_batch, "vqm_msssim_submit_batch", refs, diss, bpc)
+
     def vqm_collect(self, want_lcs: bool = False):
         score = ctypes.c_double()
         lcs = np.full(VQM_MSSSIM_LCS, np.nan)
@@ -219,10 +250,11 @@ class Context:
         _check(lib().vqm_ctx_set_timing(self._h, 1 if enable else 0), "vqm_ctx_set_timing")
 
     def vqm_ctx_kernel_time(self, kernel_class: int):
-        ms, n = ctypes.c_double(), ctypes.c_int()
-        _check(lib().vqm_ctx_kernel_time(self._h, int(kernel_class), ctypes.byref(ms), ctypes.byref(n)),
-               "vqm_ctx_kernel_time")
-        return ms.value, n.value
+        """(total_ms, launches, frames) of one kernel class since timing was switched on."""
+        ms, n, f = ctypes.c_double(), ctypes.c_int(), ctypes.c_int()
+        _check(lib().vqm_ctx_kernel_time(self._h, int(kernel_class), ctypes.byref(ms), ctypes.byref(n),
+                                         ctypes.byref(f)), "vqm_ctx_kernel_time")
+        return ms.value, n.value, f.value
 
     def vqm_debug_decimate(self, ref, dis, bpc: int, scale: int = 0):
         pr, pd, w, h, _ = _pair(ref, dis, bpc)

@@ -76,7 +76,10 @@ extern "C" {
 #endif
 
 /* Frames a context holds in flight between submit and collect. */
-#define VQM_MAX_IN_FLIGHT 4
+#define VQM_MAX_IN_FLIGHT 16
+
+/* Frames one batched submit may hand over (processed per kernel launch). */
+#define VQM_MAX_BATCH 8
 
 /* Number of per-level means vqm_msssim_frame_lcs returns: L_1..L_5,
  * C_1..C_5, S_1..S_5 ([R-1363] Finding 6, enable_lcs). */
@@ -133,6 +136,19 @@ VQM_API int vqm_ssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int 
 /* Enqueue one MS-SSIM frame (all five levels and the combine). */
 VQM_API int vqm_msssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc);
 
+/* Enqueue n (1..VQM_MAX_BATCH) frames of the same size and depth as one
+ * batch: refs[i], dis[i] are frame i's planes (each pointer of any kind
+ * above).  Every kernel of the path runs once for the whole batch, which
+ * shares each launch's ramp-up and drain among n frames (at 2160p a lone
+ * frame's decimation spends a fifth of its time there).  Each frame still
+ * has its own upload, result slot and completion: collect them one by one,
+ * in submission order, one wait each.  Needs n free in-flight slots
+ * (-EAGAIN otherwise); nothing is enqueued on error. */
+VQM_API int vqm_ssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n,
+                                  int w, int h, int bpc);
+VQM_API int vqm_msssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n,
+                                    int w, int h, int bpc);
+
 /* Wait for the oldest frame in flight (the one device wait of that frame)
  * and return its score.  lcs (may be NULL) receives the 15 per-level means
  * when the frame was an MS-SSIM frame; for a float_ssim frame it is left
@@ -157,9 +173,11 @@ enum vqm_kernel_class {
     VQM_KERNEL_MSSSIM_COARSE = 3
 };
 
-/* Total milliseconds and launch count of one kernel class since timing was
- * switched on.  Waits for the context's stream.  Either output may be NULL. */
-VQM_API int vqm_ctx_kernel_time(vqm_ctx *ctx, int kernel_class, double *total_ms, int *launches);
+/* Total milliseconds, launch count and frames processed by one kernel class
+ * since timing was switched on (a batched launch counts once and processes
+ * several frames).  Waits for the context's stream.  Any output may be NULL. */
+VQM_API int vqm_ctx_kernel_time(vqm_ctx *ctx, int kernel_class, double *total_ms, int *launches,
+                                int *frames);
 
 /* Decimate one frame pair on the device with the float_ssim decimation
  * kernels and copy the two fp32 planes back (ceil(w/scale) x ceil(h/scale)

@@ -197,17 +197,18 @@ def test_ssim_geometry_changes_between_frames(ctx):
 
 
 def test_pipelined_submit_collect_and_flow_control(ctx):
-    src = synth.FrameSource(3)
-    pairs = [src.pair(t) for t in range(6)]
+    src = synth.FrameSource(3, w=640, h=400)
+    n = vqm.VQM_MAX_IN_FLIGHT + 2
+    pairs = [src.pair(t) for t in range(n)]
     say("ssim pipelined")
     want = [vqm.vqm_ssim_frame(r, d, 8) for (r, d) in pairs]
     for r, d in pairs[:vqm.VQM_MAX_IN_FLIGHT]:
         ctx.vqm_ssim_submit(r, d, 8)
     with pytest.raises(vqm.VqmError) as e:
-        ctx.vqm_ssim_submit(*pairs[4], 8)
+        ctx.vqm_ssim_submit(*pairs[vqm.VQM_MAX_IN_FLIGHT], 8)
     assert e.value.rc == -errno.EAGAIN
     got = [ctx.vqm_collect()]
-    for r, d in pairs[4:]:
+    for r, d in pairs[vqm.VQM_MAX_IN_FLIGHT:]:
         ctx.vqm_ssim_submit(r, d, 8)
         got.append(ctx.vqm_collect())
     while ctx.vqm_in_flight():
@@ -216,6 +217,46 @@ def test_pipelined_submit_collect_and_flow_control(ctx):
     with pytest.raises(vqm.VqmError) as e:
         ctx.vqm_collect()
     assert e.value.rc == -errno.EAGAIN
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4])
+def test_batched_submit_equals_single_frames(torch_cuda, ctx, c):
+    torch = torch_cuda
+    src = synth.FrameSource(c)
+    n = 11  # the generator draws any frame index, whatever the workload's count
+    pairs = [src.pair(t) for t in range(n)]
+    say(f"ssim batches config {c}")
+    single = [vqm.vqm_ssim_frame(r, d, src.bpc) for r, d in pairs]
+    # device-resident frames in batches of 1..8 (a ragged last batch)
+    dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
+    for b in (1, 3, 8):
+        got = []
+        for i in range(0, n, b):
+            chunk = dev[i:i + b]
+            ctx.vqm_ssim_submit_batch([r for r, _ in chunk], [d for _, d in chunk], src.bpc)
+            got += [ctx.vqm_collect() for _ in chunk]
+        assert got == single, b
+    # host frames, mixed with device frames, in one batch
+    mixed_r = [pairs[0][0], dev[1][0], pairs[2][0]]
+    mixed_d = [dev[0][1], pairs[1][1], pairs[2][1]]
+    ctx.vqm_ssim_submit_batch(mixed_r, mixed_d, src.bpc)
+    assert [ctx.vqm_collect() for _ in range(3)] == single[:3]
+    for t in (0, n - 1):
+        assert abs(single[t] - oracle.ssim(*pairs[t], src.bpc)) <= TOL
+
+
+def test_batch_limits(ctx):
+    src = synth.FrameSource(1)
+    r, d = src.pair(0)
+    with pytest.raises(ValueError):
+        ctx.vqm_ssim_submit_batch([r] * (vqm.VQM_MAX_BATCH + 1), [d] * (vqm.VQM_MAX_BATCH + 1), 8)
+    for _ in range(vqm.VQM_MAX_IN_FLIGHT // vqm.VQM_MAX_BATCH):
+        ctx.vqm_ssim_submit_batch([r] * vqm.VQM_MAX_BATCH, [d] * vqm.VQM_MAX_BATCH, 8)
+    with pytest.raises(vqm.VqmError) as e:
+        ctx.vqm_ssim_submit_batch([r], [d], 8)
+    assert e.value.rc == -errno.EAGAIN
+    vals = [ctx.vqm_collect() for _ in range(vqm.VQM_MAX_IN_FLIGHT)]
+    assert len(set(vals)) == 1
 
 
 def test_gate_on_gpu(ctx):
@@ -284,3 +325,16 @@ def test_msssim_repeatable(ctx):
     for _ in range(3):
         ctx.vqm_msssim_submit(ref, dis, 8)
     assert [ctx.vqm_collect() for _ in range(3)] == [a] * 3
+
+
+def test_msssim_batched_equals_single(ctx):
+    src = synth.FrameSource(5, w=960, h=544)
+    pairs = [src.pair(t) for t in range(5)]
+    say("msssim batch")
+    single = [vqm.vqm_msssim_frame_lcs(r, d, 8) for r, d in pairs]
+    ctx.vqm_msssim_submit_batch([r for r, _ in pairs], [d for _, d in pairs], 8)
+    for s1, l1 in single:
+        s2, l2 = ctx.vqm_collect(want_lcs=True)
+        assert s2 == s1
+        assert np.array_equal(l1, l2)
+    assert abs(single[2][0] - oracle.msssim(*pairs[2], 8)) <= TOL
