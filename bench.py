@@ -46,28 +46,12 @@ def algorithmic_bytes(wl, s: int) -> int:
     return 2 * covered_extent(wl.w, s) * covered_extent(wl.h, s) * bps
 
 
-def run_pass(ctxs, frames, metric, bpc, batch, lag):
-    """Submit every frame once in batches of `batch`, rotating over the
-    contexts, and collect each frame (one wait each) once more than `lag`
-    frames are in flight; return the scores in frame order."""
-    import collections
-    pending = collections.deque()
-    scores = []
-    for k, f0 in enumerate(range(0, len(frames), batch)):
-        c = ctxs[k % len(ctxs)]
-        chunk = frames[f0:f0 + batch]
-        refs = [r for r, _ in chunk]
-        diss = [d for _, d in chunk]
-        if metric == "ms_ssim":
-            c.vqm_msssim_submit_batch(refs, diss, bpc)
-        else:
-            c.vqm_ssim_submit_batch(refs, diss, bpc)
-        pending.extend([c] * len(chunk))
-        while len(pending) > lag:
-            scores.append(pending.popleft().vqm_collect())
-    while pending:
-        scores.append(pending.popleft().vqm_collect())
-    return scores
+def run_pass(ctxs, frameset, metric, batch, lag):
+    """One step: every frame of the workload scored once through the C ABI's
+    pipelined loop (batches rotate over the contexts; one wait per frame)."""
+    from full_reference_video_amd import vqm
+    m = vqm.VQM_METRIC_MS_SSIM if metric == "ms_ssim" else vqm.VQM_METRIC_FLOAT_SSIM
+    return vqm.vqm_score_frames(ctxs, m, frameset, batch, lag).tolist()
 
 
 def cpu_baseline(host, wl, budget_s: float):
@@ -95,8 +79,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="workload number 1..5")
-    ap.add_argument("--streams", type=int, default=1, help="contexts/streams batches rotate over")
-    ap.add_argument("--batch", type=int, default=4, help="frames per submit (and per kernel launch)")
+    ap.add_argument("--streams", type=int, default=2, help="contexts/streams batches rotate over")
+    ap.add_argument("--batch", type=int, default=8, help="frames per submit (and per kernel launch)")
     ap.add_argument("--lag", type=int, default=0,
                     help="frames in flight before a collect (0: 2*batch, capped by the in-flight slots)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0: skip)")
@@ -130,14 +114,13 @@ def main():
 
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
     ctxs = [vqm.Context(0, st) for st in streams]
-    lag = args.lag if args.lag > 0 else min(2 * args.batch, args.streams * vqm.VQM_MAX_IN_FLIGHT - args.batch)
-    if lag + args.batch > args.streams * vqm.VQM_MAX_IN_FLIGHT:
-        raise SystemExit(f"lag {lag} + batch {args.batch} exceeds the in-flight slots")
+    lag = args.lag if args.lag > 0 else 2 * args.batch
+    frameset = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], wl.bpc)
 
     log(f"warmup {args.warmup} passes")
     ref_scores = None
     for _ in range(args.warmup):
-        sc = run_pass(ctxs, dev, wl.metric, wl.bpc, args.batch, lag)
+        sc = run_pass(ctxs, frameset, wl.metric, args.batch, lag)
         if ref_scores is None:
             ref_scores = sc
         elif sc != ref_scores:
@@ -148,7 +131,7 @@ def main():
         f"lag {lag}")
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        sc = run_pass(ctxs, dev, wl.metric, wl.bpc, args.batch, lag)
+        sc = run_pass(ctxs, frameset, wl.metric, args.batch, lag)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     if ref_scores is not None and sc != ref_scores:
@@ -162,7 +145,7 @@ def main():
         c.vqm_ctx_set_timing(True)
     tsteps = max(1, min(args.steps, 10))
     for _ in range(tsteps):
-        run_pass(ctxs, dev, wl.metric, wl.bpc, args.batch, lag)
+        run_pass(ctxs, frameset, wl.metric, args.batch, lag)
     kt = {}
     for cls, name in ((vqm.VQM_KERNEL_DECIMATE, "decimate"), (vqm.VQM_KERNEL_SSIM, "ssim_map"),
                       (vqm.VQM_KERNEL_MSSSIM_LEVEL1, "ms_level1"),

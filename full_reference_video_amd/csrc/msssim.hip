@@ -26,16 +26,17 @@
 namespace vqm {
 namespace {
 
-constexpr int kTW = 64, kTH = 16, kNT = 256;
+constexpr int kTW = 64, kTH = 16, kNT = 256, kRB = 4;
 
 __constant__ double kBeta[5] = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333};
 
-template <int TW, int TH, int NT, typename TIn>
+template <int TW, int TH, int NT, int RB, typename TIn>
 __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int H, int next_pitch, float unit,
                                                Taps taps) {
-    constexpr int IW = TW + 10, IH = TH + 10;
-    __shared__ float sx[IH * IW], sy[IH * IW];
-    __shared__ float hmx[IH * TW], hmy[IH * TW], hxx[IH * TW], hyy[IH * TW], hxy[IH * TW];
+    constexpr int IH = TH + 10, IP = in_pitch<TW>();
+    __shared__ __attribute__((aligned(16))) float sx[IH * IP];
+    __shared__ __attribute__((aligned(16))) float sy[IH * IP];
+    __shared__ __attribute__((aligned(16))) float hm[5 * IH * TW];
     __shared__ double red[3][NT / 64];
 
     int bx, by, bz;
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
     const int MW = W - 10, MH = H - 10;
     const int x0 = bx * TW, y0 = by * TH;
 
-    stage_tile<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
+    stage<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
     __syncthreads();
 
     // Next level: 2x2 means of this tile's share of the plane, from the
@@ -62,41 +63,37 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
         for (int i = threadIdx.x; i < nw * nh; i += NT) {
             const int r = i / nw, c = i - r * nw;
             const int lr = 2 * r, lc = 2 * c;  // tile-local position of the block
-            const float x00 = sx[lr * IW + lc], x01 = sx[lr * IW + lc + 1];
-            const float x10 = sx[(lr + 1) * IW + lc], x11 = sx[(lr + 1) * IW + lc + 1];
-            const float y00 = sy[lr * IW + lc], y01 = sy[lr * IW + lc + 1];
-            const float y10 = sy[(lr + 1) * IW + lc], y11 = sy[(lr + 1) * IW + lc + 1];
+            const float x00 = sx[lr * IP + lc], x01 = sx[lr * IP + lc + 1];
+            const float x10 = sx[(lr + 1) * IP + lc], x11 = sx[(lr + 1) * IP + lc + 1];
+            const float y00 = sy[lr * IP + lc], y01 = sy[lr * IP + lc + 1];
+            const float y10 = sy[(lr + 1) * IP + lc], y11 = sy[(lr + 1) * IP + lc + 1];
             const size_t o = (size_t)(ny0 + r) * (size_t)next_pitch + (size_t)(nx0 + c);
             t.next_ref[o] = ((x00 + x01) + (x10 + x11)) * 0.25f + kMomentOffset;
             t.next_dis[o] = ((y00 + y01) + (y10 + y11)) * 0.25f + kMomentOffset;
         }
     }
 
-    horizontal_moments<TW, TH, NT>(sx, sy, taps, hmx, hmy, hxx, hyy, hxy);
+    horizontal_moments<TW, TH, NT>(sx, sy, taps, hm);
     __syncthreads();
 
     constexpr float kC3 = kC2 / 2.0f;
     double acc[3] = {0.0, 0.0, 0.0};
-    for (int i = threadIdx.x; i < TH * TW; i += NT) {
-        const int r = i / TW, c = i - r * TW;
-        if (x0 + c < MW && y0 + r < MH) {
-            float mx, my, xx, yy, xy;
-            vertical_moments<TW>(hmx, hmy, hxx, hyy, hxy, taps, r, c, mx, my, xx, yy, xy);
-            const float vx = xx - mx * mx;
-            const float vy = yy - my * my;
-            const float cxy = xy - mx * my;
-            const float sdx = sqrtf(fmaxf(vx, 0.0f));
-            const float sdy = sqrtf(fmaxf(vy, 0.0f));
-            const float ux = mx + kMomentOffset;
-            const float uy = my + kMomentOffset;
-            const float l = (ux * uy + ux * uy + kC1) / (ux * ux + uy * uy + kC1);
-            const float cs = (sdx * sdy + sdx * sdy + kC2) / (sdx * sdx + sdy * sdy + kC2);
-            const float st = (cxy + kC3) / (sdx * sdy + kC3);
-            acc[0] += (double)l;
-            acc[1] += (double)cs;
-            acc[2] += (double)st;
-        }
-    }
+    vertical_moments<TW, TH, NT, RB>(hm, taps, x0, y0, MW, MH,
+                                     [&](int, int, float mx, float my, float xx, float yy, float xy) {
+        const float vx = xx - mx * mx;
+        const float vy = yy - my * my;
+        const float cxy = xy - mx * my;
+        const float sdx = sqrtf(fmaxf(vx, 0.0f));
+        const float sdy = sqrtf(fmaxf(vy, 0.0f));
+        const float ux = mx + kMomentOffset;
+        const float uy = my + kMomentOffset;
+        const float l = (ux * uy + ux * uy + kC1) / (ux * ux + uy * uy + kC1);
+        const float cs = (sdx * sdy + sdx * sdy + kC2) / (sdx * sdx + sdy * sdy + kC2);
+        const float st = (cxy + kC3) / (sdx * sdy + kC3);
+        acc[0] += (double)l;
+        acc[1] += (double)cs;
+        acc[2] += (double)st;
+    });
 
     block_sum<NT, 3>(acc, red);
     if (threadIdx.x == 0) {
@@ -148,15 +145,15 @@ hipError_t launch_ms_level(const MsBatch &b, int n, InKind kind, int pitch, int 
     const dim3 grid((W - 10 + kTW - 1) / kTW, (H - 10 + kTH - 1) / kTH, n);
     switch (kind) {
     case IN_F32:
-        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, float>), grid, dim3(kNT), 0, stream, b, pitch, W, H, next_pitch,
+        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, kRB, float>), grid, dim3(kNT), 0, stream, b, pitch, W, H, next_pitch,
                            unit, taps);
         break;
     case IN_U8:
-        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, uint8_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H,
+        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, kRB, uint8_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H,
                            next_pitch, unit, taps);
         break;
     case IN_U16:
-        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, uint16_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H,
+        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, kRB, uint16_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H,
                            next_pitch, unit, taps);
         break;
     default:

@@ -12,9 +12,10 @@
 //
 // One workgroup per TW x TH tile of the map.  The tile's (TW+10) x (TH+10)
 // input window of both planes is staged in LDS, the horizontal 11-tap pass
-// writes five moment planes to LDS, and the vertical pass forms the moments
-// of each map pixel and its SSIM term in fp32 (with the mid-scale offset
-// removed first, so E[x^2] - mu^2 cancels less).  Each thread adds its map
+// writes five moment planes to LDS (four columns per thread step), and the
+// vertical pass (four rows per thread step) forms the moments of each map
+// pixel and its SSIM term in fp32, with the mid-scale offset removed first
+// so E[x^2] - mu^2 cancels less.  Each thread adds its map
 // pixels in fp64; the workgroup sum goes to a partials array, and a finish
 // kernel (one workgroup per frame) sums the partials in index order and
 // writes the mean straight into the pinned host result slot.
@@ -23,13 +24,14 @@
 namespace vqm {
 namespace {
 
-constexpr int kTW = 64, kTH = 8, kNT = 256;
+constexpr int kTW = 32, kTH = 32, kNT = 256, kRB = 4;
 
-template <int TW, int TH, int NT, typename TIn>
+template <int TW, int TH, int NT, int RB, typename TIn>
 __global__ __launch_bounds__(NT) void ssim_map(SsimBatch b, int pitch, int W, int H, float unit, Taps taps) {
-    constexpr int IW = TW + 10, IH = TH + 10;
-    __shared__ float sx[IH * IW], sy[IH * IW];
-    __shared__ float hmx[IH * TW], hmy[IH * TW], hxx[IH * TW], hyy[IH * TW], hxy[IH * TW];
+    constexpr int IH = TH + 10, IP = in_pitch<TW>();
+    __shared__ __attribute__((aligned(16))) float sx[IH * IP];
+    __shared__ __attribute__((aligned(16))) float sy[IH * IP];
+    __shared__ __attribute__((aligned(16))) float hm[5 * IH * TW];
     __shared__ double red[1][NT / 64];
 
     int bx, by, bz;
@@ -41,29 +43,25 @@ __global__ __launch_bounds__(NT) void ssim_map(SsimBatch b, int pitch, int W, in
     const int MW = W - 10, MH = H - 10;
     const int x0 = bx * TW, y0 = by * TH;
 
-    stage_tile<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
+    stage<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
     __syncthreads();
-    horizontal_moments<TW, TH, NT>(sx, sy, taps, hmx, hmy, hxx, hyy, hxy);
+    horizontal_moments<TW, TH, NT>(sx, sy, taps, hm);
     __syncthreads();
 
     double acc[1] = {0.0};
-    for (int i = threadIdx.x; i < TH * TW; i += NT) {
-        const int r = i / TW, c = i - r * TW;
-        if (x0 + c < MW && y0 + r < MH) {
-            float mx, my, xx, yy, xy;
-            vertical_moments<TW>(hmx, hmy, hxx, hyy, hxy, taps, r, c, mx, my, xx, yy, xy);
-            const float sxx = xx - mx * mx;
-            const float syy = yy - my * my;
-            const float sxy = xy - mx * my;
-            const float ux = mx + kMomentOffset;
-            const float uy = my + kMomentOffset;
-            // Numerator and denominator as mirror images (contraction is
-            // off), so identical planes give exactly 1.
-            const float num = (ux * uy + ux * uy + kC1) * (sxy + sxy + kC2);
-            const float den = (ux * ux + uy * uy + kC1) * (sxx + syy + kC2);
-            acc[0] += (double)(num / den);
-        }
-    }
+    vertical_moments<TW, TH, NT, RB>(hm, taps, x0, y0, MW, MH,
+                                     [&](int, int, float mx, float my, float xx, float yy, float xy) {
+        const float sxx = xx - mx * mx;
+        const float syy = yy - my * my;
+        const float sxy = xy - mx * my;
+        const float ux = mx + kMomentOffset;
+        const float uy = my + kMomentOffset;
+        // Numerator and denominator as mirror images (contraction is off),
+        // so identical planes give exactly 1.
+        const float num = (ux * uy + ux * uy + kC1) * (sxy + sxy + kC2);
+        const float den = (ux * ux + uy * uy + kC1) * (sxx + syy + kC2);
+        acc[0] += (double)(num / den);
+    });
 
     block_sum<NT, 1>(acc, red);
     if (threadIdx.x == 0) fr.partials[by * gridDim.x + bx] = acc[0];
@@ -95,13 +93,13 @@ hipError_t launch_ssim(const SsimBatch &b, int n, InKind kind, int pitch, int W,
     const dim3 grid((W - 10 + kTW - 1) / kTW, (H - 10 + kTH - 1) / kTH, n);
     switch (kind) {
     case IN_F32:
-        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, float>), grid, dim3(kNT), 0, stream, b, pitch, W, H, unit, taps);
+        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, kRB, float>), grid, dim3(kNT), 0, stream, b, pitch, W, H, unit, taps);
         break;
     case IN_U8:
-        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, uint8_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H, unit, taps);
+        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, kRB, uint8_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H, unit, taps);
         break;
     case IN_U16:
-        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, uint16_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H, unit,
+        hipLaunchKernelGGL((ssim_map<kTW, kTH, kNT, kRB, uint16_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H, unit,
                            taps);
         break;
     default:

@@ -41,73 +41,194 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
+// LDS row pitch (floats) of a staged input tile: a multiple of 4 with room
+// for the 16-byte reads of the horizontal pass.
+template <int TW>
+constexpr int in_pitch() {
+    static_assert(TW % 4 == 0, "tile width must be a multiple of 4");
+    return TW + 12;
+}
+
 // Stage the (TH + 10) x (TW + 10) input tile of both planes at (x0, y0),
-// offset-subtracted, in LDS; cells outside the plane hold 0 (they feed only
-// map pixels outside the valid region).
+// offset-subtracted, in LDS with row pitch in_pitch<TW>(); cells outside the
+// plane hold 0 (they feed only map pixels outside the valid region).  All of
+// a thread's global loads are issued before the first LDS store, so the tile
+// costs one memory latency, not one per element.
 template <int TW, int TH, int NT, typename TIn>
 __device__ __forceinline__ void stage_tile(const TIn *__restrict__ ref, const TIn *__restrict__ dis,
                                            int pitch, int W, int H, float unit, int x0, int y0,
                                            float *sx, float *sy) {
-    constexpr int IW = TW + 10, IH = TH + 10;
-    for (int i = threadIdx.x; i < IH * IW; i += NT) {
+    constexpr int IW = TW + 10, IH = TH + 10, IP = in_pitch<TW>();
+    constexpr int N = (IH * IW + NT - 1) / NT;
+    float va[N], vb[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int i = threadIdx.x + k * NT;
         const int r = i / IW, c = i - r * IW;
         const int gx = x0 + c, gy = y0 + r;
-        float a = 0.0f, b = 0.0f;
-        if (gx < W && gy < H) {
+        va[k] = vb[k] = 0.0f;
+        if (i < IH * IW && gx < W && gy < H) {
             const size_t o = (size_t)gy * (size_t)pitch + (size_t)gx;
-            a = load_sample(ref, o, unit) - kMomentOffset;
-            b = load_sample(dis, o, unit) - kMomentOffset;
+            va[k] = load_sample(ref, o, unit) - kMomentOffset;
+            vb[k] = load_sample(dis, o, unit) - kMomentOffset;
         }
-        sx[i] = a;
-        sy[i] = b;
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int i = threadIdx.x + k * NT;
+        const int r = i / IW, c = i - r * IW;
+        if (i < IH * IW) {
+            sx[r * IP + c] = va[k];
+            sy[r * IP + c] = vb[k];
+        }
     }
 }
 
-// Horizontal pass: the five Gaussian moments of every staged row at each of
-// the TW map columns, into five LDS planes of (TH + 10) x TW.
+// The same for fp32 planes whose row pitch is a multiple of 4 floats (x0 is
+// a multiple of TW, itself a multiple of 4): 16-byte loads and LDS stores;
+// the ragged last chunk of a row is read element by element.
+template <int TW, int TH, int NT>
+__device__ __forceinline__ void stage_tile_f32x4(const float *__restrict__ ref, const float *__restrict__ dis,
+                                                 int pitch, int W, int H, int x0, int y0, float *sx, float *sy) {
+    constexpr int IW = TW + 10, IH = TH + 10, IP = in_pitch<TW>();
+    constexpr int QI = (IW + 3) / 4;  // 4-wide chunks per row (the last holds 2 columns)
+    constexpr int N = (IH * QI + NT - 1) / NT;
+    const float off = kMomentOffset;
+    float4 va[N], vb[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int i = threadIdx.x + k * NT;
+        const int r = i / QI, q = i - r * QI;
+        const int gx = x0 + 4 * q, gy = y0 + r;
+        va[k] = vb[k] = make_float4(off, off, off, off);  // cells outside the plane end up 0
+        if (i < IH * QI && gy < H) {
+            const size_t o = (size_t)gy * (size_t)pitch + (size_t)gx;
+            if (gx + 3 < W && 4 * q + 3 < IW) {
+                va[k] = *reinterpret_cast<const float4 *>(ref + o);
+                vb[k] = *reinterpret_cast<const float4 *>(dis + o);
+            } else {
+                float ta[4], tb[4];
+                for (int e = 0; e < 4; ++e)
+                    if (gx + e < W && 4 * q + e < IW) {
+                        ta[e] = ref[o + e];
+                        tb[e] = dis[o + e];
+                    } else {
+                        ta[e] = tb[e] = off;
+                    }
+                va[k] = make_float4(ta[0], ta[1], ta[2], ta[3]);
+                vb[k] = make_float4(tb[0], tb[1], tb[2], tb[3]);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int i = threadIdx.x + k * NT;
+        const int r = i / QI, q = i - r * QI;
+        if (i < IH * QI) {
+            const float4 a = make_float4(va[k].x - off, va[k].y - off, va[k].z - off, va[k].w - off);
+            const float4 b = make_float4(vb[k].x - off, vb[k].y - off, vb[k].z - off, vb[k].w - off);
+            *reinterpret_cast<float4 *>(sx + r * IP + 4 * q) = a;
+            *reinterpret_cast<float4 *>(sy + r * IP + 4 * q) = b;
+        }
+    }
+}
+
+// Stage with 16-byte loads when the input is an fp32 plane (its pitch is
+// then a multiple of 64 floats by construction), else element by element.
+template <int TW, int TH, int NT, typename TIn>
+__device__ __forceinline__ void stage(const TIn *__restrict__ ref, const TIn *__restrict__ dis, int pitch, int W,
+                                      int H, float unit, int x0, int y0, float *sx, float *sy) {
+    if constexpr (sizeof(TIn) == 4) {
+        stage_tile_f32x4<TW, TH, NT>(ref, dis, pitch, W, H, x0, y0, sx, sy);
+    } else {
+        stage_tile<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
+    }
+}
+
+// Horizontal pass: the five Gaussian moments (x, y, x^2, y^2, xy) of every
+// staged row at each of the TW map columns, into five LDS planes of
+// (TH + 10) x TW (hm + p * (TH + 10) * TW).  A thread forms four adjacent
+// columns at once from 14 inputs read with 16-byte LDS loads, and squares
+// each input once.  Per output the FMA order is k = 0..10.
 template <int TW, int TH, int NT>
 __device__ __forceinline__ void horizontal_moments(const float *sx, const float *sy, const Taps &taps,
-                                                   float *hmx, float *hmy, float *hxx, float *hyy,
-                                                   float *hxy) {
-    constexpr int IW = TW + 10, IH = TH + 10;
-    for (int i = threadIdx.x; i < IH * TW; i += NT) {
-        const int r = i / TW, c = i - r * TW;
-        const float *px = sx + r * IW + c;
-        const float *py = sy + r * IW + c;
-        float mx = 0.f, my = 0.f, xx = 0.f, yy = 0.f, xy = 0.f;
+                                                   float *hm) {
+    constexpr int IH = TH + 10, IP = in_pitch<TW>(), QW = TW / 4, PL = IH * TW;
+    for (int it = threadIdx.x; it < IH * QW; it += NT) {
+        const int r = it / QW, c0 = (it - r * QW) * 4;
+        float a[14], b[14];
+        const float *pa = sx + r * IP + c0, *pb = sy + r * IP + c0;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const float4 va = *reinterpret_cast<const float4 *>(pa + 4 * q);
+            const float4 vb = *reinterpret_cast<const float4 *>(pb + 4 * q);
+            a[4 * q] = va.x; a[4 * q + 1] = va.y; a[4 * q + 2] = va.z; a[4 * q + 3] = va.w;
+            b[4 * q] = vb.x; b[4 * q + 1] = vb.y; b[4 * q + 2] = vb.z; b[4 * q + 3] = vb.w;
+        }
+        {
+            const float2 va = *reinterpret_cast<const float2 *>(pa + 12);
+            const float2 vb = *reinterpret_cast<const float2 *>(pb + 12);
+            a[12] = va.x; a[13] = va.y;
+            b[12] = vb.x; b[13] = vb.y;
+        }
+        float aa[14], bb[14], ab[14];
+#pragma unroll
+        for (int i = 0; i < 14; ++i) {
+            aa[i] = a[i] * a[i];
+            bb[i] = b[i] * b[i];
+            ab[i] = a[i] * b[i];
+        }
+        float m[5][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[0][j] = m[1][j] = m[2][j] = m[3][j] = m[4][j] = 0.f;
 #pragma unroll
         for (int k = 0; k < 11; ++k) {
-            const float a = px[k], b = py[k], g = taps.g[k];
-            mx = fmaf(g, a, mx);
-            my = fmaf(g, b, my);
-            xx = fmaf(g, a * a, xx);
-            yy = fmaf(g, b * b, yy);
-            xy = fmaf(g, a * b, xy);
+            const float g = taps.g[k];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                m[0][j] = fmaf(g, a[j + k], m[0][j]);
+                m[1][j] = fmaf(g, b[j + k], m[1][j]);
+                m[2][j] = fmaf(g, aa[j + k], m[2][j]);
+                m[3][j] = fmaf(g, bb[j + k], m[3][j]);
+                m[4][j] = fmaf(g, ab[j + k], m[4][j]);
+            }
         }
-        hmx[i] = mx;
-        hmy[i] = my;
-        hxx[i] = xx;
-        hyy[i] = yy;
-        hxy[i] = xy;
+        const int o = r * TW + c0;
+#pragma unroll
+        for (int p = 0; p < 5; ++p)
+            *reinterpret_cast<float4 *>(hm + p * PL + o) = make_float4(m[p][0], m[p][1], m[p][2], m[p][3]);
     }
 }
 
-// Vertical pass at map pixel (r, c) of the tile: the five moments.
-template <int TW>
-__device__ __forceinline__ void vertical_moments(const float *hmx, const float *hmy, const float *hxx,
-                                                 const float *hyy, const float *hxy, const Taps &taps,
-                                                 int r, int c, float &mx, float &my, float &xx,
-                                                 float &yy, float &xy) {
-    mx = my = xx = yy = xy = 0.f;
+// Vertical pass: for RB stacked map rows of one tile column at a time, the
+// five moments from RB + 10 values of each horizontal plane (FMA order
+// k = 0..10), handed to `fn(r, c, mx, my, xx, yy, xy)` for every map pixel
+// inside the valid region (mx0 = x0 + c < MW, y0 + r < MH).
+template <int TW, int TH, int NT, int RB, typename F>
+__device__ __forceinline__ void vertical_moments(const float *hm, const Taps &taps, int x0, int y0, int MW,
+                                                 int MH, F &&fn) {
+    static_assert(TH % RB == 0, "tile height must be a multiple of the row block");
+    constexpr int IH = TH + 10, PL = IH * TW;
+    for (int it = threadIdx.x; it < (TH / RB) * TW; it += NT) {
+        const int c = it % TW, r0 = (it / TW) * RB;
+        if (x0 + c >= MW || y0 + r0 >= MH) continue;
+        float m[5][RB];
 #pragma unroll
-    for (int k = 0; k < 11; ++k) {
-        const int o = (r + k) * TW + c;
-        const float g = taps.g[k];
-        mx = fmaf(g, hmx[o], mx);
-        my = fmaf(g, hmy[o], my);
-        xx = fmaf(g, hxx[o], xx);
-        yy = fmaf(g, hyy[o], yy);
-        xy = fmaf(g, hxy[o], xy);
+        for (int p = 0; p < 5; ++p) {
+            float v[RB + 10];
+#pragma unroll
+            for (int i = 0; i < RB + 10; ++i) v[i] = hm[p * PL + (r0 + i) * TW + c];
+#pragma unroll
+            for (int j = 0; j < RB; ++j) {
+                float acc = 0.f;
+#pragma unroll
+                for (int k = 0; k < 11; ++k) acc = fmaf(taps.g[k], v[j + k], acc);
+                m[p][j] = acc;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+            if (y0 + r0 + j < MH) fn(r0 + j, c, m[0][j], m[1][j], m[2][j], m[3][j], m[4][j]);
     }
 }
 

@@ -160,7 +160,8 @@ struct Slot {
     size_t partials_count = 0;
     double *result_host = nullptr;  // pinned: score + 15 means
     double *result_dev = nullptr;   // its device-visible address
-    hipEvent_t done = nullptr;
+    bool ready = false;             // scratch allocated for geo
+    struct BatchEvent *batch = nullptr;  // completion of the batch this frame rode in
     int kind = KIND_NONE;
 
     // offsets (in floats) of the planes inside `planes`
@@ -173,9 +174,17 @@ struct Slot {
         if (planes) (void)hipFree(planes);
         if (partials) (void)hipFree(partials);
         if (result_host) (void)hipHostFree(result_host);
-        if (done) (void)hipEventDestroy(done);
         *this = Slot();
     }
+};
+
+// One completion event per submitted batch, shared by the batch's frames:
+// the first collect of the batch waits on it, the others find it done.  It
+// returns to the pool when its last frame is collected.
+struct BatchEvent {
+    hipEvent_t ev = nullptr;
+    int refs = 0;
+    bool completed = false;
 };
 
 struct TimedLaunch {
@@ -193,6 +202,7 @@ struct vqm_ctx {
     vqm::Taps taps;
     Slot slots[VQM_MAX_IN_FLIGHT];
     int head = 0, count = 0;
+    std::vector<std::unique_ptr<BatchEvent>> batch_events;
     bool timing = false;
     std::vector<TimedLaunch> timed;      // recorded, not yet read
     std::vector<hipEvent_t> event_pool;  // free timing events
@@ -212,10 +222,9 @@ int ensure_device(vqm_ctx *ctx) {
 
 // Size (or rebuild) a slot's scratch for geometry g.  The slot is idle.
 int prepare_slot(Slot &sl, const Geometry &g) {
-    if (sl.done != nullptr && sl.geo == g) return 0;
+    if (sl.ready && sl.geo == g) return 0;
     sl.release();
     sl.geo = g;
-    HIP_TRY(hipEventCreateWithFlags(&sl.done, hipEventDisableTiming));
     size_t floats = 0, partials = 0;
     if (g.kind == KIND_SSIM) {
         const size_t plane = (size_t)g.dpitch * (size_t)g.dh;
@@ -241,6 +250,21 @@ int prepare_slot(Slot &sl, const Geometry &g) {
     HIP_TRY_ALLOC(hipMalloc(&sl.partials, partials * sizeof(double)));
     HIP_TRY_ALLOC(hipHostMalloc(&sl.result_host, 16 * sizeof(double), hipHostMallocMapped | hipHostMallocCoherent));
     HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void **>(&sl.result_dev), sl.result_host, 0));
+    sl.ready = true;
+    return 0;
+}
+
+// A free batch event (no frame of an earlier batch still refers to it).
+int take_batch_event(vqm_ctx *ctx, BatchEvent **out) {
+    for (auto &be : ctx->batch_events)
+        if (be->refs == 0) {
+            *out = be.get();
+            return 0;
+        }
+    std::unique_ptr<BatchEvent> be(new BatchEvent());
+    HIP_TRY(hipEventCreateWithFlags(&be->ev, hipEventDisableTiming));
+    *out = be.get();
+    ctx->batch_events.push_back(std::move(be));
     return 0;
 }
 
@@ -499,8 +523,14 @@ int submit(vqm_ctx *ctx, int kind, const void *const *refs, const void *const *d
     }
     rc = kind == KIND_SSIM ? enqueue_ssim(ctx, sl, n, in_r, in_d, false) : enqueue_msssim(ctx, sl, n, in_r, in_d);
     if (rc) return rc;
+    BatchEvent *be = nullptr;
+    rc = take_batch_event(ctx, &be);
+    if (rc) return rc;
+    HIP_TRY(hipEventRecord(be->ev, ctx->stream));
+    be->refs = n;
+    be->completed = false;
     for (int i = 0; i < n; ++i) {
-        HIP_TRY(hipEventRecord(sl[i]->done, ctx->stream));
+        sl[i]->batch = be;
         sl[i]->kind = kind;
     }
     ctx->count += n;
@@ -514,9 +544,15 @@ int collect(vqm_ctx *ctx, double *score, double *lcs) {
     int rc = ensure_device(ctx);
     if (rc) return rc;
     Slot &sl = ctx->slots[ctx->head];
-    HIP_TRY(hipEventSynchronize(sl.done));  // the one wait of this frame
+    BatchEvent *be = sl.batch;
+    if (!be->completed) {
+        HIP_TRY(hipEventSynchronize(be->ev));  // the one wait of this frame (and its batch)
+        be->completed = true;
+    }
     ctx->head = (ctx->head + 1) % VQM_MAX_IN_FLIGHT;
     ctx->count -= 1;
+    be->refs -= 1;
+    sl.batch = nullptr;
     *score = sl.result_host[0];
     if (lcs && sl.kind == KIND_MSSSIM) memcpy(lcs, sl.result_host + 1, 15 * sizeof(double));
     return 0;
@@ -557,6 +593,7 @@ void destroy(vqm_ctx *ctx) {
     (void)hipSetDevice(ctx->device);
     (void)hipStreamSynchronize(ctx->stream);
     for (Slot &s : ctx->slots) s.release();
+    for (auto &be : ctx->batch_events) (void)hipEventDestroy(be->ev);
     for (const TimedLaunch &t : ctx->timed) {
         (void)hipEventDestroy(t.start);
         (void)hipEventDestroy(t.stop);
@@ -614,6 +651,47 @@ int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, 
     *score = s;
     if (lcs) memcpy(lcs, l, sizeof l);
     return 0;
+}
+
+// The pipelined scoring loop of vqm_score_frames.
+int score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *refs, const void *const *diss,
+                 int n, int w, int h, int bpc, int batch, int lag, double *scores, double *lcs) {
+    if (!ctxs || nctx < 1 || !refs || !diss || !scores) return fail(-EINVAL, "NULL argument or no context");
+    if (metric != VQM_METRIC_FLOAT_SSIM && metric != VQM_METRIC_MS_SSIM)
+        return fail(-EINVAL, "unknown metric %d", metric);
+    if (n < 0) return fail(-EINVAL, "negative frame count");
+    if (batch < 1 || batch > VQM_MAX_BATCH) return fail(-EINVAL, "batch %d outside 1..%d", batch, VQM_MAX_BATCH);
+    for (int c = 0; c < nctx; ++c) {
+        if (!ctxs[c]) return fail(-EINVAL, "NULL context %d", c);
+        if (ctxs[c]->count != 0) return fail(-EINVAL, "context %d has frames in flight", c);
+    }
+    const int kind = metric == VQM_METRIC_MS_SSIM ? KIND_MSSSIM : KIND_SSIM;
+    if (lag <= 0) lag = 2 * batch;
+    // FIFO of submitted frames: (context, frame index)
+    std::vector<std::pair<int, int>> fifo;
+    fifo.reserve(n);
+    size_t front = 0;
+    int rc = 0;
+    auto collect_one = [&]() -> int {
+        const std::pair<int, int> e = fifo[front++];
+        return collect(ctxs[e.first], scores + e.second, lcs ? lcs + 15 * (size_t)e.second : nullptr);
+    };
+    for (int b0 = 0, k = 0; b0 < n && rc == 0; b0 += batch, ++k) {
+        const int m = n - b0 < batch ? n - b0 : batch;
+        const int c = k % nctx;
+        while (rc == 0 && front < fifo.size() &&
+               ((int)(fifo.size() - front) + m > lag + batch || ctxs[c]->count + m > VQM_MAX_IN_FLIGHT))
+            rc = collect_one();
+        if (rc) break;
+        rc = submit(ctxs[c], kind, refs + b0, diss + b0, m, w, h, bpc);
+        if (rc) break;
+        for (int i = 0; i < m; ++i) fifo.emplace_back(c, b0 + i);
+    }
+    while (front < fifo.size()) {
+        const int rc2 = collect_one();
+        if (rc == 0) rc = rc2;
+    }
+    return rc;
 }
 
 // One frame into the next free slot for the debug exports (synchronous; the
@@ -684,6 +762,11 @@ int vqm_msssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *c
 }
 
 int vqm_collect(vqm_ctx *ctx, double *score, double *lcs) { return collect(ctx, score, lcs); }
+
+int vqm_score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *refs, const void *const *dis,
+                     int n, int w, int h, int bpc, int batch, int lag, double *scores, double *lcs) {
+    return score_frames(ctxs, nctx, metric, refs, dis, n, w, h, bpc, batch, lag, scores, lcs);
+}
 
 int vqm_in_flight(const vqm_ctx *ctx) { return ctx ? ctx->count : 0; }
 

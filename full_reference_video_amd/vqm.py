@@ -24,6 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libvqm.so")
 VQM_MAX_IN_FLIGHT = 16
 VQM_MAX_BATCH = 8
 VQM_MSSSIM_LCS = 15
+VQM_METRIC_FLOAT_SSIM = 0
+VQM_METRIC_MS_SSIM = 1
 VQM_KERNEL_DECIMATE = 0
 VQM_KERNEL_SSIM = 1
 VQM_KERNEL_MSSSIM_LEVEL1 = 2
@@ -67,6 +69,9 @@ def lib() -> ctypes.CDLL:
             getattr(L, n).argtypes = [c_void_p, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int,
                                       c_int, c_int, c_int]
         L.vqm_collect.argtypes = [c_void_p, c_double_p, c_double_p]
+        L.vqm_score_frames.argtypes = [ctypes.POINTER(c_void_p), c_int, c_int, ctypes.POINTER(c_void_p),
+                                       ctypes.POINTER(c_void_p), c_int, c_int, c_int, c_int, c_int, c_int,
+                                       c_double_p, c_double_p]
         L.vqm_in_flight.argtypes = [c_void_p]
         L.vqm_ctx_set_timing.argtypes = [c_void_p, c_int]
         L.vqm_ctx_kernel_time.argtypes = [c_void_p, c_int, c_double_p, c_int_p, c_int_p]
@@ -280,3 +285,41 @@ class Context:
 
 def vqm_ctx_create(device: int = 0, stream=None) -> Context:
     return Context(device, stream)
+
+
+class FrameSet:
+    """Plane pointers of many frame pairs, marshalled once for repeated
+    vqm_score_frames calls (the planes stay referenced)."""
+
+    def __init__(self, refs, diss, bpc: int):
+        if len(refs) != len(diss) or not refs:
+            raise ValueError("refs and dis must be non-empty and of equal length")
+        n = len(refs)
+        self.n, self.bpc = n, int(bpc)
+        self.refs = (ctypes.c_void_p * n)()
+        self.diss = (ctypes.c_void_p * n)()
+        self._keep = []
+        self.w = self.h = None
+        for i, (r, d) in enumerate(zip(refs, diss)):
+            a, b, w, h, k = _pair(r, d, bpc)
+            if self.w is None:
+                self.w, self.h = w, h
+            elif (w, h) != (self.w, self.h):
+                raise ValueError("all frames must share their size")
+            self.refs[i], self.diss[i] = a, b
+            self._keep.append(k)
+
+
+def vqm_score_frames(ctxs, metric: int, frames: FrameSet, batch: int = 8, lag: int = 0,
+                     want_lcs: bool = False):
+    """Score every frame of `frames` through the contexts `ctxs` (see the C
+    call); returns the scores (and the 15 MS-SSIM level means per frame)."""
+    handles = (ctypes.c_void_p * len(ctxs))(*[c._h.value for c in ctxs])
+    scores = np.empty(frames.n, np.float64)
+    lcs = np.empty((frames.n, VQM_MSSSIM_LCS), np.float64) if want_lcs else None
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(lib().vqm_score_frames(handles, len(ctxs), int(metric), frames.refs, frames.diss, frames.n,
+                                  frames.w, frames.h, frames.bpc, int(batch), int(lag),
+                                  scores.ctypes.data_as(dp),
+                                  lcs.ctypes.data_as(dp) if want_lcs else None), "vqm_score_frames")
+    return (scores, lcs) if want_lcs else scores

@@ -158,6 +158,22 @@ VQM_API int vqm_collect(vqm_ctx *ctx, double *score, double *lcs);
 /* Number of frames in flight. */
 VQM_API int vqm_in_flight(const vqm_ctx *ctx);
 
+/* Metrics of vqm_score_frames. */
+enum vqm_metric { VQM_METRIC_FLOAT_SSIM = 0, VQM_METRIC_MS_SSIM = 1 };
+
+/* Score n frame pairs of one size and depth, pipelined, and block until all
+ * are scored.  Frames go in batches of `batch` (1..VQM_MAX_BATCH) to the
+ * nctx contexts in turn (several contexts on several streams let one
+ * batch's SSIM kernels overlap the next batch's decimation); a frame is
+ * collected — its one wait — once about `lag` later frames have been
+ * submitted (lag <= 0: 2 * batch).  scores[i] receives frame i's score;
+ * lcs (may be NULL) receives 15 doubles per frame for MS-SSIM.  The contexts
+ * must have no frames in flight.  On error every submitted frame is still
+ * collected before the call returns. */
+VQM_API int vqm_score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *refs,
+                             const void *const *dis, int n, int w, int h, int bpc, int batch, int lag,
+                             double *scores, double *lcs);
+
 /* ---- measurement and inspection ---- */
 
 /* Turn per-kernel timing on or off: while on, every decimation, SSIM and

@@ -338,3 +338,28 @@ def test_msssim_batched_equals_single(ctx):
         assert s2 == s1
         assert np.array_equal(l1, l2)
     assert abs(single[2][0] - oracle.msssim(*pairs[2], 8)) <= TOL
+
+
+@pytest.mark.parametrize("metric,c", [(0, 2), (0, 4), (1, 5)])
+def test_score_frames_loop_matches_single_frames(torch_cuda, metric, c):
+    torch = torch_cuda
+    src = synth.FrameSource(c, w=960, h=544) if c == 5 else synth.FrameSource(c)
+    n = 13
+    pairs = [src.pair(t) for t in range(n)]
+    say(f"score_frames metric {metric} config {c}")
+    one = vqm.vqm_msssim_frame if metric == 1 else vqm.vqm_ssim_frame
+    want = [one(r, d, src.bpc) for r, d in pairs]
+    dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
+    fs = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], src.bpc)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    ctxs = [vqm.Context(0, s) for s in streams]
+    try:
+        for batch, lag, nc in [(1, 0, 1), (4, 0, 2), (8, 3, 2), (8, 0, 1)]:
+            got = vqm.vqm_score_frames(ctxs[:nc], metric, fs, batch, lag)
+            assert got.tolist() == want, (batch, lag, nc)
+        # host frames through the same loop
+        fs_host = vqm.FrameSet([r for r, _ in pairs], [d for _, d in pairs], src.bpc)
+        assert vqm.vqm_score_frames(ctxs, metric, fs_host, 5, 0).tolist() == want
+    finally:
+        for x in ctxs:
+            x.close()
