@@ -3,10 +3,10 @@
 One step = one pass of the whole scoring path (upload-free: decimate, SSIM
 map, fixed-tree reduction, 8-byte result, one host wait per frame) over the
 workload's 50 distinct device-resident frame pairs (1.66 GB, larger than the
-256 MB last-level cache, so every frame comes from HBM).  Frames are
-submitted through the C ABI with a lag: frame f is collected after frame
-f + lag is submitted, so the GPU never idles on the host, and every frame
-still costs exactly one wait.
+256 MB last-level cache, so every frame comes from HBM).  The K timed steps
+run as one continuous stream of 50*K frames through the C ABI's pipelined
+loop (vqm_score_frames): batches of frames per launch, each frame collected
+with one wait once `lag` later frames are submitted.
 
 Prints one JSON line (see the keys below).  ``--workload`` picks another of
 the five synthetic workloads; the default is the 2160p 10-bit float_ssim one.
@@ -47,8 +47,9 @@ def algorithmic_bytes(wl, s: int) -> int:
 
 
 def run_pass(ctxs, frameset, metric, batch, lag):
-    """One step: every frame of the workload scored once through the C ABI's
-    pipelined loop (batches rotate over the contexts; one wait per frame)."""
+    """Score every frame pair of `frameset` once, as one continuous stream,
+    through the C ABI's pipelined loop (batches rotate over the contexts; one
+    wait per frame)."""
     from full_reference_video_amd import vqm
     m = vqm.VQM_METRIC_MS_SSIM if metric == "ms_ssim" else vqm.VQM_METRIC_FLOAT_SSIM
     return vqm.vqm_score_frames(ctxs, m, frameset, batch, lag).tolist()
@@ -76,13 +77,13 @@ def cpu_baseline(host, wl, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="workload number 1..5")
-    ap.add_argument("--streams", type=int, default=2, help="contexts/streams batches rotate over")
+    ap.add_argument("--streams", type=int, default=1, help="contexts/streams batches rotate over")
     ap.add_argument("--batch", type=int, default=8, help="frames per submit (and per kernel launch)")
     ap.add_argument("--lag", type=int, default=0,
-                    help="frames in flight before a collect (0: 2*batch, capped by the in-flight slots)")
+                    help="frames submitted after a frame before it is collected (0: 3*batch)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0: skip)")
     args = ap.parse_args()
 
@@ -114,8 +115,12 @@ def main():
 
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
     ctxs = [vqm.Context(0, st) for st in streams]
-    lag = args.lag if args.lag > 0 else 2 * args.batch
+    lag = args.lag if args.lag > 0 else 3 * args.batch
     frameset = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], wl.bpc)
+    # The timed run streams the workload's frames K times over without a
+    # break, as a video is scored (the pipeline fills once and drains once).
+    stream_set = vqm.FrameSet([r for _ in range(args.steps) for r, _ in dev],
+                              [d for _ in range(args.steps) for _, d in dev], wl.bpc)
 
     log(f"warmup {args.warmup} passes")
     ref_scores = None
@@ -130,11 +135,10 @@ def main():
     log(f"timed {args.steps} passes over {wl.frames} frames, batch {args.batch}, {args.streams} streams, "
         f"lag {lag}")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        sc = run_pass(ctxs, frameset, wl.metric, args.batch, lag)
+    sc = run_pass(ctxs, stream_set, wl.metric, args.batch, lag)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    if ref_scores is not None and sc != ref_scores:
+    if ref_scores is not None and sc != ref_scores * args.steps:
         raise RuntimeError("scores changed between passes")
     frames = args.steps * wl.frames
     fps = frames / el
@@ -143,11 +147,9 @@ def main():
     log("kernel timing pass")
     for c in ctxs:
         c.vqm_ctx_set_timing(True)
-    tsteps = max(1, min(args.steps, 10))
-    for _ in range(tsteps):
-        run_pass(ctxs, frameset, wl.metric, args.batch, lag)
+    run_pass(ctxs, stream_set, wl.metric, args.batch, lag)
     kt = {}
-    for cls, name in ((vqm.VQM_KERNEL_DECIMATE, "decimate"), (vqm.VQM_KERNEL_SSIM, "ssim_map"),
+    for cls, name in ((vqm.VQM_KERNEL_SSIM_STEP, "ssim_step"), (vqm.VQM_KERNEL_SSIM_DRAIN, "ssim_drain"),
                       (vqm.VQM_KERNEL_MSSSIM_LEVEL1, "ms_level1"),
                       (vqm.VQM_KERNEL_MSSSIM_COARSE, "ms_levels2_5")):
         ms = n = nf = 0
@@ -163,14 +165,13 @@ def main():
 
     alg = algorithmic_bytes(wl, s)
     if wl.metric == "float_ssim":
-        name = "decimate" if "decimate" in kt else "ssim_map"
+        name = "ssim_step" if "ssim_step" in kt else "ssim_drain"
         per_launch = alg * kt[name]["frames_per_launch"]
         avg_s = kt[name]["avg_us"] * 1e-6
         achieved = per_launch / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "decimate_pow2" if name == "decimate" else "ssim_map",
-                "bytes_per_launch": int(per_launch)}
+                "kernel": "ssim_step", "bytes_per_launch": int(per_launch)}
     else:
         # MS-SSIM level 1 is VALU-bound: flops of the separable moments and
         # the l/c/s terms per valid map pixel (see the design notes).

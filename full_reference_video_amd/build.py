@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvqm.so")
 
-SOURCES = ["vqm_runtime.cpp", "decimate.hip", "ssim.hip", "msssim.hip"]
+SOURCES = ["vqm_runtime.cpp", "ssim_step.hip", "msssim.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -1,4 +1,5 @@
-// decimate.hip — exact box low-pass and decimate for gfx950.
+// decimate_device.h — exact box low-pass and decimate for gfx950 (device
+// code, library-private; the decimation role of the float_ssim step kernel).
 //
 // "ADR-1405: float_ssim_hip decimates on the device, bit-identical to the
 // CPU", Context and Decision 1: output (X, Y) of a plane is the window at
@@ -8,13 +9,13 @@
 // 2^-52 units: every product is a multiple of 2^-45 and the window sum stays
 // below 2^8, so it fits an int64 for s <= 128 with no fp64 anywhere.
 //
-// Two kernels compute that same integer:
+// Two code paths compute that same integer:
 //
-//  * decimate_general — any s <= 128: each product is formed in fp32 and its
+//  * general_block — any s <= 128: each product is formed in fp32 and its
 //    exact value is turned into 2^-52 units from its exponent and
 //    significand, then added as a uint64.
 //
-//  * decimate_pow2 — s = 2^k, where tap = 2^-2k and every product is exact,
+//  * pow2_wave — s = 2^k, where tap = 2^-2k and every product is exact,
 //    so the units of a product are raw * 2^(52 - 2k - (bpc-8)): a constant
 //    shift of the raw integer.  The shift is hoisted out of the window sum,
 //    which becomes a plain integer sum of raw samples (v_sad_u8 / v_sad_u16
@@ -22,7 +23,7 @@
 //    scaled by the exact power of two.  This is the HBM-bound path of the
 //    1080p and 2160p frames.
 //
-// Layout of decimate_pow2.  Chunk k of a row is the s raw columns
+// Layout of pow2_wave.  Chunk k of a row is the s raw columns
 // [k*s, k*s + s); window X covers the high half of chunk X-1 and the low half
 // of chunk X.  A lane owns one aligned group of G = max(s, 16/sizeof(T))
 // columns (CPT = G/s chunks) and reads it with 128-bit non-temporal loads for
@@ -33,10 +34,12 @@
 // 0 re-reads the last group of the previous wave (1/64 extra, which the XCD
 // remap keeps in the same L2) and outputs nothing.  At the left edge lane 0
 // of wave 0 stands in for group -1 with the mirror of chunk 0's low half.
+#pragma once
+
 #include "vqm_kernels.h"
 
 namespace vqm {
-namespace {
+namespace dec {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -64,14 +67,15 @@ __device__ __forceinline__ uint64_t product_units(uint32_t raw, float tap, int s
     return m << (e + shift_base);
 }
 
+// One 256-thread block of the general kernel: outputs (64 bx + lane,
+// 4 by + wave).
 template <typename T>
-__global__ __launch_bounds__(256) void decimate_general(DecimateBatch b, int w, int h, int bpc, int s,
-                                                        float tap, int dec_w, int dec_h, int opitch) {
-    const DecimateFrame &fr = b.f[blockIdx.z];
+__device__ __forceinline__ void general_block(const DecimateFrame &fr, int bx, int by, int w, int h, int bpc,
+                                              int s, float tap, int dec_w, int dec_h, int opitch) {
     const T *__restrict__ ref = static_cast<const T *>(fr.ref);
     const T *__restrict__ dis = static_cast<const T *>(fr.dis);
-    const int X = blockIdx.x * 64 + (threadIdx.x & 63);
-    const int Y = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int X = bx * 64 + (threadIdx.x & 63);
+    const int Y = by * 4 + (threadIdx.x >> 6);
     if (X >= dec_w || Y >= dec_h) return;
     const int lo = -(s / 2);
     const int shift_base = -90 - bpc;
@@ -145,23 +149,17 @@ template <typename T, int S> struct Pow2Shape {
     static constexpr int CPT = G / S;                 // chunks (outputs) per lane
 };
 
-constexpr int kPow2Waves = 1;  // waves per workgroup
-
+// One wave of the power-of-two kernel: wave wv of output row Y.
 template <typename T, int S>
-__global__ __launch_bounds__(64 * kPow2Waves) void decimate_pow2(DecimateBatch b, int w, int h, int dec_w,
-                                                                 float post, int opitch) {
+__device__ __forceinline__ void pow2_wave(const DecimateFrame &fr, int wv, int Y, int w, int h, int dec_w,
+                                          float post, int opitch) {
     using Sh = Pow2Shape<T, S>;
     constexpr int V = Sh::V, NV = Sh::NV, CPT = Sh::CPT, G = Sh::G;
     constexpr int HALF = S / 2;
-
-    int bx, Y, bz;
-    xcd_block(bx, Y, bz);
-    const DecimateFrame &fr = b.f[bz];
     const T *__restrict__ ref = static_cast<const T *>(fr.ref);
     const T *__restrict__ dis = static_cast<const T *>(fr.dis);
 
     const int lane = threadIdx.x & 63;
-    const int wv = bx * kPow2Waves + (threadIdx.x >> 6);
     const int g = 63 * wv + lane - 1;  // this lane's group; -1 stands for the left mirror
     const int c0 = (g < 0 ? 0 : g) * G;
 
@@ -213,66 +211,5 @@ __global__ __launch_bounds__(64 * kPow2Waves) void decimate_pow2(DecimateBatch b
     }
 }
 
-template <typename T, int S>
-hipError_t launch_pow2(const DecimateBatch &b, int n, int w, int h, int bpc, int dec_w, int dec_h,
-                       int opitch, hipStream_t stream) {
-    using Sh = Pow2Shape<T, S>;
-    int k = 0;
-    while ((1 << k) < S) ++k;
-    const float post = ldexpf(1.0f, -(2 * k + bpc - 8));
-    const int groups = (dec_w + Sh::CPT - 1) / Sh::CPT;  // groups holding outputs
-    const int waves = (groups + 62) / 63;
-    const dim3 grid((waves + kPow2Waves - 1) / kPow2Waves, dec_h, n);
-    hipLaunchKernelGGL((decimate_pow2<T, S>), grid, dim3(64 * kPow2Waves), 0, stream, b, w, h, dec_w, post,
-                       opitch);
-    return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_pow2_any(int s, const DecimateBatch &b, int n, int w, int h, int bpc, int dec_w, int dec_h,
-                           int opitch, hipStream_t stream) {
-    switch (s) {
-    case 2: return launch_pow2<T, 2>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
-    case 4: return launch_pow2<T, 4>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
-    case 8: return launch_pow2<T, 8>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
-    case 16: return launch_pow2<T, 16>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
-    case 32: return launch_pow2<T, 32>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
-    case 64: return launch_pow2<T, 64>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
-    case 128: return launch_pow2<T, 128>(b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-}  // namespace
-
-bool decimate_fast_path(const DecimateBatch &b, int n, int w, int h, int bpc, int s) {
-    (void)h;
-    if (s < 2 || s > 128 || (s & (s - 1)) != 0) return false;
-    const int V = bpc == 8 ? 16 : 8;
-    if (w % V != 0) return false;
-    for (int i = 0; i < n; ++i)
-        if (((uintptr_t)b.f[i].ref | (uintptr_t)b.f[i].dis) & 15u) return false;
-    const int dec_w = (w + s - 1) / s;
-    // the last window's right half must lie inside the row (no right mirror)
-    if (w - s * (dec_w - 1) < s / 2) return false;
-    return true;
-}
-
-hipError_t launch_decimate(const DecimateBatch &b, int n, int w, int h, int bpc, int s, float tap, int dec_w,
-                           int dec_h, int opitch, hipStream_t stream) {
-    if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
-    if (decimate_fast_path(b, n, w, h, bpc, s)) {
-        if (bpc == 8) return launch_pow2_any<uint8_t>(s, b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
-        return launch_pow2_any<uint16_t>(s, b, n, w, h, bpc, dec_w, dec_h, opitch, stream);
-    }
-    const dim3 grid((dec_w + 63) / 64, (dec_h + 3) / 4, n);
-    if (bpc == 8)
-        hipLaunchKernelGGL(decimate_general<uint8_t>, grid, dim3(256), 0, stream, b, w, h, bpc, s, tap, dec_w,
-                           dec_h, opitch);
-    else
-        hipLaunchKernelGGL(decimate_general<uint16_t>, grid, dim3(256), 0, stream, b, w, h, bpc, s, tap, dec_w,
-                           dec_h, opitch);
-    return hipGetLastError();
-}
-
+}  // namespace dec
 }  // namespace vqm

@@ -1,0 +1,228 @@
+// ssim_step.hip — the float_ssim step kernel: decimation, SSIM map and
+// fixed-tree reduction of a stream of frame batches, software-pipelined.
+//
+// "ADR-1405: float_ssim_hip decimates on the device, bit-identical to the
+// CPU", Context and Decision 1–4: each plane is decimated (exactly, see
+// decimate_device.h), then the 11x11 Gaussian local means, variances and
+// covariance give a per-pixel SSIM term over the valid region whose mean is
+// the frame score; at scale 1 the map reads the raw samples directly.
+// "Research-1363: Device-resident ssimulacra2 and a single-wait MS-SSIM on
+// SYCL", Finding 4: the sum runs through a fixed tree — a fixed pixel subset
+// per work-item, a tree per work-group, one group over the partials — so
+// the result depends only on the plane size.
+//
+// One launch holds three independent roles, each over its own batch of
+// frames: decimation of batch k, the SSIM map of batch k-1 (whose decimated
+// planes the previous launch wrote) and the finish of batch k-2 (whose
+// partials the previous launch wrote).  No workgroup waits for another, and
+// the map's ALU work overlaps the decimation's HBM streaming inside one grid
+// instead of costing a launch of its own.  The roles take contiguous ranges
+// of the XCD-remapped block order: [decimation | map | finish].
+//
+// Map role: one workgroup per TW x TH tile of the map.  The tile's
+// (TW+10) x (TH+10) input window of both planes is staged in LDS, the
+// horizontal 11-tap pass writes five moment planes to LDS (four columns per
+// thread step), and the vertical pass (four rows per thread step) forms the
+// moments of each map pixel and its SSIM term in fp32, with the mid-scale
+// offset removed first so E[x^2] - mu^2 cancels less.  Each thread adds its
+// map pixels in fp64 and the workgroup's fixed-tree sum goes to the
+// frame's partials array.  Finish role: one workgroup per frame sums the
+// partials in index order and writes the mean straight into the pinned host
+// result slot.
+#include "decimate_device.h"
+#include "ssim_common.h"
+
+namespace vqm {
+namespace {
+
+constexpr int kNT = 256;                       // threads per workgroup, every role
+constexpr int kTW = 32, kTH = 32, kRB = 4;     // map tile
+constexpr int kDecWaves = kNT / 64;            // waves per decimation workgroup
+
+// ------------------------------------------------------------ decimation policies
+
+struct DecNone {
+    static int blocks_per_frame(const StepGeometry &) { return 0; }
+    __device__ static void run(const DecimateFrame &, int, const StepGeometry &) {}
+};
+
+template <typename T, int S>
+struct DecPow2 {
+    using Sh = dec::Pow2Shape<T, S>;
+    __host__ __device__ static int waves_per_row(const StepGeometry &g) {
+        const int groups = (g.dec_w + Sh::CPT - 1) / Sh::CPT;  // groups holding outputs
+        return (groups + 62) / 63;
+    }
+    __host__ __device__ static int blocks_per_row(const StepGeometry &g) {
+        return (waves_per_row(g) + kDecWaves - 1) / kDecWaves;
+    }
+    static int blocks_per_frame(const StepGeometry &g) { return blocks_per_row(g) * g.dec_h; }
+    __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
+        const int bpr = blocks_per_row(g);
+        const int Y = b / bpr, bx = b - Y * bpr;
+        dec::pow2_wave<T, S>(fr, bx * kDecWaves + (int)(threadIdx.x >> 6), Y, g.w, g.h, g.dec_w, g.post,
+                             g.dec_pitch);
+    }
+};
+
+template <typename T>
+struct DecGeneral {
+    __host__ __device__ static int blocks_x(const StepGeometry &g) { return (g.dec_w + 63) / 64; }
+    static int blocks_per_frame(const StepGeometry &g) { return blocks_x(g) * ((g.dec_h + 3) / 4); }
+    __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
+        const int bx = b % blocks_x(g), by = b / blocks_x(g);
+        dec::general_block<T>(fr, bx, by, g.w, g.h, g.bpc, g.s, g.tap, g.dec_w, g.dec_h, g.dec_pitch);
+    }
+};
+
+// ------------------------------------------------------------ map and finish roles
+
+__host__ __device__ inline int tiles_x(const StepGeometry &g) { return (g.dec_w - 10 + kTW - 1) / kTW; }
+__host__ __device__ inline int tiles_y(const StepGeometry &g) { return (g.dec_h - 10 + kTH - 1) / kTH; }
+
+template <typename TIn>
+__device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const StepGeometry &g, int pitch,
+                                         float unit, const Taps &taps) {
+    constexpr int IH = kTH + 10, IP = in_pitch<kTW>();
+    __shared__ __attribute__((aligned(16))) float sx[IH * IP];
+    __shared__ __attribute__((aligned(16))) float sy[IH * IP];
+    __shared__ __attribute__((aligned(16))) float hm[5 * IH * kTW];
+    __shared__ double red[1][kNT / 64];
+
+    const int tx = tiles_x(g);
+    const int bx = tile % tx, by = tile / tx;
+    const TIn *ref = static_cast<const TIn *>(fr.ref);
+    const TIn *dis = static_cast<const TIn *>(fr.dis);
+    const int W = g.dec_w, H = g.dec_h, MW = W - 10, MH = H - 10;
+    const int x0 = bx * kTW, y0 = by * kTH;
+
+    stage<kTW, kTH, kNT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
+    __syncthreads();
+    horizontal_moments<kTW, kTH, kNT>(sx, sy, taps, hm);
+    __syncthreads();
+
+    double acc[1] = {0.0};
+    vertical_moments<kTW, kTH, kNT, kRB>(hm, taps, x0, y0, MW, MH,
+                                         [&](int, int, float mx, float my, float xx, float yy, float xy) {
+        const float sxx = xx - mx * mx;
+        const float syy = yy - my * my;
+        const float sxy = xy - mx * my;
+        const float ux = mx + kMomentOffset;
+        const float uy = my + kMomentOffset;
+        // Numerator and denominator as mirror images (contraction is off),
+        // so identical planes give exactly 1.
+        const float num = (ux * uy + ux * uy + kC1) * (sxy + sxy + kC2);
+        const float den = (ux * ux + uy * uy + kC1) * (sxx + syy + kC2);
+        acc[0] += (double)(num / den);
+    });
+
+    block_sum<kNT, 1>(acc, red);
+    if (threadIdx.x == 0) fr.partials[tile] = acc[0];
+}
+
+__device__ __forceinline__ void finish_frame(const SsimFrame &fr, const StepGeometry &g) {
+    __shared__ double red[1][kNT / 64];
+    double tot[1];
+    sum_spans<kNT, 1>(fr.partials, tiles_x(g) * tiles_y(g), 0, tot, red);
+    if (threadIdx.x == 0) {
+        *fr.result = tot[0] / ((double)(g.dec_w - 10) * (double)(g.dec_h - 10));
+        __threadfence_system();
+    }
+}
+
+template <class Dec, typename TIn>
+__global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, int map_pitch, float unit,
+                                                 Taps taps) {
+    const int n = gridDim.x;
+    const int L = blockIdx.x;
+    const int per = n / 8;
+    const int Lp = L < per * 8 ? (L % 8) * per + L / 8 : L;  // XCD-aware order
+    const int dec_pf = r.n_dec ? r.dec_blocks_per_frame : 0;
+    const int dec_blocks = r.n_dec * dec_pf;
+    const int map_pf = tiles_x(g) * tiles_y(g);
+    const int map_blocks = r.n_map * map_pf;
+    if (Lp < dec_blocks) {
+        const int f = Lp / dec_pf;
+        Dec::run(r.dec.f[f], Lp - f * dec_pf, g);
+    } else if (Lp < dec_blocks + map_blocks) {
+        const int m = Lp - dec_blocks;
+        const int f = m / map_pf;
+        map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, taps);
+    } else {
+        finish_frame(r.fin.f[Lp - dec_blocks - map_blocks], g);
+    }
+}
+
+template <class Dec, typename TIn>
+hipError_t launch_step(StepRoles r, const StepGeometry &g, int map_pitch, float unit, const Taps &taps,
+                       hipStream_t stream) {
+    r.dec_blocks_per_frame = Dec::blocks_per_frame(g);
+    if (r.n_dec > 0 && r.dec_blocks_per_frame == 0) return hipErrorInvalidValue;
+    const long long blocks = (long long)r.n_dec * r.dec_blocks_per_frame +
+                             (long long)r.n_map * tiles_x(g) * tiles_y(g) + r.n_fin;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((ssim_step<Dec, TIn>), dim3((unsigned)blocks), dim3(kNT), 0, stream, r, g, map_pitch, unit,
+                       taps);
+    return hipGetLastError();
+}
+
+template <typename T, typename TIn>
+hipError_t launch_dec_pow2(int s, const StepRoles &r, const StepGeometry &g, int map_pitch, float unit,
+                           const Taps &taps, hipStream_t stream) {
+    switch (s) {
+    case 2: return launch_step<DecPow2<T, 2>, TIn>(r, g, map_pitch, unit, taps, stream);
+    case 4: return launch_step<DecPow2<T, 4>, TIn>(r, g, map_pitch, unit, taps, stream);
+    case 8: return launch_step<DecPow2<T, 8>, TIn>(r, g, map_pitch, unit, taps, stream);
+    case 16: return launch_step<DecPow2<T, 16>, TIn>(r, g, map_pitch, unit, taps, stream);
+    case 32: return launch_step<DecPow2<T, 32>, TIn>(r, g, map_pitch, unit, taps, stream);
+    case 64: return launch_step<DecPow2<T, 64>, TIn>(r, g, map_pitch, unit, taps, stream);
+    case 128: return launch_step<DecPow2<T, 128>, TIn>(r, g, map_pitch, unit, taps, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool decimate_fast_path(const DecimateBatch &b, int n, int w, int h, int bpc, int s) {
+    (void)h;
+    if (s < 2 || s > 128 || (s & (s - 1)) != 0) return false;
+    const int V = bpc == 8 ? 16 : 8;
+    if (w % V != 0) return false;
+    for (int i = 0; i < n; ++i)
+        if (((uintptr_t)b.f[i].ref | (uintptr_t)b.f[i].dis) & 15u) return false;
+    const int dec_w = (w + s - 1) / s;
+    // the last window's right half must lie inside the row (no right mirror)
+    if (w - s * (dec_w - 1) < s / 2) return false;
+    return true;
+}
+
+int ssim_partials(int W, int H) {
+    return ((W - 10 + kTW - 1) / kTW) * ((H - 10 + kTH - 1) / kTH);
+}
+
+hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind map_kind, int map_pitch, float unit,
+                            const Taps &taps, hipStream_t stream) {
+    if (r.n_dec < 0 || r.n_dec > kMaxBatch || r.n_map < 0 || r.n_map > kMaxBatch || r.n_fin < 0 ||
+        r.n_fin > kMaxBatch)
+        return hipErrorInvalidValue;
+    if (r.n_dec > 0) {
+        // Decimation feeds fp32 planes to the map role.
+        if (map_kind != IN_F32 && r.n_map > 0) return hipErrorInvalidValue;
+        const bool fast = decimate_fast_path(r.dec, r.n_dec, g.w, g.h, g.bpc, g.s);
+        if (g.bpc == 8) {
+            if (fast) return launch_dec_pow2<uint8_t, float>(g.s, r, g, map_pitch, unit, taps, stream);
+            return launch_step<DecGeneral<uint8_t>, float>(r, g, map_pitch, unit, taps, stream);
+        }
+        if (fast) return launch_dec_pow2<uint16_t, float>(g.s, r, g, map_pitch, unit, taps, stream);
+        return launch_step<DecGeneral<uint16_t>, float>(r, g, map_pitch, unit, taps, stream);
+    }
+    switch (map_kind) {
+    case IN_F32: return launch_step<DecNone, float>(r, g, map_pitch, unit, taps, stream);
+    case IN_U8: return launch_step<DecNone, uint8_t>(r, g, map_pitch, unit, taps, stream);
+    case IN_U16: return launch_step<DecNone, uint16_t>(r, g, map_pitch, unit, taps, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace vqm

@@ -29,45 +29,59 @@ enum InKind { IN_F32 = 0, IN_U8 = 1, IN_U16 = 2 };
 // it; it keeps E[x^2] small so fp32 loses less to cancellation.
 constexpr float kMomentOffset = 128.0f;
 
-// ---------------------------------------------------------------- decimation
+// ---------------------------------------------------------------- float_ssim
 
 struct DecimateFrame {
     const void *ref, *dis;       // raw planes, w x h, tightly packed
-    float *out_ref, *out_dis;    // dec_w x dec_h, row pitch opitch floats
+    float *out_ref, *out_dis;    // dec_w x dec_h, row pitch dec_pitch floats
 };
 struct DecimateBatch {
     DecimateFrame f[kMaxBatch];
 };
 
-// Whether the vectorised power-of-two kernel handles these frames
-// (otherwise the general kernel runs; both compute the same exact sums).
-bool decimate_fast_path(const DecimateBatch &b, int n, int w, int h, int bpc, int s);
-
-// Box low-pass and decimate both planes of n frames.  `tap` = 1.0f/(s*s)
-// formed by the caller.
-hipError_t launch_decimate(const DecimateBatch &b, int n, int w, int h, int bpc, int s, float tap,
-                           int dec_w, int dec_h, int opitch, hipStream_t stream);
-
-// ---------------------------------------------------------------- SSIM map
-
 struct SsimFrame {
-    const void *ref, *dis;       // planes with row pitch `pitch` samples
-    double *partials;            // >= ssim_partials(W, H) doubles
+    const void *ref, *dis;       // map input planes (decimated fp32, or raw at scale 1)
+    double *partials;            // >= ssim_partials(dec_w, dec_h) doubles
     double *result;              // device-visible address of the score (pinned host)
 };
 struct SsimBatch {
     SsimFrame f[kMaxBatch];
 };
 
-// Number of partial sums the SSIM-map kernel writes per frame.
+// Geometry shared by every role of a step launch.
+struct StepGeometry {
+    int w, h, bpc, s;            // raw frame and decimation factor
+    float tap;                   // 1.0f / (s * s), formed on the host
+    float post;                  // 2^-(2k + bpc - 8) when s = 2^k (power-of-two path)
+    int dec_w, dec_h, dec_pitch; // decimated plane (= raw size at scale 1)
+};
+
+// The three independent roles of one step launch: decimate one batch, map
+// another (whose decimated planes an earlier launch wrote), finish a third
+// (whose partials an earlier launch wrote).  Any role may be empty.
+struct StepRoles {
+    DecimateBatch dec;
+    int n_dec;
+    int dec_blocks_per_frame;    // filled in by the launcher
+    SsimBatch map;
+    int n_map;
+    SsimBatch fin;               // only partials and result are used
+    int n_fin;
+};
+
+// Whether the vectorised power-of-two decimation handles these frames
+// (otherwise the general path runs; both compute the same exact sums).
+bool decimate_fast_path(const DecimateBatch &b, int n, int w, int h, int bpc, int s);
+
+// Number of partial sums the map role writes per frame.
 int ssim_partials(int W, int H);
 
-// Fused 11x11 Gaussian moments + SSIM map + fixed-tree mean over the valid
-// (W-10) x (H-10) region, for n frames: the map kernel (one partial per
-// workgroup) and the finish kernel (one workgroup per frame).  Raw planes
-// (IN_U8 / IN_U16) are scaled by `unit` = 2^-(bpc-8).
-hipError_t launch_ssim(const SsimBatch &b, int n, InKind kind, int pitch, int W, int H, float unit,
-                       const Taps &taps, hipStream_t stream);
+// One step launch.  map_kind / map_pitch / unit describe the map role's
+// input: IN_F32 decimated planes (pitch dec_pitch, unit 1) whenever a
+// decimation role is present, raw samples (pitch w, unit 2^-(bpc-8)) at
+// scale 1.
+hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind map_kind, int map_pitch, float unit,
+                            const Taps &taps, hipStream_t stream);
 
 // ---------------------------------------------------------------- MS-SSIM
 

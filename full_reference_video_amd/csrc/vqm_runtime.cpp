@@ -19,6 +19,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <deque>
 #include <map>
 #include <memory>
 #include <string>
@@ -187,6 +188,15 @@ struct BatchEvent {
     bool completed = false;
 };
 
+// A float_ssim batch inside the step pipeline.
+enum Stage { STAGE_DECIMATED = 0, STAGE_MAPPED = 1 };
+struct PendingBatch {
+    Slot *sl[VQM_MAX_BATCH];
+    const void *in_r[VQM_MAX_BATCH], *in_d[VQM_MAX_BATCH];  // device-readable raw planes
+    int n = 0;
+    int stage = STAGE_DECIMATED;  // the last stage a launch already enqueued for it
+};
+
 struct TimedLaunch {
     hipEvent_t start, stop;
     int cls;
@@ -203,6 +213,9 @@ struct vqm_ctx {
     Slot slots[VQM_MAX_IN_FLIGHT];
     int head = 0, count = 0;
     std::vector<std::unique_ptr<BatchEvent>> batch_events;
+    // float_ssim batches whose pipeline (decimate -> map -> finish, one stage
+    // per step launch) has not finished yet, oldest first; same geometry.
+    std::deque<PendingBatch> pipeline;
     bool timing = false;
     std::vector<TimedLaunch> timed;      // recorded, not yet read
     std::vector<hipEvent_t> event_pool;  // free timing events
@@ -405,48 +418,95 @@ int drain_timing(vqm_ctx *ctx) {
         if (rc_) return rc_;                                                                       \
     } while (0)
 
-// float_ssim of n frames in slots sl[0..n-1] (same geometry) whose planes
-// are device-readable at in_r[i], in_d[i].  `decimate_only` stops after the
-// decimation (debug export).
-int enqueue_ssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r, const void *const *in_d,
-                 bool decimate_only) {
-    const Geometry &g = sl[0]->geo;
-    const float unit = ldexpf(1.0f, -(g.bpc - 8));
-    vqm::SsimBatch sb;
-    memset(&sb, 0, sizeof sb);
-    vqm::InKind kind = g.bpc == 8 ? vqm::IN_U8 : vqm::IN_U16;
-    int pitch = g.w;
-    if (g.s > 1 || decimate_only) {
-        vqm::DecimateBatch db;
-        memset(&db, 0, sizeof db);
-        for (int i = 0; i < n; ++i) {
-            db.f[i].ref = in_r[i];
-            db.f[i].dis = in_d[i];
-            db.f[i].out_ref = sl[i]->planes + sl[i]->off_ref[0];
-            db.f[i].out_dis = sl[i]->planes + sl[i]->off_dis[0];
-        }
-        const float tap = 1.0f / (float)(g.s * g.s);  // formed on the host
-        LAUNCH_TIMED(ctx, VQM_KERNEL_DECIMATE, n,
-                     vqm::launch_decimate(db, n, g.w, g.h, g.bpc, g.s, tap, g.dw, g.dh, g.dpitch, ctx->stream));
-        for (int i = 0; i < n; ++i) {
-            sb.f[i].ref = db.f[i].out_ref;
-            sb.f[i].dis = db.f[i].out_dis;
-        }
-        kind = vqm::IN_F32;
-        pitch = g.dpitch;
-    } else {
-        for (int i = 0; i < n; ++i) {
-            sb.f[i].ref = in_r[i];
-            sb.f[i].dis = in_d[i];
+vqm::StepGeometry step_geometry(const Geometry &g) {
+    vqm::StepGeometry sg;
+    sg.w = g.w;
+    sg.h = g.h;
+    sg.bpc = g.bpc;
+    sg.s = g.s;
+    sg.tap = 1.0f / (float)(g.s * g.s);  // formed on the host
+    int k = 0;
+    while ((1 << k) < g.s) ++k;
+    sg.post = ldexpf(1.0f, -(2 * k + g.bpc - 8));
+    sg.dec_w = g.dw;
+    sg.dec_h = g.dh;
+    sg.dec_pitch = g.dpitch;
+    return sg;
+}
+
+void fill_map_frame(vqm::SsimFrame &f, const PendingBatch &p, int i, bool decimated) {
+    Slot &s = *p.sl[i];
+    f.ref = decimated ? static_cast<const void *>(s.planes + s.off_ref[0]) : p.in_r[i];
+    f.dis = decimated ? static_cast<const void *>(s.planes + s.off_dis[0]) : p.in_d[i];
+    f.partials = s.partials;
+    f.result = s.result_dev;
+}
+
+// One step launch: decimate `fresh` (may be NULL; at scale 1 it is mapped
+// instead, since there is nothing to decimate), map the pipeline's decimated
+// batch, finish its mapped batch.  Batches finished by this launch get their
+// completion event and leave the pipeline.
+int step(vqm_ctx *ctx, PendingBatch *fresh) {
+    const Geometry &g = (fresh ? *fresh->sl[0] : *ctx->pipeline.front().sl[0]).geo;
+    const bool decimating = g.s > 1;
+    vqm::StepRoles r;
+    memset(&r, 0, sizeof r);
+    PendingBatch *to_map = nullptr, *to_finish = nullptr;
+    for (PendingBatch &p : ctx->pipeline) {
+        if (p.stage == STAGE_DECIMATED) to_map = &p;
+        else if (p.stage == STAGE_MAPPED) to_finish = &p;
+    }
+    if (fresh && !decimating) to_map = fresh;  // scale 1: mapped straight from the raw planes
+    if (fresh && decimating) {
+        r.n_dec = fresh->n;
+        for (int i = 0; i < fresh->n; ++i) {
+            Slot &s = *fresh->sl[i];
+            r.dec.f[i].ref = fresh->in_r[i];
+            r.dec.f[i].dis = fresh->in_d[i];
+            r.dec.f[i].out_ref = s.planes + s.off_ref[0];
+            r.dec.f[i].out_dis = s.planes + s.off_dis[0];
         }
     }
-    if (decimate_only) return 0;
-    for (int i = 0; i < n; ++i) {
-        sb.f[i].partials = sl[i]->partials;
-        sb.f[i].result = sl[i]->result_dev;
+    if (to_map) {
+        r.n_map = to_map->n;
+        for (int i = 0; i < to_map->n; ++i) fill_map_frame(r.map.f[i], *to_map, i, decimating);
     }
-    LAUNCH_TIMED(ctx, VQM_KERNEL_SSIM, n,
-                 vqm::launch_ssim(sb, n, kind, pitch, g.dw, g.dh, unit, ctx->taps, ctx->stream));
+    if (to_finish) {
+        r.n_fin = to_finish->n;
+        for (int i = 0; i < to_finish->n; ++i) fill_map_frame(r.fin.f[i], *to_finish, i, decimating);
+    }
+    const vqm::StepGeometry sg = step_geometry(g);
+    const vqm::InKind kind = decimating ? vqm::IN_F32 : (g.bpc == 8 ? vqm::IN_U8 : vqm::IN_U16);
+    const int pitch = decimating ? g.dpitch : g.w;
+    const float unit = decimating ? 1.0f : ldexpf(1.0f, -(g.bpc - 8));
+    const int cls = r.n_dec ? VQM_KERNEL_SSIM_STEP : VQM_KERNEL_SSIM_DRAIN;
+    LAUNCH_TIMED(ctx, cls, r.n_dec ? r.n_dec : r.n_map,
+                 vqm::launch_ssim_step(r, sg, kind, pitch, unit, ctx->taps, ctx->stream));
+    if (to_finish) {
+        BatchEvent *be = nullptr;
+        int rc = take_batch_event(ctx, &be);
+        if (rc) return rc;
+        HIP_TRY(hipEventRecord(be->ev, ctx->stream));
+        be->refs = to_finish->n;
+        be->completed = false;
+        for (int i = 0; i < to_finish->n; ++i) to_finish->sl[i]->batch = be;
+    }
+    // advance the stages (the finished batch is always the oldest)
+    if (to_finish) ctx->pipeline.pop_front();
+    if (to_map && to_map != fresh) to_map->stage = STAGE_MAPPED;
+    if (fresh) {
+        fresh->stage = decimating ? STAGE_DECIMATED : STAGE_MAPPED;
+        ctx->pipeline.push_back(*fresh);
+    }
+    return 0;
+}
+
+// Run step launches without new work until every pipelined batch is done.
+int drain(vqm_ctx *ctx) {
+    while (!ctx->pipeline.empty()) {
+        int rc = step(ctx, nullptr);
+        if (rc) return rc;
+    }
     return 0;
 }
 
@@ -511,27 +571,36 @@ int submit(vqm_ctx *ctx, int kind, const void *const *refs, const void *const *d
     rc = ensure_device(ctx);
     if (rc) return rc;
     const Geometry geo = make_geometry(kind, w, h, bpc);
-    Slot *sl[VQM_MAX_BATCH];
-    const void *in_r[VQM_MAX_BATCH], *in_d[VQM_MAX_BATCH];
-    for (int i = 0; i < n; ++i) {
-        sl[i] = &ctx->slots[(ctx->head + ctx->count + i) % VQM_MAX_IN_FLIGHT];
-        rc = prepare_slot(*sl[i], geo);
-        if (rc) return rc;
-        for (int k = 0; k < 16; ++k) sl[i]->result_host[k] = NAN;
-        rc = upload(ctx, *sl[i], refs[i], diss[i], &in_r[i], &in_d[i]);
+    // A batch of another geometry or metric first drains the pipeline.
+    if (!ctx->pipeline.empty() && !(kind == KIND_SSIM && ctx->pipeline.front().sl[0]->geo == geo)) {
+        rc = drain(ctx);
         if (rc) return rc;
     }
-    rc = kind == KIND_SSIM ? enqueue_ssim(ctx, sl, n, in_r, in_d, false) : enqueue_msssim(ctx, sl, n, in_r, in_d);
-    if (rc) return rc;
-    BatchEvent *be = nullptr;
-    rc = take_batch_event(ctx, &be);
-    if (rc) return rc;
-    HIP_TRY(hipEventRecord(be->ev, ctx->stream));
-    be->refs = n;
-    be->completed = false;
+    PendingBatch p;
+    p.n = n;
     for (int i = 0; i < n; ++i) {
-        sl[i]->batch = be;
-        sl[i]->kind = kind;
+        p.sl[i] = &ctx->slots[(ctx->head + ctx->count + i) % VQM_MAX_IN_FLIGHT];
+        rc = prepare_slot(*p.sl[i], geo);
+        if (rc) return rc;
+        for (int k = 0; k < 16; ++k) p.sl[i]->result_host[k] = NAN;
+        p.sl[i]->batch = nullptr;
+        p.sl[i]->kind = kind;
+        rc = upload(ctx, *p.sl[i], refs[i], diss[i], &p.in_r[i], &p.in_d[i]);
+        if (rc) return rc;
+    }
+    if (kind == KIND_SSIM) {
+        rc = step(ctx, &p);
+        if (rc) return rc;
+    } else {
+        rc = enqueue_msssim(ctx, p.sl, n, p.in_r, p.in_d);
+        if (rc) return rc;
+        BatchEvent *be = nullptr;
+        rc = take_batch_event(ctx, &be);
+        if (rc) return rc;
+        HIP_TRY(hipEventRecord(be->ev, ctx->stream));
+        be->refs = n;
+        be->completed = false;
+        for (int i = 0; i < n; ++i) p.sl[i]->batch = be;
     }
     ctx->count += n;
     return 0;
@@ -544,6 +613,11 @@ int collect(vqm_ctx *ctx, double *score, double *lcs) {
     int rc = ensure_device(ctx);
     if (rc) return rc;
     Slot &sl = ctx->slots[ctx->head];
+    if (sl.batch == nullptr) {
+        // Its batch is still in the step pipeline: drain it.
+        rc = drain(ctx);
+        if (rc) return rc;
+    }
     BatchEvent *be = sl.batch;
     if (!be->completed) {
         HIP_TRY(hipEventSynchronize(be->ev));  // the one wait of this frame (and its batch)
@@ -666,7 +740,7 @@ int score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *
         if (ctxs[c]->count != 0) return fail(-EINVAL, "context %d has frames in flight", c);
     }
     const int kind = metric == VQM_METRIC_MS_SSIM ? KIND_MSSSIM : KIND_SSIM;
-    if (lag <= 0) lag = 2 * batch;
+    if (lag <= 0) lag = 3 * batch;
     // FIFO of submitted frames: (context, frame index)
     std::vector<std::pair<int, int>> fifo;
     fifo.reserve(n);
@@ -679,13 +753,15 @@ int score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *
     for (int b0 = 0, k = 0; b0 < n && rc == 0; b0 += batch, ++k) {
         const int m = n - b0 < batch ? n - b0 : batch;
         const int c = k % nctx;
-        while (rc == 0 && front < fifo.size() &&
-               ((int)(fifo.size() - front) + m > lag + batch || ctxs[c]->count + m > VQM_MAX_IN_FLIGHT))
-            rc = collect_one();
+        // room in the target context (collecting the oldest frames first)
+        while (rc == 0 && front < fifo.size() && ctxs[c]->count + m > VQM_MAX_IN_FLIGHT) rc = collect_one();
         if (rc) break;
         rc = submit(ctxs[c], kind, refs + b0, diss + b0, m, w, h, bpc);
         if (rc) break;
         for (int i = 0; i < m; ++i) fifo.emplace_back(c, b0 + i);
+        // frames with `lag` later frames submitted are due
+        const int last = b0 + m - 1;
+        while (rc == 0 && front < fifo.size() && fifo[front].second <= last - lag) rc = collect_one();
     }
     while (front < fifo.size()) {
         const int rc2 = collect_one();
@@ -818,12 +894,23 @@ int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, in
         g.dh = (h + scale - 1) / scale;
         g.dpitch = round_up(g.dw, 64);
     }
+    rc = drain(ctx);
+    if (rc) return rc;
     Slot *sl = nullptr;
     const void *dref = nullptr, *ddis = nullptr;
     rc = debug_slot(ctx, g, ref, dis, &sl, &dref, &ddis);
     if (rc) return rc;
-    rc = enqueue_ssim(ctx, &sl, 1, &dref, &ddis, true);
-    if (rc) return rc;
+    // A step launch with the decimation role only (scale 1 included: the
+    // general path with tap 1 writes the sample values).
+    vqm::StepRoles r;
+    memset(&r, 0, sizeof r);
+    r.n_dec = 1;
+    r.dec.f[0].ref = dref;
+    r.dec.f[0].dis = ddis;
+    r.dec.f[0].out_ref = sl->planes + sl->off_ref[0];
+    r.dec.f[0].out_dis = sl->planes + sl->off_dis[0];
+    LAUNCH_TIMED(ctx, VQM_KERNEL_SSIM_STEP, 1,
+                 vqm::launch_ssim_step(r, step_geometry(g), vqm::IN_F32, g.dpitch, 1.0f, ctx->taps, ctx->stream));
     HIP_TRY(hipMemcpy2DAsync(out_ref, g.dw * sizeof(float), sl->planes + sl->off_ref[0], g.dpitch * sizeof(float),
                              g.dw * sizeof(float), g.dh, hipMemcpyDeviceToHost, ctx->stream));
     HIP_TRY(hipMemcpy2DAsync(out_dis, g.dw * sizeof(float), sl->planes + sl->off_dis[0], g.dpitch * sizeof(float),
@@ -841,6 +928,8 @@ int vqm_debug_pyramid(vqm_ctx *ctx, const void *ref, const void *dis, int w, int
     rc = gate_msssim(w, h);
     if (rc) return rc;
     const Geometry g = make_geometry(KIND_MSSSIM, w, h, bpc);
+    rc = drain(ctx);
+    if (rc) return rc;
     Slot *sl = nullptr;
     const void *dref = nullptr, *ddis = nullptr;
     rc = debug_slot(ctx, g, ref, dis, &sl, &dref, &ddis);

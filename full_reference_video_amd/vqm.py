@@ -21,13 +21,13 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvqm.so")
 
-VQM_MAX_IN_FLIGHT = 16
+VQM_MAX_IN_FLIGHT = 48
 VQM_MAX_BATCH = 8
 VQM_MSSSIM_LCS = 15
 VQM_METRIC_FLOAT_SSIM = 0
 VQM_METRIC_MS_SSIM = 1
-VQM_KERNEL_DECIMATE = 0
-VQM_KERNEL_SSIM = 1
+VQM_KERNEL_SSIM_STEP = 0
+VQM_KERNEL_SSIM_DRAIN = 1
 VQM_KERNEL_MSSSIM_LEVEL1 = 2
 VQM_KERNEL_MSSSIM_COARSE = 3
 

@@ -76,7 +76,7 @@ extern "C" {
 #endif
 
 /* Frames a context holds in flight between submit and collect. */
-#define VQM_MAX_IN_FLIGHT 16
+#define VQM_MAX_IN_FLIGHT 48
 
 /* Frames one batched submit may hand over (processed per kernel launch). */
 #define VQM_MAX_BATCH 8
@@ -165,8 +165,9 @@ enum vqm_metric { VQM_METRIC_FLOAT_SSIM = 0, VQM_METRIC_MS_SSIM = 1 };
  * are scored.  Frames go in batches of `batch` (1..VQM_MAX_BATCH) to the
  * nctx contexts in turn (several contexts on several streams let one
  * batch's SSIM kernels overlap the next batch's decimation); a frame is
- * collected — its one wait — once about `lag` later frames have been
- * submitted (lag <= 0: 2 * batch).  scores[i] receives frame i's score;
+ * collected — its one wait — once `lag` later frames have been submitted
+ * (lag <= 0: 3 * batch, which keeps a float_ssim batch's three pipeline
+ * stages enqueued before its result is awaited).  scores[i] receives frame i's score;
  * lcs (may be NULL) receives 15 doubles per frame for MS-SSIM.  The contexts
  * must have no frames in flight.  On error every submitted frame is still
  * collected before the call returns. */
@@ -181,10 +182,14 @@ VQM_API int vqm_score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const v
  * Switching clears the accumulated times. */
 VQM_API int vqm_ctx_set_timing(vqm_ctx *ctx, int enable);
 
-/* Kernel classes reported by vqm_ctx_kernel_time. */
+/* Kernel classes reported by vqm_ctx_kernel_time.  A float_ssim "step"
+ * launch decimates one batch while it maps the batch before and finishes the
+ * one before that; its frame count is the frames it decimates.  "Drain"
+ * launches only map and finish (the pipeline's tail, and every launch at
+ * scale 1); their frame count is the frames they map. */
 enum vqm_kernel_class {
-    VQM_KERNEL_DECIMATE = 0,
-    VQM_KERNEL_SSIM = 1,
+    VQM_KERNEL_SSIM_STEP = 0,
+    VQM_KERNEL_SSIM_DRAIN = 1,
     VQM_KERNEL_MSSSIM_LEVEL1 = 2,
     VQM_KERNEL_MSSSIM_COARSE = 3
 };

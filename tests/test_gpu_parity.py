@@ -363,3 +363,20 @@ def test_score_frames_loop_matches_single_frames(torch_cuda, metric, c):
     finally:
         for x in ctxs:
             x.close()
+
+
+def test_mixed_metrics_and_sizes_in_one_context(ctx):
+    # float_ssim batches sit in a three-stage pipeline; an MS-SSIM frame or a
+    # frame of another size in between must drain it without reordering.
+    a = synth.FrameSource(4).pair(1)
+    b = synth.FrameSource(5, w=640, h=360).pair(0)
+    c = synth.FrameSource(2).pair(3)
+    want = [vqm.vqm_ssim_frame(*a, 10), vqm.vqm_msssim_frame(*b, 8), vqm.vqm_ssim_frame(*c, 12)]
+    say("mixed metrics pipeline")
+    ctx.vqm_ssim_submit_batch([a[0]] * 3, [a[1]] * 3, 10)
+    ctx.vqm_msssim_submit(*b, 8)
+    ctx.vqm_ssim_submit(*c, 12)
+    ctx.vqm_ssim_submit_batch([a[0]] * 2, [a[1]] * 2, 10)
+    got = [ctx.vqm_collect() for _ in range(7)]
+    assert got == [want[0]] * 3 + [want[1], want[2]] + [want[0]] * 2
+    assert abs(want[0] - oracle.ssim(*a, 10)) <= TOL
