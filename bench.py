@@ -85,7 +85,21 @@ def main():
     ap.add_argument("--lag", type=int, default=0,
                     help="frames submitted after a frame before it is collected (0: 3*batch)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0: skip)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run torch's device-to-device copy of MIB MiB 20 times (a kernel of known "
+                         "traffic, to calibrate the FETCH_SIZE/WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 20}), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build scores on one GPU; --gpus {args.gpus} is not supported "

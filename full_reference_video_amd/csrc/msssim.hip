@@ -26,13 +26,13 @@
 namespace vqm {
 namespace {
 
-constexpr int kTW = 64, kTH = 16, kNT = 256, kRB = 4;
+constexpr int kTW = 32, kTH = 32, kNT = 256, kRB = 4;
 
 __constant__ double kBeta[5] = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333};
 
 template <int TW, int TH, int NT, int RB, typename TIn>
 __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int H, int next_pitch, float unit,
-                                               Taps taps) {
+                                               int vec4, Taps taps) {
     constexpr int IH = TH + 10, IP = in_pitch<TW>();
     __shared__ __attribute__((aligned(16))) float sx[IH * IP];
     __shared__ __attribute__((aligned(16))) float sy[IH * IP];
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
     const int MW = W - 10, MH = H - 10;
     const int x0 = bx * TW, y0 = by * TH;
 
-    stage<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
+    stage<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy, vec4 != 0);
     __syncthreads();
 
     // Next level: 2x2 means of this tile's share of the plane, from the
@@ -76,24 +76,27 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
     horizontal_moments<TW, TH, NT>(sx, sy, taps, hm);
     __syncthreads();
 
+    // Per pixel: l = 1 - (mx - my)^2 / (mux^2 + muy^2 + C1) and
+    // c = 1 - (sx - sy)^2 / (sx^2 + sy^2 + C2) (the mirrored quotients
+    // rewritten, exactly 1 for identical planes), s = (sxy + C3) / (sx sy + C3).
+    // A thread's few pixels are summed in fp32, the rest of the tree in fp64.
     constexpr float kC3 = kC2 / 2.0f;
-    double acc[3] = {0.0, 0.0, 0.0};
+    float pl = 0.0f, pc = 0.0f, ps = 0.0f;
     vertical_moments<TW, TH, NT, RB>(hm, taps, x0, y0, MW, MH,
                                      [&](int, int, float mx, float my, float xx, float yy, float xy) {
         const float vx = xx - mx * mx;
         const float vy = yy - my * my;
         const float cxy = xy - mx * my;
-        const float sdx = sqrtf(fmaxf(vx, 0.0f));
-        const float sdy = sqrtf(fmaxf(vy, 0.0f));
+        const float sdx = hw_sqrt(fmaxf(vx, 0.0f));
+        const float sdy = hw_sqrt(fmaxf(vy, 0.0f));
         const float ux = mx + kMomentOffset;
         const float uy = my + kMomentOffset;
-        const float l = (ux * uy + ux * uy + kC1) / (ux * ux + uy * uy + kC1);
-        const float cs = (sdx * sdy + sdx * sdy + kC2) / (sdx * sdx + sdy * sdy + kC2);
-        const float st = (cxy + kC3) / (sdx * sdy + kC3);
-        acc[0] += (double)l;
-        acc[1] += (double)cs;
-        acc[2] += (double)st;
+        const float dm = mx - my, ds = sdx - sdy;
+        pl += 1.0f - dm * dm * rcp(ux * ux + uy * uy + kC1);
+        pc += 1.0f - ds * ds * rcp(sdx * sdx + sdy * sdy + kC2);
+        ps += (cxy + kC3) * rcp(sdx * sdy + kC3);
     });
+    double acc[3] = {(double)pl, (double)pc, (double)ps};
 
     block_sum<NT, 3>(acc, red);
     if (threadIdx.x == 0) {
@@ -140,26 +143,26 @@ int ms_partials(int W, int H) {
 }
 
 hipError_t launch_ms_level(const MsBatch &b, int n, InKind kind, int pitch, int W, int H, int next_pitch,
-                           float unit, const Taps &taps, hipStream_t stream) {
+                           float unit, const Taps &taps, hipStream_t stream, const KernelTimer &timer) {
     if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
     const dim3 grid((W - 10 + kTW - 1) / kTW, (H - 10 + kTH - 1) / kTH, n);
+    const size_t bytes = kind == IN_F32 ? 4 : (kind == IN_U16 ? 2 : 1);
+    int vec4 = 1;
+    for (int i = 0; i < n; ++i)
+        if (!stage_vec4_ok(b.f[i].ref, pitch, bytes) || !stage_vec4_ok(b.f[i].dis, pitch, bytes)) vec4 = 0;
     switch (kind) {
     case IN_F32:
-        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, kRB, float>), grid, dim3(kNT), 0, stream, b, pitch, W, H, next_pitch,
-                           unit, taps);
-        break;
+        return launch_kernel(ms_level<kTW, kTH, kNT, kRB, float>, grid, dim3(kNT), stream, timer, b, pitch, W, H,
+                             next_pitch, unit, vec4, taps);
     case IN_U8:
-        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, kRB, uint8_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H,
-                           next_pitch, unit, taps);
-        break;
+        return launch_kernel(ms_level<kTW, kTH, kNT, kRB, uint8_t>, grid, dim3(kNT), stream, timer, b, pitch, W, H,
+                             next_pitch, unit, vec4, taps);
     case IN_U16:
-        hipLaunchKernelGGL((ms_level<kTW, kTH, kNT, kRB, uint16_t>), grid, dim3(kNT), 0, stream, b, pitch, W, H,
-                           next_pitch, unit, taps);
-        break;
+        return launch_kernel(ms_level<kTW, kTH, kNT, kRB, uint16_t>, grid, dim3(kNT), stream, timer, b, pitch, W,
+                             H, next_pitch, unit, vec4, taps);
     default:
         return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_ms_finish(const MsFinishBatch &b, int n, const MsLevels &lv, hipStream_t stream) {

@@ -84,14 +84,29 @@ __device__ __forceinline__ void stage_tile(const TIn *__restrict__ ref, const TI
     }
 }
 
-// The same for fp32 planes whose row pitch is a multiple of 4 floats (x0 is
-// a multiple of TW, itself a multiple of 4): 16-byte loads and LDS stores;
-// the ragged last chunk of a row is read element by element.
-template <int TW, int TH, int NT>
-__device__ __forceinline__ void stage_tile_f32x4(const float *__restrict__ ref, const float *__restrict__ dis,
-                                                 int pitch, int W, int H, int x0, int y0, float *sx, float *sy) {
+// Four consecutive samples at p (aligned to 4 samples), as floats on the
+// 8-bit scale.
+__device__ __forceinline__ float4 load4(const float *p, float) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 load4(const uint8_t *p, float unit) {
+    const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+    return make_float4((float)(v & 0xffu) * unit, (float)((v >> 8) & 0xffu) * unit,
+                       (float)((v >> 16) & 0xffu) * unit, (float)(v >> 24) * unit);
+}
+__device__ __forceinline__ float4 load4(const uint16_t *p, float unit) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    return make_float4((float)(v.x & 0xffffu) * unit, (float)(v.x >> 16) * unit, (float)(v.y & 0xffffu) * unit,
+                       (float)(v.y >> 16) * unit);
+}
+
+// The same with 4-sample loads, for planes whose base is aligned to 4
+// samples and whose row pitch is a multiple of 4 samples (x0, a multiple of
+// TW, is a multiple of 4).  The ragged last chunk of a row is read element
+// by element.
+template <int TW, int TH, int NT, typename TIn>
+__device__ __forceinline__ void stage_tile_x4(const TIn *__restrict__ ref, const TIn *__restrict__ dis, int pitch,
+                                              int W, int H, float unit, int x0, int y0, float *sx, float *sy) {
     constexpr int IW = TW + 10, IH = TH + 10, IP = in_pitch<TW>();
-    constexpr int QI = (IW + 3) / 4;  // 4-wide chunks per row (the last holds 2 columns)
+    constexpr int QI = (IW + 3) / 4;  // 4-wide chunks per row (the last one partly past the tile)
     constexpr int N = (IH * QI + NT - 1) / NT;
     const float off = kMomentOffset;
     float4 va[N], vb[N];
@@ -104,14 +119,14 @@ __device__ __forceinline__ void stage_tile_f32x4(const float *__restrict__ ref, 
         if (i < IH * QI && gy < H) {
             const size_t o = (size_t)gy * (size_t)pitch + (size_t)gx;
             if (gx + 3 < W && 4 * q + 3 < IW) {
-                va[k] = *reinterpret_cast<const float4 *>(ref + o);
-                vb[k] = *reinterpret_cast<const float4 *>(dis + o);
+                va[k] = load4(ref + o, unit);
+                vb[k] = load4(dis + o, unit);
             } else {
                 float ta[4], tb[4];
                 for (int e = 0; e < 4; ++e)
                     if (gx + e < W && 4 * q + e < IW) {
-                        ta[e] = ref[o + e];
-                        tb[e] = dis[o + e];
+                        ta[e] = load_sample(ref, o + e, unit);
+                        tb[e] = load_sample(dis, o + e, unit);
                     } else {
                         ta[e] = tb[e] = off;
                     }
@@ -133,16 +148,45 @@ __device__ __forceinline__ void stage_tile_f32x4(const float *__restrict__ ref, 
     }
 }
 
-// Stage with 16-byte loads when the input is an fp32 plane (its pitch is
-// then a multiple of 64 floats by construction), else element by element.
+// Stage with 4-sample loads when `vec4` says the planes allow it (fp32
+// planes always do: their pitch is a multiple of 64 floats), else element by
+// element.  `vec4` is uniform over the grid.
 template <int TW, int TH, int NT, typename TIn>
 __device__ __forceinline__ void stage(const TIn *__restrict__ ref, const TIn *__restrict__ dis, int pitch, int W,
-                                      int H, float unit, int x0, int y0, float *sx, float *sy) {
-    if constexpr (sizeof(TIn) == 4) {
-        stage_tile_f32x4<TW, TH, NT>(ref, dis, pitch, W, H, x0, y0, sx, sy);
-    } else {
+                                      int H, float unit, int x0, int y0, float *sx, float *sy, bool vec4) {
+    if (vec4)
+        stage_tile_x4<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
+    else
         stage_tile<TW, TH, NT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
-    }
+}
+
+// Whether planes at this address with this pitch (in samples) can be staged
+// with 4-sample loads.
+inline bool stage_vec4_ok(const void *p, int pitch, size_t sample_bytes) {
+    return ((uintptr_t)p % (4 * sample_bytes)) == 0 && pitch % 4 == 0;
+}
+
+// Hardware reciprocal and square root (v_rcp_f32, v_sqrt_f32: about 1 ulp).
+// The map terms are written so that identical planes stay exactly 1 anyway.
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+
+// Per-pixel SSIM term from the five (offset) moments, as
+// (1 - (mx - my)^2 / A)(1 - v / B) with A = mux^2 + muy^2 + C1,
+// B = sxx + syy + C2 and v = sxx + syy - 2 sxy (the variance of x - y):
+// algebraically ((2 mux muy + C1)(2 sxy + C2)) / (A B), and exactly 1 for
+// identical planes, since then mx = my and sxx = syy = sxy bit for bit.
+__device__ __forceinline__ float ssim_term(float mx, float my, float xx, float yy, float xy) {
+    const float sxx = xx - mx * mx;
+    const float syy = yy - my * my;
+    const float sxy = xy - mx * my;
+    const float ux = mx + kMomentOffset;
+    const float uy = my + kMomentOffset;
+    const float dm = mx - my;
+    const float A = ux * ux + uy * uy + kC1;
+    const float B = sxx + syy + kC2;
+    const float v = (sxx + syy) - (sxy + sxy);
+    return (1.0f - dm * dm * rcp(A)) * (1.0f - v * rcp(B));
 }
 
 // Horizontal pass: the five Gaussian moments (x, y, x^2, y^2, xy) of every

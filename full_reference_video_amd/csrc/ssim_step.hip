@@ -82,7 +82,7 @@ __host__ __device__ inline int tiles_y(const StepGeometry &g) { return (g.dec_h 
 
 template <typename TIn>
 __device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const StepGeometry &g, int pitch,
-                                         float unit, const Taps &taps) {
+                                         float unit, bool vec4, const Taps &taps) {
     constexpr int IH = kTH + 10, IP = in_pitch<kTW>();
     __shared__ __attribute__((aligned(16))) float sx[IH * IP];
     __shared__ __attribute__((aligned(16))) float sy[IH * IP];
@@ -96,26 +96,20 @@ __device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const St
     const int W = g.dec_w, H = g.dec_h, MW = W - 10, MH = H - 10;
     const int x0 = bx * kTW, y0 = by * kTH;
 
-    stage<kTW, kTH, kNT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy);
+    stage<kTW, kTH, kNT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy, vec4);
     __syncthreads();
     horizontal_moments<kTW, kTH, kNT>(sx, sy, taps, hm);
     __syncthreads();
 
-    double acc[1] = {0.0};
+    // A thread's few map pixels are summed in fp32, the rest of the tree in
+    // fp64.
+    float part = 0.0f;
     vertical_moments<kTW, kTH, kNT, kRB>(hm, taps, x0, y0, MW, MH,
                                          [&](int, int, float mx, float my, float xx, float yy, float xy) {
-        const float sxx = xx - mx * mx;
-        const float syy = yy - my * my;
-        const float sxy = xy - mx * my;
-        const float ux = mx + kMomentOffset;
-        const float uy = my + kMomentOffset;
-        // Numerator and denominator as mirror images (contraction is off),
-        // so identical planes give exactly 1.
-        const float num = (ux * uy + ux * uy + kC1) * (sxy + sxy + kC2);
-        const float den = (ux * ux + uy * uy + kC1) * (sxx + syy + kC2);
-        acc[0] += (double)(num / den);
+        part += ssim_term(mx, my, xx, yy, xy);
     });
 
+    double acc[1] = {(double)part};
     block_sum<kNT, 1>(acc, red);
     if (threadIdx.x == 0) fr.partials[tile] = acc[0];
 }
@@ -131,7 +125,7 @@ __device__ __forceinline__ void finish_frame(const SsimFrame &fr, const StepGeom
 }
 
 template <class Dec, typename TIn>
-__global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, int map_pitch, float unit,
+__global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, int map_pitch, float unit, int vec4,
                                                  Taps taps) {
     const int n = gridDim.x;
     const int L = blockIdx.x;
@@ -147,7 +141,7 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, in
     } else if (Lp < dec_blocks + map_blocks) {
         const int m = Lp - dec_blocks;
         const int f = m / map_pf;
-        map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, taps);
+        map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
     } else {
         finish_frame(r.fin.f[Lp - dec_blocks - map_blocks], g);
     }
@@ -155,29 +149,33 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, in
 
 template <class Dec, typename TIn>
 hipError_t launch_step(StepRoles r, const StepGeometry &g, int map_pitch, float unit, const Taps &taps,
-                       hipStream_t stream) {
+                       hipStream_t stream, const KernelTimer &timer) {
     r.dec_blocks_per_frame = Dec::blocks_per_frame(g);
     if (r.n_dec > 0 && r.dec_blocks_per_frame == 0) return hipErrorInvalidValue;
     const long long blocks = (long long)r.n_dec * r.dec_blocks_per_frame +
                              (long long)r.n_map * tiles_x(g) * tiles_y(g) + r.n_fin;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((ssim_step<Dec, TIn>), dim3((unsigned)blocks), dim3(kNT), 0, stream, r, g, map_pitch, unit,
-                       taps);
-    return hipGetLastError();
+    int vec4 = 1;
+    for (int i = 0; i < r.n_map; ++i)
+        if (!stage_vec4_ok(r.map.f[i].ref, map_pitch, sizeof(TIn)) ||
+            !stage_vec4_ok(r.map.f[i].dis, map_pitch, sizeof(TIn)))
+            vec4 = 0;
+    return launch_kernel(ssim_step<Dec, TIn>, dim3((unsigned)blocks), dim3(kNT), stream, timer, r, g, map_pitch,
+                         unit, vec4, taps);
 }
 
 template <typename T, typename TIn>
 hipError_t launch_dec_pow2(int s, const StepRoles &r, const StepGeometry &g, int map_pitch, float unit,
-                           const Taps &taps, hipStream_t stream) {
+                           const Taps &taps, hipStream_t stream, const KernelTimer &timer) {
     switch (s) {
-    case 2: return launch_step<DecPow2<T, 2>, TIn>(r, g, map_pitch, unit, taps, stream);
-    case 4: return launch_step<DecPow2<T, 4>, TIn>(r, g, map_pitch, unit, taps, stream);
-    case 8: return launch_step<DecPow2<T, 8>, TIn>(r, g, map_pitch, unit, taps, stream);
-    case 16: return launch_step<DecPow2<T, 16>, TIn>(r, g, map_pitch, unit, taps, stream);
-    case 32: return launch_step<DecPow2<T, 32>, TIn>(r, g, map_pitch, unit, taps, stream);
-    case 64: return launch_step<DecPow2<T, 64>, TIn>(r, g, map_pitch, unit, taps, stream);
-    case 128: return launch_step<DecPow2<T, 128>, TIn>(r, g, map_pitch, unit, taps, stream);
+    case 2: return launch_step<DecPow2<T, 2>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    case 4: return launch_step<DecPow2<T, 4>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    case 8: return launch_step<DecPow2<T, 8>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    case 16: return launch_step<DecPow2<T, 16>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    case 32: return launch_step<DecPow2<T, 32>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    case 64: return launch_step<DecPow2<T, 64>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    case 128: return launch_step<DecPow2<T, 128>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
     default: return hipErrorInvalidValue;
     }
 }
@@ -202,7 +200,7 @@ int ssim_partials(int W, int H) {
 }
 
 hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind map_kind, int map_pitch, float unit,
-                            const Taps &taps, hipStream_t stream) {
+                            const Taps &taps, hipStream_t stream, const KernelTimer &timer) {
     if (r.n_dec < 0 || r.n_dec > kMaxBatch || r.n_map < 0 || r.n_map > kMaxBatch || r.n_fin < 0 ||
         r.n_fin > kMaxBatch)
         return hipErrorInvalidValue;
@@ -211,16 +209,16 @@ hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind ma
         if (map_kind != IN_F32 && r.n_map > 0) return hipErrorInvalidValue;
         const bool fast = decimate_fast_path(r.dec, r.n_dec, g.w, g.h, g.bpc, g.s);
         if (g.bpc == 8) {
-            if (fast) return launch_dec_pow2<uint8_t, float>(g.s, r, g, map_pitch, unit, taps, stream);
-            return launch_step<DecGeneral<uint8_t>, float>(r, g, map_pitch, unit, taps, stream);
+            if (fast) return launch_dec_pow2<uint8_t, float>(g.s, r, g, map_pitch, unit, taps, stream, timer);
+            return launch_step<DecGeneral<uint8_t>, float>(r, g, map_pitch, unit, taps, stream, timer);
         }
-        if (fast) return launch_dec_pow2<uint16_t, float>(g.s, r, g, map_pitch, unit, taps, stream);
-        return launch_step<DecGeneral<uint16_t>, float>(r, g, map_pitch, unit, taps, stream);
+        if (fast) return launch_dec_pow2<uint16_t, float>(g.s, r, g, map_pitch, unit, taps, stream, timer);
+        return launch_step<DecGeneral<uint16_t>, float>(r, g, map_pitch, unit, taps, stream, timer);
     }
     switch (map_kind) {
-    case IN_F32: return launch_step<DecNone, float>(r, g, map_pitch, unit, taps, stream);
-    case IN_U8: return launch_step<DecNone, uint8_t>(r, g, map_pitch, unit, taps, stream);
-    case IN_U16: return launch_step<DecNone, uint16_t>(r, g, map_pitch, unit, taps, stream);
+    case IN_F32: return launch_step<DecNone, float>(r, g, map_pitch, unit, taps, stream, timer);
+    case IN_U8: return launch_step<DecNone, uint8_t>(r, g, map_pitch, unit, taps, stream, timer);
+    case IN_U16: return launch_step<DecNone, uint16_t>(r, g, map_pitch, unit, taps, stream, timer);
     default: return hipErrorInvalidValue;
     }
 }

@@ -9,6 +9,7 @@
 // ramp-up and drain per kernel that a batch of frames shares.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,6 +21,23 @@ constexpr int kMaxBatch = 8;
 struct Taps {
     float g[11];
 };
+
+// Optional kernel timing: when `start` is set, the launch records start and
+// stop on the events with the kernel's own begin and end (hipExtLaunchKernel),
+// not around the enqueue.
+struct KernelTimer {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename F, typename... Args>
+inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t stream, const KernelTimer &t,
+                                Args... args) {
+    if (t.start != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, t.start, t.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+    return hipGetLastError();
+}
 
 // Input sample kinds of the SSIM-map and MS-SSIM level kernels.
 enum InKind { IN_F32 = 0, IN_U8 = 1, IN_U16 = 2 };
@@ -81,7 +99,7 @@ int ssim_partials(int W, int H);
 // decimation role is present, raw samples (pitch w, unit 2^-(bpc-8)) at
 // scale 1.
 hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind map_kind, int map_pitch, float unit,
-                            const Taps &taps, hipStream_t stream);
+                            const Taps &taps, hipStream_t stream, const KernelTimer &timer);
 
 // ---------------------------------------------------------------- MS-SSIM
 
@@ -99,7 +117,7 @@ int ms_partials(int W, int H);
 // One MS-SSIM level of n frames: moments and the l/c/s partial sums of the
 // valid region, plus the exact 2x2 mean of the level into the next plane.
 hipError_t launch_ms_level(const MsBatch &b, int n, InKind kind, int pitch, int W, int H, int next_pitch,
-                           float unit, const Taps &taps, hipStream_t stream);
+                           float unit, const Taps &taps, hipStream_t stream, const KernelTimer &timer);
 
 struct MsFinishFrame {
     const double *partials;      // base of the frame's partials (all levels)

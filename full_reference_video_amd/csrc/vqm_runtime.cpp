@@ -366,7 +366,9 @@ int upload(vqm_ctx *ctx, Slot &sl, const void *ref, const void *dis, const void 
     return 0;
 }
 
-int timing_begin(vqm_ctx *ctx, TimedLaunch *tl, int cls, int frames) {
+// Events for one timed launch (taken from the pool); the launch itself
+// records them at the kernel's start and end.
+int timing_begin(vqm_ctx *ctx, TimedLaunch *tl, int cls, int frames, vqm::KernelTimer *kt) {
     if (!ctx->timing) return 0;
     for (int i = 0; i < 2; ++i) {
         hipEvent_t e;
@@ -380,15 +382,13 @@ int timing_begin(vqm_ctx *ctx, TimedLaunch *tl, int cls, int frames) {
     }
     tl->cls = cls;
     tl->frames = frames;
-    HIP_TRY(hipEventRecord(tl->start, ctx->stream));
+    kt->start = tl->start;
+    kt->stop = tl->stop;
     return 0;
 }
 
-int timing_end(vqm_ctx *ctx, TimedLaunch *tl) {
-    if (!ctx->timing) return 0;
-    HIP_TRY(hipEventRecord(tl->stop, ctx->stream));
-    ctx->timed.push_back(*tl);
-    return 0;
+void timing_end(vqm_ctx *ctx, TimedLaunch *tl) {
+    if (ctx->timing) ctx->timed.push_back(*tl);
 }
 
 int drain_timing(vqm_ctx *ctx) {
@@ -407,15 +407,17 @@ int drain_timing(vqm_ctx *ctx) {
     return 0;
 }
 
+// Launch `launch_expr` (which names the KernelTimer `timer_`), timed when
+// the context's timing is on.
 #define LAUNCH_TIMED(ctx, cls, frames, launch_expr)                                                \
     do {                                                                                           \
         TimedLaunch tl_;                                                                           \
-        int rc_ = timing_begin(ctx, &tl_, cls, frames);                                            \
+        vqm::KernelTimer timer_;                                                                   \
+        int rc_ = timing_begin(ctx, &tl_, cls, frames, &timer_);                                   \
         if (rc_) return rc_;                                                                       \
         hipError_t e_ = (launch_expr);                                                             \
         if (e_ != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e_));       \
-        rc_ = timing_end(ctx, &tl_);                                                               \
-        if (rc_) return rc_;                                                                       \
+        timing_end(ctx, &tl_);                                                                     \
     } while (0)
 
 vqm::StepGeometry step_geometry(const Geometry &g) {
@@ -481,7 +483,7 @@ int step(vqm_ctx *ctx, PendingBatch *fresh) {
     const float unit = decimating ? 1.0f : ldexpf(1.0f, -(g.bpc - 8));
     const int cls = r.n_dec ? VQM_KERNEL_SSIM_STEP : VQM_KERNEL_SSIM_DRAIN;
     LAUNCH_TIMED(ctx, cls, r.n_dec ? r.n_dec : r.n_map,
-                 vqm::launch_ssim_step(r, sg, kind, pitch, unit, ctx->taps, ctx->stream));
+                 vqm::launch_ssim_step(r, sg, kind, pitch, unit, ctx->taps, ctx->stream, timer_));
     if (to_finish) {
         BatchEvent *be = nullptr;
         int rc = take_batch_event(ctx, &be);
@@ -529,7 +531,7 @@ int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r
         const int next_pitch = j + 1 < kLevels ? g.lpitch[j + 1] : 0;
         LAUNCH_TIMED(ctx, j == 0 ? VQM_KERNEL_MSSSIM_LEVEL1 : VQM_KERNEL_MSSSIM_COARSE, n,
                      vqm::launch_ms_level(mb, n, kind, g.lpitch[j], g.lw[j], g.lh[j], next_pitch,
-                                          j == 0 ? unit : 1.0f, ctx->taps, ctx->stream));
+                                          j == 0 ? unit : 1.0f, ctx->taps, ctx->stream, timer_));
     }
     vqm::MsFinishBatch fb;
     memset(&fb, 0, sizeof fb);
@@ -910,7 +912,8 @@ int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, in
     r.dec.f[0].out_ref = sl->planes + sl->off_ref[0];
     r.dec.f[0].out_dis = sl->planes + sl->off_dis[0];
     LAUNCH_TIMED(ctx, VQM_KERNEL_SSIM_STEP, 1,
-                 vqm::launch_ssim_step(r, step_geometry(g), vqm::IN_F32, g.dpitch, 1.0f, ctx->taps, ctx->stream));
+                 vqm::launch_ssim_step(r, step_geometry(g), vqm::IN_F32, g.dpitch, 1.0f, ctx->taps, ctx->stream,
+                                           timer_));
     HIP_TRY(hipMemcpy2DAsync(out_ref, g.dw * sizeof(float), sl->planes + sl->off_ref[0], g.dpitch * sizeof(float),
                              g.dw * sizeof(float), g.dh, hipMemcpyDeviceToHost, ctx->stream));
     HIP_TRY(hipMemcpy2DAsync(out_dis, g.dw * sizeof(float), sl->planes + sl->off_dis[0], g.dpitch * sizeof(float),
