@@ -62,6 +62,8 @@ def lib():
         L.vqm_oracle_msssim_level_maps.argtypes = [fp, fp, ip, ip, dp, dp, dp]
         L.vqm_oracle_downsample.argtypes = [fp, ip, ip, fp]
         L.vqm_oracle_msssim.argtypes = [vp, vp, ip, ip, ip, dp, dp]
+        L.vqm_oracle_db.argtypes = [ctypes.c_double]
+        L.vqm_oracle_db.restype = ctypes.c_double
         for name in ("vqm_oracle_sample_plane", "vqm_oracle_decimate", "vqm_oracle_ssim_planes",
                      "vqm_oracle_ssim", "vqm_oracle_msssim_level_maps", "vqm_oracle_downsample",
                      "vqm_oracle_msssim"):
@@ -178,3 +180,8 @@ def msssim(ref: np.ndarray, dis: np.ndarray, bpc: int, want_lcs: bool = False):
 def msssim_rc(ref: np.ndarray, dis: np.ndarray, w: int, h: int, bpc: int) -> int:
     score = ctypes.c_double()
     return lib().vqm_oracle_msssim(_ptr(ref), _ptr(dis), w, h, bpc, ctypes.byref(score), None)
+
+
+def db(ssim: float) -> float:
+    """-10 log10(1 - ssim), +inf at ssim >= 1 ([ADR-1405] Consequences, enable_db)."""
+    return lib().vqm_oracle_db(float(ssim))

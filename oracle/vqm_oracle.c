@@ -348,3 +348,10 @@ done:
     free(ms);
     return rc;
 }
+
+double vqm_oracle_db(double ssim)
+{
+    if (!(ssim < 1.0))
+        return ssim >= 1.0 ? INFINITY : NAN;
+    return -10.0 * log10(1.0 - ssim);
+}

@@ -39,6 +39,9 @@
  *                       under 2x2 averaging (isolates level 1 and its
  *                       exponent), and a pixel-replicated frame whose levels
  *                       2..5 equal the original's levels 1..4.
+ *   db                — 10, 20, 30 dB at 1 - ssim = 1e-1, 1e-2, 1e-3; the
+ *                       ADR's sensitivity 4.34 / (1 - ssim) as a finite
+ *                       difference, and its 0.018 dB at 30 dB example.
  */
 #ifndef VQM_ORACLE_H
 #define VQM_ORACLE_H
@@ -106,6 +109,13 @@ int vqm_oracle_downsample(const float *in, int w, int h, float *out);
  * [R-1363] Finding 6 (per-scale l/c/s spans). */
 int vqm_oracle_msssim(const void *ref, const void *dis, int w, int h, int bpc,
                       double *score, double *lcs);
+
+/* A score in decibels, the enable_db form of float_ssim:
+ *   db = -10 log10(1 - ssim),  +inf when ssim >= 1 (reading: the page gives
+ * only the form's sensitivity, 4.34 / (1 - ssim) dB per unit of ssim, which is
+ * the derivative of this function; identical planes have no finite value).
+ * [ADR-1405] Consequences. */
+double vqm_oracle_db(double ssim);
 
 #ifdef __cplusplus
 }

@@ -380,3 +380,68 @@ def test_mixed_metrics_and_sizes_in_one_context(ctx):
     got = [ctx.vqm_collect() for _ in range(7)]
     assert got == [want[0]] * 3 + [want[1], want[2]] + [want[0]] * 2
     assert abs(want[0] - oracle.ssim(*a, 10)) <= TOL
+
+
+# ------------------------------------------------------------ full workloads, bench launch shape
+
+def _score_stream(torch, pairs, bpc, metric, batch=8, lag=24, n_streams=1):
+    """Score device-resident pairs the way bench.py times them: one context
+    per torch stream, batches of 8 frames per launch, each frame collected
+    three batches after its submit."""
+    dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
+    fs = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], bpc)
+    streams = [torch.cuda.Stream() for _ in range(n_streams)]
+    ctxs = [vqm.Context(0, s) for s in streams]
+    try:
+        first = vqm.vqm_score_frames(ctxs, metric, fs, batch, lag).tolist()
+        again = vqm.vqm_score_frames(ctxs, metric, fs, batch, lag).tolist()
+    finally:
+        for x in ctxs:
+            x.close()
+    assert again == first, "scores not bitwise repeatable"
+    return first
+
+
+@pytest.mark.parametrize("c", [2, 3, 4])
+def test_full_float_ssim_workload_in_bench_launch_shape(torch_cuda, c):
+    # Every frame of the workload at its full size, against the oracle frame
+    # by frame.
+    src = synth.FrameSource(c)
+    n = src.workload.frames
+    say(f"full workload {c}: generating {n} pairs {src.w}x{src.h} bpc {src.bpc}")
+    pairs = [src.pair(t) for t in range(n)]
+    say(f"full workload {c}: scoring on the GPU")
+    got = _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_FLOAT_SSIM)
+    say(f"full workload {c}: oracle")
+    worst = 0.0
+    for t, (r, d) in enumerate(pairs):
+        e = abs(got[t] - oracle.ssim(r, d, src.bpc))
+        worst = max(worst, e)
+        assert e <= TOL, (c, t, got[t])
+    say(f"full workload {c}: worst |gpu - oracle| {worst:.3g}")
+
+
+def test_full_float_ssim_2160p_two_streams(torch_cuda):
+    # The same 2160p frames rotated over two streams give the same bits.
+    src = synth.FrameSource(4)
+    pairs = [src.pair(t) for t in range(20)]
+    say("2160p two streams")
+    one = _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_FLOAT_SSIM)
+    two = _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_FLOAT_SSIM, n_streams=2)
+    assert one == two
+
+
+def test_full_msssim_workload_in_bench_launch_shape(torch_cuda):
+    # All 50 frames scored on the GPU; the oracle (seconds per 2160p frame)
+    # checks a sample of them, and every frame equals its single-frame call.
+    src = synth.FrameSource(5)
+    n = src.workload.frames
+    say(f"full MS-SSIM workload: generating {n} pairs")
+    pairs = [src.pair(t) for t in range(n)]
+    say("full MS-SSIM workload: scoring on the GPU")
+    got = _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_MS_SSIM)
+    single = [vqm.vqm_msssim_frame(r, d, src.bpc) for r, d in pairs]
+    assert got == single
+    for t in (0, 23, n - 1):
+        say(f"full MS-SSIM workload: oracle frame {t}")
+        assert abs(got[t] - oracle.msssim(*pairs[t], src.bpc)) <= TOL, (t, got[t])

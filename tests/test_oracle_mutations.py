@@ -34,6 +34,8 @@ MUTANTS = {
     "integer_division_scale": ("double r = round((double)m / 256.0);", "double r = (double)(m / 256);"),
     "valid_region_off_by_one": ("const int mw = w - (WIN - 1), mh = h - (WIN - 1);\n    double total",
                                 "const int mw = w - WIN, mh = h - WIN;\n    double total"),
+    "db_natural_log": ("return -10.0 * log10(1.0 - ssim);", "return -10.0 * log(1.0 - ssim);"),
+    "db_amplitude_form": ("return -10.0 * log10(1.0 - ssim);", "return -20.0 * log10(1.0 - ssim);"),
     "ceil_dim_as_floor": ("return (n + scale - 1) / scale;", "return n / scale > 0 ? n / scale : 1;"),
 }
 

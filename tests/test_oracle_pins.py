@@ -10,6 +10,7 @@ exponent) fails at least one of them.
 
 import errno
 import json
+import math
 import os
 from fractions import Fraction
 
@@ -436,3 +437,34 @@ def test_msssim_negative_structure_is_nan():
     ref = rng.integers(0, 256, size=(h, w)).astype(np.uint8)
     dis = (255 - ref).astype(np.uint8)  # anti-correlated at every level
     assert np.isnan(oracle.msssim(ref, dis, 8))
+
+
+# ------------------------------------------------------------ enable_db
+
+def test_db_decades():
+    # -10 log10(1 - ssim): each decade of 1 - ssim is 10 dB.
+    for k in range(1, 8):
+        assert abs(oracle.db(1.0 - 10.0 ** -k) - 10.0 * k) < 1e-6 * k
+    assert oracle.db(0.0) == 0.0
+    assert oracle.db(1.0) == float("inf")
+    assert oracle.db(1.0 + 1e-15) == float("inf")
+    assert oracle.db(-1.0) < 0.0
+
+
+def test_db_sensitivity_is_the_page_figure():
+    # The ADR's 4.34 / (1 - ssim) dB per unit of ssim is this function's
+    # derivative (10 / ln 10 = 4.3429...).
+    fact = FACTS["db_magnification"]
+    for s in (0.5, 0.9, 0.99, 0.999, 0.9999):
+        h = (1.0 - s) * 1e-4
+        d = (oracle.db(s + h) - oracle.db(s - h)) / (2 * h)
+        assert abs(d * (1.0 - s) - fact["factor"]) < 0.005
+        assert abs(d * (1.0 - s) - 10.0 / math.log(10.0)) < 1e-6
+    # The printed example: 0.018 dB at 30 dB is a linear residual of about
+    # 0.018 / 4343 = 4.1e-6, inside the 5e-5 score bar.
+    ex = fact["example"]
+    s30 = 1.0 - 10.0 ** (-ex["db"] / 10.0)
+    resid = ex["delta_db"] * (1.0 - s30) / fact["factor"]
+    assert abs(oracle.db(s30) - ex["db"]) < 1e-9
+    assert abs(oracle.db(s30 + resid) - ex["db"] - ex["delta_db"]) < 5e-4
+    assert resid < FACTS["score_tolerance"]["abs"]
