@@ -112,7 +112,7 @@ def cpu_baseline(host, wl, budget_s: float):
         fn(r, d, wl.bpc)
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 4 * len(host):
+        if el >= budget_s or n >= 40 * len(host):
             break
     return {"value": round(n / el, 3), "unit": "frames/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} frame pairs of {wl.name} (frames 0..{min(n, len(host)) - 1}, cycling), "

@@ -119,7 +119,12 @@ __device__ __forceinline__ void finish_frame(const SsimFrame &fr, const StepGeom
     double tot[1];
     sum_spans<kNT, 1>(fr.partials, tiles_x(g) * tiles_y(g), 0, tot, red);
     if (threadIdx.x == 0) {
-        *fr.result = tot[0] / ((double)(g.dec_w - 10) * (double)(g.dec_h - 10));
+        const double m = tot[0] / ((double)(g.dec_w - 10) * (double)(g.dec_h - 10));
+        fr.result[0] = m;
+        // The decibel form -10 log10(1 - ssim), +inf for a score of 1 or
+        // more ("ADR-1405: float_ssim_hip decimates on the device,
+        // bit-identical to the CPU", Consequences: enable_db).
+        fr.result[1] = m < 1.0 ? -10.0 * log10(1.0 - m) : (m >= 1.0 ? __builtin_inf() : m);
         __threadfence_system();
     }
 }

@@ -60,7 +60,7 @@ struct DecimateBatch {
 struct SsimFrame {
     const void *ref, *dis;       // map input planes (decimated fp32, or raw at scale 1)
     double *partials;            // >= ssim_partials(dec_w, dec_h) doubles
-    double *result;              // device-visible address of the score (pinned host)
+    double *result;              // device-visible address of [score, dB] (pinned host)
 };
 struct SsimBatch {
     SsimFrame f[kMaxBatch];

@@ -608,7 +608,7 @@ int submit(vqm_ctx *ctx, int kind, const void *const *refs, const void *const *d
     return 0;
 }
 
-int collect(vqm_ctx *ctx, double *score, double *lcs) {
+int collect(vqm_ctx *ctx, double *score, double *lcs, double *db) {
     if (!ctx) return fail(-EINVAL, "NULL context");
     if (!score) return fail(-EINVAL, "NULL score pointer");
     if (ctx->count == 0) return fail(-EAGAIN, "no frame in flight");
@@ -631,6 +631,7 @@ int collect(vqm_ctx *ctx, double *score, double *lcs) {
     sl.batch = nullptr;
     *score = sl.result_host[0];
     if (lcs && sl.kind == KIND_MSSSIM) memcpy(lcs, sl.result_host + 1, 15 * sizeof(double));
+    if (db) *db = sl.kind == KIND_SSIM ? sl.result_host[1] : NAN;
     return 0;
 }
 
@@ -708,7 +709,8 @@ int implicit_ctx(vqm_ctx **out) {
     return 0;
 }
 
-int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, double *score, double *lcs) {
+int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, double *score, double *lcs,
+             double *db) {
     if (!score) return fail(-EINVAL, "NULL score pointer");
     int rc = check_args(ref, dis, w, h, bpc);
     if (rc) return rc;
@@ -720,18 +722,19 @@ int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, 
     // The implicit context never holds frames between calls.
     rc = submit(ctx, kind, &ref, &dis, 1, w, h, bpc);
     if (rc) return rc;
-    double s = 0.0;
+    double s = 0.0, d = 0.0;
     double l[15];
-    rc = collect(ctx, &s, l);
+    rc = collect(ctx, &s, l, &d);
     if (rc) return rc;
     *score = s;
     if (lcs) memcpy(lcs, l, sizeof l);
+    if (db) *db = d;
     return 0;
 }
 
 // The pipelined scoring loop of vqm_score_frames.
 int score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *refs, const void *const *diss,
-                 int n, int w, int h, int bpc, int batch, int lag, double *scores, double *lcs) {
+                 int n, int w, int h, int bpc, int batch, int lag, double *scores, double *lcs, double *db) {
     if (!ctxs || nctx < 1 || !refs || !diss || !scores) return fail(-EINVAL, "NULL argument or no context");
     if (metric != VQM_METRIC_FLOAT_SSIM && metric != VQM_METRIC_MS_SSIM)
         return fail(-EINVAL, "unknown metric %d", metric);
@@ -750,7 +753,8 @@ int score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *
     int rc = 0;
     auto collect_one = [&]() -> int {
         const std::pair<int, int> e = fifo[front++];
-        return collect(ctxs[e.first], scores + e.second, lcs ? lcs + 15 * (size_t)e.second : nullptr);
+        return collect(ctxs[e.first], scores + e.second, lcs ? lcs + 15 * (size_t)e.second : nullptr,
+                       db ? db + e.second : nullptr);
     };
     for (int b0 = 0, k = 0; b0 < n && rc == 0; b0 += batch, ++k) {
         const int m = n - b0 < batch ? n - b0 : batch;
@@ -804,17 +808,22 @@ int vqm_ssim_geometry(int w, int h, int bpc, int *scale, int *dec_w, int *dec_h)
 }
 
 int vqm_ssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score) {
-    return blocking(KIND_SSIM, ref, dis, w, h, bpc, score, nullptr);
+    return blocking(KIND_SSIM, ref, dis, w, h, bpc, score, nullptr, nullptr);
+}
+
+int vqm_ssim_frame_db(const void *ref, const void *dis, int w, int h, int bpc, double *score, double *db) {
+    if (!db) return fail(-EINVAL, "NULL db pointer");
+    return blocking(KIND_SSIM, ref, dis, w, h, bpc, score, nullptr, db);
 }
 
 int vqm_msssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score) {
-    return blocking(KIND_MSSSIM, ref, dis, w, h, bpc, score, nullptr);
+    return blocking(KIND_MSSSIM, ref, dis, w, h, bpc, score, nullptr, nullptr);
 }
 
 int vqm_msssim_frame_lcs(const void *ref, const void *dis, int w, int h, int bpc, double *score,
                          double *lcs) {
     if (!lcs) return fail(-EINVAL, "NULL lcs pointer");
-    return blocking(KIND_MSSSIM, ref, dis, w, h, bpc, score, lcs);
+    return blocking(KIND_MSSSIM, ref, dis, w, h, bpc, score, lcs, nullptr);
 }
 
 int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out) { return create(device, hip_stream, out); }
@@ -839,11 +848,14 @@ int vqm_msssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *c
     return submit(ctx, KIND_MSSSIM, refs, dis, n, w, h, bpc);
 }
 
-int vqm_collect(vqm_ctx *ctx, double *score, double *lcs) { return collect(ctx, score, lcs); }
+int vqm_collect(vqm_ctx *ctx, double *score, double *lcs) { return collect(ctx, score, lcs, nullptr); }
+
+int vqm_collect_db(vqm_ctx *ctx, double *score, double *db) { return collect(ctx, score, nullptr, db); }
 
 int vqm_score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *refs, const void *const *dis,
-                     int n, int w, int h, int bpc, int batch, int lag, double *scores, double *lcs) {
-    return score_frames(ctxs, nctx, metric, refs, dis, n, w, h, bpc, batch, lag, scores, lcs);
+                     int n, int w, int h, int bpc, int batch, int lag, double *scores, double *lcs,
+                     double *db) {
+    return score_frames(ctxs, nctx, metric, refs, dis, n, w, h, bpc, batch, lag, scores, lcs, db);
 }
 
 int vqm_in_flight(const vqm_ctx *ctx) { return ctx ? ctx->count : 0; }

@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
         for n in ("vqm_ssim_frame", "vqm_msssim_frame"):
             getattr(L, n).argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_double_p]
         L.vqm_msssim_frame_lcs.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_double_p, c_double_p]
+        L.vqm_ssim_frame_db.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_double_p, c_double_p]
         L.vqm_ctx_create.argtypes = [c_int, c_void_p, ctypes.POINTER(c_void_p)]
         L.vqm_ctx_destroy.argtypes = [c_void_p]
         L.vqm_ctx_destroy.restype = None
@@ -69,9 +70,10 @@ def lib() -> ctypes.CDLL:
             getattr(L, n).argtypes = [c_void_p, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int,
                                       c_int, c_int, c_int]
         L.vqm_collect.argtypes = [c_void_p, c_double_p, c_double_p]
+        L.vqm_collect_db.argtypes = [c_void_p, c_double_p, c_double_p]
         L.vqm_score_frames.argtypes = [ctypes.POINTER(c_void_p), c_int, c_int, ctypes.POINTER(c_void_p),
                                        ctypes.POINTER(c_void_p), c_int, c_int, c_int, c_int, c_int, c_int,
-                                       c_double_p, c_double_p]
+                                       c_double_p, c_double_p, c_double_p]
         L.vqm_in_flight.argtypes = [c_void_p]
         L.vqm_ctx_set_timing.argtypes = [c_void_p, c_int]
         L.vqm_ctx_kernel_time.argtypes = [c_void_p, c_int, c_double_p, c_int_p, c_int_p]
@@ -143,6 +145,15 @@ def vqm_ssim_frame(ref, dis, bpc: int) -> float:
     score = ctypes.c_double()
     _check(lib().vqm_ssim_frame(pr, pd, w, h, int(bpc), ctypes.byref(score)), "vqm_ssim_frame")
     return score.value
+
+
+def vqm_ssim_frame_db(ref, dis, bpc: int):
+    """(score, decibel form) of one frame pair."""
+    pr, pd, w, h, _ = _pair(ref, dis, bpc)
+    score, db = ctypes.c_double(), ctypes.c_double()
+    _check(lib().vqm_ssim_frame_db(pr, pd, w, h, int(bpc), ctypes.byref(score), ctypes.byref(db)),
+           "vqm_ssim_frame_db")
+    return score.value, db.value
 
 
 def vqm_msssim_frame(ref, dis, bpc: int) -> float:
@@ -248,6 +259,14 @@ class Context:
             self._inflight.popleft()
         return (score.value, lcs) if want_lcs else score.value
 
+    def vqm_collect_db(self):
+        """(score, decibel form) of the oldest frame in flight."""
+        score, db = ctypes.c_double(), ctypes.c_double()
+        _check(lib().vqm_collect_db(self._h, ctypes.byref(score), ctypes.byref(db)), "vqm_collect_db")
+        if self._inflight:
+            self._inflight.popleft()
+        return score.value, db.value
+
     def vqm_in_flight(self) -> int:
         return lib().vqm_in_flight(self._h)
 
@@ -311,15 +330,19 @@ class FrameSet:
 
 
 def vqm_score_frames(ctxs, metric: int, frames: FrameSet, batch: int = 8, lag: int = 0,
-                     want_lcs: bool = False):
+                     want_lcs: bool = False, want_db: bool = False):
     """Score every frame of `frames` through the contexts `ctxs` (see the C
-    call); returns the scores (and the 15 MS-SSIM level means per frame)."""
+    call); returns the scores, followed by the 15 MS-SSIM level means per
+    frame when want_lcs and the decibel forms when want_db."""
     handles = (ctypes.c_void_p * len(ctxs))(*[c._h.value for c in ctxs])
     scores = np.empty(frames.n, np.float64)
     lcs = np.empty((frames.n, VQM_MSSSIM_LCS), np.float64) if want_lcs else None
+    db = np.empty(frames.n, np.float64) if want_db else None
     dp = ctypes.POINTER(ctypes.c_double)
     _check(lib().vqm_score_frames(handles, len(ctxs), int(metric), frames.refs, frames.diss, frames.n,
                                   frames.w, frames.h, frames.bpc, int(batch), int(lag),
                                   scores.ctypes.data_as(dp),
-                                  lcs.ctypes.data_as(dp) if want_lcs else None), "vqm_score_frames")
-    return (scores, lcs) if want_lcs else scores
+                                  lcs.ctypes.data_as(dp) if want_lcs else None,
+                                  db.ctypes.data_as(dp) if want_db else None), "vqm_score_frames")
+    out = (scores,) + ((lcs,) if want_lcs else ()) + ((db,) if want_db else ())
+    return out if len(out) > 1 else scores

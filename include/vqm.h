@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define VQM_ABI_VERSION 1
+#define VQM_ABI_VERSION 2
 
 /* Exported symbols (the library is built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -103,6 +103,14 @@ VQM_API int vqm_ssim_geometry(int w, int h, int bpc, int *scale, int *dec_w, int
  * the planes are already on the device), one device wait, one 8-byte result.
  * *score receives the mean SSIM. */
 VQM_API int vqm_ssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score);
+
+/* float_ssim plus its decibel form, blocking; as vqm_ssim_frame.  *db
+ * receives -10 log10(1 - score), +inf when the score is 1 or more
+ * ([ADR-1405] Consequences, enable_db: the form magnifies a score residual by
+ * 4.34 / (1 - score) dB).  The finish kernel computes it beside the score;
+ * the read-back is 16 bytes.  -EINVAL when db is NULL. */
+VQM_API int vqm_ssim_frame_db(const void *ref, const void *dis, int w, int h, int bpc, double *score,
+                              double *db);
 
 /* 5-scale MS-SSIM of one frame pair, blocking; as vqm_ssim_frame. */
 VQM_API int vqm_msssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score);
@@ -155,6 +163,11 @@ VQM_API int vqm_msssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const
  * untouched. */
 VQM_API int vqm_collect(vqm_ctx *ctx, double *score, double *lcs);
 
+/* As vqm_collect, with the decibel form of a float_ssim frame's score in *db
+ * (may be NULL; see vqm_ssim_frame_db).  An MS-SSIM frame has no decibel
+ * form here: *db receives NaN. */
+VQM_API int vqm_collect_db(vqm_ctx *ctx, double *score, double *db);
+
 /* Number of frames in flight. */
 VQM_API int vqm_in_flight(const vqm_ctx *ctx);
 
@@ -168,12 +181,14 @@ enum vqm_metric { VQM_METRIC_FLOAT_SSIM = 0, VQM_METRIC_MS_SSIM = 1 };
  * collected — its one wait — once `lag` later frames have been submitted
  * (lag <= 0: 3 * batch, which keeps a float_ssim batch's three pipeline
  * stages enqueued before its result is awaited).  scores[i] receives frame i's score;
- * lcs (may be NULL) receives 15 doubles per frame for MS-SSIM.  The contexts
+ * lcs (may be NULL) receives 15 doubles per frame for MS-SSIM;
+ * db (may be NULL) receives each float_ssim frame's decibel form (NaN for
+ * MS-SSIM).  The contexts
  * must have no frames in flight.  On error every submitted frame is still
  * collected before the call returns. */
 VQM_API int vqm_score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *refs,
                              const void *const *dis, int n, int w, int h, int bpc, int batch, int lag,
-                             double *scores, double *lcs);
+                             double *scores, double *lcs, double *db);
 
 /* ---- measurement and inspection ---- */
 

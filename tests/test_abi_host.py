@@ -47,7 +47,7 @@ def test_binding_names_match_the_abi():
 
 
 def test_abi_version():
-    assert vqm.vqm_abi_version() == 1
+    assert vqm.vqm_abi_version() == 2
 
 
 def test_scale_rule_matches_oracle():
@@ -100,7 +100,9 @@ def test_argument_errors_before_any_hip_call():
     assert L.vqm_msssim_frame(p, p, 175, 400, 8, ctypes.byref(s)) == -errno.ENOTSUP
     assert s.value == 123.0  # untouched on error
     assert "11x11" in vqm.vqm_last_error()
+    assert L.vqm_ssim_frame_db(p, p, 20, 20, 8, ctypes.byref(s), None) == -errno.EINVAL
     assert L.vqm_collect(None, ctypes.byref(s), None) == -errno.EINVAL
+    assert L.vqm_collect_db(None, ctypes.byref(s), None) == -errno.EINVAL
     assert L.vqm_ssim_submit(None, p, p, 20, 20, 8) == -errno.EINVAL
 
 

@@ -445,3 +445,46 @@ def test_full_msssim_workload_in_bench_launch_shape(torch_cuda):
     for t in (0, 23, n - 1):
         say(f"full MS-SSIM workload: oracle frame {t}")
         assert abs(got[t] - oracle.msssim(*pairs[t], src.bpc)) <= TOL, (t, got[t])
+
+
+# ------------------------------------------------------------ enable_db
+
+def _db_bound(s_gpu, s_oracle):
+    # The score bar carried through -10 log10(1 - s): its slope is
+    # 4.343 / (1 - s), largest at the larger score.
+    return 4.35 * TOL / (1.0 - max(s_gpu, s_oracle)) + 1e-9
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4])
+def test_ssim_db_form(ctx, c):
+    src = synth.FrameSource(c)
+    r, d = src.pair(0)
+    say(f"dB form config {c}")
+    s, db = vqm.vqm_ssim_frame_db(r, d, src.bpc)
+    assert s == vqm.vqm_ssim_frame(r, d, src.bpc)
+    # the device's log10 against the oracle's, on the same score
+    assert abs(db - oracle.db(s)) <= 1e-12 * max(1.0, db)
+    so = oracle.ssim(r, d, src.bpc)
+    assert abs(db - oracle.db(so)) <= _db_bound(s, so)
+
+
+def test_ssim_db_identity_and_pipeline(ctx, torch_cuda):
+    r, d = synth.FrameSource(2).pair(5)
+    s, db = vqm.vqm_ssim_frame_db(r, r, 12)
+    assert s == 1.0 and db == float("inf")
+    want = vqm.vqm_ssim_frame_db(r, d, 12)
+    b = synth.FrameSource(5, w=640, h=360).pair(0)
+    ctx.vqm_ssim_submit_batch([r, r], [d, r], 12)
+    ctx.vqm_msssim_submit(*b, 8)
+    assert ctx.vqm_collect_db() == want
+    assert ctx.vqm_collect_db() == (1.0, float("inf"))
+    ms, ms_db = ctx.vqm_collect_db()
+    assert ms == vqm.vqm_msssim_frame(*b, 8) and np.isnan(ms_db)
+    # the scoring loop's dB outputs
+    src = synth.FrameSource(3)
+    pairs = [src.pair(t) for t in range(11)]
+    dev = [(to_dev(torch_cuda, x), to_dev(torch_cuda, y)) for x, y in pairs]
+    fs = vqm.FrameSet([x for x, _ in dev], [y for _, y in dev], src.bpc)
+    scores, dbs = vqm.vqm_score_frames([ctx], vqm.VQM_METRIC_FLOAT_SSIM, fs, 4, 0, want_db=True)
+    for t, (x, y) in enumerate(pairs):
+        assert (scores[t], dbs[t]) == vqm.vqm_ssim_frame_db(x, y, src.bpc)
