@@ -170,16 +170,19 @@ __device__ __forceinline__ void pow2_wave(const DecimateFrame &fr, int wv, int Y
     constexpr int kRowUnroll = S <= 16 ? S : 4;
 #pragma unroll kRowUnroll
     for (int r = 0; r < S; ++r) {
-        const size_t row = (size_t)mirror(Y * S - HALF + r, h) * (size_t)w + (size_t)c0;
+        const size_t row = (size_t)mirror(Y * S - HALF + r, h) * (size_t)w;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            u32x4 a = {0u, 0u, 0u, 0u}, d = {0u, 0u, 0u, 0u};
             // w is a multiple of V, so a vector is wholly inside or outside
-            // the row; vectors outside hold only unused samples.
-            if (c0 + v * V < w) {
-                a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ref + row + v * V));
-                d = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(dis + row + v * V));
-            }
+            // the row.  A vector outside reads the row's last vector instead
+            // (no branch: a load under a per-lane branch makes the compiler
+            // wait for every earlier load first).  Its samples land only in
+            // the high half of the last chunk or in chunks past it, that is
+            // in outputs X >= dec_w, which are never stored: the fast path
+            // keeps the last window's low half inside the row.
+            const int col = c0 + v * V < w ? c0 + v * V : w - V;
+            const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ref + row + col));
+            const u32x4 d = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(dis + row + col));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 add_word<T, S, CPT>(a[q], v * V + q * Sh::SPW, lr, hr);

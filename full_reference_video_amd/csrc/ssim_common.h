@@ -20,18 +20,12 @@ namespace vqm {
 constexpr float kC1 = (float)((0.01 * 255.0) * (0.01 * 255.0));
 constexpr float kC2 = (float)((0.03 * 255.0) * (0.03 * 255.0));
 
-template <typename TIn>
-__device__ __forceinline__ float load_sample(const TIn *p, size_t i, float unit);
-template <>
-__device__ __forceinline__ float load_sample<float>(const float *p, size_t i, float) { return p[i]; }
-template <>
-__device__ __forceinline__ float load_sample<uint8_t>(const uint8_t *p, size_t i, float unit) {
-    return (float)p[i] * unit;
-}
-template <>
-__device__ __forceinline__ float load_sample<uint16_t>(const uint16_t *p, size_t i, float unit) {
-    return (float)p[i] * unit;
-}
+// Raw samples as loaded, and their value on the 8-bit scale.  Loads and
+// conversions are separate so that a tile's loads can all be in flight
+// before the first conversion waits for one.
+__device__ __forceinline__ float to_value(float v, float) { return v; }
+__device__ __forceinline__ float to_value(uint8_t v, float unit) { return (float)v * unit; }
+__device__ __forceinline__ float to_value(uint16_t v, float unit) { return (float)v * unit; }
 
 // Sum over the 64 lanes of a wave in a fixed butterfly order; every lane
 // ends with the same bits.
@@ -51,97 +45,102 @@ constexpr int in_pitch() {
 
 // Stage the (TH + 10) x (TW + 10) input tile of both planes at (x0, y0),
 // offset-subtracted, in LDS with row pitch in_pitch<TW>(); cells outside the
-// plane hold 0 (they feed only map pixels outside the valid region).  All of
-// a thread's global loads are issued before the first LDS store, so the tile
-// costs one memory latency, not one per element.
+// plane hold 0 (they feed only map pixels outside the valid region).  Every
+// load is unconditional — a cell outside the plane reads the plane's first
+// sample and is dropped afterwards — and all of them are issued before the
+// first conversion, so the tile costs one memory latency.  (A load under a
+// per-lane branch makes the compiler wait for every earlier load before it.)
 template <int TW, int TH, int NT, typename TIn>
 __device__ __forceinline__ void stage_tile(const TIn *__restrict__ ref, const TIn *__restrict__ dis,
                                            int pitch, int W, int H, float unit, int x0, int y0,
                                            float *sx, float *sy) {
     constexpr int IW = TW + 10, IH = TH + 10, IP = in_pitch<TW>();
     constexpr int N = (IH * IW + NT - 1) / NT;
-    float va[N], vb[N];
+    TIn ra[N], rb[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         const int i = threadIdx.x + k * NT;
         const int r = i / IW, c = i - r * IW;
         const int gx = x0 + c, gy = y0 + r;
-        va[k] = vb[k] = 0.0f;
-        if (i < IH * IW && gx < W && gy < H) {
-            const size_t o = (size_t)gy * (size_t)pitch + (size_t)gx;
-            va[k] = load_sample(ref, o, unit) - kMomentOffset;
-            vb[k] = load_sample(dis, o, unit) - kMomentOffset;
-        }
+        const bool in = i < IH * IW && gx < W && gy < H;
+        const size_t o = in ? (size_t)gy * (size_t)pitch + (size_t)gx : 0;
+        ra[k] = ref[o];
+        rb[k] = dis[o];
     }
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         const int i = threadIdx.x + k * NT;
         const int r = i / IW, c = i - r * IW;
+        const bool in = x0 + c < W && y0 + r < H;
         if (i < IH * IW) {
-            sx[r * IP + c] = va[k];
-            sy[r * IP + c] = vb[k];
+            sx[r * IP + c] = in ? to_value(ra[k], unit) - kMomentOffset : 0.0f;
+            sy[r * IP + c] = in ? to_value(rb[k], unit) - kMomentOffset : 0.0f;
         }
     }
 }
 
-// Four consecutive samples at p (aligned to 4 samples), as floats on the
-// 8-bit scale.
-__device__ __forceinline__ float4 load4(const float *p, float) { return *reinterpret_cast<const float4 *>(p); }
-__device__ __forceinline__ float4 load4(const uint8_t *p, float unit) {
-    const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
-    return make_float4((float)(v & 0xffu) * unit, (float)((v >> 8) & 0xffu) * unit,
-                       (float)((v >> 16) & 0xffu) * unit, (float)(v >> 24) * unit);
-}
-__device__ __forceinline__ float4 load4(const uint16_t *p, float unit) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(p);
-    return make_float4((float)(v.x & 0xffffu) * unit, (float)(v.x >> 16) * unit, (float)(v.y & 0xffffu) * unit,
-                       (float)(v.y >> 16) * unit);
-}
+// Four consecutive raw samples (aligned to 4 samples) as one load.
+template <typename TIn> struct Raw4;
+template <> struct Raw4<float> {
+    using type = float4;
+    __device__ static float4 load(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+    __device__ static float4 value(float4 v, float) { return v; }
+};
+template <> struct Raw4<uint8_t> {
+    using type = uint32_t;
+    __device__ static uint32_t load(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+    __device__ static float4 value(uint32_t v, float unit) {
+        return make_float4((float)(v & 0xffu) * unit, (float)((v >> 8) & 0xffu) * unit,
+                           (float)((v >> 16) & 0xffu) * unit, (float)(v >> 24) * unit);
+    }
+};
+template <> struct Raw4<uint16_t> {
+    using type = uint2;
+    __device__ static uint2 load(const uint16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+    __device__ static float4 value(uint2 v, float unit) {
+        return make_float4((float)(v.x & 0xffffu) * unit, (float)(v.x >> 16) * unit,
+                           (float)(v.y & 0xffffu) * unit, (float)(v.y >> 16) * unit);
+    }
+};
 
 // The same with 4-sample loads, for planes whose base is aligned to 4
 // samples and whose row pitch is a multiple of 4 samples (x0, a multiple of
-// TW, is a multiple of 4).  The ragged last chunk of a row is read element
-// by element.
+// TW, is a multiple of 4).  A chunk that starts inside a row lies wholly
+// inside the row's pitch (the pitch is a multiple of 4 samples), so it is
+// read whole and its samples past the plane's edge are dropped; a chunk
+// that starts outside the plane reads the plane's first chunk instead.
 template <int TW, int TH, int NT, typename TIn>
 __device__ __forceinline__ void stage_tile_x4(const TIn *__restrict__ ref, const TIn *__restrict__ dis, int pitch,
                                               int W, int H, float unit, int x0, int y0, float *sx, float *sy) {
     constexpr int IW = TW + 10, IH = TH + 10, IP = in_pitch<TW>();
     constexpr int QI = (IW + 3) / 4;  // 4-wide chunks per row (the last one partly past the tile)
     constexpr int N = (IH * QI + NT - 1) / NT;
-    const float off = kMomentOffset;
-    float4 va[N], vb[N];
+    using R4 = Raw4<TIn>;
+    typename R4::type ra[N], rb[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         const int i = threadIdx.x + k * NT;
         const int r = i / QI, q = i - r * QI;
         const int gx = x0 + 4 * q, gy = y0 + r;
-        va[k] = vb[k] = make_float4(off, off, off, off);  // cells outside the plane end up 0
-        if (i < IH * QI && gy < H) {
-            const size_t o = (size_t)gy * (size_t)pitch + (size_t)gx;
-            if (gx + 3 < W && 4 * q + 3 < IW) {
-                va[k] = load4(ref + o, unit);
-                vb[k] = load4(dis + o, unit);
-            } else {
-                float ta[4], tb[4];
-                for (int e = 0; e < 4; ++e)
-                    if (gx + e < W && 4 * q + e < IW) {
-                        ta[e] = load_sample(ref, o + e, unit);
-                        tb[e] = load_sample(dis, o + e, unit);
-                    } else {
-                        ta[e] = tb[e] = off;
-                    }
-                va[k] = make_float4(ta[0], ta[1], ta[2], ta[3]);
-                vb[k] = make_float4(tb[0], tb[1], tb[2], tb[3]);
-            }
-        }
+        const bool in = i < IH * QI && gy < H && gx < W;
+        const size_t o = in ? (size_t)gy * (size_t)pitch + (size_t)gx : 0;
+        ra[k] = R4::load(ref + o);
+        rb[k] = R4::load(dis + o);
     }
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         const int i = threadIdx.x + k * NT;
         const int r = i / QI, q = i - r * QI;
+        const int gx = x0 + 4 * q, gy = y0 + r;
         if (i < IH * QI) {
-            const float4 a = make_float4(va[k].x - off, va[k].y - off, va[k].z - off, va[k].w - off);
-            const float4 b = make_float4(vb[k].x - off, vb[k].y - off, vb[k].z - off, vb[k].w - off);
+            const float4 va = R4::value(ra[k], unit), vb = R4::value(rb[k], unit);
+            const bool row_in = gy < H;
+            const float off = kMomentOffset;
+            // cells outside the plane end up 0
+            const float4 a = make_float4(row_in && gx + 0 < W ? va.x - off : 0.0f, row_in && gx + 1 < W ? va.y - off : 0.0f,
+                                         row_in && gx + 2 < W ? va.z - off : 0.0f, row_in && gx + 3 < W ? va.w - off : 0.0f);
+            const float4 b = make_float4(row_in && gx + 0 < W ? vb.x - off : 0.0f, row_in && gx + 1 < W ? vb.y - off : 0.0f,
+                                         row_in && gx + 2 < W ? vb.z - off : 0.0f, row_in && gx + 3 < W ? vb.w - off : 0.0f);
             *reinterpret_cast<float4 *>(sx + r * IP + 4 * q) = a;
             *reinterpret_cast<float4 *>(sy + r * IP + 4 * q) = b;
         }

@@ -16,11 +16,13 @@
 // planes the previous launch wrote) and the finish of batch k-2 (whose
 // partials the previous launch wrote).  No workgroup waits for another, and
 // the map's ALU work overlaps the decimation's HBM streaming inside one grid
-// instead of costing a launch of its own.  The roles take contiguous ranges
-// of the XCD-remapped block order: [decimation | map | finish].
+// instead of costing a launch of its own.  Every XCD receives, in order, a
+// few map workgroups that loop over its eighth of the map tiles, its eighth
+// of the decimation workgroups, and its share of the finish workgroups
+// (StepLayout).
 //
-// Map role: one workgroup per TW x TH tile of the map.  The tile's
-// (TW+10) x (TH+10) input window of both planes is staged in LDS, the
+// Map role: a workgroup scores TW x TH tiles of the map one after another.
+// A tile's (TW+10) x (TH+10) input window of both planes is staged in LDS, the
 // horizontal 11-tap pass writes five moment planes to LDS (four columns per
 // thread step), and the vertical pass (four rows per thread step) forms the
 // moments of each map pixel and its SSIM term in fp32, with the mid-scale
@@ -129,36 +131,68 @@ __device__ __forceinline__ void finish_frame(const SsimFrame &fr, const StepGeom
     }
 }
 
+// Where each role sits in the grid.  The dispatcher hands workgroup L to
+// XCD L % 8; position q = L / 8 is the order in which that XCD receives its
+// workgroups.  Each XCD gets, in order: `map_wg` map workgroups that loop
+// over its eighth of the map tiles (so the map holds a few slots for the
+// whole launch instead of crowding out the decimation), then its eighth of
+// the decimation workgroups (short-lived, so the dispatcher balances them),
+// then its share of the finish workgroups.
+struct StepLayout {
+    int map_per_xcd;   // map tiles per XCD (contiguous ranges of the tile order)
+    int map_wg;        // map workgroups per XCD
+    int dec_per_xcd;   // decimation workgroups per XCD
+    int fin_per_xcd;   // finish workgroups per XCD
+};
+
+// Map workgroups per XCD: about one per CU.
+constexpr int kMapWorkgroupsPerXcd = 32;
+
 template <class Dec, typename TIn>
-__global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, int map_pitch, float unit, int vec4,
-                                                 Taps taps) {
-    const int n = gridDim.x;
-    const int L = blockIdx.x;
-    const int per = n / 8;
-    const int Lp = L < per * 8 ? (L % 8) * per + L / 8 : L;  // XCD-aware order
-    const int dec_pf = r.n_dec ? r.dec_blocks_per_frame : 0;
-    const int dec_blocks = r.n_dec * dec_pf;
-    const int map_pf = tiles_x(g) * tiles_y(g);
-    const int map_blocks = r.n_map * map_pf;
-    if (Lp < dec_blocks) {
-        const int f = Lp / dec_pf;
-        Dec::run(r.dec.f[f], Lp - f * dec_pf, g);
-    } else if (Lp < dec_blocks + map_blocks) {
-        const int m = Lp - dec_blocks;
-        const int f = m / map_pf;
-        map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
-    } else {
-        finish_frame(r.fin.f[Lp - dec_blocks - map_blocks], g);
+__global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, StepLayout lay, int map_pitch,
+                                                 float unit, int vec4, Taps taps) {
+    const int x = (int)(blockIdx.x & 7u);
+    int q = (int)(blockIdx.x >> 3);
+    if (q < lay.map_wg) {
+        const int map_pf = tiles_x(g) * tiles_y(g);
+        const int m0 = x * lay.map_per_xcd;
+        const int m1 = min(m0 + lay.map_per_xcd, r.n_map * map_pf);
+        for (int m = m0 + q; m < m1; m += lay.map_wg) {
+            const int f = m / map_pf;
+            map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+            __syncthreads();  // the next tile reuses the LDS
+        }
+        return;
     }
+    q -= lay.map_wg;
+    if (q < lay.dec_per_xcd) {
+        const int dec_pf = r.dec_blocks_per_frame;
+        const int d = x * lay.dec_per_xcd + q;
+        if (d < r.n_dec * dec_pf) {
+            const int f = d / dec_pf;
+            Dec::run(r.dec.f[f], d - f * dec_pf, g);
+        }
+        return;
+    }
+    q -= lay.dec_per_xcd;
+    const int fi = x * lay.fin_per_xcd + q;
+    if (fi < r.n_fin) finish_frame(r.fin.f[fi], g);
 }
 
 template <class Dec, typename TIn>
 hipError_t launch_step(StepRoles r, const StepGeometry &g, int map_pitch, float unit, const Taps &taps,
                        hipStream_t stream, const KernelTimer &timer) {
-    r.dec_blocks_per_frame = Dec::blocks_per_frame(g);
+    r.dec_blocks_per_frame = r.n_dec > 0 ? Dec::blocks_per_frame(g) : 0;
     if (r.n_dec > 0 && r.dec_blocks_per_frame == 0) return hipErrorInvalidValue;
-    const long long blocks = (long long)r.n_dec * r.dec_blocks_per_frame +
-                             (long long)r.n_map * tiles_x(g) * tiles_y(g) + r.n_fin;
+    const long long dec_blocks = (long long)r.n_dec * r.dec_blocks_per_frame;
+    const long long map_tiles = (long long)r.n_map * tiles_x(g) * tiles_y(g);
+    if (dec_blocks > 0x0fffffffLL || map_tiles > 0x0fffffffLL) return hipErrorInvalidValue;
+    StepLayout lay;
+    lay.map_per_xcd = (int)((map_tiles + 7) / 8);
+    lay.map_wg = min(kMapWorkgroupsPerXcd, lay.map_per_xcd);
+    lay.dec_per_xcd = (int)((dec_blocks + 7) / 8);
+    lay.fin_per_xcd = (r.n_fin + 7) / 8;
+    const long long blocks = 8LL * (lay.map_wg + lay.dec_per_xcd + lay.fin_per_xcd);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     int vec4 = 1;
@@ -166,8 +200,8 @@ hipError_t launch_step(StepRoles r, const StepGeometry &g, int map_pitch, float 
         if (!stage_vec4_ok(r.map.f[i].ref, map_pitch, sizeof(TIn)) ||
             !stage_vec4_ok(r.map.f[i].dis, map_pitch, sizeof(TIn)))
             vec4 = 0;
-    return launch_kernel(ssim_step<Dec, TIn>, dim3((unsigned)blocks), dim3(kNT), stream, timer, r, g, map_pitch,
-                         unit, vec4, taps);
+    return launch_kernel(ssim_step<Dec, TIn>, dim3((unsigned)blocks), dim3(kNT), stream, timer, r, g, lay,
+                         map_pitch, unit, vec4, taps);
 }
 
 template <typename T, typename TIn>
