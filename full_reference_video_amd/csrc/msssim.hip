@@ -34,10 +34,9 @@ template <int TW, int TH, int NT, int RB, typename TIn>
 __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int H, int next_pitch, float unit,
                                                int vec4, Taps taps) {
     constexpr int IH = TH + 10, IP = in_pitch<TW>();
-    __shared__ __attribute__((aligned(16))) float sx[IH * IP];
-    __shared__ __attribute__((aligned(16))) float sy[IH * IP];
-    __shared__ __attribute__((aligned(16))) float hm[5 * IH * TW];
+    __shared__ __attribute__((aligned(16))) float lds[tile_lds_floats<TW, TH>()];
     __shared__ double red[3][NT / 64];
+    float *sx = lds, *sy = lds + IH * IP;
 
     int bx, by, bz;
     xcd_block(bx, by, bz);
@@ -73,8 +72,7 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
         }
     }
 
-    horizontal_moments<TW, TH, NT>(sx, sy, taps, hm);
-    __syncthreads();
+    horizontal_moments_in_place<TW, TH, NT>(lds, taps);
 
     // Per pixel: l = 1 - (mx - my)^2 / (mux^2 + muy^2 + C1) and
     // c = 1 - (sx - sy)^2 / (sx^2 + sy^2 + C2) (the mirrored quotients
@@ -82,7 +80,7 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
     // A thread's few pixels are summed in fp32, the rest of the tree in fp64.
     constexpr float kC3 = kC2 / 2.0f;
     float pl = 0.0f, pc = 0.0f, ps = 0.0f;
-    vertical_moments<TW, TH, NT, RB>(hm, taps, x0, y0, MW, MH,
+    vertical_moments<TW, TH, NT, RB>(lds, taps, x0, y0, MW, MH,
                                      [&](int, int, float mx, float my, float xx, float yy, float xy) {
         const float vx = xx - mx * mx;
         const float vy = yy - my * my;

@@ -188,59 +188,97 @@ __device__ __forceinline__ float ssim_term(float mx, float my, float xx, float y
     return (1.0f - dm * dm * rcp(A)) * (1.0f - v * rcp(B));
 }
 
-// Horizontal pass: the five Gaussian moments (x, y, x^2, y^2, xy) of every
-// staged row at each of the TW map columns, into five LDS planes of
-// (TH + 10) x TW (hm + p * (TH + 10) * TW).  A thread forms four adjacent
-// columns at once from 14 inputs read with 16-byte LDS loads, and squares
-// each input once.  Per output the FMA order is k = 0..10.
+// LDS of a tile: the staged input (two planes, IH rows of pitch
+// in_pitch<TW>()) and, after the horizontal pass, the five horizontal moment
+// planes (IH x TW each) in the same buffer.
+template <int TW, int TH>
+constexpr int tile_lds_floats() {
+    constexpr int stage = 2 * (TH + 10) * in_pitch<TW>(), moments = 5 * (TH + 10) * TW;
+    return stage > moments ? stage : moments;
+}
+
+// Horizontal 11-tap pass of one item: four adjacent columns c0..c0+3 of
+// tile row r, for x, y, x^2, y^2 and xy, from the 14 inputs of each plane
+// (FMA order k = 0..10).
+__device__ __forceinline__ void h_item_load(const float *pa, const float *pb, float (&a)[14], float (&b)[14]) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const float4 va = *reinterpret_cast<const float4 *>(pa + 4 * q);
+        const float4 vb = *reinterpret_cast<const float4 *>(pb + 4 * q);
+        a[4 * q] = va.x; a[4 * q + 1] = va.y; a[4 * q + 2] = va.z; a[4 * q + 3] = va.w;
+        b[4 * q] = vb.x; b[4 * q + 1] = vb.y; b[4 * q + 2] = vb.z; b[4 * q + 3] = vb.w;
+    }
+    const float2 va = *reinterpret_cast<const float2 *>(pa + 12);
+    const float2 vb = *reinterpret_cast<const float2 *>(pb + 12);
+    a[12] = va.x; a[13] = va.y;
+    b[12] = vb.x; b[13] = vb.y;
+}
+
+__device__ __forceinline__ void h_item_compute(const float (&a)[14], const float (&b)[14], const Taps &taps,
+                                               float (&m)[5][4]) {
+    float aa[14], bb[14], ab[14];
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+        aa[i] = a[i] * a[i];
+        bb[i] = b[i] * b[i];
+        ab[i] = a[i] * b[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[0][j] = m[1][j] = m[2][j] = m[3][j] = m[4][j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 11; ++k) {
+        const float g = taps.g[k];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m[0][j] = fmaf(g, a[j + k], m[0][j]);
+            m[1][j] = fmaf(g, b[j + k], m[1][j]);
+            m[2][j] = fmaf(g, aa[j + k], m[2][j]);
+            m[3][j] = fmaf(g, bb[j + k], m[3][j]);
+            m[4][j] = fmaf(g, ab[j + k], m[4][j]);
+        }
+    }
+}
+
+// The horizontal pass over a staged tile, in place: the moment planes
+// (plane p at lds + p * IH * TW, row pitch TW) overwrite the staged input.
+// Each thread has at most two items (row, four columns).  It computes its
+// first item and reads the inputs of its second into registers, then the
+// workgroup synchronises, and only then are the moments written — so the
+// tile needs the LDS of the larger of the two layouts, not of both, and more
+// workgroups fit on a CU.  Ends with the moment planes visible to the whole
+// workgroup.
 template <int TW, int TH, int NT>
-__device__ __forceinline__ void horizontal_moments(const float *sx, const float *sy, const Taps &taps,
-                                                   float *hm) {
+__device__ __forceinline__ void horizontal_moments_in_place(float *lds, const Taps &taps) {
     constexpr int IH = TH + 10, IP = in_pitch<TW>(), QW = TW / 4, PL = IH * TW;
-    for (int it = threadIdx.x; it < IH * QW; it += NT) {
-        const int r = it / QW, c0 = (it - r * QW) * 4;
-        float a[14], b[14];
-        const float *pa = sx + r * IP + c0, *pb = sy + r * IP + c0;
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const float4 va = *reinterpret_cast<const float4 *>(pa + 4 * q);
-            const float4 vb = *reinterpret_cast<const float4 *>(pb + 4 * q);
-            a[4 * q] = va.x; a[4 * q + 1] = va.y; a[4 * q + 2] = va.z; a[4 * q + 3] = va.w;
-            b[4 * q] = vb.x; b[4 * q + 1] = vb.y; b[4 * q + 2] = vb.z; b[4 * q + 3] = vb.w;
-        }
-        {
-            const float2 va = *reinterpret_cast<const float2 *>(pa + 12);
-            const float2 vb = *reinterpret_cast<const float2 *>(pb + 12);
-            a[12] = va.x; a[13] = va.y;
-            b[12] = vb.x; b[13] = vb.y;
-        }
-        float aa[14], bb[14], ab[14];
-#pragma unroll
-        for (int i = 0; i < 14; ++i) {
-            aa[i] = a[i] * a[i];
-            bb[i] = b[i] * b[i];
-            ab[i] = a[i] * b[i];
-        }
-        float m[5][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) m[0][j] = m[1][j] = m[2][j] = m[3][j] = m[4][j] = 0.f;
-#pragma unroll
-        for (int k = 0; k < 11; ++k) {
-            const float g = taps.g[k];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                m[0][j] = fmaf(g, a[j + k], m[0][j]);
-                m[1][j] = fmaf(g, b[j + k], m[1][j]);
-                m[2][j] = fmaf(g, aa[j + k], m[2][j]);
-                m[3][j] = fmaf(g, bb[j + k], m[3][j]);
-                m[4][j] = fmaf(g, ab[j + k], m[4][j]);
-            }
-        }
-        const int o = r * TW + c0;
+    constexpr int ITEMS = IH * QW;
+    static_assert(ITEMS <= 2 * NT, "at most two horizontal items per thread");
+    const float *sx = lds, *sy = lds + IH * IP;
+    const int i1 = threadIdx.x, i2 = threadIdx.x + NT;
+    const bool has1 = i1 < ITEMS, has2 = i2 < ITEMS;
+    const int r1 = i1 / QW, c1 = (i1 - r1 * QW) * 4;
+    const int r2 = i2 / QW, c2 = (i2 - r2 * QW) * 4;
+    float m[5][4];
+    float a[14], b[14];
+    if (has1) {
+        h_item_load(sx + r1 * IP + c1, sy + r1 * IP + c1, a, b);
+        h_item_compute(a, b, taps, m);
+    }
+    if (has2) h_item_load(sx + r2 * IP + c2, sy + r2 * IP + c2, a, b);
+    __syncthreads();  // every read of the staged tile is done
+    if (has1) {
+        const int o = r1 * TW + c1;
 #pragma unroll
         for (int p = 0; p < 5; ++p)
-            *reinterpret_cast<float4 *>(hm + p * PL + o) = make_float4(m[p][0], m[p][1], m[p][2], m[p][3]);
+            *reinterpret_cast<float4 *>(lds + p * PL + o) = make_float4(m[p][0], m[p][1], m[p][2], m[p][3]);
     }
+    if (has2) {
+        h_item_compute(a, b, taps, m);
+        const int o = r2 * TW + c2;
+#pragma unroll
+        for (int p = 0; p < 5; ++p)
+            *reinterpret_cast<float4 *>(lds + p * PL + o) = make_float4(m[p][0], m[p][1], m[p][2], m[p][3]);
+    }
+    __syncthreads();
 }
 
 // Vertical pass: for RB stacked map rows of one tile column at a time, the

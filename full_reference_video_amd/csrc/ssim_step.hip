@@ -23,7 +23,7 @@
 //
 // Map role: a workgroup scores TW x TH tiles of the map one after another.
 // A tile's (TW+10) x (TH+10) input window of both planes is staged in LDS, the
-// horizontal 11-tap pass writes five moment planes to LDS (four columns per
+// horizontal 11-tap pass writes five moment planes over it (four columns per
 // thread step), and the vertical pass (four rows per thread step) forms the
 // moments of each map pixel and its SSIM term in fp32, with the mid-scale
 // offset removed first so E[x^2] - mu^2 cancels less.  Each thread adds its
@@ -86,10 +86,9 @@ template <typename TIn>
 __device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const StepGeometry &g, int pitch,
                                          float unit, bool vec4, const Taps &taps) {
     constexpr int IH = kTH + 10, IP = in_pitch<kTW>();
-    __shared__ __attribute__((aligned(16))) float sx[IH * IP];
-    __shared__ __attribute__((aligned(16))) float sy[IH * IP];
-    __shared__ __attribute__((aligned(16))) float hm[5 * IH * kTW];
+    __shared__ __attribute__((aligned(16))) float lds[tile_lds_floats<kTW, kTH>()];
     __shared__ double red[1][kNT / 64];
+    float *sx = lds, *sy = lds + IH * IP;
 
     const int tx = tiles_x(g);
     const int bx = tile % tx, by = tile / tx;
@@ -100,13 +99,12 @@ __device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const St
 
     stage<kTW, kTH, kNT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy, vec4);
     __syncthreads();
-    horizontal_moments<kTW, kTH, kNT>(sx, sy, taps, hm);
-    __syncthreads();
+    horizontal_moments_in_place<kTW, kTH, kNT>(lds, taps);
 
     // A thread's few map pixels are summed in fp32, the rest of the tree in
     // fp64.
     float part = 0.0f;
-    vertical_moments<kTW, kTH, kNT, kRB>(hm, taps, x0, y0, MW, MH,
+    vertical_moments<kTW, kTH, kNT, kRB>(lds, taps, x0, y0, MW, MH,
                                          [&](int, int, float mx, float my, float xx, float yy, float xy) {
         part += ssim_term(mx, my, xx, yy, xy);
     });
@@ -157,6 +155,7 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
         const int map_pf = tiles_x(g) * tiles_y(g);
         const int m0 = x * lay.map_per_xcd;
         const int m1 = min(m0 + lay.map_per_xcd, r.n_map * map_pf);
+#pragma unroll 1
         for (int m = m0 + q; m < m1; m += lay.map_wg) {
             const int f = m / map_pf;
             map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
