@@ -26,7 +26,9 @@
 namespace vqm {
 namespace {
 
-constexpr int kTW = 32, kTH = 32, kNT = 256, kRB = 4;
+// 32 x 64 tiles, 512 threads: the horizontal pass computes 74 rows for 64
+// map rows (16 % halo, against 31 % for 32-row tiles).
+constexpr int kTW = 32, kTH = 64, kNT = 512, kRB = 4;
 
 __constant__ double kBeta[5] = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333};
 
@@ -76,8 +78,10 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
 
     // Per pixel: l = 1 - (mx - my)^2 / (mux^2 + muy^2 + C1) and
     // c = 1 - (sx - sy)^2 / (sx^2 + sy^2 + C2) (the mirrored quotients
-    // rewritten, exactly 1 for identical planes), s = (sxy + C3) / (sx sy + C3).
-    // A thread's few pixels are summed in fp32, the rest of the tree in fp64.
+    // rewritten, exactly 1 for identical planes), s = (sxy + C3) / (sx sy + C3),
+    // the three quotients from one reciprocal of the product of the
+    // denominators (at most ~1e14, far inside fp32 range).  A thread's few
+    // pixels and then its wave are summed in fp32, the waves in fp64.
     constexpr float kC3 = kC2 / 2.0f;
     float pl = 0.0f, pc = 0.0f, ps = 0.0f;
     vertical_moments<TW, TH, NT, RB>(lds, taps, x0, y0, MW, MH,
@@ -90,13 +94,17 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
         const float ux = mx + kMomentOffset;
         const float uy = my + kMomentOffset;
         const float dm = mx - my, ds = sdx - sdy;
-        pl += 1.0f - dm * dm * rcp(ux * ux + uy * uy + kC1);
-        pc += 1.0f - ds * ds * rcp(sdx * sdx + sdy * sdy + kC2);
-        ps += (cxy + kC3) * rcp(sdx * sdy + kC3);
+        const float d1 = ux * ux + uy * uy + kC1;
+        const float d2 = sdx * sdx + sdy * sdy + kC2;
+        const float d3 = sdx * sdy + kC3;
+        const float r = rcp(d1 * d2 * d3);
+        pl += 1.0f - dm * dm * ((d2 * d3) * r);
+        pc += 1.0f - ds * ds * ((d1 * d3) * r);
+        ps += (cxy + kC3) * ((d1 * d2) * r);
     });
-    double acc[3] = {(double)pl, (double)pc, (double)ps};
-
-    block_sum<NT, 3>(acc, red);
+    const float terms[3] = {pl, pc, ps};
+    double acc[3];
+    block_sum_terms<NT, 3>(terms, red, acc);
     if (threadIdx.x == 0) {
         const int nb = gridDim.x * gridDim.y;
         const int slot = by * gridDim.x + bx;

@@ -185,7 +185,9 @@ __device__ __forceinline__ float ssim_term(float mx, float my, float xx, float y
     const float A = ux * ux + uy * uy + kC1;
     const float B = sxx + syy + kC2;
     const float v = (sxx + syy) - (sxy + sxy);
-    return (1.0f - dm * dm * rcp(A)) * (1.0f - v * rcp(B));
+    // One reciprocal for both quotients (A * B stays far inside fp32 range).
+    const float r = rcp(A * B);
+    return (1.0f - dm * dm * (B * r)) * (1.0f - v * (A * r));
 }
 
 // LDS of a tile: the staged input (two planes, IH rows of pitch
@@ -331,6 +333,37 @@ __device__ __forceinline__ void block_sum(double (&v)[NV], double (*red)[NT / 64
             double t = 0.0;
             for (int w = 0; w < NT / 64; ++w) t += red[j][w];
             v[j] = t;
+        }
+    }
+}
+
+// Sum over the 64 lanes of a wave in fp32, in the same fixed butterfly order.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Workgroup sum of a tile's map terms: each thread's few terms and then the
+// wave's 64 lanes are summed in fp32 (a wave holds a few hundred terms, each
+// of magnitude at most 1, so the fp32 sum is good to about 1e-5 of a term),
+// the waves in index order in fp64.  Fixed shape; `out` is valid in thread 0
+// only and `red` may be reused after the next __syncthreads.
+template <int NT, int NV>
+__device__ __forceinline__ void block_sum_terms(const float (&v)[NV], double (*red)[NT / 64], double (&out)[NV]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const float w = wave_sum_f32(v[j]);
+        if (lane == 0) red[j][wave] = (double)w;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            double t = 0.0;
+            for (int w = 0; w < NT / 64; ++w) t += red[j][w];
+            out[j] = t;
         }
     }
 }

@@ -101,16 +101,17 @@ __device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const St
     __syncthreads();
     horizontal_moments_in_place<kTW, kTH, kNT>(lds, taps);
 
-    // A thread's few map pixels are summed in fp32, the rest of the tree in
-    // fp64.
+    // A thread's few map pixels and then its wave are summed in fp32, the
+    // waves in fp64.
     float part = 0.0f;
     vertical_moments<kTW, kTH, kNT, kRB>(lds, taps, x0, y0, MW, MH,
                                          [&](int, int, float mx, float my, float xx, float yy, float xy) {
         part += ssim_term(mx, my, xx, yy, xy);
     });
 
-    double acc[1] = {(double)part};
-    block_sum<kNT, 1>(acc, red);
+    const float terms[1] = {part};
+    double acc[1];
+    block_sum_terms<kNT, 1>(terms, red, acc);
     if (threadIdx.x == 0) fr.partials[tile] = acc[0];
 }
 
