@@ -79,30 +79,34 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
     // Per pixel: l = 1 - (mx - my)^2 / (mux^2 + muy^2 + C1) and
     // c = 1 - (sx - sy)^2 / (sx^2 + sy^2 + C2) (the mirrored quotients
     // rewritten, exactly 1 for identical planes), s = (sxy + C3) / (sx sy + C3),
-    // the three quotients from one reciprocal of the product of the
-    // denominators (at most ~1e14, far inside fp32 range).  A thread's few
-    // pixels and then its wave are summed in fp32, the waves in fp64.
+    // with sx^2 = max(var_x, 0).  The three quotients come from one
+    // reciprocal of the product of the denominators (at most ~1e14, far
+    // inside fp32 range).  For l and c a thread sums only the subtracted
+    // parts and takes them from its count of valid pixels at the end.  A
+    // thread's few pixels and then its wave are summed in fp32, the waves in
+    // fp64.
     constexpr float kC3 = kC2 / 2.0f;
-    float pl = 0.0f, pc = 0.0f, ps = 0.0f;
+    float dl = 0.0f, dc = 0.0f, ps = 0.0f;
+    int npx = 0;
     vertical_moments<TW, TH, NT, RB>(lds, taps, x0, y0, MW, MH,
                                      [&](int, int, float mx, float my, float xx, float yy, float xy) {
-        const float vx = xx - mx * mx;
-        const float vy = yy - my * my;
-        const float cxy = xy - mx * my;
-        const float sdx = hw_sqrt(fmaxf(vx, 0.0f));
-        const float sdy = hw_sqrt(fmaxf(vy, 0.0f));
-        const float ux = mx + kMomentOffset;
-        const float uy = my + kMomentOffset;
+        const float vx = fmaxf(fmaf(-mx, mx, xx), 0.0f);
+        const float vy = fmaxf(fmaf(-my, my, yy), 0.0f);
+        const float cxy = fmaf(-mx, my, xy);
+        const float sdx = hw_sqrt(vx), sdy = hw_sqrt(vy);
+        const float ux = mx + kMomentOffset, uy = my + kMomentOffset;
         const float dm = mx - my, ds = sdx - sdy;
-        const float d1 = ux * ux + uy * uy + kC1;
-        const float d2 = sdx * sdx + sdy * sdy + kC2;
-        const float d3 = sdx * sdy + kC3;
-        const float r = rcp(d1 * d2 * d3);
-        pl += 1.0f - dm * dm * ((d2 * d3) * r);
-        pc += 1.0f - ds * ds * ((d1 * d3) * r);
-        ps += (cxy + kC3) * ((d1 * d2) * r);
+        const float d1 = fmaf(ux, ux, fmaf(uy, uy, kC1));
+        const float d2 = (vx + vy) + kC2;
+        const float d3 = fmaf(sdx, sdy, kC3);
+        const float d12 = d1 * d2;
+        const float r = rcp(d12 * d3);
+        dl = fmaf(dm * dm, (d2 * d3) * r, dl);
+        dc = fmaf(ds * ds, (d1 * d3) * r, dc);
+        ps = fmaf(cxy + kC3, d12 * r, ps);
+        ++npx;
     });
-    const float terms[3] = {pl, pc, ps};
+    const float terms[3] = {(float)npx - dl, (float)npx - dc, ps};
     double acc[3];
     block_sum_terms<NT, 3>(terms, red, acc);
     if (threadIdx.x == 0) {

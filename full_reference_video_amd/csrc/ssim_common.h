@@ -43,13 +43,40 @@ constexpr int in_pitch() {
     return TW + 12;
 }
 
+// LDS of a tile: the staged input (two planes, IH rows of pitch
+// in_pitch<TW>()) and, after the horizontal pass, the five horizontal moment
+// planes (IH x TW each) in the same buffer.
+template <int TW, int TH>
+constexpr int tile_lds_floats() {
+    constexpr int stage = 2 * (TH + 10) * in_pitch<TW>(), moments = 5 * (TH + 10) * TW;
+    return stage > moments ? stage : moments;
+}
+
+// LDS float offset, relative to the first staged plane, where threads past a
+// staged tile's last cell put their (unused) value, so that every thread
+// stores: a store under a per-lane condition lets the compiler sink the
+// matching load behind the stores of earlier cells, and the tile then costs
+// two memory latencies.  It lies past both staged planes and inside the
+// tile's buffer (sized for the moment planes), four floats wide.
+template <int TW, int TH>
+constexpr int stage_spare() {
+    constexpr int IH = TH + 10, IP = in_pitch<TW>();
+    static_assert(2 * IH * IP + IH * IP + 4 <= tile_lds_floats<TW, TH>(), "no spare LDS past the staged tile");
+    return 2 * IH * IP;
+}
+
 // Stage the (TH + 10) x (TW + 10) input tile of both planes at (x0, y0),
-// offset-subtracted, in LDS with row pitch in_pitch<TW>(); cells outside the
-// plane hold 0 (they feed only map pixels outside the valid region).  Every
-// load is unconditional — a cell outside the plane reads the plane's first
-// sample and is dropped afterwards — and all of them are issued before the
-// first conversion, so the tile costs one memory latency.  (A load under a
-// per-lane branch makes the compiler wait for every earlier load before it.)
+// offset-subtracted, in LDS with row pitch in_pitch<TW>().  A cell outside
+// the plane (column >= W or row >= H) is read from the plane's first sample
+// instead and left as it comes: such cells feed only the moments of map
+// pixels outside the valid region, which are never summed, and never the
+// next pyramid level (its 2x2 blocks lie inside the plane), so they need an
+// in-bounds address but no masking.  Every load is unconditional and all of
+// them are issued before the first conversion, so the tile costs one memory
+// latency.  (A load under a per-lane branch makes the compiler wait for
+// every earlier load before it.)  The conversion raw * unit - 128 is one
+// fused multiply-add: raw * unit is exact (unit is a power of two), so it
+// rounds once either way.
 template <int TW, int TH, int NT, typename TIn>
 __device__ __forceinline__ void stage_tile(const TIn *__restrict__ ref, const TIn *__restrict__ dis,
                                            int pitch, int W, int H, float unit, int x0, int y0,
@@ -57,6 +84,7 @@ __device__ __forceinline__ void stage_tile(const TIn *__restrict__ ref, const TI
     constexpr int IW = TW + 10, IH = TH + 10, IP = in_pitch<TW>();
     constexpr int N = (IH * IW + NT - 1) / NT;
     TIn ra[N], rb[N];
+    int lds_off[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         const int i = threadIdx.x + k * NT;
@@ -66,49 +94,52 @@ __device__ __forceinline__ void stage_tile(const TIn *__restrict__ ref, const TI
         const size_t o = in ? (size_t)gy * (size_t)pitch + (size_t)gx : 0;
         ra[k] = ref[o];
         rb[k] = dis[o];
+        lds_off[k] = i < IH * IW ? r * IP + c : stage_spare<TW, TH>();
     }
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-        const int i = threadIdx.x + k * NT;
-        const int r = i / IW, c = i - r * IW;
-        const bool in = x0 + c < W && y0 + r < H;
-        if (i < IH * IW) {
-            sx[r * IP + c] = in ? to_value(ra[k], unit) - kMomentOffset : 0.0f;
-            sy[r * IP + c] = in ? to_value(rb[k], unit) - kMomentOffset : 0.0f;
-        }
+        sx[lds_off[k]] = fmaf(to_value(ra[k], 1.0f), unit, -kMomentOffset);
+        sy[lds_off[k]] = fmaf(to_value(rb[k], 1.0f), unit, -kMomentOffset);
     }
 }
 
-// Four consecutive raw samples (aligned to 4 samples) as one load.
+// Four consecutive raw samples (aligned to 4 samples) as one load, and
+// their values on the 8-bit scale with the mid-scale offset removed.
 template <typename TIn> struct Raw4;
 template <> struct Raw4<float> {
     using type = float4;
     __device__ static float4 load(const float *p) { return *reinterpret_cast<const float4 *>(p); }
-    __device__ static float4 value(float4 v, float) { return v; }
+    __device__ static float4 centred(float4 v, float) {
+        return make_float4(v.x - kMomentOffset, v.y - kMomentOffset, v.z - kMomentOffset, v.w - kMomentOffset);
+    }
 };
 template <> struct Raw4<uint8_t> {
     using type = uint32_t;
     __device__ static uint32_t load(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
-    __device__ static float4 value(uint32_t v, float unit) {
-        return make_float4((float)(v & 0xffu) * unit, (float)((v >> 8) & 0xffu) * unit,
-                           (float)((v >> 16) & 0xffu) * unit, (float)(v >> 24) * unit);
+    __device__ static float4 centred(uint32_t v, float unit) {
+        return make_float4(fmaf((float)(v & 0xffu), unit, -kMomentOffset),
+                           fmaf((float)((v >> 8) & 0xffu), unit, -kMomentOffset),
+                           fmaf((float)((v >> 16) & 0xffu), unit, -kMomentOffset),
+                           fmaf((float)(v >> 24), unit, -kMomentOffset));
     }
 };
 template <> struct Raw4<uint16_t> {
     using type = uint2;
     __device__ static uint2 load(const uint16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
-    __device__ static float4 value(uint2 v, float unit) {
-        return make_float4((float)(v.x & 0xffffu) * unit, (float)(v.x >> 16) * unit,
-                           (float)(v.y & 0xffffu) * unit, (float)(v.y >> 16) * unit);
+    __device__ static float4 centred(uint2 v, float unit) {
+        return make_float4(fmaf((float)(v.x & 0xffffu), unit, -kMomentOffset),
+                           fmaf((float)(v.x >> 16), unit, -kMomentOffset),
+                           fmaf((float)(v.y & 0xffffu), unit, -kMomentOffset),
+                           fmaf((float)(v.y >> 16), unit, -kMomentOffset));
     }
 };
 
 // The same with 4-sample loads, for planes whose base is aligned to 4
 // samples and whose row pitch is a multiple of 4 samples (x0, a multiple of
 // TW, is a multiple of 4).  A chunk that starts inside a row lies wholly
-// inside the row's pitch (the pitch is a multiple of 4 samples), so it is
-// read whole and its samples past the plane's edge are dropped; a chunk
-// that starts outside the plane reads the plane's first chunk instead.
+// inside the row's pitch, so it is read whole; a chunk that starts outside
+// the plane reads the plane's first chunk instead.  As above, cells outside
+// the plane are left unmasked.
 template <int TW, int TH, int NT, typename TIn>
 __device__ __forceinline__ void stage_tile_x4(const TIn *__restrict__ ref, const TIn *__restrict__ dis, int pitch,
                                               int W, int H, float unit, int x0, int y0, float *sx, float *sy) {
@@ -117,33 +148,22 @@ __device__ __forceinline__ void stage_tile_x4(const TIn *__restrict__ ref, const
     constexpr int N = (IH * QI + NT - 1) / NT;
     using R4 = Raw4<TIn>;
     typename R4::type ra[N], rb[N];
+    int lds_off[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         const int i = threadIdx.x + k * NT;
         const int r = i / QI, q = i - r * QI;
         const int gx = x0 + 4 * q, gy = y0 + r;
-        const bool in = i < IH * QI && gy < H && gx < W;
+        const bool in = i < IH * QI && gx < W && gy < H;
         const size_t o = in ? (size_t)gy * (size_t)pitch + (size_t)gx : 0;
         ra[k] = R4::load(ref + o);
         rb[k] = R4::load(dis + o);
+        lds_off[k] = i < IH * QI ? r * IP + 4 * q : stage_spare<TW, TH>();
     }
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-        const int i = threadIdx.x + k * NT;
-        const int r = i / QI, q = i - r * QI;
-        const int gx = x0 + 4 * q, gy = y0 + r;
-        if (i < IH * QI) {
-            const float4 va = R4::value(ra[k], unit), vb = R4::value(rb[k], unit);
-            const bool row_in = gy < H;
-            const float off = kMomentOffset;
-            // cells outside the plane end up 0
-            const float4 a = make_float4(row_in && gx + 0 < W ? va.x - off : 0.0f, row_in && gx + 1 < W ? va.y - off : 0.0f,
-                                         row_in && gx + 2 < W ? va.z - off : 0.0f, row_in && gx + 3 < W ? va.w - off : 0.0f);
-            const float4 b = make_float4(row_in && gx + 0 < W ? vb.x - off : 0.0f, row_in && gx + 1 < W ? vb.y - off : 0.0f,
-                                         row_in && gx + 2 < W ? vb.z - off : 0.0f, row_in && gx + 3 < W ? vb.w - off : 0.0f);
-            *reinterpret_cast<float4 *>(sx + r * IP + 4 * q) = a;
-            *reinterpret_cast<float4 *>(sy + r * IP + 4 * q) = b;
-        }
+        *reinterpret_cast<float4 *>(sx + lds_off[k]) = R4::centred(ra[k], unit);
+        *reinterpret_cast<float4 *>(sy + lds_off[k]) = R4::centred(rb[k], unit);
     }
 }
 
@@ -188,15 +208,6 @@ __device__ __forceinline__ float ssim_term(float mx, float my, float xx, float y
     // One reciprocal for both quotients (A * B stays far inside fp32 range).
     const float r = rcp(A * B);
     return (1.0f - dm * dm * (B * r)) * (1.0f - v * (A * r));
-}
-
-// LDS of a tile: the staged input (two planes, IH rows of pitch
-// in_pitch<TW>()) and, after the horizontal pass, the five horizontal moment
-// planes (IH x TW each) in the same buffer.
-template <int TW, int TH>
-constexpr int tile_lds_floats() {
-    constexpr int stage = 2 * (TH + 10) * in_pitch<TW>(), moments = 5 * (TH + 10) * TW;
-    return stage > moments ? stage : moments;
 }
 
 // Horizontal 11-tap pass of one item: four adjacent columns c0..c0+3 of
