@@ -119,6 +119,47 @@ def cpu_baseline(host, wl, budget_s: float):
                       f"one thread, {el:.1f} s"}
 
 
+# Frames the all-cores baseline's worker processes read (inherited through
+# fork, never pickled).
+_BASELINE_FRAMES = None
+
+
+def _oracle_worker(args):
+    """One process of the all-cores baseline: the unchanged oracle over
+    frames i, i + P, ... (cycling) for about `budget_s` seconds."""
+    metric, bpc, i, p, budget_s = args
+    import oracle
+    host = _BASELINE_FRAMES
+    fn = oracle.msssim if metric == "ms_ssim" else oracle.ssim
+    n, k = 0, i
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        r, d = host[k % len(host)]
+        fn(r, d, bpc)
+        n += 1
+        k += p
+    return n, time.perf_counter() - t0
+
+
+def cpu_baseline_all_cores(host, wl, budget_s: float, cores: int):
+    """The same oracle, one single-threaded process per core, each on its own
+    frames; frames/s summed over the processes.  Forks: call it before the
+    GPU is touched."""
+    import multiprocessing as mp
+    global _BASELINE_FRAMES
+    _BASELINE_FRAMES = host
+    try:
+        with mp.get_context("fork").Pool(cores) as pool:
+            res = pool.map(_oracle_worker, [(wl.metric, wl.bpc, i, cores, budget_s) for i in range(cores)])
+    finally:
+        _BASELINE_FRAMES = None
+    n = sum(r[0] for r in res)
+    el = max(r[1] for r in res)
+    return {"value": round(n / el, 3), "unit": "frames/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} frame pairs of {wl.name}, {cores} processes of the single-threaded oracle "
+                      f"on disjoint frames, {el:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +171,8 @@ def main():
     ap.add_argument("--lag", type=int, default=0,
                     help="frames submitted after a frame before it is collected (0: 3*batch)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0: skip)")
+    ap.add_argument("--cpu-cores", type=int, default=0,
+                    help="processes of the all-cores oracle baseline (0: the host's CPUs, at most 16; -1: skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB 20 times (a kernel of known "
                          "traffic, to calibrate the FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -152,19 +195,34 @@ def main():
         sys.exit(2)
 
     import numpy as np
+
+    from full_reference_video_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    src = synth.FrameSource(args.workload)
+    log(f"generating {wl.frames} frame pairs of {wl.name}")
+    host = [src.pair(t) for t in range(wl.frames)]
+
+    # The oracle baselines run first, before anything touches the GPU (the
+    # all-cores one forks worker processes).
+    cpu = cpu_all = None
+    if args.cpu_budget > 0:
+        log("oracle timing on the host")
+        cpu = cpu_baseline(host, wl, args.cpu_budget)
+        if args.cpu_cores >= 0:
+            cores = args.cpu_cores or min(16, len(os.sched_getaffinity(0)))
+            log(f"oracle timing on {cores} host processes")
+            cpu_all = cpu_baseline_all_cores(host, wl, args.cpu_budget, cores)
+
     import torch
 
-    from full_reference_video_amd import synth, vqm
+    from full_reference_video_amd import vqm
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    wl = synth.WORKLOADS[args.workload]
-    src = synth.FrameSource(args.workload)
     s = vqm.vqm_ssim_scale(wl.w, wl.h) if wl.metric == "float_ssim" else 1
-    log(f"generating {wl.frames} frame pairs of {wl.name}")
-    host = [src.pair(t) for t in range(wl.frames)]
     dev = []
     for r, d in host:
         tr = torch.from_numpy(r.view(np.int16) if r.dtype == np.uint16 else r).cuda()
@@ -244,10 +302,6 @@ def main():
                 "kernel": "ms_level (all five levels)",
                 "flops_per_frame": ms_flops_per_frame(wl.w, wl.h)}
 
-    cpu = None
-    if args.cpu_budget > 0:
-        log("oracle timing on the host")
-        cpu = cpu_baseline(host, wl, args.cpu_budget)
 
     out = {
         "metric": "frames/sec and achieved HBM GB/s (% of peak), float_ssim at 3840x2160"
@@ -269,6 +323,7 @@ def main():
         "kernels": kt,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
     }
     print(json.dumps(out), flush=True)
     for c in ctxs:

@@ -120,26 +120,38 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
 
 template <int NT>
 __global__ __launch_bounds__(NT) void ms_finish(MsFinishBatch b, MsLevels lv) {
+    static_assert(NT >= 64, "the powers take one wave");
     __shared__ double red[3][NT / 64];
+    __shared__ double lcs[15];
+    __shared__ double pw[11];
     const MsFinishFrame &fr = b.f[blockIdx.x];
-    double lcs[15];
     for (int j = 0; j < 5; ++j) {
         double tot[3];
         sum_spans<NT, 3>(fr.partials + lv.offset[j], lv.nb[j], (size_t)lv.nb[j], tot, red);
-        __syncthreads();  // red[] is reused by the next level
-        lcs[j] = tot[0] / lv.count[j];
-        lcs[5 + j] = tot[1] / lv.count[j];
-        lcs[10 + j] = tot[2] / lv.count[j];
+        if (threadIdx.x == 0) {
+            lcs[j] = tot[0] / lv.count[j];
+            lcs[5 + j] = tot[1] / lv.count[j];
+            lcs[10 + j] = tot[2] / lv.count[j];
+        }
+        __syncthreads();  // red[] is reused by the next level; lcs[] is complete after the last
     }
-    if (threadIdx.x != 0) return;
-    double ms = pow(lcs[4], kBeta[4]);
+    // The eleven powers at once, one per lane: L_5^b5, C_j^bj, S_j^bj.
+    const int t = threadIdx.x;
+    if (t < 11) {
+        const int j = t == 0 ? 4 : (t - 1) % 5;
+        const double base = t == 0 ? lcs[4] : (t <= 5 ? lcs[5 + j] : lcs[10 + j]);
+        pw[t] = pow(base, kBeta[j]);
+    }
+    __syncthreads();
+    if (t != 0) return;
+    double ms = pw[0];
     for (int j = 0; j < 5; ++j) {
         const double cj = lcs[5 + j], sj = lcs[10 + j];
         if (!(cj > 0.0) || !(sj > 0.0)) {
             ms = __longlong_as_double(0x7ff8000000000000ll);
             break;
         }
-        ms *= pow(cj, kBeta[j]) * pow(sj, kBeta[j]);
+        ms *= pw[1 + j] * pw[6 + j];
     }
     fr.result[0] = ms;
     for (int j = 0; j < 15; ++j) fr.result[1 + j] = lcs[j];

@@ -387,10 +387,23 @@ __device__ __forceinline__ void block_sum_terms(const float (&v)[NV], double (*r
 template <int NT, int NV>
 __device__ __forceinline__ void sum_spans(const double *partials, int nb, size_t stride, double (&tot)[NV],
                                           double (*red)[NT / 64]) {
+    // Eight loads in flight per thread and span; the additions keep the
+    // index order (a slot past the span adds +0.0, which changes nothing).
+    constexpr int U = 8;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
+        const double *p = partials + (size_t)j * stride;
         double t = 0.0;
-        for (int i = threadIdx.x; i < nb; i += NT) t += partials[(size_t)j * stride + i];
+        for (int i0 = threadIdx.x; i0 < nb; i0 += U * NT) {
+            double v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * NT;
+                v[u] = p[i < nb ? i : nb - 1];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) t += i0 + u * NT < nb ? v[u] : 0.0;
+        }
         tot[j] = t;
     }
     block_sum<NT, NV>(tot, red);
