@@ -62,6 +62,8 @@ def lib():
         L.vqm_oracle_msssim_level_maps.argtypes = [fp, fp, ip, ip, dp, dp, dp]
         L.vqm_oracle_downsample.argtypes = [fp, ip, ip, fp]
         L.vqm_oracle_msssim.argtypes = [vp, vp, ip, ip, ip, dp, dp]
+        L.vqm_oracle_plane_dims.argtypes = [ip, ip, ip, ip, ctypes.POINTER(ip), ctypes.POINTER(ip)]
+        L.vqm_oracle_plane_dims.restype = ip
         L.vqm_oracle_db.argtypes = [ctypes.c_double]
         L.vqm_oracle_db.restype = ctypes.c_double
         for name in ("vqm_oracle_sample_plane", "vqm_oracle_decimate", "vqm_oracle_ssim_planes",
@@ -185,3 +187,13 @@ def msssim_rc(ref: np.ndarray, dis: np.ndarray, w: int, h: int, bpc: int) -> int
 def db(ssim: float) -> float:
     """-10 log10(1 - ssim), +inf at ssim >= 1 ([ADR-1405] Consequences, enable_db)."""
     return lib().vqm_oracle_db(float(ssim))
+
+
+CHROMA_420, CHROMA_422, CHROMA_444 = 0, 1, 2
+
+
+def plane_dims(w: int, h: int, chroma: int, plane: int):
+    """(width, height) of plane 0..2 of a w x h picture in a chroma layout."""
+    pw, ph = ctypes.c_int(), ctypes.c_int()
+    _check(lib().vqm_oracle_plane_dims(w, h, chroma, plane, ctypes.byref(pw), ctypes.byref(ph)), "plane_dims")
+    return pw.value, ph.value

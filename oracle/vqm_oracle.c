@@ -355,3 +355,17 @@ double vqm_oracle_db(double ssim)
         return ssim >= 1.0 ? INFINITY : NAN;
     return -10.0 * log10(1.0 - ssim);
 }
+
+int vqm_oracle_plane_dims(int w, int h, int chroma, int plane, int *pw, int *ph)
+{
+    if (w <= 0 || h <= 0 || plane < 0 || plane > 2 || chroma < 0 || chroma > 2 || !pw || !ph)
+        return -EINVAL;
+    int sx = 0, sy = 0;
+    if (plane > 0) {
+        sx = chroma == 2 ? 0 : 1;
+        sy = chroma == 0 ? 1 : 0;
+    }
+    *pw = sx ? (w + 1) / 2 : w;
+    *ph = sy ? (h + 1) / 2 : h;
+    return 0;
+}

@@ -110,6 +110,17 @@ int vqm_oracle_downsample(const float *in, int w, int h, float *out);
 int vqm_oracle_msssim(const void *ref, const void *dis, int w, int h, int bpc,
                       double *score, double *lcs);
 
+/* Size of plane `plane` (0 = Y, 1 = Cb, 2 = Cr) of a w x h picture whose
+ * chroma layout is `chroma`: 0 = 4:2:0 (chroma halved both ways), 1 = 4:2:2
+ * (halved horizontally), 2 = 4:4:4.  An odd size halves rounding up, so the
+ * last chroma sample covers the last luma column or row alone (reading: the
+ * pages score Cb and Cr planes of 4:2:0 and 4:2:2 pictures, the Netflix pair
+ * and its 4:2:2 conversion among them, but give no formula for their sizes).
+ * Each plane is scored on its own, with its own decimation scale.
+ * [R-1363] Finding 6 (enable_chroma); "Research-1369: SYCL psnr_hvs,
+ * motion_v2 and psnr at 4K", section 4.  Returns -EINVAL for bad arguments. */
+int vqm_oracle_plane_dims(int w, int h, int chroma, int plane, int *pw, int *ph);
+
 /* A score in decibels, the enable_db form of float_ssim:
  *   db = -10 log10(1 - ssim),  +inf when ssim >= 1 (reading: the page gives
  * only the form's sensitivity, 4.34 / (1 - ssim) dB per unit of ssim, which is

@@ -36,6 +36,7 @@ MUTANTS = {
                                 "const int mw = w - WIN, mh = h - WIN;\n    double total"),
     "db_natural_log": ("return -10.0 * log10(1.0 - ssim);", "return -10.0 * log(1.0 - ssim);"),
     "db_amplitude_form": ("return -10.0 * log10(1.0 - ssim);", "return -20.0 * log10(1.0 - ssim);"),
+    "chroma_halves_down": ("*pw = sx ? (w + 1) / 2 : w;", "*pw = sx ? w / 2 : w;"),
     "ceil_dim_as_floor": ("return (n + scale - 1) / scale;", "return n / scale > 0 ? n / scale : 1;"),
 }
 

@@ -468,3 +468,36 @@ def test_db_sensitivity_is_the_page_figure():
     assert abs(oracle.db(s30) - ex["db"]) < 1e-9
     assert abs(oracle.db(s30 + resid) - ex["db"] - ex["delta_db"]) < 5e-4
     assert resid < FACTS["score_tolerance"]["abs"]
+
+
+# ------------------------------------------------------------ chroma planes
+
+def test_plane_dims_page_example():
+    # 288-byte chroma rows at 576x324 8-bit: Cb and Cr are 288 samples wide.
+    fact = FACTS["chroma_row_bytes"]
+    for plane in (1, 2):
+        pw, ph = oracle.plane_dims(fact["w"], fact["h"], oracle.CHROMA_420, plane)
+        assert pw * (1 if fact["bpc"] == 8 else 2) == fact["row_bytes"]
+        assert ph == fact["h"] // 2
+
+
+@pytest.mark.parametrize("w,h", [(1920, 1080), (853, 481), (17, 16), (1, 1), (2, 3)])
+def test_plane_dims_closed_form(w, h):
+    for chroma in (oracle.CHROMA_420, oracle.CHROMA_422, oracle.CHROMA_444):
+        assert oracle.plane_dims(w, h, chroma, 0) == (w, h)
+        for plane in (1, 2):
+            pw, ph = oracle.plane_dims(w, h, chroma, plane)
+            sx = chroma != oracle.CHROMA_444
+            sy = chroma == oracle.CHROMA_420
+            # every luma column/row is covered, by at most one chroma sample
+            # of its own: 2 pw - 1 <= w <= 2 pw when halved
+            assert (2 * pw - 1 <= w <= 2 * pw) if sx else pw == w
+            assert (2 * ph - 1 <= h <= 2 * ph) if sy else ph == h
+    assert oracle.plane_dims(853, 481, oracle.CHROMA_420, 1) == (427, 241)
+    assert oracle.plane_dims(853, 481, oracle.CHROMA_422, 2) == (427, 481)
+
+
+def test_plane_dims_rejects_bad_arguments():
+    for args in [(0, 10, 0, 1), (10, 10, 3, 1), (10, 10, 0, 3), (10, 10, -1, 0)]:
+        with pytest.raises(Exception):
+            oracle.plane_dims(*args)
