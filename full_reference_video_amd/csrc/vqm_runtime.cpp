@@ -732,6 +732,75 @@ int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, 
     return 0;
 }
 
+// Size of one plane of a picture in a chroma layout: Cb and Cr are halved
+// horizontally (4:2:0, 4:2:2) and vertically (4:2:0), odd sizes rounding up.
+int plane_dims(int w, int h, int chroma, int plane, int *pw, int *ph) {
+    if (w <= 0 || h <= 0) return fail(-EINVAL, "size %dx%d", w, h);
+    if (chroma < VQM_CHROMA_420 || chroma > VQM_CHROMA_444) return fail(-EINVAL, "unknown chroma layout %d", chroma);
+    if (plane < 0 || plane > 2) return fail(-EINVAL, "plane %d outside 0..2", plane);
+    const bool sx = plane > 0 && chroma != VQM_CHROMA_444, sy = plane > 0 && chroma == VQM_CHROMA_420;
+    if (pw) *pw = sx ? (w + 1) / 2 : w;
+    if (ph) *ph = sy ? (h + 1) / 2 : h;
+    return 0;
+}
+
+// Wait for every frame in flight with one device wait: the stream is in
+// order, so once the newest batch has completed every earlier one has too.
+int wait_all(vqm_ctx *ctx) {
+    if (ctx->count == 0) return 0;
+    int rc = drain(ctx);
+    if (rc) return rc;
+    const Slot &last = ctx->slots[(ctx->head + ctx->count - 1) % VQM_MAX_IN_FLIGHT];
+    if (last.batch && !last.batch->completed) {
+        HIP_TRY(hipEventSynchronize(last.batch->ev));
+        last.batch->completed = true;
+    }
+    for (int i = 0; i < ctx->count; ++i) {
+        Slot &sl = ctx->slots[(ctx->head + i) % VQM_MAX_IN_FLIGHT];
+        if (sl.batch) sl.batch->completed = true;
+    }
+    return 0;
+}
+
+// The three planes of a Y'CbCr frame pair: luma as one batch, Cb and Cr (one
+// size) as another, one wait, three results.  Every plane is checked and
+// gated first, so an error enqueues nothing.
+int frame_yuv(int kind, const void *const *ref, const void *const *dis, int w, int h, int bpc, int chroma,
+              double *scores, double *lcs, double *db) {
+    if (!ref || !dis || !scores) return fail(-EINVAL, "NULL plane array or score pointer");
+    int pw[3], ph[3];
+    for (int p = 0; p < 3; ++p) {
+        int rc = plane_dims(w, h, chroma, p, &pw[p], &ph[p]);
+        if (rc) return rc;
+        rc = check_args(ref[p], dis[p], pw[p], ph[p], bpc);
+        if (rc) return rc;
+        rc = gate(kind, pw[p], ph[p], bpc);
+        if (rc) return fail(rc, "plane %d (%dx%d): %s", p, pw[p], ph[p], vqm_last_error());
+    }
+    vqm_ctx *ctx = nullptr;
+    int rc = implicit_ctx(&ctx);
+    if (rc) return rc;
+    rc = submit(ctx, kind, ref, dis, 1, pw[0], ph[0], bpc);
+    if (rc == 0) rc = submit(ctx, kind, ref + 1, dis + 1, 2, pw[1], ph[1], bpc);
+    if (rc == 0) rc = wait_all(ctx);
+    // Collect whatever was enqueued, so the implicit context ends empty.
+    double s[3] = {0.0, 0.0, 0.0}, l[3][15], d[3];
+    int n = 0;
+    while (ctx->count > 0) {
+        const int rc2 = collect(ctx, &s[n < 3 ? n : 2], l[n < 3 ? n : 2], &d[n < 3 ? n : 2]);
+        if (rc == 0) rc = rc2;
+        if (rc2) break;
+        ++n;
+    }
+    if (rc) return rc;
+    for (int p = 0; p < 3; ++p) {
+        scores[p] = s[p];
+        if (lcs) memcpy(lcs + 15 * p, l[p], sizeof l[p]);
+        if (db) db[p] = d[p];
+    }
+    return 0;
+}
+
 // The pipelined scoring loop of vqm_score_frames.
 int score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *refs, const void *const *diss,
                  int n, int w, int h, int bpc, int batch, int lag, double *scores, double *lcs, double *db) {
@@ -824,6 +893,20 @@ int vqm_msssim_frame_lcs(const void *ref, const void *dis, int w, int h, int bpc
                          double *lcs) {
     if (!lcs) return fail(-EINVAL, "NULL lcs pointer");
     return blocking(KIND_MSSSIM, ref, dis, w, h, bpc, score, lcs, nullptr);
+}
+
+int vqm_plane_dims(int w, int h, int chroma, int plane, int *pw, int *ph) {
+    return plane_dims(w, h, chroma, plane, pw, ph);
+}
+
+int vqm_ssim_frame_yuv(const void *const *ref, const void *const *dis, int w, int h, int bpc, int chroma,
+                       double *scores, double *db) {
+    return frame_yuv(KIND_SSIM, ref, dis, w, h, bpc, chroma, scores, nullptr, db);
+}
+
+int vqm_msssim_frame_yuv(const void *const *ref, const void *const *dis, int w, int h, int bpc, int chroma,
+                         double *scores, double *lcs) {
+    return frame_yuv(KIND_MSSSIM, ref, dis, w, h, bpc, chroma, scores, lcs, nullptr);
 }
 
 int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out) { return create(device, hip_stream, out); }

@@ -184,6 +184,28 @@ class FrameSource:
         return np.ascontiguousarray(ref), np.ascontiguousarray(dis)
 
 
+def chroma_pair(c: int, t: int, plane: int, w: int, h: int, bpc: int):
+    """(ref, dis) of chroma plane 1 (Cb) or 2 (Cr), w x h, of frame ``t`` in
+    the style of config ``c``: a smooth field of its own (seed
+    1000 c + 100 plane), narrower than luma about the mid value, plus uniform
+    noise in +-4; dis adds Gaussian noise of sigma 3 (8-bit units)."""
+    full = (1 << bpc) - 1
+    rng = np.random.default_rng(1000 * c + 100 * plane)
+    period = rng.uniform(24.0, 192.0, size=3)
+    theta = rng.uniform(0.0, np.pi, size=3)
+    phase = rng.uniform(0.0, 2.0 * np.pi, size=3)
+    x = np.arange(w, dtype=np.float64)[None, :]
+    y = np.arange(h, dtype=np.float64)[:, None]
+    f = np.full((h, w), 128.0)
+    for k in range(3):
+        f = f + 10.0 * np.sin(2.0 * np.pi * (x * np.cos(theta[k]) + y * np.sin(theta[k])) / period[k] + phase[k])
+    noise = np.random.default_rng(1000 * c + 100 * plane + 1 + t)
+    scale = full / 255.0
+    ref = _quantise((f + noise.integers(-4, 5, size=(h, w))) * scale, bpc)
+    dis = _quantise(ref + noise.standard_normal(size=(h, w)) * (3.0 * scale), bpc)
+    return np.ascontiguousarray(ref), np.ascontiguousarray(dis)
+
+
 def random_planes(seed: int, w: int, h: int, bpc: int, kind: str = "uniform"):
     """Small seeded planes for edge-case and property tests.
 

@@ -30,6 +30,9 @@ VQM_KERNEL_SSIM_STEP = 0
 VQM_KERNEL_SSIM_DRAIN = 1
 VQM_KERNEL_MSSSIM_LEVEL1 = 2
 VQM_KERNEL_MSSSIM_COARSE = 3
+VQM_CHROMA_420 = 0
+VQM_CHROMA_422 = 1
+VQM_CHROMA_444 = 2
 
 
 class VqmError(RuntimeError):
@@ -61,6 +64,10 @@ def lib() -> ctypes.CDLL:
             getattr(L, n).argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_double_p]
         L.vqm_msssim_frame_lcs.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_double_p, c_double_p]
         L.vqm_ssim_frame_db.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_double_p, c_double_p]
+        L.vqm_plane_dims.argtypes = [c_int, c_int, c_int, c_int, c_int_p, c_int_p]
+        for n in ("vqm_ssim_frame_yuv", "vqm_msssim_frame_yuv"):
+            getattr(L, n).argtypes = [ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int, c_int, c_int, c_int,
+                                      c_double_p, c_double_p]
         L.vqm_ctx_create.argtypes = [c_int, c_void_p, ctypes.POINTER(c_void_p)]
         L.vqm_ctx_destroy.argtypes = [c_void_p]
         L.vqm_ctx_destroy.restype = None
@@ -154,6 +161,52 @@ def vqm_ssim_frame_db(ref, dis, bpc: int):
     _check(lib().vqm_ssim_frame_db(pr, pd, w, h, int(bpc), ctypes.byref(score), ctypes.byref(db)),
            "vqm_ssim_frame_db")
     return score.value, db.value
+
+
+def vqm_plane_dims(w: int, h: int, chroma: int, plane: int):
+    """(width, height) of plane 0..2 of a w x h picture in a chroma layout."""
+    pw, ph = ctypes.c_int(), ctypes.c_int()
+    _check(lib().vqm_plane_dims(int(w), int(h), int(chroma), int(plane), ctypes.byref(pw), ctypes.byref(ph)),
+           "vqm_plane_dims")
+    return pw.value, ph.value
+
+
+def _yuv(refs, diss, bpc: int, chroma: int):
+    if len(refs) != 3 or len(diss) != 3:
+        raise ValueError("three planes (Y, Cb, Cr) per picture")
+    pr = (ctypes.c_void_p * 3)()
+    pd = (ctypes.c_void_p * 3)()
+    keep = []
+    w = h = None
+    for p in range(3):
+        a, b, pw, ph, k = _pair(refs[p], diss[p], bpc)
+        if p == 0:
+            w, h = pw, ph
+        elif (pw, ph) != vqm_plane_dims(w, h, chroma, p):
+            raise ValueError(f"plane {p} is {pw}x{ph}, the layout needs {vqm_plane_dims(w, h, chroma, p)}")
+        pr[p], pd[p] = a, b
+        keep.append(k)
+    return pr, pd, w, h, keep
+
+
+def vqm_ssim_frame_yuv(refs, diss, bpc: int, chroma: int):
+    """(scores[3], decibel forms[3]) of the Y, Cb and Cr planes of a frame pair."""
+    pr, pd, w, h, _keep = _yuv(refs, diss, bpc, chroma)
+    scores, db = np.empty(3, np.float64), np.empty(3, np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(lib().vqm_ssim_frame_yuv(pr, pd, w, h, int(bpc), int(chroma), scores.ctypes.data_as(dp),
+                                    db.ctypes.data_as(dp)), "vqm_ssim_frame_yuv")
+    return scores, db
+
+
+def vqm_msssim_frame_yuv(refs, diss, bpc: int, chroma: int):
+    """(scores[3], per-level means [3, 15]) of the Y, Cb and Cr planes."""
+    pr, pd, w, h, _keep = _yuv(refs, diss, bpc, chroma)
+    scores, lcs = np.empty(3, np.float64), np.empty((3, VQM_MSSSIM_LCS), np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(lib().vqm_msssim_frame_yuv(pr, pd, w, h, int(bpc), int(chroma), scores.ctypes.data_as(dp),
+                                      lcs.ctypes.data_as(dp)), "vqm_msssim_frame_yuv")
+    return scores, lcs
 
 
 def vqm_msssim_frame(ref, dis, bpc: int) -> float:

@@ -120,6 +120,34 @@ VQM_API int vqm_msssim_frame(const void *ref, const void *dis, int w, int h, int
 VQM_API int vqm_msssim_frame_lcs(const void *ref, const void *dis, int w, int h, int bpc,
                          double *score, double *lcs);
 
+/* ---- Y'CbCr pictures: every plane scored ---- */
+
+/* Chroma layouts.  Plane 0 is luma, w x h; planes 1 and 2 (Cb, Cr) are
+ * halved horizontally in 4:2:0 and 4:2:2 and vertically in 4:2:0, an odd
+ * size rounding up ((w + 1) / 2). */
+enum vqm_chroma { VQM_CHROMA_420 = 0, VQM_CHROMA_422 = 1, VQM_CHROMA_444 = 2 };
+
+/* Width and height of plane `plane` (0 = Y, 1 = Cb, 2 = Cr) of a w x h
+ * picture in layout `chroma`.  Pure host; -EINVAL for bad arguments.
+ * ([R-1363] Finding 6, enable_chroma; [R-1369] section 4.) */
+VQM_API int vqm_plane_dims(int w, int h, int chroma, int plane, int *pw, int *ph);
+
+/* float_ssim of each plane of a Y'CbCr frame pair ([R-1363] Finding 6,
+ * enable_chroma): ref[p] and dis[p] are plane p (0 = Y, 1 = Cb, 2 = Cr),
+ * tightly packed at the vqm_plane_dims size, each pointer of any kind
+ * above.  Every plane is scored on its own (its own decimation scale);
+ * scores[p] receives plane p's score and db (may be NULL) its decibel form.
+ * The three planes are enqueued together and the call waits once.  Every
+ * plane is checked and gated before anything is enqueued: -ENOTSUP when any
+ * plane is refused (vqm_last_error names it). */
+VQM_API int vqm_ssim_frame_yuv(const void *const *ref, const void *const *dis, int w, int h, int bpc, int chroma,
+                               double *scores, double *db);
+
+/* MS-SSIM of each plane, as vqm_ssim_frame_yuv; lcs (may be NULL) receives
+ * 3 x VQM_MSSSIM_LCS doubles, plane by plane. */
+VQM_API int vqm_msssim_frame_yuv(const void *const *ref, const void *const *dis, int w, int h, int bpc,
+                                 int chroma, double *scores, double *lcs);
+
 /* ---- explicit contexts: caller-chosen device and stream, pipelined ---- */
 
 typedef struct vqm_ctx vqm_ctx;

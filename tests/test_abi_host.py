@@ -125,3 +125,27 @@ def test_no_device_is_enodev():
     a = np.zeros((400, 400), np.uint8)
     assert _rc(vqm.vqm_ssim_frame, a, a, 8) == -errno.ENODEV
     assert _rc(vqm.Context, 0, None) == -errno.ENODEV
+
+
+def test_plane_dims_match_oracle():
+    for (w, h) in [(1920, 1080), (853, 481), (576, 324), (1, 1), (7, 9)]:
+        for chroma in (vqm.VQM_CHROMA_420, vqm.VQM_CHROMA_422, vqm.VQM_CHROMA_444):
+            for plane in range(3):
+                assert vqm.vqm_plane_dims(w, h, chroma, plane) == oracle.plane_dims(w, h, chroma, plane)
+    L = vqm.lib()
+    a, b = ctypes.c_int(), ctypes.c_int()
+    assert L.vqm_plane_dims(10, 10, 3, 1, ctypes.byref(a), ctypes.byref(b)) == -errno.EINVAL
+    assert L.vqm_plane_dims(10, 10, 0, 3, ctypes.byref(a), ctypes.byref(b)) == -errno.EINVAL
+
+
+def test_yuv_gate_refuses_before_any_hip_call():
+    # 576x324 4:2:0: the 288x162 chroma planes are below MS-SSIM's
+    # 11 x 16 rows, so the whole call is refused, naming the plane.
+    w, h = 576, 324
+    planes = [np.zeros(oracle.plane_dims(w, h, 0, p)[::-1], np.uint8) for p in range(3)]
+    with pytest.raises(vqm.VqmError) as e:
+        vqm.vqm_msssim_frame_yuv(planes, planes, 8, vqm.VQM_CHROMA_420)
+    assert e.value.rc == -errno.ENOTSUP
+    assert "plane 1" in vqm.vqm_last_error()
+    with pytest.raises(ValueError):  # wrong chroma size for the layout
+        vqm.vqm_ssim_frame_yuv(planes, planes, 8, vqm.VQM_CHROMA_444)

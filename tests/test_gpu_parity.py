@@ -488,3 +488,49 @@ def test_ssim_db_identity_and_pipeline(ctx, torch_cuda):
     scores, dbs = vqm.vqm_score_frames([ctx], vqm.VQM_METRIC_FLOAT_SSIM, fs, 4, 0, want_db=True)
     for t, (x, y) in enumerate(pairs):
         assert (scores[t], dbs[t]) == vqm.vqm_ssim_frame_db(x, y, src.bpc)
+
+
+# ------------------------------------------------------------ Y'CbCr pictures
+
+def _yuv_frame(c, t, w, h, bpc, chroma):
+    y = synth.FrameSource(c, w=w, h=h, bpc=bpc).pair(t)
+    planes = [y]
+    for p in (1, 2):
+        pw, ph = oracle.plane_dims(w, h, chroma, p)
+        planes.append(synth.chroma_pair(c, t, p, pw, ph, bpc))
+    return [r for r, _ in planes], [d for _, d in planes]
+
+
+@pytest.mark.parametrize("w,h,bpc,chroma", [(1920, 1080, 8, 0), (853, 481, 12, 0), (853, 481, 10, 1),
+                                            (640, 360, 8, 2), (1921, 1079, 16, 0)])
+def test_ssim_yuv_planes(ctx, w, h, bpc, chroma):
+    refs, diss = _yuv_frame(3, 2, w, h, bpc, chroma)
+    say(f"yuv float_ssim {w}x{h} bpc {bpc} chroma {chroma}")
+    scores, db = vqm.vqm_ssim_frame_yuv(refs, diss, bpc, chroma)
+    for p in range(3):
+        # the same kernels as a lone plane, bit for bit
+        assert (scores[p], db[p]) == vqm.vqm_ssim_frame_db(refs[p], diss[p], bpc), p
+        assert abs(scores[p] - oracle.ssim(refs[p], diss[p], bpc)) <= TOL, p
+
+
+@pytest.mark.parametrize("w,h,bpc,chroma", [(1920, 1080, 8, 0), (723, 389, 10, 2)])
+def test_msssim_yuv_planes(ctx, w, h, bpc, chroma):
+    refs, diss = _yuv_frame(5, 1, w, h, bpc, chroma)
+    say(f"yuv MS-SSIM {w}x{h} bpc {bpc} chroma {chroma}")
+    scores, lcs = vqm.vqm_msssim_frame_yuv(refs, diss, bpc, chroma)
+    for p in range(3):
+        one, one_lcs = vqm.vqm_msssim_frame_lcs(refs[p], diss[p], bpc)
+        assert scores[p] == one and np.array_equal(lcs[p], one_lcs), p
+    # the oracle on the chroma planes (the smaller ones)
+    for p in (1, 2):
+        assert abs(scores[p] - oracle.msssim(refs[p], diss[p], bpc)) <= TOL, p
+
+
+def test_yuv_leaves_the_implicit_context_empty(ctx):
+    # A refused picture enqueues nothing; the next calls are unaffected.
+    w, h = 576, 324
+    refs, diss = _yuv_frame(1, 0, w, h, 8, 0)
+    with pytest.raises(vqm.VqmError):
+        vqm.vqm_msssim_frame_yuv(refs, diss, 8, 0)
+    scores, _ = vqm.vqm_ssim_frame_yuv(refs, diss, 8, 0)
+    assert scores[0] == vqm.vqm_ssim_frame(refs[0], diss[0], 8)
