@@ -56,15 +56,18 @@ struct DecPow2 {
         const int groups = (g.dec_w + Sh::CPT - 1) / Sh::CPT;  // groups holding outputs
         return (groups + 62) / 63;
     }
-    __host__ __device__ static int blocks_per_row(const StepGeometry &g) {
-        return (waves_per_row(g) + kDecWaves - 1) / kDecWaves;
+    // A frame's waves are its (row, wave-in-row) units in row order, packed
+    // kDecWaves to a workgroup, so rows that need fewer waves than a
+    // workgroup has (1080p: 2) leave no wave idle.
+    static int blocks_per_frame(const StepGeometry &g) {
+        return (waves_per_row(g) * g.dec_h + kDecWaves - 1) / kDecWaves;
     }
-    static int blocks_per_frame(const StepGeometry &g) { return blocks_per_row(g) * g.dec_h; }
     __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
-        const int bpr = blocks_per_row(g);
-        const int Y = b / bpr, bx = b - Y * bpr;
-        dec::pow2_wave<T, S>(fr, bx * kDecWaves + (int)(threadIdx.x >> 6), Y, g.w, g.h, g.dec_w, g.post,
-                             g.dec_pitch);
+        const int wpr = waves_per_row(g);
+        const int u = b * kDecWaves + (int)(threadIdx.x >> 6);
+        if (u >= wpr * g.dec_h) return;  // the frame's last workgroup may be partly empty
+        const int Y = u / wpr;
+        dec::pow2_wave<T, S>(fr, u - Y * wpr, Y, g.w, g.h, g.dec_w, g.post, g.dec_pitch);
     }
 };
 
