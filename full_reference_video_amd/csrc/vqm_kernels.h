@@ -3,10 +3,10 @@
 // The runtime (vqm_runtime.cpp) validates every argument, sizes the scratch
 // and owns the streams; these launchers only compute grids and enqueue.
 //
-// Every launcher takes a batch of 1..kMaxBatch frames of the same geometry:
-// one launch processes all of them (blockIdx.z, after the XCD remap, picks
-// the frame).  A lone 2160p frame leaves a couple of microseconds of launch
-// ramp-up and drain per kernel that a batch of frames shares.
+// Every launcher takes a batch of 1..kMaxBatch frames of the same geometry
+// and one launch processes all of them: a lone 2160p frame leaves a couple
+// of microseconds of launch ramp-up and drain per kernel that a batch of
+// frames shares.
 #pragma once
 
 #include <hip/hip_ext.h>

@@ -226,10 +226,34 @@ struct vqm_ctx {
 
 namespace {
 
+// The caller's current device is theirs: an entry point that switches to a
+// context's device switches back before it returns.  The outermost scope of
+// a thread records the device ensure_device found, and only if it switched
+// (so entry points still make no HIP call before their argument checks).
+struct DeviceScope;
+thread_local DeviceScope *t_scope = nullptr;
+struct DeviceScope {
+    int prev = -1;
+    bool outer;
+    DeviceScope() : outer(t_scope == nullptr) {
+        if (outer) t_scope = this;
+    }
+    ~DeviceScope() {
+        if (!outer) return;
+        t_scope = nullptr;
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+    DeviceScope(const DeviceScope &) = delete;
+    DeviceScope &operator=(const DeviceScope &) = delete;
+};
+
 int ensure_device(vqm_ctx *ctx) {
     int cur = -1;
     HIP_TRY(hipGetDevice(&cur));
-    if (cur != ctx->device) HIP_TRY(hipSetDevice(ctx->device));
+    if (cur != ctx->device) {
+        if (t_scope && t_scope->prev < 0) t_scope->prev = cur;
+        HIP_TRY(hipSetDevice(ctx->device));
+    }
     return 0;
 }
 
@@ -909,41 +933,59 @@ int vqm_msssim_frame_yuv(const void *const *ref, const void *const *dis, int w, 
     return frame_yuv(KIND_MSSSIM, ref, dis, w, h, bpc, chroma, scores, lcs, nullptr);
 }
 
-int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out) { return create(device, hip_stream, out); }
+int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out) {
+    DeviceScope scope;
+    return create(device, hip_stream, out);
+}
 
-void vqm_ctx_destroy(vqm_ctx *ctx) { destroy(ctx); }
+void vqm_ctx_destroy(vqm_ctx *ctx) {
+    DeviceScope scope;
+    destroy(ctx);
+}
 
 int vqm_ssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc) {
+    DeviceScope scope;
     return submit(ctx, KIND_SSIM, &ref, &dis, 1, w, h, bpc);
 }
 
 int vqm_msssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc) {
+    DeviceScope scope;
     return submit(ctx, KIND_MSSSIM, &ref, &dis, 1, w, h, bpc);
 }
 
 int vqm_ssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n, int w, int h,
                           int bpc) {
+    DeviceScope scope;
     return submit(ctx, KIND_SSIM, refs, dis, n, w, h, bpc);
 }
 
 int vqm_msssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n, int w, int h,
                             int bpc) {
+    DeviceScope scope;
     return submit(ctx, KIND_MSSSIM, refs, dis, n, w, h, bpc);
 }
 
-int vqm_collect(vqm_ctx *ctx, double *score, double *lcs) { return collect(ctx, score, lcs, nullptr); }
+int vqm_collect(vqm_ctx *ctx, double *score, double *lcs) {
+    DeviceScope scope;
+    return collect(ctx, score, lcs, nullptr);
+}
 
-int vqm_collect_db(vqm_ctx *ctx, double *score, double *db) { return collect(ctx, score, nullptr, db); }
+int vqm_collect_db(vqm_ctx *ctx, double *score, double *db) {
+    DeviceScope scope;
+    return collect(ctx, score, nullptr, db);
+}
 
 int vqm_score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *refs, const void *const *dis,
                      int n, int w, int h, int bpc, int batch, int lag, double *scores, double *lcs,
                      double *db) {
+    DeviceScope scope;
     return score_frames(ctxs, nctx, metric, refs, dis, n, w, h, bpc, batch, lag, scores, lcs, db);
 }
 
 int vqm_in_flight(const vqm_ctx *ctx) { return ctx ? ctx->count : 0; }
 
 int vqm_ctx_set_timing(vqm_ctx *ctx, int enable) {
+    DeviceScope scope;
     if (!ctx) return fail(-EINVAL, "NULL context");
     int rc = ensure_device(ctx);
     if (rc) return rc;
@@ -959,6 +1001,7 @@ int vqm_ctx_set_timing(vqm_ctx *ctx, int enable) {
 }
 
 int vqm_ctx_kernel_time(vqm_ctx *ctx, int kernel_class, double *total_ms, int *launches, int *frames) {
+    DeviceScope scope;
     if (!ctx) return fail(-EINVAL, "NULL context");
     if (kernel_class < 0 || kernel_class > 3) return fail(-EINVAL, "kernel class %d", kernel_class);
     int rc = ensure_device(ctx);
@@ -973,6 +1016,7 @@ int vqm_ctx_kernel_time(vqm_ctx *ctx, int kernel_class, double *total_ms, int *l
 
 int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc, int scale,
                        float *out_ref, float *out_dis) {
+    DeviceScope scope;
     if (!ctx || !out_ref || !out_dis) return fail(-EINVAL, "NULL argument");
     int rc = check_args(ref, dis, w, h, bpc);
     if (rc) return rc;
@@ -1019,6 +1063,7 @@ int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, in
 
 int vqm_debug_pyramid(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc, int level,
                       float *out_ref, float *out_dis) {
+    DeviceScope scope;
     if (!ctx || !out_ref || !out_dis) return fail(-EINVAL, "NULL argument");
     if (level < 2 || level > kLevels) return fail(-EINVAL, "pyramid level %d outside 2..5", level);
     int rc = check_args(ref, dis, w, h, bpc);

@@ -155,7 +155,9 @@ typedef struct vqm_ctx vqm_ctx;
 /* Create a context on HIP device `device`.  `hip_stream` is a hipStream_t
  * on that device to enqueue on (e.g. torch.cuda.current_stream().cuda_stream),
  * or NULL for a library-owned non-blocking stream.  The stream must outlive
- * the context.  A context is not thread-safe: use one per thread. */
+ * the context.  A context is not thread-safe: use one per thread.  Calls on
+ * a context make its device current while they run and restore the calling
+ * thread's current device before they return. */
 VQM_API int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out);
 
 /* Wait for the context's frames, then free everything it owns.  NULL is a
