@@ -160,10 +160,30 @@ def cpu_baseline_all_cores(host, wl, budget_s: float, cores: int):
                       f"on disjoint frames, {el:.1f} s"}
 
 
+def copy_bandwidth(torch, mib: int = 1024, reps: int = 10) -> float:
+    """Bytes read plus written per second by torch's device-to-device copy of
+    `mib` MiB: a measured ceiling on this machine, reported beside the roofline's
+    published peak."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    del src, dst
+    return round(2.0 * n * reps / el / 1e9, 1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--reps", type=int, default=5,
+                    help="timed runs of K steps each; value is the median run's rate")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="workload number 1..5")
     ap.add_argument("--streams", type=int, default=1, help="contexts/streams batches rotate over")
@@ -233,31 +253,40 @@ def main():
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
     ctxs = [vqm.Context(0, st) for st in streams]
     lag = args.lag if args.lag > 0 else 3 * args.batch
-    frameset = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], wl.bpc)
     # The timed run streams the workload's frames K times over without a
     # break, as a video is scored (the pipeline fills once and drains once).
     stream_set = vqm.FrameSet([r for _ in range(args.steps) for r, _ in dev],
                               [d for _ in range(args.steps) for _, d in dev], wl.bpc)
 
-    log(f"warmup {args.warmup} passes")
+    # Each warm-up pass streams the workload's frames, repeated to at least
+    # twice the in-flight limit: a context's in-flight slots allocate their
+    # buffers on first use, and the timed stream must find them all ready.
+    reps = max(1, -(-2 * vqm.VQM_MAX_IN_FLIGHT // wl.frames))
+    warm_set = vqm.FrameSet([r for _ in range(reps) for r, _ in dev],
+                            [d for _ in range(reps) for _, d in dev], wl.bpc)
+    log(f"warmup {args.warmup} passes of {reps * wl.frames} frames")
     ref_scores = None
     for _ in range(args.warmup):
-        sc = run_pass(ctxs, frameset, wl.metric, args.batch, lag)
+        sc = run_pass(ctxs, warm_set, wl.metric, args.batch, lag)
         if ref_scores is None:
-            ref_scores = sc
-        elif sc != ref_scores:
+            ref_scores = sc[:wl.frames]
+        if sc != ref_scores * reps:
             raise RuntimeError("scores changed between passes")
     torch.cuda.synchronize()
 
-    log(f"timed {args.steps} passes over {wl.frames} frames, batch {args.batch}, {args.streams} streams, "
-        f"lag {lag}")
-    t0 = time.perf_counter()
-    sc = run_pass(ctxs, stream_set, wl.metric, args.batch, lag)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    if ref_scores is not None and sc != ref_scores * args.steps:
-        raise RuntimeError("scores changed between passes")
+    log(f"timed {args.reps} x {args.steps} passes over {wl.frames} frames, batch {args.batch}, "
+        f"{args.streams} streams, lag {lag}")
     frames = args.steps * wl.frames
+    runs = []
+    for _ in range(args.reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        sc = run_pass(ctxs, stream_set, wl.metric, args.batch, lag)
+        torch.cuda.synchronize()
+        runs.append(time.perf_counter() - t0)
+        if ref_scores is not None and sc != ref_scores * args.steps:
+            raise RuntimeError("scores changed between passes")
+    el = sorted(runs)[len(runs) // 2]  # the median run
     fps = frames / el
 
     # Per-kernel durations from HIP events on each context's stream.
@@ -279,6 +308,9 @@ def main():
             kt[name] = {"avg_us": 1000.0 * ms / n, "launches": n, "frames_per_launch": nf / n}
     for c in ctxs:
         c.vqm_ctx_set_timing(False)
+    # After the kernel timing: a burst of copies changes the clocks that a
+    # compute-bound kernel timed right after it would see.
+    copy_gbps = copy_bandwidth(torch)
 
     alg = algorithmic_bytes(wl, s)
     if wl.metric == "float_ssim":
@@ -320,6 +352,9 @@ def main():
         "config": {"workload": wl.name, "w": wl.w, "h": wl.h, "bpc": wl.bpc, "frames_per_step": wl.frames,
                    "scale": s, "batch": args.batch, "streams": args.streams, "lag": lag,
                    "path_GBps": round(alg * fps / 1e9, 1)},
+        "runs": {"n": len(runs), "frames_per_s_min": round(frames / max(runs), 1),
+                 "frames_per_s_max": round(frames / min(runs), 1)},
+        "copy_GBps": copy_gbps,
         "kernels": kt,
         "roofline": roof,
         "cpu_baseline": cpu,
