@@ -193,6 +193,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0: skip)")
     ap.add_argument("--cpu-cores", type=int, default=0,
                     help="processes of the all-cores oracle baseline (0: the host's CPUs, at most 16; -1: skip)")
+    ap.add_argument("--host-input", choices=("none", "pinned", "pageable"), default="none",
+                    help="score frames from host memory (pinned tensors or pageable arrays) instead of HBM: the "
+                         "end-to-end rate with one upload per frame, reported under its own metric name")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB 20 times (a kernel of known "
                          "traffic, to calibrate the FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -245,8 +248,14 @@ def main():
     s = vqm.vqm_ssim_scale(wl.w, wl.h) if wl.metric == "float_ssim" else 1
     dev = []
     for r, d in host:
-        tr = torch.from_numpy(r.view(np.int16) if r.dtype == np.uint16 else r).cuda()
-        td = torch.from_numpy(d.view(np.int16) if d.dtype == np.uint16 else d).cuda()
+        tr = torch.from_numpy(r.view(np.int16) if r.dtype == np.uint16 else r)
+        td = torch.from_numpy(d.view(np.int16) if d.dtype == np.uint16 else d)
+        if args.host_input == "none":
+            tr, td = tr.cuda(), td.cuda()
+        elif args.host_input == "pinned":
+            tr, td = tr.pin_memory(), td.pin_memory()
+        else:
+            tr, td = r, d
         dev.append((tr, td))
     torch.cuda.synchronize()
 
@@ -336,8 +345,9 @@ def main():
 
 
     out = {
-        "metric": "frames/sec and achieved HBM GB/s (% of peak), float_ssim at 3840x2160"
-                  if wl.index == 4 else f"frames/sec, {wl.name}",
+        "metric": ("frames/sec and achieved HBM GB/s (% of peak), float_ssim at 3840x2160"
+                   if wl.index == 4 else f"frames/sec, {wl.name}")
+                  + ("" if args.host_input == "none" else f", end to end from {args.host_input} host frames"),
         "value": round(fps, 1),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -349,7 +359,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "w": wl.w, "h": wl.h, "bpc": wl.bpc, "frames_per_step": wl.frames,
+        "config": {"workload": wl.name, "input": "hbm" if args.host_input == "none" else args.host_input + " host",
+                   "w": wl.w, "h": wl.h, "bpc": wl.bpc, "frames_per_step": wl.frames,
                    "scale": s, "batch": args.batch, "streams": args.streams, "lag": lag,
                    "path_GBps": round(alg * fps / 1e9, 1)},
         "runs": {"n": len(runs), "frames_per_s_min": round(frames / max(runs), 1),

@@ -22,6 +22,7 @@
 #include <deque>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -705,32 +706,52 @@ void destroy(vqm_ctx *ctx) {
     delete ctx;
 }
 
-// Per-thread implicit contexts of the blocking calls, one per device.  They
-// live until the process ends: tearing them down from a thread-exit
-// destructor could run after the HIP runtime itself has been torn down.
-struct ImplicitContexts {
-    std::map<int, vqm_ctx *> by_device;
-};
-thread_local ImplicitContexts g_implicit;
+// The blocking calls' contexts: a pool of idle contexts per device.  A
+// call leases one (creating it when none is idle), uses it and gives it
+// back empty, so the pool holds as many contexts as calls ever ran at once,
+// whatever the number of threads that came and went.  Pooled contexts live
+// until the process ends: tearing them down at exit could run after the
+// HIP runtime itself has been torn down.
+std::mutex g_pool_mu;
+std::map<int, std::vector<vqm_ctx *>> g_pool;
 
-int implicit_ctx(vqm_ctx **out) {
+struct Lease {
+    vqm_ctx *ctx = nullptr;
+    int dev = 0;
+    Lease() = default;
+    Lease(const Lease &) = delete;
+    Lease &operator=(const Lease &) = delete;
+    ~Lease() {
+        if (!ctx) return;
+        // A context the call left frames in (after an error) goes back only
+        // once they are collected; otherwise it is dropped.
+        while (ctx->count > 0) {
+            double s;
+            if (collect(ctx, &s, nullptr, nullptr) != 0) return;
+        }
+        std::lock_guard<std::mutex> lk(g_pool_mu);
+        g_pool[dev].push_back(ctx);
+    }
+};
+
+int lease_ctx(Lease &l) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return fail(-ENODEV, "no HIP device (%s)", hipGetErrorString(e));
     }
-    auto it = g_implicit.by_device.find(dev);
-    if (it != g_implicit.by_device.end()) {
-        *out = it->second;
-        return 0;
+    l.dev = dev;
+    {
+        std::lock_guard<std::mutex> lk(g_pool_mu);
+        std::vector<vqm_ctx *> &idle = g_pool[dev];
+        if (!idle.empty()) {
+            l.ctx = idle.back();
+            idle.pop_back();
+            return 0;
+        }
     }
-    vqm_ctx *ctx = nullptr;
-    int rc = create(dev, nullptr, &ctx);
-    if (rc) return rc;
-    g_implicit.by_device[dev] = ctx;
-    *out = ctx;
-    return 0;
+    return create(dev, nullptr, &l.ctx);
 }
 
 int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, double *score, double *lcs,
@@ -740,10 +761,10 @@ int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, 
     if (rc) return rc;
     rc = gate(kind, w, h, bpc);
     if (rc) return rc;
-    vqm_ctx *ctx = nullptr;
-    rc = implicit_ctx(&ctx);
+    Lease lease;
+    rc = lease_ctx(lease);
     if (rc) return rc;
-    // The implicit context never holds frames between calls.
+    vqm_ctx *ctx = lease.ctx;
     rc = submit(ctx, kind, &ref, &dis, 1, w, h, bpc);
     if (rc) return rc;
     double s = 0.0, d = 0.0;
@@ -801,13 +822,14 @@ int frame_yuv(int kind, const void *const *ref, const void *const *dis, int w, i
         rc = gate(kind, pw[p], ph[p], bpc);
         if (rc) return fail(rc, "plane %d (%dx%d): %s", p, pw[p], ph[p], vqm_last_error());
     }
-    vqm_ctx *ctx = nullptr;
-    int rc = implicit_ctx(&ctx);
+    Lease lease;
+    int rc = lease_ctx(lease);
     if (rc) return rc;
+    vqm_ctx *ctx = lease.ctx;
     rc = submit(ctx, kind, ref, dis, 1, pw[0], ph[0], bpc);
     if (rc == 0) rc = submit(ctx, kind, ref + 1, dis + 1, 2, pw[1], ph[1], bpc);
     if (rc == 0) rc = wait_all(ctx);
-    // Collect whatever was enqueued, so the implicit context ends empty.
+    // Collect whatever was enqueued, so the leased context goes back empty.
     double s[3] = {0.0, 0.0, 0.0}, l[3][15], d[3];
     int n = 0;
     while (ctx->count > 0) {

@@ -98,10 +98,12 @@ VQM_API int vqm_ssim_scale(int w, int h);
  * vqm_ssim_frame would, without touching the GPU.  Any output may be NULL. */
 VQM_API int vqm_ssim_geometry(int w, int h, int bpc, int *scale, int *dec_w, int *dec_h);
 
-/* float_ssim of one frame pair, blocking.  Uses a per-thread implicit context
- * on the current HIP device with a library-owned stream; one upload (unless
- * the planes are already on the device), one device wait, one 8-byte result.
- * *score receives the mean SSIM. */
+/* float_ssim of one frame pair, blocking.  Runs on an idle library-owned
+ * context of the current HIP device (each with its own stream; threads
+ * calling at once each get their own, and the contexts are kept for later
+ * calls); one upload (unless the planes are already on the device), one
+ * device wait, one 8-byte result.  *score receives the mean SSIM.  Thread-
+ * safe. */
 VQM_API int vqm_ssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score);
 
 /* float_ssim plus its decibel form, blocking; as vqm_ssim_frame.  *db

@@ -534,3 +534,37 @@ def test_yuv_leaves_the_implicit_context_empty(ctx):
         vqm.vqm_msssim_frame_yuv(refs, diss, 8, 0)
     scores, _ = vqm.vqm_ssim_frame_yuv(refs, diss, 8, 0)
     assert scores[0] == vqm.vqm_ssim_frame(refs[0], diss[0], 8)
+
+
+def test_blocking_calls_from_many_threads(torch_cuda):
+    # Blocking calls from threads at once (ctypes releases the GIL around
+    # them) each take their own pooled context; threads that come and go
+    # reuse the pool.  Every score equals the single-threaded one.
+    import threading
+    src = synth.FrameSource(2)
+    pairs = [src.pair(t) for t in range(5)]
+    want = [vqm.vqm_ssim_frame(r, d, 12) for r, d in pairs]
+    b = synth.FrameSource(5, w=400, h=352, bpc=10).pair(0)
+    want_ms = vqm.vqm_msssim_frame(*b, 10)
+    results, errors = {}, []
+
+    def worker(k):
+        try:
+            got = []
+            for _ in range(3):
+                got += [vqm.vqm_ssim_frame(r, d, 12) for r, d in pairs]
+                got.append(vqm.vqm_msssim_frame(*b, 10))
+            results[k] = got
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(repr(e))
+
+    say("blocking calls from 6 threads, twice")
+    for _ in range(2):
+        threads = [threading.Thread(target=worker, args=(k,)) for k in range(6)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+    assert not errors, errors
+    for k in range(6):
+        assert results[k] == (want + [want_ms]) * 3, k
