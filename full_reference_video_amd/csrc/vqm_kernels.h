@@ -15,7 +15,7 @@
 
 namespace vqm {
 
-constexpr int kMaxBatch = 8;
+constexpr int kMaxBatch = 32;
 
 // The 11 taps of the normalised Gaussian (sigma 1.5) in fp32.
 struct Taps {
@@ -86,6 +86,10 @@ struct StepRoles {
     SsimBatch fin;               // only partials and result are used
     int n_fin;
 };
+
+// A step launch passes StepRoles by value with a few small structs beside
+// it; the kernel argument block holds at most 4 KiB.
+static_assert(sizeof(StepRoles) <= 3584, "step launch arguments exceed the kernel argument block");
 
 // Whether the vectorised power-of-two decimation handles these frames
 // (otherwise the general path runs; both compute the same exact sums).

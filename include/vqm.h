@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define VQM_ABI_VERSION 2
+#define VQM_ABI_VERSION 3
 
 /* Exported symbols (the library is built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -75,11 +75,16 @@ extern "C" {
 #define VQM_API
 #endif
 
-/* Frames a context holds in flight between submit and collect. */
-#define VQM_MAX_IN_FLIGHT 48
+/* Frames a context holds in flight between submit and collect: six full
+ * batches, so a float_ssim batch's three pipeline stages can all be
+ * enqueued before its frames are awaited. */
+#define VQM_MAX_IN_FLIGHT 192
 
-/* Frames one batched submit may hand over (processed per kernel launch). */
-#define VQM_MAX_BATCH 8
+/* Frames one batched submit may hand over (processed per kernel launch).
+ * Consecutive launches on one stream leave the GPU idle for a few
+ * microseconds between them (the next kernel starts only once the last one
+ * has drained); 32 frames per launch share that gap. */
+#define VQM_MAX_BATCH 32
 
 /* Number of per-level means vqm_msssim_frame_lcs returns: L_1..L_5,
  * C_1..C_5, S_1..S_5 ([R-1363] Finding 6, enable_lcs). */
@@ -179,8 +184,9 @@ VQM_API int vqm_msssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, in
 /* Enqueue n (1..VQM_MAX_BATCH) frames of the same size and depth as one
  * batch: refs[i], dis[i] are frame i's planes (each pointer of any kind
  * above).  Every kernel of the path runs once for the whole batch, which
- * shares each launch's ramp-up and drain among n frames (at 2160p a lone
- * frame's decimation spends a fifth of its time there).  Each frame still
+ * shares each launch's ramp-up, drain and the idle gap before the next
+ * launch among n frames (at 2160p a lone frame's decimation spends a fifth
+ * of its time there).  Each frame still
  * has its own upload, result slot and completion: collect them one by one,
  * in submission order, one wait each.  Needs n free in-flight slots
  * (-EAGAIN otherwise); nothing is enqueued on error. */
@@ -208,8 +214,9 @@ enum vqm_metric { VQM_METRIC_FLOAT_SSIM = 0, VQM_METRIC_MS_SSIM = 1 };
 
 /* Score n frame pairs of one size and depth, pipelined, and block until all
  * are scored.  Frames go in batches of `batch` (1..VQM_MAX_BATCH) to the
- * nctx contexts in turn (several contexts on several streams let one
- * batch's SSIM kernels overlap the next batch's decimation); a frame is
+ * nctx contexts in turn (for example one per device; on one device a
+ * single context is fastest, since concurrent step kernels contend for the
+ * same memory bandwidth); a frame is
  * collected — its one wait — once `lag` later frames have been submitted
  * (lag <= 0: 3 * batch, which keeps a float_ssim batch's three pipeline
  * stages enqueued before its result is awaited).  scores[i] receives frame i's score;

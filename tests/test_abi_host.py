@@ -46,8 +46,22 @@ def test_binding_names_match_the_abi():
         assert hasattr(vqm, n) or hasattr(vqm.Context, n), n
 
 
+def header_constants():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(VQM_\w+)\s+(-?\d+)\s*$", text, re.M)}
+
+
 def test_abi_version():
-    assert vqm.vqm_abi_version() == 2
+    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 3
+
+
+def test_binding_constants_match_the_header():
+    consts = header_constants()
+    for name in ("VQM_MAX_IN_FLIGHT", "VQM_MAX_BATCH", "VQM_MSSSIM_LCS"):
+        assert getattr(vqm, name) == consts[name], name
+    # a float_ssim batch passes through three step launches before its
+    # frames can be collected; the in-flight limit leaves room for more
+    assert consts["VQM_MAX_IN_FLIGHT"] >= 4 * consts["VQM_MAX_BATCH"]
 
 
 def test_scale_rule_matches_oracle():

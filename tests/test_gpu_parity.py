@@ -227,9 +227,9 @@ def test_batched_submit_equals_single_frames(torch_cuda, ctx, c):
     pairs = [src.pair(t) for t in range(n)]
     say(f"ssim batches config {c}")
     single = [vqm.vqm_ssim_frame(r, d, src.bpc) for r, d in pairs]
-    # device-resident frames in batches of 1..8 (a ragged last batch)
+    # device-resident frames in batches of 1..VQM_MAX_BATCH (a ragged last batch)
     dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
-    for b in (1, 3, 8):
+    for b in (1, 3, 8, vqm.VQM_MAX_BATCH):
         got = []
         for i in range(0, n, b):
             chunk = dev[i:i + b]
@@ -354,7 +354,7 @@ def test_score_frames_loop_matches_single_frames(torch_cuda, metric, c):
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     ctxs = [vqm.Context(0, s) for s in streams]
     try:
-        for batch, lag, nc in [(1, 0, 1), (4, 0, 2), (8, 3, 2), (8, 0, 1)]:
+        for batch, lag, nc in [(1, 0, 1), (4, 0, 2), (8, 3, 2), (8, 0, 1), (vqm.VQM_MAX_BATCH, 0, 1)]:
             got = vqm.vqm_score_frames(ctxs[:nc], metric, fs, batch, lag)
             assert got.tolist() == want, (batch, lag, nc)
         # host frames through the same loop
@@ -384,10 +384,10 @@ def test_mixed_metrics_and_sizes_in_one_context(ctx):
 
 # ------------------------------------------------------------ full workloads, bench launch shape
 
-def _score_stream(torch, pairs, bpc, metric, batch=8, lag=24, n_streams=1):
+def _score_stream(torch, pairs, bpc, metric, batch=vqm.VQM_MAX_BATCH, lag=0, n_streams=1):
     """Score device-resident pairs the way bench.py times them: one context
-    per torch stream, batches of 8 frames per launch, each frame collected
-    three batches after its submit."""
+    per torch stream, batches of VQM_MAX_BATCH frames per launch, each frame
+    collected three batches after its submit (lag 0)."""
     dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
     fs = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], bpc)
     streams = [torch.cuda.Stream() for _ in range(n_streams)]
