@@ -29,6 +29,7 @@ namespace {
 // 32 x 64 tiles, 512 threads: the horizontal pass computes 74 rows for 64
 // map rows (16 % halo, against 31 % for 32-row tiles).
 constexpr int kTW = 32, kTH = 64, kNT = 512, kRB = 4;
+constexpr int kNP = 5;  // moment planes: x, y, x^2, y^2, xy (contrast needs both sigmas)
 
 __constant__ double kBeta[5] = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333};
 
@@ -36,7 +37,7 @@ template <int TW, int TH, int NT, int RB, typename TIn>
 __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int H, int next_pitch, float unit,
                                                int vec4, Taps taps) {
     constexpr int IH = TH + 10, IP = in_pitch<TW>();
-    __shared__ __attribute__((aligned(16))) float lds[tile_lds_floats<TW, TH>()];
+    __shared__ __attribute__((aligned(16))) float lds[tile_lds_floats<TW, TH, kNP>()];
     __shared__ double red[3][NT / 64];
     float *sx = lds, *sy = lds + IH * IP;
 
@@ -53,28 +54,34 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
     __syncthreads();
 
     // Next level: 2x2 means of this tile's share of the plane, from the
-    // staged (offset) samples.  Every step is exact, so adding the offset
-    // back gives the same bits as averaging the plain samples.
+    // staged (offset) samples.  Every step is exact (the sum of four offset
+    // samples and the next level's values fit fp32's significand), so adding
+    // the offset back gives the same bits as averaging the plain samples.
+    // Thread t takes the blocks in columns t % (TW/2) + k TW/2 and rows
+    // t / (TW/2) + k NT/(TW/2): one block each in an inner tile (TW/2 x TH/2
+    // blocks); the last tile column and row also take the plane's edge.
     if (t.next_ref != nullptr) {
+        static_assert(NT % (TW / 2) == 0, "block rows must tile the workgroup");
+        constexpr int CW = TW / 2, RS = NT / CW;
         const int xe = (bx == (int)gridDim.x - 1) ? W : x0 + TW;
         const int ye = (by == (int)gridDim.y - 1) ? H : y0 + TH;
         const int nx0 = x0 / 2, ny0 = y0 / 2;
-        const int nxe = min(xe / 2, W / 2), nye = min(ye / 2, H / 2);
-        const int nw = nxe - nx0, nh = nye - ny0;
-        for (int i = threadIdx.x; i < nw * nh; i += NT) {
-            const int r = i / nw, c = i - r * nw;
-            const int lr = 2 * r, lc = 2 * c;  // tile-local position of the block
-            const float x00 = sx[lr * IP + lc], x01 = sx[lr * IP + lc + 1];
-            const float x10 = sx[(lr + 1) * IP + lc], x11 = sx[(lr + 1) * IP + lc + 1];
-            const float y00 = sy[lr * IP + lc], y01 = sy[lr * IP + lc + 1];
-            const float y10 = sy[(lr + 1) * IP + lc], y11 = sy[(lr + 1) * IP + lc + 1];
-            const size_t o = (size_t)(ny0 + r) * (size_t)next_pitch + (size_t)(nx0 + c);
-            t.next_ref[o] = ((x00 + x01) + (x10 + x11)) * 0.25f + kMomentOffset;
-            t.next_dis[o] = ((y00 + y01) + (y10 + y11)) * 0.25f + kMomentOffset;
+        const int nw = min(xe / 2, W / 2) - nx0, nh = min(ye / 2, H / 2) - ny0;
+        for (int r = (int)threadIdx.x / CW; r < nh; r += RS) {
+            for (int c = (int)threadIdx.x % CW; c < nw; c += CW) {
+                const int l = 2 * r * IP + 2 * c;  // tile-local cell of the block, 8-byte aligned
+                const float2 x0v = *reinterpret_cast<const float2 *>(sx + l);
+                const float2 x1v = *reinterpret_cast<const float2 *>(sx + l + IP);
+                const float2 y0v = *reinterpret_cast<const float2 *>(sy + l);
+                const float2 y1v = *reinterpret_cast<const float2 *>(sy + l + IP);
+                const int o = (ny0 + r) * next_pitch + nx0 + c;
+                t.next_ref[o] = fmaf((x0v.x + x0v.y) + (x1v.x + x1v.y), 0.25f, kMomentOffset);
+                t.next_dis[o] = fmaf((y0v.x + y0v.y) + (y1v.x + y1v.y), 0.25f, kMomentOffset);
+            }
         }
     }
 
-    horizontal_moments_in_place<TW, TH, NT>(lds, taps);
+    horizontal_moments_in_place<TW, TH, NT, kNP>(lds, taps);
 
     // Per pixel: l = 1 - (mx - my)^2 / (mux^2 + muy^2 + C1) and
     // c = 1 - (sx - sy)^2 / (sx^2 + sy^2 + C2) (the mirrored quotients
@@ -88,8 +95,8 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
     constexpr float kC3 = kC2 / 2.0f;
     float dl = 0.0f, dc = 0.0f, ps = 0.0f;
     int npx = 0;
-    vertical_moments<TW, TH, NT, RB>(lds, taps, x0, y0, MW, MH,
-                                     [&](int, int, float mx, float my, float xx, float yy, float xy) {
+    vertical_moments<TW, TH, NT, RB, kNP>(lds, taps, x0, y0, MW, MH, [&](int, int, const float (&m)[kNP]) {
+        const float mx = m[0], my = m[1], xx = m[2], yy = m[3], xy = m[4];
         const float vx = fmaxf(fmaf(-mx, mx, xx), 0.0f);
         const float vy = fmaxf(fmaf(-my, my, yy), 0.0f);
         const float cxy = fmaf(-mx, my, xy);

@@ -43,26 +43,34 @@ constexpr int in_pitch() {
     return TW + 12;
 }
 
-// LDS of a tile: the staged input (two planes, IH rows of pitch
-// in_pitch<TW>()) and, after the horizontal pass, the five horizontal moment
-// planes (IH x TW each) in the same buffer.
-template <int TW, int TH>
-constexpr int tile_lds_floats() {
-    constexpr int stage = 2 * (TH + 10) * in_pitch<TW>(), moments = 5 * (TH + 10) * TW;
-    return stage > moments ? stage : moments;
+// The separable pass filters NP moment planes.  float_ssim needs the two
+// variances only as their sum, so it filters four: x, y, x^2 + y^2 and xy.
+// MS-SSIM's contrast term needs sigma_x and sigma_y apart, so it filters
+// five: x, y, x^2, y^2 and xy.
+template <int NP>
+constexpr bool valid_moment_set() {
+    return NP == 4 || NP == 5;
 }
 
 // LDS float offset, relative to the first staged plane, where threads past a
 // staged tile's last cell put their (unused) value, so that every thread
 // stores: a store under a per-lane condition lets the compiler sink the
 // matching load behind the stores of earlier cells, and the tile then costs
-// two memory latencies.  It lies past both staged planes and inside the
-// tile's buffer (sized for the moment planes), four floats wide.
+// two memory latencies.  It lies past both staged planes, four floats wide
+// (for either plane's base, so up to 3 IH IP + 4 floats into the buffer).
 template <int TW, int TH>
 constexpr int stage_spare() {
-    constexpr int IH = TH + 10, IP = in_pitch<TW>();
-    static_assert(2 * IH * IP + IH * IP + 4 <= tile_lds_floats<TW, TH>(), "no spare LDS past the staged tile");
-    return 2 * IH * IP;
+    return 2 * (TH + 10) * in_pitch<TW>();
+}
+
+// LDS of a tile: the staged input (two planes, IH rows of pitch
+// in_pitch<TW>(), plus the spare slot) and, after the horizontal pass, the NP
+// horizontal moment planes (IH x TW each) in the same buffer.
+template <int TW, int TH, int NP>
+constexpr int tile_lds_floats() {
+    static_assert(valid_moment_set<NP>(), "four or five moment planes");
+    constexpr int stage = 3 * (TH + 10) * in_pitch<TW>() + 4, moments = NP * (TH + 10) * TW;
+    return stage > moments ? stage : moments;
 }
 
 // Stage the (TH + 10) x (TW + 10) input tile of both planes at (x0, y0),
@@ -190,28 +198,34 @@ inline bool stage_vec4_ok(const void *p, int pitch, size_t sample_bytes) {
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
 
-// Per-pixel SSIM term from the five (offset) moments, as
-// (1 - (mx - my)^2 / A)(1 - v / B) with A = mux^2 + muy^2 + C1,
-// B = sxx + syy + C2 and v = sxx + syy - 2 sxy (the variance of x - y):
-// algebraically ((2 mux muy + C1)(2 sxy + C2)) / (A B), and exactly 1 for
-// identical planes, since then mx = my and sxx = syy = sxy bit for bit.
-__device__ __forceinline__ float ssim_term(float mx, float my, float xx, float yy, float xy) {
-    const float sxx = xx - mx * mx;
-    const float syy = yy - my * my;
+// The sum of two squares as the four-plane set forms it: fma(a, a, b * b).
+// When a = b this is 2 fl(a^2) exactly: the exact a^2 + fl(a^2) lies within a
+// quarter of an ulp of 2 fl(a^2).
+__device__ __forceinline__ float sum_of_squares(float a, float b) { return fmaf(a, a, b * b); }
+
+// Per-pixel SSIM term from the four (offset) moments mx, my, ss = E[x^2 + y^2]
+// and xy = E[xy], as (1 - (mx - my)^2 / A)(1 - v / B) with
+// A = mux^2 + muy^2 + C1, S = sxx + syy = ss - (mx^2 + my^2), B = S + C2 and
+// v = S - 2 sxy (the variance of x - y): algebraically
+// ((2 mux muy + C1)(2 sxy + C2)) / (A B).  Exactly 1 for identical planes:
+// then every x^2 + y^2 is 2 fl(x^2), and doubling commutes with each rounding
+// of the filters, so ss = 2 xy, mx = my and S = 2 sxy bit for bit.
+__device__ __forceinline__ float ssim_term4(float mx, float my, float ss, float xy) {
+    const float S = ss - sum_of_squares(mx, my);
     const float sxy = xy - mx * my;
     const float ux = mx + kMomentOffset;
     const float uy = my + kMomentOffset;
     const float dm = mx - my;
     const float A = ux * ux + uy * uy + kC1;
-    const float B = sxx + syy + kC2;
-    const float v = (sxx + syy) - (sxy + sxy);
+    const float B = S + kC2;
+    const float v = S - (sxy + sxy);
     // One reciprocal for both quotients (A * B stays far inside fp32 range).
     const float r = rcp(A * B);
     return (1.0f - dm * dm * (B * r)) * (1.0f - v * (A * r));
 }
 
 // Horizontal 11-tap pass of one item: four adjacent columns c0..c0+3 of
-// tile row r, for x, y, x^2, y^2 and xy, from the 14 inputs of each plane
+// tile row r, for the NP moment planes, from the 14 inputs of each plane
 // (FMA order k = 0..10).
 __device__ __forceinline__ void h_item_load(const float *pa, const float *pb, float (&a)[14], float (&b)[14]) {
 #pragma unroll
@@ -227,17 +241,26 @@ __device__ __forceinline__ void h_item_load(const float *pa, const float *pb, fl
     b[12] = vb.x; b[13] = vb.y;
 }
 
+template <int NP>
 __device__ __forceinline__ void h_item_compute(const float (&a)[14], const float (&b)[14], const Taps &taps,
-                                               float (&m)[5][4]) {
-    float aa[14], bb[14], ab[14];
+                                               float (&m)[NP][4]) {
+    static_assert(valid_moment_set<NP>(), "four or five moment planes");
+    float q[NP - 2][14];  // the second-order products of each input
 #pragma unroll
     for (int i = 0; i < 14; ++i) {
-        aa[i] = a[i] * a[i];
-        bb[i] = b[i] * b[i];
-        ab[i] = a[i] * b[i];
+        if constexpr (NP == 5) {
+            q[0][i] = a[i] * a[i];
+            q[1][i] = b[i] * b[i];
+            q[2][i] = a[i] * b[i];
+        } else {
+            q[0][i] = sum_of_squares(a[i], b[i]);
+            q[1][i] = a[i] * b[i];
+        }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m[0][j] = m[1][j] = m[2][j] = m[3][j] = m[4][j] = 0.f;
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[p][j] = 0.f;
 #pragma unroll
     for (int k = 0; k < 11; ++k) {
         const float g = taps.g[k];
@@ -245,22 +268,25 @@ __device__ __forceinline__ void h_item_compute(const float (&a)[14], const float
         for (int j = 0; j < 4; ++j) {
             m[0][j] = fmaf(g, a[j + k], m[0][j]);
             m[1][j] = fmaf(g, b[j + k], m[1][j]);
-            m[2][j] = fmaf(g, aa[j + k], m[2][j]);
-            m[3][j] = fmaf(g, bb[j + k], m[3][j]);
-            m[4][j] = fmaf(g, ab[j + k], m[4][j]);
+#pragma unroll
+            for (int p = 0; p < NP - 2; ++p) m[2 + p][j] = fmaf(g, q[p][j + k], m[2 + p][j]);
         }
     }
 }
 
 // The horizontal pass over a staged tile, in place: the moment planes
 // (plane p at lds + p * IH * TW, row pitch TW) overwrite the staged input.
+// Item i is row i / (TW/4), columns 4 (i % (TW/4)) on.  (Reading two staged
+// rows whose offsets differ by half the LDS banks in one step instead halves
+// the bank conflicts, 18 % -> 10 % of LDS-active cycles, but the kernels are
+// VALU-bound and ran no faster.)
 // Each thread has at most two items (row, four columns).  It computes its
 // first item and reads the inputs of its second into registers, then the
 // workgroup synchronises, and only then are the moments written — so the
 // tile needs the LDS of the larger of the two layouts, not of both, and more
 // workgroups fit on a CU.  Ends with the moment planes visible to the whole
 // workgroup.
-template <int TW, int TH, int NT>
+template <int TW, int TH, int NT, int NP>
 __device__ __forceinline__ void horizontal_moments_in_place(float *lds, const Taps &taps) {
     constexpr int IH = TH + 10, IP = in_pitch<TW>(), QW = TW / 4, PL = IH * TW;
     constexpr int ITEMS = IH * QW;
@@ -270,35 +296,35 @@ __device__ __forceinline__ void horizontal_moments_in_place(float *lds, const Ta
     const bool has1 = i1 < ITEMS, has2 = i2 < ITEMS;
     const int r1 = i1 / QW, c1 = (i1 - r1 * QW) * 4;
     const int r2 = i2 / QW, c2 = (i2 - r2 * QW) * 4;
-    float m[5][4];
+    float m[NP][4];
     float a[14], b[14];
     if (has1) {
         h_item_load(sx + r1 * IP + c1, sy + r1 * IP + c1, a, b);
-        h_item_compute(a, b, taps, m);
+        h_item_compute<NP>(a, b, taps, m);
     }
     if (has2) h_item_load(sx + r2 * IP + c2, sy + r2 * IP + c2, a, b);
     __syncthreads();  // every read of the staged tile is done
     if (has1) {
         const int o = r1 * TW + c1;
 #pragma unroll
-        for (int p = 0; p < 5; ++p)
+        for (int p = 0; p < NP; ++p)
             *reinterpret_cast<float4 *>(lds + p * PL + o) = make_float4(m[p][0], m[p][1], m[p][2], m[p][3]);
     }
     if (has2) {
-        h_item_compute(a, b, taps, m);
+        h_item_compute<NP>(a, b, taps, m);
         const int o = r2 * TW + c2;
 #pragma unroll
-        for (int p = 0; p < 5; ++p)
+        for (int p = 0; p < NP; ++p)
             *reinterpret_cast<float4 *>(lds + p * PL + o) = make_float4(m[p][0], m[p][1], m[p][2], m[p][3]);
     }
     __syncthreads();
 }
 
 // Vertical pass: for RB stacked map rows of one tile column at a time, the
-// five moments from RB + 10 values of each horizontal plane (FMA order
-// k = 0..10), handed to `fn(r, c, mx, my, xx, yy, xy)` for every map pixel
-// inside the valid region (mx0 = x0 + c < MW, y0 + r < MH).
-template <int TW, int TH, int NT, int RB, typename F>
+// NP moments from RB + 10 values of each horizontal plane (FMA order
+// k = 0..10), handed to `fn(r, c, m)` (m: the NP moments of the pixel) for
+// every map pixel inside the valid region (x0 + c < MW, y0 + r < MH).
+template <int TW, int TH, int NT, int RB, int NP, typename F>
 __device__ __forceinline__ void vertical_moments(const float *hm, const Taps &taps, int x0, int y0, int MW,
                                                  int MH, F &&fn) {
     static_assert(TH % RB == 0, "tile height must be a multiple of the row block");
@@ -306,9 +332,9 @@ __device__ __forceinline__ void vertical_moments(const float *hm, const Taps &ta
     for (int it = threadIdx.x; it < (TH / RB) * TW; it += NT) {
         const int c = it % TW, r0 = (it / TW) * RB;
         if (x0 + c >= MW || y0 + r0 >= MH) continue;
-        float m[5][RB];
+        float m[RB][NP];
 #pragma unroll
-        for (int p = 0; p < 5; ++p) {
+        for (int p = 0; p < NP; ++p) {
             float v[RB + 10];
 #pragma unroll
             for (int i = 0; i < RB + 10; ++i) v[i] = hm[p * PL + (r0 + i) * TW + c];
@@ -317,12 +343,12 @@ __device__ __forceinline__ void vertical_moments(const float *hm, const Taps &ta
                 float acc = 0.f;
 #pragma unroll
                 for (int k = 0; k < 11; ++k) acc = fmaf(taps.g[k], v[j + k], acc);
-                m[p][j] = acc;
+                m[j][p] = acc;
             }
         }
 #pragma unroll
         for (int j = 0; j < RB; ++j)
-            if (y0 + r0 + j < MH) fn(r0 + j, c, m[0][j], m[1][j], m[2][j], m[3][j], m[4][j]);
+            if (y0 + r0 + j < MH) fn(r0 + j, c, m[j]);
     }
 }
 
@@ -348,11 +374,27 @@ __device__ __forceinline__ void block_sum(double (&v)[NV], double (*red)[NT / 64
     }
 }
 
-// Sum over the 64 lanes of a wave in fp32, in the same fixed butterfly order.
+// v plus lane (lane ^ 1), (lane ^ 2), or the lane mirrored in its row of 8
+// or 16 lanes, as one DPP add.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xF, false);
+    return v + __builtin_bit_cast(float, o);
+}
+
+// Sum over the 64 lanes of a wave in fp32, in a fixed order: pairs, quads
+// (DPP quad permutations), rows of 8 and 16 (row half-mirror and mirror), then
+// row 0 into row 1 and row 2 into row 3 (row broadcast 15), then rows 0-1 into
+// rows 2-3 (row broadcast 31).  The total is in lane 63 and returned to every
+// lane (a wave-uniform value).
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // Workgroup sum of a tile's map terms: each thread's few terms and then the

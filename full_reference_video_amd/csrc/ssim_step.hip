@@ -22,7 +22,8 @@
 //
 // Map role: a workgroup scores TW x TH tiles of the map one after another.
 // A tile's (TW+10) x (TH+10) input window of both planes is staged in LDS, the
-// horizontal 11-tap pass writes five moment planes over it (four columns per
+// horizontal 11-tap pass writes four moment planes over it (x, y, x^2 + y^2
+// and xy: the map needs the two variances only as their sum; four columns per
 // thread step), and the vertical pass (four rows per thread step) forms the
 // moments of each map pixel and its SSIM term in fp32, with the mid-scale
 // offset removed first so E[x^2] - mu^2 cancels less.  Each thread adds its
@@ -40,6 +41,7 @@ namespace {
 
 constexpr int kNT = 256;                       // threads per workgroup, every role
 constexpr int kTW = 32, kTH = 32, kRB = 4;     // map tile
+constexpr int kNP = 4;                         // moment planes: x, y, x^2 + y^2, xy
 constexpr int kDecWaves = kNT / 64;            // waves per decimation workgroup
 
 // ------------------------------------------------------------ decimation policies
@@ -86,11 +88,22 @@ struct DecGeneral {
 __host__ __device__ inline int tiles_x(const StepGeometry &g) { return (g.dec_w - 10 + kTW - 1) / kTW; }
 __host__ __device__ inline int tiles_y(const StepGeometry &g) { return (g.dec_h - 10 + kTH - 1) / kTH; }
 
-template <typename TIn>
+// In the looping layout (below) the tile buffer is oversized on purpose: LDS
+// (160 KiB per CU) is what limits how many step workgroups share a CU, and at
+// 2160p the decimation streams fastest with at most three of them per CU.
+// Measured per launch of 32 frames: 198.3 us with two, 189.1 us with three,
+// 190.9 us with four, 192.1 us with no cap (VGPRs then allow four).
+constexpr int kLoopWorkgroupsPerCu = 3;
+constexpr int kLoopLdsFloats = (160 * 1024 / (kLoopWorkgroupsPerCu + 1)) / 4;
+static_assert(kLoopLdsFloats >= tile_lds_floats<kTW, kTH, kNP>(), "the capped tile buffer must hold the tile");
+static_assert(kLoopWorkgroupsPerCu * (kLoopLdsFloats * 4 + 1024) <= 160 * 1024,
+              "the capped buffer must still let kLoopWorkgroupsPerCu workgroups share a CU");
+
+template <typename TIn, bool kLoopMap>
 __device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const StepGeometry &g, int pitch,
                                          float unit, bool vec4, const Taps &taps) {
     constexpr int IH = kTH + 10, IP = in_pitch<kTW>();
-    __shared__ __attribute__((aligned(16))) float lds[tile_lds_floats<kTW, kTH>()];
+    __shared__ __attribute__((aligned(16))) float lds[kLoopMap ? kLoopLdsFloats : tile_lds_floats<kTW, kTH, kNP>()];
     __shared__ double red[1][kNT / 64];
     float *sx = lds, *sy = lds + IH * IP;
 
@@ -103,14 +116,14 @@ __device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const St
 
     stage<kTW, kTH, kNT>(ref, dis, pitch, W, H, unit, x0, y0, sx, sy, vec4);
     __syncthreads();
-    horizontal_moments_in_place<kTW, kTH, kNT>(lds, taps);
+    horizontal_moments_in_place<kTW, kTH, kNT, kNP>(lds, taps);
 
     // A thread's few map pixels and then its wave are summed in fp32, the
     // waves in fp64.
     float part = 0.0f;
-    vertical_moments<kTW, kTH, kNT, kRB>(lds, taps, x0, y0, MW, MH,
-                                         [&](int, int, float mx, float my, float xx, float yy, float xy) {
-        part += ssim_term(mx, my, xx, yy, xy);
+    vertical_moments<kTW, kTH, kNT, kRB, kNP>(lds, taps, x0, y0, MW, MH,
+                                              [&](int, int, const float (&m)[kNP]) {
+        part += ssim_term4(m[0], m[1], m[2], m[3]);
     });
 
     const float terms[1] = {part};
@@ -175,14 +188,14 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
 #pragma unroll 1
             for (int m = m0 + q; m < m1; m += lay.map_wg) {
                 const int f = m / map_pf;
-                map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                map_tile<TIn, kLoopMap>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
                 __syncthreads();  // the next tile reuses the LDS
             }
         } else {
             const int m = m0 + q;
             if (m < m1) {
                 const int f = m / map_pf;
-                map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                map_tile<TIn, kLoopMap>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
             }
         }
         return;
