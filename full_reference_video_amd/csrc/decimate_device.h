@@ -71,7 +71,7 @@ __device__ __forceinline__ uint64_t product_units(uint32_t raw, float tap, int s
 // 4 by + wave).
 template <typename T>
 __device__ __forceinline__ void general_block(const DecimateFrame &fr, int bx, int by, int w, int h, int bpc,
-                                              int s, float tap, int dec_w, int dec_h, int opitch) {
+                                              int s, float tap, int dec_w, int dec_h, int opitch, bool packed) {
     const T *__restrict__ ref = static_cast<const T *>(fr.ref);
     const T *__restrict__ dis = static_cast<const T *>(fr.dis);
     const int X = bx * 64 + (threadIdx.x & 63);
@@ -88,11 +88,19 @@ __device__ __forceinline__ void general_block(const DecimateFrame &fr, int bx, i
             ad += product_units(dis[row + xx], tap, shift_base);
         }
     }
+    const size_t o = (size_t)Y * opitch + X;
+    if (packed) {
+        // s = 2^k: every product is raw * 2^(60 - 2k - bpc) units, so the
+        // shift gives the window's raw integer sum back exactly.
+        const int shift = 60 - 2 * (__ffs(s) - 1) - bpc;
+        static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)(ar >> shift);
+        static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)(ad >> shift);
+        return;
+    }
     // One rounding to fp32 (the sum has at most 53 significant bits), then an
     // exact scaling by 2^-52.
-    const size_t o = (size_t)Y * opitch + X;
-    fr.out_ref[o] = (float)ar * 0x1p-52f;
-    fr.out_dis[o] = (float)ad * 0x1p-52f;
+    static_cast<float *>(fr.out_ref)[o] = (float)ar * 0x1p-52f;
+    static_cast<float *>(fr.out_dis)[o] = (float)ad * 0x1p-52f;
 }
 
 // ------------------------------------------------------------ power-of-two path
@@ -152,7 +160,7 @@ template <typename T, int S> struct Pow2Shape {
 // One wave of the power-of-two kernel: wave wv of output row Y.
 template <typename T, int S>
 __device__ __forceinline__ void pow2_wave(const DecimateFrame &fr, int wv, int Y, int w, int h, int dec_w,
-                                          float post, int opitch) {
+                                          float post, int opitch, bool packed) {
     using Sh = Pow2Shape<T, S>;
     constexpr int V = Sh::V, NV = Sh::NV, CPT = Sh::CPT, G = Sh::G;
     constexpr int HALF = S / 2;
@@ -205,11 +213,17 @@ __device__ __forceinline__ void pow2_wave(const DecimateFrame &fr, int wv, int Y
         if (X < dec_w) {
             const uint32_t tr = (k == 0 ? pr : hr[k - 1]) + lr[k];
             const uint32_t td = (k == 0 ? pd : hd[k - 1]) + ld[k];
-            // One rounding (the only one: sums below 2^24 are exact), then
-            // the exact power of two.
             const size_t o = (size_t)Y * opitch + X;
-            fr.out_ref[o] = (float)tr * post;
-            fr.out_dis[o] = (float)td * post;
+            if (packed) {
+                // The raw sums themselves (below 2^16 when packed).
+                static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)tr;
+                static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)td;
+            } else {
+                // One rounding (the only one: sums below 2^24 are exact),
+                // then the exact power of two.
+                static_cast<float *>(fr.out_ref)[o] = (float)tr * post;
+                static_cast<float *>(fr.out_dis)[o] = (float)td * post;
+            }
         }
     }
 }

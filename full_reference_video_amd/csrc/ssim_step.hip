@@ -69,7 +69,7 @@ struct DecPow2 {
         const int u = b * kDecWaves + (int)(threadIdx.x >> 6);
         if (u >= wpr * g.dec_h) return;  // the frame's last workgroup may be partly empty
         const int Y = u / wpr;
-        dec::pow2_wave<T, S>(fr, u - Y * wpr, Y, g.w, g.h, g.dec_w, g.post, g.dec_pitch);
+        dec::pow2_wave<T, S>(fr, u - Y * wpr, Y, g.w, g.h, g.dec_w, g.post, g.dec_pitch, g.packed != 0);
     }
 };
 
@@ -79,7 +79,8 @@ struct DecGeneral {
     static int blocks_per_frame(const StepGeometry &g) { return blocks_x(g) * ((g.dec_h + 3) / 4); }
     __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
         const int bx = b % blocks_x(g), by = b / blocks_x(g);
-        dec::general_block<T>(fr, bx, by, g.w, g.h, g.bpc, g.s, g.tap, g.dec_w, g.dec_h, g.dec_pitch);
+        dec::general_block<T>(fr, bx, by, g.w, g.h, g.bpc, g.s, g.tap, g.dec_w, g.dec_h, g.dec_pitch,
+                              g.packed != 0);
     }
 };
 
@@ -262,6 +263,23 @@ hipError_t launch_dec_pow2(int s, const StepRoles &r, const StepGeometry &g, int
     }
 }
 
+// The packed scales: s = 2^k with bpc + 2k <= 16, so s <= 16 for 8-bit and
+// s <= 8 for deeper samples; the map reads the uint16 window sums.
+template <typename T>
+hipError_t launch_dec_pow2_packed(int s, const StepRoles &r, const StepGeometry &g, int map_pitch, float unit,
+                                  const Taps &taps, hipStream_t stream, const KernelTimer &timer) {
+    switch (s) {
+    case 2: return launch_step<DecPow2<T, 2>, uint16_t>(r, g, map_pitch, unit, taps, stream, timer);
+    case 4: return launch_step<DecPow2<T, 4>, uint16_t>(r, g, map_pitch, unit, taps, stream, timer);
+    case 8: return launch_step<DecPow2<T, 8>, uint16_t>(r, g, map_pitch, unit, taps, stream, timer);
+    case 16:
+        if constexpr (sizeof(T) == 1) return launch_step<DecPow2<T, 16>, uint16_t>(r, g, map_pitch, unit, taps,
+                                                                                 stream, timer);
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 bool decimate_fast_path(const DecimateBatch &b, int n, int w, int h, int bpc, int s) {
@@ -286,10 +304,20 @@ hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind ma
     if (r.n_dec < 0 || r.n_dec > kMaxBatch || r.n_map < 0 || r.n_map > kMaxBatch || r.n_fin < 0 ||
         r.n_fin > kMaxBatch)
         return hipErrorInvalidValue;
+    if ((g.packed != 0) != packed_planes(g.s, g.bpc)) return hipErrorInvalidValue;
     if (r.n_dec > 0) {
-        // Decimation feeds fp32 planes to the map role.
-        if (map_kind != IN_F32 && r.n_map > 0) return hipErrorInvalidValue;
+        // The map role reads what the decimation writes: uint16 window sums
+        // or fp32 values.
+        if (map_kind != (g.packed ? IN_U16 : IN_F32) && r.n_map > 0) return hipErrorInvalidValue;
         const bool fast = decimate_fast_path(r.dec, r.n_dec, g.w, g.h, g.bpc, g.s);
+        if (g.packed) {
+            if (g.bpc == 8) {
+                if (fast) return launch_dec_pow2_packed<uint8_t>(g.s, r, g, map_pitch, unit, taps, stream, timer);
+                return launch_step<DecGeneral<uint8_t>, uint16_t>(r, g, map_pitch, unit, taps, stream, timer);
+            }
+            if (fast) return launch_dec_pow2_packed<uint16_t>(g.s, r, g, map_pitch, unit, taps, stream, timer);
+            return launch_step<DecGeneral<uint16_t>, uint16_t>(r, g, map_pitch, unit, taps, stream, timer);
+        }
         if (g.bpc == 8) {
             if (fast) return launch_dec_pow2<uint8_t, float>(g.s, r, g, map_pitch, unit, taps, stream, timer);
             return launch_step<DecGeneral<uint8_t>, float>(r, g, map_pitch, unit, taps, stream, timer);

@@ -51,7 +51,8 @@ constexpr float kMomentOffset = 128.0f;
 
 struct DecimateFrame {
     const void *ref, *dis;       // raw planes, w x h, tightly packed
-    float *out_ref, *out_dis;    // dec_w x dec_h, row pitch dec_pitch floats
+    void *out_ref, *out_dis;     // dec_w x dec_h, row pitch dec_pitch samples: fp32 values, or the
+                                 // uint16 raw window sums when StepGeometry::packed
 };
 struct DecimateBatch {
     DecimateFrame f[kMaxBatch];
@@ -72,7 +73,22 @@ struct StepGeometry {
     float tap;                   // 1.0f / (s * s), formed on the host
     float post;                  // 2^-(2k + bpc - 8) when s = 2^k (power-of-two path)
     int dec_w, dec_h, dec_pitch; // decimated plane (= raw size at scale 1)
+    int packed;                  // packed_planes(s, bpc): the decimated planes hold uint16 window sums
 };
+
+// Whether the decimated planes can hold the integer sums of the raw window
+// samples as uint16 instead of fp32 values: s = 2^k >= 2 with
+// bpc + 2k <= 16, so that a window sum (s^2 samples below 2^bpc) fits 16
+// bits.  The decimated value is then exactly sum * post (an integer below
+// 2^24 times a power of two), so the map reads the same values from half the
+// bytes.  2160p 10-bit (s = 8: 10 + 6 = 16), 1080p 8-bit and 853x481 12-bit
+// qualify; 16-bit samples at s = 2 do not.
+inline bool packed_planes(int s, int bpc) {
+    if (s < 2 || (s & (s - 1)) != 0) return false;
+    int k = 0;
+    while ((1 << k) < s) ++k;
+    return bpc + 2 * k <= 16;
+}
 
 // The three independent roles of one step launch: decimate one batch, map
 // another (whose decimated planes an earlier launch wrote), finish a third
@@ -99,9 +115,9 @@ bool decimate_fast_path(const DecimateBatch &b, int n, int w, int h, int bpc, in
 int ssim_partials(int W, int H);
 
 // One step launch.  map_kind / map_pitch / unit describe the map role's
-// input: IN_F32 decimated planes (pitch dec_pitch, unit 1) whenever a
-// decimation role is present, raw samples (pitch w, unit 2^-(bpc-8)) at
-// scale 1.
+// input: the decimated planes whenever a decimation role is present (pitch
+// dec_pitch; IN_U16 window sums with unit post when g.packed, else IN_F32
+// values with unit 1), raw samples (pitch w, unit 2^-(bpc-8)) at scale 1.
 hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind map_kind, int map_pitch, float unit,
                             const Taps &taps, hipStream_t stream, const KernelTimer &timer);
 

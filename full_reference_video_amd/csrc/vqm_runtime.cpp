@@ -458,6 +458,7 @@ vqm::StepGeometry step_geometry(const Geometry &g) {
     sg.dec_w = g.dw;
     sg.dec_h = g.dh;
     sg.dec_pitch = g.dpitch;
+    sg.packed = vqm::packed_planes(g.s, g.bpc) ? 1 : 0;
     return sg;
 }
 
@@ -503,9 +504,12 @@ int step(vqm_ctx *ctx, PendingBatch *fresh) {
         for (int i = 0; i < to_finish->n; ++i) fill_map_frame(r.fin.f[i], *to_finish, i, decimating);
     }
     const vqm::StepGeometry sg = step_geometry(g);
-    const vqm::InKind kind = decimating ? vqm::IN_F32 : (g.bpc == 8 ? vqm::IN_U8 : vqm::IN_U16);
+    // The map reads the decimated planes (uint16 window sums scaled by post,
+    // or fp32 values), or the raw samples at scale 1.
+    const vqm::InKind kind = decimating ? (sg.packed ? vqm::IN_U16 : vqm::IN_F32)
+                                        : (g.bpc == 8 ? vqm::IN_U8 : vqm::IN_U16);
     const int pitch = decimating ? g.dpitch : g.w;
-    const float unit = decimating ? 1.0f : ldexpf(1.0f, -(g.bpc - 8));
+    const float unit = decimating ? (sg.packed ? sg.post : 1.0f) : ldexpf(1.0f, -(g.bpc - 8));
     const int cls = r.n_dec ? VQM_KERNEL_SSIM_STEP : VQM_KERNEL_SSIM_DRAIN;
     LAUNCH_TIMED(ctx, cls, r.n_dec ? r.n_dec : r.n_map,
                  vqm::launch_ssim_step(r, sg, kind, pitch, unit, ctx->taps, ctx->stream, timer_));
@@ -1072,14 +1076,31 @@ int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, in
     r.dec.f[0].dis = ddis;
     r.dec.f[0].out_ref = sl->planes + sl->off_ref[0];
     r.dec.f[0].out_dis = sl->planes + sl->off_dis[0];
+    const vqm::StepGeometry sg = step_geometry(g);
     LAUNCH_TIMED(ctx, VQM_KERNEL_SSIM_STEP, 1,
-                 vqm::launch_ssim_step(r, step_geometry(g), vqm::IN_F32, g.dpitch, 1.0f, ctx->taps, ctx->stream,
-                                           timer_));
-    HIP_TRY(hipMemcpy2DAsync(out_ref, g.dw * sizeof(float), sl->planes + sl->off_ref[0], g.dpitch * sizeof(float),
-                             g.dw * sizeof(float), g.dh, hipMemcpyDeviceToHost, ctx->stream));
-    HIP_TRY(hipMemcpy2DAsync(out_dis, g.dw * sizeof(float), sl->planes + sl->off_dis[0], g.dpitch * sizeof(float),
-                             g.dw * sizeof(float), g.dh, hipMemcpyDeviceToHost, ctx->stream));
+                 vqm::launch_ssim_step(r, sg, sg.packed ? vqm::IN_U16 : vqm::IN_F32, g.dpitch,
+                                       sg.packed ? sg.post : 1.0f, ctx->taps, ctx->stream, timer_));
+    if (!sg.packed) {
+        HIP_TRY(hipMemcpy2DAsync(out_ref, g.dw * sizeof(float), sl->planes + sl->off_ref[0],
+                                 g.dpitch * sizeof(float), g.dw * sizeof(float), g.dh, hipMemcpyDeviceToHost,
+                                 ctx->stream));
+        HIP_TRY(hipMemcpy2DAsync(out_dis, g.dw * sizeof(float), sl->planes + sl->off_dis[0],
+                                 g.dpitch * sizeof(float), g.dw * sizeof(float), g.dh, hipMemcpyDeviceToHost,
+                                 ctx->stream));
+        HIP_TRY(hipStreamSynchronize(ctx->stream));
+        return 0;
+    }
+    // Packed planes hold the window sums: the value is sum * post, exact.
+    std::vector<uint16_t> sums((size_t)g.dw * (size_t)g.dh * 2);
+    uint16_t *hs[2] = {sums.data(), sums.data() + (size_t)g.dw * g.dh};
+    const float *dev[2] = {sl->planes + sl->off_ref[0], sl->planes + sl->off_dis[0]};
+    for (int i = 0; i < 2; ++i)
+        HIP_TRY(hipMemcpy2DAsync(hs[i], g.dw * sizeof(uint16_t), dev[i], g.dpitch * sizeof(uint16_t),
+                                 g.dw * sizeof(uint16_t), g.dh, hipMemcpyDeviceToHost, ctx->stream));
     HIP_TRY(hipStreamSynchronize(ctx->stream));
+    float *outs[2] = {out_ref, out_dis};
+    for (int i = 0; i < 2; ++i)
+        for (size_t k = 0; k < (size_t)g.dw * g.dh; ++k) outs[i][k] = (float)hs[i][k] * sg.post;
     return 0;
 }
 

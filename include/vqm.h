@@ -259,7 +259,10 @@ VQM_API int vqm_ctx_kernel_time(vqm_ctx *ctx, int kernel_class, double *total_ms
  * floats each, tightly packed).  scale = 0 picks the automatic scale and
  * applies the float_ssim gate, exactly as vqm_ssim_submit does; scale in
  * 1..128 forces that factor (the decimated plane may then be any size >= 1).
- * At scale 1 the planes are the sample values v.  Blocking.  For the
+ * At scale 1 the planes are the sample values v.  Where the scoring path
+ * keeps the decimated planes as 16-bit window sums (scale 2^k with
+ * bpc + 2k <= 16), the kernels write those sums and this call returns them
+ * times 2^-(2k + bpc - 8), which is exact.  Blocking.  For the
  * bit-exactness tests ([ADR-1405] Decision 2). */
 VQM_API int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc,
                                int scale, float *out_ref, float *out_dis);

@@ -103,6 +103,23 @@ def test_decimate_extreme_values(ctx):
                 assert np.array_equal(bits(gr), bits(oracle.decimate(p, bpc, s)))
 
 
+@pytest.mark.parametrize("bpc,s", [(8, 16), (10, 8), (12, 4), (14, 2), (16, 2), (12, 8)])
+def test_decimate_window_sums_at_the_16_bit_limit(ctx, bpc, s):
+    # Where bpc + 2 log2(s) <= 16 the scoring path keeps the decimated planes
+    # as 16-bit window sums; all-maximum samples put the sum at its largest
+    # (s^2 (2^bpc - 1), just below 2^16 at the limit).  16-bit at s = 2 and
+    # 12-bit at s = 8 lie past the limit and keep fp32 planes.  Both the fast
+    # path (w a multiple of 16) and the general path (odd w) run.
+    for w, h in ((16 * s * 9, 7 * s), (16 * s * 9 + 3, 7 * s + 1)):
+        p = synth.random_planes(0, w, h, bpc, "max")
+        q = synth.random_planes(bpc, w, h, bpc)
+        say(f"decimate limit s {s} bpc {bpc} {w}x{h}")
+        gr, gd = ctx.vqm_debug_decimate(p, q, bpc, s)
+        assert np.array_equal(bits(gr), bits(oracle.decimate(p, bpc, s))), (bpc, s, w, h)
+        assert np.array_equal(bits(gd), bits(oracle.decimate(q, bpc, s))), (bpc, s, w, h)
+        assert gr.max() == float(s * s * ((1 << bpc) - 1)) / float(s * s << (bpc - 8))
+
+
 # ------------------------------------------------------------ float_ssim
 
 @pytest.mark.parametrize("c", [1, 2, 3, 4])
