@@ -92,6 +92,16 @@ def ms_flops_per_frame(w: int, h: int) -> float:
     return total
 
 
+def ssim_map_flops_per_frame(w: int, h: int, s: int) -> float:
+    """Algorithmic fp32 flops of one float_ssim frame's SSIM map: per valid map
+    pixel of the decimated plane, the separable 11-tap moments of the four
+    planes the map needs (x, y, x^2 + y^2, xy: 4 x 11 FMA horizontally and
+    vertically = 176 flops), the three products of its input sample (3) and
+    the per-pixel term (20, the reciprocal counted once)."""
+    dw, dh = -(-w // s), -(-h // s)
+    return float((dw - 10) * (dh - 10) * (176 + 3 + 20))
+
+
 def run_pass(ctxs, frameset, metric, batch, lag):
     """Score every frame pair of `frameset` once, as one continuous stream,
     through the C ABI's pipelined loop (batches rotate over the contexts; one
@@ -197,6 +207,9 @@ def main():
     ap.add_argument("--host-input", choices=("none", "pinned", "pageable"), default="none",
                     help="score frames from host memory (pinned tensors or pageable arrays) instead of HBM: the "
                          "end-to-end rate with one upload per frame, reported under its own metric name")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a recorded pass (vqm_graph_*) over the workload's device frames, one "
+                         "replay and one wait per step, reported under its own metric name")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB 20 times (a kernel of known "
                          "traffic, to calibrate the FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -284,18 +297,46 @@ def main():
             raise RuntimeError("scores changed between passes")
     torch.cuda.synchronize()
 
-    log(f"timed {args.reps} x {args.steps} passes over {wl.frames} frames, batch {args.batch}, "
-        f"{args.streams} streams, lag {lag}")
     frames = args.steps * wl.frames
     runs = []
-    for _ in range(args.reps):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        sc = run_pass(ctxs, stream_set, wl.metric, args.batch, lag)
-        torch.cuda.synchronize()
-        runs.append(time.perf_counter() - t0)
-        if ref_scores is not None and sc != ref_scores * args.steps:
-            raise RuntimeError("scores changed between passes")
+    if args.graph:
+        if args.host_input != "none":
+            raise SystemExit("--graph replays device-resident frames only")
+        # One recorded pass over the workload's frames; a step is one replay
+        # and its one wait.
+        graph = vqm.Graph(0, streams[0], vqm.VQM_METRIC_MS_SSIM if wl.metric == "ms_ssim"
+                          else vqm.VQM_METRIC_FLOAT_SSIM, vqm.FrameSet([r for r, _ in dev], [d for _, d in dev],
+                                                                        wl.bpc), args.batch)
+        for _ in range(max(1, args.warmup)):
+            graph.vqm_graph_launch()
+            got = graph.vqm_graph_collect().tolist()
+            if ref_scores is None:
+                ref_scores = got
+            elif got != ref_scores:
+                raise RuntimeError("a replay differs from the eager pass")
+        log(f"timed {args.reps} x {args.steps} graph replays over {wl.frames} frames, batch {args.batch}")
+        for _ in range(args.reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                graph.vqm_graph_launch()
+                sc = graph.vqm_graph_collect()
+            torch.cuda.synchronize()
+            runs.append(time.perf_counter() - t0)
+            if sc.tolist() != ref_scores:
+                raise RuntimeError("a replay differs from the eager pass")
+        graph.close()
+    else:
+        log(f"timed {args.reps} x {args.steps} passes over {wl.frames} frames, batch {args.batch}, "
+            f"{args.streams} streams, lag {lag}")
+        for _ in range(args.reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            sc = run_pass(ctxs, stream_set, wl.metric, args.batch, lag)
+            torch.cuda.synchronize()
+            runs.append(time.perf_counter() - t0)
+            if ref_scores is not None and sc != ref_scores * args.steps:
+                raise RuntimeError("scores changed between passes")
     el = sorted(runs)[len(runs) // 2]  # the median run
     fps = frames / el
 
@@ -324,14 +365,26 @@ def main():
 
     alg = algorithmic_bytes(wl, s)
     if wl.metric == "float_ssim":
+        # The step kernel streams the raw samples (HBM) and computes the SSIM
+        # map (VALU).  Both rooflines are computed; the one the kernel comes
+        # closer to binds (HBM at 2160p, the map's VALU work at the smaller
+        # frames, where there is little to decimate) and the other is listed
+        # under "other".
         name = "ssim_step" if "ssim_step" in kt else "ssim_drain"
         per_launch = alg * kt[name]["frames_per_launch"]
         avg_s = kt[name]["avg_us"] * 1e-6
         achieved = per_launch / avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(wl.name, kt[name]["frames_per_launch"]),
-                "kernel": "ssim_step", "bytes_per_launch": int(per_launch)}
+        hbm = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(achieved / HBM_PEAK_GBS, 4),
+               "traffic": recorded_traffic(wl.name, kt[name]["frames_per_launch"]),
+               "kernel": "ssim_step", "bytes_per_launch": int(per_launch)}
+        map_flops = ssim_map_flops_per_frame(wl.w, wl.h, s) * kt[name]["frames_per_launch"]
+        alu_tflops = map_flops / avg_s / 1e12
+        alu = {"bound": "alu", "achieved": round(alu_tflops, 2), "peak": round(FP32_VALU_PEAK_TFLOPS, 1),
+               "unit": "TFLOP/s", "frac": round(alu_tflops / FP32_VALU_PEAK_TFLOPS, 4), "traffic": hbm["traffic"],
+               "kernel": "ssim_step", "flops_per_launch": int(map_flops)}
+        roof, other = (hbm, alu) if hbm["frac"] >= alu["frac"] else (alu, hbm)
+        roof["other"] = {k: other[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
     else:
         # MS-SSIM is VALU-bound; every level kernel counts, with its share of
         # the frame's algorithmic flops.
@@ -348,7 +401,8 @@ def main():
     out = {
         "metric": ("frames/sec and achieved HBM GB/s (% of peak), float_ssim at 3840x2160"
                    if wl.index == 4 else f"frames/sec, {wl.name}")
-                  + ("" if args.host_input == "none" else f", end to end from {args.host_input} host frames"),
+                  + ("" if args.host_input == "none" else f", end to end from {args.host_input} host frames")
+                  + (", recorded-pass replays" if args.graph else ""),
         "value": round(fps, 1),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -363,6 +417,7 @@ def main():
         "config": {"workload": wl.name, "input": "hbm" if args.host_input == "none" else args.host_input + " host",
                    "w": wl.w, "h": wl.h, "bpc": wl.bpc, "frames_per_step": wl.frames,
                    "scale": s, "batch": args.batch, "streams": args.streams, "lag": lag,
+                   "mode": "graph replay" if args.graph else "stream",
                    "path_GBps": round(alg * fps / 1e9, 1)},
         "runs": {"n": len(runs), "frames_per_s_min": round(frames / max(runs), 1),
                  "frames_per_s_max": round(frames / min(runs), 1)},

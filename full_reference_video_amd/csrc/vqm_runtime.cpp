@@ -218,6 +218,7 @@ struct vqm_ctx {
     // per step launch) has not finished yet, oldest first; same geometry.
     std::deque<PendingBatch> pipeline;
     bool timing = false;
+    bool capturing = false;              // launches go into a graph: no completion events
     std::vector<TimedLaunch> timed;      // recorded, not yet read
     std::vector<hipEvent_t> event_pool;  // free timing events
     double time_ms[4] = {0, 0, 0, 0};
@@ -513,7 +514,7 @@ int step(vqm_ctx *ctx, PendingBatch *fresh) {
     const int cls = r.n_dec ? VQM_KERNEL_SSIM_STEP : VQM_KERNEL_SSIM_DRAIN;
     LAUNCH_TIMED(ctx, cls, r.n_dec ? r.n_dec : r.n_map,
                  vqm::launch_ssim_step(r, sg, kind, pitch, unit, ctx->taps, ctx->stream, timer_));
-    if (to_finish) {
+    if (to_finish && !ctx->capturing) {
         BatchEvent *be = nullptr;
         int rc = take_batch_event(ctx, &be);
         if (rc) return rc;
@@ -913,9 +914,167 @@ int debug_slot(vqm_ctx *ctx, const Geometry &g, const void *ref, const void *dis
 
 }  // namespace
 
+// A recorded scoring pass over a fixed set of device-resident frames
+// ("ADR-1357: Run the SYCL CAMBI extractor entirely on the device", Decision
+// and Consequences: the kernels register once with a combined graph and its
+// replay absorbs their launches; "Research-1363: Device-resident ssimulacra2
+// and a single-wait MS-SSIM on SYCL", Finding 6: one wait per pass).  It owns
+// a private context, whose first n slots hold the frames' scratch and
+// results for the graph's lifetime.
+struct vqm_graph {
+    vqm_ctx *ctx = nullptr;
+    int kind = KIND_NONE;
+    int n = 0;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t done = nullptr;
+    bool pending = false;  // launched and not yet collected
+};
+
+namespace {
+
+// Record every launch of one pass over the frames (float_ssim: the step
+// pipeline and its drain; MS-SSIM: five levels and the combine per batch)
+// into g->graph.  The frames are device memory, so the pass has no copies;
+// it records no events and no memsets.
+int record_pass(vqm_graph *g, const void *const *refs, const void *const *dis, int w, int h, int bpc,
+                int batch) {
+    vqm_ctx *ctx = g->ctx;
+    const Geometry geo = make_geometry(g->kind, w, h, bpc);
+    for (int i = 0; i < g->n; ++i) {
+        int rc = prepare_slot(ctx->slots[i], geo);
+        if (rc) return rc;
+        for (int k = 0; k < 16; ++k) ctx->slots[i].result_host[k] = NAN;
+    }
+    HIP_TRY(hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal));
+    ctx->capturing = true;
+    int rc = 0;
+    for (int b0 = 0; b0 < g->n && rc == 0; b0 += batch) {
+        PendingBatch p;
+        p.n = g->n - b0 < batch ? g->n - b0 : batch;
+        for (int i = 0; i < p.n; ++i) {
+            p.sl[i] = &ctx->slots[b0 + i];
+            p.in_r[i] = refs[b0 + i];
+            p.in_d[i] = dis[b0 + i];
+        }
+        rc = g->kind == KIND_SSIM ? step(ctx, &p) : enqueue_msssim(ctx, p.sl, p.n, p.in_r, p.in_d);
+    }
+    if (rc == 0 && g->kind == KIND_SSIM) rc = drain(ctx);
+    ctx->capturing = false;
+    ctx->pipeline.clear();
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(ctx->stream, &graph);
+    if (rc) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+    }
+    if (e != hipSuccess) return fail(-EIO, "hipStreamEndCapture: %s", hipGetErrorString(e));
+    g->graph = graph;
+    HIP_TRY(hipGraphInstantiateWithFlags(&g->exec, g->graph, 0));
+    return 0;
+}
+
+void destroy_graph(vqm_graph *g) {
+    if (!g) return;
+    if (g->ctx) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(g->ctx->device);
+        (void)hipStreamSynchronize(g->ctx->stream);
+        if (g->exec) (void)hipGraphExecDestroy(g->exec);
+        if (g->graph) (void)hipGraphDestroy(g->graph);
+        if (g->done) (void)hipEventDestroy(g->done);
+        if (cur >= 0) (void)hipSetDevice(cur);
+        destroy(g->ctx);
+    }
+    delete g;
+}
+
+int graph_create(int device, void *stream, int metric, const void *const *refs, const void *const *dis, int n,
+                 int w, int h, int bpc, int batch, vqm_graph **out) {
+    if (!out) return fail(-EINVAL, "NULL output pointer");
+    *out = nullptr;
+    if (metric != VQM_METRIC_FLOAT_SSIM && metric != VQM_METRIC_MS_SSIM)
+        return fail(-EINVAL, "unknown metric %d", metric);
+    if (!refs || !dis) return fail(-EINVAL, "NULL plane array");
+    if (n < 1 || n > VQM_MAX_IN_FLIGHT) return fail(-EINVAL, "%d frames outside 1..%d", n, VQM_MAX_IN_FLIGHT);
+    if (batch < 1 || batch > VQM_MAX_BATCH) return fail(-EINVAL, "batch %d outside 1..%d", batch, VQM_MAX_BATCH);
+    for (int i = 0; i < n; ++i) {
+        int rc = check_args(refs[i], dis[i], w, h, bpc);
+        if (rc) return rc;
+    }
+    const int kind = metric == VQM_METRIC_MS_SSIM ? KIND_MSSSIM : KIND_SSIM;
+    int rc = gate(kind, w, h, bpc);
+    if (rc) return rc;
+    std::unique_ptr<vqm_graph, void (*)(vqm_graph *)> g(new vqm_graph(), destroy_graph);
+    g->kind = kind;
+    g->n = n;
+    rc = create(device, stream, &g->ctx);
+    if (rc) return rc;
+    for (int i = 0; i < n; ++i)
+        for (const void *p : {refs[i], dis[i]}) {
+            PtrKind k;
+            rc = classify(p, device, &k);
+            if (rc) return rc;
+            if (k != PTR_DEVICE) return fail(-EINVAL, "frame %d: a recorded pass takes device memory only", i);
+        }
+    HIP_TRY(hipEventCreateWithFlags(&g->done, hipEventDisableTiming));
+    rc = record_pass(g.get(), refs, dis, w, h, bpc, batch);
+    if (rc) return rc;
+    *out = g.release();
+    return 0;
+}
+
+int graph_launch(vqm_graph *g) {
+    if (!g) return fail(-EINVAL, "NULL graph");
+    if (g->pending) return fail(-EBUSY, "the previous replay has not been collected");
+    int rc = ensure_device(g->ctx);
+    if (rc) return rc;
+    HIP_TRY(hipGraphLaunch(g->exec, g->ctx->stream));
+    HIP_TRY(hipEventRecord(g->done, g->ctx->stream));
+    g->pending = true;
+    return 0;
+}
+
+int graph_collect(vqm_graph *g, double *scores, double *lcs, double *db) {
+    if (!g || !scores) return fail(-EINVAL, "NULL argument");
+    if (!g->pending) return fail(-EAGAIN, "no replay in flight");
+    int rc = ensure_device(g->ctx);
+    if (rc) return rc;
+    HIP_TRY(hipEventSynchronize(g->done));  // the one wait of the replay
+    g->pending = false;
+    for (int i = 0; i < g->n; ++i) {
+        const Slot &sl = g->ctx->slots[i];
+        scores[i] = sl.result_host[0];
+        if (lcs && g->kind == KIND_MSSSIM) memcpy(lcs + 15 * (size_t)i, sl.result_host + 1, 15 * sizeof(double));
+        if (db) db[i] = g->kind == KIND_SSIM ? sl.result_host[1] : NAN;
+    }
+    return 0;
+}
+
+}  // namespace
+
 extern "C" {
 
 int vqm_abi_version(void) { return VQM_ABI_VERSION; }
+
+int vqm_graph_create(int device, void *hip_stream, int metric, const void *const *refs, const void *const *dis,
+                     int n, int w, int h, int bpc, int batch, vqm_graph **out) {
+    DeviceScope scope;
+    return graph_create(device, hip_stream, metric, refs, dis, n, w, h, bpc, batch, out);
+}
+
+int vqm_graph_launch(vqm_graph *g) {
+    DeviceScope scope;
+    return graph_launch(g);
+}
+
+int vqm_graph_collect(vqm_graph *g, double *scores, double *lcs, double *db) {
+    DeviceScope scope;
+    return graph_collect(g, scores, lcs, db);
+}
+
+void vqm_graph_destroy(vqm_graph *g) { destroy_graph(g); }
 
 int vqm_ssim_scale(int w, int h) {
     if (w <= 0 || h <= 0) return 0;

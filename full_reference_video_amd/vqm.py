@@ -88,6 +88,12 @@ def lib() -> ctypes.CDLL:
                                          c_void_p, c_void_p]
         L.vqm_debug_pyramid.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                         c_void_p, c_void_p]
+        L.vqm_graph_create.argtypes = [c_int, c_void_p, c_int, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p),
+                                       c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(c_void_p)]
+        L.vqm_graph_launch.argtypes = [c_void_p]
+        L.vqm_graph_collect.argtypes = [c_void_p, c_double_p, c_double_p, c_double_p]
+        L.vqm_graph_destroy.argtypes = [c_void_p]
+        L.vqm_graph_destroy.restype = None
         L.vqm_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -382,7 +388,7 @@ class FrameSet:
             self._keep.append(k)
 
 
-def vqm_score_frames(ctxs, metric: int, frames: FrameSet, batch: int = 8, lag: int = 0,
+def vqm_score_frames(ctxs, metric: int, frames: FrameSet, batch: int = VQM_MAX_BATCH, lag: int = 0,
                      want_lcs: bool = False, want_db: bool = False):
     """Score every frame of `frames` through the contexts `ctxs` (see the C
     call); returns the scores, followed by the 15 MS-SSIM level means per
@@ -399,3 +405,50 @@ def vqm_score_frames(ctxs, metric: int, frames: FrameSet, batch: int = 8, lag: i
                                   db.ctypes.data_as(dp) if want_db else None), "vqm_score_frames")
     out = (scores,) + ((lcs,) if want_lcs else ()) + ((db,) if want_db else ())
     return out if len(out) > 1 else scores
+
+
+class Graph:
+    """A ``vqm_graph``: one scoring pass over a fixed FrameSet of device
+    frames, recorded once and replayed (see vqm_graph_create)."""
+
+    def __init__(self, device: int, stream, metric: int, frames: FrameSet, batch: int = VQM_MAX_BATCH):
+        self._h = ctypes.c_void_p()
+        # the frames and the stream stay referenced for the graph's lifetime
+        self.metric, self.frames, self._stream = int(metric), frames, stream
+        _check(lib().vqm_graph_create(int(device), _stream_handle(stream), self.metric, frames.refs, frames.diss,
+                                      frames.n, frames.w, frames.h, frames.bpc, int(batch), ctypes.byref(self._h)),
+               "vqm_graph_create")
+
+    def vqm_graph_launch(self):
+        _check(lib().vqm_graph_launch(self._h), "vqm_graph_launch")
+
+    def vqm_graph_collect(self, want_lcs: bool = False, want_db: bool = False):
+        """The replay's scores, followed by the per-level means when want_lcs
+        and the decibel forms when want_db."""
+        n = self.frames.n
+        scores = np.empty(n, np.float64)
+        lcs = np.empty((n, VQM_MSSSIM_LCS), np.float64) if want_lcs else None
+        db = np.empty(n, np.float64) if want_db else None
+        dp = ctypes.POINTER(ctypes.c_double)
+        _check(lib().vqm_graph_collect(self._h, scores.ctypes.data_as(dp),
+                                       lcs.ctypes.data_as(dp) if want_lcs else None,
+                                       db.ctypes.data_as(dp) if want_db else None), "vqm_graph_collect")
+        out = (scores,) + ((lcs,) if want_lcs else ()) + ((db,) if want_db else ())
+        return out if len(out) > 1 else scores
+
+    def close(self):
+        if self._h:
+            lib().vqm_graph_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass

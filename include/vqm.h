@@ -229,6 +229,41 @@ VQM_API int vqm_score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const v
                              const void *const *dis, int n, int w, int h, int bpc, int batch, int lag,
                              double *scores, double *lcs, double *db);
 
+/* ---- recorded passes: one HIP graph replayed over a fixed set of frames ---- */
+
+typedef struct vqm_graph vqm_graph;
+
+/* Record one scoring pass over n (1..VQM_MAX_IN_FLIGHT) frame pairs as a HIP
+ * graph on `device` and `hip_stream` (NULL: a stream of the graph's own):
+ * for float_ssim the step launches of every batch of `batch`
+ * (1..VQM_MAX_BATCH) frames and the pipeline's drain, for MS-SSIM the five
+ * level launches and the combine of every batch
+ * ([ADR-1357] Decision and Consequences: a frame's kernels registered once
+ * with a combined graph, whose replay absorbs their launches; [R-1363]
+ * Finding 6: one wait per pass).  refs[i], dis[i] must be device memory of
+ * that device, w x h samples of bpc bits as in vqm_ssim_submit; the graph
+ * keeps their addresses and reads whatever they hold when it is replayed.
+ * The graph owns its scratch (n frame slots).  The same gate and argument
+ * checks as a submit apply; on error nothing is recorded and *out is NULL. */
+VQM_API int vqm_graph_create(int device, void *hip_stream, int metric, const void *const *refs,
+                             const void *const *dis, int n, int w, int h, int bpc, int batch, vqm_graph **out);
+
+/* Enqueue one replay of the recorded pass on the graph's stream and return
+ * without waiting.  -EBUSY while the previous replay is not collected (a
+ * replay overwrites the results of the last one). */
+VQM_API int vqm_graph_launch(vqm_graph *g);
+
+/* Wait for the replay (its one device wait) and read its n scores into
+ * scores[0..n-1]; lcs (may be NULL) receives 15 doubles per frame for
+ * MS-SSIM, db (may be NULL) each float_ssim frame's decibel form (NaN for
+ * MS-SSIM).  -EAGAIN when no replay is in flight.  After it returns the
+ * caller may overwrite the frames for the next replay. */
+VQM_API int vqm_graph_collect(vqm_graph *g, double *scores, double *lcs, double *db);
+
+/* Wait for the graph's stream, then free the graph and its scratch.  NULL is
+ * a no-op. */
+VQM_API void vqm_graph_destroy(vqm_graph *g);
+
 /* ---- measurement and inspection ---- */
 
 /* Turn per-kernel timing on or off: while on, every decimation, SSIM and

@@ -41,9 +41,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_binding_names_match_the_abi():
     for n in declared_symbols():
-        if n in ("vqm_ctx_destroy",):
-            continue
-        assert hasattr(vqm, n) or hasattr(vqm.Context, n), n
+        if n in ("vqm_ctx_destroy", "vqm_graph_create", "vqm_graph_destroy"):
+            continue  # Context() / Graph() and their close()
+        assert hasattr(vqm, n) or hasattr(vqm.Context, n) or hasattr(vqm.Graph, n), n
 
 
 def header_constants():
@@ -118,6 +118,33 @@ def test_argument_errors_before_any_hip_call():
     assert L.vqm_collect(None, ctypes.byref(s), None) == -errno.EINVAL
     assert L.vqm_collect_db(None, ctypes.byref(s), None) == -errno.EINVAL
     assert L.vqm_ssim_submit(None, p, p, 20, 20, 8) == -errno.EINVAL
+
+
+def test_graph_argument_errors_before_any_hip_call():
+    L = vqm.lib()
+    a = np.zeros((400, 400), np.uint8)
+    p = a.ctypes.data
+    arr = (ctypes.c_void_p * 2)(p, p)
+    g = ctypes.c_void_p(7)
+    out = ctypes.byref(g)
+    F, M = vqm.VQM_METRIC_FLOAT_SSIM, vqm.VQM_METRIC_MS_SSIM
+    assert L.vqm_graph_create(0, None, 2, arr, arr, 2, 400, 400, 8, 8, out) == -errno.EINVAL  # metric
+    assert L.vqm_graph_create(0, None, F, None, arr, 2, 400, 400, 8, 8, out) == -errno.EINVAL
+    assert L.vqm_graph_create(0, None, F, arr, arr, 0, 400, 400, 8, 8, out) == -errno.EINVAL
+    big = (ctypes.c_void_p * (vqm.VQM_MAX_IN_FLIGHT + 1))(*([p] * (vqm.VQM_MAX_IN_FLIGHT + 1)))
+    assert L.vqm_graph_create(0, None, F, big, big, vqm.VQM_MAX_IN_FLIGHT + 1, 400, 400, 8, 8,
+                              out) == -errno.EINVAL
+    assert L.vqm_graph_create(0, None, F, arr, arr, 2, 400, 400, 8, 0, out) == -errno.EINVAL
+    assert L.vqm_graph_create(0, None, F, arr, arr, 2, 400, 400, 8, vqm.VQM_MAX_BATCH + 1, out) == -errno.EINVAL
+    assert L.vqm_graph_create(0, None, F, arr, arr, 2, 400, 400, 7, 8, out) == -errno.EINVAL
+    assert L.vqm_graph_create(0, None, F, arr, arr, 2, 10, 400, 8, 8, out) == -errno.ENOTSUP  # the gate
+    assert L.vqm_graph_create(0, None, M, arr, arr, 2, 175, 400, 8, 8, out) == -errno.ENOTSUP
+    assert g.value is None  # *out is cleared on error
+    assert L.vqm_graph_create(0, None, F, arr, arr, 2, 400, 400, 8, 8, None) == -errno.EINVAL
+    assert L.vqm_graph_launch(None) == -errno.EINVAL
+    s = ctypes.c_double()
+    assert L.vqm_graph_collect(None, ctypes.byref(s), None, None) == -errno.EINVAL
+    L.vqm_graph_destroy(None)  # a no-op
 
 
 def test_binding_checks_sample_size_and_shape():

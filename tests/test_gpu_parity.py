@@ -585,3 +585,107 @@ def test_blocking_calls_from_many_threads(torch_cuda):
     assert not errors, errors
     for k in range(6):
         assert results[k] == (want + [want_ms]) * 3, k
+
+
+# ------------------------------------------------------------ recorded passes (graph replay)
+
+def _eager(torch, metric, fs, batch):
+    st = torch.cuda.Stream()
+    c = vqm.Context(0, st)
+    try:
+        return vqm.vqm_score_frames([c], metric, fs, batch, 0, want_lcs=metric == vqm.VQM_METRIC_MS_SSIM)
+    finally:
+        c.close()
+
+
+def test_graph_replays_match_the_eager_pass(torch_cuda):
+    # One recorded float_ssim pass over 40 device frames (a batch of 32 and a
+    # ragged one of 8), replayed three times with other GPU work and host
+    # waits in between; every replay equals the eager pipelined pass bit for
+    # bit.  Then the frames are overwritten in place and the next replay
+    # scores the new contents.
+    torch = torch_cuda
+    src = synth.FrameSource(2)
+    n = 40
+    pairs = [src.pair(t) for t in range(n)]
+    dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
+    fs = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], src.bpc)
+    want = _eager(torch, vqm.VQM_METRIC_FLOAT_SSIM, fs, 32)
+    for t in (0, n - 1):
+        assert abs(want[t] - oracle.ssim(*pairs[t], src.bpc)) <= TOL
+    say("graph float_ssim: record")
+    with vqm.Graph(0, torch.cuda.Stream(), vqm.VQM_METRIC_FLOAT_SSIM, fs, 32) as g:
+        other = synth.FrameSource(4).pair(7)
+        for k in range(3):
+            say(f"graph float_ssim: replay {k}")
+            g.vqm_graph_launch()
+            with pytest.raises(vqm.VqmError) as e:
+                g.vqm_graph_launch()
+            assert e.value.rc == -errno.EBUSY
+            got, db = g.vqm_graph_collect(want_db=True)
+            assert np.array_equal(got, want), k
+            assert np.all(np.isfinite(db))
+            with pytest.raises(vqm.VqmError) as e:
+                g.vqm_graph_collect()
+            assert e.value.rc == -errno.EAGAIN
+            vqm.vqm_ssim_frame(*other, 10)                      # eager work in between
+            torch.cuda.synchronize()
+        # new contents in the same buffers: frames shifted by 40
+        new = [src.pair(t) for t in range(n, 2 * n)]
+        for (dr, dd), (r, d) in zip(dev, new):
+            dr.copy_(to_dev(torch, r))
+            dd.copy_(to_dev(torch, d))
+        torch.cuda.synchronize()
+        want_new = _eager(torch, vqm.VQM_METRIC_FLOAT_SSIM, fs, 32)
+        assert not np.array_equal(want_new, want)
+        g.vqm_graph_launch()
+        assert np.array_equal(g.vqm_graph_collect(), want_new)
+
+
+def test_graph_msssim_with_level_means(torch_cuda):
+    torch = torch_cuda
+    src = synth.FrameSource(5, w=960, h=544)
+    n = 10
+    pairs = [src.pair(t) for t in range(n)]
+    dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
+    fs = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], src.bpc)
+    want, want_lcs = _eager(torch, vqm.VQM_METRIC_MS_SSIM, fs, 4)
+    assert abs(want[3] - oracle.msssim(*pairs[3], src.bpc)) <= TOL
+    say("graph MS-SSIM: record and replay twice")
+    with vqm.Graph(0, None, vqm.VQM_METRIC_MS_SSIM, fs, 4) as g:
+        for _ in range(2):
+            g.vqm_graph_launch()
+            got, lcs, db = g.vqm_graph_collect(want_lcs=True, want_db=True)
+            assert np.array_equal(got, want)
+            assert np.array_equal(lcs, want_lcs)
+            assert np.all(np.isnan(db))
+
+
+def test_graph_full_2160p_workload_in_bench_shape(torch_cuda):
+    # The 50 frames of the 2160p workload, batches of 32, as bench.py --graph
+    # replays them; every frame equals the eager pass, a sample the oracle.
+    torch = torch_cuda
+    src = synth.FrameSource(4)
+    n = src.workload.frames
+    say(f"graph 2160p: generating {n} pairs")
+    pairs = [src.pair(t) for t in range(n)]
+    dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
+    fs = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], src.bpc)
+    want = _eager(torch, vqm.VQM_METRIC_FLOAT_SSIM, fs, vqm.VQM_MAX_BATCH)
+    with vqm.Graph(0, None, vqm.VQM_METRIC_FLOAT_SSIM, fs, vqm.VQM_MAX_BATCH) as g:
+        for k in range(2):
+            say(f"graph 2160p: replay {k}")
+            g.vqm_graph_launch()
+            assert np.array_equal(g.vqm_graph_collect(), want)
+    for t in (0, n - 1):
+        assert abs(want[t] - oracle.ssim(*pairs[t], src.bpc)) <= TOL
+
+
+def test_graph_takes_device_frames_only(torch_cuda):
+    src = synth.FrameSource(2)
+    r, d = src.pair(0)
+    fs = vqm.FrameSet([r], [d], src.bpc)   # host arrays
+    with pytest.raises(vqm.VqmError) as e:
+        vqm.Graph(0, None, vqm.VQM_METRIC_FLOAT_SSIM, fs, 8)
+    assert e.value.rc == -errno.EINVAL
+    assert "device memory" in vqm.vqm_last_error()
