@@ -155,19 +155,22 @@ __device__ __forceinline__ void finish_frame(const SsimFrame &fr, const StepGeom
 // (short-lived, so the dispatcher balances them), then its share of the
 // finish workgroups.
 //
-// Two shapes of the map role.  When the decimation streams far more bytes
-// than the map has tiles (2160p: ~245 KB of raw input per map tile), ~32 map
+// Three shapes of the map role.  When the decimation streams far more bytes
+// than the map has tiles (2160p: ~270 KB of raw input per map tile), ~32 map
 // workgroups per XCD loop over the tiles: the map holds about one slot per
 // CU for the whole launch and hides under the decimation, which keeps the
-// other slots.  When the map dominates (1080p and below: ~30 KB per tile),
-// every tile gets its own workgroup, ahead of the decimation, so the map
-// runs at full width.  Measured at 8 frames per launch: 2160p 47.8 us
-// looping against 49.7 us one tile each; 1080p 21.1 us against 15.6 us.
+// other slots.  Otherwise every tile gets its own workgroup, so the map runs
+// at full width: interleaved with the decimation workgroups when the
+// decimation still reads enough per tile to take about as long (1080p: ~31 KB
+// per tile), ahead of them when the map dominates (853x481: ~15 KB).
+// Measured at 8 frames per launch: 2160p 47.8 us looping against 49.7 us
+// one tile each; 1080p 21.1 us looping against 15.6 us one tile each.
 struct StepLayout {
     int map_per_xcd;   // map tiles per XCD (contiguous ranges of the tile order)
     int map_wg;        // map workgroups per XCD
     int dec_per_xcd;   // decimation workgroups per XCD
     int fin_per_xcd;   // finish workgroups per XCD
+    int interleave;    // 1: one tile per map workgroup, interleaved with the decimation workgroups
 };
 
 // Map workgroups per XCD when they loop: about one per CU.
@@ -175,12 +178,50 @@ constexpr int kMapWorkgroupsPerXcd = 32;
 // Raw input bytes the decimation reads per map tile above which the map
 // workgroups loop.
 constexpr long long kLoopBytesPerTile = 100 * 1024;
+// Below that, and above this, one-tile map workgroups are interleaved with
+// the decimation workgroups instead of dispatched ahead of them: the
+// decimation's HBM time is then about the map's ALU time or more, and both
+// run side by side.  Measured per launch of 32 frames: 1080p (31 KB per
+// tile) 45.1 us ahead, 42.9 us interleaved; 853x481 (15 KB per tile, the
+// map dominates and its long tiles are best started first) 39.8 us ahead,
+// 43.0 us interleaved.
+constexpr long long kInterleaveBytesPerTile = 20 * 1024;
 
 template <class Dec, typename TIn, bool kLoopMap>
 __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, StepLayout lay, int map_pitch,
                                                  float unit, int vec4, Taps taps) {
     const int x = (int)(blockIdx.x & 7u);
     int q = (int)(blockIdx.x >> 3);
+    if (!kLoopMap && lay.interleave) {
+        // Position q of this XCD's map_wg + dec_per_xcd first workgroups is a
+        // map workgroup when floor((q+1) M / (M+D)) > floor(q M / (M+D)): the
+        // map's M tiles spread evenly among the D decimation workgroups, so
+        // that ALU-bound map tiles and HBM-bound decimation share the CUs.
+        const int M = lay.map_wg, MD = lay.map_wg + lay.dec_per_xcd;
+        if (q < MD) {
+            const int mq = (int)((long long)q * M / MD), mq1 = (int)((long long)(q + 1) * M / MD);
+            if (mq1 > mq) {
+                const int map_pf = tiles_x(g) * tiles_y(g);
+                const int m = x * lay.map_per_xcd + mq;
+                if (mq < lay.map_per_xcd && m < r.n_map * map_pf) {
+                    const int f = m / map_pf;
+                    map_tile<TIn, kLoopMap>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                }
+                return;
+            }
+            const int dec_pf = r.dec_blocks_per_frame;
+            const int d = x * lay.dec_per_xcd + (q - mq);
+            if (d < r.n_dec * dec_pf) {
+                const int f = d / dec_pf;
+                Dec::run(r.dec.f[f], d - f * dec_pf, g);
+            }
+            return;
+        }
+        q -= MD;
+        const int fi = x * lay.fin_per_xcd + q;
+        if (fi < r.n_fin) finish_frame(r.fin.f[fi], g);
+        return;
+    }
     if (q < lay.map_wg) {
         const int map_pf = tiles_x(g) * tiles_y(g);
         const int m0 = x * lay.map_per_xcd;
@@ -231,6 +272,7 @@ hipError_t launch_step(StepRoles r, const StepGeometry &g, int map_pitch, float 
     lay.map_wg = loop ? min(kMapWorkgroupsPerXcd, lay.map_per_xcd) : lay.map_per_xcd;
     lay.dec_per_xcd = (int)((dec_blocks + 7) / 8);
     lay.fin_per_xcd = (r.n_fin + 7) / 8;
+    lay.interleave = !loop && map_tiles > 0 && dec_blocks > 0 && raw_bytes >= kInterleaveBytesPerTile * map_tiles;
     const long long blocks = 8LL * (lay.map_wg + lay.dec_per_xcd + lay.fin_per_xcd);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
