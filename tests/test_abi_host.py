@@ -55,6 +55,14 @@ def test_abi_version():
     assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 3
 
 
+def test_graft_entry_check_matches_the_built_library():
+    # build() ends with this check: the loaded library's ABI version against
+    # the header's (a stale literal there once failed every build).
+    import __graft_entry__
+    assert __graft_entry__.header_abi_version() == header_constants()["VQM_ABI_VERSION"]
+    __graft_entry__.check_loaded()
+
+
 def test_binding_constants_match_the_header():
     consts = header_constants()
     for name in ("VQM_MAX_IN_FLIGHT", "VQM_MAX_BATCH", "VQM_MSSSIM_LCS"):
