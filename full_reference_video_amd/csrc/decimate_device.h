@@ -9,11 +9,14 @@
 // 2^-52 units: every product is a multiple of 2^-45 and the window sum stays
 // below 2^8, so it fits an int64 for s <= 128 with no fp64 anywhere.
 //
-// Two code paths compute that same integer:
+// Three code paths compute that same integer:
 //
 //  * general_block — any s <= 128: each product is formed in fp32 and its
 //    exact value is turned into 2^-52 units from its exponent and
 //    significand, then added as a uint64.
+//
+//  * pow2_scalar_block — s = 2^k on planes whose rows are not 16-byte
+//    aligned: the plain integer sum of the raw samples, read one by one.
 //
 //  * pow2_wave — s = 2^k, where tap = 2^-2k and every product is exact,
 //    so the units of a product are raw * 2^(52 - 2k - (bpc-8)): a constant
@@ -101,6 +104,46 @@ __device__ __forceinline__ void general_block(const DecimateFrame &fr, int bx, i
     // exact scaling by 2^-52.
     static_cast<float *>(fr.out_ref)[o] = (float)ar * 0x1p-52f;
     static_cast<float *>(fr.out_dis)[o] = (float)ad * 0x1p-52f;
+}
+
+// One 256-thread block of the power-of-two path for planes whose rows are not
+// 16-byte aligned (odd widths): outputs (64 bx + lane, 4 by + wave), each
+// the integer sum of its S x S raw samples, read one by one (every product
+// v * tap is exact at s = 2^k, so the window sum is sum(raw) * post).  The
+// mirrored row and column of each window position are found once.
+template <typename T, int S>
+__device__ __forceinline__ void pow2_scalar_block(const DecimateFrame &fr, int bx, int by, int w, int h,
+                                                  int dec_w, int dec_h, int opitch, float post, bool packed) {
+    const T *__restrict__ ref = static_cast<const T *>(fr.ref);
+    const T *__restrict__ dis = static_cast<const T *>(fr.dis);
+    const int X = bx * 64 + (threadIdx.x & 63);
+    const int Y = by * 4 + (threadIdx.x >> 6);
+    if (X >= dec_w || Y >= dec_h) return;
+    int col[S];
+    size_t row[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        col[i] = mirror(X * S - S / 2 + i, w);
+        row[i] = (size_t)mirror(Y * S - S / 2 + i, h) * (size_t)w;
+    }
+    uint32_t ar = 0, ad = 0;
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            ar += ref[row[j] + col[i]];
+            ad += dis[row[j] + col[i]];
+        }
+    const size_t o = (size_t)Y * opitch + X;
+    if (packed) {
+        static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)ar;
+        static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)ad;
+    } else {
+        // One rounding of the exact sum (uint32 -> fp32 is RNE), then the
+        // exact power of two.
+        static_cast<float *>(fr.out_ref)[o] = (float)ar * post;
+        static_cast<float *>(fr.out_dis)[o] = (float)ad * post;
+    }
 }
 
 // ------------------------------------------------------------ power-of-two path

@@ -84,6 +84,17 @@ struct DecGeneral {
     }
 };
 
+// s = 2^k on planes the vector path cannot take (rows not 16-byte aligned).
+template <typename T, int S>
+struct DecPow2Scalar {
+    __host__ __device__ static int blocks_x(const StepGeometry &g) { return (g.dec_w + 63) / 64; }
+    static int blocks_per_frame(const StepGeometry &g) { return blocks_x(g) * ((g.dec_h + 3) / 4); }
+    __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
+        const int bx = b % blocks_x(g), by = b / blocks_x(g);
+        dec::pow2_scalar_block<T, S>(fr, bx, by, g.w, g.h, g.dec_w, g.dec_h, g.dec_pitch, g.post, g.packed != 0);
+    }
+};
+
 // ------------------------------------------------------------ map and finish roles
 
 __host__ __device__ inline int tiles_x(const StepGeometry &g) { return (g.dec_w - 10 + kTW - 1) / kTW; }
@@ -305,6 +316,19 @@ hipError_t launch_dec_pow2(int s, const StepRoles &r, const StepGeometry &g, int
     }
 }
 
+// s = 2^k on rows that are not 16-byte aligned: the scalar integer path.
+template <typename T, typename TIn>
+hipError_t launch_dec_pow2_scalar(int s, const StepRoles &r, const StepGeometry &g, int map_pitch, float unit,
+                                  const Taps &taps, hipStream_t stream, const KernelTimer &timer) {
+    switch (s) {
+    case 2: return launch_step<DecPow2Scalar<T, 2>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    case 4: return launch_step<DecPow2Scalar<T, 4>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    case 8: return launch_step<DecPow2Scalar<T, 8>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    case 16: return launch_step<DecPow2Scalar<T, 16>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    default: return launch_step<DecGeneral<T>, TIn>(r, g, map_pitch, unit, taps, stream, timer);
+    }
+}
+
 // The packed scales: s = 2^k with bpc + 2k <= 16, so s <= 16 for 8-bit and
 // s <= 8 for deeper samples; the map reads the uint16 window sums.
 template <typename T>
@@ -353,19 +377,20 @@ hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind ma
         if (map_kind != (g.packed ? IN_U16 : IN_F32) && r.n_map > 0) return hipErrorInvalidValue;
         const bool fast = decimate_fast_path(r.dec, r.n_dec, g.w, g.h, g.bpc, g.s);
         if (g.packed) {
+            // packed implies s = 2^k: the vector path, else the scalar one
             if (g.bpc == 8) {
                 if (fast) return launch_dec_pow2_packed<uint8_t>(g.s, r, g, map_pitch, unit, taps, stream, timer);
-                return launch_step<DecGeneral<uint8_t>, uint16_t>(r, g, map_pitch, unit, taps, stream, timer);
+                return launch_dec_pow2_scalar<uint8_t, uint16_t>(g.s, r, g, map_pitch, unit, taps, stream, timer);
             }
             if (fast) return launch_dec_pow2_packed<uint16_t>(g.s, r, g, map_pitch, unit, taps, stream, timer);
-            return launch_step<DecGeneral<uint16_t>, uint16_t>(r, g, map_pitch, unit, taps, stream, timer);
+            return launch_dec_pow2_scalar<uint16_t, uint16_t>(g.s, r, g, map_pitch, unit, taps, stream, timer);
         }
         if (g.bpc == 8) {
             if (fast) return launch_dec_pow2<uint8_t, float>(g.s, r, g, map_pitch, unit, taps, stream, timer);
-            return launch_step<DecGeneral<uint8_t>, float>(r, g, map_pitch, unit, taps, stream, timer);
+            return launch_dec_pow2_scalar<uint8_t, float>(g.s, r, g, map_pitch, unit, taps, stream, timer);
         }
         if (fast) return launch_dec_pow2<uint16_t, float>(g.s, r, g, map_pitch, unit, taps, stream, timer);
-        return launch_step<DecGeneral<uint16_t>, float>(r, g, map_pitch, unit, taps, stream, timer);
+        return launch_dec_pow2_scalar<uint16_t, float>(g.s, r, g, map_pitch, unit, taps, stream, timer);
     }
     switch (map_kind) {
     case IN_F32: return launch_step<DecNone, float>(r, g, map_pitch, unit, taps, stream, timer);
