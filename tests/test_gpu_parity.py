@@ -147,6 +147,24 @@ def test_ssim_ragged_sizes_and_depths(ctx, w, h, bpc):
     assert abs(got - want) <= TOL, (w, h, bpc, got, want)
 
 
+def test_8k_frames(ctx):
+    # The largest common frame, 7680x4320 10-bit: scale round(4320/256) = 17,
+    # a scale that is not a power of two (the general decimation), and a
+    # six-level-deep MS-SSIM pyramid of 33 M samples.
+    src = synth.FrameSource(4, w=7680, h=4320, bpc=10)
+    ref, dis = src.pair(2)
+    s = oracle.scale(7680, 4320)
+    assert s == 17
+    say("8k decimation")
+    gr, gd = ctx.vqm_debug_decimate(ref, dis, 10)
+    assert np.array_equal(bits(gr), bits(oracle.decimate(ref, 10, s)))
+    assert np.array_equal(bits(gd), bits(oracle.decimate(dis, 10, s)))
+    say("8k float_ssim")
+    assert abs(vqm.vqm_ssim_frame(ref, dis, 10) - oracle.ssim(ref, dis, 10)) <= TOL
+    say("8k MS-SSIM")
+    assert abs(vqm.vqm_msssim_frame(ref, dis, 10) - oracle.msssim(ref, dis, 10)) <= TOL
+
+
 def test_ssim_minimum_plane(ctx):
     # the smallest accepted decimated plane: one map pixel
     for (w, h) in [(11, 11), (11, 40), (40, 11)]:
