@@ -15,6 +15,7 @@ the five synthetic workloads; the default is the 2160p 10-bit float_ssim one.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -210,6 +211,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a recorded pass (vqm_graph_*) over the workload's device frames, one "
                          "replay and one wait per step, reported under its own metric name")
+    ap.add_argument("--frame", default="", metavar="WxHxBPC",
+                    help="score frames of this size and depth instead (the 2160p workload's recipe, 16 frames; for "
+                         "sizes outside the workloads, e.g. 1280x720x8, 2560x1440x10 or 7680x4320x10)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB 20 times (a kernel of known "
                          "traffic, to calibrate the FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -237,6 +241,11 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     src = synth.FrameSource(args.workload)
+    if args.frame:
+        fw, fh, fb = (int(v) for v in args.frame.lower().split("x"))
+        base = synth.WORKLOADS[4] if wl.metric == "float_ssim" else wl
+        wl = dataclasses.replace(base, name=f"{base.metric}_{fw}x{fh}_{fb}bit", w=fw, h=fh, bpc=fb, frames=16)
+        src = synth.FrameSource(base.index, w=fw, h=fh, bpc=fb)
     log(f"generating {wl.frames} frame pairs of {wl.name}")
     host = [src.pair(t) for t in range(wl.frames)]
 
@@ -400,7 +409,7 @@ def main():
 
     out = {
         "metric": ("frames/sec and achieved HBM GB/s (% of peak), float_ssim at 3840x2160"
-                   if wl.index == 4 else f"frames/sec, {wl.name}")
+                   if wl.index == 4 and not args.frame else f"frames/sec, {wl.name}")
                   + ("" if args.host_input == "none" else f", end to end from {args.host_input} host frames")
                   + (", recorded-pass replays" if args.graph else ""),
         "value": round(fps, 1),

@@ -5,22 +5,22 @@
 // CPU", Context and Decision 1: output (X, Y) of a plane is the window at
 // (X*s + i, Y*s + j), i, j in [-s/2, s-1-s/2], half-sample symmetric edges,
 // of the fp32 products v * tap (tap = 1.0f/(s*s) formed on the host), summed
-// exactly and rounded once to fp32.  The exact sum is an integer number of
-// 2^-52 units: every product is a multiple of 2^-45 and the window sum stays
-// below 2^8, so it fits an int64 for s <= 128 with no fp64 anywhere.
+// exactly and rounded once to fp32.  The pages keep the exact sum as an int64
+// count of 2^-52 units (every product is a multiple of 2^-45 and the sum stays
+// below 2^8, so it fits for s <= 128).  Here it is kept wherever it is
+// cheapest, always exactly:
 //
-// Three code paths compute that same integer:
+// Three code paths compute that same exact sum:
 //
-//  * general_block — any s <= 128: each product is formed in fp32 and its
-//    exact value is turned into 2^-52 units from its exponent and
-//    significand, then added as a uint64.
+//  * general_block — any s <= 128: each product is formed in fp32 and the
+//    products are summed exactly in fp64 (the bound is at the function).
 //
 //  * pow2_scalar_block — s = 2^k on planes whose rows are not 16-byte
 //    aligned: the plain integer sum of the raw samples, read one by one.
 //
 //  * pow2_wave — s = 2^k, where tap = 2^-2k and every product is exact,
-//    so the units of a product are raw * 2^(52 - 2k - (bpc-8)): a constant
-//    shift of the raw integer.  The shift is hoisted out of the window sum,
+//    so a product is raw * 2^-(2k + bpc - 8): a constant scaling of the raw
+//    integer.  The scaling is hoisted out of the window sum,
 //    which becomes a plain integer sum of raw samples (v_sad_u8 / v_sad_u16
 //    add four or two samples per instruction), rounded once to fp32 and
 //    scaled by the exact power of two.  This is the HBM-bound path of the
@@ -58,18 +58,6 @@ __device__ __forceinline__ int mirror(int i, int n) {
 
 // ------------------------------------------------------------ general path
 
-// Exact value of the fp32 product raw * tap, scaled by 2^-(bpc-8), as an
-// integer count of 2^-52 units.  q = raw * tap is normal and >= 2^-14 for
-// s <= 128, so its exponent field e >= 113 and the shift e - 90 - bpc >= 7.
-__device__ __forceinline__ uint64_t product_units(uint32_t raw, float tap, int shift_base) {
-    const float q = (float)raw * tap;  // one fp32 rounding; contraction is off
-    const uint32_t bits = __float_as_uint(q);
-    if (bits == 0u) return 0ull;
-    const uint64_t m = (uint64_t)((bits & 0x7fffffu) | 0x800000u);
-    const int e = (int)(bits >> 23);
-    return m << (e + shift_base);
-}
-
 // One 256-thread block of the general kernel: outputs (64 bx + lane,
 // 4 by + wave).
 template <typename T>
@@ -80,30 +68,64 @@ __device__ __forceinline__ void general_block(const DecimateFrame &fr, int bx, i
     const int X = bx * 64 + (threadIdx.x & 63);
     const int Y = by * 4 + (threadIdx.x >> 6);
     if (X >= dec_w || Y >= dec_h) return;
-    const int lo = -(s / 2);
-    const int shift_base = -90 - bpc;
-    uint64_t ar = 0, ad = 0;
-    for (int j = 0; j < s; ++j) {
-        const size_t row = (size_t)mirror(Y * s + lo + j, h) * (size_t)w;
-        for (int i = 0; i < s; ++i) {
-            const int xx = mirror(X * s + lo + i, w);
-            ar += product_units(ref[row + xx], tap, shift_base);
-            ad += product_units(dis[row + xx], tap, shift_base);
+    const int x0 = X * s - s / 2, y0 = Y * s - s / 2;
+    // The exact sum of the fp32 products raw * tap, accumulated in fp64: every
+    // product is a multiple of ulp(tap) = 2^(e - 23) (tap in [2^e, 2^(e+1)),
+    // e = -ceil(2 log2 s)) and the window's sum stays below 2^bpc, so every
+    // partial sum is an integer multiple of ulp(tap) below
+    // 2^(bpc + 23 + ceil(2 log2 s)) <= 2^53 for bpc <= 16 and s <= 128: fp64
+    // holds it exactly, as the int64 count of 2^-52 units does.
+    // Every partial sum of any subset of the products is exact too, so the
+    // order of the additions is free: four independent sums per plane keep
+    // four loads in flight.
+    double ar = 0.0, ad = 0.0;
+    if (x0 >= 0 && x0 + s <= w && y0 >= 0 && y0 + s <= h) {
+        const T *pr = ref + (size_t)y0 * (size_t)w + x0;
+        const T *pd = dis + (size_t)y0 * (size_t)w + x0;
+        double a4[4] = {0.0, 0.0, 0.0, 0.0}, d4[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int j = 0; j < s; ++j, pr += w, pd += w) {
+            int i = 0;
+            for (; i + 4 <= s; i += 4) {
+                T rv[4], dv[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    rv[k] = pr[i + k];
+                    dv[k] = pd[i + k];
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    a4[k] += (double)((float)rv[k] * tap);
+                    d4[k] += (double)((float)dv[k] * tap);
+                }
+            }
+            for (; i < s; ++i) {
+                a4[0] += (double)((float)pr[i] * tap);
+                d4[0] += (double)((float)pd[i] * tap);
+            }
+        }
+        ar = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+        ad = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+    } else {
+        for (int j = 0; j < s; ++j) {
+            const size_t row = (size_t)mirror(y0 + j, h) * (size_t)w;
+            for (int i = 0; i < s; ++i) {
+                const int xx = mirror(x0 + i, w);
+                ar += (double)((float)ref[row + xx] * tap);
+                ad += (double)((float)dis[row + xx] * tap);
+            }
         }
     }
     const size_t o = (size_t)Y * opitch + X;
     if (packed) {
-        // s = 2^k: every product is raw * 2^(60 - 2k - bpc) units, so the
-        // shift gives the window's raw integer sum back exactly.
-        const int shift = 60 - 2 * (__ffs(s) - 1) - bpc;
-        static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)(ar >> shift);
-        static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)(ad >> shift);
+        // s = 2^k: tap = 2^-2k and the sum times s^2 is the raw integer sum.
+        const double ss = (double)s * (double)s;
+        static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)(ar * ss);
+        static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)(ad * ss);
         return;
     }
-    // One rounding to fp32 (the sum has at most 53 significant bits), then an
-    // exact scaling by 2^-52.
-    static_cast<float *>(fr.out_ref)[o] = (float)ar * 0x1p-52f;
-    static_cast<float *>(fr.out_dis)[o] = (float)ad * 0x1p-52f;
+    // One rounding to fp32, then the exact scaling of the samples to 8 bits.
+    static_cast<float *>(fr.out_ref)[o] = ldexpf((float)ar, 8 - bpc);
+    static_cast<float *>(fr.out_dis)[o] = ldexpf((float)ad, 8 - bpc);
 }
 
 // One 256-thread block of the power-of-two path for planes whose rows are not

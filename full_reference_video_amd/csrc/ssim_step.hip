@@ -47,12 +47,14 @@ constexpr int kDecWaves = kNT / 64;            // waves per decimation workgroup
 // ------------------------------------------------------------ decimation policies
 
 struct DecNone {
+    static constexpr bool kStreams = false;  // whether the decimation is the wide HBM stream (see map_tile)
     static int blocks_per_frame(const StepGeometry &) { return 0; }
     __device__ static void run(const DecimateFrame &, int, const StepGeometry &) {}
 };
 
 template <typename T, int S>
 struct DecPow2 {
+    static constexpr bool kStreams = true;
     using Sh = dec::Pow2Shape<T, S>;
     __host__ __device__ static int waves_per_row(const StepGeometry &g) {
         const int groups = (g.dec_w + Sh::CPT - 1) / Sh::CPT;  // groups holding outputs
@@ -75,6 +77,7 @@ struct DecPow2 {
 
 template <typename T>
 struct DecGeneral {
+    static constexpr bool kStreams = false;
     __host__ __device__ static int blocks_x(const StepGeometry &g) { return (g.dec_w + 63) / 64; }
     static int blocks_per_frame(const StepGeometry &g) { return blocks_x(g) * ((g.dec_h + 3) / 4); }
     __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
@@ -87,6 +90,7 @@ struct DecGeneral {
 // s = 2^k on planes the vector path cannot take (rows not 16-byte aligned).
 template <typename T, int S>
 struct DecPow2Scalar {
+    static constexpr bool kStreams = false;
     __host__ __device__ static int blocks_x(const StepGeometry &g) { return (g.dec_w + 63) / 64; }
     static int blocks_per_frame(const StepGeometry &g) { return blocks_x(g) * ((g.dec_h + 3) / 4); }
     __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
@@ -100,9 +104,11 @@ struct DecPow2Scalar {
 __host__ __device__ inline int tiles_x(const StepGeometry &g) { return (g.dec_w - 10 + kTW - 1) / kTW; }
 __host__ __device__ inline int tiles_y(const StepGeometry &g) { return (g.dec_h - 10 + kTH - 1) / kTH; }
 
-// In the looping layout (below) the tile buffer is oversized on purpose: LDS
-// (160 KiB per CU) is what limits how many step workgroups share a CU, and at
-// 2160p the decimation streams fastest with at most three of them per CU.
+// In the looping layout (below) with the vector decimation the tile buffer is
+// oversized on purpose: LDS (160 KiB per CU) is what limits how many step
+// workgroups share a CU, and at 2160p that decimation streams fastest with at
+// most three of them per CU.  The scalar and general decimations are bound by
+// load latency instead and keep every slot.
 // Measured per launch of 32 frames: 198.3 us with two, 189.1 us with three,
 // 190.9 us with four, 192.1 us with no cap (VGPRs then allow four).
 constexpr int kLoopWorkgroupsPerCu = 3;
@@ -111,11 +117,11 @@ static_assert(kLoopLdsFloats >= tile_lds_floats<kTW, kTH, kNP>(), "the capped ti
 static_assert(kLoopWorkgroupsPerCu * (kLoopLdsFloats * 4 + 1024) <= 160 * 1024,
               "the capped buffer must still let kLoopWorkgroupsPerCu workgroups share a CU");
 
-template <typename TIn, bool kLoopMap>
+template <typename TIn, bool kCapped>
 __device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const StepGeometry &g, int pitch,
                                          float unit, bool vec4, const Taps &taps) {
     constexpr int IH = kTH + 10, IP = in_pitch<kTW>();
-    __shared__ __attribute__((aligned(16))) float lds[kLoopMap ? kLoopLdsFloats : tile_lds_floats<kTW, kTH, kNP>()];
+    __shared__ __attribute__((aligned(16))) float lds[kCapped ? kLoopLdsFloats : tile_lds_floats<kTW, kTH, kNP>()];
     __shared__ double red[1][kNT / 64];
     float *sx = lds, *sy = lds + IH * IP;
 
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
                 const int m = x * lay.map_per_xcd + mq;
                 if (mq < lay.map_per_xcd && m < r.n_map * map_pf) {
                     const int f = m / map_pf;
-                    map_tile<TIn, kLoopMap>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                    map_tile<TIn, kLoopMap && Dec::kStreams>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
                 }
                 return;
             }
@@ -241,14 +247,14 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
 #pragma unroll 1
             for (int m = m0 + q; m < m1; m += lay.map_wg) {
                 const int f = m / map_pf;
-                map_tile<TIn, kLoopMap>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                map_tile<TIn, kLoopMap && Dec::kStreams>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
                 __syncthreads();  // the next tile reuses the LDS
             }
         } else {
             const int m = m0 + q;
             if (m < m1) {
                 const int f = m / map_pf;
-                map_tile<TIn, kLoopMap>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                map_tile<TIn, kLoopMap && Dec::kStreams>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
             }
         }
         return;
