@@ -199,9 +199,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="workload number 1..5")
     ap.add_argument("--streams", type=int, default=1, help="contexts/streams batches rotate over")
-    ap.add_argument("--batch", type=int, default=32,
-                    help="frames per submit (and per kernel launch), up to VQM_MAX_BATCH = 64: 32 is fastest at 2160p, "
-                         "64 at 1080p and below")
+    ap.add_argument("--batch", type=int, default=32, help="frames per submit (and per kernel launch)")
     ap.add_argument("--lag", type=int, default=0,
                     help="frames submitted after a frame before it is collected (0: 3*batch)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0: skip)")

@@ -104,20 +104,6 @@ struct DecPow2Scalar {
 __host__ __device__ inline int tiles_x(const StepGeometry &g) { return (g.dec_w - 10 + kTW - 1) / kTW; }
 __host__ __device__ inline int tiles_y(const StepGeometry &g) { return (g.dec_h - 10 + kTH - 1) / kTH; }
 
-// Frame f of each role, from the launch's arrays and the context's slot table.
-__device__ __forceinline__ DecimateFrame dec_frame(const StepRoles &r, int f) {
-    const SlotDesc &d = r.slots[r.dec_slot[f]];
-    return DecimateFrame{r.dec_in[0][f], r.dec_in[1][f], d.dec_ref, d.dec_dis};
-}
-__device__ __forceinline__ SsimFrame map_frame(const StepRoles &r, int f) {
-    const SlotDesc &d = r.slots[r.map_slot[f]];
-    return SsimFrame{r.map_in[0][f], r.map_in[1][f], d.partials, d.result};
-}
-__device__ __forceinline__ SsimFrame fin_frame(const StepRoles &r, int f) {
-    const SlotDesc &d = r.slots[r.fin_slot[f]];
-    return SsimFrame{nullptr, nullptr, d.partials, d.result};
-}
-
 // In the looping layout (below) with the vector decimation the tile buffer is
 // oversized on purpose: LDS (160 KiB per CU) is what limits how many step
 // workgroups share a CU, and at 2160p that decimation streams fastest with at
@@ -236,7 +222,7 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
                 const int m = x * lay.map_per_xcd + mq;
                 if (mq < lay.map_per_xcd && m < r.n_map * map_pf) {
                     const int f = m / map_pf;
-                    map_tile<TIn, kLoopMap && Dec::kStreams>(map_frame(r, f), m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                    map_tile<TIn, kLoopMap && Dec::kStreams>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
                 }
                 return;
             }
@@ -244,13 +230,13 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
             const int d = x * lay.dec_per_xcd + (q - mq);
             if (d < r.n_dec * dec_pf) {
                 const int f = d / dec_pf;
-                Dec::run(dec_frame(r, f), d - f * dec_pf, g);
+                Dec::run(r.dec.f[f], d - f * dec_pf, g);
             }
             return;
         }
         q -= MD;
         const int fi = x * lay.fin_per_xcd + q;
-        if (fi < r.n_fin) finish_frame(fin_frame(r, fi), g);
+        if (fi < r.n_fin) finish_frame(r.fin.f[fi], g);
         return;
     }
     if (q < lay.map_wg) {
@@ -261,14 +247,14 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
 #pragma unroll 1
             for (int m = m0 + q; m < m1; m += lay.map_wg) {
                 const int f = m / map_pf;
-                map_tile<TIn, kLoopMap && Dec::kStreams>(map_frame(r, f), m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                map_tile<TIn, kLoopMap && Dec::kStreams>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
                 __syncthreads();  // the next tile reuses the LDS
             }
         } else {
             const int m = m0 + q;
             if (m < m1) {
                 const int f = m / map_pf;
-                map_tile<TIn, kLoopMap && Dec::kStreams>(map_frame(r, f), m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                map_tile<TIn, kLoopMap && Dec::kStreams>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
             }
         }
         return;
@@ -279,13 +265,13 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
         const int d = x * lay.dec_per_xcd + q;
         if (d < r.n_dec * dec_pf) {
             const int f = d / dec_pf;
-            Dec::run(dec_frame(r, f), d - f * dec_pf, g);
+            Dec::run(r.dec.f[f], d - f * dec_pf, g);
         }
         return;
     }
     q -= lay.dec_per_xcd;
     const int fi = x * lay.fin_per_xcd + q;
-    if (fi < r.n_fin) finish_frame(fin_frame(r, fi), g);
+    if (fi < r.n_fin) finish_frame(r.fin.f[fi], g);
 }
 
 template <class Dec, typename TIn>
@@ -309,8 +295,8 @@ hipError_t launch_step(StepRoles r, const StepGeometry &g, int map_pitch, float 
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     int vec4 = 1;
     for (int i = 0; i < r.n_map; ++i)
-        if (!stage_vec4_ok(r.map_in[0][i], map_pitch, sizeof(TIn)) ||
-            !stage_vec4_ok(r.map_in[1][i], map_pitch, sizeof(TIn)))
+        if (!stage_vec4_ok(r.map.f[i].ref, map_pitch, sizeof(TIn)) ||
+            !stage_vec4_ok(r.map.f[i].dis, map_pitch, sizeof(TIn)))
             vec4 = 0;
     if constexpr (!std::is_same<Dec, DecNone>::value) {
         if (loop)
@@ -368,13 +354,13 @@ hipError_t launch_dec_pow2_packed(int s, const StepRoles &r, const StepGeometry 
 
 }  // namespace
 
-bool decimate_fast_path(const StepRoles &r, int w, int h, int bpc, int s) {
+bool decimate_fast_path(const DecimateBatch &b, int n, int w, int h, int bpc, int s) {
     (void)h;
     if (s < 2 || s > 128 || (s & (s - 1)) != 0) return false;
     const int V = bpc == 8 ? 16 : 8;
     if (w % V != 0) return false;
-    for (int i = 0; i < r.n_dec; ++i)
-        if (((uintptr_t)r.dec_in[0][i] | (uintptr_t)r.dec_in[1][i]) & 15u) return false;
+    for (int i = 0; i < n; ++i)
+        if (((uintptr_t)b.f[i].ref | (uintptr_t)b.f[i].dis) & 15u) return false;
     const int dec_w = (w + s - 1) / s;
     // the last window's right half must lie inside the row (no right mirror)
     if (w - s * (dec_w - 1) < s / 2) return false;
@@ -391,18 +377,11 @@ hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind ma
         r.n_fin > kMaxBatch)
         return hipErrorInvalidValue;
     if ((g.packed != 0) != packed_planes(g.s, g.bpc)) return hipErrorInvalidValue;
-    if (r.n_dec + r.n_map + r.n_fin > 0 && r.slots == nullptr) return hipErrorInvalidValue;
-    for (int i = 0; i < r.n_dec; ++i)
-        if (r.dec_slot[i] >= r.n_slots) return hipErrorInvalidValue;
-    for (int i = 0; i < r.n_map; ++i)
-        if (r.map_slot[i] >= r.n_slots) return hipErrorInvalidValue;
-    for (int i = 0; i < r.n_fin; ++i)
-        if (r.fin_slot[i] >= r.n_slots) return hipErrorInvalidValue;
     if (r.n_dec > 0) {
         // The map role reads what the decimation writes: uint16 window sums
         // or fp32 values.
         if (map_kind != (g.packed ? IN_U16 : IN_F32) && r.n_map > 0) return hipErrorInvalidValue;
-        const bool fast = decimate_fast_path(r, g.w, g.h, g.bpc, g.s);
+        const bool fast = decimate_fast_path(r.dec, r.n_dec, g.w, g.h, g.bpc, g.s);
         if (g.packed) {
             // packed implies s = 2^k: the vector path, else the scalar one
             if (g.bpc == 8) {

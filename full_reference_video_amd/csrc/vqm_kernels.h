@@ -15,7 +15,7 @@
 
 namespace vqm {
 
-constexpr int kMaxBatch = 64;
+constexpr int kMaxBatch = 32;
 
 // The 11 taps of the normalised Gaussian (sigma 1.5) in fp32.
 struct Taps {
@@ -49,27 +49,22 @@ constexpr float kMomentOffset = 128.0f;
 
 // ---------------------------------------------------------------- float_ssim
 
-// One frame of the decimation role (device side).
 struct DecimateFrame {
     const void *ref, *dis;       // raw planes, w x h, tightly packed
     void *out_ref, *out_dis;     // dec_w x dec_h, row pitch dec_pitch samples: fp32 values, or the
                                  // uint16 raw window sums when StepGeometry::packed
 };
+struct DecimateBatch {
+    DecimateFrame f[kMaxBatch];
+};
 
-// One frame of the map and finish roles (device side).
 struct SsimFrame {
-    const void *ref, *dis;       // map input planes (decimated, or raw at scale 1)
+    const void *ref, *dis;       // map input planes (decimated fp32, or raw at scale 1)
     double *partials;            // >= ssim_partials(dec_w, dec_h) doubles
     double *result;              // device-visible address of [score, dB] (pinned host)
 };
-
-// Where an in-flight slot keeps a frame's step outputs.  A context holds one
-// per slot in a device-memory table, written when the slot's scratch is
-// (re)allocated, so that a launch names a frame's slot by its index.
-struct SlotDesc {
-    void *dec_ref, *dec_dis;     // decimated planes
-    double *partials;
-    double *result;              // device-visible address of the pinned result block
+struct SsimBatch {
+    SsimFrame f[kMaxBatch];
 };
 
 // Geometry shared by every role of a step launch.
@@ -99,15 +94,13 @@ inline bool packed_planes(int s, int bpc) {
 // another (whose decimated planes an earlier launch wrote), finish a third
 // (whose partials an earlier launch wrote).  Any role may be empty.
 struct StepRoles {
-    const void *dec_in[2][kMaxBatch];  // raw ref / dis planes of the frames to decimate
-    const void *map_in[2][kMaxBatch];  // map inputs: decimated planes, or raw planes at scale 1
-    uint16_t dec_slot[kMaxBatch];      // slot-table index of each frame, per role
-    uint16_t map_slot[kMaxBatch];
-    uint16_t fin_slot[kMaxBatch];
-    int n_dec, n_map, n_fin;
-    int dec_blocks_per_frame;          // filled in by the launcher
-    const SlotDesc *slots;             // the context's slot table (device memory)
-    int n_slots;                       // its length (every index above is below it)
+    DecimateBatch dec;
+    int n_dec;
+    int dec_blocks_per_frame;    // filled in by the launcher
+    SsimBatch map;
+    int n_map;
+    SsimBatch fin;               // only partials and result are used
+    int n_fin;
 };
 
 // A step launch passes StepRoles by value with a few small structs beside
@@ -115,8 +108,8 @@ struct StepRoles {
 static_assert(sizeof(StepRoles) <= 3584, "step launch arguments exceed the kernel argument block");
 
 // Whether the vectorised power-of-two decimation handles these frames
-// (otherwise the scalar or general paths run; all compute the same exact sums).
-bool decimate_fast_path(const StepRoles &r, int w, int h, int bpc, int s);
+// (otherwise the general path runs; both compute the same exact sums).
+bool decimate_fast_path(const DecimateBatch &b, int n, int w, int h, int bpc, int s);
 
 // Number of partial sums the map role writes per frame.
 int ssim_partials(int W, int H);
@@ -138,7 +131,6 @@ struct MsFrame {
 struct MsBatch {
     MsFrame f[kMaxBatch];
 };
-static_assert(sizeof(MsBatch) <= 3584, "level launch arguments exceed the kernel argument block");
 
 int ms_partials(int W, int H);
 

@@ -219,8 +219,6 @@ struct vqm_ctx {
     std::deque<PendingBatch> pipeline;
     bool timing = false;
     bool capturing = false;              // launches go into a graph: no completion events
-    vqm::SlotDesc *slot_table = nullptr;       // device: where each slot's step outputs live
-    vqm::SlotDesc *slot_table_host = nullptr;  // pinned mirror the table is copied from
     std::vector<TimedLaunch> timed;      // recorded, not yet read
     std::vector<hipEvent_t> event_pool;  // free timing events
     double time_ms[4] = {0, 0, 0, 0};
@@ -261,12 +259,8 @@ int ensure_device(vqm_ctx *ctx) {
     return 0;
 }
 
-// Size (or rebuild) a slot's scratch for geometry g.  The slot is idle.  A
-// rebuilt slot's entry of the slot table is copied to the device on the
-// context's stream, ahead of every launch that can name it; its pinned
-// mirror entry changes only here, when no copy of it is pending (the slot's
-// earlier launches, which come after that copy, have been collected).
-int prepare_slot(vqm_ctx *ctx, Slot &sl, const Geometry &g) {
+// Size (or rebuild) a slot's scratch for geometry g.  The slot is idle.
+int prepare_slot(Slot &sl, const Geometry &g) {
     if (sl.ready && sl.geo == g) return 0;
     sl.release();
     sl.geo = g;
@@ -295,13 +289,6 @@ int prepare_slot(vqm_ctx *ctx, Slot &sl, const Geometry &g) {
     HIP_TRY_ALLOC(hipMalloc(&sl.partials, partials * sizeof(double)));
     HIP_TRY_ALLOC(hipHostMalloc(&sl.result_host, 16 * sizeof(double), hipHostMallocMapped | hipHostMallocCoherent));
     HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void **>(&sl.result_dev), sl.result_host, 0));
-    const size_t idx = (size_t)(&sl - ctx->slots);
-    vqm::SlotDesc &d = ctx->slot_table_host[idx];
-    d.dec_ref = sl.planes + sl.off_ref[0];
-    d.dec_dis = sl.planes + sl.off_dis[0];
-    d.partials = sl.partials;
-    d.result = sl.result_dev;
-    HIP_TRY(hipMemcpyAsync(ctx->slot_table + idx, &d, sizeof d, hipMemcpyHostToDevice, ctx->stream));
     sl.ready = true;
     return 0;
 }
@@ -476,7 +463,13 @@ vqm::StepGeometry step_geometry(const Geometry &g) {
     return sg;
 }
 
-int slot_index(const vqm_ctx *ctx, const Slot *sl) { return (int)(sl - ctx->slots); }
+void fill_map_frame(vqm::SsimFrame &f, const PendingBatch &p, int i, bool decimated) {
+    Slot &s = *p.sl[i];
+    f.ref = decimated ? static_cast<const void *>(s.planes + s.off_ref[0]) : p.in_r[i];
+    f.dis = decimated ? static_cast<const void *>(s.planes + s.off_dis[0]) : p.in_d[i];
+    f.partials = s.partials;
+    f.result = s.result_dev;
+}
 
 // One step launch: decimate `fresh` (may be NULL; at scale 1 it is mapped
 // instead, since there is nothing to decimate), map the pipeline's decimated
@@ -487,8 +480,6 @@ int step(vqm_ctx *ctx, PendingBatch *fresh) {
     const bool decimating = g.s > 1;
     vqm::StepRoles r;
     memset(&r, 0, sizeof r);
-    r.slots = ctx->slot_table;
-    r.n_slots = VQM_MAX_IN_FLIGHT;
     PendingBatch *to_map = nullptr, *to_finish = nullptr;
     for (PendingBatch &p : ctx->pipeline) {
         if (p.stage == STAGE_DECIMATED) to_map = &p;
@@ -498,24 +489,20 @@ int step(vqm_ctx *ctx, PendingBatch *fresh) {
     if (fresh && decimating) {
         r.n_dec = fresh->n;
         for (int i = 0; i < fresh->n; ++i) {
-            r.dec_in[0][i] = fresh->in_r[i];
-            r.dec_in[1][i] = fresh->in_d[i];
-            r.dec_slot[i] = (uint16_t)slot_index(ctx, fresh->sl[i]);
+            Slot &s = *fresh->sl[i];
+            r.dec.f[i].ref = fresh->in_r[i];
+            r.dec.f[i].dis = fresh->in_d[i];
+            r.dec.f[i].out_ref = s.planes + s.off_ref[0];
+            r.dec.f[i].out_dis = s.planes + s.off_dis[0];
         }
     }
     if (to_map) {
-        // the decimated planes of its slots, or its raw planes at scale 1
         r.n_map = to_map->n;
-        for (int i = 0; i < to_map->n; ++i) {
-            const Slot &s = *to_map->sl[i];
-            r.map_in[0][i] = decimating ? static_cast<const void *>(s.planes + s.off_ref[0]) : to_map->in_r[i];
-            r.map_in[1][i] = decimating ? static_cast<const void *>(s.planes + s.off_dis[0]) : to_map->in_d[i];
-            r.map_slot[i] = (uint16_t)slot_index(ctx, to_map->sl[i]);
-        }
+        for (int i = 0; i < to_map->n; ++i) fill_map_frame(r.map.f[i], *to_map, i, decimating);
     }
     if (to_finish) {
         r.n_fin = to_finish->n;
-        for (int i = 0; i < to_finish->n; ++i) r.fin_slot[i] = (uint16_t)slot_index(ctx, to_finish->sl[i]);
+        for (int i = 0; i < to_finish->n; ++i) fill_map_frame(r.fin.f[i], *to_finish, i, decimating);
     }
     const vqm::StepGeometry sg = step_geometry(g);
     // The map reads the decimated planes (uint16 window sums scaled by post,
@@ -625,7 +612,7 @@ int submit(vqm_ctx *ctx, int kind, const void *const *refs, const void *const *d
     p.n = n;
     for (int i = 0; i < n; ++i) {
         p.sl[i] = &ctx->slots[(ctx->head + ctx->count + i) % VQM_MAX_IN_FLIGHT];
-        rc = prepare_slot(ctx, *p.sl[i], geo);
+        rc = prepare_slot(*p.sl[i], geo);
         if (rc) return rc;
         for (int k = 0; k < 16; ++k) p.sl[i]->result_host[k] = NAN;
         p.sl[i]->batch = nullptr;
@@ -678,8 +665,6 @@ int collect(vqm_ctx *ctx, double *score, double *lcs, double *db) {
     return 0;
 }
 
-void destroy(vqm_ctx *ctx);
-
 int create(int device, void *stream, vqm_ctx **out) {
     if (!out) return fail(-EINVAL, "NULL output pointer");
     int n = 0;
@@ -704,15 +689,6 @@ int create(int device, void *stream, vqm_ctx **out) {
         HIP_TRY(hipStreamCreateWithFlags(&ctx->stream, hipStreamNonBlocking));
         ctx->own_stream = true;
     }
-    const size_t table = VQM_MAX_IN_FLIGHT * sizeof(vqm::SlotDesc);
-    hipError_t e1 = hipMalloc(&ctx->slot_table, table);
-    hipError_t e2 = e1 == hipSuccess ? hipHostMalloc(&ctx->slot_table_host, table, hipHostMallocDefault) : e1;
-    if (e1 != hipSuccess || e2 != hipSuccess) {
-        const hipError_t e3 = e1 != hipSuccess ? e1 : e2;
-        destroy(ctx.release());
-        return fail(e3 == hipErrorOutOfMemory ? -ENOMEM : -EIO, "slot table: %s", hipGetErrorString(e3));
-    }
-    memset(ctx->slot_table_host, 0, table);
     *out = ctx.release();
     return 0;
 }
@@ -730,8 +706,6 @@ void destroy(vqm_ctx *ctx) {
         (void)hipEventDestroy(t.stop);
     }
     for (hipEvent_t e : ctx->event_pool) (void)hipEventDestroy(e);
-    if (ctx->slot_table) (void)hipFree(ctx->slot_table);
-    if (ctx->slot_table_host) (void)hipHostFree(ctx->slot_table_host);
     if (ctx->own_stream) (void)hipStreamDestroy(ctx->stream);
     if (cur >= 0) (void)hipSetDevice(cur);
     delete ctx;
@@ -930,7 +904,7 @@ int debug_slot(vqm_ctx *ctx, const Geometry &g, const void *ref, const void *dis
     int rc = ensure_device(ctx);
     if (rc) return rc;
     Slot &sl = ctx->slots[(ctx->head + ctx->count) % VQM_MAX_IN_FLIGHT];
-    rc = prepare_slot(ctx, sl, g);
+    rc = prepare_slot(sl, g);
     if (rc) return rc;
     rc = upload(ctx, sl, ref, dis, dref, ddis);
     if (rc) return rc;
@@ -968,7 +942,7 @@ int record_pass(vqm_graph *g, const void *const *refs, const void *const *dis, i
     vqm_ctx *ctx = g->ctx;
     const Geometry geo = make_geometry(g->kind, w, h, bpc);
     for (int i = 0; i < g->n; ++i) {
-        int rc = prepare_slot(ctx, ctx->slots[i], geo);
+        int rc = prepare_slot(ctx->slots[i], geo);
         if (rc) return rc;
         for (int k = 0; k < 16; ++k) ctx->slots[i].result_host[k] = NAN;
     }
@@ -1256,12 +1230,11 @@ int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, int w, in
     // general path with tap 1 writes the sample values).
     vqm::StepRoles r;
     memset(&r, 0, sizeof r);
-    r.slots = ctx->slot_table;
-    r.n_slots = VQM_MAX_IN_FLIGHT;
     r.n_dec = 1;
-    r.dec_in[0][0] = dref;
-    r.dec_in[1][0] = ddis;
-    r.dec_slot[0] = (uint16_t)slot_index(ctx, sl);
+    r.dec.f[0].ref = dref;
+    r.dec.f[0].dis = ddis;
+    r.dec.f[0].out_ref = sl->planes + sl->off_ref[0];
+    r.dec.f[0].out_dis = sl->planes + sl->off_dis[0];
     const vqm::StepGeometry sg = step_geometry(g);
     LAUNCH_TIMED(ctx, VQM_KERNEL_SSIM_STEP, 1,
                  vqm::launch_ssim_step(r, sg, sg.packed ? vqm::IN_U16 : vqm::IN_F32, g.dpitch,

@@ -21,8 +21,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvqm.so")
 
-VQM_MAX_IN_FLIGHT = 384
-VQM_MAX_BATCH = 64
+VQM_MAX_IN_FLIGHT = 192
+VQM_MAX_BATCH = 32
 VQM_MSSSIM_LCS = 15
 VQM_METRIC_FLOAT_SSIM = 0
 VQM_METRIC_MS_SSIM = 1

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define VQM_ABI_VERSION 4
+#define VQM_ABI_VERSION 3
 
 /* Exported symbols (the library is built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -78,15 +78,13 @@ extern "C" {
 /* Frames a context holds in flight between submit and collect: six full
  * batches, so a float_ssim batch's three pipeline stages can all be
  * enqueued before its frames are awaited. */
-#define VQM_MAX_IN_FLIGHT 384
+#define VQM_MAX_IN_FLIGHT 192
 
 /* Frames one batched submit may hand over (processed per kernel launch).
  * Consecutive launches on one stream leave the GPU idle for a few
  * microseconds between them (the next kernel starts only once the last one
- * has drained), which a batch of frames shares.  Measured float_ssim
- * throughput is highest at 64 frames per batch for 1080p and smaller frames
- * and at 32 for 2160p. */
-#define VQM_MAX_BATCH 64
+ * has drained); 32 frames per launch share that gap. */
+#define VQM_MAX_BATCH 32
 
 /* Number of per-level means vqm_msssim_frame_lcs returns: L_1..L_5,
  * C_1..C_5, S_1..S_5 ([R-1363] Finding 6, enable_lcs). */
