@@ -23,6 +23,9 @@
 // so every pixel of the next level is written exactly once.
 #include "ssim_common.h"
 
+#include <algorithm>
+#include <utility>
+
 namespace vqm {
 namespace {
 
@@ -32,6 +35,42 @@ constexpr int kTW = 32, kTH = 64, kNT = 512, kRB = 4;
 constexpr int kNP = 5;  // moment planes: x, y, x^2, y^2, xy (contrast needs both sigmas)
 
 __constant__ double kBeta[5] = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333};
+
+// One map pixel's terms from its five moments (means with the offset
+// removed, raw second moments): the luminance and contrast deficits 1 - l and
+// 1 - c and the structure s, each in units of 2^-24 truncated toward zero.
+// l = 1 - (mx - my)^2 / (mux^2 + muy^2 + C1) and
+// c = 1 - (sx - sy)^2 / (sx^2 + sy^2 + C2) (the mirrored quotients
+// rewritten, so identical planes give deficits of exactly 0),
+// s = (sxy + C3) / (sx sy + C3), with sx^2 = max(var_x, 0); the three
+// quotients share one reciprocal of the product of the denominators (at most
+// ~1e14).  Both level kernels take every pixel through this function and add
+// the integers exactly (a level's sums stay far below 2^53 in fp64), so the
+// sums, and the score, do not depend on which kernel ran, how it split the
+// plane, or how many frames shared the launch.  Truncation moves a mean by
+// less than 2^-24.
+struct LcsAcc {
+    int dl = 0, dc = 0, s = 0;
+};
+
+__device__ __forceinline__ void ms_pixel(const float (&m)[5], LcsAcc &a) {
+    constexpr float kC3 = kC2 / 2.0f;
+    const float mx = m[0], my = m[1], xx = m[2], yy = m[3], xy = m[4];
+    const float vx = fmaxf(fmaf(-mx, mx, xx), 0.0f);
+    const float vy = fmaxf(fmaf(-my, my, yy), 0.0f);
+    const float cxy = fmaf(-mx, my, xy);
+    const float sdx = hw_sqrt(vx), sdy = hw_sqrt(vy);
+    const float ux = mx + kMomentOffset, uy = my + kMomentOffset;
+    const float dm = mx - my, ds = sdx - sdy;
+    const float d1 = fmaf(ux, ux, fmaf(uy, uy, kC1));
+    const float d2 = (vx + vy) + kC2;
+    const float d3 = fmaf(sdx, sdy, kC3);
+    const float d12 = d1 * d2;
+    const float r = rcp(d12 * d3) * 0x1p24f;
+    a.dl += (int)((dm * dm) * ((d2 * d3) * r));
+    a.dc += (int)((ds * ds) * ((d1 * d3) * r));
+    a.s += (int)((cxy + kC3) * (d12 * r));
+}
 
 template <int TW, int TH, int NT, int RB, typename TIn>
 __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int H, int next_pitch, float unit,
@@ -83,45 +122,271 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
 
     horizontal_moments_in_place<TW, TH, NT, kNP>(lds, taps);
 
-    // Per pixel: l = 1 - (mx - my)^2 / (mux^2 + muy^2 + C1) and
-    // c = 1 - (sx - sy)^2 / (sx^2 + sy^2 + C2) (the mirrored quotients
-    // rewritten, exactly 1 for identical planes), s = (sxy + C3) / (sx sy + C3),
-    // with sx^2 = max(var_x, 0).  The three quotients come from one
-    // reciprocal of the product of the denominators (at most ~1e14, far
-    // inside fp32 range).  For l and c a thread sums only the subtracted
-    // parts and takes them from its count of valid pixels at the end.  A
-    // thread's few pixels and then its wave are summed in fp32, the waves in
-    // fp64.
-    constexpr float kC3 = kC2 / 2.0f;
-    float dl = 0.0f, dc = 0.0f, ps = 0.0f;
+    // A thread's few pixels (at most 64, so the integer sums fit 32 bits),
+    // then the workgroup in fp64, exactly.
+    LcsAcc acc;
     int npx = 0;
     vertical_moments<TW, TH, NT, RB, kNP>(lds, taps, x0, y0, MW, MH, [&](int, int, const float (&m)[kNP]) {
-        const float mx = m[0], my = m[1], xx = m[2], yy = m[3], xy = m[4];
-        const float vx = fmaxf(fmaf(-mx, mx, xx), 0.0f);
-        const float vy = fmaxf(fmaf(-my, my, yy), 0.0f);
-        const float cxy = fmaf(-mx, my, xy);
-        const float sdx = hw_sqrt(vx), sdy = hw_sqrt(vy);
-        const float ux = mx + kMomentOffset, uy = my + kMomentOffset;
-        const float dm = mx - my, ds = sdx - sdy;
-        const float d1 = fmaf(ux, ux, fmaf(uy, uy, kC1));
-        const float d2 = (vx + vy) + kC2;
-        const float d3 = fmaf(sdx, sdy, kC3);
-        const float d12 = d1 * d2;
-        const float r = rcp(d12 * d3);
-        dl = fmaf(dm * dm, (d2 * d3) * r, dl);
-        dc = fmaf(ds * ds, (d1 * d3) * r, dc);
-        ps = fmaf(cxy + kC3, d12 * r, ps);
+        ms_pixel(m, acc);
         ++npx;
     });
-    const float terms[3] = {(float)npx - dl, (float)npx - dc, ps};
-    double acc[3];
-    block_sum_terms<NT, 3>(terms, red, acc);
+    double terms[3] = {(double)npx * 0x1p24 - acc.dl, (double)npx * 0x1p24 - acc.dc, (double)acc.s};
+    block_sum<NT, 3>(terms, red);
     if (threadIdx.x == 0) {
         const int nb = gridDim.x * gridDim.y;
         const int slot = by * gridDim.x + bx;
-        t.partials[slot] = acc[0];
-        t.partials[nb + slot] = acc[1];
-        t.partials[2 * nb + slot] = acc[2];
+        t.partials[slot] = terms[0];
+        t.partials[nb + slot] = terms[1];
+        t.partials[2 * nb + slot] = terms[2];
+    }
+}
+
+// ------------------------------------------------------------ row streaming
+//
+// The level kernel above stages a 2-D tile and filters it horizontally over
+// its 10-row halo too, so 16 % of its horizontal work is repeated by the tile
+// below, and its moment planes make a round trip through LDS.  This kernel
+// walks a strip down the plane instead: each thread owns two adjacent map
+// columns, takes one input row at a time, filters it horizontally from a
+// shared row buffer, and adds it into the eleven unfinished outputs of its
+// columns held in registers (output j = t - 10 is complete after input row
+// t).  Only the strip's top and bottom edges repeat work, (R + 10) / R.  The
+// moments are bit-identical to the tile kernel's: the same products, and
+// both 11-tap sums in the order k = 0..10.
+//
+// Workgroup: kRowsThreads threads, a strip of kRowsStrip map columns and up
+// to R map rows (R even, so the strip starts on an even row and the next
+// level's 2x2 blocks do not straddle strips).  The row buffer holds the five
+// per-sample planes x, y, x^2, y^2, xy of the strip's kRowsStrip + 10 input
+// columns; it is double-buffered, so one barrier per row suffices (a buffer
+// is rewritten two rows later, after every thread has passed the barrier of
+// the row between).  The first five threads also convert the ten columns past
+// the strip.
+//
+// Loads and stores go through buffer resources whose row offset is a scalar,
+// so a row costs no per-lane address arithmetic; columns past the plane are
+// clamped to its last column (they feed only map columns outside the valid
+// region, or no output at all), and rows never leave the plane.
+constexpr int kRowsStrip = 256;
+constexpr int kRowsThreads = kRowsStrip / 2;
+constexpr int kRowsPitch = kRowsStrip + 12;  // >= kRowsStrip + 10 floats, a multiple of 4
+constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
+
+template <typename TIn> struct RowRaw;
+template <> struct RowRaw<uint8_t> {
+    __device__ static uint32_t load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        return __builtin_amdgcn_raw_buffer_load_b8(r, vo, so, 0);
+    }
+    __device__ static float value(uint32_t v) { return (float)v; }
+};
+template <> struct RowRaw<uint16_t> {
+    __device__ static uint32_t load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
+    }
+    __device__ static float value(uint32_t v) { return (float)v; }
+};
+template <> struct RowRaw<float> {
+    __device__ static uint32_t load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0);
+    }
+    __device__ static float value(uint32_t v) { return __builtin_bit_cast(float, v); }
+};
+
+// The raw samples of one input row that a thread converts: its two columns
+// of both planes.
+struct RowPair {
+    uint32_t ra, rb, da, db;
+};
+
+template <int... U, typename F>
+__device__ __forceinline__ void static_steps(std::integer_sequence<int, U...>, F &&f) {
+    (f(std::integral_constant<int, U>{}), ...);
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kRowsThreads) void ms_level_rows(MsBatch b, int pitch, int W, int H, int next_pitch,
+                                                              float unit, int R, Taps taps) {
+    using Raw = RowRaw<TIn>;
+    constexpr int P = kRowsPitch, S = kRowsStrip;
+    __shared__ __attribute__((aligned(16))) float lds[2 * 5 * P];
+    __shared__ double red[3][kRowsThreads / 64];
+
+    int bx, by, bz;
+    xcd_block(bx, by, bz);
+    const MsFrame &fr = b.f[bz];
+    const int MW = W - 10, MH = H - 10;
+    const int x0 = bx * S, y0 = by * R;
+    const int tid = threadIdx.x, c = 2 * tid;
+    const bool last_x = bx == (int)gridDim.x - 1, last_y = by == (int)gridDim.y - 1;
+    const int out_rows = min(R, MH - y0);     // map rows of this strip
+    const int in_rows = min(R + 10, H - y0);  // input rows it reads
+
+    const int nbytes = pitch * H * (int)sizeof(TIn);  // below 2^31 (checked by the launcher)
+    const __amdgpu_buffer_rsrc_t rref = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(fr.ref), 0, nbytes,
+                                                                          kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rdis = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(fr.dis), 0, nbytes,
+                                                                          kRsrcWord3);
+    const int row_bytes = pitch * (int)sizeof(TIn);
+    const int voA = min(x0 + c, W - 1) * (int)sizeof(TIn), voB = min(x0 + c + 1, W - 1) * (int)sizeof(TIn);
+    const int hvoA = min(x0 + S + c, W - 1) * (int)sizeof(TIn);
+    const int hvoB = min(x0 + S + c + 1, W - 1) * (int)sizeof(TIn);
+    const bool wave0 = tid < 64, halo = tid < 5;
+
+    auto load_row = [&](int t, RowPair &m, RowPair &h) __attribute__((always_inline)) {
+        const int so = (y0 + t) * row_bytes;
+        m.ra = Raw::load(rref, voA, so);
+        m.rb = Raw::load(rref, voB, so);
+        m.da = Raw::load(rdis, voA, so);
+        m.db = Raw::load(rdis, voB, so);
+        if (wave0) {
+            h.ra = Raw::load(rref, hvoA, so);
+            h.rb = Raw::load(rref, hvoB, so);
+            h.da = Raw::load(rdis, hvoA, so);
+            h.db = Raw::load(rdis, hvoB, so);
+        }
+    };
+
+    // Next level: this thread's 2x2 block column, and (last strip only) the
+    // halo threads' ones; a block row is complete at each odd input row.
+    float *const nref = fr.next_ref;
+    const bool has_next = nref != nullptr;
+    const int nW = W / 2, nH = H / 2;
+    const int nbx = (x0 + c) / 2, hnbx = (x0 + S + c) / 2;
+    const bool own_x = nbx < nW, hown_x = last_x && halo && hnbx < nW;
+    // (At the last level there is no next plane: the resources then cover
+    // nothing and no store is issued.)
+    const int nbytes_next = has_next ? next_pitch * nH * 4 : 0;
+    const __amdgpu_buffer_rsrc_t nr = __builtin_amdgcn_make_buffer_rsrc(nref, 0, nbytes_next, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t nd = __builtin_amdgcn_make_buffer_rsrc(fr.next_dis, 0, nbytes_next, kRsrcWord3);
+
+    float ring[11][5][2];  // the eleven unfinished outputs of the thread's two columns
+#pragma unroll
+    for (int s = 0; s < 11; ++s)
+#pragma unroll
+        for (int p = 0; p < 5; ++p) ring[s][p][0] = ring[s][p][1] = 0.0f;
+
+    const bool vA = x0 + c < MW, vB = x0 + c + 1 < MW;
+    LcsAcc acc;  // at most 22 pixels (one group of rows) in 32-bit integers
+    double DL = 0.0, DC = 0.0, PS = 0.0;
+    float psx = 0.0f, psy = 0.0f, hpsx = 0.0f, hpsy = 0.0f;  // the previous row's pair sums
+
+    RowPair nm{}, nh{};
+    load_row(0, nm, nh);
+    for (int t0 = 0; t0 < in_rows; t0 += 11) {
+        static_steps(std::make_integer_sequence<int, 11>{}, [&](auto uc) __attribute__((always_inline)) {
+            constexpr int u = decltype(uc)::value;
+            const int t = t0 + u;
+            if (t >= in_rows) return;
+            // Convert this row, then reuse its registers for the next row's
+            // loads (they land while this row is filtered).
+            float *buf = lds + (t & 1) * 5 * P;
+            const float xa = fmaf(Raw::value(nm.ra), unit, -kMomentOffset);
+            const float xb = fmaf(Raw::value(nm.rb), unit, -kMomentOffset);
+            const float ya = fmaf(Raw::value(nm.da), unit, -kMomentOffset);
+            const float yb = fmaf(Raw::value(nm.db), unit, -kMomentOffset);
+            *reinterpret_cast<float2 *>(buf + 0 * P + c) = make_float2(xa, xb);
+            *reinterpret_cast<float2 *>(buf + 1 * P + c) = make_float2(ya, yb);
+            *reinterpret_cast<float2 *>(buf + 2 * P + c) = make_float2(xa * xa, xb * xb);
+            *reinterpret_cast<float2 *>(buf + 3 * P + c) = make_float2(ya * ya, yb * yb);
+            *reinterpret_cast<float2 *>(buf + 4 * P + c) = make_float2(xa * ya, xb * yb);
+            // Next level: the block row (t - 1, t) when t is odd.
+            const bool block_row = has_next && (t & 1) != 0 && (t - 1 < R || last_y);
+            const int so_next = ((y0 + t) / 2) * next_pitch * 4;
+            const float sx = xa + xb, sy = ya + yb;
+            if (block_row && own_x) {
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __builtin_bit_cast(uint32_t, fmaf(psx + sx, 0.25f, kMomentOffset)), nr, nbx * 4, so_next, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __builtin_bit_cast(uint32_t, fmaf(psy + sy, 0.25f, kMomentOffset)), nd, nbx * 4, so_next, 0);
+            }
+            psx = sx;
+            psy = sy;
+            if (halo) {
+                const float hxa = fmaf(Raw::value(nh.ra), unit, -kMomentOffset);
+                const float hxb = fmaf(Raw::value(nh.rb), unit, -kMomentOffset);
+                const float hya = fmaf(Raw::value(nh.da), unit, -kMomentOffset);
+                const float hyb = fmaf(Raw::value(nh.db), unit, -kMomentOffset);
+                float *hb = buf + S + c;
+                *reinterpret_cast<float2 *>(hb + 0 * P) = make_float2(hxa, hxb);
+                *reinterpret_cast<float2 *>(hb + 1 * P) = make_float2(hya, hyb);
+                *reinterpret_cast<float2 *>(hb + 2 * P) = make_float2(hxa * hxa, hxb * hxb);
+                *reinterpret_cast<float2 *>(hb + 3 * P) = make_float2(hya * hya, hyb * hyb);
+                *reinterpret_cast<float2 *>(hb + 4 * P) = make_float2(hxa * hya, hxb * hyb);
+                const float hsx = hxa + hxb, hsy = hya + hyb;
+                if (block_row && hown_x) {
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __builtin_bit_cast(uint32_t, fmaf(hpsx + hsx, 0.25f, kMomentOffset)), nr, hnbx * 4, so_next, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __builtin_bit_cast(uint32_t, fmaf(hpsy + hsy, 0.25f, kMomentOffset)), nd, hnbx * 4, so_next, 0);
+                }
+                hpsx = hsx;
+                hpsy = hsy;
+            }
+            if (t + 1 < in_rows) load_row(t + 1, nm, nh);
+
+            __syncthreads();  // the row is in the buffer
+
+            // Horizontal 11-tap sums of the thread's two columns, plane by
+            // plane, each added at once into the eleven unfinished outputs.
+#pragma unroll
+            for (int p = 0; p < 5; ++p) {
+                float v[12];
+#pragma unroll
+                for (int k = 0; k < 6; ++k) {
+                    const float2 w = *reinterpret_cast<const float2 *>(buf + p * P + c + 2 * k);
+                    v[2 * k] = w.x;
+                    v[2 * k + 1] = w.y;
+                }
+                float h0 = 0.0f, h1 = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 11; ++k) {
+                    h0 = fmaf(taps.g[k], v[k], h0);
+                    h1 = fmaf(taps.g[k], v[k + 1], h1);
+                }
+#pragma unroll
+                for (int s = 0; s < 11; ++s) {
+                    const int k = (u - s + 11) % 11;  // this row's tap for the output in slot s
+                    if (k == 0) {
+                        ring[s][p][0] = fmaf(taps.g[0], h0, 0.0f);
+                        ring[s][p][1] = fmaf(taps.g[0], h1, 0.0f);
+                    } else {
+                        ring[s][p][0] = fmaf(taps.g[k], h0, ring[s][p][0]);
+                        ring[s][p][1] = fmaf(taps.g[k], h1, ring[s][p][1]);
+                    }
+                }
+            }
+
+            // Output t - 10 is complete; it sits in slot (u + 1) % 11.
+            const int j = t - 10;
+            if (j >= 0 && j < out_rows) {
+                constexpr int sc = (u + 1) % 11;
+                if (vA) {
+                    const float mm[5] = {ring[sc][0][0], ring[sc][1][0], ring[sc][2][0], ring[sc][3][0],
+                                         ring[sc][4][0]};
+                    ms_pixel(mm, acc);
+                }
+                if (vB) {
+                    const float mm[5] = {ring[sc][0][1], ring[sc][1][1], ring[sc][2][1], ring[sc][3][1],
+                                         ring[sc][4][1]};
+                    ms_pixel(mm, acc);
+                }
+            }
+        });
+        DL += (double)acc.dl;
+        DC += (double)acc.dc;
+        PS += (double)acc.s;
+        acc = LcsAcc{};
+    }
+
+    const double npx = (double)out_rows * (double)((int)vA + (int)vB) * 0x1p24;
+    double terms[3] = {npx - DL, npx - DC, PS};
+    block_sum<kRowsThreads, 3>(terms, red);
+    if (tid == 0) {
+        const int nb = gridDim.x * gridDim.y;
+        const int slot = by * gridDim.x + bx;
+        fr.partials[slot] = terms[0];
+        fr.partials[nb + slot] = terms[1];
+        fr.partials[2 * nb + slot] = terms[2];
     }
 }
 
@@ -136,9 +401,9 @@ __global__ __launch_bounds__(NT) void ms_finish(MsFinishBatch b, MsLevels lv) {
         double tot[3];
         sum_spans<NT, 3>(fr.partials + lv.offset[j], lv.nb[j], (size_t)lv.nb[j], tot, red);
         if (threadIdx.x == 0) {
-            lcs[j] = tot[0] / lv.count[j];
-            lcs[5 + j] = tot[1] / lv.count[j];
-            lcs[10 + j] = tot[2] / lv.count[j];
+            lcs[j] = tot[0] / lv.count[j] * 0x1p-24;
+            lcs[5 + j] = tot[1] / lv.count[j] * 0x1p-24;
+            lcs[10 + j] = tot[2] / lv.count[j] * 0x1p-24;
         }
         __syncthreads();  // red[] is reused by the next level; lcs[] is complete after the last
     }
@@ -165,16 +430,88 @@ __global__ __launch_bounds__(NT) void ms_finish(MsFinishBatch b, MsLevels lv) {
     __threadfence_system();
 }
 
+// Which level kernel a batch takes, and its grid.  The choice compares
+// estimates of the VALU issue each needs per SIMD (256 CUs x 4 SIMDs), from
+// the instruction counts of their compiled code: the tile kernel issues about
+// 914 VALU instructions per wave, spread over the whole chip; the row kernel
+// about 330 per wave and input row, and it runs in rounds of three waves per
+// SIMD (its register use allows three), each round as long as its strips are
+// tall.  So the row kernel wins on large planes in large batches (2160p
+// levels 1-3 in batches of 32), and the tile kernel on small planes or
+// batches, whose few tall strips would leave most SIMDs idle.  The strip
+// height R (even, at least 16 rows) is picked by the same estimate: 136 rows
+// (five rounds) at 2160p level 1 and 180 rows (one round) at level 2 in
+// batches of 32, which a sweep of R on the hardware also found best.  The row
+// kernel's buffer offsets are 32-bit, so planes of 2^31 bytes or more (fp32
+// levels, pitch up to W + 63) always take the tile kernel.
+struct MsPlan {
+    bool rows;
+    int R, gx, gy;
+};
+
+constexpr double kTileWaveInstr = 914.0, kRowsStepInstr = 330.0;
+constexpr int kSimds = 256 * 4, kRowsWavesPerSimd = 3, kRowsMinR = 16;
+// A plan's rounds cost a tenth of a round more, for the spread of its
+// strips' finishing times: measured at 2160p (batches of 32), strips of
+// 120-136 rows in five rounds run 8 % faster than strips of 718 rows in one
+// round that leaves 6 % of the slots empty, which the bare count calls even.
+constexpr double kRowsTail = 0.1;
+
+MsPlan ms_plan(int W, int H, int n) {
+    const int MW = W - 10, MH = H - 10;
+    MsPlan p{false, 0, (MW + kTW - 1) / kTW, (MH + kTH - 1) / kTH};
+    if ((long long)(W + 64) * (long long)H * 4 >= (1ll << 31)) return p;
+    double best = kTileWaveInstr * (kNT / 64) * (double)p.gx * (double)p.gy * n / kSimds;
+    const int gx = (MW + kRowsStrip - 1) / kRowsStrip;
+    const long long slots = (long long)kRowsWavesPerSimd * kSimds;
+    for (int strips = 1; strips <= MH / kRowsMinR; ++strips) {
+        int R = (MH + strips - 1) / strips;
+        R += R & 1;
+        const int gy = (MH + R - 1) / R;
+        const long long waves = (long long)(kRowsThreads / 64) * gx * gy * n;
+        const double rounds = (double)((waves + slots - 1) / slots) + kRowsTail;
+        const double cost = rounds * kRowsWavesPerSimd * (R + 10) * kRowsStepInstr;
+        if (cost < best) {
+            best = cost;
+            p = MsPlan{true, R, gx, gy};
+        }
+    }
+    return p;
+}
+
 }  // namespace
 
-int ms_partials(int W, int H) {
-    return ((W - 10 + kTW - 1) / kTW) * ((H - 10 + kTH - 1) / kTH);
+int ms_partials(int W, int H, int n) {
+    const MsPlan p = ms_plan(W, H, n);
+    return p.gx * p.gy;
+}
+
+int ms_partials_max(int W, int H) {
+    int m = 0;
+    for (int n = 1; n <= kMaxBatch; ++n) m = std::max(m, ms_partials(W, H, n));
+    return m;
 }
 
 hipError_t launch_ms_level(const MsBatch &b, int n, InKind kind, int pitch, int W, int H, int next_pitch,
                            float unit, const Taps &taps, hipStream_t stream, const KernelTimer &timer) {
     if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
-    const dim3 grid((W - 10 + kTW - 1) / kTW, (H - 10 + kTH - 1) / kTH, n);
+    const MsPlan p = ms_plan(W, H, n);
+    const dim3 grid(p.gx, p.gy, n);
+    if (p.rows) {
+        switch (kind) {
+        case IN_F32:
+            return launch_kernel(ms_level_rows<float>, grid, dim3(kRowsThreads), stream, timer, b, pitch, W, H,
+                                 next_pitch, unit, p.R, taps);
+        case IN_U8:
+            return launch_kernel(ms_level_rows<uint8_t>, grid, dim3(kRowsThreads), stream, timer, b, pitch, W, H,
+                                 next_pitch, unit, p.R, taps);
+        case IN_U16:
+            return launch_kernel(ms_level_rows<uint16_t>, grid, dim3(kRowsThreads), stream, timer, b, pitch, W, H,
+                                 next_pitch, unit, p.R, taps);
+        default:
+            return hipErrorInvalidValue;
+        }
+    }
     const size_t bytes = kind == IN_F32 ? 4 : (kind == IN_U16 ? 2 : 1);
     int vec4 = 1;
     for (int i = 0; i < n; ++i)

@@ -125,14 +125,17 @@ hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind ma
 
 struct MsFrame {
     const void *ref, *dis;       // level planes with row pitch `pitch`
-    double *partials;            // this level's 3 spans (l, c, s) of ms_partials(W, H) doubles
+    double *partials;            // this level's 3 spans (l, c, s) of ms_partials(W, H, n) doubles
     float *next_ref, *next_dis;  // floor(W/2) x floor(H/2), pitch next_pitch; NULL at level 5
 };
 struct MsBatch {
     MsFrame f[kMaxBatch];
 };
 
-int ms_partials(int W, int H);
+// Partial sums per span that a batch of n frames writes at a W x H level (the
+// grid of the kernel the batch takes), and the most any batch writes.
+int ms_partials(int W, int H, int n);
+int ms_partials_max(int W, int H);
 
 // One MS-SSIM level of n frames: moments and the l/c/s partial sums of the
 // valid region, plus the exact 2x2 mean of the level into the next plane.

@@ -280,7 +280,7 @@ int prepare_slot(Slot &sl, const Geometry &g) {
         }
         for (int j = 0; j < kLevels; ++j) {
             sl.span[j] = partials;
-            partials += 3 * (size_t)vqm::ms_partials(g.lw[j], g.lh[j]);
+            partials += 3 * (size_t)vqm::ms_partials_max(g.lw[j], g.lh[j]);
         }
     }
     sl.planes_bytes = floats * sizeof(float);
@@ -571,7 +571,7 @@ int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r
     }
     vqm::MsLevels lv;
     for (int j = 0; j < kLevels; ++j) {
-        lv.nb[j] = vqm::ms_partials(g.lw[j], g.lh[j]);
+        lv.nb[j] = vqm::ms_partials(g.lw[j], g.lh[j], n);
         lv.offset[j] = (long long)sl[0]->span[j];
         lv.count[j] = (double)(g.lw[j] - 10) * (double)(g.lh[j] - 10);
     }
@@ -1288,6 +1288,52 @@ int vqm_debug_pyramid(vqm_ctx *ctx, const void *ref, const void *dis, int w, int
     HIP_TRY(hipMemcpy2DAsync(out_dis, g.lw[j] * sizeof(float), sl->planes + sl->off_dis[j],
                              g.lpitch[j] * sizeof(float), g.lw[j] * sizeof(float), g.lh[j], hipMemcpyDeviceToHost,
                              ctx->stream));
+    HIP_TRY(hipStreamSynchronize(ctx->stream));
+    return 0;
+}
+
+int vqm_debug_pyramid_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n, int w, int h,
+                            int bpc, int level, float *out_ref, float *out_dis) {
+    DeviceScope scope;
+    if (!ctx || !refs || !dis || !out_ref || !out_dis) return fail(-EINVAL, "NULL argument");
+    if (n < 1 || n > VQM_MAX_BATCH) return fail(-EINVAL, "batch of %d frames outside 1..%d", n, VQM_MAX_BATCH);
+    if (level < 2 || level > kLevels) return fail(-EINVAL, "pyramid level %d outside 2..5", level);
+    int rc = 0;
+    for (int i = 0; i < n; ++i) {
+        rc = check_args(refs[i], dis[i], w, h, bpc);
+        if (rc) return rc;
+    }
+    rc = gate_msssim(w, h);
+    if (rc) return rc;
+    const Geometry g = make_geometry(KIND_MSSSIM, w, h, bpc);
+    rc = drain(ctx);
+    if (rc) return rc;
+    if (ctx->count + n > VQM_MAX_IN_FLIGHT)
+        return fail(-EAGAIN, "%d frames in flight leave no room for %d more", ctx->count, n);
+    rc = ensure_device(ctx);
+    if (rc) return rc;
+    Slot *sl[VQM_MAX_BATCH];
+    const void *dref[VQM_MAX_BATCH], *ddis[VQM_MAX_BATCH];
+    for (int i = 0; i < n; ++i) {
+        Slot &s = ctx->slots[(ctx->head + ctx->count + i) % VQM_MAX_IN_FLIGHT];
+        rc = prepare_slot(s, g);
+        if (rc) return rc;
+        rc = upload(ctx, s, refs[i], dis[i], &dref[i], &ddis[i]);
+        if (rc) return rc;
+        sl[i] = &s;
+    }
+    rc = enqueue_msssim(ctx, sl, n, dref, ddis);
+    if (rc) return rc;
+    const int j = level - 1;
+    const size_t plane = (size_t)g.lw[j] * (size_t)g.lh[j];
+    for (int i = 0; i < n; ++i) {
+        HIP_TRY(hipMemcpy2DAsync(out_ref + i * plane, g.lw[j] * sizeof(float), sl[i]->planes + sl[i]->off_ref[j],
+                                 g.lpitch[j] * sizeof(float), g.lw[j] * sizeof(float), g.lh[j],
+                                 hipMemcpyDeviceToHost, ctx->stream));
+        HIP_TRY(hipMemcpy2DAsync(out_dis + i * plane, g.lw[j] * sizeof(float), sl[i]->planes + sl[i]->off_dis[j],
+                                 g.lpitch[j] * sizeof(float), g.lw[j] * sizeof(float), g.lh[j],
+                                 hipMemcpyDeviceToHost, ctx->stream));
+    }
     HIP_TRY(hipStreamSynchronize(ctx->stream));
     return 0;
 }

@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
                                          c_void_p, c_void_p]
         L.vqm_debug_pyramid.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                         c_void_p, c_void_p]
+        L.vqm_debug_pyramid_batch.argtypes = [c_void_p, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int,
+                                              c_int, c_int, c_int, c_int, c_void_p, c_void_p]
         L.vqm_graph_create.argtypes = [c_int, c_void_p, c_int, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p),
                                        c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(c_void_p)]
         L.vqm_graph_launch.argtypes = [c_void_p]
@@ -358,6 +360,34 @@ class Context:
         out_d = np.empty((lh, lw), np.float32)
         _check(lib().vqm_debug_pyramid(self._h, pr, pd, w, h, int(bpc), int(level), out_r.ctypes.data,
                                        out_d.ctypes.data), "vqm_debug_pyramid")
+        return out_r, out_d
+
+
+    def vqm_debug_pyramid_batch(self, refs, diss, bpc: int, level: int):
+        """Level `level` of each frame's pyramid, built as one batch: two
+        arrays of shape (n, lh, lw)."""
+        if len(refs) != len(diss):
+            raise ValueError("refs and dis differ in length")
+        n = len(refs)
+        if not 1 <= n <= VQM_MAX_BATCH:
+            raise ValueError(f"batch of {n} frames outside 1..{VQM_MAX_BATCH}")
+        pr = (ctypes.c_void_p * n)()
+        pd = (ctypes.c_void_p * n)()
+        keep = []  # the planes the pointers address, alive until the call returns
+        w = h = None
+        for i, (r, d) in enumerate(zip(refs, diss)):
+            a, b, fw, fh, k = _pair(r, d, bpc)
+            keep.append(k)
+            if w is None:
+                w, h = fw, fh
+            elif (fw, fh) != (w, h):
+                raise ValueError("frames of one batch must share their size")
+            pr[i], pd[i] = a, b
+        lw, lh = w >> (level - 1), h >> (level - 1)
+        out_r = np.empty((n, lh, lw), np.float32)
+        out_d = np.empty((n, lh, lw), np.float32)
+        _check(lib().vqm_debug_pyramid_batch(self._h, pr, pd, n, w, h, int(bpc), int(level), out_r.ctypes.data,
+                                             out_d.ctypes.data), "vqm_debug_pyramid_batch")
         return out_r, out_d
 
 

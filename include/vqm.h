@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define VQM_ABI_VERSION 3
+#define VQM_ABI_VERSION 4
 
 /* Exported symbols (the library is built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -309,6 +309,15 @@ VQM_API int vqm_debug_decimate(vqm_ctx *ctx, const void *ref, const void *dis, i
  * the bit-exactness tests of the pyramid. */
 VQM_API int vqm_debug_pyramid(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc,
                       int level, float *out_ref, float *out_dis);
+
+/* vqm_debug_pyramid for a batch of n frames (1..VQM_MAX_BATCH) of one size,
+ * built in one launch per level exactly as vqm_msssim_submit_batch builds
+ * them (so the level kernel a batch of that size takes runs): level `level` of
+ * frame i is copied to out_ref + i * lw * lh and out_dis + i * lw * lh, with
+ * lw x lh the level's size.  Blocking.  For the bit-exactness tests of the
+ * pyramid. */
+VQM_API int vqm_debug_pyramid_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n, int w,
+                                    int h, int bpc, int level, float *out_ref, float *out_dis);
 
 /* Message of the last failed call on this thread ("" if none). */
 VQM_API const char *vqm_last_error(void);

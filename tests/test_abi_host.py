@@ -52,7 +52,7 @@ def header_constants():
 
 
 def test_abi_version():
-    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 3
+    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 4
 
 
 def test_graft_entry_check_matches_the_built_library():
@@ -126,6 +126,9 @@ def test_argument_errors_before_any_hip_call():
     assert L.vqm_collect(None, ctypes.byref(s), None) == -errno.EINVAL
     assert L.vqm_collect_db(None, ctypes.byref(s), None) == -errno.EINVAL
     assert L.vqm_ssim_submit(None, p, p, 20, 20, 8) == -errno.EINVAL
+    arr = (ctypes.c_void_p * 2)(p, p)
+    out = np.zeros(4, np.float32).ctypes.data
+    assert L.vqm_debug_pyramid_batch(None, arr, arr, 2, 400, 400, 8, 2, out, out) == -errno.EINVAL
 
 
 def test_graph_argument_errors_before_any_hip_call():

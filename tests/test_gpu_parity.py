@@ -343,6 +343,47 @@ def test_msssim_pyramid_bit_exact(ctx, w, h, bpc):
         assert np.array_equal(bits(gd), bits(xd))
 
 
+# Sizes and batches that take the row-streaming level kernel at levels 1-2
+# (strips of 256 columns with a ragged last one, odd plane sizes, several
+# strip rows); a batch of one frame takes the tile kernel.
+ROWS_CASES = [(2001, 1203, 16), (1921, 1081, 8), (1283, 767, 12)]
+
+
+@pytest.mark.parametrize("w,h,bpc", ROWS_CASES)
+def test_msssim_pyramid_bit_exact_in_a_full_batch(ctx, w, h, bpc):
+    src = synth.FrameSource(5, w=w, h=h, bpc=bpc)
+    n = vqm.VQM_MAX_BATCH
+    pairs = [src.pair(t) for t in range(n)]
+    sample = (0, n // 2, n - 1)
+    want = {t: (oracle.sample_plane(pairs[t][0], bpc), oracle.sample_plane(pairs[t][1], bpc)) for t in sample}
+    for level in range(2, 6):
+        say(f"batched pyramid {w}x{h} bpc {bpc} level {level}")
+        gr, gd = ctx.vqm_debug_pyramid_batch([r for r, _ in pairs], [d for _, d in pairs], bpc, level)
+        for t in sample:
+            xr, xd = oracle.downsample(want[t][0]), oracle.downsample(want[t][1])
+            want[t] = (xr, xd)
+            assert np.array_equal(bits(gr[t]), bits(xr)), (level, t)
+            assert np.array_equal(bits(gd[t]), bits(xd)), (level, t)
+
+
+@pytest.mark.parametrize("w,h,bpc", ROWS_CASES)
+def test_msssim_score_does_not_depend_on_the_batch(ctx, w, h, bpc):
+    # A level's sums are exact (integer terms), so the score is the same
+    # bits whichever level kernel the batch size selects.
+    src = synth.FrameSource(5, w=w, h=h, bpc=bpc)
+    n = vqm.VQM_MAX_BATCH
+    pairs = [src.pair(t) for t in range(n)]
+    say(f"msssim batch independence {w}x{h} bpc {bpc}")
+    ctx.vqm_msssim_submit_batch([r for r, _ in pairs], [d for _, d in pairs], bpc)
+    batched = [ctx.vqm_collect(want_lcs=True) for _ in range(n)]
+    for t in (0, 7, n - 1):
+        s1, l1 = vqm.vqm_msssim_frame_lcs(*pairs[t], bpc)
+        assert batched[t][0] == s1, t
+        assert np.array_equal(batched[t][1], l1), t
+    say(f"msssim batch independence {w}x{h}: oracle")
+    assert abs(batched[7][0] - oracle.msssim(*pairs[7], bpc)) <= TOL
+
+
 def test_msssim_identity(ctx):
     src = synth.FrameSource(5, w=960, h=540)
     ref, _ = src.pair(0)
