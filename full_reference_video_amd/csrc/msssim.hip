@@ -16,11 +16,18 @@
 // L_5^b5 * prod_j C_j^b_j * S_j^b_j, b = {0.0448, 0.2856, 0.3001, 0.2363,
 // 0.1333} (the published MS-SSIM weights), NaN when any C_j or S_j <= 0.
 //
-// The tile kernel is the SSIM-map kernel's (LDS-staged halo tile, separable
-// 11-tap moments) with three fp64 sums per thread, plus the downsample: each
-// workgroup writes the next level's pixels whose 2x2 block starts inside its
-// own tile (the last tile column/row also takes the plane's remaining edge),
-// so every pixel of the next level is written exactly once.
+// Two level kernels compute the same per-pixel moments and terms, bit for
+// bit (the same products and 11-tap sums in the same order, and one shared
+// term function), and each writes every pixel of the next level exactly once:
+// - the tile kernel is the SSIM-map kernel's (LDS-staged halo tile,
+//   separable 11-tap moments) plus the downsample of the 2x2 blocks that
+//   start inside its tile (the last tile column/row also takes the plane's
+//   remaining edge);
+// - the row-streaming kernel walks 256-column strips down the plane with the
+//   vertical filter in registers (below).
+// The per-pixel terms are summed exactly as integers, so which kernel ran,
+// and how it split the plane, does not change a single bit of the score; the
+// launcher picks per level and batch size (ms_plan).
 #include "ssim_common.h"
 
 #include <algorithm>
