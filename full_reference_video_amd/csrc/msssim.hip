@@ -27,7 +27,11 @@
 //   vertical filter in registers (below).
 // The per-pixel terms are summed exactly as integers, so which kernel ran,
 // and how it split the plane, does not change a single bit of the score; the
-// launcher picks per level and batch size (ms_plan).
+// launcher picks per level and batch size (ms_plan).  Both ideas have a
+// precedent in "ADR-1357: Run the SYCL CAMBI extractor entirely on the
+// device", Decision: there a work-item owns a column and slides its window
+// down the rows, and the pooled sum is formed exactly as an integer in units
+// of 2^-24.
 #include "ssim_common.h"
 
 #include <algorithm>
