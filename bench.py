@@ -112,6 +112,18 @@ def run_pass(ctxs, frameset, metric, batch, lag):
     return vqm.vqm_score_frames(ctxs, m, frameset, batch, lag).tolist()
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, as /proc/cpuinfo gives it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(host, wl, budget_s: float):
     """The oracle as it stands, one thread, over the workload's frames in order
     (cycling), until about ``budget_s`` seconds of oracle time are spent."""
@@ -128,7 +140,7 @@ def cpu_baseline(host, wl, budget_s: float):
             break
     return {"value": round(n / el, 3), "unit": "frames/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} frame pairs of {wl.name} (frames 0..{min(n, len(host)) - 1}, cycling), "
-                      f"one thread, {el:.1f} s"}
+                      f"one thread, {el:.1f} s, {cpu_model()}"}
 
 
 # Frames the all-cores baseline's worker processes read (inherited through
@@ -169,7 +181,7 @@ def cpu_baseline_all_cores(host, wl, budget_s: float, cores: int):
     el = max(r[1] for r in res)
     return {"value": round(n / el, 3), "unit": "frames/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} frame pairs of {wl.name}, {cores} processes of the single-threaded oracle "
-                      f"on disjoint frames, {el:.1f} s"}
+                      f"on disjoint frames, {el:.1f} s, {cpu_model()}"}
 
 
 def copy_bandwidth(torch, mib: int = 1024, reps: int = 10) -> float:

@@ -67,3 +67,8 @@ def test_recorded_traffic_scales_per_frame_and_checks_the_sources(tmp_path, monk
     rec["kernel_sources_sha256"] = "0" * 64
     p.write_text(json.dumps(rec))
     assert bench.recorded_traffic("float_ssim_3840x2160_10bit", 32.0) is None
+
+
+def test_cpu_model_names_the_host_cpu():
+    m = bench.cpu_model()
+    assert isinstance(m, str) and m
