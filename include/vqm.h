@@ -56,8 +56,12 @@
  *     (C3 = C2/2); MS = L5^b5 * prod_j (C_j S_j)^b_j with
  *     b = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333}; NaN when any C_j or S_j
  *     is <= 0.  All five levels and the combine are enqueued at once and the
- *     host waits once per frame ([R-1363] Finding 6).
- *   - Scores are bitwise repeatable for the same input on the same device.
+ *     host waits once per frame ([R-1363] Finding 6).  Each pixel's l, c, s
+ *     terms are truncated to units of 2^-24 and summed exactly, so a level's
+ *     means do not depend on the order of addition ([ADR-1357] Decision sums
+ *     CAMBI's pool exactly in the same units).
+ *   - Scores are bitwise repeatable for the same input on the same device,
+ *     whatever the batch a frame is submitted in.
  */
 #ifndef VQM_H
 #define VQM_H
