@@ -293,6 +293,15 @@ int prepare_slot(Slot &sl, const Geometry &g) {
     return 0;
 }
 
+// Flags of the events the host waits on before it reads a batch's results.
+// The results are the only memory the host reads after such a wait, and the
+// finish roles write them to coherent pinned host memory followed by a
+// system-scope fence of their own, so they are visible before the kernel
+// ends; the event's own system-scope release (an L2 write-back of the
+// decimated planes and partials, which the host never reads) is dropped:
+// 1.2 % of the 2160p float_ssim stream.
+constexpr unsigned kResultEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
+
 // A free batch event (no frame of an earlier batch still refers to it).
 int take_batch_event(vqm_ctx *ctx, BatchEvent **out) {
     for (auto &be : ctx->batch_events)
@@ -301,7 +310,7 @@ int take_batch_event(vqm_ctx *ctx, BatchEvent **out) {
             return 0;
         }
     std::unique_ptr<BatchEvent> be(new BatchEvent());
-    HIP_TRY(hipEventCreateWithFlags(&be->ev, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&be->ev, kResultEventFlags));
     *out = be.get();
     ctx->batch_events.push_back(std::move(be));
     return 0;
@@ -1018,7 +1027,7 @@ int graph_create(int device, void *stream, int metric, const void *const *refs, 
             if (rc) return rc;
             if (k != PTR_DEVICE) return fail(-EINVAL, "frame %d: a recorded pass takes device memory only", i);
         }
-    HIP_TRY(hipEventCreateWithFlags(&g->done, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&g->done, kResultEventFlags));
     rc = record_pass(g.get(), refs, dis, w, h, bpc, batch);
     if (rc) return rc;
     *out = g.release();
