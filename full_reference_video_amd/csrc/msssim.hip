@@ -23,7 +23,7 @@
 //   separable 11-tap moments) plus the downsample of the 2x2 blocks that
 //   start inside its tile (the last tile column/row also takes the plane's
 //   remaining edge);
-// - the row-streaming kernel walks 256-column strips down the plane with the
+// - the row-streaming kernel walks 128-column strips down the plane with the
 //   vertical filter in registers (below).
 // The per-pixel terms are summed exactly as integers, so which kernel ran,
 // and how it split the plane, does not change a single bit of the score; the
@@ -165,23 +165,24 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
 // moments are bit-identical to the tile kernel's: the same products, and
 // both 11-tap sums in the order k = 0..10.
 //
-// Workgroup: kRowsThreads threads, a strip of kRowsStrip map columns and up
+// Workgroup: NW waves, a strip of 128 NW map columns and up
 // to R map rows (R even, so the strip starts on an even row and the next
 // level's 2x2 blocks do not straddle strips).  The row buffer holds the five
-// per-sample planes x, y, x^2, y^2, xy of the strip's kRowsStrip + 10 input
+// per-sample planes x, y, x^2, y^2, xy of the strip's 128 NW + 10 input
 // columns; it is double-buffered, so one barrier per row suffices (a buffer
 // is rewritten two rows later, after every thread has passed the barrier of
 // the row between).  The first five threads also convert the ten columns past
-// the strip.
+// the strip.  One wave per workgroup (kRowsWaves) measured fastest: its
+// barrier waits for no other wave, which outweighs the halo columns costing
+// the wave a second conversion pass (2160p MS-SSIM 19.6k frames/s against
+// 19.0k with two waves and 17.0k with three).
 //
 // Loads and stores go through buffer resources whose row offset is a scalar,
 // so a row costs no per-lane address arithmetic; columns past the plane are
 // clamped to its last column (they feed only map columns outside the valid
 // region, or no output at all), and rows never leave the plane.
-constexpr int kRowsStrip = 256;
-constexpr int kRowsThreads = kRowsStrip / 2;
-constexpr int kRowsPitch = kRowsStrip + 12;  // >= kRowsStrip + 10 floats, a multiple of 4
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
+constexpr int kRowsWaves = 1;                // waves per workgroup (strips of 128 kRowsWaves columns)
 
 template <typename TIn> struct RowRaw;
 template <> struct RowRaw<uint8_t> {
@@ -214,13 +215,14 @@ __device__ __forceinline__ void static_steps(std::integer_sequence<int, U...>, F
     (f(std::integral_constant<int, U>{}), ...);
 }
 
-template <typename TIn>
-__global__ __launch_bounds__(kRowsThreads) void ms_level_rows(MsBatch b, int pitch, int W, int H, int next_pitch,
-                                                              float unit, int R, Taps taps) {
+template <typename TIn, int NW>
+__global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, int W, int H, int next_pitch,
+                                                         float unit, int R, Taps taps) {
     using Raw = RowRaw<TIn>;
-    constexpr int P = kRowsPitch, S = kRowsStrip;
+    constexpr int S = 128 * NW;   // map columns of the strip, two per thread
+    constexpr int P = S + 12;     // LDS row pitch: >= S + 10 floats, a multiple of 4
     __shared__ __attribute__((aligned(16))) float lds[2 * 5 * P];
-    __shared__ double red[3][kRowsThreads / 64];
+    __shared__ double red[3][NW];
 
     int bx, by, bz;
     xcd_block(bx, by, bz);
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(kRowsThreads) void ms_level_rows(MsBatch b, int pit
 
     const double npx = (double)out_rows * (double)((int)vA + (int)vB) * 0x1p24;
     double terms[3] = {npx - DL, npx - DC, PS};
-    block_sum<kRowsThreads, 3>(terms, red);
+    block_sum<64 * NW, 3>(terms, red);
     if (tid == 0) {
         const int nb = gridDim.x * gridDim.y;
         const int slot = by * gridDim.x + bx;
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(NT) void ms_finish(MsFinishBatch b, MsLevels lv) {
 // levels, pitch up to W + 63) always take the tile kernel.
 struct MsPlan {
     bool rows;
-    int R, gx, gy;
+    int nw, R, gx, gy;  // nw: waves per row-kernel workgroup (strips of 128 nw columns)
 };
 
 constexpr double kTileWaveInstr = 914.0, kRowsStepInstr = 330.0;
@@ -470,21 +472,22 @@ constexpr double kRowsTail = 0.1;
 
 MsPlan ms_plan(int W, int H, int n) {
     const int MW = W - 10, MH = H - 10;
-    MsPlan p{false, 0, (MW + kTW - 1) / kTW, (MH + kTH - 1) / kTH};
+    MsPlan p{false, 0, 0, (MW + kTW - 1) / kTW, (MH + kTH - 1) / kTH};
     if ((long long)(W + 64) * (long long)H * 4 >= (1ll << 31)) return p;
     double best = kTileWaveInstr * (kNT / 64) * (double)p.gx * (double)p.gy * n / kSimds;
-    const int gx = (MW + kRowsStrip - 1) / kRowsStrip;
     const long long slots = (long long)kRowsWavesPerSimd * kSimds;
+    const int nw = kRowsWaves;
+    const int gx = (MW + 128 * nw - 1) / (128 * nw);
     for (int strips = 1; strips <= MH / kRowsMinR; ++strips) {
         int R = (MH + strips - 1) / strips;
         R += R & 1;
         const int gy = (MH + R - 1) / R;
-        const long long waves = (long long)(kRowsThreads / 64) * gx * gy * n;
+        const long long waves = (long long)nw * gx * gy * n;
         const double rounds = (double)((waves + slots - 1) / slots) + kRowsTail;
         const double cost = rounds * kRowsWavesPerSimd * (R + 10) * kRowsStepInstr;
         if (cost < best) {
             best = cost;
-            p = MsPlan{true, R, gx, gy};
+            p = MsPlan{true, nw, R, gx, gy};
         }
     }
     return p;
@@ -503,6 +506,14 @@ int ms_partials_max(int W, int H) {
     return m;
 }
 
+template <typename TIn>
+hipError_t launch_rows(const MsPlan &p, const MsBatch &b, int n, int pitch, int W, int H, int next_pitch,
+                       float unit, const Taps &taps, hipStream_t stream, const KernelTimer &timer) {
+    const dim3 grid(p.gx, p.gy, n);
+    return launch_kernel(ms_level_rows<TIn, kRowsWaves>, grid, dim3(64 * kRowsWaves), stream, timer, b, pitch, W, H,
+                         next_pitch, unit, p.R, taps);
+}
+
 hipError_t launch_ms_level(const MsBatch &b, int n, InKind kind, int pitch, int W, int H, int next_pitch,
                            float unit, const Taps &taps, hipStream_t stream, const KernelTimer &timer) {
     if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
@@ -511,14 +522,11 @@ hipError_t launch_ms_level(const MsBatch &b, int n, InKind kind, int pitch, int 
     if (p.rows) {
         switch (kind) {
         case IN_F32:
-            return launch_kernel(ms_level_rows<float>, grid, dim3(kRowsThreads), stream, timer, b, pitch, W, H,
-                                 next_pitch, unit, p.R, taps);
+            return launch_rows<float>(p, b, n, pitch, W, H, next_pitch, unit, taps, stream, timer);
         case IN_U8:
-            return launch_kernel(ms_level_rows<uint8_t>, grid, dim3(kRowsThreads), stream, timer, b, pitch, W, H,
-                                 next_pitch, unit, p.R, taps);
+            return launch_rows<uint8_t>(p, b, n, pitch, W, H, next_pitch, unit, taps, stream, timer);
         case IN_U16:
-            return launch_kernel(ms_level_rows<uint16_t>, grid, dim3(kRowsThreads), stream, timer, b, pitch, W, H,
-                                 next_pitch, unit, p.R, taps);
+            return launch_rows<uint16_t>(p, b, n, pitch, W, H, next_pitch, unit, taps, stream, timer);
         default:
             return hipErrorInvalidValue;
         }
