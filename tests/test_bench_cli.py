@@ -72,3 +72,8 @@ def test_recorded_traffic_scales_per_frame_and_checks_the_sources(tmp_path, monk
 def test_cpu_model_names_the_host_cpu():
     m = bench.cpu_model()
     assert isinstance(m, str) and m
+
+
+def test_default_streams_per_metric():
+    assert bench.default_streams("float_ssim") == 1
+    assert bench.default_streams("ms_ssim") == 2

@@ -518,6 +518,9 @@ def test_full_msssim_workload_in_bench_launch_shape(torch_cuda):
     got = _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_MS_SSIM)
     single = [vqm.vqm_msssim_frame(r, d, src.bpc) for r, d in pairs]
     assert got == single
+    # two contexts on two streams, as bench.py times MS-SSIM
+    say("full MS-SSIM workload: two streams")
+    assert _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_MS_SSIM, n_streams=2) == single
     for t in (0, 23, n - 1):
         say(f"full MS-SSIM workload: oracle frame {t}")
         assert abs(got[t] - oracle.msssim(*pairs[t], src.bpc)) <= TOL, (t, got[t])
