@@ -112,14 +112,16 @@ def run_pass(ctxs, frameset, metric, batch, lag):
     return vqm.vqm_score_frames(ctxs, m, frameset, batch, lag).tolist()
 
 
-def default_streams(metric: str) -> int:
+def default_streams(metric: str, scale: int) -> int:
     """Contexts (each on its own stream) the timed stream rotates its batches
-    over.  float_ssim: one; a second one overlapping consecutive launches
-    measured slower (the steps contend for HBM and for the per-XCD layout).
-    MS-SSIM: two; a batch's small levels and its combine leave SIMDs idle,
-    which the other context's batch fills (19.4k -> 21.4k frames/s at
-    2160p)."""
-    return 2 if metric == "ms_ssim" else 1
+    over.  float_ssim with decimation: one; a second one overlapping
+    consecutive launches measured slower (the steps contend for HBM and for
+    the per-XCD layout: 2160p 164k -> 149k, 1080p 675k -> 634k, 853x481
+    919k -> 843k frames/s).  Work without an HBM-bound part takes two: the
+    compute-bound launches' tails (MS-SSIM's small levels and combine, the
+    scale-1 map's last tiles) leave SIMDs idle, which the other context's
+    batch fills (2160p MS-SSIM 19.4k -> 21.4k, 576x324 1.03M -> 1.15M)."""
+    return 2 if metric == "ms_ssim" or scale == 1 else 1
 
 
 def cpu_model() -> str:
@@ -306,7 +308,7 @@ def main():
     torch.cuda.synchronize()
 
     if args.streams <= 0:
-        args.streams = default_streams(wl.metric)
+        args.streams = default_streams(wl.metric, s)
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
     ctxs = [vqm.Context(0, st) for st in streams]
     lag = args.lag if args.lag > 0 else 3 * args.batch

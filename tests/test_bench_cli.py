@@ -74,6 +74,8 @@ def test_cpu_model_names_the_host_cpu():
     assert isinstance(m, str) and m
 
 
-def test_default_streams_per_metric():
-    assert bench.default_streams("float_ssim") == 1
-    assert bench.default_streams("ms_ssim") == 2
+def test_default_streams_per_path():
+    assert bench.default_streams("float_ssim", 8) == 1
+    assert bench.default_streams("float_ssim", 2) == 1
+    assert bench.default_streams("float_ssim", 1) == 2
+    assert bench.default_streams("ms_ssim", 1) == 2
