@@ -380,6 +380,17 @@ def test_msssim_score_does_not_depend_on_the_batch(ctx, w, h, bpc):
         s1, l1 = vqm.vqm_msssim_frame_lcs(*pairs[t], bpc)
         assert batched[t][0] == s1, t
         assert np.array_equal(batched[t][1], l1), t
+    # batches of 8, 13 and 11 frames take other strip heights (or the tile
+    # kernel) at some levels
+    say(f"msssim batch independence {w}x{h}: batches of 8, 13, 11")
+    i = 0
+    for m in (8, 13, 11):
+        ctx.vqm_msssim_submit_batch([r for r, _ in pairs[i:i + m]], [d for _, d in pairs[i:i + m]], bpc)
+        for t in range(i, i + m):
+            got = ctx.vqm_collect(want_lcs=True)
+            assert got[0] == batched[t][0], (m, t)
+            assert np.array_equal(got[1], batched[t][1]), (m, t)
+        i += m
     say(f"msssim batch independence {w}x{h}: oracle")
     assert abs(batched[7][0] - oracle.msssim(*pairs[7], bpc)) <= TOL
 
