@@ -60,18 +60,30 @@ struct DecPow2 {
         const int groups = (g.dec_w + Sh::CPT - 1) / Sh::CPT;  // groups holding outputs
         return (groups + 62) / 63;
     }
-    // A frame's waves are its (row, wave-in-row) units in row order, packed
-    // kDecWaves to a workgroup, so rows that need fewer waves than a
-    // workgroup has (1080p: 2) leave no wave idle.
+    // Units (row, wave-in-row) a wave takes in turn: two where a row needs
+    // at most two waves (1080p), so that fewer, longer decimation workgroups
+    // leave the interleaved map tiles more of the CUs (1080p step 43.0 ->
+    // 39.1 us per launch of 32 frames); one on wide rows, where the
+    // decimation is the HBM stream and a second unit per wave only delays it
+    // (2160p 179.8 -> 196.5 us).
+    __host__ __device__ static int units_per_wave(const StepGeometry &g) { return waves_per_row(g) <= 2 ? 2 : 1; }
+    // A frame's units in row order, units_per_wave to a wave and kDecWaves
+    // waves to a workgroup, so rows that need fewer waves than a workgroup
+    // has leave no wave idle.
     static int blocks_per_frame(const StepGeometry &g) {
-        return (waves_per_row(g) * g.dec_h + kDecWaves - 1) / kDecWaves;
+        const int upw = units_per_wave(g);
+        const int waves = (waves_per_row(g) * g.dec_h + upw - 1) / upw;
+        return (waves + kDecWaves - 1) / kDecWaves;
     }
     __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
-        const int wpr = waves_per_row(g);
-        const int u = b * kDecWaves + (int)(threadIdx.x >> 6);
-        if (u >= wpr * g.dec_h) return;  // the frame's last workgroup may be partly empty
-        const int Y = u / wpr;
-        dec::pow2_wave<T, S>(fr, u - Y * wpr, Y, g.w, g.h, g.dec_w, g.post, g.dec_pitch, g.packed != 0);
+        const int wpr = waves_per_row(g), upw = units_per_wave(g);
+        const int u0 = (b * kDecWaves + (int)(threadIdx.x >> 6)) * upw;
+#pragma unroll 1
+        for (int u = u0; u < u0 + upw; ++u) {
+            if (u >= wpr * g.dec_h) return;  // the frame's last workgroup may be partly empty
+            const int Y = u / wpr;
+            dec::pow2_wave<T, S>(fr, u - Y * wpr, Y, g.w, g.h, g.dec_w, g.post, g.dec_pitch, g.packed != 0);
+        }
     }
 };
 
