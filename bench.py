@@ -218,7 +218,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--reps", type=int, default=5,
+    ap.add_argument("--reps", type=int, default=7,
                     help="timed runs of K steps each; value is the median run's rate")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="workload number 1..5")
