@@ -459,7 +459,7 @@ __global__ __launch_bounds__(NT) void ms_finish(MsFinishBatch b, MsLevels lv) {
 // levels, pitch up to W + 63) always take the tile kernel.
 struct MsPlan {
     bool rows;
-    int nw, R, gx, gy;  // nw: waves per row-kernel workgroup (strips of 128 nw columns)
+    int R, gx, gy;  // strip height (row kernel) and grid
 };
 
 constexpr double kTileWaveInstr = 914.0, kRowsStepInstr = 330.0;
@@ -472,22 +472,21 @@ constexpr double kRowsTail = 0.1;
 
 MsPlan ms_plan(int W, int H, int n) {
     const int MW = W - 10, MH = H - 10;
-    MsPlan p{false, 0, 0, (MW + kTW - 1) / kTW, (MH + kTH - 1) / kTH};
+    MsPlan p{false, 0, (MW + kTW - 1) / kTW, (MH + kTH - 1) / kTH};
     if ((long long)(W + 64) * (long long)H * 4 >= (1ll << 31)) return p;
     double best = kTileWaveInstr * (kNT / 64) * (double)p.gx * (double)p.gy * n / kSimds;
     const long long slots = (long long)kRowsWavesPerSimd * kSimds;
-    const int nw = kRowsWaves;
-    const int gx = (MW + 128 * nw - 1) / (128 * nw);
+    const int gx = (MW + 128 * kRowsWaves - 1) / (128 * kRowsWaves);
     for (int strips = 1; strips <= MH / kRowsMinR; ++strips) {
         int R = (MH + strips - 1) / strips;
         R += R & 1;
         const int gy = (MH + R - 1) / R;
-        const long long waves = (long long)nw * gx * gy * n;
+        const long long waves = (long long)kRowsWaves * gx * gy * n;
         const double rounds = (double)((waves + slots - 1) / slots) + kRowsTail;
         const double cost = rounds * kRowsWavesPerSimd * (R + 10) * kRowsStepInstr;
         if (cost < best) {
             best = cost;
-            p = MsPlan{true, nw, R, gx, gy};
+            p = MsPlan{true, R, gx, gy};
         }
     }
     return p;
