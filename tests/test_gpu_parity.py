@@ -344,9 +344,10 @@ def test_msssim_pyramid_bit_exact(ctx, w, h, bpc):
 
 
 # Sizes and batches that take the row-streaming level kernel at levels 1-2
-# (strips of 256 columns with a ragged last one, odd plane sizes, several
-# strip rows); a batch of one frame takes the tile kernel.
-ROWS_CASES = [(2001, 1203, 16), (1921, 1081, 8), (1283, 767, 12)]
+# (strips of 128 columns with a ragged last one, down to a single valid
+# column at 1931 wide; odd plane sizes; several strip rows); a batch of one
+# frame takes the tile kernel.
+ROWS_CASES = [(2001, 1203, 16), (1921, 1081, 8), (1283, 767, 12), (1931, 1087, 10)]
 
 
 @pytest.mark.parametrize("w,h,bpc", ROWS_CASES)
