@@ -157,7 +157,7 @@ def cpu_baseline(host, wl, budget_s: float):
 
 # Frames the all-cores baseline's worker processes read (inherited through
 # fork, never pickled).
-_BASELINE_FRAMES = None
+_ORACLE_TIMING_FRAMES = None
 
 
 def _oracle_worker(args):
@@ -165,7 +165,7 @@ def _oracle_worker(args):
     frames i, i + P, ... (cycling) for about `budget_s` seconds."""
     metric, bpc, i, p, budget_s = args
     import oracle
-    host = _BASELINE_FRAMES
+    host = _ORACLE_TIMING_FRAMES
     fn = oracle.msssim if metric == "ms_ssim" else oracle.ssim
     n, k = 0, i
     t0 = time.perf_counter()
@@ -182,13 +182,13 @@ def cpu_baseline_all_cores(host, wl, budget_s: float, cores: int):
     frames; frames/s summed over the processes.  Forks: call it before the
     GPU is touched."""
     import multiprocessing as mp
-    global _BASELINE_FRAMES
-    _BASELINE_FRAMES = host
+    global _ORACLE_TIMING_FRAMES
+    _ORACLE_TIMING_FRAMES = host
     try:
         with mp.get_context("fork").Pool(cores) as pool:
             res = pool.map(_oracle_worker, [(wl.metric, wl.bpc, i, cores, budget_s) for i in range(cores)])
     finally:
-        _BASELINE_FRAMES = None
+        _ORACLE_TIMING_FRAMES = None
     n = sum(r[0] for r in res)
     el = max(r[1] for r in res)
     return {"value": round(n / el, 3), "unit": "frames/s", "cores": cores, "kind": "oracle",
