@@ -79,3 +79,13 @@ def test_default_streams_per_path():
     assert bench.default_streams("float_ssim", 2) == 1
     assert bench.default_streams("float_ssim", 1) == 2
     assert bench.default_streams("ms_ssim", 1) == 2
+
+
+def test_cpu_baselines_time_the_oracle():
+    from full_reference_video_amd import synth
+    wl = synth.WORKLOADS[1]
+    host = [synth.FrameSource(1).pair(0)]
+    for res, cores in ((bench.cpu_baseline(host, wl, 0.3), 1), (bench.cpu_baseline_all_cores(host, wl, 0.3, 2), 2)):
+        assert res["kind"] == "oracle" and res["unit"] == "frames/s"
+        assert res["cores"] == cores and res["value"] > 0
+        assert bench.cpu_model() in res["sample"]
