@@ -241,22 +241,33 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
                                                                           kRsrcWord3);
     const int row_bytes = pitch * (int)sizeof(TIn);
     const int voA = min(x0 + c, W - 1) * (int)sizeof(TIn), voB = min(x0 + c + 1, W - 1) * (int)sizeof(TIn);
-    const int hvoA = min(x0 + S + c, W - 1) * (int)sizeof(TIn);
-    const int hvoB = min(x0 + S + c + 1, W - 1) * (int)sizeof(TIn);
-    const bool wave0 = tid < 64, halo = tid < 5;
+    // The ten columns past the strip, for two rows at once: threads 0-4 take
+    // the even row t of a pair, threads 5-9 the odd row t + 1, two columns
+    // each, so the pass runs every other row.  (One wave: a row's buffer is
+    // written one step early, after the wave has read the row it held.)
+    static_assert(NW == 1, "the paired halo rows need a one-wave workgroup");
+    const int hl = tid % 5, hr = tid < 10 ? tid / 5 : 0;
+    const bool halo = tid < 10;
+    const int hc = S + 2 * hl;  // strip-local first column of the halo thread's pair
+    const int hvoA = min(x0 + hc, W - 1) * (int)sizeof(TIn);
+    const int hvoB = min(x0 + hc + 1, W - 1) * (int)sizeof(TIn);
 
-    auto load_row = [&](int t, RowPair &m, RowPair &h) __attribute__((always_inline)) {
+    auto load_row = [&](int t, RowPair &m) __attribute__((always_inline)) {
         const int so = (y0 + t) * row_bytes;
         m.ra = Raw::load(rref, voA, so);
         m.rb = Raw::load(rref, voB, so);
         m.da = Raw::load(rdis, voA, so);
         m.db = Raw::load(rdis, voB, so);
-        if (wave0) {
-            h.ra = Raw::load(rref, hvoA, so);
-            h.rb = Raw::load(rref, hvoB, so);
-            h.da = Raw::load(rdis, hvoA, so);
-            h.db = Raw::load(rdis, hvoB, so);
-        }
+    };
+    // Halo samples of the row pair (t, t + 1), t even; without a row t + 1
+    // the odd threads read row t again (and their values go unused).
+    auto load_halo = [&](int t, RowPair &h) __attribute__((always_inline)) {
+        const int so = (y0 + t) * row_bytes;
+        const int dr = (hr != 0 && t + 1 < in_rows) ? row_bytes : 0;
+        h.ra = Raw::load(rref, hvoA + dr, so);
+        h.rb = Raw::load(rref, hvoB + dr, so);
+        h.da = Raw::load(rdis, hvoA + dr, so);
+        h.db = Raw::load(rdis, hvoB + dr, so);
     };
 
     // Next level: this thread's 2x2 block column, and (last strip only) the
@@ -264,8 +275,8 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
     float *const nref = fr.next_ref;
     const bool has_next = nref != nullptr;
     const int nW = W / 2, nH = H / 2;
-    const int nbx = (x0 + c) / 2, hnbx = (x0 + S + c) / 2;
-    const bool own_x = nbx < nW, hown_x = last_x && halo && hnbx < nW;
+    const int nbx = (x0 + c) / 2, hnbx = (x0 + hc) / 2;
+    const bool own_x = nbx < nW, hown_x = last_x && tid < 5 && hnbx < nW;
     // (At the last level there is no next plane: the resources then cover
     // nothing and no store is issued.)
     const int nbytes_next = has_next ? next_pitch * nH * 4 : 0;
@@ -281,10 +292,11 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
     const bool vA = x0 + c < MW, vB = x0 + c + 1 < MW;
     LcsAcc acc;  // at most 22 pixels (one group of rows) in 32-bit integers
     double DL = 0.0, DC = 0.0, PS = 0.0;
-    float psx = 0.0f, psy = 0.0f, hpsx = 0.0f, hpsy = 0.0f;  // the previous row's pair sums
+    float psx = 0.0f, psy = 0.0f;  // the previous row's pair sums
 
     RowPair nm{}, nh{};
-    load_row(0, nm, nh);
+    load_row(0, nm);
+    load_halo(0, nh);
     for (int t0 = 0; t0 < in_rows; t0 += 11) {
         static_steps(std::make_integer_sequence<int, 11>{}, [&](auto uc) __attribute__((always_inline)) {
             constexpr int u = decltype(uc)::value;
@@ -314,28 +326,39 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
             }
             psx = sx;
             psy = sy;
-            if (halo) {
-                const float hxa = fmaf(Raw::value(nh.ra), unit, -kMomentOffset);
-                const float hxb = fmaf(Raw::value(nh.rb), unit, -kMomentOffset);
-                const float hya = fmaf(Raw::value(nh.da), unit, -kMomentOffset);
-                const float hyb = fmaf(Raw::value(nh.db), unit, -kMomentOffset);
-                float *hb = buf + S + c;
-                *reinterpret_cast<float2 *>(hb + 0 * P) = make_float2(hxa, hxb);
-                *reinterpret_cast<float2 *>(hb + 1 * P) = make_float2(hya, hyb);
-                *reinterpret_cast<float2 *>(hb + 2 * P) = make_float2(hxa * hxa, hxb * hxb);
-                *reinterpret_cast<float2 *>(hb + 3 * P) = make_float2(hya * hya, hyb * hyb);
-                *reinterpret_cast<float2 *>(hb + 4 * P) = make_float2(hxa * hya, hxb * hyb);
-                const float hsx = hxa + hxb, hsy = hya + hyb;
-                if (block_row && hown_x) {
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        __builtin_bit_cast(uint32_t, fmaf(hpsx + hsx, 0.25f, kMomentOffset)), nr, hnbx * 4, so_next, 0);
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        __builtin_bit_cast(uint32_t, fmaf(hpsy + hsy, 0.25f, kMomentOffset)), nd, hnbx * 4, so_next, 0);
+            if ((t & 1) == 0) {
+                // Row t + 1's halo goes into the buffer the previous row was
+                // read from: those reads come first.
+                __syncthreads();
+                if (halo) {
+                    const float hxa = fmaf(Raw::value(nh.ra), unit, -kMomentOffset);
+                    const float hxb = fmaf(Raw::value(nh.rb), unit, -kMomentOffset);
+                    const float hya = fmaf(Raw::value(nh.da), unit, -kMomentOffset);
+                    const float hyb = fmaf(Raw::value(nh.db), unit, -kMomentOffset);
+                    float *hb = lds + ((t + hr) & 1) * 5 * P;  // row t, or row t + 1's buffer
+                    *reinterpret_cast<float2 *>(hb + 0 * P + hc) = make_float2(hxa, hxb);
+                    *reinterpret_cast<float2 *>(hb + 1 * P + hc) = make_float2(hya, hyb);
+                    *reinterpret_cast<float2 *>(hb + 2 * P + hc) = make_float2(hxa * hxa, hxb * hxb);
+                    *reinterpret_cast<float2 *>(hb + 3 * P + hc) = make_float2(hya * hya, hyb * hyb);
+                    *reinterpret_cast<float2 *>(hb + 4 * P + hc) = make_float2(hxa * hya, hxb * hyb);
+                    // Next level: the block row (t, t + 1) of the halo
+                    // columns, the odd row's pair sums from thread + 5.
+                    const float hsx = hxa + hxb, hsy = hya + hyb;
+                    const float osx = __builtin_bit_cast(
+                        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hsx), 0x105, 0xF, 0xF, false));
+                    const float osy = __builtin_bit_cast(
+                        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hsy), 0x105, 0xF, 0xF, false));
+                    if (has_next && hown_x && (t < R || last_y) && t + 1 < in_rows) {
+                        const int so_h = ((y0 + t) / 2) * next_pitch * 4;
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __builtin_bit_cast(uint32_t, fmaf(hsx + osx, 0.25f, kMomentOffset)), nr, hnbx * 4, so_h, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __builtin_bit_cast(uint32_t, fmaf(hsy + osy, 0.25f, kMomentOffset)), nd, hnbx * 4, so_h, 0);
+                    }
                 }
-                hpsx = hsx;
-                hpsy = hsy;
+                if (t + 2 < in_rows) load_halo(t + 2, nh);
             }
-            if (t + 1 < in_rows) load_row(t + 1, nm, nh);
+            if (t + 1 < in_rows) load_row(t + 1, nm);
 
             __syncthreads();  // the row is in the buffer
 
