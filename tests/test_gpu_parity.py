@@ -396,6 +396,28 @@ def test_msssim_score_does_not_depend_on_the_batch(ctx, w, h, bpc):
     assert abs(batched[7][0] - oracle.msssim(*pairs[7], bpc)) <= TOL
 
 
+def test_msssim_anti_correlated_is_nan(ctx):
+    # Inverted planes: the fine levels' mean structure is negative, so the
+    # score is NaN (the oracle's pin), alone (tile kernel) and in a full batch
+    # (the row kernel at levels 1-2); the level means still match the oracle.
+    rng = np.random.default_rng(9)
+    ref = rng.integers(0, 256, size=(192, 192)).astype(np.uint8)
+    say("msssim anti-correlated 192x192")
+    assert np.isnan(vqm.vqm_msssim_frame(ref, 255 - ref, 8))
+    ref = rng.integers(0, 256, size=(1081, 1921)).astype(np.uint8)
+    dis = (255 - ref).astype(np.uint8)
+    n = vqm.VQM_MAX_BATCH
+    say("msssim anti-correlated 1921x1081, full batch")
+    ctx.vqm_msssim_submit_batch([ref] * n, [dis] * n, 8)
+    got = [ctx.vqm_collect(want_lcs=True) for _ in range(n)]
+    want, want_lcs = oracle.msssim(ref, dis, 8, want_lcs=True)
+    assert np.isnan(want)
+    for score, lcs in got:
+        assert np.isnan(score)
+        assert np.all(np.abs(lcs - want_lcs) <= TOL)
+        assert lcs[10] < 0
+
+
 def test_msssim_identity(ctx):
     src = synth.FrameSource(5, w=960, h=540)
     ref, _ = src.pair(0)
