@@ -66,6 +66,8 @@ def lib():
         L.vqm_oracle_plane_dims.restype = ip
         L.vqm_oracle_db.argtypes = [ctypes.c_double]
         L.vqm_oracle_db.restype = ctypes.c_double
+        L.vqm_oracle_msssim_combine.argtypes = [dp]
+        L.vqm_oracle_msssim_combine.restype = ctypes.c_double
         for name in ("vqm_oracle_sample_plane", "vqm_oracle_decimate", "vqm_oracle_ssim_planes",
                      "vqm_oracle_ssim", "vqm_oracle_msssim_level_maps", "vqm_oracle_downsample",
                      "vqm_oracle_msssim"):
@@ -177,6 +179,14 @@ def msssim(ref: np.ndarray, dis: np.ndarray, bpc: int, want_lcs: bool = False):
     _check(lib().vqm_oracle_msssim(_ptr(ref), _ptr(dis), w, h, bpc, ctypes.byref(score),
                                    _ptr(lcs)), "msssim")
     return (score.value, lcs) if want_lcs else score.value
+
+
+def msssim_combine(lcs) -> float:
+    """MS-SSIM of 15 level means L_1..L_5, C_1..C_5, S_1..S_5 (the oracle's combine)."""
+    a = np.ascontiguousarray(lcs, np.float64)
+    if a.shape != (15,):
+        raise ValueError(f"15 level means expected, got shape {a.shape}")
+    return lib().vqm_oracle_msssim_combine(_ptr(a))
 
 
 def msssim_rc(ref: np.ndarray, dis: np.ndarray, w: int, h: int, bpc: int) -> int:

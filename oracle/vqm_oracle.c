@@ -278,6 +278,18 @@ static double mean_of(const double *v, size_t n)
     return t / (double)n;
 }
 
+double vqm_oracle_msssim_combine(const double lcs[15])
+{
+    const double *L = lcs, *C = lcs + 5, *S = lcs + 10;
+    double msv = pow(L[4], MS_EXPONENT[4]);
+    for (int j = 0; j < 5; j++) {
+        if (!(C[j] > 0.0) || !(S[j] > 0.0))
+            return NAN;
+        msv *= pow(C[j], MS_EXPONENT[j]) * pow(S[j], MS_EXPONENT[j]);
+    }
+    return msv;
+}
+
 int vqm_oracle_msssim(const void *ref, const void *dis, int w, int h, int bpc,
                       double *score, double *lcs)
 {
@@ -322,21 +334,16 @@ int vqm_oracle_msssim(const void *ref, const void *dis, int w, int h, int bpc,
         }
     }
 
-    double msv = pow(L[4], MS_EXPONENT[4]);
+    double means[15];
     for (int j = 0; j < 5; j++) {
-        if (!(C[j] > 0.0) || !(S[j] > 0.0)) {
-            msv = NAN;
-            break;
-        }
-        msv *= pow(C[j], MS_EXPONENT[j]) * pow(S[j], MS_EXPONENT[j]);
+        means[j] = L[j];
+        means[5 + j] = C[j];
+        means[10 + j] = S[j];
     }
-    *score = msv;
+    *score = vqm_oracle_msssim_combine(means);
     if (lcs) {
-        for (int j = 0; j < 5; j++) {
-            lcs[j] = L[j];
-            lcs[5 + j] = C[j];
-            lcs[10 + j] = S[j];
-        }
+        for (int k = 0; k < 15; k++)
+            lcs[k] = means[k];
     }
 done:
     free(xr);

@@ -39,6 +39,9 @@
  *                       under 2x2 averaging (isolates level 1 and its
  *                       exponent), and a pixel-replicated frame whose levels
  *                       2..5 equal the original's levels 1..4.
+ *   ms combine        — each exponent on its own: means of 1 except
+ *                       C_j = S_j = 1/2 give 4^-b_j, L_5 = 1/2 gives 2^-b5,
+ *                       against the five weights of the published MS-SSIM.
  *   db                — 10, 20, 30 dB at 1 - ssim = 1e-1, 1e-2, 1e-3; the
  *                       ADR's sensitivity 4.34 / (1 - ssim) as a finite
  *                       difference, and its 0.018 dB at 30 dB example.
@@ -99,6 +102,15 @@ int vqm_oracle_msssim_level_maps(const float *ref, const float *dis, int w, int 
 
 /* 2x2 mean in fp32, ((a + b) + (c + d)) * 0.25f, output floor(w/2) x floor(h/2). */
 int vqm_oracle_downsample(const float *in, int w, int h, float *out);
+
+/* The MS-SSIM combine of 15 level means (L_1..L_5, C_1..C_5, S_1..S_5):
+ *   MS = L5^b5 * prod_{j=1..5} C_j^b_j * S_j^b_j,
+ *   b = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333}
+ * (reading: the five weights of the published multi-scale SSIM, Wang,
+ * Simoncelli and Bovik 2003, which the MS-SSIM workload states; luminance
+ * enters at the coarsest level only).  NaN when any C_j or S_j is <= 0
+ * (reading: the power of a non-positive mean is not defined). */
+double vqm_oracle_msssim_combine(const double lcs[15]);
 
 /* 5-scale MS-SSIM at full resolution (no decimation first):
  *   MS = L5^b5 * prod_{j=1..5} C_j^b_j * S_j^b_j,

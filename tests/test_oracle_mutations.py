@@ -28,6 +28,10 @@ MUTANTS = {
     "c3_equals_c2": ("const double c3 = SSIM_C2 / 2.0;", "const double c3 = SSIM_C2;"),
     "exponents_reversed": ("{0.0448, 0.2856, 0.3001, 0.2363, 0.1333}",
                            "{0.1333, 0.2363, 0.3001, 0.2856, 0.0448}"),
+    "exponents_b2_b4_swapped": ("{0.0448, 0.2856, 0.3001, 0.2363, 0.1333}",
+                                "{0.0448, 0.2363, 0.3001, 0.2856, 0.1333}"),
+    "exponent_b3_misread": ("{0.0448, 0.2856, 0.3001, 0.2363, 0.1333}",
+                            "{0.0448, 0.2856, 0.3010, 0.2363, 0.1333}"),
     "luminance_every_level": ("msv *= pow(C[j], MS_EXPONENT[j]) * pow(S[j], MS_EXPONENT[j]);",
                               "msv *= pow(L[j], MS_EXPONENT[j]) * pow(C[j], MS_EXPONENT[j]) * pow(S[j], MS_EXPONENT[j]);"),
     "downsample_drops_sample": ("((a + b) + (c + d)) * 0.25f", "((a + b) + (c + c)) * 0.25f"),

@@ -28,7 +28,8 @@ with open(os.path.join(GOLDEN, "page_facts.json")) as f:
 
 C1 = (0.01 * 255) ** 2
 C2 = (0.03 * 255) ** 2
-MS_BETA = [0.0448, 0.2856, 0.3001, 0.2363, 0.1333]
+# The five MS-SSIM weights as the workload and the published method state them.
+MS_BETA = [float(b) for b in FACTS["msssim_exponents"]["beta"]]
 
 
 # ---------------------------------------------------------------- scale, tap
@@ -403,6 +404,64 @@ def test_msssim_checkerboard_isolates_level_one():
     l1, c1, s1 = oracle.msssim_level_maps(x, y)
     want = (c1.mean() * s1.mean()) ** MS_BETA[0]
     assert abs(score - want) < 1e-12
+
+
+@pytest.mark.parametrize("j", range(5))
+def test_msssim_combine_isolates_each_exponent(j):
+    # Means of 1 everywhere except C_j = S_j = 1/2: every other factor is
+    # exactly 1, so the score is (1/4)^b_j and names b_j alone.
+    lcs = np.ones(15)
+    lcs[5 + j] = 0.5
+    lcs[10 + j] = 0.5
+    want = 0.25 ** MS_BETA[j]
+    assert abs(oracle.msssim_combine(lcs) - want) < 1e-15
+    # contrast and structure enter with the same exponent, each on its own
+    lcs[10 + j] = 1.0
+    assert abs(oracle.msssim_combine(lcs) - 0.5 ** MS_BETA[j]) < 1e-15
+    lcs[5 + j], lcs[10 + j] = 1.0, 0.5
+    assert abs(oracle.msssim_combine(lcs) - 0.5 ** MS_BETA[j]) < 1e-15
+
+
+def test_msssim_combine_luminance_at_level_five_only():
+    for j in range(4):
+        lcs = np.ones(15)
+        lcs[j] = 0.5
+        assert oracle.msssim_combine(lcs) == 1.0
+    lcs = np.ones(15)
+    lcs[4] = 0.5
+    assert abs(oracle.msssim_combine(lcs) - 0.5 ** MS_BETA[4]) < 1e-15
+
+
+def test_msssim_combine_generic_means():
+    # Distinct means at every level: the product of the published weights'
+    # powers, evaluated here in exact-enough fp64 from the fixture's values.
+    rng = np.random.default_rng(11)
+    lcs = rng.uniform(0.3, 0.99, 15)
+    L, C, S = lcs[:5], lcs[5:10], lcs[10:]
+    want = L[4] ** MS_BETA[4] * math.prod((C[j] * S[j]) ** MS_BETA[j] for j in range(5))
+    assert abs(oracle.msssim_combine(lcs) - want) < 1e-14
+
+
+@pytest.mark.parametrize("k", list(range(5, 15)))
+def test_msssim_combine_nonpositive_mean_is_nan(k):
+    lcs = np.full(15, 0.9)
+    lcs[k] = 0.0
+    assert math.isnan(oracle.msssim_combine(lcs))
+    lcs[k] = -0.25
+    assert math.isnan(oracle.msssim_combine(lcs))
+
+
+def test_msssim_score_is_the_combine_of_its_level_means():
+    # On a frame whose C_j and S_j differ from 1 at every level, the score the
+    # full path returns is the fixture's weighted product of its own means.
+    src = synth.FrameSource(5, w=256, h=208)
+    ref, dis = src.pair(1)
+    score, lcs = oracle.msssim(ref, dis, 8, want_lcs=True)
+    L, C, S = lcs[:5], lcs[5:10], lcs[10:]
+    # a misplaced exponent moves the score by about |d_beta * log C_j| >> 1e-14
+    assert np.all(np.abs(C - 1) > 1e-6) and np.all(np.abs(S - 1) > 1e-6)
+    want = L[4] ** MS_BETA[4] * math.prod((C[j] * S[j]) ** MS_BETA[j] for j in range(5))
+    assert abs(score - want) < 1e-14
 
 
 def test_msssim_pixel_replication_shifts_levels():
