@@ -462,7 +462,8 @@ __global__ __launch_bounds__(NT) void ms_finish(MsFinishBatch b, MsLevels lv) {
         ms *= pw[1 + j] * pw[6 + j];
     }
     fr.result[0] = ms;
-    for (int j = 0; j < 15; ++j) fr.result[1 + j] = lcs[j];
+    if ((b.lcs_mask >> blockIdx.x) & 1u)
+        for (int j = 0; j < 15; ++j) fr.result[1 + j] = lcs[j];
     __threadfence_system();
 }
 

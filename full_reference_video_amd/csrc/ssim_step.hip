@@ -162,7 +162,9 @@ __device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const St
     if (threadIdx.x == 0) fr.partials[tile] = acc[0];
 }
 
-__device__ __forceinline__ void finish_frame(const SsimFrame &fr, const StepGeometry &g) {
+// The frame's score goes to result[0]; result[1] receives the decibel form
+// only when the caller asked for it, so the read-back is 8 bytes otherwise.
+__device__ __forceinline__ void finish_frame(const SsimFrame &fr, const StepGeometry &g, bool want_db) {
     __shared__ double red[1][kNT / 64];
     double tot[1];
     sum_spans<kNT, 1>(fr.partials, tiles_x(g) * tiles_y(g), 0, tot, red);
@@ -172,7 +174,7 @@ __device__ __forceinline__ void finish_frame(const SsimFrame &fr, const StepGeom
         // The decibel form -10 log10(1 - ssim), +inf for a score of 1 or
         // more ("ADR-1405: float_ssim_hip decimates on the device,
         // bit-identical to the CPU", Consequences: enable_db).
-        fr.result[1] = m < 1.0 ? -10.0 * log10(1.0 - m) : (m >= 1.0 ? __builtin_inf() : m);
+        if (want_db) fr.result[1] = m < 1.0 ? -10.0 * log10(1.0 - m) : (m >= 1.0 ? __builtin_inf() : m);
         __threadfence_system();
     }
 }
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
         }
         q -= MD;
         const int fi = x * lay.fin_per_xcd + q;
-        if (fi < r.n_fin) finish_frame(r.fin.f[fi], g);
+        if (fi < r.n_fin) finish_frame(r.fin.f[fi], g, (r.fin_db_mask >> fi) & 1u);
         return;
     }
     if (q < lay.map_wg) {
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
     }
     q -= lay.dec_per_xcd;
     const int fi = x * lay.fin_per_xcd + q;
-    if (fi < r.n_fin) finish_frame(r.fin.f[fi], g);
+    if (fi < r.n_fin) finish_frame(r.fin.f[fi], g, (r.fin_db_mask >> fi) & 1u);
 }
 
 template <class Dec, typename TIn>

@@ -61,7 +61,8 @@ struct DecimateBatch {
 struct SsimFrame {
     const void *ref, *dis;       // map input planes (decimated fp32, or raw at scale 1)
     double *partials;            // >= ssim_partials(dec_w, dec_h) doubles
-    double *result;              // device-visible address of [score, dB] (pinned host)
+    double *result;              // device-visible address of the score (and the dB form after it
+                                 // when asked for; pinned host memory or device memory)
 };
 struct SsimBatch {
     SsimFrame f[kMaxBatch];
@@ -101,6 +102,7 @@ struct StepRoles {
     int n_map;
     SsimBatch fin;               // only partials and result are used
     int n_fin;
+    unsigned fin_db_mask;        // bit i: finish frame i also writes its decibel form to result[1]
 };
 
 // A step launch passes StepRoles by value with a few small structs beside
@@ -144,10 +146,11 @@ hipError_t launch_ms_level(const MsBatch &b, int n, InKind kind, int pitch, int 
 
 struct MsFinishFrame {
     const double *partials;      // base of the frame's partials (all levels)
-    double *result;              // score + 15 means, device-visible pinned host
+    double *result;              // score (+ 15 means when asked for), device-visible pinned host
 };
 struct MsFinishBatch {
     MsFinishFrame f[kMaxBatch];
+    unsigned lcs_mask;           // bit i: frame i also writes its 15 level means to result[1..15]
 };
 // Where each level's spans sit in a frame's partials.
 struct MsLevels {

@@ -165,6 +165,7 @@ struct Slot {
     bool ready = false;             // scratch allocated for geo
     struct BatchEvent *batch = nullptr;  // completion of the batch this frame rode in
     int kind = KIND_NONE;
+    bool extra = false;             // the finish also writes the dB form / the 15 level means
 
     // offsets (in floats) of the planes inside `planes`
     size_t off_ref[kLevels] = {}, off_dis[kLevels] = {};
@@ -511,7 +512,10 @@ int step(vqm_ctx *ctx, PendingBatch *fresh) {
     }
     if (to_finish) {
         r.n_fin = to_finish->n;
-        for (int i = 0; i < to_finish->n; ++i) fill_map_frame(r.fin.f[i], *to_finish, i, decimating);
+        for (int i = 0; i < to_finish->n; ++i) {
+            fill_map_frame(r.fin.f[i], *to_finish, i, decimating);
+            if (to_finish->sl[i]->extra) r.fin_db_mask |= 1u << i;
+        }
     }
     const vqm::StepGeometry sg = step_geometry(g);
     // The map reads the decimated planes (uint16 window sums scaled by post,
@@ -577,6 +581,7 @@ int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r
     for (int i = 0; i < n; ++i) {
         fb.f[i].partials = sl[i]->partials;
         fb.f[i].result = sl[i]->result_dev;
+        if (sl[i]->extra) fb.lcs_mask |= 1u << i;
     }
     vqm::MsLevels lv;
     for (int j = 0; j < kLevels; ++j) {
@@ -595,9 +600,11 @@ int gate(int kind, int w, int h, int bpc) {
 
 // Enqueue n frames of one geometry as one batch: every frame gets the next
 // free slot, its own upload, result and completion event; the kernels
-// process the whole batch per launch.
+// process the whole batch per launch.  `extra`: the finish also writes the
+// dB form (float_ssim) or the 15 level means (MS-SSIM) beside the score;
+// without it the read-back is the 8-byte score alone.
 int submit(vqm_ctx *ctx, int kind, const void *const *refs, const void *const *diss, int n, int w, int h,
-           int bpc) {
+           int bpc, bool extra) {
     if (!ctx) return fail(-EINVAL, "NULL context");
     if (!refs || !diss) return fail(-EINVAL, "NULL plane array");
     if (n < 1 || n > VQM_MAX_BATCH) return fail(-EINVAL, "batch of %d frames outside 1..%d", n, VQM_MAX_BATCH);
@@ -626,6 +633,7 @@ int submit(vqm_ctx *ctx, int kind, const void *const *refs, const void *const *d
         for (int k = 0; k < 16; ++k) p.sl[i]->result_host[k] = NAN;
         p.sl[i]->batch = nullptr;
         p.sl[i]->kind = kind;
+        p.sl[i]->extra = extra;
         rc = upload(ctx, *p.sl[i], refs[i], diss[i], &p.in_r[i], &p.in_d[i]);
         if (rc) return rc;
     }
@@ -669,12 +677,18 @@ int collect(vqm_ctx *ctx, double *score, double *lcs, double *db) {
     be->refs -= 1;
     sl.batch = nullptr;
     *score = sl.result_host[0];
+    // Without `extra` the finish wrote the score alone; the rest of the block
+    // still holds the NaN the submit put there.
     if (lcs && sl.kind == KIND_MSSSIM) memcpy(lcs, sl.result_host + 1, 15 * sizeof(double));
     if (db) *db = sl.kind == KIND_SSIM ? sl.result_host[1] : NAN;
     return 0;
 }
 
-int create(int device, void *stream, vqm_ctx **out) {
+// A context on `device`, enqueuing on `stream`, or on a stream of its own
+// when `stream` is NULL: a blocking stream (ordered after work on the legacy
+// default stream, where torch's default stream enqueues) unless
+// `own_nonblocking`.
+int create(int device, void *stream, vqm_ctx **out, bool own_nonblocking = false) {
     if (!out) return fail(-EINVAL, "NULL output pointer");
     int n = 0;
     hipError_t e = hipGetDeviceCount(&n);
@@ -695,7 +709,7 @@ int create(int device, void *stream, vqm_ctx **out) {
             return fail(-EINVAL, "stream belongs to device %d, context is on %d", sdev, device);
         (void)hipGetLastError();
     } else {
-        HIP_TRY(hipStreamCreateWithFlags(&ctx->stream, hipStreamNonBlocking));
+        HIP_TRY(hipStreamCreateWithFlags(&ctx->stream, own_nonblocking ? hipStreamNonBlocking : hipStreamDefault));
         ctx->own_stream = true;
     }
     *out = ctx.release();
@@ -779,7 +793,7 @@ int blocking(int kind, const void *ref, const void *dis, int w, int h, int bpc, 
     rc = lease_ctx(lease);
     if (rc) return rc;
     vqm_ctx *ctx = lease.ctx;
-    rc = submit(ctx, kind, &ref, &dis, 1, w, h, bpc);
+    rc = submit(ctx, kind, &ref, &dis, 1, w, h, bpc, lcs != nullptr || db != nullptr);
     if (rc) return rc;
     double s = 0.0, d = 0.0;
     double l[15];
@@ -840,8 +854,9 @@ int frame_yuv(int kind, const void *const *ref, const void *const *dis, int w, i
     int rc = lease_ctx(lease);
     if (rc) return rc;
     vqm_ctx *ctx = lease.ctx;
-    rc = submit(ctx, kind, ref, dis, 1, pw[0], ph[0], bpc);
-    if (rc == 0) rc = submit(ctx, kind, ref + 1, dis + 1, 2, pw[1], ph[1], bpc);
+    const bool extra = lcs != nullptr || db != nullptr;
+    rc = submit(ctx, kind, ref, dis, 1, pw[0], ph[0], bpc, extra);
+    if (rc == 0) rc = submit(ctx, kind, ref + 1, dis + 1, 2, pw[1], ph[1], bpc, extra);
     if (rc == 0) rc = wait_all(ctx);
     // Collect whatever was enqueued, so the leased context goes back empty.
     double s[3] = {0.0, 0.0, 0.0}, l[3][15], d[3];
@@ -891,7 +906,7 @@ int score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *
         // room in the target context (collecting the oldest frames first)
         while (rc == 0 && front < fifo.size() && ctxs[c]->count + m > VQM_MAX_IN_FLIGHT) rc = collect_one();
         if (rc) break;
-        rc = submit(ctxs[c], kind, refs + b0, diss + b0, m, w, h, bpc);
+        rc = submit(ctxs[c], kind, refs + b0, diss + b0, m, w, h, bpc, lcs != nullptr || db != nullptr);
         if (rc) break;
         for (int i = 0; i < m; ++i) fifo.emplace_back(c, b0 + i);
         // frames with `lag` later frames submitted are due
@@ -954,6 +969,7 @@ int record_pass(vqm_graph *g, const void *const *refs, const void *const *dis, i
         int rc = prepare_slot(ctx->slots[i], geo);
         if (rc) return rc;
         for (int k = 0; k < 16; ++k) ctx->slots[i].result_host[k] = NAN;
+        ctx->slots[i].extra = true;  // a replay's collect may ask for every output
     }
     HIP_TRY(hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal));
     ctx->capturing = true;
@@ -1018,7 +1034,7 @@ int graph_create(int device, void *stream, int metric, const void *const *refs, 
     std::unique_ptr<vqm_graph, void (*)(vqm_graph *)> g(new vqm_graph(), destroy_graph);
     g->kind = kind;
     g->n = n;
-    rc = create(device, stream, &g->ctx);
+    rc = create(device, stream, &g->ctx, /*own_nonblocking=*/true);
     if (rc) return rc;
     for (int i = 0; i < n; ++i)
         for (const void *p : {refs[i], dis[i]}) {
@@ -1066,6 +1082,7 @@ int graph_collect(vqm_graph *g, double *scores, double *lcs, double *db) {
 extern "C" {
 
 int vqm_abi_version(void) { return VQM_ABI_VERSION; }
+
 
 int vqm_graph_create(int device, void *hip_stream, int metric, const void *const *refs, const void *const *dis,
                      int n, int w, int h, int bpc, int batch, vqm_graph **out) {
@@ -1139,24 +1156,24 @@ void vqm_ctx_destroy(vqm_ctx *ctx) {
 
 int vqm_ssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc) {
     DeviceScope scope;
-    return submit(ctx, KIND_SSIM, &ref, &dis, 1, w, h, bpc);
+    return submit(ctx, KIND_SSIM, &ref, &dis, 1, w, h, bpc, true);
 }
 
 int vqm_msssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc) {
     DeviceScope scope;
-    return submit(ctx, KIND_MSSSIM, &ref, &dis, 1, w, h, bpc);
+    return submit(ctx, KIND_MSSSIM, &ref, &dis, 1, w, h, bpc, true);
 }
 
 int vqm_ssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n, int w, int h,
                           int bpc) {
     DeviceScope scope;
-    return submit(ctx, KIND_SSIM, refs, dis, n, w, h, bpc);
+    return submit(ctx, KIND_SSIM, refs, dis, n, w, h, bpc, true);
 }
 
 int vqm_msssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n, int w, int h,
                             int bpc) {
     DeviceScope scope;
-    return submit(ctx, KIND_MSSSIM, refs, dis, n, w, h, bpc);
+    return submit(ctx, KIND_MSSSIM, refs, dis, n, w, h, bpc, true);
 }
 
 int vqm_collect(vqm_ctx *ctx, double *score, double *lcs) {

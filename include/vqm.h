@@ -39,6 +39,17 @@
  *     input is sent directly; device input is read in place ([R-1369] §4).
  *   - The caller owns every buffer it passes.  The library owns its device
  *     scratch, pinned staging and result slots.
+ *   - Ordering of device input: the library reads device planes on its own
+ *     stream.  A stream the library creates for itself (the blocking calls',
+ *     a context created with a NULL stream) is a blocking stream, so it
+ *     starts after work already enqueued on the legacy default stream, which
+ *     is where torch's default stream enqueues.  Planes written on any other
+ *     stream must be complete before the call: synchronise with that stream
+ *     first, or give that stream to vqm_ctx_create.
+ *   - Read-back: a frame's result is one 8-byte double, written by the
+ *     device straight into pinned host memory ([R-1363] Finding 6; the pages'
+ *     one read-back per frame).  The decibel form (8 more bytes) and the 15
+ *     MS-SSIM level means (120 more) cross only when a call asks for them.
  *
  * Numerics:
  *   - Every bit depth is mapped onto the 8-bit scale, v = raw * 2^-(bpc-8),
@@ -70,7 +81,7 @@
 extern "C" {
 #endif
 
-#define VQM_ABI_VERSION 4
+#define VQM_ABI_VERSION 5
 
 /* Exported symbols (the library is built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -104,15 +115,20 @@ VQM_API int vqm_ssim_scale(int w, int h);
 
 /* Size of the decimated plane of a w x h frame (ceil(w/s) x ceil(h/s)) and
  * whether float_ssim accepts the frame: returns 0, or -EINVAL / -ENOTSUP as
- * vqm_ssim_frame would, without touching the GPU.  Any output may be NULL. */
+ * vqm_ssim_frame would, without touching the GPU.  Any output may be NULL.
+ * ([ADR-1405] Context: the scale rule; Decision 4: the gate refuses a
+ * decimated plane below 11 x 11 or a scale above 128, nothing else.) */
 VQM_API int vqm_ssim_geometry(int w, int h, int bpc, int *scale, int *dec_w, int *dec_h);
 
-/* float_ssim of one frame pair, blocking.  Runs on an idle library-owned
- * context of the current HIP device (each with its own stream; threads
- * calling at once each get their own, and the contexts are kept for later
- * calls); one upload (unless the planes are already on the device), one
- * device wait, one 8-byte result.  *score receives the mean SSIM.  Thread-
- * safe. */
+/* float_ssim of one frame pair, blocking ([ADR-1405] Context: decimate by
+ * the automatic scale, then the SSIM map and its mean; Decision 1: exact
+ * window sums; Decision 4: the gate; Context again: each frame is uploaded
+ * once and read back once).  Runs on an idle library-owned context of the
+ * current HIP device
+ * (each with its own blocking stream; threads calling at once each get their
+ * own, and the contexts are kept for later calls); one upload (unless the
+ * planes are already on the device), one device wait, one 8-byte result.
+ * *score receives the mean SSIM.  Thread-safe. */
 VQM_API int vqm_ssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score);
 
 /* float_ssim plus its decibel form, blocking; as vqm_ssim_frame.  *db
@@ -123,7 +139,9 @@ VQM_API int vqm_ssim_frame(const void *ref, const void *dis, int w, int h, int b
 VQM_API int vqm_ssim_frame_db(const void *ref, const void *dis, int w, int h, int bpc, double *score,
                               double *db);
 
-/* 5-scale MS-SSIM of one frame pair, blocking; as vqm_ssim_frame. */
+/* 5-scale MS-SSIM of one frame pair, blocking; as vqm_ssim_frame.  All five
+ * levels and the combine are enqueued together and the call waits once
+ * ([R-1363] Finding 6: a partials span per scale, one wait per frame). */
 VQM_API int vqm_msssim_frame(const void *ref, const void *dis, int w, int h, int bpc, double *score);
 
 /* MS-SSIM plus the 15 per-level means (lcs: VQM_MSSSIM_LCS doubles, in the
@@ -163,12 +181,15 @@ VQM_API int vqm_msssim_frame_yuv(const void *const *ref, const void *const *dis,
 
 typedef struct vqm_ctx vqm_ctx;
 
-/* Create a context on HIP device `device`.  `hip_stream` is a hipStream_t
- * on that device to enqueue on (e.g. torch.cuda.current_stream().cuda_stream),
- * or NULL for a library-owned non-blocking stream.  The stream must outlive
- * the context.  A context is not thread-safe: use one per thread.  Calls on
- * a context make its device current while they run and restore the calling
- * thread's current device before they return. */
+/* Create a context on HIP device `device` ([R-1363] Finding 6: a twin's
+ * submit() enqueues a frame and collect() waits once; [R-1369] §4–§5: the
+ * pinned staging and the per-slot scratch such a context owns).  `hip_stream`
+ * is a hipStream_t on that device to enqueue on (e.g.
+ * torch.cuda.current_stream().cuda_stream), or NULL for a library-owned
+ * blocking stream (see "Ordering of device input" above).  The stream must
+ * outlive the context.  A context is not thread-safe: use one per thread.
+ * Calls on a context make its device current while they run and restore the
+ * calling thread's current device before they return. */
 VQM_API int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out);
 
 /* Wait for the context's frames, then free everything it owns.  NULL is a
@@ -176,13 +197,19 @@ VQM_API int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out);
 VQM_API void vqm_ctx_destroy(vqm_ctx *ctx);
 
 /* Enqueue one float_ssim frame (upload if needed, decimate, SSIM map,
- * fixed-tree reduction) and return without waiting.  Host pageable input is
- * copied before the call returns; pinned or device input must stay unchanged
- * until the matching vqm_collect.  Frames of different sizes may follow one
- * another: scratch is keyed by (w, h, bpc) and rebuilt when it changes. */
+ * fixed-tree reduction) and return without waiting ([R-1363] Finding 6:
+ * submit() enqueues every stage; [R-1369] §4: pageable input through pinned
+ * staging, one DMA; §5: a slot is reused only after its frame was collected;
+ * §7: scratch keyed by the geometry).  Host pageable input is copied before
+ * the call returns; pinned or device input must stay unchanged until the
+ * matching vqm_collect.  Frames of different sizes may follow one another:
+ * scratch is keyed by (w, h, bpc) and rebuilt when it changes.  The finish
+ * also writes the decibel form, which vqm_collect_db may read. */
 VQM_API int vqm_ssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc);
 
-/* Enqueue one MS-SSIM frame (all five levels and the combine). */
+/* Enqueue one MS-SSIM frame (all five levels and the combine; [R-1363]
+ * Finding 6).  The finish also writes the 15 level means, which vqm_collect
+ * may read. */
 VQM_API int vqm_msssim_submit(vqm_ctx *ctx, const void *ref, const void *dis, int w, int h, int bpc);
 
 /* Enqueue n (1..VQM_MAX_BATCH) frames of the same size and depth as one
@@ -199,8 +226,9 @@ VQM_API int vqm_ssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const v
 VQM_API int vqm_msssim_submit_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n,
                                     int w, int h, int bpc);
 
-/* Wait for the oldest frame in flight (the one device wait of that frame)
- * and return its score.  lcs (may be NULL) receives the 15 per-level means
+/* Wait for the oldest frame in flight (the one device wait of that frame,
+ * [R-1363] Finding 6; [R-1369] §5: its slot is free again afterwards) and
+ * return its score.  lcs (may be NULL) receives the 15 per-level means
  * when the frame was an MS-SSIM frame; for a float_ssim frame it is left
  * untouched. */
 VQM_API int vqm_collect(vqm_ctx *ctx, double *score, double *lcs);

@@ -52,7 +52,7 @@ def header_constants():
 
 
 def test_abi_version():
-    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 4
+    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 5
 
 
 def test_graft_entry_check_matches_the_built_library():

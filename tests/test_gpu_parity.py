@@ -683,6 +683,53 @@ def test_blocking_calls_from_many_threads(torch_cuda):
         assert results[k] == (want + [want_ms]) * 3, k
 
 
+def _late_default_stream_copy(torch, host):
+    """A device tensor whose content arrives late on the default stream.
+
+    It holds zeros at first; a few long fp32 products on the default stream
+    (tens of milliseconds) come first, then the copy of ``host`` (pinned), so
+    a reader on a stream that does not wait for the default stream sees the
+    zeros.
+    """
+    out = torch.zeros_like(host, device="cuda")
+    x = torch.rand(4096, 4096, device="cuda")
+    for _ in range(12):
+        x = torch.mm(x, x) * (1.0 / 4096)
+    out.copy_(host, non_blocking=True)
+    return out, x
+
+
+@pytest.mark.parametrize("metric", ["ssim", "msssim"])
+def test_blocking_call_orders_after_default_stream_work(torch_cuda, metric):
+    # A plane produced by torch on its default stream, passed straight to a
+    # blocking call with no synchronisation: the library's own stream is a
+    # blocking stream, so it starts after that work and scores the finished
+    # plane.
+    torch = torch_cuda
+    c = 4 if metric == "ssim" else 5
+    src = synth.FrameSource(c, w=960, h=544) if metric == "msssim" else synth.FrameSource(c)
+    ref, dis = src.pair(1)
+    want = oracle.ssim(ref, dis, src.bpc) if metric == "ssim" else oracle.msssim(ref, dis, src.bpc)
+    view = (lambda a: a.view(np.int16)) if src.bpc > 8 else (lambda a: a)
+    r = to_dev(torch, ref)
+    host = torch.from_numpy(view(dis)).pin_memory()
+    torch.cuda.synchronize()
+    say(f"{metric}: dis produced on the default stream, scored without a wait")
+    for _ in range(2):
+        d, keep = _late_default_stream_copy(torch, host)
+        fn = vqm.vqm_ssim_frame if metric == "ssim" else vqm.vqm_msssim_frame
+        got = fn(r, d, src.bpc)
+        assert abs(got - want) <= TOL, (got, want)
+    torch.cuda.synchronize()
+    # the same through a context on a library-owned stream
+    with vqm.Context(0) as cx:
+        d, keep = _late_default_stream_copy(torch, host)
+        (cx.vqm_ssim_submit if metric == "ssim" else cx.vqm_msssim_submit)(r, d, src.bpc)
+        got = cx.vqm_collect()
+        assert abs(got - want) <= TOL, (got, want)
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------ recorded passes (graph replay)
 
 def _eager(torch, metric, fs, batch):
