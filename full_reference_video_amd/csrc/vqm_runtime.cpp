@@ -1077,12 +1077,143 @@ int graph_collect(vqm_graph *g, double *scores, double *lcs, double *db) {
     return 0;
 }
 
+// ---- the allocation-free float_ssim pass (vqm_ssim_frame_noalloc) ----
+//
+// Its scratch (both decimated planes and the map's partial sums) lives in one
+// file-scope device array per GPU, which each GPU the library runs on holds
+// until the process ends.  In host code the array's name only stands in for
+// the symbol: its device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address ever reaches a
+// kernel.  Every call on a device shares the array, so calls that overlap on
+// one GPU race; the kernels overwrite every byte they later read, so nothing
+// needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[VQM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxScratchDevices] = {};
+
+int noalloc_scratch(int device, unsigned char **out) {
+    if (device < 0 || device >= kMaxScratchDevices)
+        return fail(-EINVAL, "device %d outside the 0..%d the allocation-free path serves", device,
+                    kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_dev[device]) {
+        void *ptr = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));  // the current device is `device`
+        if (!ptr) return fail(-EIO, "hipGetSymbolAddress returned no address for the scratch array");
+        g_scratch_dev[device] = ptr;
+    }
+    *out = static_cast<unsigned char *>(g_scratch_dev[device]);
+    return 0;
+}
+
+// Device-visible address of the caller's score buffer: device memory of
+// `device`, or pinned host memory (its mapped address).
+int noalloc_result(double *score, int device, double **dev) {
+    hipPointerAttribute_t a;
+    memset(&a, 0, sizeof a);
+    if (hipPointerGetAttributes(&a, score) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(-EINVAL, "score must be device memory or pinned host memory");
+    }
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+        if (a.device != device)
+            return fail(-EINVAL, "score is device memory of device %d, the call runs on %d", a.device, device);
+        *dev = score;
+        return 0;
+    }
+    if (a.type == hipMemoryTypeHost && a.devicePointer) {
+        *dev = static_cast<double *>(a.devicePointer);
+        return 0;
+    }
+    return fail(-EINVAL, "score must be device memory or pinned host memory");
+}
+
+int ssim_noalloc(const void *ref, const void *dis, int w, int h, int bpc, double *score, void *stream) {
+    if (!score) return fail(-EINVAL, "NULL score pointer");
+    int rc = check_args(ref, dis, w, h, bpc);
+    if (rc) return rc;
+    rc = gate_ssim(w, h, bpc, nullptr, nullptr, nullptr);
+    if (rc) return rc;
+    const Geometry g = make_geometry(KIND_SSIM, w, h, bpc);
+    // Scratch: two decimated planes (none at scale 1: the map reads the raw
+    // samples), then one double per map tile.
+    const size_t plane_bytes = g.s > 1 ? (size_t)g.dpitch * (size_t)g.dh * sizeof(float) : 0;
+    const size_t planes_bytes = (2 * plane_bytes + 255) / 256 * 256;
+    const size_t need = planes_bytes + (size_t)vqm::ssim_partials(g.dw, g.dh) * sizeof(double);
+    if (need > (size_t)VQM_NOALLOC_SCRATCH_BYTES)
+        return fail(-ENOSPC, "a %dx%d frame needs %zu bytes of scratch; the allocation-free path holds %d", w, h,
+                    need, VQM_NOALLOC_SCRATCH_BYTES);
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (st) {
+        int sdev = -1;
+        if (hipStreamGetDevice(st, &sdev) == hipSuccess && sdev != dev)
+            return fail(-EINVAL, "stream belongs to device %d, the current device is %d", sdev, dev);
+        (void)hipGetLastError();
+    }
+    for (const void *p : {ref, dis}) {
+        PtrKind k;
+        rc = classify(p, dev, &k);
+        if (rc) return rc;
+        if (k != PTR_DEVICE) return fail(-EINVAL, "the allocation-free path reads device planes only");
+    }
+    double *result = nullptr;
+    rc = noalloc_result(score, dev, &result);
+    if (rc) return rc;
+    unsigned char *base = nullptr;
+    rc = noalloc_scratch(dev, &base);
+    if (rc) return rc;
+
+    static const vqm::Taps taps = make_taps();
+    const vqm::StepGeometry sg = step_geometry(g);
+    const bool decimating = g.s > 1;
+    void *out_ref = base, *out_dis = base + plane_bytes;
+    double *partials = reinterpret_cast<double *>(base + planes_bytes);
+    const vqm::KernelTimer no_timer;
+    vqm::StepRoles r;
+    // The same step kernel as the pipelined path, one role per launch:
+    // decimate, map, finish (no decimation at scale 1).
+    if (decimating) {
+        memset(&r, 0, sizeof r);
+        r.n_dec = 1;
+        r.dec.f[0] = vqm::DecimateFrame{ref, dis, out_ref, out_dis};
+        const hipError_t e = vqm::launch_ssim_step(r, sg, sg.packed ? vqm::IN_U16 : vqm::IN_F32, g.dpitch,
+                                                   sg.packed ? sg.post : 1.0f, taps, st, no_timer);
+        if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
+    }
+    const vqm::InKind kind = decimating ? (sg.packed ? vqm::IN_U16 : vqm::IN_F32)
+                                        : (g.bpc == 8 ? vqm::IN_U8 : vqm::IN_U16);
+    const int pitch = decimating ? g.dpitch : g.w;
+    const float unit = decimating ? (sg.packed ? sg.post : 1.0f) : ldexpf(1.0f, -(g.bpc - 8));
+    const vqm::SsimFrame f{decimating ? out_ref : ref, decimating ? out_dis : dis, partials, result};
+    for (int role = 0; role < 2; ++role) {
+        memset(&r, 0, sizeof r);
+        if (role == 0) {
+            r.n_map = 1;
+            r.map.f[0] = f;
+        } else {
+            r.n_fin = 1;
+            r.fin.f[0] = f;
+        }
+        const hipError_t e = vqm::launch_ssim_step(r, sg, kind, pitch, unit, taps, st, no_timer);
+        if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
+    }
+    return 0;
+}
+
 }  // namespace
 
 extern "C" {
 
 int vqm_abi_version(void) { return VQM_ABI_VERSION; }
 
+int vqm_ssim_frame_noalloc(const void *ref, const void *dis, int w, int h, int bpc, double *score,
+                           void *hip_stream) {
+    return ssim_noalloc(ref, dis, w, h, bpc, score, hip_stream);
+}
 
 int vqm_graph_create(int device, void *hip_stream, int metric, const void *const *refs, const void *const *dis,
                      int n, int w, int h, int bpc, int batch, vqm_graph **out) {

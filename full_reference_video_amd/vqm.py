@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
         L.vqm_graph_collect.argtypes = [c_void_p, c_double_p, c_double_p, c_double_p]
         L.vqm_graph_destroy.argtypes = [c_void_p]
         L.vqm_graph_destroy.restype = None
+        L.vqm_ssim_frame_noalloc.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p]
         L.vqm_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -232,6 +233,31 @@ def vqm_msssim_frame_lcs(ref, dis, bpc: int):
                                       lcs.ctypes.data_as(ctypes.POINTER(ctypes.c_double))),
            "vqm_msssim_frame_lcs")
     return score.value, lcs
+
+
+def vqm_ssim_frame_noalloc(ref, dis, bpc: int, score, stream=None) -> None:
+    """Enqueue float_ssim of one device-resident frame pair with no allocation.
+
+    ``score`` is a float64 tensor of at least one element in device memory (or
+    pinned host memory) that receives the score once ``stream`` (a
+    ``torch.cuda.Stream``, a raw handle, or None for the legacy default
+    stream) reaches this point; the call does not wait.
+    """
+    pr, pd, w, h, _ = _pair(ref, dis, bpc)
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        torch = None
+    if torch is not None and isinstance(score, torch.Tensor):
+        if score.dtype != torch.float64 or score.numel() < 1:
+            raise TypeError("score must be a float64 tensor with at least one element")
+        sp = score.data_ptr()
+    elif isinstance(score, int):
+        sp = score
+    else:
+        raise TypeError(f"unsupported score buffer {type(score)!r}")
+    _check(lib().vqm_ssim_frame_noalloc(pr, pd, w, h, int(bpc), sp, _stream_handle(stream)),
+           "vqm_ssim_frame_noalloc")
 
 
 def _stream_handle(stream):

@@ -27,6 +27,8 @@
  *       -EIO      a HIP runtime error (the message names it).
  *       -EAGAIN   vqm_collect with no frame in flight; a submit with
  *                 VQM_MAX_IN_FLIGHT frames already in flight.
+ *       -ENOSPC   vqm_ssim_frame_noalloc: the frame needs more scratch than
+ *                 its fixed array holds.
  *   - Planes are row-major and tightly packed (stride = w samples): uint8_t
  *     samples when bpc == 8, native-endian uint16_t with the value in the low
  *     bits when 9 <= bpc <= 16.  Samples above 2^bpc - 1 violate the
@@ -104,6 +106,10 @@ extern "C" {
 /* Number of per-level means vqm_msssim_frame_lcs returns: L_1..L_5,
  * C_1..C_5, S_1..S_5 ([R-1363] Finding 6, enable_lcs). */
 #define VQM_MSSSIM_LCS 15
+
+/* Device scratch, in bytes (8 MiB), of vqm_ssim_frame_noalloc: one array per GPU the
+ * library runs on, held until the process ends. */
+#define VQM_NOALLOC_SCRATCH_BYTES 8388608
 
 /* ABI version of the loaded library (VQM_ABI_VERSION it was built with). */
 VQM_API int vqm_abi_version(void);
@@ -350,6 +356,33 @@ VQM_API int vqm_debug_pyramid(vqm_ctx *ctx, const void *ref, const void *dis, in
  * pyramid. */
 VQM_API int vqm_debug_pyramid_batch(vqm_ctx *ctx, const void *const *refs, const void *const *dis, int n, int w,
                                     int h, int bpc, int level, float *out_ref, float *out_dis);
+
+/* ---- allocation-free float_ssim ---- */
+
+/* float_ssim of one device-resident frame pair that allocates nothing, for
+ * callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It enqueues the same kernels as
+ * vqm_ssim_frame (decimation, SSIM map, fixed-tree finish) on `hip_stream`
+ * (a stream of the current device; NULL is the legacy default stream) and
+ * returns without waiting: *score holds the frame's score once that stream's
+ * work up to this call has completed.
+ *   ref, dis   device memory of the current device, w x h samples of bpc bits
+ *              as for vqm_ssim_frame; they must stay unchanged until the
+ *              score is written.
+ *   score      one double of device memory of the current device, or of
+ *              pinned host memory (hipHostMalloc).
+ * Scratch: a file-scope device array of VQM_NOALLOC_SCRATCH_BYTES per GPU
+ * (both decimated planes and one double per 32 x 32 map tile), held until
+ * the process ends.  Frames whose scratch exceeds it are refused with
+ * -ENOSPC (every frame up to 8192 x 4320 fits; a decimated plane of about
+ * a million samples does not).  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and give unspecified scores.
+ * Host memory planes are refused (-EINVAL), as are the gate's frames
+ * (-ENOTSUP).  Makes no allocation of any kind; the first call on each device
+ * takes the array's device address once. */
+VQM_API int vqm_ssim_frame_noalloc(const void *ref, const void *dis, int w, int h, int bpc, double *score,
+                                   void *hip_stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 VQM_API const char *vqm_last_error(void);

@@ -201,3 +201,24 @@ def test_yuv_gate_refuses_before_any_hip_call():
     assert "plane 1" in vqm.vqm_last_error()
     with pytest.raises(ValueError):  # wrong chroma size for the layout
         vqm.vqm_ssim_frame_yuv(planes, planes, 8, vqm.VQM_CHROMA_444)
+
+
+def test_noalloc_refuses_oversized_and_bad_frames_before_any_hip_call():
+    # The allocation-free entry point checks its arguments, the gate and its
+    # fixed scratch size on the host first; none of these touches the GPU.
+    lib = ctypes.CDLL(vqm.LIB_PATH)
+    f = lib.vqm_ssim_frame_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    dummy = ctypes.c_void_p(0x1000)
+    # 65535 x 400 decimates by 2 to 32768 x 200: two fp32 planes of 25 MiB
+    assert f(dummy, dummy, 65535, 400, 8, dummy, None) == -errno.ENOSPC
+    assert "scratch" in vqm.vqm_last_error()
+    assert f(dummy, dummy, 3840, 2160, 10, None, None) == -errno.EINVAL      # no score buffer
+    assert f(None, dummy, 3840, 2160, 10, dummy, None) == -errno.EINVAL      # no plane
+    assert f(dummy, dummy, 3840, 2160, 7, dummy, None) == -errno.EINVAL      # depth
+    assert f(dummy, dummy, 100, 8, 8, dummy, None) == -errno.ENOTSUP        # below the window
+    # 8K (scale 17) needs about 1 MiB of the 8 MiB array: past the size check
+    # (here it then fails at the device or pointer checks instead)
+    assert header_constants()["VQM_NOALLOC_SCRATCH_BYTES"] == 8 << 20
+    assert f(dummy, dummy, 7680, 4320, 10, dummy, None) not in (0, -errno.ENOSPC)
