@@ -15,6 +15,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "vqm_oracle.c")
+_SS2_SRC = os.path.join(_HERE, "ss2_oracle.c")
+SOURCES = [_SRC, _SS2_SRC]
 _LIB = os.path.join(_HERE, "libvqm_oracle.so")
 
 # Contraction off and no fast-math: every fp32 product and the single
@@ -26,7 +28,7 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-s
 def build(cc: str = "gcc") -> str:
     """Compile the oracle into ``oracle/libvqm_oracle.so`` (always recompiles)."""
     tmp = _LIB + ".tmp"
-    subprocess.run([cc, *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+    subprocess.run([cc, *CFLAGS, "-o", tmp, *SOURCES, "-lm"], check=True)
     os.replace(tmp, _LIB)
     return _LIB
 
@@ -45,7 +47,7 @@ def lib():
         path = os.environ.get("VQM_ORACLE_LIB")
         if not path:
             path = _LIB
-            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            if not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(f) for f in SOURCES):
                 build()
         L = ctypes.CDLL(path)
         vp, ip, fp, dp = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
@@ -66,6 +68,15 @@ def lib():
         L.vqm_oracle_plane_dims.restype = ip
         L.vqm_oracle_db.argtypes = [ctypes.c_double]
         L.vqm_oracle_db.restype = ctypes.c_double
+        L.vqm_oracle_ss2_channel_sums.argtypes = [fp] * 7 + [ip, ip, dp]
+        L.vqm_oracle_ss2_channel_sums.restype = ip
+        fl = ctypes.c_float
+        for name in ("vqm_oracle_two_sum", "vqm_oracle_two_prod"):
+            getattr(L, name).argtypes = [fl, fl, fp]
+            getattr(L, name).restype = None
+        for name in ("vqm_oracle_ff_add", "vqm_oracle_ff_mul", "vqm_oracle_ff_div"):
+            getattr(L, name).argtypes = [fp, fp, fp]
+            getattr(L, name).restype = None
         L.vqm_oracle_msssim_combine.argtypes = [dp]
         L.vqm_oracle_msssim_combine.restype = ctypes.c_double
         for name in ("vqm_oracle_sample_plane", "vqm_oracle_decimate", "vqm_oracle_ssim_planes",
@@ -207,3 +218,55 @@ def plane_dims(w: int, h: int, chroma: int, plane: int):
     pw, ph = ctypes.c_int(), ctypes.c_int()
     _check(lib().vqm_oracle_plane_dims(w, h, chroma, plane, ctypes.byref(pw), ctypes.byref(ph)), "plane_dims")
     return pw.value, ph.value
+
+
+# ---------------------------------------------------------------- ssimulacra2
+
+SS2_PLANES = ("img1", "img2", "mu1", "mu2", "s11", "s22", "s12")
+
+
+def ss2_channel_sums(img1, img2, mu1, mu2, s11, s22, s12) -> np.ndarray:
+    """The six ssimulacra2 sums of one channel at one scale (fp64, in the
+    order sum d, sum d^4, sum art, sum art^4, sum det, sum det^4)."""
+    planes = [np.ascontiguousarray(p, np.float32) for p in (img1, img2, mu1, mu2, s11, s22, s12)]
+    h, w = planes[0].shape
+    for p in planes:
+        if p.shape != (h, w):
+            raise ValueError("all seven planes must have one shape")
+    out = np.empty(6, np.float64)
+    _check(lib().vqm_oracle_ss2_channel_sums(*[_ptr(p) for p in planes], w, h, _ptr(out)), "ss2_channel_sums")
+    return out
+
+
+def _pair_out(fn, *args):
+    out = np.empty(2, np.float32)
+    fn(*args, _ptr(out))
+    return out[0], out[1]
+
+
+def two_sum(a, b):
+    return _pair_out(lib().vqm_oracle_two_sum, float(np.float32(a)), float(np.float32(b)))
+
+
+def two_prod(a, b):
+    return _pair_out(lib().vqm_oracle_two_prod, float(np.float32(a)), float(np.float32(b)))
+
+
+def _ff(name, a, b):
+    pa = np.ascontiguousarray(a, np.float32)
+    pb = np.ascontiguousarray(b, np.float32)
+    if pa.shape != (2,) or pb.shape != (2,):
+        raise ValueError("pairs are two float32 values (hi, lo)")
+    return _pair_out(getattr(lib(), name), _ptr(pa), _ptr(pb))
+
+
+def ff_add(a, b):
+    return _ff("vqm_oracle_ff_add", a, b)
+
+
+def ff_mul(a, b):
+    return _ff("vqm_oracle_ff_mul", a, b)
+
+
+def ff_div(a, b):
+    return _ff("vqm_oracle_ff_div", a, b)

@@ -45,6 +45,12 @@
  *   db                — 10, 20, 30 dB at 1 - ssim = 1e-1, 1e-2, 1e-3; the
  *                       ADR's sensitivity 4.34 / (1 - ssim) as a finite
  *                       difference, and its 0.018 dB at 30 dB example.
+ *   ss2 sums          — exact rational sums on planes whose fp32 steps are
+ *                       exact; identical inputs give six zeros; closed forms
+ *                       of constant planes.  Parity with the pages' own
+ *                       ssimulacra2 scores is unpinned (no fixture here).
+ *   pairs             — two_sum and two_prod exact against Fraction; ff_add,
+ *                       ff_mul and ff_div within their error bounds.
  */
 #ifndef VQM_ORACLE_H
 #define VQM_ORACLE_H
@@ -139,6 +145,49 @@ int vqm_oracle_plane_dims(int w, int h, int chroma, int plane, int *pw, int *ph)
  * the derivative of this function; identical planes have no finite value).
  * [ADR-1405] Consequences. */
 double vqm_oracle_db(double ssim);
+
+/* ---------------------------------------------------------------------
+ * ssimulacra2: the per-scale statistics and exact fp32 pairs
+ * ("Research-1363: Device-resident ssimulacra2 and a single-wait MS-SSIM on
+ * SYCL", Findings 3-5).  Source: ss2_oracle.c.
+ *
+ * The six sums of one channel at one scale, from seven w x h fp32 planes:
+ * the two images r1, r2, their blurred means mu1, mu2, and the blurred
+ * products s11 = blur(r1 r1), s22 = blur(r2 r2), s12 = blur(r1 r2).  Per
+ * pixel, in fp32 and in this order (readings: the page names num_m, num_s,
+ * denom_s and the term 1 - q without defining them; these are the published
+ * ssimulacra2 definitions, with its one constant C2 = 0.0009f):
+ *   num_m   = 1 - (mu1 - mu2)^2
+ *   num_s   = 2 (s12 - mu1 mu2) + C2
+ *   denom_s = (s11 - mu1^2) + (s22 - mu2^2) + C2
+ * then in fp64, as the page's CPU extractor does (Finding 3):
+ *   d   = max(1 - num_m num_s / denom_s, 0)       (reading: the published
+ *         metric clamps the SSIM deficit at 0)
+ *   e   = (1 + |r2 - mu2|) / (1 + |r1 - mu1|) - 1  (Finding 4, as printed;
+ *         each |.| of an fp32 difference)
+ *   art = max(e, 0), det = max(-e, 0)
+ * sums[] = { sum d, sum d^4, sum art, sum art^4, sum det, sum det^4 }, each
+ * an fp64 sum of the terms one after another in row-major order (Finding 3:
+ * the CPU adds the fp64 terms sequentially).
+ * Returns -EINVAL for NULL pointers or a non-positive size. */
+int vqm_oracle_ss2_channel_sums(const float *img1, const float *img2, const float *mu1, const float *mu2,
+                                const float *s11, const float *s22, const float *s12, int w, int h,
+                                double sums[6]);
+
+/* Error-free transformations and fp32-pair ("double-float") arithmetic, the
+ * tools of Finding 4.  A pair (hi, lo) stands for the real number hi + lo.
+ *   two_sum(a, b):   s = fl(a + b), e = a + b - s exactly (Knuth).
+ *   two_prod(a, b):  p = fl(a b), e = a b - p exactly, by one fused
+ *                    multiply-add (exact barring underflow).
+ *   ff_add(a, b):    a + b as a pair, relative error below about 3 * 2^-48.
+ *   ff_mul(a, b):    a b as a pair, relative error below about 7 * 2^-48.
+ *   ff_div(a, b):    a / b from two correctly rounded fp32 partial quotients
+ *                    (the page's ff_div), relative error about 2^-46. */
+void vqm_oracle_two_sum(float a, float b, float out[2]);
+void vqm_oracle_two_prod(float a, float b, float out[2]);
+void vqm_oracle_ff_add(const float a[2], const float b[2], float out[2]);
+void vqm_oracle_ff_mul(const float a[2], const float b[2], float out[2]);
+void vqm_oracle_ff_div(const float a[2], const float b[2], float out[2]);
 
 #ifdef __cplusplus
 }
