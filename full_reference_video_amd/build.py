@@ -7,6 +7,9 @@ recompiles.  Flags:
 * ``-ffp-contract=off``: no implicit FMA contraction, so expressions that must
   round the same way for both planes (the SSIM map's mirrored numerator and
   denominator) do; the kernels ask for FMA explicitly where they want it.
+* ``-fhip-fp32-correctly-rounded-divide-sqrt``: fp32 ``/`` is IEEE division
+  (the ssimulacra2 pair quotients rely on correctly rounded partial
+  quotients).
 * ``-Xclang -target-feature -Xclang -packed-fp32-ops``: no packed fp32 math.
 """
 
@@ -19,7 +22,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvqm.so")
 
-SOURCES = ["vqm_runtime.cpp", "ssim_step.hip", "msssim.hip"]
+SOURCES = ["vqm_runtime.cpp", "ssim_step.hip", "msssim.hip", "ss2_stats.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -28,6 +31,7 @@ FLAGS = [
     "-fPIC",
     "-shared",
     "-ffp-contract=off",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-fvisibility=hidden",

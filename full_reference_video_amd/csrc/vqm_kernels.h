@@ -163,6 +163,27 @@ struct MsLevels {
 // fixed tree, and the combined score.
 hipError_t launch_ms_finish(const MsFinishBatch &b, int n, const MsLevels &lv, hipStream_t stream);
 
+// ---------------------------------------------------------------- ssimulacra2 statistics
+
+constexpr int kSs2MaxChannels = 3;
+constexpr int kSs2MaxBlocks = 1024;
+
+// Workgroups per channel of the statistics' first stage for a plane of n
+// pixels (a function of n alone, so the tree's shape is too).
+int ss2_blocks(long long n);
+
+// The six ssimulacra2 sums of nch channels of n pixels each: planes holds 7
+// device pointers per channel (img1, img2, mu1, mu2, s11, s22, s12; fp32,
+// tightly packed); partials is device scratch of nch * ss2_blocks(n) * 6
+// fp32 pairs; result receives 6 doubles per channel (a device-visible
+// address).  Two launches: workgroup partials, then one group per channel.
+hipError_t launch_ss2_sums(const float *const *planes, int nch, long long n, void *partials, double *result,
+                           hipStream_t stream);
+
+// The pair operations elementwise (0 two_sum, 1 two_prod, 2 ff_add,
+// 3 ff_mul, 4 ff_div) over n pairs of device arrays, for the tests.
+hipError_t launch_pair_ops(int op, const float *a, const float *b, float *out, int n, hipStream_t stream);
+
 // ---------------------------------------------------------------- shared
 
 // XCD-aware block order.  The dispatcher hands consecutive workgroups of a

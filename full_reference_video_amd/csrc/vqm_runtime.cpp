@@ -225,6 +225,9 @@ struct vqm_ctx {
     double time_ms[4] = {0, 0, 0, 0};
     int launches[4] = {0, 0, 0, 0};
     int frames[4] = {0, 0, 0, 0};
+    // ssimulacra2 statistics: workgroup partials and the pinned result block
+    void *ss2_partials = nullptr;
+    double *ss2_result_host = nullptr, *ss2_result_dev = nullptr;
 };
 
 namespace {
@@ -729,6 +732,8 @@ void destroy(vqm_ctx *ctx) {
         (void)hipEventDestroy(t.stop);
     }
     for (hipEvent_t e : ctx->event_pool) (void)hipEventDestroy(e);
+    if (ctx->ss2_partials) (void)hipFree(ctx->ss2_partials);
+    if (ctx->ss2_result_host) (void)hipHostFree(ctx->ss2_result_host);
     if (ctx->own_stream) (void)hipStreamDestroy(ctx->stream);
     if (cur >= 0) (void)hipSetDevice(cur);
     delete ctx;
@@ -918,6 +923,66 @@ int score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *
         if (rc == 0) rc = rc2;
     }
     return rc;
+}
+
+// The ssimulacra2 statistics of one scale ("Research-1363: Device-resident
+// ssimulacra2 and a single-wait MS-SSIM on SYCL", Finding 4): two launches on
+// a leased context's stream, one wait, one read-back of 6 doubles per
+// channel.
+int ss2_sums(const float *const *planes, int nch, int w, int h, double *sums) {
+    if (!planes || !sums) return fail(-EINVAL, "NULL plane array or sums pointer");
+    if (nch < 1 || nch > vqm::kSs2MaxChannels)
+        return fail(-EINVAL, "%d channels outside 1..%d", nch, vqm::kSs2MaxChannels);
+    if (w <= 0 || h <= 0) return fail(-EINVAL, "plane size %dx%d is not positive", w, h);
+    if ((long long)w * (long long)h > 0x7fffffffLL) return fail(-EINVAL, "plane %dx%d too large", w, h);
+    for (int i = 0; i < 7 * nch; ++i)
+        if (!planes[i]) return fail(-EINVAL, "NULL plane %d", i);
+    Lease lease;
+    int rc = lease_ctx(lease);
+    if (rc) return rc;
+    vqm_ctx *ctx = lease.ctx;
+    for (int i = 0; i < 7 * nch; ++i) {
+        PtrKind k;
+        rc = classify(planes[i], ctx->device, &k);
+        if (rc) return rc;
+        if (k != PTR_DEVICE) return fail(-EINVAL, "plane %d: the statistics read device memory only", i);
+    }
+    if (!ctx->ss2_partials) {
+        HIP_TRY_ALLOC(hipMalloc(&ctx->ss2_partials, (size_t)vqm::kSs2MaxChannels * vqm::kSs2MaxBlocks * 6 *
+                                                        2 * sizeof(float)));
+        HIP_TRY_ALLOC(hipHostMalloc(&ctx->ss2_result_host, 6 * vqm::kSs2MaxChannels * sizeof(double),
+                                    hipHostMallocMapped | hipHostMallocCoherent));
+        HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void **>(&ctx->ss2_result_dev), ctx->ss2_result_host, 0));
+    }
+    for (int k = 0; k < 6 * nch; ++k) ctx->ss2_result_host[k] = NAN;
+    const hipError_t e =
+        vqm::launch_ss2_sums(planes, nch, (long long)w * h, ctx->ss2_partials, ctx->ss2_result_dev, ctx->stream);
+    if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
+    HIP_TRY(hipStreamSynchronize(ctx->stream));  // the one wait
+    memcpy(sums, ctx->ss2_result_host, 6 * (size_t)nch * sizeof(double));
+    return 0;
+}
+
+int pair_ops(int op, const float *a, const float *b, float *out, int n) {
+    if (!a || !b || !out) return fail(-EINVAL, "NULL argument");
+    if (op < 0 || op > 4) return fail(-EINVAL, "pair operation %d outside 0..4", op);
+    if (n < 1 || n > (1 << 24)) return fail(-EINVAL, "%d elements outside 1..2^24", n);
+    Lease lease;
+    int rc = lease_ctx(lease);
+    if (rc) return rc;
+    vqm_ctx *ctx = lease.ctx;
+    const size_t bytes = 2 * (size_t)n * sizeof(float);
+    float *d = nullptr;
+    HIP_TRY_ALLOC(hipMalloc(&d, 3 * bytes));
+    float *da = d, *db = d + 2 * (size_t)n, *dout = d + 4 * (size_t)n;
+    hipError_t e = hipMemcpyAsync(da, a, bytes, hipMemcpyHostToDevice, ctx->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(db, b, bytes, hipMemcpyHostToDevice, ctx->stream);
+    if (e == hipSuccess) e = vqm::launch_pair_ops(op, da, db, dout, n, ctx->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(out, dout, bytes, hipMemcpyDeviceToHost, ctx->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+    (void)hipFree(d);
+    if (e != hipSuccess) return fail(-EIO, "pair operations: %s", hipGetErrorString(e));
+    return 0;
 }
 
 // One frame into the next free slot for the debug exports (synchronous; the
@@ -1493,6 +1558,14 @@ int vqm_debug_pyramid_batch(vqm_ctx *ctx, const void *const *refs, const void *c
     }
     HIP_TRY(hipStreamSynchronize(ctx->stream));
     return 0;
+}
+
+int vqm_ss2_channel_sums(const float *const *planes, int nch, int w, int h, double *sums) {
+    return ss2_sums(planes, nch, w, h, sums);
+}
+
+int vqm_debug_pair_ops(int op, const float *a, const float *b, float *out, int n) {
+    return pair_ops(op, a, b, out, n);
 }
 
 const char *vqm_last_error(void) { return g_err.c_str(); }

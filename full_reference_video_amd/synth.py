@@ -226,3 +226,52 @@ def random_planes(seed: int, w: int, h: int, bpc: int, kind: str = "uniform"):
         yy, xx = np.mgrid[0:h, 0:w]
         return ((hi + 1) // 2 + ((xx + yy) & 1)).astype(dt)
     raise ValueError(kind)
+
+
+def _box5_symmetric(a: np.ndarray) -> np.ndarray:
+    """5 x 5 mean with half-sample symmetric edges, in fp64 (input
+    preparation only)."""
+    p = np.pad(a, 2, mode="symmetric")
+    h, w = a.shape
+    acc = np.zeros((h, w), dtype=np.float64)
+    for dy in range(5):
+        for dx in range(5):
+            acc += p[dy:dy + h, dx:dx + w]
+    return acc / 25.0
+
+
+def ss2_planes(seed: int, w: int, h: int, channels: int = 3):
+    """Inputs of the ssimulacra2 per-scale statistics: per channel the seven
+    float32 planes (img1, img2, mu1, mu2, s11, s22, s12), each h x w.
+
+    The pages measure ssimulacra2 on the Netflix 576x324 pair, Big Buck Bunny
+    at 3840x2160 and an 853x481 rescale ("Device-resident ssimulacra2 and a
+    single-wait MS-SSIM on SYCL", Sources and Finding 5); none is available
+    here, so seeded planes of those sizes stand in.  Each channel image is a
+    smooth field in [0, 1] (3 sinusoids of amplitude 0.08 about a level drawn
+    in [0.3, 0.7], from ``default_rng(seed * 10 + channel)``) plus uniform
+    noise in +-0.02; img2 is img1 plus Gaussian noise of sigma 0.01, clipped to
+    [0, 1].  The blurred planes are 5 x 5 means (symmetric edges, fp64, then
+    rounded to float32) of the images and of their products: a stand-in for
+    the metric's own blur, so that every variance the statistics form is
+    non-negative, as a blur with non-negative weights keeps it.
+    """
+    out = []
+    x = np.arange(w, dtype=np.float64)[None, :]
+    y = np.arange(h, dtype=np.float64)[:, None]
+    for ch in range(channels):
+        rng = np.random.default_rng(seed * 10 + ch)
+        level = rng.uniform(0.3, 0.7)
+        f = np.full((h, w), level)
+        for _ in range(3):
+            period = rng.uniform(12.0, 96.0)
+            theta = rng.uniform(0.0, np.pi)
+            phase = rng.uniform(0.0, 2.0 * np.pi)
+            f = f + 0.08 * np.sin(2.0 * np.pi * (x * np.cos(theta) + y * np.sin(theta)) / period + phase)
+        img1 = np.clip(f + rng.uniform(-0.02, 0.02, size=(h, w)), 0.0, 1.0).astype(np.float32)
+        img2 = np.clip(img1 + rng.normal(0.0, 0.01, size=(h, w)), 0.0, 1.0).astype(np.float32)
+        a, b = img1.astype(np.float64), img2.astype(np.float64)
+        mu1, mu2 = _box5_symmetric(a), _box5_symmetric(b)
+        s11, s22, s12 = _box5_symmetric(a * a), _box5_symmetric(b * b), _box5_symmetric(a * b)
+        out.append([np.ascontiguousarray(p, dtype=np.float32) for p in (img1, img2, mu1, mu2, s11, s22, s12)])
+    return out

@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.vqm_graph_destroy.argtypes = [c_void_p]
         L.vqm_graph_destroy.restype = None
         L.vqm_ssim_frame_noalloc.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p]
+        L.vqm_ss2_channel_sums.argtypes = [ctypes.POINTER(c_void_p), c_int, c_int, c_int, c_double_p]
+        L.vqm_debug_pair_ops.argtypes = [c_int, c_void_p, c_void_p, c_void_p, c_int]
         L.vqm_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -258,6 +260,49 @@ def vqm_ssim_frame_noalloc(ref, dis, bpc: int, score, stream=None) -> None:
         raise TypeError(f"unsupported score buffer {type(score)!r}")
     _check(lib().vqm_ssim_frame_noalloc(pr, pd, w, h, int(bpc), sp, _stream_handle(stream)),
            "vqm_ssim_frame_noalloc")
+
+
+SS2_PLANES = ("img1", "img2", "mu1", "mu2", "s11", "s22", "s12")
+
+
+def vqm_ss2_channel_sums(channels) -> np.ndarray:
+    """The six ssimulacra2 sums per channel (array [nch, 6]).
+
+    ``channels`` is a list of 1..3 channels, each a sequence of seven float32
+    device tensors in the order of ``SS2_PLANES``, all of one (h, w) shape.
+    """
+    import torch
+    nch = len(channels)
+    ptrs = (ctypes.c_void_p * (7 * nch))()
+    h = w = None
+    for c, planes in enumerate(channels):
+        if len(planes) != 7:
+            raise ValueError("seven planes per channel")
+        for p, t in enumerate(planes):
+            if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2 or not t.is_contiguous():
+                raise TypeError("planes are contiguous 2-D float32 tensors")
+            if h is None:
+                h, w = t.shape
+            elif tuple(t.shape) != (h, w):
+                raise ValueError("all planes must have one shape")
+            ptrs[c * 7 + p] = t.data_ptr()
+    out = np.empty((nch, 6), np.float64)
+    _check(lib().vqm_ss2_channel_sums(ptrs, nch, int(w), int(h), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))),
+           "vqm_ss2_channel_sums")
+    return out
+
+
+def vqm_debug_pair_ops(op: int, a, b) -> np.ndarray:
+    """op (0 two_sum, 1 two_prod, 2 ff_add, 3 ff_mul, 4 ff_div) on the device
+    over float32 pair arrays a, b of shape [n, 2] (hi, lo); returns [n, 2]."""
+    a = np.ascontiguousarray(a, np.float32)
+    b = np.ascontiguousarray(b, np.float32)
+    if a.ndim != 2 or a.shape[1] != 2 or a.shape != b.shape:
+        raise ValueError("pair arrays of shape [n, 2]")
+    out = np.empty_like(a)
+    _check(lib().vqm_debug_pair_ops(int(op), a.ctypes.data, b.ctypes.data, out.ctypes.data, a.shape[0]),
+           "vqm_debug_pair_ops")
+    return out
 
 
 def _stream_handle(stream):

@@ -384,6 +384,43 @@ VQM_API int vqm_debug_pyramid_batch(vqm_ctx *ctx, const void *const *refs, const
 VQM_API int vqm_ssim_frame_noalloc(const void *ref, const void *dis, int w, int h, int bpc, double *score,
                                    void *hip_stream);
 
+/* ---- ssimulacra2: the per-scale statistics on the device ---- */
+
+/* The six ssimulacra2 sums of nch (1..3) channels at one scale, computed on
+ * the device without fp64 and read back once ("Research-1363: Device-resident
+ * ssimulacra2 and a single-wait MS-SSIM on SYCL", Findings 3-4).
+ *   planes  7 * nch device pointers of the current device, channel by
+ *           channel: img1, img2 (the two images), mu1, mu2 (their blurred
+ *           means), s11, s22, s12 (the blurred products img1 img1, img2 img2,
+ *           img1 img2); fp32, w x h, tightly packed.  Every pixel must have
+ *           (s11 - mu1^2) + (s22 - mu2^2) + 0.0009 > 0 (true of any blur
+ *           with non-negative weights, which keeps the variances >= 0).
+ *   sums    6 * nch doubles (host memory): per channel
+ *           { sum d, sum d^4, sum art, sum art^4, sum det, sum det^4 } with,
+ *           per pixel, num_m = 1 - (mu1 - mu2)^2,
+ *           num_s = 2 (s12 - mu1 mu2) + 0.0009, denom_s = (s11 - mu1^2) +
+ *           (s22 - mu2^2) + 0.0009 (fp32, in this order),
+ *           d = max(1 - num_m num_s / denom_s, 0),
+ *           e = (1 + |img2 - mu2|) / (1 + |img1 - mu1|) - 1,
+ *           art = max(e, 0), det = max(-e, 0).
+ * Each term is an exact fp32 pair (two_prod, two-quotient ff_div, pair
+ * products for the fourth powers) and each sum runs through a fixed tree —
+ * a fixed strided subset of pixels per thread, a tree per workgroup, one
+ * workgroup per channel over the partials — whose shape depends only on
+ * w * h: the sums are bitwise repeatable and within about 1e-12 relative of
+ * the exact sums.  Blocking: two launches on a library-owned blocking stream
+ * and one wait.  -EINVAL for NULL pointers, a bad size or channel count, or
+ * planes that are not device memory of the current device. */
+VQM_API int vqm_ss2_channel_sums(const float *const *planes, int nch, int w, int h, double *sums);
+
+/* The fp32-pair operations of vqm_ss2_channel_sums run elementwise on the
+ * device, for the bit-exactness tests: out[i] = op(a[i], b[i]) over n
+ * (1..2^24) pairs stored (hi, lo) interleaved in host arrays of 2n floats.
+ * op: 0 two_sum(a.hi, b.hi), 1 two_prod(a.hi, b.hi), 2 ff_add, 3 ff_mul,
+ * 4 ff_div.  Every step is a correctly rounded fp32 operation, so the
+ * results are unique.  Blocking. */
+VQM_API int vqm_debug_pair_ops(int op, const float *a, const float *b, float *out, int n);
+
 /* Message of the last failed call on this thread ("" if none). */
 VQM_API const char *vqm_last_error(void);
 
