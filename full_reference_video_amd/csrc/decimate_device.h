@@ -12,8 +12,11 @@
 //
 // Three code paths compute that same exact sum:
 //
-//  * general_block — any s <= 128: each product is formed in fp32 and the
-//    products are summed exactly in fp64 (the bound is at the function).
+//  * general_rows_block — any s <= 128: each product's exact integer count
+//    of units, formed with one fused multiply-add, summed as integers over
+//    the window into the int64 count of 2^-52 units (the bound is at the
+//    function); lanes read consecutive columns.  No fp64 anywhere, as the
+//    ADR's contract for the decimation asks.
 //
 //  * pow2_scalar_block — s = 2^k on planes whose rows are not 16-byte
 //    aligned: the plain integer sum of the raw samples, read one by one.
@@ -58,74 +61,158 @@ __device__ __forceinline__ int mirror(int i, int n) {
 
 // ------------------------------------------------------------ general path
 
-// One 256-thread block of the general kernel: outputs (64 bx + lane,
-// 4 by + wave).
+// Raw columns one workgroup of the general path covers per output row (four
+// per thread of 256), and the windows that makes: K windows of s columns,
+// K s <= kGenCols, at most one window per thread.
+constexpr int kGenThreads = 256;
+constexpr int kGenJ = 4;
+constexpr int kGenCols = kGenJ * kGenThreads;
+__host__ __device__ inline int gen_windows_per_block(int s) {
+    const int k = kGenCols / s;
+    return k < 1 ? 1 : (k > kGenThreads ? kGenThreads : k);
+}
+// LDS ints the general path needs: per plane a column's raw sum and its
+// error sum.
+constexpr int kGenLdsInts = 4 * kGenCols;
+
+// The s rows of a window band, summed per column.  sr: the raw samples (exact
+// integers); er: the errors raw * m - fl(raw * m) of the products by the
+// tap's significand m (exact integers, |sum| <= 2^22, so exact in fp32).
 template <typename T>
-__device__ __forceinline__ void general_block(const DecimateFrame &fr, int bx, int by, int w, int h, int bpc,
-                                              int s, float tap, int dec_w, int dec_h, int opitch, bool packed) {
+struct GenColumns {
+    uint32_t sr[kGenJ], sd[kGenJ];
+    float er[kGenJ], ed[kGenJ];
+    // Rows are loaded in groups of U before any of them is added, so the
+    // group's 8 U loads are in flight together (the compiler keeps loads and
+    // arithmetic in source order row by row otherwise).
+    template <int U>
+    __device__ __forceinline__ void add_rows(const T *__restrict__ rrow, const T *__restrict__ drow, size_t w,
+                                             const int (&col)[kGenJ], float m) {
+        uint32_t a[U][kGenJ], d[U][kGenJ];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < kGenJ; ++j) {
+                a[u][j] = rrow[u * w + col[j]];
+                d[u][j] = drow[u * w + col[j]];
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < kGenJ; ++j) {
+                const float fa = (float)a[u][j], fd = (float)d[u][j];
+                const float qa = fa * m, qd = fd * m;
+                er[j] += fmaf(fa, m, -qa);
+                ed[j] += fmaf(fd, m, -qd);
+                sr[j] += a[u][j];
+                sd[j] += d[u][j];
+            }
+    }
+};
+
+// One workgroup of the general path: windows X0 .. X0 + K - 1 of output row Y
+// (X0 = seg K), any s <= 128.
+//
+// The exact window sum without fp64: with tap = M 2^(e - 23) (M its 24-bit
+// significand) every product is fl(raw * 2^-(bpc-8) * tap) = q 2^E with
+// q = fl(raw * M) and E = e - 23 - (bpc - 8) (scaling by a power of two
+// commutes with the rounding).  raw * M is an integer below 2^40, so q is one
+// too and its error r = raw * M - q, formed exactly by one fused multiply-add,
+// is an integer with |r| <= 2^15.  The window's sum of q is therefore the
+// integer M * sum(raw) - sum(r), exact in int64 (below 2^54); shifted into
+// units of 2^-52 (the shift E + 52 is >= 7) it is the pages' int64 window
+// sum, converted once to fp32.  Per column the s errors add exactly in fp32
+// (|sum| <= 2^22, integers), then as int32 over the window (|sum| <= 2^29).
+//
+// Layout: thread t owns the virtual columns cs + t + 256 j (j < 4) of the
+// band (cs = X0 s - s/2), each read from its mirrored raw column, so a wave's
+// loads of one raw row are consecutive samples.  It sums its columns over the
+// s rows of the band (the same rows for the whole workgroup: a scalar row
+// pointer, four rows of loads in flight), the column sums meet in LDS, and
+// thread k forms window X0 + k from its s consecutive virtual columns.
+template <typename T>
+__device__ __forceinline__ void general_rows_block(const DecimateFrame &fr, int seg, int Y, int w, int h, int bpc,
+                                                   int s, float tap, int dec_w, int opitch, bool packed,
+                                                   int *lds) {
     const T *__restrict__ ref = static_cast<const T *>(fr.ref);
     const T *__restrict__ dis = static_cast<const T *>(fr.dis);
-    const int X = bx * 64 + (threadIdx.x & 63);
-    const int Y = by * 4 + (threadIdx.x >> 6);
-    if (X >= dec_w || Y >= dec_h) return;
-    const int x0 = X * s - s / 2, y0 = Y * s - s / 2;
-    // The exact sum of the fp32 products raw * tap, accumulated in fp64: every
-    // product is a multiple of ulp(tap) = 2^(e - 23) (tap in [2^e, 2^(e+1)),
-    // e = -ceil(2 log2 s)) and the window's sum stays below 2^bpc, so every
-    // partial sum is an integer multiple of ulp(tap) below
-    // 2^(bpc + 23 + ceil(2 log2 s)) <= 2^53 for bpc <= 16 and s <= 128: fp64
-    // holds it exactly, as the int64 count of 2^-52 units does.
-    // Every partial sum of any subset of the products is exact too, so the
-    // order of the additions is free: four independent sums per plane keep
-    // four loads in flight.
-    double ar = 0.0, ad = 0.0;
-    if (x0 >= 0 && x0 + s <= w && y0 >= 0 && y0 + s <= h) {
-        const T *pr = ref + (size_t)y0 * (size_t)w + x0;
-        const T *pd = dis + (size_t)y0 * (size_t)w + x0;
-        double a4[4] = {0.0, 0.0, 0.0, 0.0}, d4[4] = {0.0, 0.0, 0.0, 0.0};
-        for (int j = 0; j < s; ++j, pr += w, pd += w) {
-            int i = 0;
-            for (; i + 4 <= s; i += 4) {
-                T rv[4], dv[4];
+    const int K = gen_windows_per_block(s);
+    const int X0 = seg * K;
+    const int ncols = K * s;
+    const int cs = X0 * s - s / 2;
+    const int t = threadIdx.x;
+    const uint32_t tb = __float_as_uint(tap);
+    const uint32_t m_int = (tb & 0x7fffffu) | 0x800000u;
+    const float m = (float)m_int;  // exact: below 2^24
+    const int shift = (int)((tb >> 23) & 0xffu) - 127 - 23 - (bpc - 8) + 52;
+
+    // Every load is unconditional: a column the thread does not own reads a
+    // mirrored column in the plane, and its sums are never stored.
+    int col[kGenJ];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    rv[k] = pr[i + k];
-                    dv[k] = pd[i + k];
-                }
+    for (int j = 0; j < kGenJ; ++j) col[j] = mirror(cs + t + kGenThreads * j, w);
+    GenColumns<T> acc;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    a4[k] += (double)((float)rv[k] * tap);
-                    d4[k] += (double)((float)dv[k] * tap);
-                }
-            }
-            for (; i < s; ++i) {
-                a4[0] += (double)((float)pr[i] * tap);
-                d4[0] += (double)((float)pd[i] * tap);
-            }
+    for (int j = 0; j < kGenJ; ++j) {
+        acc.sr[j] = acc.sd[j] = 0u;
+        acc.er[j] = acc.ed[j] = 0.f;
+    }
+    const int y0 = Y * s - s / 2;
+    if (y0 >= 0 && y0 + s <= h) {
+        // Inside the plane: rows y0 .. y0 + s - 1, no mirror.
+        const T *rrow = ref + (size_t)y0 * (size_t)w, *drow = dis + (size_t)y0 * (size_t)w;
+        int r = 0;
+        for (; r + 4 <= s; r += 4, rrow += 4 * (size_t)w, drow += 4 * (size_t)w)
+            acc.template add_rows<4>(rrow, drow, (size_t)w, col, m);
+        // the last s % 4 rows as one group as well
+        switch (s - r) {
+        case 3: acc.template add_rows<3>(rrow, drow, (size_t)w, col, m); break;
+        case 2: acc.template add_rows<2>(rrow, drow, (size_t)w, col, m); break;
+        case 1: acc.template add_rows<1>(rrow, drow, (size_t)w, col, m); break;
+        default: break;
         }
-        ar = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-        ad = (d4[0] + d4[1]) + (d4[2] + d4[3]);
     } else {
-        for (int j = 0; j < s; ++j) {
-            const size_t row = (size_t)mirror(y0 + j, h) * (size_t)w;
-            for (int i = 0; i < s; ++i) {
-                const int xx = mirror(x0 + i, w);
-                ar += (double)((float)ref[row + xx] * tap);
-                ad += (double)((float)dis[row + xx] * tap);
-            }
+        for (int r = 0; r < s; ++r) {
+            const size_t row = (size_t)mirror(y0 + r, h) * (size_t)w;
+            acc.template add_rows<1>(ref + row, dis + row, (size_t)w, col, m);
         }
     }
-    const size_t o = (size_t)Y * opitch + X;
-    if (packed) {
-        // s = 2^k: tap = 2^-2k and the sum times s^2 is the raw integer sum.
-        const double ss = (double)s * (double)s;
-        static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)(ar * ss);
-        static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)(ad * ss);
-        return;
+    int *col_sr = lds, *col_sd = lds + kGenCols, *col_er = lds + 2 * kGenCols, *col_ed = lds + 3 * kGenCols;
+#pragma unroll
+    for (int j = 0; j < kGenJ; ++j) {
+        const int v = t + kGenThreads * j;
+        if (v < ncols) {
+            col_sr[v] = (int)acc.sr[j];
+            col_sd[v] = (int)acc.sd[j];
+            col_er[v] = (int)acc.er[j];
+            col_ed[v] = (int)acc.ed[j];
+        }
     }
-    // One rounding to fp32, then the exact scaling of the samples to 8 bits.
-    static_cast<float *>(fr.out_ref)[o] = ldexpf((float)ar, 8 - bpc);
-    static_cast<float *>(fr.out_dis)[o] = ldexpf((float)ad, 8 - bpc);
+    __syncthreads();
+    const int X = X0 + t;
+    if (t < K && X < dec_w) {
+        int sumr = 0, sumd = 0, errr = 0, errd = 0;
+        for (int i = 0; i < s; ++i) {
+            sumr += col_sr[t * s + i];
+            sumd += col_sd[t * s + i];
+            errr += col_er[t * s + i];
+            errd += col_ed[t * s + i];
+        }
+        const size_t o = (size_t)Y * opitch + X;
+        if (packed) {
+            // s = 2^k: every product is exact and the sum is sum(raw) 2^-2k.
+            static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)sumr;
+            static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)sumd;
+        } else {
+            const long long qr = (long long)m_int * (long long)(uint32_t)sumr - (long long)errr;
+            const long long qd = (long long)m_int * (long long)(uint32_t)sumd - (long long)errd;
+            // the int64 count of 2^-52 units, one rounding to fp32, then the
+            // exact power of two
+            static_cast<float *>(fr.out_ref)[o] = ldexpf((float)(qr << shift), -52);
+            static_cast<float *>(fr.out_dis)[o] = ldexpf((float)(qd << shift), -52);
+        }
+    }
+    __syncthreads();  // the LDS is reused by the workgroup's next role or unit
 }
 
 // One 256-thread block of the power-of-two path for planes whose rows are not

@@ -46,10 +46,12 @@ constexpr int kDecWaves = kNT / 64;            // waves per decimation workgroup
 
 // ------------------------------------------------------------ decimation policies
 
+// Each policy's run() gets the workgroup's LDS buffer (the map tile's, which
+// a workgroup of the decimation role does not otherwise use).
 struct DecNone {
     static constexpr bool kStreams = false;  // whether the decimation is the wide HBM stream (see map_tile)
     static int blocks_per_frame(const StepGeometry &) { return 0; }
-    __device__ static void run(const DecimateFrame &, int, const StepGeometry &) {}
+    __device__ static void run(const DecimateFrame &, int, const StepGeometry &, float *) {}
 };
 
 template <typename T, int S>
@@ -75,7 +77,7 @@ struct DecPow2 {
         const int waves = (waves_per_row(g) * g.dec_h + upw - 1) / upw;
         return (waves + kDecWaves - 1) / kDecWaves;
     }
-    __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
+    __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g, float *) {
         const int wpr = waves_per_row(g), upw = units_per_wave(g);
         const int u0 = (b * kDecWaves + (int)(threadIdx.x >> 6)) * upw;
 #pragma unroll 1
@@ -87,15 +89,20 @@ struct DecPow2 {
     }
 };
 
+// Any other scale: one workgroup per (output row, segment of windows).
 template <typename T>
 struct DecGeneral {
     static constexpr bool kStreams = false;
-    __host__ __device__ static int blocks_x(const StepGeometry &g) { return (g.dec_w + 63) / 64; }
-    static int blocks_per_frame(const StepGeometry &g) { return blocks_x(g) * ((g.dec_h + 3) / 4); }
-    __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
-        const int bx = b % blocks_x(g), by = b / blocks_x(g);
-        dec::general_block<T>(fr, bx, by, g.w, g.h, g.bpc, g.s, g.tap, g.dec_w, g.dec_h, g.dec_pitch,
-                              g.packed != 0);
+    __host__ __device__ static int segments(const StepGeometry &g) {
+        const int k = dec::gen_windows_per_block(g.s);
+        return (g.dec_w + k - 1) / k;
+    }
+    static int blocks_per_frame(const StepGeometry &g) { return segments(g) * g.dec_h; }
+    __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g, float *smem) {
+        const int segs = segments(g);
+        const int Y = b / segs;
+        dec::general_rows_block<T>(fr, b - Y * segs, Y, g.w, g.h, g.bpc, g.s, g.tap, g.dec_w, g.dec_pitch,
+                                   g.packed != 0, reinterpret_cast<int *>(smem));
     }
 };
 
@@ -105,7 +112,7 @@ struct DecPow2Scalar {
     static constexpr bool kStreams = false;
     __host__ __device__ static int blocks_x(const StepGeometry &g) { return (g.dec_w + 63) / 64; }
     static int blocks_per_frame(const StepGeometry &g) { return blocks_x(g) * ((g.dec_h + 3) / 4); }
-    __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g) {
+    __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g, float *) {
         const int bx = b % blocks_x(g), by = b / blocks_x(g);
         dec::pow2_scalar_block<T, S>(fr, bx, by, g.w, g.h, g.dec_w, g.dec_h, g.dec_pitch, g.post, g.packed != 0);
     }
@@ -129,11 +136,18 @@ static_assert(kLoopLdsFloats >= tile_lds_floats<kTW, kTH, kNP>(), "the capped ti
 static_assert(kLoopWorkgroupsPerCu * (kLoopLdsFloats * 4 + 1024) <= 160 * 1024,
               "the capped buffer must still let kLoopWorkgroupsPerCu workgroups share a CU");
 
-template <typename TIn, bool kCapped>
+// LDS floats of a step workgroup: the map tile's buffer (oversized on
+// purpose in the capped layout), which the general decimation borrows.
+template <bool kCapped>
+constexpr int step_lds_floats() {
+    return kCapped ? kLoopLdsFloats : tile_lds_floats<kTW, kTH, kNP>();
+}
+static_assert(tile_lds_floats<kTW, kTH, kNP>() >= dec::kGenLdsInts, "the general decimation borrows the tile buffer");
+
+template <typename TIn>
 __device__ __forceinline__ void map_tile(const SsimFrame &fr, int tile, const StepGeometry &g, int pitch,
-                                         float unit, bool vec4, const Taps &taps) {
+                                         float unit, bool vec4, const Taps &taps, float *lds) {
     constexpr int IH = kTH + 10, IP = in_pitch<kTW>();
-    __shared__ __attribute__((aligned(16))) float lds[kCapped ? kLoopLdsFloats : tile_lds_floats<kTW, kTH, kNP>()];
     __shared__ double red[1][kNT / 64];
     float *sx = lds, *sy = lds + IH * IP;
 
@@ -221,6 +235,7 @@ constexpr long long kInterleaveBytesPerTile = 20 * 1024;
 template <class Dec, typename TIn, bool kLoopMap>
 __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, StepLayout lay, int map_pitch,
                                                  float unit, int vec4, Taps taps) {
+    __shared__ __attribute__((aligned(16))) float smem[step_lds_floats<kLoopMap && Dec::kStreams>()];
     const int x = (int)(blockIdx.x & 7u);
     int q = (int)(blockIdx.x >> 3);
     if (!kLoopMap && lay.interleave) {
@@ -236,7 +251,7 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
                 const int m = x * lay.map_per_xcd + mq;
                 if (mq < lay.map_per_xcd && m < r.n_map * map_pf) {
                     const int f = m / map_pf;
-                    map_tile<TIn, kLoopMap && Dec::kStreams>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                    map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps, smem);
                 }
                 return;
             }
@@ -244,7 +259,7 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
             const int d = x * lay.dec_per_xcd + (q - mq);
             if (d < r.n_dec * dec_pf) {
                 const int f = d / dec_pf;
-                Dec::run(r.dec.f[f], d - f * dec_pf, g);
+                Dec::run(r.dec.f[f], d - f * dec_pf, g, smem);
             }
             return;
         }
@@ -261,14 +276,14 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
 #pragma unroll 1
             for (int m = m0 + q; m < m1; m += lay.map_wg) {
                 const int f = m / map_pf;
-                map_tile<TIn, kLoopMap && Dec::kStreams>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps, smem);
                 __syncthreads();  // the next tile reuses the LDS
             }
         } else {
             const int m = m0 + q;
             if (m < m1) {
                 const int f = m / map_pf;
-                map_tile<TIn, kLoopMap && Dec::kStreams>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps);
+                map_tile<TIn>(r.map.f[f], m - f * map_pf, g, map_pitch, unit, vec4 != 0, taps, smem);
             }
         }
         return;
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(kNT) void ssim_step(StepRoles r, StepGeometry g, St
         const int d = x * lay.dec_per_xcd + q;
         if (d < r.n_dec * dec_pf) {
             const int f = d / dec_pf;
-            Dec::run(r.dec.f[f], d - f * dec_pf, g);
+            Dec::run(r.dec.f[f], d - f * dec_pf, g, smem);
         }
         return;
     }
