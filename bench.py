@@ -239,6 +239,13 @@ def main():
     ap.add_argument("--frame", default="", metavar="WxHxBPC",
                     help="score frames of this size and depth instead (the 2160p workload's recipe, 16 frames; for "
                          "sizes outside the workloads, e.g. 1280x720x8, 2560x1440x10 or 7680x4320x10)")
+    ap.add_argument("--blocking", action="store_true",
+                    help="score the stream one blocking call per frame (vqm_ssim_frame / vqm_msssim_frame on the "
+                         "device frames: one submit, one wait, one 8-byte read-back each), reported under its own "
+                         "metric name")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
+                    help="only time the library's streaming 16-byte non-temporal read over MIB MiB of device memory "
+                         "(the HBM read ceiling of the decimation's loads) and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB 20 times (a kernel of known "
                          "traffic, to calibrate the FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -253,6 +260,19 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 20}), flush=True)
+        return
+
+    if args.read_probe:
+        import torch
+
+        from full_reference_video_amd import vqm
+        n = args.read_probe << 20
+        buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        torch.cuda.synchronize()
+        ms = vqm.vqm_debug_read_probe(buf, reps=20)
+        gbps = n / (ms * 1e-3) / 1e9
+        print(json.dumps({"read_probe_bytes": n, "kernel_ms": round(ms, 4), "GBps": round(gbps, 1),
+                          "frac_of_peak": round(gbps / HBM_PEAK_GBS, 4)}), flush=True)
         return
 
     if args.gpus != 1:
@@ -363,6 +383,20 @@ def main():
             if sc.tolist() != ref_scores:
                 raise RuntimeError("a replay differs from the eager pass")
         graph.close()
+    elif args.blocking:
+        fn = vqm.vqm_msssim_frame if wl.metric == "ms_ssim" else vqm.vqm_ssim_frame
+        # the blocking calls' pooled context allocates its slot on first use
+        for r, d in dev:
+            fn(r, d, wl.bpc)
+        log(f"timed {args.reps} x {args.steps} passes over {wl.frames} frames, one blocking call per frame")
+        for _ in range(args.reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            sc = [fn(r, d, wl.bpc) for r, d in zip(stream_set_r, stream_set_d)]
+            torch.cuda.synchronize()
+            runs.append(time.perf_counter() - t0)
+            if ref_scores is not None and sc != ref_scores * args.steps:
+                raise RuntimeError("scores changed between passes")
     else:
         log(f"timed {args.reps} x {args.steps} passes over {wl.frames} frames, batch {args.batch}, "
             f"{args.streams} streams, lag {lag}")
@@ -377,7 +411,7 @@ def main():
     el = sorted(runs)[len(runs) // 2]  # the median run
     fps = frames / el
     marginal_us = None
-    if not args.graph and frames > 2:
+    if not args.graph and not args.blocking and frames > 2:
         # The pages' per-frame figure, (t(N) - t(2)) / (N - 2): the same
         # stream over its first two frames, timed as often, takes out the
         # pipeline's fill and drain and the loop's start.
@@ -456,7 +490,8 @@ def main():
         "metric": ("frames/sec and achieved HBM GB/s (% of peak), float_ssim at 3840x2160"
                    if wl.index == 4 and not args.frame else f"frames/sec, {wl.name}")
                   + ("" if args.host_input == "none" else f", end to end from {args.host_input} host frames")
-                  + (", recorded-pass replays" if args.graph else ""),
+                  + (", recorded-pass replays" if args.graph else "")
+                  + (", one blocking call per frame" if args.blocking else ""),
         "value": round(fps, 1),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -471,7 +506,7 @@ def main():
         "config": {"workload": wl.name, "input": "hbm" if args.host_input == "none" else args.host_input + " host",
                    "w": wl.w, "h": wl.h, "bpc": wl.bpc, "frames_per_step": wl.frames,
                    "scale": s, "batch": args.batch, "streams": args.streams, "lag": lag,
-                   "mode": "graph replay" if args.graph else "stream",
+                   "mode": "graph replay" if args.graph else ("blocking calls" if args.blocking else "stream"),
                    "path_GBps": round(alg * fps / 1e9, 1)},
         "runs": {"n": len(runs), "frames_per_s_min": round(frames / max(runs), 1),
                  "frames_per_s_max": round(frames / min(runs), 1),

@@ -184,6 +184,15 @@ hipError_t launch_ss2_sums(const float *const *planes, int nch, long long n, voi
 // 3 ff_mul, 4 ff_div) over n pairs of device arrays, for the tests.
 hipError_t launch_pair_ops(int op, const float *a, const float *b, float *out, int n, hipStream_t stream);
 
+// ---------------------------------------------------------------- inspection
+
+// A streaming read of bytes / 16 16-byte vectors of buf (non-temporal loads,
+// one workgroup of 256 threads per 64 KiB); sink receives one word per
+// workgroup (read_probe_blocks of them).
+long long read_probe_blocks(long long bytes);
+hipError_t launch_read_probe(const void *buf, long long bytes, uint32_t *sink, hipStream_t stream,
+                             const KernelTimer &timer);
+
 // ---------------------------------------------------------------- shared
 
 // XCD-aware block order.  The dispatcher hands consecutive workgroups of a

@@ -963,6 +963,45 @@ int ss2_sums(const float *const *planes, int nch, int w, int h, double *sums) {
     return 0;
 }
 
+// The read-ceiling probe: `reps` timed launches of the streaming read over a
+// device buffer, on a leased context's stream; the mean kernel time.
+int read_probe(const void *buf, long long bytes, int reps, double *ms) {
+    if (!buf || !ms) return fail(-EINVAL, "NULL argument");
+    if (bytes < 16 || reps < 1) return fail(-EINVAL, "need at least 16 bytes and one repetition");
+    Lease lease;
+    int rc = lease_ctx(lease);
+    if (rc) return rc;
+    vqm_ctx *ctx = lease.ctx;
+    PtrKind k;
+    rc = classify(buf, ctx->device, &k);
+    if (rc) return rc;
+    if (k != PTR_DEVICE) return fail(-EINVAL, "the probe reads device memory only");
+    const long long blocks = vqm::read_probe_blocks(bytes);
+    if (blocks > 0x7fffffffLL) return fail(-EINVAL, "%lld bytes are too many for one probe launch", bytes);
+    uint32_t *sink = nullptr;
+    HIP_TRY_ALLOC(hipMalloc(&sink, (size_t)blocks * sizeof(uint32_t)));
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    hipError_t e = hipEventCreate(&ev[0]);
+    if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+    double total = 0.0;
+    for (int r = 0; r <= reps && e == hipSuccess; ++r) {  // launch 0 warms up
+        vqm::KernelTimer kt;
+        kt.start = ev[0];
+        kt.stop = ev[1];
+        e = vqm::launch_read_probe(buf, bytes, sink, ctx->stream, kt);
+        if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+        float t = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[0], ev[1]);
+        if (r > 0) total += t;
+    }
+    for (hipEvent_t x : ev)
+        if (x) (void)hipEventDestroy(x);
+    (void)hipFree(sink);
+    if (e != hipSuccess) return fail(-EIO, "read probe: %s", hipGetErrorString(e));
+    *ms = total / reps;
+    return 0;
+}
+
 int pair_ops(int op, const float *a, const float *b, float *out, int n) {
     if (!a || !b || !out) return fail(-EINVAL, "NULL argument");
     if (op < 0 || op > 4) return fail(-EINVAL, "pair operation %d outside 0..4", op);
@@ -1562,6 +1601,10 @@ int vqm_debug_pyramid_batch(vqm_ctx *ctx, const void *const *refs, const void *c
 
 int vqm_ss2_channel_sums(const float *const *planes, int nch, int w, int h, double *sums) {
     return ss2_sums(planes, nch, w, h, sums);
+}
+
+int vqm_debug_read_probe(const void *buf, long long bytes, int reps, double *ms) {
+    return read_probe(buf, bytes, reps, ms);
 }
 
 int vqm_debug_pair_ops(int op, const float *a, const float *b, float *out, int n) {

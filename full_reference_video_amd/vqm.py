@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
         L.vqm_ssim_frame_noalloc.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p]
         L.vqm_ss2_channel_sums.argtypes = [ctypes.POINTER(c_void_p), c_int, c_int, c_int, c_double_p]
         L.vqm_debug_pair_ops.argtypes = [c_int, c_void_p, c_void_p, c_void_p, c_int]
+        L.vqm_debug_read_probe.argtypes = [c_void_p, ctypes.c_longlong, c_int, c_double_p]
         L.vqm_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -303,6 +304,15 @@ def vqm_debug_pair_ops(op: int, a, b) -> np.ndarray:
     _check(lib().vqm_debug_pair_ops(int(op), a.ctypes.data, b.ctypes.data, out.ctypes.data, a.shape[0]),
            "vqm_debug_pair_ops")
     return out
+
+
+def vqm_debug_read_probe(buf, reps: int = 20) -> float:
+    """Mean milliseconds of the library's streaming read over a device
+    tensor's bytes."""
+    ms = ctypes.c_double()
+    _check(lib().vqm_debug_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), int(reps),
+                                      ctypes.byref(ms)), "vqm_debug_read_probe")
+    return ms.value
 
 
 def _stream_handle(stream):

@@ -421,6 +421,14 @@ VQM_API int vqm_ss2_channel_sums(const float *const *planes, int nch, int w, int
  * results are unique.  Blocking. */
 VQM_API int vqm_debug_pair_ops(int op, const float *a, const float *b, float *out, int n);
 
+/* A streaming read of `bytes` (>= 16) of device memory `buf` with 16-byte
+ * non-temporal loads, one workgroup of 256 threads per 64 KiB, timed
+ * with HIP events around each of `reps` launches (after one untimed one);
+ * *ms receives the mean kernel time.  The HBM read ceiling that the
+ * decimation's loads can reach on this GPU, for the measurements beside the
+ * published peak.  Blocking; allocates a small sink. */
+VQM_API int vqm_debug_read_probe(const void *buf, long long bytes, int reps, double *ms);
+
 /* Message of the last failed call on this thread ("" if none). */
 VQM_API const char *vqm_last_error(void);
 
