@@ -215,43 +215,86 @@ __device__ __forceinline__ void general_rows_block(const DecimateFrame &fr, int 
     __syncthreads();  // the LDS is reused by the workgroup's next role or unit
 }
 
+// Output rows each thread of the scalar power-of-two path sums (of one output
+// column): enough that a thread has 32 or more raw samples of both planes in
+// flight at s = 2 and 4 (a workgroup with one 2 x 2 window per thread reads
+// too little to hide the memory latency).
+template <int S>
+__host__ __device__ constexpr int scalar_rows_per_thread() {
+    return S == 2 ? 4 : (S == 4 ? 2 : 1);
+}
+
 // One 256-thread block of the power-of-two path for planes whose rows are not
-// 16-byte aligned (odd widths): outputs (64 bx + lane, 4 by + wave), each
-// the integer sum of its S x S raw samples, read one by one (every product
-// v * tap is exact at s = 2^k, so the window sum is sum(raw) * post).  The
-// mirrored row and column of each window position are found once.
+// 16-byte aligned (odd widths): output column 64 bx + lane, output rows
+// RPT (4 by + wave) .. + RPT - 1, each the integer sum of its S x S raw
+// samples, read one by one (every product v * tap is exact at s = 2^k, so
+// the window sum is sum(raw) * post).  The mirrored rows and columns are
+// found once, and every sample of the thread's windows is loaded before any
+// is added.
 template <typename T, int S>
 __device__ __forceinline__ void pow2_scalar_block(const DecimateFrame &fr, int bx, int by, int w, int h,
                                                   int dec_w, int dec_h, int opitch, float post, bool packed) {
+    constexpr int RPT = scalar_rows_per_thread<S>();
     const T *__restrict__ ref = static_cast<const T *>(fr.ref);
     const T *__restrict__ dis = static_cast<const T *>(fr.dis);
     const int X = bx * 64 + (threadIdx.x & 63);
-    const int Y = by * 4 + (threadIdx.x >> 6);
-    if (X >= dec_w || Y >= dec_h) return;
+    const int Y0 = (by * 4 + (threadIdx.x >> 6)) * RPT;
+    if (X >= dec_w || Y0 >= dec_h) return;
     int col[S];
-    size_t row[S];
+    size_t row[RPT * S];  // the window rows of outputs Y0 .. Y0 + RPT - 1, in order
 #pragma unroll
-    for (int i = 0; i < S; ++i) {
-        col[i] = mirror(X * S - S / 2 + i, w);
-        row[i] = (size_t)mirror(Y * S - S / 2 + i, h) * (size_t)w;
-    }
-    uint32_t ar = 0, ad = 0;
+    for (int i = 0; i < S; ++i) col[i] = mirror(X * S - S / 2 + i, w);
 #pragma unroll
-    for (int j = 0; j < S; ++j)
+    for (int q = 0; q < RPT * S; ++q) row[q] = (size_t)mirror(Y0 * S - S / 2 + q, h) * (size_t)w;
+    uint32_t ar[RPT], ad[RPT];
+    if constexpr (RPT * S * S <= 16) {
+        // All of them in flight at once (a row past the plane reads a mirrored
+        // row inside it; its output is not stored).
+        T va[RPT * S][S], vd[RPT * S][S];
 #pragma unroll
-        for (int i = 0; i < S; ++i) {
-            ar += ref[row[j] + col[i]];
-            ad += dis[row[j] + col[i]];
+        for (int q = 0; q < RPT * S; ++q)
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                va[q][i] = ref[row[q] + col[i]];
+                vd[q][i] = dis[row[q] + col[i]];
+            }
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            ar[k] = ad[k] = 0u;
+#pragma unroll
+            for (int j = 0; j < S; ++j)
+#pragma unroll
+                for (int i = 0; i < S; ++i) {
+                    ar[k] += va[k * S + j][i];
+                    ad[k] += vd[k * S + j][i];
+                }
         }
-    const size_t o = (size_t)Y * opitch + X;
-    if (packed) {
-        static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)ar;
-        static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)ad;
     } else {
-        // One rounding of the exact sum (uint32 -> fp32 is RNE), then the
-        // exact power of two.
-        static_cast<float *>(fr.out_ref)[o] = (float)ar * post;
-        static_cast<float *>(fr.out_dis)[o] = (float)ad * post;
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            ar[k] = ad[k] = 0u;
+#pragma unroll
+            for (int j = 0; j < S; ++j)
+#pragma unroll
+                for (int i = 0; i < S; ++i) {
+                    ar[k] += ref[row[k * S + j] + col[i]];
+                    ad[k] += dis[row[k * S + j] + col[i]];
+                }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        if (Y0 + k >= dec_h) break;
+        const size_t o = (size_t)(Y0 + k) * opitch + X;
+        if (packed) {
+            static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)ar[k];
+            static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)ad[k];
+        } else {
+            // One rounding of the exact sum (uint32 -> fp32 is RNE), then the
+            // exact power of two.
+            static_cast<float *>(fr.out_ref)[o] = (float)ar[k] * post;
+            static_cast<float *>(fr.out_dis)[o] = (float)ad[k] * post;
+        }
     }
 }
 
@@ -309,7 +352,49 @@ template <typename T, int S> struct Pow2Shape {
     static constexpr int CPT = G / S;                 // chunks (outputs) per lane
 };
 
-// One wave of the power-of-two kernel: wave wv of output row Y.
+// The windows of one unit from its half-chunk sums: the high half before a
+// lane's first chunk comes from the previous lane (one cross-lane shift);
+// store them.
+template <typename T, int S>
+__device__ __forceinline__ void pow2_finish(const DecimateFrame &fr, int wv, int Y, int dec_w, float post,
+                                            int opitch, bool packed, uint32_t (&lr)[Pow2Shape<T, S>::CPT],
+                                            uint32_t (&hr)[Pow2Shape<T, S>::CPT], uint32_t (&ld)[Pow2Shape<T, S>::CPT],
+                                            uint32_t (&hd)[Pow2Shape<T, S>::CPT]) {
+    constexpr int CPT = Pow2Shape<T, S>::CPT;
+    const int lane = threadIdx.x & 63;
+    const int g = 63 * wv + lane - 1;
+    if (g < 0) {
+        // Columns -s/2..-1 mirror onto 0..s/2-1: the low half of chunk 0.
+        hr[CPT - 1] = lr[0];
+        hd[CPT - 1] = ld[0];
+    }
+    // High half of the chunk just before this lane's first chunk.
+    const uint32_t pr = __shfl_up(hr[CPT - 1], 1, 64);
+    const uint32_t pd = __shfl_up(hd[CPT - 1], 1, 64);
+    if (lane == 0) return;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int X = g * CPT + k;
+        if (X < dec_w) {
+            const uint32_t tr = (k == 0 ? pr : hr[k - 1]) + lr[k];
+            const uint32_t td = (k == 0 ? pd : hd[k - 1]) + ld[k];
+            const size_t o = (size_t)Y * opitch + X;
+            if (packed) {
+                // The raw sums themselves (below 2^16 when packed).
+                static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)tr;
+                static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)td;
+            } else {
+                // One rounding (the only one: sums below 2^24 are exact),
+                // then the exact power of two.
+                static_cast<float *>(fr.out_ref)[o] = (float)tr * post;
+                static_cast<float *>(fr.out_dis)[o] = (float)td * post;
+            }
+        }
+    }
+}
+
+// One wave of the power-of-two kernel: wave wv of output row Y (rows
+// streamed: each row's loads are added as they arrive, so any S fits).
 template <typename T, int S>
 __device__ __forceinline__ void pow2_wave(const DecimateFrame &fr, int wv, int Y, int w, int h, int dec_w,
                                           float post, int opitch, bool packed) {
@@ -350,34 +435,7 @@ __device__ __forceinline__ void pow2_wave(const DecimateFrame &fr, int wv, int Y
             }
         }
     }
-    if (g < 0) {
-        // Columns -s/2..-1 mirror onto 0..s/2-1: the low half of chunk 0.
-        hr[CPT - 1] = lr[0];
-        hd[CPT - 1] = ld[0];
-    }
-    // High half of the chunk just before this lane's first chunk.
-    const uint32_t pr = __shfl_up(hr[CPT - 1], 1, 64);
-    const uint32_t pd = __shfl_up(hd[CPT - 1], 1, 64);
-    if (lane == 0) return;
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-        const int X = g * CPT + k;
-        if (X < dec_w) {
-            const uint32_t tr = (k == 0 ? pr : hr[k - 1]) + lr[k];
-            const uint32_t td = (k == 0 ? pd : hd[k - 1]) + ld[k];
-            const size_t o = (size_t)Y * opitch + X;
-            if (packed) {
-                // The raw sums themselves (below 2^16 when packed).
-                static_cast<uint16_t *>(fr.out_ref)[o] = (uint16_t)tr;
-                static_cast<uint16_t *>(fr.out_dis)[o] = (uint16_t)td;
-            } else {
-                // One rounding (the only one: sums below 2^24 are exact),
-                // then the exact power of two.
-                static_cast<float *>(fr.out_ref)[o] = (float)tr * post;
-                static_cast<float *>(fr.out_dis)[o] = (float)td * post;
-            }
-        }
-    }
+    pow2_finish<T, S>(fr, wv, Y, dec_w, post, opitch, packed, lr, hr, ld, hd);
 }
 
 }  // namespace dec

@@ -210,18 +210,22 @@ __device__ __forceinline__ float sum_of_squares(float a, float b) { return fmaf(
 // ((2 mux muy + C1)(2 sxy + C2)) / (A B).  Exactly 1 for identical planes:
 // then every x^2 + y^2 is 2 fl(x^2), and doubling commutes with each rounding
 // of the filters, so ss = 2 xy, mx = my and S = 2 sxy bit for bit.
+// Written with explicit fused multiply-adds (the library compiles with
+// contraction off): about 21 instructions.  Identity still gives exactly 1:
+// dm = 0, and v = S - 2 sxy is one rounding of an exact 0 (sxy rounds mx my
+// first, as S rounds its squares, so S = 2 sxy bit for bit).
 __device__ __forceinline__ float ssim_term4(float mx, float my, float ss, float xy) {
     const float S = ss - sum_of_squares(mx, my);
     const float sxy = xy - mx * my;
     const float ux = mx + kMomentOffset;
     const float uy = my + kMomentOffset;
     const float dm = mx - my;
-    const float A = ux * ux + uy * uy + kC1;
+    const float A = fmaf(ux, ux, fmaf(uy, uy, kC1));
     const float B = S + kC2;
-    const float v = S - (sxy + sxy);
+    const float v = fmaf(-2.0f, sxy, S);
     // One reciprocal for both quotients (A * B stays far inside fp32 range).
     const float r = rcp(A * B);
-    return (1.0f - dm * dm * (B * r)) * (1.0f - v * (A * r));
+    return fmaf(-(dm * dm), B * r, 1.0f) * fmaf(-v, A * r, 1.0f);
 }
 
 // Horizontal 11-tap pass of one item: four adjacent columns c0..c0+3 of

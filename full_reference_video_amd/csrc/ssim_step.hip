@@ -65,9 +65,11 @@ struct DecPow2 {
     // Units (row, wave-in-row) a wave takes in turn: two where a row needs
     // at most two waves (1080p), so that fewer, longer decimation workgroups
     // leave the interleaved map tiles more of the CUs (1080p step 43.0 ->
-    // 39.1 us per launch of 32 frames); one on wide rows, where the
-    // decimation is the HBM stream and a second unit per wave only delays it
-    // (2160p 179.8 -> 196.5 us).
+    // 39.1 us per launch of 32 frames; loading both units before adding
+    // either measured no faster, 39.4 -> 39.5 us, and its registers cost the
+    // 2160p step 177.7 -> 180.2 us); one on wide rows, where the decimation
+    // is the HBM stream and a second unit per wave only delays it (2160p
+    // 179.8 -> 196.5 us).
     __host__ __device__ static int units_per_wave(const StepGeometry &g) { return waves_per_row(g) <= 2 ? 2 : 1; }
     // A frame's units in row order, units_per_wave to a wave and kDecWaves
     // waves to a workgroup, so rows that need fewer waves than a workgroup
@@ -111,7 +113,10 @@ template <typename T, int S>
 struct DecPow2Scalar {
     static constexpr bool kStreams = false;
     __host__ __device__ static int blocks_x(const StepGeometry &g) { return (g.dec_w + 63) / 64; }
-    static int blocks_per_frame(const StepGeometry &g) { return blocks_x(g) * ((g.dec_h + 3) / 4); }
+    static int blocks_per_frame(const StepGeometry &g) {
+        constexpr int rows = 4 * dec::scalar_rows_per_thread<S>();  // output rows per workgroup
+        return blocks_x(g) * ((g.dec_h + rows - 1) / rows);
+    }
     __device__ static void run(const DecimateFrame &fr, int b, const StepGeometry &g, float *) {
         const int bx = b % blocks_x(g), by = b / blocks_x(g);
         dec::pow2_scalar_block<T, S>(fr, bx, by, g.w, g.h, g.dec_w, g.dec_h, g.dec_pitch, g.post, g.packed != 0);
