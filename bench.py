@@ -243,6 +243,9 @@ def main():
                     help="score the stream one blocking call per frame (vqm_ssim_frame / vqm_msssim_frame on the "
                          "device frames: one submit, one wait, one 8-byte read-back each), reported under its own "
                          "metric name")
+    ap.add_argument("--ss2", default="", metavar="WxH",
+                    help="only time the ssimulacra2 per-scale statistics (vqm_ss2_channel_sums) of three channels of "
+                         "WxH seeded planes, against the HBM roofline of its seven fp32 planes per channel, and exit")
     ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
                     help="only time the library's streaming 16-byte non-temporal read over MIB MiB of device memory "
                          "(the HBM read ceiling of the decimation's loads) and exit")
@@ -260,6 +263,42 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 20}), flush=True)
+        return
+
+    if args.ss2:
+        import numpy as np
+        import torch
+
+        from full_reference_video_amd import synth, vqm
+        sw, sh = (int(v) for v in args.ss2.lower().split("x"))
+        # Distinct plane sets, more bytes than the 256 MB last-level cache.
+        sets = max(2, -(-(300 << 20) // (3 * 7 * 4 * sw * sh)))
+        host = synth.ss2_planes(11, sw, sh, 3)
+        dev = []
+        for k in range(sets):
+            dev.append([[torch.from_numpy(p).cuda().add_(0.0) for p in ch] for ch in host])
+        torch.cuda.synchronize()
+        ref = vqm.vqm_ss2_channel_sums(dev[0])
+        for d in dev:
+            vqm.vqm_ss2_channel_sums(d)  # warm-up
+        n = max(1, args.steps)
+        runs = []
+        for _ in range(max(1, args.reps)):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(n):
+                got = vqm.vqm_ss2_channel_sums(dev[i % sets])
+            torch.cuda.synchronize()
+            runs.append((time.perf_counter() - t0) / n)
+        if not np.array_equal(vqm.vqm_ss2_channel_sums(dev[0]), ref):
+            raise RuntimeError("ssimulacra2 sums changed between calls")
+        el = sorted(runs)[len(runs) // 2]
+        alg = 3 * 7 * 4 * sw * sh
+        gbps = alg / el / 1e9
+        print(json.dumps({"metric": f"ssimulacra2 per-scale statistics, 3 channels of {sw}x{sh}, one blocking call",
+                          "value": round(1.0 / el, 1), "unit": "calls/s", "us_per_call": round(el * 1e6, 2),
+                          "algorithmic_bytes": alg, "GBps": round(gbps, 1),
+                          "hbm_frac": round(gbps / HBM_PEAK_GBS, 4), "plane_sets": sets}), flush=True)
         return
 
     if args.read_probe:
