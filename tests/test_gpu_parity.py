@@ -494,10 +494,11 @@ def test_mixed_metrics_and_sizes_in_one_context(ctx):
 
 # ------------------------------------------------------------ full workloads, bench launch shape
 
-def _score_stream(torch, pairs, bpc, metric, batch=vqm.VQM_MAX_BATCH, lag=0, n_streams=1):
+def _score_stream(torch, pairs, bpc, metric, batch=vqm.VQM_MAX_BATCH, lag=0, n_streams=1, want_lcs=False):
     """Score device-resident pairs the way bench.py times them: one context
     per torch stream, batches of VQM_MAX_BATCH frames per launch, each frame
-    collected three batches after its submit (lag 0)."""
+    collected three batches after its submit (lag 0).  With want_lcs, also
+    the 15 level means per frame (from a second pass that asks for them)."""
     dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
     fs = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], bpc)
     streams = [torch.cuda.Stream() for _ in range(n_streams)]
@@ -505,11 +506,14 @@ def _score_stream(torch, pairs, bpc, metric, batch=vqm.VQM_MAX_BATCH, lag=0, n_s
     try:
         first = vqm.vqm_score_frames(ctxs, metric, fs, batch, lag).tolist()
         again = vqm.vqm_score_frames(ctxs, metric, fs, batch, lag).tolist()
+        if want_lcs:
+            scores, lcs = vqm.vqm_score_frames(ctxs, metric, fs, batch, lag, want_lcs=True)
+            assert scores.tolist() == first, "asking for the level means changed a score"
     finally:
         for x in ctxs:
             x.close()
     assert again == first, "scores not bitwise repeatable"
-    return first
+    return (first, lcs) if want_lcs else first
 
 
 @pytest.mark.parametrize("c", [2, 3, 4])
@@ -542,22 +546,33 @@ def test_full_float_ssim_2160p_two_streams(torch_cuda):
 
 
 def test_full_msssim_workload_in_bench_launch_shape(torch_cuda):
-    # All 50 frames scored on the GPU; the oracle (seconds per 2160p frame)
-    # checks a sample of them, and every frame equals its single-frame call.
+    # All 50 frames scored on the GPU in the bench's launch shape, each score
+    # and each of its 15 level means within 5e-5 of the oracle's (stored by
+    # tests/golden/make_golden.py, which calls only the oracle: seconds per
+    # 2160p frame on one core); one frame is also recomputed by the oracle.
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "msssim_2160p8_oracle.json")) as f:
+        rec = json.load(f)["frames"]
     src = synth.FrameSource(5)
     n = src.workload.frames
     say(f"full MS-SSIM workload: generating {n} pairs")
     pairs = [src.pair(t) for t in range(n)]
     say("full MS-SSIM workload: scoring on the GPU")
-    got = _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_MS_SSIM)
+    got, lcs = _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_MS_SSIM, want_lcs=True)
     single = [vqm.vqm_msssim_frame(r, d, src.bpc) for r, d in pairs]
     assert got == single
+    worst = max(abs(got[t] - rec[str(t)]["score"]) for t in range(n))
+    worst_lcs = max(float(np.max(np.abs(lcs[t] - np.array(rec[str(t)]["lcs"])))) for t in range(n))
+    say(f"full MS-SSIM workload: largest difference from the oracle {worst:.3e} (score), {worst_lcs:.3e} (means)")
+    for t in range(n):
+        assert abs(got[t] - rec[str(t)]["score"]) <= TOL, (t, got[t], rec[str(t)]["score"])
+        assert np.all(np.abs(lcs[t] - np.array(rec[str(t)]["lcs"])) <= TOL), t
     # two contexts on two streams, as bench.py times MS-SSIM
     say("full MS-SSIM workload: two streams")
     assert _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_MS_SSIM, n_streams=2) == single
-    for t in (0, 23, n - 1):
-        say(f"full MS-SSIM workload: oracle frame {t}")
-        assert abs(got[t] - oracle.msssim(*pairs[t], src.bpc)) <= TOL, (t, got[t])
+    say("full MS-SSIM workload: oracle frame 23")
+    assert abs(got[23] - oracle.msssim(*pairs[23], src.bpc)) <= TOL, got[23]
 
 
 # ------------------------------------------------------------ enable_db

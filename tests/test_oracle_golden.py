@@ -25,3 +25,18 @@ def test_msssim_golden_small():
     score, lcs = oracle.msssim(*src.pair(1), 8, want_lcs=True)
     assert score == rec["score"]
     assert lcs.tolist() == rec["lcs"]
+
+
+def test_msssim_workload_record_matches_the_oracle():
+    # The stored record of all 50 frames of the 2160p MS-SSIM workload (which
+    # the GPU test compares every frame with) is the oracle's own output: two
+    # of its frames, recomputed here, match bit for bit.
+    with open(os.path.join(os.path.dirname(__file__), "golden", "msssim_2160p8_oracle.json")) as f:
+        rec = json.load(f)
+    src = synth.FrameSource(5)
+    assert (rec["w"], rec["h"], rec["bpc"]) == (src.w, src.h, src.bpc)
+    assert sorted(int(t) for t in rec["frames"]) == list(range(src.workload.frames))
+    for t in (0, src.workload.frames - 1):
+        score, lcs = oracle.msssim(*src.pair(t), src.bpc, want_lcs=True)
+        assert score == rec["frames"][str(t)]["score"]
+        assert lcs.tolist() == rec["frames"][str(t)]["lcs"]
