@@ -77,6 +77,16 @@ def lib():
         for name in ("vqm_oracle_ff_add", "vqm_oracle_ff_mul", "vqm_oracle_ff_div"):
             getattr(L, name).argtypes = [fp, fp, fp]
             getattr(L, name).restype = None
+        L.vqm_oracle_iir_line.argtypes = [fp, ip, fp, fp]
+        L.vqm_oracle_ss2_blur.argtypes = [fp, ip, ip, fp, fp]
+        L.vqm_oracle_ss2_downsampled_dim.argtypes = [ip, ip, ctypes.POINTER(ip), ctypes.POINTER(ip)]
+        L.vqm_oracle_ss2_downsampled_dim.restype = None
+        L.vqm_oracle_ss2_downsample.argtypes = [fp, ip, ip, fp]
+        L.vqm_oracle_ss2_cascade_coefficients.argtypes = [ctypes.c_double, fp]
+        L.vqm_oracle_ss2_chain.argtypes = [vp, vp, ip, ip, ip, ip, fp, dp]
+        for name in ("vqm_oracle_iir_line", "vqm_oracle_ss2_blur", "vqm_oracle_ss2_downsample",
+                     "vqm_oracle_ss2_cascade_coefficients", "vqm_oracle_ss2_chain"):
+            getattr(L, name).restype = ip
         L.vqm_oracle_msssim_combine.argtypes = [dp]
         L.vqm_oracle_msssim_combine.restype = ctypes.c_double
         for name in ("vqm_oracle_sample_plane", "vqm_oracle_decimate", "vqm_oracle_ssim_planes",
@@ -270,3 +280,75 @@ def ff_mul(a, b):
 
 def ff_div(a, b):
     return _ff("vqm_oracle_ff_div", a, b)
+
+
+# ------------------------------------------------- ssimulacra2 per-scale chain
+
+
+def _coef(coef) -> np.ndarray:
+    c = np.ascontiguousarray(coef, np.float32)
+    if c.shape != (4,):
+        raise ValueError("the recursion takes four coefficients (B, a1, a2, a3)")
+    return c
+
+
+def ss2_cascade_coefficients(sigma: float) -> np.ndarray:
+    """(B, a1, a2, a3) of three symmetric exponential smoothers whose impulse
+    response has variance sigma^2, as float32."""
+    out = np.empty(4, np.float32)
+    _check(lib().vqm_oracle_ss2_cascade_coefficients(float(sigma), _ptr(out)), "ss2_cascade_coefficients")
+    return out
+
+
+def iir_line(x, coef) -> np.ndarray:
+    """One line through the causal, then anticausal, third-order recursion."""
+    x = np.ascontiguousarray(x, np.float32)
+    c = _coef(coef)
+    y = np.empty_like(x)
+    _check(lib().vqm_oracle_iir_line(_ptr(x), x.size, _ptr(c), _ptr(y)), "iir_line")
+    return y
+
+
+def ss2_blur(plane, coef) -> np.ndarray:
+    """The recursion along every row, then every column."""
+    plane = np.ascontiguousarray(plane, np.float32)
+    h, w = plane.shape
+    c = _coef(coef)
+    out = np.empty_like(plane)
+    _check(lib().vqm_oracle_ss2_blur(_ptr(plane), w, h, _ptr(c), _ptr(out)), "ss2_blur")
+    return out
+
+
+def ss2_downsampled_dim(w: int, h: int):
+    ow, oh = ctypes.c_int(), ctypes.c_int()
+    lib().vqm_oracle_ss2_downsampled_dim(int(w), int(h), ctypes.byref(ow), ctypes.byref(oh))
+    return ow.value, oh.value
+
+
+def ss2_downsample(plane) -> np.ndarray:
+    plane = np.ascontiguousarray(plane, np.float32)
+    h, w = plane.shape
+    ow, oh = ss2_downsampled_dim(w, h)
+    out = np.empty((oh, ow), np.float32)
+    _check(lib().vqm_oracle_ss2_downsample(_ptr(plane), w, h, _ptr(out)), "ss2_downsample")
+    return out
+
+
+def ss2_chain(ref_planes, dis_planes, nscales: int, coef) -> np.ndarray:
+    """The six sums per channel at every scale, shape [nscales, nch, 6]."""
+    ref = [np.ascontiguousarray(p, np.float32) for p in ref_planes]
+    dis = [np.ascontiguousarray(p, np.float32) for p in dis_planes]
+    if len(ref) != len(dis) or not ref:
+        raise ValueError("one reference and one distorted plane per channel")
+    h, w = ref[0].shape
+    for p in ref + dis:
+        if p.shape != (h, w):
+            raise ValueError("all planes must have one shape")
+    nch = len(ref)
+    arr = ctypes.c_void_p * nch
+    rp = arr(*[p.ctypes.data for p in ref])
+    dp_ = arr(*[p.ctypes.data for p in dis])
+    c = _coef(coef)
+    out = np.empty((max(int(nscales), 1), nch, 6), np.float64)
+    _check(lib().vqm_oracle_ss2_chain(rp, dp_, nch, w, h, int(nscales), _ptr(c), _ptr(out)), "ss2_chain")
+    return out

@@ -51,6 +51,16 @@
  *                       ssimulacra2 scores is unpinned (no fixture here).
  *   pairs             — two_sum and two_prod exact against Fraction; ff_add,
  *                       ff_mul and ff_div within their error bounds.
+ *   ss2 blur          — exact rational recursions on dyadic coefficients and
+ *                       inputs; the closed-form impulse response of the
+ *                       exponential cascade; scipy.signal.lfilter in fp64 on
+ *                       random lines and planes, within fp32 rounding.
+ *   ss2 downsample    — exact 2x2 means of dyadic samples, odd edges.
+ *   ss2 coefficients  — variance sigma^2 and unit gain of the impulse
+ *                       response, in closed form and summed.
+ *   ss2 chain         — identical inputs give zeros at every scale; an
+ *                       independent fp64 numpy/scipy evaluation of the same
+ *                       stages within the fp32 chain's rounding.
  */
 #ifndef VQM_ORACLE_H
 #define VQM_ORACLE_H
@@ -188,6 +198,49 @@ void vqm_oracle_two_prod(float a, float b, float out[2]);
 void vqm_oracle_ff_add(const float a[2], const float b[2], float out[2]);
 void vqm_oracle_ff_mul(const float a[2], const float b[2], float out[2]);
 void vqm_oracle_ff_div(const float a[2], const float b[2], float out[2]);
+
+/* The per-scale chain that feeds those sums (Finding 7's stages after the
+ * colour transform: three multiplies, horizontal and vertical blur passes,
+ * the sums, the downsample; Finding 2: each stage reproducible bit for bit
+ * in fp32 with contraction off and every product its own rounded value).
+ *
+ * The blur (reading: the pages name a recursive Gaussian walked along each
+ * row, then each column, without its coefficients or edges).  A third-order
+ * recursion with caller coefficients coef = {B, a1, a2, a3}, at rest
+ * outside the line (zero state), causal then anticausal:
+ *   w[i] = ((B x[i] + a3 w[i-3]) + a2 w[i-2]) + a1 w[i-1],   i = 0..n-1
+ *   y[i] = ((B w[i] + a3 y[i+3]) + a2 y[i+2]) + a1 y[i+1],   i = n-1..0
+ * each product rounded to fp32 on its own, the sum from the oldest state to
+ * the newest.  ss2_blur applies it to every row, then to every column of
+ * the row pass's fp32 output.
+ *
+ * The downsample (reading: only "downsample_2x2" is named): a w x h plane
+ * to ceil(w/2) x ceil(h/2), out = ((a + b) + (c + d)) * 0.25f over the 2x2
+ * block, a and b from the upper row, with the last column and row repeated
+ * when the size is odd.
+ *
+ * The chain, per scale s = 0..nscales-1 (nscales 1..6; reading: the
+ * published ssimulacra2 has six scales), for each of nch (1..3) channels of
+ * w x h fp32 planes ref[c], dis[c] (scale 0 as given, each later scale the
+ * downsample of the one before): aa = a a, bb = b b, ab = a b; the five
+ * blurs mu1, mu2, s11, s22, s12 of a, b, aa, bb, ab; then
+ * ss2_channel_sums(a, b, mu1, mu2, s11, s22, s12) into
+ * sums[(s * nch + c) * 6 ..].  The planes are whatever the colour transform
+ * gives (reading: the pages fix none of its constants, so the chain starts
+ * from the transformed planes and downsamples them).
+ *
+ * cascade_coefficients(sigma): the coefficients of three symmetric
+ * exponential smoothers in series, {(1-p)^3, 3p, -3p^2, p^3} with p the
+ * root in (0, 1) of 6p / (1-p)^2 = sigma^2, so the filter's impulse
+ * response has variance sigma^2 (reading: one choice of recursive Gaussian
+ * among many; the chain takes any coefficients). */
+int vqm_oracle_iir_line(const float *x, int n, const float coef[4], float *y);
+int vqm_oracle_ss2_blur(const float *in, int w, int h, const float coef[4], float *out);
+void vqm_oracle_ss2_downsampled_dim(int w, int h, int *ow, int *oh);
+int vqm_oracle_ss2_downsample(const float *in, int w, int h, float *out);
+int vqm_oracle_ss2_cascade_coefficients(double sigma, float coef[4]);
+int vqm_oracle_ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, int h, int nscales,
+                         const float coef[4], double *sums);
 
 #ifdef __cplusplus
 }

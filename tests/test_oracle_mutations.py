@@ -62,6 +62,38 @@ SS2_MUTANTS = {
 }
 
 
+# Slips in the per-scale chain (the recursion, the downsample, the filter
+# design and the chain's stage wiring), caught by test_ss2_chain_pins.py.
+CHAIN_MUTANTS = {
+    "iir_causal_a1_a3_swapped": ("float t3 = a3 * p3;", "float t3 = a1 * p3;",
+                                 "float t1 = a1 * p1;", "float t1 = a3 * p1;"),
+    "iir_anticausal_drops_a2": ("float t2 = a2 * q2;", "float t2 = 0.0f * q2;"),
+    "iir_anticausal_reads_input": ("float in = B * w[i];", "float in = B * x[(long)i * sx];"),
+    "iir_state_shift_order": ("p3 = p2;\n        p2 = p1;", "p2 = p1;\n        p3 = p2;"),
+    "iir_anticausal_start_one_early": ("for (int i = n - 1; i >= 0; i--) {", "for (int i = n - 2; i >= 0; i--) {"),
+    "blur_columns_first": (
+        "for (int r = 0; r < h; r++) /* every row first */\n"
+        "        iir_line(in + (size_t)r * w, 1, rows + (size_t)r * w, 1, w, coef, line);\n"
+        "    for (int c = 0; c < w; c++) /* then every column of the row pass's output */\n"
+        "        iir_line(rows + c, w, out + c, w, h, coef, line);",
+        "for (int c = 0; c < w; c++)\n"
+        "        iir_line(in + c, w, rows + c, w, h, coef, line);\n"
+        "    for (int r = 0; r < h; r++)\n"
+        "        iir_line(rows + (size_t)r * w, 1, out + (size_t)r * w, 1, w, coef, line);"),
+    "downsample_floor_dims": ("*ow = (w + 1) / 2;", "*ow = w / 2 > 0 ? w / 2 : 1;"),
+    "downsample_drops_a_sample": ("out[(size_t)y * ow + x] = ((a + b) + (c + d)) * 0.25f;",
+                                  "out[(size_t)y * ow + x] = ((a + b) + (c + c)) * 0.25f;"),
+    "cascade_wrong_root": ("double p = ((s2 + 3.0) - sqrt(6.0 * s2 + 9.0)) / s2;",
+                           "double p = ((s2 + 3.0) + sqrt(6.0 * s2 + 9.0)) / s2;"),
+    "cascade_one_pass_variance": ("double p = ((s2 + 3.0) - sqrt(6.0 * s2 + 9.0)) / s2;",
+                                  "double p = ((s2 + 1.0) - sqrt(2.0 * s2 + 1.0)) / s2;"),
+    "cascade_a2_sign": ("coef[2] = (float)(-3.0 * p * p);", "coef[2] = (float)(3.0 * p * p);"),
+    "chain_cross_product_as_square": ("ab[i] = a[i] * b[i];", "ab[i] = a[i] * a[i];"),
+    "chain_means_swapped": ("const float *src[5] = {a, b, aa, bb, ab};", "const float *src[5] = {b, a, aa, bb, ab};"),
+    "chain_never_downsamples": ("if (s > 0) { /* the next scale's images", "if (0) { /* the next scale's images"),
+}
+
+
 def _build_mutant(tmp_path, name, edits, path=SRC):
     src = open(path).read()
     for old, new in zip(edits[0::2], edits[1::2]):
@@ -101,8 +133,15 @@ def test_ss2_pins_catch_mutant(tmp_path, name):
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
 
 
+@pytest.mark.parametrize("name", sorted(CHAIN_MUTANTS))
+def test_chain_pins_catch_mutant(tmp_path, name):
+    so = _build_mutant(tmp_path, name, CHAIN_MUTANTS[name], SS2_SRC)
+    r = _run_pins(so, "test_ss2_chain_pins.py")
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+
+
 def test_unmodified_sources_pass_the_pins(tmp_path):
     so = _build_mutant(tmp_path, "unmodified", ())
-    for pins in ("test_oracle_pins.py", "test_ss2_oracle_pins.py"):
+    for pins in ("test_oracle_pins.py", "test_ss2_oracle_pins.py", "test_ss2_chain_pins.py"):
         r = _run_pins(so, pins)
         assert r.returncode == 0, f"{pins}:\n{r.stdout[-2000:]}"
