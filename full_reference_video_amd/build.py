@@ -22,7 +22,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvqm.so")
 
-SOURCES = ["vqm_runtime.cpp", "ssim_step.hip", "msssim.hip", "ss2_stats.hip", "probe.hip"]
+SOURCES = ["vqm_runtime.cpp", "ssim_step.hip", "msssim.hip", "ss2_stats.hip", "ss2_chain.hip", "probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -184,6 +184,28 @@ hipError_t launch_ss2_sums(const float *const *planes, int nch, long long n, voi
 // 3 ff_mul, 4 ff_div) over n pairs of device arrays, for the tests.
 hipError_t launch_pair_ops(int op, const float *a, const float *b, float *out, int n, hipStream_t stream);
 
+// ---------------------------------------------------------------- ssimulacra2 per-scale chain
+
+// The recursive blur's row pass over nch channels of w x h fp32 planes
+// (tightly packed).  nplanes 5: out[c] receives the five planes a, b, a a,
+// b b, a b of a[c], b[c], each blurred along its rows, pstride floats
+// apart; nplanes 1: out[c] receives a[c] blurred along its rows (b unused;
+// out may equal a).  coef = {B, a1, a2, a3}.
+hipError_t launch_ss2_rows(const float *const *a, const float *const *b, float *const *out, int nch, int nplanes,
+                           int w, int h, long long pstride, const float coef[4], hipStream_t stream,
+                           const KernelTimer &timer);
+
+// The column pass, in place on nplanes (1 or 5) planes per channel.
+hipError_t launch_ss2_cols(float *const *planes, int nch, int nplanes, int w, int h, long long pstride,
+                           const float coef[4], hipStream_t stream, const KernelTimer &timer);
+
+// ceil(w/2) x ceil(h/2).
+void ss2_downsampled_dim(int w, int h, int *ow, int *oh);
+
+// The 2x2 downsample of nplanes (up to 6) w x h planes in[i] into out[i].
+hipError_t launch_ss2_down(const float *const *in, float *const *out, int nplanes, int w, int h,
+                           hipStream_t stream);
+
 // ---------------------------------------------------------------- inspection
 
 // A streaming read of bytes / 16 16-byte vectors of buf (non-temporal loads,

@@ -15,6 +15,7 @@
 #include <errno.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -228,6 +229,11 @@ struct vqm_ctx {
     // ssimulacra2 statistics: workgroup partials and the pinned result block
     void *ss2_partials = nullptr;
     double *ss2_result_host = nullptr, *ss2_result_dev = nullptr;
+    // ssimulacra2 per-scale chain: the five blurred planes per channel and
+    // the downsampled images, and the pinned block of every scale's sums
+    float *ss2c_work = nullptr;
+    size_t ss2c_work_floats = 0;
+    double *ss2c_result_host = nullptr, *ss2c_result_dev = nullptr;
 };
 
 namespace {
@@ -734,6 +740,8 @@ void destroy(vqm_ctx *ctx) {
     for (hipEvent_t e : ctx->event_pool) (void)hipEventDestroy(e);
     if (ctx->ss2_partials) (void)hipFree(ctx->ss2_partials);
     if (ctx->ss2_result_host) (void)hipHostFree(ctx->ss2_result_host);
+    if (ctx->ss2c_work) (void)hipFree(ctx->ss2c_work);
+    if (ctx->ss2c_result_host) (void)hipHostFree(ctx->ss2c_result_host);
     if (ctx->own_stream) (void)hipStreamDestroy(ctx->stream);
     if (cur >= 0) (void)hipSetDevice(cur);
     delete ctx;
@@ -925,6 +933,18 @@ int score_frames(vqm_ctx *const *ctxs, int nctx, int metric, const void *const *
     return rc;
 }
 
+// The statistics' workgroup partials and the one-scale result block.
+int ss2_buffers(vqm_ctx *ctx) {
+    if (!ctx->ss2_partials) {
+        HIP_TRY_ALLOC(hipMalloc(&ctx->ss2_partials, (size_t)vqm::kSs2MaxChannels * vqm::kSs2MaxBlocks * 6 *
+                                                        2 * sizeof(float)));
+        HIP_TRY_ALLOC(hipHostMalloc(&ctx->ss2_result_host, 6 * vqm::kSs2MaxChannels * sizeof(double),
+                                    hipHostMallocMapped | hipHostMallocCoherent));
+        HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void **>(&ctx->ss2_result_dev), ctx->ss2_result_host, 0));
+    }
+    return 0;
+}
+
 // The ssimulacra2 statistics of one scale ("Research-1363: Device-resident
 // ssimulacra2 and a single-wait MS-SSIM on SYCL", Finding 4): two launches on
 // a leased context's stream, one wait, one read-back of 6 doubles per
@@ -947,19 +967,201 @@ int ss2_sums(const float *const *planes, int nch, int w, int h, double *sums) {
         if (rc) return rc;
         if (k != PTR_DEVICE) return fail(-EINVAL, "plane %d: the statistics read device memory only", i);
     }
-    if (!ctx->ss2_partials) {
-        HIP_TRY_ALLOC(hipMalloc(&ctx->ss2_partials, (size_t)vqm::kSs2MaxChannels * vqm::kSs2MaxBlocks * 6 *
-                                                        2 * sizeof(float)));
-        HIP_TRY_ALLOC(hipHostMalloc(&ctx->ss2_result_host, 6 * vqm::kSs2MaxChannels * sizeof(double),
-                                    hipHostMallocMapped | hipHostMallocCoherent));
-        HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void **>(&ctx->ss2_result_dev), ctx->ss2_result_host, 0));
-    }
+    rc = ss2_buffers(ctx);
+    if (rc) return rc;
     for (int k = 0; k < 6 * nch; ++k) ctx->ss2_result_host[k] = NAN;
     const hipError_t e =
         vqm::launch_ss2_sums(planes, nch, (long long)w * h, ctx->ss2_partials, ctx->ss2_result_dev, ctx->stream);
     if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
     HIP_TRY(hipStreamSynchronize(ctx->stream));  // the one wait
     memcpy(sums, ctx->ss2_result_host, 6 * (size_t)nch * sizeof(double));
+    return 0;
+}
+
+// ---- the ssimulacra2 per-scale chain ("Research-1363: Device-resident
+// ssimulacra2 and a single-wait MS-SSIM on SYCL", Findings 2 and 7)
+
+int check_coef(const float *coef) {
+    if (!coef) return fail(-EINVAL, "NULL coefficient array");
+    for (int i = 0; i < 4; ++i)
+        if (!std::isfinite(coef[i])) return fail(-EINVAL, "coefficient %d is not finite", i);
+    return 0;
+}
+
+int check_ss2_size(int w, int h) {
+    if (w <= 0 || h <= 0) return fail(-EINVAL, "plane size %dx%d is not positive", w, h);
+    if ((long long)w * (long long)h > 0x7fffffffLL) return fail(-EINVAL, "plane %dx%d too large", w, h);
+    return 0;
+}
+
+int device_only(vqm_ctx *ctx, const void *p, const char *what) {
+    PtrKind k;
+    const int rc = classify(p, ctx->device, &k);
+    if (rc) return rc;
+    if (k != PTR_DEVICE) return fail(-EINVAL, "%s: the chain reads and writes device memory only", what);
+    return 0;
+}
+
+// Device memory of at least `floats` floats in the context's chain workspace
+// (the context is idle: blocking calls end with a wait).
+int ss2c_workspace(vqm_ctx *ctx, size_t floats) {
+    if (ctx->ss2c_work_floats >= floats) return 0;
+    if (ctx->ss2c_work) {
+        (void)hipFree(ctx->ss2c_work);
+        ctx->ss2c_work = nullptr;
+        ctx->ss2c_work_floats = 0;
+    }
+    HIP_TRY_ALLOC(hipMalloc(&ctx->ss2c_work, floats * sizeof(float)));
+    ctx->ss2c_work_floats = floats;
+    return 0;
+}
+
+// One plane through the row pass and the column pass.
+int ss2_blur_plane(const float *in, float *out, int w, int h, const float *coef) {
+    if (!in || !out) return fail(-EINVAL, "NULL plane pointer");
+    int rc = check_ss2_size(w, h);
+    if (!rc) rc = check_coef(coef);
+    if (rc) return rc;
+    Lease lease;
+    rc = lease_ctx(lease);
+    if (rc) return rc;
+    vqm_ctx *ctx = lease.ctx;
+    if ((rc = device_only(ctx, in, "input plane")) || (rc = device_only(ctx, out, "output plane"))) return rc;
+    const vqm::KernelTimer none;
+    hipError_t e = vqm::launch_ss2_rows(&in, &in, &out, 1, 1, w, h, (long long)w * h, coef, ctx->stream, none);
+    if (e == hipSuccess) e = vqm::launch_ss2_cols(&out, 1, 1, w, h, (long long)w * h, coef, ctx->stream, none);
+    if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
+    HIP_TRY(hipStreamSynchronize(ctx->stream));
+    return 0;
+}
+
+int ss2_down_plane(const float *in, float *out, int w, int h) {
+    if (!in || !out) return fail(-EINVAL, "NULL plane pointer");
+    int rc = check_ss2_size(w, h);
+    if (rc) return rc;
+    Lease lease;
+    rc = lease_ctx(lease);
+    if (rc) return rc;
+    vqm_ctx *ctx = lease.ctx;
+    if ((rc = device_only(ctx, in, "input plane")) || (rc = device_only(ctx, out, "output plane"))) return rc;
+    const hipError_t e = vqm::launch_ss2_down(&in, &out, 1, w, h, ctx->stream);
+    if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
+    HIP_TRY(hipStreamSynchronize(ctx->stream));
+    return 0;
+}
+
+constexpr int kSs2MaxScales = 6;
+
+size_t align64(size_t n) { return (n + 63) & ~(size_t)63; }
+
+// Every scale enqueued on one stream: per scale the downsample (from the
+// second scale on), the row pass with the products, the column pass, and
+// the statistics into the scale's span of the pinned result block; one
+// wait, one read-back.
+int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, int h, int nscales,
+              const float *coef, double *sums) {
+    if (!ref || !dis || !sums) return fail(-EINVAL, "NULL plane array or sums pointer");
+    if (nch < 1 || nch > vqm::kSs2MaxChannels)
+        return fail(-EINVAL, "%d channels outside 1..%d", nch, vqm::kSs2MaxChannels);
+    if (nscales < 1 || nscales > kSs2MaxScales)
+        return fail(-EINVAL, "%d scales outside 1..%d", nscales, kSs2MaxScales);
+    int rc = check_ss2_size(w, h);
+    if (!rc) rc = check_coef(coef);
+    if (rc) return rc;
+    for (int c = 0; c < nch; ++c)
+        if (!ref[c] || !dis[c]) return fail(-EINVAL, "NULL plane of channel %d", c);
+    Lease lease;
+    rc = lease_ctx(lease);
+    if (rc) return rc;
+    vqm_ctx *ctx = lease.ctx;
+    for (int c = 0; c < nch; ++c)
+        if ((rc = device_only(ctx, ref[c], "reference plane")) || (rc = device_only(ctx, dis[c], "distorted plane")))
+            return rc;
+
+    // sizes; the workspace holds five blurred planes per channel at the
+    // first scale's size, then two images per channel for every later scale
+    int sw[kSs2MaxScales], sh[kSs2MaxScales];
+    size_t pyr_off[kSs2MaxScales] = {0};
+    sw[0] = w;
+    sh[0] = h;
+    const size_t ps0 = align64((size_t)w * h);
+    size_t total = 5 * (size_t)nch * ps0;
+    for (int s = 1; s < nscales; ++s) {
+        vqm::ss2_downsampled_dim(sw[s - 1], sh[s - 1], &sw[s], &sh[s]);
+        pyr_off[s] = total;
+        total += 2 * (size_t)nch * align64((size_t)sw[s] * sh[s]);
+    }
+    if ((rc = ss2c_workspace(ctx, total)) || (rc = ss2_buffers(ctx))) return rc;
+    if (!ctx->ss2c_result_host) {
+        HIP_TRY_ALLOC(hipHostMalloc(&ctx->ss2c_result_host, 6 * vqm::kSs2MaxChannels * kSs2MaxScales * sizeof(double),
+                                    hipHostMallocMapped | hipHostMallocCoherent));
+        HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void **>(&ctx->ss2c_result_dev), ctx->ss2c_result_host, 0));
+    }
+    const int nres = 6 * nch * nscales;
+    for (int k = 0; k < nres; ++k) ctx->ss2c_result_host[k] = NAN;
+
+    const vqm::KernelTimer none;
+    float *const work = ctx->ss2c_work;
+    const float *a[vqm::kSs2MaxChannels], *b[vqm::kSs2MaxChannels];
+    for (int c = 0; c < nch; ++c) {
+        a[c] = ref[c];
+        b[c] = dis[c];
+    }
+    hipError_t e = hipSuccess;
+    for (int s = 0; s < nscales && e == hipSuccess; ++s) {
+        const long long n = (long long)sw[s] * sh[s];
+        const size_t ps = align64((size_t)n);
+        if (s > 0) {
+            const float *from[2 * vqm::kSs2MaxChannels];
+            float *to[2 * vqm::kSs2MaxChannels];
+            for (int c = 0; c < nch; ++c) {
+                from[2 * c] = a[c];
+                from[2 * c + 1] = b[c];
+                to[2 * c] = work + pyr_off[s] + (2 * (size_t)c) * ps;
+                to[2 * c + 1] = work + pyr_off[s] + (2 * (size_t)c + 1) * ps;
+            }
+            e = vqm::launch_ss2_down(from, to, 2 * nch, sw[s - 1], sh[s - 1], ctx->stream);
+            for (int c = 0; c < nch; ++c) {
+                a[c] = to[2 * c];
+                b[c] = to[2 * c + 1];
+            }
+        }
+        float *blur[vqm::kSs2MaxChannels];
+        for (int c = 0; c < nch; ++c) blur[c] = work + 5 * (size_t)c * ps0;
+        if (e == hipSuccess)
+            e = vqm::launch_ss2_rows(a, b, blur, nch, 5, sw[s], sh[s], (long long)ps, coef, ctx->stream, none);
+        if (e == hipSuccess)
+            e = vqm::launch_ss2_cols(blur, nch, 5, sw[s], sh[s], (long long)ps, coef, ctx->stream, none);
+        const float *planes[7 * vqm::kSs2MaxChannels];
+        for (int c = 0; c < nch; ++c) {
+            planes[7 * c] = a[c];
+            planes[7 * c + 1] = b[c];
+            for (int p = 0; p < 5; ++p) planes[7 * c + 2 + p] = blur[c] + (size_t)p * ps;
+        }
+        if (e == hipSuccess)
+            e = vqm::launch_ss2_sums(planes, nch, n, ctx->ss2_partials, ctx->ss2c_result_dev + 6 * (size_t)nch * s,
+                                     ctx->stream);
+    }
+    if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
+    HIP_TRY(hipStreamSynchronize(ctx->stream));  // the one wait
+    memcpy(sums, ctx->ss2c_result_host, nres * sizeof(double));
+    return 0;
+}
+
+// Three symmetric exponential smoothers in series with variance sigma^2.
+int ss2_cascade(double sigma, float *coef) {
+    if (!coef) return fail(-EINVAL, "NULL coefficient array");
+    if (!(sigma > 0.0) || !(sigma < 1e6)) return fail(-EINVAL, "sigma %g outside (0, 1e6)", sigma);
+    // one smoother with pole p has variance 2p / (1 - p)^2; three have
+    // 6p / (1 - p)^2.  p is the smaller root of
+    // sigma^2 p^2 - (2 sigma^2 + 6) p + sigma^2 = 0, the one in (0, 1).
+    const double v = sigma * sigma;
+    const double p = ((v + 3.0) - std::sqrt(6.0 * v + 9.0)) / v;
+    const double g = 1.0 - p;
+    coef[0] = (float)(g * g * g);
+    coef[1] = (float)(3.0 * p);
+    coef[2] = (float)(-3.0 * p * p);
+    coef[3] = (float)(p * p * p);
     return 0;
 }
 
@@ -1602,6 +1804,19 @@ int vqm_debug_pyramid_batch(vqm_ctx *ctx, const void *const *refs, const void *c
 int vqm_ss2_channel_sums(const float *const *planes, int nch, int w, int h, double *sums) {
     return ss2_sums(planes, nch, w, h, sums);
 }
+
+int vqm_ss2_blur(const float *in, float *out, int w, int h, const float *coef) {
+    return ss2_blur_plane(in, out, w, h, coef);
+}
+
+int vqm_ss2_downsample(const float *in, float *out, int w, int h) { return ss2_down_plane(in, out, w, h); }
+
+int vqm_ss2_scale_sums(const float *const *ref, const float *const *dis, int nch, int w, int h, int nscales,
+                       const float *coef, double *sums) {
+    return ss2_chain(ref, dis, nch, w, h, nscales, coef, sums);
+}
+
+int vqm_ss2_cascade_coefficients(double sigma, float *coef) { return ss2_cascade(sigma, coef); }
 
 int vqm_debug_read_probe(const void *buf, long long bytes, int reps, double *ms) {
     return read_probe(buf, bytes, reps, ms);

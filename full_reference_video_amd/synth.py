@@ -240,23 +240,21 @@ def _box5_symmetric(a: np.ndarray) -> np.ndarray:
     return acc / 25.0
 
 
-def ss2_planes(seed: int, w: int, h: int, channels: int = 3):
-    """Inputs of the ssimulacra2 per-scale statistics: per channel the seven
-    float32 planes (img1, img2, mu1, mu2, s11, s22, s12), each h x w.
+def ss2_images(seed: int, w: int, h: int, channels: int = 3):
+    """The two pictures' colour-transformed planes for the ssimulacra2
+    per-scale chain: lists ``ref``, ``dis`` of ``channels`` float32 h x w
+    planes.
 
     The pages measure ssimulacra2 on the Netflix 576x324 pair, Big Buck Bunny
     at 3840x2160 and an 853x481 rescale ("Device-resident ssimulacra2 and a
     single-wait MS-SSIM on SYCL", Sources and Finding 5); none is available
-    here, so seeded planes of those sizes stand in.  Each channel image is a
-    smooth field in [0, 1] (3 sinusoids of amplitude 0.08 about a level drawn
-    in [0.3, 0.7], from ``default_rng(seed * 10 + channel)``) plus uniform
-    noise in +-0.02; img2 is img1 plus Gaussian noise of sigma 0.01, clipped to
-    [0, 1].  The blurred planes are 5 x 5 means (symmetric edges, fp64, then
-    rounded to float32) of the images and of their products: a stand-in for
-    the metric's own blur, so that every variance the statistics form is
-    non-negative, as a blur with non-negative weights keeps it.
+    here, so seeded planes of those sizes stand in.  Each reference channel
+    is a smooth field in [0, 1] (3 sinusoids of amplitude 0.08 about a level
+    drawn in [0.3, 0.7], from ``default_rng(seed * 10 + channel)``) plus
+    uniform noise in +-0.02; the distorted channel adds Gaussian noise of
+    sigma 0.01, clipped to [0, 1].
     """
-    out = []
+    refs, diss = [], []
     x = np.arange(w, dtype=np.float64)[None, :]
     y = np.arange(h, dtype=np.float64)[:, None]
     for ch in range(channels):
@@ -270,6 +268,24 @@ def ss2_planes(seed: int, w: int, h: int, channels: int = 3):
             f = f + 0.08 * np.sin(2.0 * np.pi * (x * np.cos(theta) + y * np.sin(theta)) / period + phase)
         img1 = np.clip(f + rng.uniform(-0.02, 0.02, size=(h, w)), 0.0, 1.0).astype(np.float32)
         img2 = np.clip(img1 + rng.normal(0.0, 0.01, size=(h, w)), 0.0, 1.0).astype(np.float32)
+        refs.append(img1)
+        diss.append(img2)
+    return refs, diss
+
+
+def ss2_planes(seed: int, w: int, h: int, channels: int = 3):
+    """Inputs of the ssimulacra2 per-scale statistics: per channel the seven
+    float32 planes (img1, img2, mu1, mu2, s11, s22, s12), each h x w.
+
+    img1 and img2 are ``ss2_images(seed, w, h, channels)``.  The blurred
+    planes are 5 x 5 means (symmetric edges, fp64, then
+    rounded to float32) of the images and of their products: a stand-in for
+    the metric's own blur, so that every variance the statistics form is
+    non-negative, as a blur with non-negative weights keeps it.
+    """
+    out = []
+    refs, diss = ss2_images(seed, w, h, channels)
+    for img1, img2 in zip(refs, diss):
         a, b = img1.astype(np.float64), img2.astype(np.float64)
         mu1, mu2 = _box5_symmetric(a), _box5_symmetric(b)
         s11, s22, s12 = _box5_symmetric(a * a), _box5_symmetric(b * b), _box5_symmetric(a * b)

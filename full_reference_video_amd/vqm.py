@@ -99,6 +99,11 @@ def lib() -> ctypes.CDLL:
         L.vqm_ssim_frame_noalloc.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p]
         L.vqm_ss2_channel_sums.argtypes = [ctypes.POINTER(c_void_p), c_int, c_int, c_int, c_double_p]
         L.vqm_debug_pair_ops.argtypes = [c_int, c_void_p, c_void_p, c_void_p, c_int]
+        L.vqm_ss2_blur.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p]
+        L.vqm_ss2_downsample.argtypes = [c_void_p, c_void_p, c_int, c_int]
+        L.vqm_ss2_scale_sums.argtypes = [ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int, c_int, c_int,
+                                         c_int, c_void_p, c_double_p]
+        L.vqm_ss2_cascade_coefficients.argtypes = [ctypes.c_double, c_void_p]
         L.vqm_debug_read_probe.argtypes = [c_void_p, ctypes.c_longlong, c_int, c_double_p]
         L.vqm_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -290,6 +295,75 @@ def vqm_ss2_channel_sums(channels) -> np.ndarray:
     out = np.empty((nch, 6), np.float64)
     _check(lib().vqm_ss2_channel_sums(ptrs, nch, int(w), int(h), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))),
            "vqm_ss2_channel_sums")
+    return out
+
+
+def _f32_plane(t, what):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2 or not t.is_contiguous():
+        raise TypeError(f"{what}: a contiguous 2-D float32 device tensor")
+    return t
+
+
+def _coef_array(coef) -> np.ndarray:
+    c = np.ascontiguousarray(coef, np.float32)
+    if c.shape != (4,):
+        raise ValueError("four recursion coefficients (B, a1, a2, a3)")
+    return c
+
+
+def vqm_ss2_cascade_coefficients(sigma: float) -> np.ndarray:
+    """(B, a1, a2, a3) of the library's recursive bell of variance sigma^2."""
+    out = np.empty(4, np.float32)
+    _check(lib().vqm_ss2_cascade_coefficients(float(sigma), out.ctypes.data), "vqm_ss2_cascade_coefficients")
+    return out
+
+
+def vqm_ss2_blur(plane, coef, out=None):
+    """The recursive blur (rows, then columns) of a float32 device plane;
+    ``out`` (default: a new tensor) may be ``plane`` itself."""
+    import torch
+    plane = _f32_plane(plane, "plane")
+    out = torch.empty_like(plane) if out is None else _f32_plane(out, "out")
+    if out.shape != plane.shape:
+        raise ValueError("out must have the plane's shape")
+    c = _coef_array(coef)
+    h, w = plane.shape
+    _check(lib().vqm_ss2_blur(plane.data_ptr(), out.data_ptr(), int(w), int(h), c.ctypes.data), "vqm_ss2_blur")
+    return out
+
+
+def vqm_ss2_downsample(plane):
+    """The chain's 2x2 downsample of a float32 device plane (sizes round up)."""
+    import torch
+    plane = _f32_plane(plane, "plane")
+    h, w = plane.shape
+    out = torch.empty(((h + 1) // 2, (w + 1) // 2), dtype=torch.float32, device=plane.device)
+    _check(lib().vqm_ss2_downsample(plane.data_ptr(), out.data_ptr(), int(w), int(h)), "vqm_ss2_downsample")
+    return out
+
+
+def vqm_ss2_scale_sums(ref_planes, dis_planes, nscales: int, coef) -> np.ndarray:
+    """The six sums per channel at every scale of the per-scale chain,
+    array [nscales, nch, 6]; ``ref_planes``/``dis_planes`` hold 1..3 float32
+    device tensors of one (h, w) shape."""
+    nch = len(ref_planes)
+    if nch != len(dis_planes):
+        raise ValueError("one reference and one distorted plane per channel")
+    rp, dp = (ctypes.c_void_p * max(nch, 1))(), (ctypes.c_void_p * max(nch, 1))()
+    h = w = None
+    for c in range(nch):
+        for arr, t, what in ((rp, ref_planes[c], "reference"), (dp, dis_planes[c], "distorted")):
+            _f32_plane(t, what)
+            if h is None:
+                h, w = t.shape
+            elif tuple(t.shape) != (h, w):
+                raise ValueError("all planes must have one shape")
+            arr[c] = t.data_ptr()
+    cf = _coef_array(coef)
+    out = np.empty((max(int(nscales), 1), max(nch, 1), 6), np.float64)
+    _check(lib().vqm_ss2_scale_sums(rp, dp, nch, int(w or 0), int(h or 0), int(nscales), cf.ctypes.data,
+                                    out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))), "vqm_ss2_scale_sums")
     return out
 
 

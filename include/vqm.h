@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define VQM_ABI_VERSION 5
+#define VQM_ABI_VERSION 6
 
 /* Exported symbols (the library is built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -420,6 +420,71 @@ VQM_API int vqm_ss2_channel_sums(const float *const *planes, int nch, int w, int
  * 4 ff_div.  Every step is a correctly rounded fp32 operation, so the
  * results are unique.  Blocking. */
 VQM_API int vqm_debug_pair_ops(int op, const float *a, const float *b, float *out, int n);
+
+/* ---- ssimulacra2: the per-scale chain on the device ---- */
+
+/* The recursive blur of one w x h fp32 plane (tightly packed), the blur of
+ * "Research-1363: Device-resident ssimulacra2 and a single-wait MS-SSIM on
+ * SYCL", Findings 2 and 7: a sequential recursion along every row, then
+ * along every column of the row pass's fp32 output.  The pages give no
+ * coefficients; this is the third-order recursion with
+ * coef = {B, a1, a2, a3} (host memory, finite), at rest outside the line,
+ * causal then anticausal:
+ *   w[i] = ((B x[i] + a3 w[i-3]) + a2 w[i-2]) + a1 w[i-1],   i = 0..n-1
+ *   y[i] = ((B w[i] + a3 y[i+3]) + a2 y[i+2]) + a1 y[i+1],   i = n-1..0
+ * each product rounded to fp32 on its own and the sum from the oldest state
+ * to the newest, so the result is unique and bit-exact.
+ *   in, out  device memory of the current device, w * h floats each; out
+ *            may equal in (the blur then runs in place).
+ * Blocking: two launches on a library-owned blocking stream and one wait.
+ * -EINVAL for NULL pointers, a bad size, non-finite coefficients or planes
+ * that are not device memory of the current device. */
+VQM_API int vqm_ss2_blur(const float *in, float *out, int w, int h, const float *coef);
+
+/* The 2x2 downsample between the chain's scales (Finding 7's "downsample"
+ * stage; its form is a reading): a w x h plane to ceil(w/2) x ceil(h/2),
+ * out = ((a + b) + (c + d)) * 0.25f over each 2x2 block (a, b its upper
+ * row), the last column and row repeated when w or h is odd.  in, out:
+ * device memory of the current device, tightly packed, not overlapping.
+ * Blocking.  -EINVAL as vqm_ss2_blur. */
+VQM_API int vqm_ss2_downsample(const float *in, float *out, int w, int h);
+
+/* The ssimulacra2 per-scale chain of one frame, every scale on the device
+ * and one wait (Finding 1's request of no round trips; Finding 7's stages
+ * after the colour transform: three multiplies, horizontal and vertical
+ * blur passes, the sums, the downsample).  For scale s = 0..nscales-1
+ * (nscales 1..6) and channel c = 0..nch-1 (nch 1..3): a, b are ref[c],
+ * dis[c] at s = 0 and the downsample of the previous scale's a, b after
+ * that; the five planes a, b, a a, b b, a b go through vqm_ss2_blur's blur
+ * with coef; and the six sums of vqm_ss2_channel_sums of
+ * (a, b, blur(a), blur(b), blur(a a), blur(b b), blur(a b)) go to
+ * sums[(s * nch + c) * 6 ..] (host memory, 6 * nch * nscales doubles).
+ *   ref, dis  nch device pointers each (the current device), w x h fp32
+ *             planes, tightly packed: the colour-transformed planes of the
+ *             two pictures (the pages fix no constants of the transform, so
+ *             it stays with the caller).
+ *   coef      the recursion's four coefficients, as vqm_ss2_blur; a blur
+ *             with a non-negative impulse response keeps every variance,
+ *             and so the statistics' denominators, positive.
+ * The multiplies, blurs and downsample are bit-exact; the sums are within
+ * about 1e-12 relative of exact and bitwise repeatable.  The library keeps
+ * a device workspace of about 5 * nch * w * h floats per blocking context
+ * (and the smaller scales' images), grown on demand.  Blocking: four
+ * launches per scale (three at the first) on a library-owned blocking
+ * stream and one wait.  -EINVAL for NULL pointers, bad counts or sizes,
+ * non-finite coefficients or planes that are not device memory of the
+ * current device; -ENOMEM when the workspace cannot grow. */
+VQM_API int vqm_ss2_scale_sums(const float *const *ref, const float *const *dis, int nch, int w, int h,
+                               int nscales, const float *coef, double *sums);
+
+/* Coefficients {B, a1, a2, a3} for the chain's blur whose impulse response
+ * is a Gaussian-like bell of variance sigma^2 (0 < sigma < 1e6): three
+ * symmetric exponential smoothers in series, B = (1 - p)^3, a1 = 3p,
+ * a2 = -3p^2, a3 = p^3, with p in (0, 1) solving 6p / (1 - p)^2 = sigma^2.
+ * One choice of recursive Gaussian among many (the pages name the filter,
+ * not its coefficients); host arithmetic only.  -EINVAL for a NULL array or
+ * sigma outside the range. */
+VQM_API int vqm_ss2_cascade_coefficients(double sigma, float *coef);
 
 /* A streaming read of `bytes` (>= 16) of device memory `buf` with 16-byte
  * non-temporal loads, one workgroup of 256 threads per 64 KiB, timed

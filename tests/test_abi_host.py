@@ -52,7 +52,7 @@ def header_constants():
 
 
 def test_abi_version():
-    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 5
+    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 6
 
 
 def test_graft_entry_check_matches_the_built_library():
@@ -222,3 +222,34 @@ def test_noalloc_refuses_oversized_and_bad_frames_before_any_hip_call():
     # (here it then fails at the device or pointer checks instead)
     assert header_constants()["VQM_NOALLOC_SCRATCH_BYTES"] == 8 << 20
     assert f(dummy, dummy, 7680, 4320, 10, dummy, None) not in (0, -errno.ENOSPC)
+
+
+def test_ss2_chain_refuses_bad_arguments_before_any_hip_call():
+    # Every check of the chain's entry points precedes the first HIP call.
+    L = vqm.lib()
+    dummy = ctypes.c_void_p(0x1000)
+    coef = np.array([0.5, 0.25, -0.125, 0.0625], np.float32)
+    bad = np.array([0.5, np.inf, 0.0, 0.0], np.float32)
+    sums = np.zeros(6 * 3 * 6, np.float64)
+    sp = sums.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    arr = (ctypes.c_void_p * 3)(dummy, dummy, dummy)
+    f = L.vqm_ss2_scale_sums
+    assert f(None, arr, 1, 64, 64, 2, coef.ctypes.data, sp) == -errno.EINVAL
+    assert f(arr, arr, 0, 64, 64, 2, coef.ctypes.data, sp) == -errno.EINVAL       # channels
+    assert f(arr, arr, 4, 64, 64, 2, coef.ctypes.data, sp) == -errno.EINVAL
+    assert f(arr, arr, 1, 64, 64, 0, coef.ctypes.data, sp) == -errno.EINVAL       # scales
+    assert f(arr, arr, 1, 64, 64, 7, coef.ctypes.data, sp) == -errno.EINVAL
+    assert f(arr, arr, 1, 0, 64, 2, coef.ctypes.data, sp) == -errno.EINVAL        # size
+    assert f(arr, arr, 1, 65536, 65536, 2, coef.ctypes.data, sp) == -errno.EINVAL
+    assert f(arr, arr, 1, 64, 64, 2, bad.ctypes.data, sp) == -errno.EINVAL        # coefficients
+    assert "coefficient 1" in vqm.vqm_last_error()
+    assert f(arr, arr, 1, 64, 64, 2, None, sp) == -errno.EINVAL
+    assert f(arr, arr, 1, 64, 64, 2, coef.ctypes.data, None) == -errno.EINVAL
+    assert L.vqm_ss2_blur(None, dummy, 8, 8, coef.ctypes.data) == -errno.EINVAL
+    assert L.vqm_ss2_blur(dummy, dummy, 8, -1, coef.ctypes.data) == -errno.EINVAL
+    assert L.vqm_ss2_blur(dummy, dummy, 8, 8, bad.ctypes.data) == -errno.EINVAL
+    assert L.vqm_ss2_downsample(dummy, None, 8, 8) == -errno.EINVAL
+    assert L.vqm_ss2_downsample(dummy, dummy, 0, 8) == -errno.EINVAL
+    c = np.zeros(4, np.float32)
+    assert L.vqm_ss2_cascade_coefficients(0.0, c.ctypes.data) == -errno.EINVAL
+    assert L.vqm_ss2_cascade_coefficients(1.5, None) == -errno.EINVAL

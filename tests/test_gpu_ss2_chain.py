@@ -1,0 +1,162 @@
+"""The device's ssimulacra2 per-scale chain against the oracle, on an MI355X.
+
+"Research-1363: Device-resident ssimulacra2 and a single-wait MS-SSIM on
+SYCL", Findings 2 and 7.  Bars:
+  * the blur (both passes) and the downsample equal the oracle's bit for bit
+    (Finding 2: everything but the sums reproduces the CPU exactly);
+  * the six sums per channel and scale lie within 1e-10 relative of the
+    oracle's fp64 sequential sums, plus 2^-45 per pixel for the rounding of
+    each term's quotient (the blurred planes are identical, so only the terms'
+    last bits and the order of the sums differ), and are bitwise repeatable;
+  * identical inputs give zeros at every scale.
+Every call goes through the C ABI.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from full_reference_video_amd import synth, vqm
+
+pytestmark = pytest.mark.gpu
+
+REL = 1e-10
+# Distinct dyadic coefficients of both signs, and a stable set with complex
+# poles: the recursion's wiring is visible in every output bit.
+DYADIC = np.array([0.5, 0.25, -0.125, 0.0625], np.float32)
+COMPLEX = np.array([0.136, 1.6, -0.94, 0.204], np.float32)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def _bits_equal(got, want):
+    got = np.ascontiguousarray(got, np.float32)
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))
+    assert bad[0].size == 0, (len(bad[0]), [b[:5] for b in bad], got[bad][:5], want[bad][:5])
+
+
+@pytest.mark.parametrize("sigma", [0.5, 1.5, 2.0, 7.25])
+def test_cascade_coefficients_match_the_oracle(torch_cuda, sigma):
+    _bits_equal(vqm.vqm_ss2_cascade_coefficients(sigma), oracle.ss2_cascade_coefficients(sigma))
+
+
+COEFS = {"cascade1.5": None, "complex": COMPLEX, "dyadic": DYADIC}
+
+
+def _coef(name):
+    return oracle.ss2_cascade_coefficients(1.5) if name == "cascade1.5" else COEFS[name]
+
+
+@pytest.mark.parametrize("coef", sorted(COEFS))
+@pytest.mark.parametrize("h,w", [(1, 1), (1, 33), (33, 1), (64, 32), (65, 33), (97, 130), (128, 31),
+                                 (324, 576), (481, 853), (2160, 3840)])
+def test_blur_bit_exact(torch_cuda, coef, h, w):
+    c = _coef(coef)
+    rng = np.random.default_rng(h * 7919 + w)
+    plane = rng.uniform(0.0, 1.0, (h, w)).astype(np.float32)
+    say(f"blur {w}x{h} {coef}")
+    want = oracle.ss2_blur(plane, c)
+    got = vqm.vqm_ss2_blur(_dev(torch_cuda, plane), c).cpu().numpy()
+    _bits_equal(got, want)
+
+
+def test_blur_in_place(torch_cuda):
+    c = _coef("cascade1.5")
+    plane = np.random.default_rng(3).uniform(0.0, 1.0, (77, 141)).astype(np.float32)
+    t = _dev(torch_cuda, plane)
+    vqm.vqm_ss2_blur(t, c, out=t)
+    _bits_equal(t.cpu().numpy(), oracle.ss2_blur(plane, c))
+
+
+def test_blur_of_an_impulse_keeps_its_subnormal_tail(torch_cuda):
+    # The response decays geometrically through fp32's subnormal range along
+    # the row; the device must carry it as the CPU does (no flush to zero).
+    c = _coef("cascade1.5")
+    plane = np.zeros((3, 300), np.float32)
+    plane[1, 2] = 1.0
+    want = oracle.ss2_blur(plane, c)
+    assert np.any((want != 0) & (np.abs(want) < np.finfo(np.float32).tiny))
+    _bits_equal(vqm.vqm_ss2_blur(_dev(torch_cuda, plane), c).cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("h,w", [(1, 1), (2, 3), (5, 7), (8, 8), (481, 853), (2160, 3840)])
+def test_downsample_bit_exact(torch_cuda, h, w):
+    plane = np.random.default_rng(h + w).uniform(0.0, 1.0, (h, w)).astype(np.float32)
+    _bits_equal(vqm.vqm_ss2_downsample(_dev(torch_cuda, plane)).cpu().numpy(), oracle.ss2_downsample(plane))
+
+
+def _check_close(got, want, npix):
+    # Beside the relative bar, each pixel's term may differ by its two
+    # quotients' rounding: the oracle's fp64 division (2^-53 relative) and the
+    # device's ff_div (about 2^-46), both below 2^-45 absolute for terms formed
+    # from quotients near 1.  That matters only where a sum is tiny, as on the
+    # last scales of small planes, where 1 - q cancels.
+    for idx in np.ndindex(want.shape):
+        tol = REL * abs(want[idx]) + npix * 2.0 ** -45
+        assert abs(got[idx] - want[idx]) <= tol, (idx, got[idx], want[idx])
+
+
+@pytest.mark.parametrize("w,h,nch,nscales", [(576, 324, 3, 6), (853, 481, 3, 6), (1920, 1080, 1, 4),
+                                             (17, 9, 2, 6), (1, 1, 1, 1), (3, 2, 3, 6), (3840, 2160, 3, 6)])
+def test_scale_sums_match_the_oracle(torch_cuda, w, h, nch, nscales):
+    torch = torch_cuda
+    ref, dis = synth.ss2_images(11, w, h, nch)
+    coef = oracle.ss2_cascade_coefficients(1.5)
+    say(f"chain {w}x{h}, {nch} channels, {nscales} scales")
+    want = oracle.ss2_chain(ref, dis, nscales, coef)
+    dr, dd = [_dev(torch, p) for p in ref], [_dev(torch, p) for p in dis]
+    got = vqm.vqm_ss2_scale_sums(dr, dd, nscales, coef)
+    worst = np.max(np.abs(got - want) / np.maximum(np.abs(want), 1e-300))
+    say(f"  largest relative difference {worst:.3e}")
+    _check_close(got, want, w * h)
+    assert np.array_equal(vqm.vqm_ss2_scale_sums(dr, dd, nscales, coef), got)
+
+
+def test_scale_sums_of_identical_inputs_are_zero(torch_cuda):
+    ref, _ = synth.ss2_images(12, 300, 170, 3)
+    dr = [_dev(torch_cuda, p) for p in ref]
+    got = vqm.vqm_ss2_scale_sums(dr, dr, 6, oracle.ss2_cascade_coefficients(1.5))
+    assert np.all(got == 0.0)
+
+
+def test_scale_sums_after_a_larger_frame(torch_cuda):
+    # The workspace grows for a large frame and is reused for a small one.
+    coef = oracle.ss2_cascade_coefficients(1.5)
+    for w, h in ((1280, 720), (96, 64)):
+        ref, dis = synth.ss2_images(13, w, h, 2)
+        want = oracle.ss2_chain(ref, dis, 5, coef)
+        got = vqm.vqm_ss2_scale_sums([_dev(torch_cuda, p) for p in ref], [_dev(torch_cuda, p) for p in dis], 5,
+                                     coef)
+        _check_close(got, want, w * h)
+
+
+def test_chain_refuses_bad_arguments(torch_cuda):
+    ref, dis = synth.ss2_images(14, 32, 16, 1)
+    coef = oracle.ss2_cascade_coefficients(1.5)
+    with pytest.raises(TypeError):
+        vqm.vqm_ss2_scale_sums(ref, dis, 2, coef)  # numpy arrays, not device tensors
+    dr, dd = [_dev(torch_cuda, p) for p in ref], [_dev(torch_cuda, p) for p in dis]
+    for ns in (0, 7):
+        with pytest.raises(vqm.VqmError):
+            vqm.vqm_ss2_scale_sums(dr, dd, ns, coef)
+    with pytest.raises(vqm.VqmError):
+        vqm.vqm_ss2_scale_sums(dr, dd, 2, np.array([np.nan, 0, 0, 0], np.float32))
+    with pytest.raises(vqm.VqmError):
+        vqm.vqm_ss2_scale_sums(dr * 4, dd * 4, 2, coef)  # four channels
