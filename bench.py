@@ -214,6 +214,59 @@ def copy_bandwidth(torch, mib: int = 1024, reps: int = 10) -> float:
     return round(2.0 * n * reps / el / 1e9, 1)
 
 
+def ss2_chain_work(w: int, h: int, nscales: int = 6, nch: int = 3):
+    """Per frame: the recursions' fp32 operations (five planes per channel,
+    a causal and an anticausal walk along every row and every column, 7
+    rounded operations a step), the pixels of every scale, and the bytes the
+    chain must move at the least (the two pictures' planes read once)."""
+    ops, px, sw, sh = 0, 0, w, h
+    for _ in range(nscales):
+        n = sw * sh
+        px += n
+        ops += nch * 5 * n * 2 * 2 * 7
+        sw, sh = (sw + 1) // 2, (sh + 1) // 2
+    return ops, px, 2 * nch * 4 * w * h
+
+
+def run_ss2_chain(args):
+    import numpy as np
+    import torch
+
+    from full_reference_video_amd import synth, vqm
+    sw, sh = (int(v) for v in args.ss2_chain.lower().split("x"))
+    nscales, nch = 6, 3
+    coef = vqm.vqm_ss2_cascade_coefficients(1.5)
+    # distinct frames, more bytes than the 256 MB last-level cache
+    sets = max(2, -(-(300 << 20) // (2 * nch * 4 * sw * sh)))
+    frames = []
+    for k in range(sets):
+        ref, dis = synth.ss2_images(20 + k, sw, sh, nch)
+        frames.append(([torch.from_numpy(p).cuda() for p in ref], [torch.from_numpy(p).cuda() for p in dis]))
+    torch.cuda.synchronize()
+    first = vqm.vqm_ss2_scale_sums(*frames[0], nscales, coef)
+    for f in frames:
+        vqm.vqm_ss2_scale_sums(*f, nscales, coef)  # warm-up (grows the workspace once)
+    n = max(1, args.steps)
+    runs = []
+    for _ in range(max(1, args.reps)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            vqm.vqm_ss2_scale_sums(*frames[i % sets], nscales, coef)
+        torch.cuda.synchronize()
+        runs.append((time.perf_counter() - t0) / n)
+    if not np.array_equal(vqm.vqm_ss2_scale_sums(*frames[0], nscales, coef), first):
+        raise RuntimeError("ssimulacra2 chain sums changed between calls")
+    el = sorted(runs)[len(runs) // 2]
+    ops, px, minbytes = ss2_chain_work(sw, sh, nscales, nch)
+    print(json.dumps({"metric": f"ssimulacra2 per-scale chain, {nch} channels of {sw}x{sh}, {nscales} scales, "
+                                "one blocking call per frame",
+                      "value": round(1.0 / el, 1), "unit": "frames/s", "ms_per_frame": round(el * 1e3, 4),
+                      "recursion_ops_per_frame": ops, "recursion_Gops": round(ops / el / 1e9, 1),
+                      "pixels_all_scales": px, "min_bytes_per_frame": minbytes,
+                      "frames": sets, "reps": len(runs)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +299,10 @@ def main():
     ap.add_argument("--ss2", default="", metavar="WxH",
                     help="only time the ssimulacra2 per-scale statistics (vqm_ss2_channel_sums) of three channels of "
                          "WxH seeded planes, against the HBM roofline of its seven fp32 planes per channel, and exit")
+    ap.add_argument("--ss2-chain", default="", metavar="WxH",
+                    help="only time the ssimulacra2 per-scale chain (vqm_ss2_scale_sums: six scales of multiplies, "
+                         "recursive blur, statistics and downsample) on three channels of WxH seeded planes, one "
+                         "blocking call per frame, and exit")
     ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
                     help="only time the library's streaming 16-byte non-temporal read over MIB MiB of device memory "
                          "(the HBM read ceiling of the decimation's loads) and exit")
@@ -299,6 +356,10 @@ def main():
                           "value": round(1.0 / el, 1), "unit": "calls/s", "us_per_call": round(el * 1e6, 2),
                           "algorithmic_bytes": alg, "GBps": round(gbps, 1),
                           "hbm_frac": round(gbps / HBM_PEAK_GBS, 4), "plane_sets": sets}), flush=True)
+        return
+
+    if args.ss2_chain:
+        run_ss2_chain(args)
         return
 
     if args.read_probe:

@@ -1,44 +1,74 @@
 // ss2_chain.hip — the ssimulacra2 per-scale chain on the device: the three
-// multiplies, the recursive blur along every row and then every column, and
-// the 2x2 downsample to the next scale.  The six sums per channel come from
-// ss2_stats.hip.
+// multiplies, the recursive blur along every row and then every column, the
+// statistics of the blurred planes, and the 2x2 downsample between scales.
 //
 // "Research-1363: Device-resident ssimulacra2 and a single-wait MS-SSIM on
 // SYCL", Finding 2: with contraction off and every product its own rounded
 // value, the multiplies, both blur passes and the downsample reproduce the
 // CPU bit for bit; Finding 7: the blur is a sequential recurrence along each
 // line, so a pass has one work-item per row or column, five blurs per
-// channel and scale.  The recursion (third order, caller coefficients
-// B, a1, a2, a3, at rest outside the line), causal then anticausal:
+// channel and scale; Finding 4: the six sums per channel come from exact
+// fp32 pairs in a fixed tree.  The recursion (third order, caller
+// coefficients B, a1, a2, a3, at rest outside the line), causal then
+// anticausal:
 //   w[i] = ((B x[i] + a3 w[i-3]) + a2 w[i-2]) + a1 w[i-1]
 //   y[i] = ((B w[i] + a3 y[i+3]) + a2 y[i+2]) + a1 y[i+1]
 // (the library is compiled with -ffp-contract=off, so each product here is
 // rounded on its own).
 //
-// Row pass.  The page's horizontal walk makes every lane of a load touch its
-// own cache line.  Here a workgroup owns 64 rows of one channel, one wave
-// per blurred plane (lane = row); 32-column chunks of the two images are
-// loaded row-contiguously into LDS, each lane walks its row through the
-// chunk (forming its plane's product on the fly, so the multiplies cost no
-// pass of their own), and the chunk's outputs leave LDS row-contiguously
-// again.  The causal outputs go to the output planes, and the anticausal
-// walk reads them back chunk by chunk from the right and overwrites them.
-// Column pass: lanes own consecutive columns (loads already contiguous
-// across the wave); it runs in place on the row pass's output.
+// The work is a set of independent sequential walks, one per line, plane,
+// channel and scale, so it is laid out for them:
+//  * Every scale runs in one launch per pass.  The downsampled images come
+//    first (the pyramid of the two pictures needs no blur), so the short
+//    lines of the small scales run beside the long ones of the first scale
+//    instead of after them.
+//  * A workgroup is four waves holding 51 lines of all five planes (255 of
+//    256 lanes), one wave per SIMD, so no SIMD carries two walkers while the
+//    others wait at a barrier.
+//  * No pass writes the causal outputs w: the causal walk keeps only its
+//    state (w[i-1], w[i-2], w[i-3]) at the end of every 32-sample chunk, and
+//    the anticausal walk, chunk by chunk from the end, recomputes the
+//    chunk's w from that state (the same operations on the same values, so
+//    the same bits) and walks back over it in registers.
+//  * Row pass: chunks of the two images are loaded two ahead into
+//    registers, staged through LDS row-contiguously (the page's horizontal
+//    walk made every lane of a load touch its own cache line), and each
+//    lane reads its row's samples there, times its plane's second factor
+//    (the other image for the products, a row of ones for a and b), so the
+//    multiplies cost no pass.  Outputs go back through LDS.
+//  * Column pass: lanes own columns (loads contiguous across a lane group);
+//    each 32-row chunk's five blurred planes meet in LDS and the chunk's
+//    pixels go straight into the statistics, so the blurred planes are never
+//    written.  One more small launch sums each (scale, channel)'s partials.
+#include "ss2_pairs.h"
 #include "vqm_kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace vqm {
 namespace {
 
-constexpr int kRowsPerGroup = 64;  // one row per lane
-constexpr int kChunk = 32;         // columns per LDS chunk
-constexpr int kPitch = kChunk + 1; // odd pitch: a lane per row reads distinct banks
-constexpr int kColBatch = 8;       // rows loaded together by a column walk
+using namespace ss2;
+
+constexpr int kChunk = 32;          // samples of a line per chunk
+constexpr int kPitch = kChunk + 1;  // odd pitch: lanes reading along their own rows hit distinct banks
+constexpr int kRing = 3;            // register sets: one chunk in use, two loading
 
 struct Coef {
     float B, a1, a2, a3;
+};
+
+template <int V>
+using Ic = std::integral_constant<int, V>;
+
+// Lines per workgroup and threads: five planes of 51 lines in four waves,
+// or one plane of 64 lines in one wave.
+template <int NP>
+struct Shape {
+    static constexpr int kLines = NP == 5 ? 51 : 64;
+    static constexpr int kThreads = NP == 5 ? 256 : 64;
+    static constexpr int kState = 3 * kThreads;  // floats of one checkpoint
 };
 
 // One step of the recursion: s1, s2, s3 are the newest, second and third
@@ -51,156 +81,392 @@ __device__ __forceinline__ float recur(const Coef &k, float x, float s1, float s
     return ((in + t3) + t2) + t1;
 }
 
-struct RowPass {
+struct State {
+    float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    __device__ __forceinline__ float step(const Coef &k, float x) {
+        const float y = recur(k, x, s1, s2, s3);
+        s3 = s2;
+        s2 = s1;
+        s1 = y;
+        return y;
+    }
+};
+
+// N steps over values held in registers, replaced by the outputs; forward
+// (index 0 first) or backward (index N - 1 first).
+template <int N, bool Back>
+__device__ __forceinline__ void walk_regs(const Coef &k, float (&v)[N], State &st) {
+#pragma unroll
+    for (int jj = 0; jj < N; ++jj) {
+        const int j = Back ? N - 1 - jj : jj;
+        v[j] = st.step(k, v[j]);
+    }
+}
+
+// One scale of the chain: its size, its images, its row-blurred planes
+// (NP per channel, pstride apart), and where its workgroups, checkpoints and
+// partials start.
+struct ScaleDesc {
+    int w, h;
+    long long pstride;
     const float *a[kSs2MaxChannels], *b[kSs2MaxChannels];
-    float *out[kSs2MaxChannels];  // NP planes per channel, pstride floats apart
+    float *rows[kSs2MaxChannels];
+    float *out[kSs2MaxChannels];       // column pass output (NULL: statistics only)
+    int row_block0, col_block0;        // first workgroup of the scale in each pass
+    long long ckpt_rows0, ckpt_cols0;  // first checkpoint float of the scale
+    int part0;                         // first partial of the scale
 };
 
-// The blurred plane p of a lane, from the two images' samples: a, b, a a,
-// b b, a b (p is uniform across a wave).
-template <int NP>
-__device__ __forceinline__ float plane_input(int p, float xa, float xb) {
-    if (NP == 1) return xa;
-    const float aa = xa * xa, bb = xb * xb, ab = xa * xb;
-    return p == 0 ? xa : p == 1 ? xb : p == 2 ? aa : p == 3 ? bb : ab;
+struct Chain {
+    ScaleDesc s[kSs2MaxScales];
+    int nscales, nch;
+    float *ckpt;
+    Pair *partials;  // NULL: no statistics
+    double *result;  // 6 doubles per (scale, channel)
+};
+
+// The scale of a workgroup (scales in order, first scale's blocks first).
+__device__ __forceinline__ int scale_of(const Chain &ch, int block, bool cols) {
+    int s = 0;
+    for (int t = 1; t < ch.nscales; ++t)
+        if (block >= (cols ? ch.s[t].col_block0 : ch.s[t].row_block0)) s = t;
+    return s;
 }
 
+// ------------------------------------------------------------------ row pass
+
 template <int NP>
-__global__ __launch_bounds__(64 * NP) void ss2_rows(RowPass rp, int w, int h, long long pstride, Coef k) {
-    constexpr int NT = 64 * NP;
+__global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coef k) {
+    constexpr int L = Shape<NP>::kLines, NT = Shape<NP>::kThreads, KS = Shape<NP>::kState;
     constexpr int NI = NP == 1 ? 1 : 2;  // image tiles
-    __shared__ float tin[NI][kRowsPerGroup][kPitch];
-    __shared__ float tout[NP][kRowsPerGroup][kPitch];
+    constexpr int RS = NT / kChunk;      // tile rows one pass of the workgroup covers
+    constexpr int KI = (L + RS - 1) / RS;
+    constexpr int TILE = L * kPitch;
+    __shared__ float tin[NI * TILE + kPitch];  // the image tiles, then a row of ones
+    __shared__ float tout[NP * TILE];
 
-    const int c = blockIdx.y;
-    const int r0 = blockIdx.x * kRowsPerGroup;
-    const int nrows = min(kRowsPerGroup, h - r0);
-    const int p = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const float *img[2] = {rp.a[c], NP == 1 ? rp.a[c] : rp.b[c]};
-    float *const out = rp.out[c] + (long long)p * pstride;
+    const int s = scale_of(chain, blockIdx.x, false);
+    const ScaleDesc &d = chain.s[s];
+    const int local = blockIdx.x - d.row_block0;
+    const int c = local % chain.nch, blk = local / chain.nch;
+    const int w = d.w, r0 = blk * L, nrows = min(L, d.h - r0);
+    const int t = threadIdx.x;
+    const int p = t / L, line = t % L;  // this thread's plane and row
+    const bool live = p < NP && line < nrows;
     const int nchunks = (w + kChunk - 1) / kChunk;
-    // a thread's share of a tile: column t % kChunk, rows t / kChunk + i NT / kChunk
-    const int tcol = threadIdx.x % kChunk, trow = threadIdx.x / kChunk;
-    // a wave's share of its own plane's tile: column lane % kChunk, rows lane / kChunk + 2i
-    const int wcol = lane % kChunk, wrow = lane / kChunk;
+    float *const ck = chain.ckpt + d.ckpt_rows0 + (long long)(blk * chain.nch + c) * nchunks * KS;
+    const float *img[2] = {d.a[c], NP == 1 ? d.a[c] : d.b[c]};
+    // the plane's factors: a = a 1, b = b 1, a a, b b, a b
+    const int f0 = (NP == 5 && (p == 1 || p == 3)) ? 1 : 0;
+    const int f1 = (NP == 5 && p >= 3) ? 1 : 0;
+    const float *src0 = tin + f0 * TILE + line * kPitch;
+    const float *src1 = (NP == 5 && p >= 2) ? tin + f1 * TILE + line * kPitch : tin + NI * TILE;
+    float *const mine = tout + min(p, NP - 1) * TILE + line * kPitch;
+    const int tcol = t % kChunk, trow = t / kChunk;  // tile share (loads and stores)
 
-    // causal walk, left to right
-    float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-    for (int ch = 0; ch < nchunks; ++ch) {
+    if (t < kPitch) tin[NI * TILE + t] = 1.0f;
+
+    float pre[kRing][NI][KI];
+    const bool full_rows = nrows == L;
+    auto fetch = [&](float (&dst)[NI][KI], int ch) {
+        if (ch < 0 || ch >= nchunks) return;
         const int c0 = ch * kChunk, n = min(kChunk, w - c0);
+        if (full_rows && n == kChunk) {  // every sample of the tile exists: no per-load guard
+#pragma unroll
+            for (int q = 0; q < NI; ++q) {
+                const float *src = img[q] + (long long)(r0 + trow) * w + c0 + tcol;
+#pragma unroll
+                for (int i = 0; i < KI; ++i)
+                    dst[q][i] = (i < KI - 1 || trow + i * RS < L) ? src[(long long)i * RS * w] : 0.0f;
+            }
+            return;
+        }
+#pragma unroll
+        for (int q = 0; q < NI; ++q)
+#pragma unroll
+            for (int i = 0; i < KI; ++i) {
+                const int row = trow + i * RS;
+                dst[q][i] = (row < nrows && tcol < n) ? img[q][(long long)(r0 + row) * w + c0 + tcol] : 0.0f;
+            }
+    };
+    auto stage = [&](const float (&src)[NI][KI]) {
+#pragma unroll
+        for (int q = 0; q < NI; ++q)
+#pragma unroll
+            for (int i = 0; i < KI; ++i) {
+                const int row = trow + i * RS;
+                if (i < KI - 1 || row < L) tin[q * TILE + row * kPitch + tcol] = src[q][i];
+            }
+    };
+    auto samples = [&](float (&v)[kChunk]) {
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) v[j] = src0[j] * src1[j];
+    };
+
+    // Causal walk over every chunk but the last, keeping each end state.
+    State f;
+    fetch(pre[0], 0);
+    fetch(pre[1], 1);
+    auto fbody = [&](auto S, int ch) {
+        constexpr int si = decltype(S)::value;
+        if (ch >= nchunks - 1) return;
+        stage(pre[si]);
+        __syncthreads();
+        fetch(pre[(si + 2) % kRing], ch + 2);
+        if (live) {
+            float v[kChunk];
+            samples(v);
+            walk_regs<kChunk, false>(k, v, f);
+            ck[ch * KS + t] = f.s1;
+            ck[ch * KS + NT + t] = f.s2;
+            ck[ch * KS + 2 * NT + t] = f.s3;
+        }
+        __syncthreads();
+    };
+    for (int ch = 0; ch < nchunks - 1; ch += kRing) {
+        fbody(Ic<0>{}, ch);
+        fbody(Ic<1>{}, ch + 1);
+        fbody(Ic<2>{}, ch + 2);
+    }
+
+    // Anticausal walk, last chunk first: recompute the chunk's causal
+    // outputs from the state before it (loaded a chunk ahead), walk back
+    // over them, store every plane's chunk row-contiguously.
+    State g;
+    State before[kRing];
+    auto fetch_state = [&](State &dst, int ch) {
+        if (ch <= 0) dst = State{};  // the line starts at rest
+        if (ch <= 0 || !live) return;
+        dst.s1 = ck[(ch - 1) * KS + t];
+        dst.s2 = ck[(ch - 1) * KS + NT + t];
+        dst.s3 = ck[(ch - 1) * KS + 2 * NT + t];
+    };
+    fetch(pre[0], nchunks - 1);
+    fetch(pre[1], nchunks - 2);
+    fetch_state(before[0], nchunks - 1);
+    auto bbody = [&](auto S, int ch) {
+        constexpr int si = decltype(S)::value;
+        if (ch < 0) return;
+        const int c0 = ch * kChunk, n = min(kChunk, w - c0);
+        stage(pre[si]);
+        __syncthreads();
+        fetch(pre[(si + 2) % kRing], ch - 2);
+        fetch_state(before[(si + 1) % kRing], ch - 1);
+        if (live) {
+            State r = before[si];
+            if (n == kChunk) {
+                float v[kChunk];
+                samples(v);
+                walk_regs<kChunk, false>(k, v, r);
+                walk_regs<kChunk, true>(k, v, g);
+#pragma unroll
+                for (int j = 0; j < kChunk; ++j) mine[j] = v[j];
+            } else {  // the row's last chunk: n < 32 samples, walked through LDS
+                for (int j = 0; j < n; ++j) mine[j] = r.step(k, src0[j] * src1[j]);
+                for (int j = n - 1; j >= 0; --j) mine[j] = g.step(k, mine[j]);
+            }
+        }
+        __syncthreads();
         if (tcol < n) {
-#pragma unroll
-            for (int t = 0; t < NI; ++t)
-                for (int i = trow; i < nrows; i += NT / kChunk)
-                    tin[t][i][tcol] = img[t][(long long)(r0 + i) * w + c0 + tcol];
-        }
-        __syncthreads();
-        if (lane < nrows) {
-            for (int j = 0; j < n; ++j) {
-                const float x = plane_input<NP>(p, tin[0][lane][j], tin[NI - 1][lane][j]);
-                const float v = recur(k, x, s1, s2, s3);
-                tout[p][lane][j] = v;
-                s3 = s2;
-                s2 = s1;
-                s1 = v;
+            for (int q = 0; q < NP; ++q) {
+                float *const o = d.rows[c] + (long long)q * d.pstride + (long long)r0 * w + c0 + tcol;
+                for (int i = trow; i < nrows; i += RS) o[(long long)i * w] = tout[q * TILE + i * kPitch + tcol];
             }
         }
-        __syncthreads();
-        if (wcol < n)
-            for (int i = wrow; i < nrows; i += 2) out[(long long)(r0 + i) * w + c0 + wcol] = tout[p][i][wcol];
-        // the next chunk's first barrier orders these reads of tout before
-        // its walk writes tout again
-    }
-
-    // anticausal walk, right to left, over the causal outputs (each wave
-    // reads and writes only its own plane's tile)
-    float q1 = 0.0f, q2 = 0.0f, q3 = 0.0f;
-    for (int ch = nchunks - 1; ch >= 0; --ch) {
-        const int c0 = ch * kChunk, n = min(kChunk, w - c0);
-        __syncthreads();
-        if (wcol < n)
-            for (int i = wrow; i < nrows; i += 2) tout[p][i][wcol] = out[(long long)(r0 + i) * w + c0 + wcol];
-        __syncthreads();
-        if (lane < nrows) {
-            for (int j = n - 1; j >= 0; --j) {
-                const float v = recur(k, tout[p][lane][j], q1, q2, q3);
-                tout[p][lane][j] = v;
-                q3 = q2;
-                q2 = q1;
-                q1 = v;
-            }
-        }
-        __syncthreads();
-        if (wcol < n)
-            for (int i = wrow; i < nrows; i += 2) out[(long long)(r0 + i) * w + c0 + wcol] = tout[p][i][wcol];
+    };
+    for (int ch = nchunks - 1; ch >= 0; ch -= kRing) {
+        bbody(Ic<0>{}, ch);
+        bbody(Ic<1>{}, ch - 1);
+        bbody(Ic<2>{}, ch - 2);
     }
 }
 
-struct ColPass {
-    float *planes[kSs2MaxChannels];  // NP planes per channel, pstride floats apart
-};
+// --------------------------------------------------------------- column pass
 
-// In place: each lane walks one column of one plane, kColBatch rows loaded
-// before any of them is used.
 template <int NP>
-__global__ __launch_bounds__(64 * NP) void ss2_cols(ColPass cp, int w, int h, long long pstride, Coef k) {
-    const int c = blockIdx.y;
-    const int p = threadIdx.x >> 6;
-    const int x = blockIdx.x * 64 + (threadIdx.x & 63);
-    if (x >= w) return;  // no barriers below
-    float *const col = cp.planes[c] + (long long)p * pstride + x;
+__global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_cols(Chain chain, Coef k) {
+    constexpr int L = Shape<NP>::kLines, NT = Shape<NP>::kThreads, KS = Shape<NP>::kState;
+    constexpr int CT = kChunk * L;  // pixels of a chunk
+    __shared__ float tile[NP * CT];  // [plane][row of the chunk][column]
+    __shared__ Pair red[6][NT / 64];
+
+    const int s = scale_of(chain, blockIdx.x, true);
+    const ScaleDesc &d = chain.s[s];
+    const int local = blockIdx.x - d.col_block0;
+    const int c = local % chain.nch, blk = local / chain.nch;
+    const int w = d.w, h = d.h, x0 = blk * L, ncols = min(L, w - x0);
     const long long W = w;
+    const int t = threadIdx.x;
+    const int p = t / L, x = t % L;  // this thread's plane and column
+    const bool live = p < NP && x < ncols;
+    const float *const col = d.rows[c] + (long long)min(p, NP - 1) * d.pstride + x0 + x;
+    float *const ocol = d.out[c] ? d.out[c] + (long long)min(p, NP - 1) * d.pstride + x0 + x : nullptr;
+    const int nchunks = (h + kChunk - 1) / kChunk;
+    float *const ck = chain.ckpt + d.ckpt_cols0 + (long long)(blk * chain.nch + c) * nchunks * KS;
+    const bool stats = chain.partials != nullptr;
+    float *const mine = tile + min(p, NP - 1) * CT + x;
 
-    float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-    int r = 0;
-    for (; r + kColBatch <= h; r += kColBatch) {
-        float v[kColBatch];
+    float v[kRing][kChunk];
+    auto load = [&](float (&dst)[kChunk], int ch) {
+        if (ch < 0 || ch >= nchunks || !live) return;
+        const int y0 = ch * kChunk, n = min(kChunk, h - y0);
+        const float *src = col + y0 * W;
+        if (n == kChunk) {  // no per-load guard
 #pragma unroll
-        for (int i = 0; i < kColBatch; ++i) v[i] = col[(r + i) * W];
-#pragma unroll
-        for (int i = 0; i < kColBatch; ++i) {
-            const float y = recur(k, v[i], s1, s2, s3);
-            s3 = s2;
-            s2 = s1;
-            s1 = y;
-            v[i] = y;
+            for (int i = 0; i < kChunk; ++i) dst[i] = src[i * W];
+            return;
         }
 #pragma unroll
-        for (int i = 0; i < kColBatch; ++i) col[(r + i) * W] = v[i];
-    }
-    for (; r < h; ++r) {
-        const float y = recur(k, col[r * W], s1, s2, s3);
-        s3 = s2;
-        s2 = s1;
-        s1 = y;
-        col[r * W] = y;
+        for (int i = 0; i < kChunk; ++i) dst[i] = i < n ? src[i * W] : 0.0f;
+    };
+
+    // Causal walk over every chunk but the last, keeping each end state.
+    State f;
+    load(v[0], 0);
+    load(v[1], 1);
+    auto fbody = [&](auto S, int ch) {
+        constexpr int si = decltype(S)::value;
+        if (ch >= nchunks - 1) return;
+        load(v[(si + 2) % kRing], ch + 2);
+        if (live) {
+            walk_regs<kChunk, false>(k, v[si], f);
+            ck[ch * KS + t] = f.s1;
+            ck[ch * KS + NT + t] = f.s2;
+            ck[ch * KS + 2 * NT + t] = f.s3;
+        }
+    };
+    for (int ch = 0; ch < nchunks - 1; ch += kRing) {
+        fbody(Ic<0>{}, ch);
+        fbody(Ic<1>{}, ch + 1);
+        fbody(Ic<2>{}, ch + 2);
     }
 
-    s1 = s2 = s3 = 0.0f;
-    r = h;
-    for (; r - kColBatch >= 0; r -= kColBatch) {
-        float v[kColBatch];  // v[i] is row r - 1 - i
+    // Anticausal walk, last chunk first; each chunk's five blurred planes
+    // then meet in LDS for the statistics of its pixels.
+    Acc acc[6];
+    int since_norm = 0;
+    State g;
+    State before[kRing];
+    auto fetch_state = [&](State &dst, int ch) {
+        if (ch <= 0) dst = State{};  // the line starts at rest
+        if (ch <= 0 || !live) return;
+        dst.s1 = ck[(ch - 1) * KS + t];
+        dst.s2 = ck[(ch - 1) * KS + NT + t];
+        dst.s3 = ck[(ch - 1) * KS + 2 * NT + t];
+    };
+    // the statistics' image samples of a chunk, thread t taking pixels
+    // t, t + NT, ... (row-major over the chunk's 32 x L)
+    constexpr int KP = (CT + NT - 1) / NT;
+    float ia[KP], ib[KP];
+    auto fetch_images = [&](int ch) {
+        const int y0 = ch * kChunk, n = min(kChunk, h - y0);
+        const float *ra = d.a[c] + (long long)y0 * w + x0, *rb = d.b[c] + (long long)y0 * w + x0;
+        const bool full = n == kChunk && ncols == L;
 #pragma unroll
-        for (int i = 0; i < kColBatch; ++i) v[i] = col[(r - 1 - i) * W];
-#pragma unroll
-        for (int i = 0; i < kColBatch; ++i) {
-            const float y = recur(k, v[i], s1, s2, s3);
-            s3 = s2;
-            s2 = s1;
-            s1 = y;
-            v[i] = y;
+        for (int m = 0; m < KP; ++m) {
+            const int q = t + m * NT, i = q / L, xx = q % L;
+            const bool in = full ? ((m + 1) * NT <= CT || q < CT) : (q < n * L && xx < ncols);
+            ia[m] = in ? ra[(long long)i * w + xx] : 0.0f;
+            ib[m] = in ? rb[(long long)i * w + xx] : 0.0f;
         }
+    };
+    load(v[0], nchunks - 1);
+    load(v[1], nchunks - 2);
+    fetch_state(before[0], nchunks - 1);
+    auto bbody = [&](auto S, int ch) {
+        constexpr int si = decltype(S)::value;
+        if (ch < 0) return;
+        const int y0 = ch * kChunk, n = min(kChunk, h - y0);
+        load(v[(si + 2) % kRing], ch - 2);
+        fetch_state(before[(si + 1) % kRing], ch - 1);
+        if (NP == 5 && stats) fetch_images(ch);
+        if (live) {
+            State r = before[si];
+            if (n == kChunk) {
+                walk_regs<kChunk, false>(k, v[si], r);
+                walk_regs<kChunk, true>(k, v[si], g);
+                if (stats) {
 #pragma unroll
-        for (int i = 0; i < kColBatch; ++i) col[(r - 1 - i) * W] = v[i];
+                    for (int i = 0; i < kChunk; ++i) mine[i * L] = v[si][i];
+                }
+                if (ocol) {
+#pragma unroll
+                    for (int i = 0; i < kChunk; ++i) ocol[(y0 + i) * W] = v[si][i];
+                }
+            } else {  // the column's last chunk: n < 32 rows, walked through LDS
+                for (int i = 0; i < n; ++i) mine[i * L] = r.step(k, col[(y0 + i) * W]);
+                for (int i = n - 1; i >= 0; --i) {
+                    const float y = g.step(k, mine[i * L]);
+                    mine[i * L] = y;
+                    if (ocol) ocol[(y0 + i) * W] = y;
+                }
+            }
+        }
+        if (NP == 5 && stats) {
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < KP; ++m) {
+                const int q = t + m * NT, xx = q % L;
+                if (q >= n * L || xx >= ncols) continue;
+                pixel_terms(ia[m], ib[m], tile[q], tile[CT + q], tile[2 * CT + q], tile[3 * CT + q],
+                            tile[4 * CT + q], acc);
+                if (++since_norm == 8) {
+                    since_norm = 0;
+#pragma unroll
+                    for (int u = 0; u < 6; ++u) acc[u].norm();
+                }
+            }
+            __syncthreads();
+        }
+    };
+    for (int ch = nchunks - 1; ch >= 0; ch -= kRing) {
+        bbody(Ic<0>{}, ch);
+        bbody(Ic<1>{}, ch - 1);
+        bbody(Ic<2>{}, ch - 2);
     }
-    for (; r > 0; --r) {
-        const float y = recur(k, col[(r - 1) * W], s1, s2, s3);
-        s3 = s2;
-        s2 = s1;
-        s1 = y;
-        col[(r - 1) * W] = y;
+
+    if (NP == 5 && stats) {
+        Pair sum[6];
+#pragma unroll
+        for (int m = 0; m < 6; ++m) {
+            acc[m].norm();
+            sum[m] = Pair{acc[m].hi, acc[m].lo};
+        }
+        block_pair_sum<NT>(sum, red);
+        if (t == 0) {
+#pragma unroll
+            for (int m = 0; m < 6; ++m) chain.partials[((long long)d.part0 + local) * 6 + m] = sum[m];
+        }
     }
 }
+
+// One workgroup per (channel, scale): the scale's column-block partials of
+// the channel in index order, then the workgroup tree; 6 doubles out.
+constexpr int kFinishThreads = 256;
+
+__global__ __launch_bounds__(kFinishThreads) void ss2_chain_finish(Chain chain) {
+    __shared__ Pair red[6][kFinishThreads / 64];
+    const int c = blockIdx.x, s = blockIdx.y;
+    const ScaleDesc &d = chain.s[s];
+    const int nblk = (d.w + Shape<5>::kLines - 1) / Shape<5>::kLines;
+    Pair sum[6];
+#pragma unroll
+    for (int m = 0; m < 6; ++m) sum[m] = Pair{0.0f, 0.0f};
+    for (int blk = threadIdx.x; blk < nblk; blk += kFinishThreads) {
+        const long long at = ((long long)d.part0 + (long long)blk * chain.nch + c) * 6;
+#pragma unroll
+        for (int m = 0; m < 6; ++m) sum[m] = ff_add(sum[m], chain.partials[at + m]);
+    }
+    block_pair_sum<kFinishThreads>(sum, red);
+    if (threadIdx.x == 0) {
+        double *r = chain.result + ((long long)s * chain.nch + c) * 6;
+#pragma unroll
+        for (int m = 0; m < 6; ++m) r[m] = (double)sum[m].hi + (double)sum[m].lo;
+        __threadfence_system();
+    }
+}
+
+// ---------------------------------------------------------------- downsample
 
 struct DownPass {
     const float *in[2 * kSs2MaxChannels];
@@ -224,37 +490,113 @@ __global__ __launch_bounds__(256) void ss2_down(DownPass d, int w, int h, int ow
     }
 }
 
-Coef coef_of(const float coef[4]) { return Coef{coef[0], coef[1], coef[2], coef[3]}; }
+template <int NP>
+int row_blocks(int h) {
+    return (h + Shape<NP>::kLines - 1) / Shape<NP>::kLines;
+}
+template <int NP>
+int col_blocks(int w) {
+    return (w + Shape<NP>::kLines - 1) / Shape<NP>::kLines;
+}
+template <int NP>
+long long rows_ckpt(int w, int h) {
+    return (long long)row_blocks<NP>(h) * ((w + kChunk - 1) / kChunk) * Shape<NP>::kState;
+}
+template <int NP>
+long long cols_ckpt(int w, int h) {
+    return (long long)col_blocks<NP>(w) * ((h + kChunk - 1) / kChunk) * Shape<NP>::kState;
+}
+
+// Fills the per-scale offsets; returns the checkpoint floats and partials
+// the chain needs.
+template <int NP>
+void plan(Chain &ch, long long *ckpt_floats, long long *partials) {
+    int rb = 0, cb = 0, part = 0;
+    long long ckr = 0, ckc = 0;
+    for (int s = 0; s < ch.nscales; ++s) {
+        ScaleDesc &d = ch.s[s];
+        d.row_block0 = rb;
+        d.col_block0 = cb;
+        d.ckpt_rows0 = ckr;
+        d.ckpt_cols0 = ckc;
+        d.part0 = part;
+        rb += row_blocks<NP>(d.h) * ch.nch;
+        cb += col_blocks<NP>(d.w) * ch.nch;
+        ckr += rows_ckpt<NP>(d.w, d.h) * ch.nch;
+        ckc += cols_ckpt<NP>(d.w, d.h) * ch.nch;
+        part += col_blocks<NP>(d.w) * ch.nch;
+    }
+    *ckpt_floats = std::max(ckr, ckc);  // the row pass's checkpoints are dead once the column pass runs
+    *partials = part;
+}
 
 }  // namespace
 
-hipError_t launch_ss2_rows(const float *const *a, const float *const *b, float *const *out, int nch, int nplanes,
-                           int w, int h, long long pstride, const float coef[4], hipStream_t stream,
-                           const KernelTimer &timer) {
-    if (nch < 1 || nch > kSs2MaxChannels || w < 1 || h < 1 || (nplanes != 1 && nplanes != 5))
-        return hipErrorInvalidValue;
-    RowPass rp{};
-    for (int c = 0; c < nch; ++c) {
-        rp.a[c] = a[c];
-        rp.b[c] = nplanes == 5 ? b[c] : a[c];
-        rp.out[c] = out[c];
+size_t ss2_chain_scratch_floats(int nch, int nplanes, const int *w, const int *h, int nscales) {
+    Chain ch{};
+    ch.nch = nch;
+    ch.nscales = nscales;
+    for (int s = 0; s < nscales; ++s) {
+        ch.s[s].w = w[s];
+        ch.s[s].h = h[s];
     }
-    const dim3 grid((h + kRowsPerGroup - 1) / kRowsPerGroup, nch);
+    long long ck = 0, part = 0;
     if (nplanes == 5)
-        return launch_kernel(ss2_rows<5>, grid, dim3(320), stream, timer, rp, w, h, pstride, coef_of(coef));
-    return launch_kernel(ss2_rows<1>, grid, dim3(64), stream, timer, rp, w, h, pstride, coef_of(coef));
+        plan<5>(ch, &ck, &part);
+    else
+        plan<1>(ch, &ck, &part);
+    return (size_t)ck + (size_t)part * 6 * 2;
 }
 
-hipError_t launch_ss2_cols(float *const *planes, int nch, int nplanes, int w, int h, long long pstride,
-                           const float coef[4], hipStream_t stream, const KernelTimer &timer) {
-    if (nch < 1 || nch > kSs2MaxChannels || w < 1 || h < 1 || (nplanes != 1 && nplanes != 5))
+hipError_t launch_ss2_chain(const Ss2ChainArgs &args, hipStream_t stream, const KernelTimer &rows_timer,
+                            const KernelTimer &cols_timer) {
+    const int np = args.nplanes, nch = args.nch, ns = args.nscales;
+    if (nch < 1 || nch > kSs2MaxChannels || ns < 1 || ns > kSs2MaxScales || (np != 1 && np != 5) || !args.scratch)
         return hipErrorInvalidValue;
-    ColPass cp{};
-    for (int c = 0; c < nch; ++c) cp.planes[c] = planes[c];
-    const dim3 grid((w + 63) / 64, nch);
-    if (nplanes == 5)
-        return launch_kernel(ss2_cols<5>, grid, dim3(320), stream, timer, cp, w, h, pstride, coef_of(coef));
-    return launch_kernel(ss2_cols<1>, grid, dim3(64), stream, timer, cp, w, h, pstride, coef_of(coef));
+    if (np == 1 && (nch != 1 || args.stats)) return hipErrorInvalidValue;
+    if (args.stats && !args.result) return hipErrorInvalidValue;
+    Chain ch{};
+    ch.nch = nch;
+    ch.nscales = ns;
+    for (int s = 0; s < ns; ++s) {
+        const Ss2Scale &in = args.scale[s];
+        ScaleDesc &d = ch.s[s];
+        if (in.w < 1 || in.h < 1) return hipErrorInvalidValue;
+        d.w = in.w;
+        d.h = in.h;
+        d.pstride = in.pstride;
+        for (int c = 0; c < nch; ++c) {
+            d.a[c] = in.a[c];
+            d.b[c] = np == 5 ? in.b[c] : in.a[c];
+            d.rows[c] = in.rows[c];
+            d.out[c] = in.out[c];
+        }
+    }
+    long long ck = 0, part = 0;
+    if (np == 5)
+        plan<5>(ch, &ck, &part);
+    else
+        plan<1>(ch, &ck, &part);
+    ch.ckpt = args.scratch;
+    ch.partials = args.stats ? reinterpret_cast<Pair *>(args.scratch + ck) : nullptr;
+    ch.result = args.result;
+    const Coef k{args.coef[0], args.coef[1], args.coef[2], args.coef[3]};
+    const ScaleDesc &last = ch.s[ns - 1];
+    const int nrow = last.row_block0 + (np == 5 ? row_blocks<5>(last.h) : row_blocks<1>(last.h)) * nch;
+    const int ncol = last.col_block0 + (np == 5 ? col_blocks<5>(last.w) : col_blocks<1>(last.w)) * nch;
+    hipError_t e;
+    if (np == 5) {
+        e = launch_kernel(ss2_rows<5>, dim3(nrow), dim3(Shape<5>::kThreads), stream, rows_timer, ch, k);
+        if (e == hipSuccess)
+            e = launch_kernel(ss2_cols<5>, dim3(ncol), dim3(Shape<5>::kThreads), stream, cols_timer, ch, k);
+    } else {
+        e = launch_kernel(ss2_rows<1>, dim3(nrow), dim3(Shape<1>::kThreads), stream, rows_timer, ch, k);
+        if (e == hipSuccess)
+            e = launch_kernel(ss2_cols<1>, dim3(ncol), dim3(Shape<1>::kThreads), stream, cols_timer, ch, k);
+    }
+    if (e != hipSuccess || !args.stats) return e;
+    hipLaunchKernelGGL(ss2_chain_finish, dim3(nch, ns), dim3(kFinishThreads), 0, stream, ch);
+    return hipGetLastError();
 }
 
 void ss2_downsampled_dim(int w, int h, int *ow, int *oh) {

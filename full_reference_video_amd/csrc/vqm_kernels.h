@@ -186,18 +186,38 @@ hipError_t launch_pair_ops(int op, const float *a, const float *b, float *out, i
 
 // ---------------------------------------------------------------- ssimulacra2 per-scale chain
 
-// The recursive blur's row pass over nch channels of w x h fp32 planes
-// (tightly packed).  nplanes 5: out[c] receives the five planes a, b, a a,
-// b b, a b of a[c], b[c], each blurred along its rows, pstride floats
-// apart; nplanes 1: out[c] receives a[c] blurred along its rows (b unused;
-// out may equal a).  coef = {B, a1, a2, a3}.
-hipError_t launch_ss2_rows(const float *const *a, const float *const *b, float *const *out, int nch, int nplanes,
-                           int w, int h, long long pstride, const float coef[4], hipStream_t stream,
-                           const KernelTimer &timer);
+constexpr int kSs2MaxScales = 6;
 
-// The column pass, in place on nplanes (1 or 5) planes per channel.
-hipError_t launch_ss2_cols(float *const *planes, int nch, int nplanes, int w, int h, long long pstride,
-                           const float coef[4], hipStream_t stream, const KernelTimer &timer);
+// One scale of the chain: w x h fp32 images a[c], b[c] (tightly packed), the
+// row pass's output planes rows[c] (nplanes per channel, pstride floats
+// apart), and (optionally, NULL entries for none) the column pass's output
+// planes out[c], laid out like rows[c] (may equal rows[c]).
+struct Ss2Scale {
+    int w, h;
+    long long pstride;
+    const float *a[kSs2MaxChannels], *b[kSs2MaxChannels];
+    float *rows[kSs2MaxChannels];
+    float *out[kSs2MaxChannels];
+};
+
+// The recursive blur of every scale in two launches (rows, then columns).
+// nplanes 5: per channel the five planes a, b, a a, b b, a b; with stats,
+// the column pass also forms each workgroup's six ssimulacra2 sums and a
+// third launch sums them into result[(s * nch + c) * 6 ..] (6 doubles per
+// scale and channel, device-visible).  nplanes 1 (nch 1, no stats): the
+// blur of a alone.  coef = {B, a1, a2, a3}.  scratch: device memory of
+// ss2_chain_scratch_floats(...) floats (checkpoints and partials).
+struct Ss2ChainArgs {
+    Ss2Scale scale[kSs2MaxScales];
+    int nscales, nch, nplanes;
+    bool stats;
+    float coef[4];
+    float *scratch;
+    double *result;
+};
+size_t ss2_chain_scratch_floats(int nch, int nplanes, const int *w, const int *h, int nscales);
+hipError_t launch_ss2_chain(const Ss2ChainArgs &args, hipStream_t stream, const KernelTimer &rows_timer,
+                            const KernelTimer &cols_timer);
 
 // ceil(w/2) x ceil(h/2).
 void ss2_downsampled_dim(int w, int h, int *ow, int *oh);

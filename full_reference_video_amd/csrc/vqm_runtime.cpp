@@ -1027,9 +1027,23 @@ int ss2_blur_plane(const float *in, float *out, int w, int h, const float *coef)
     if (rc) return rc;
     vqm_ctx *ctx = lease.ctx;
     if ((rc = device_only(ctx, in, "input plane")) || (rc = device_only(ctx, out, "output plane"))) return rc;
+    if ((rc = ss2c_workspace(ctx, vqm::ss2_chain_scratch_floats(1, 1, &w, &h, 1)))) return rc;
+    vqm::Ss2ChainArgs args{};
+    vqm::Ss2Scale &sc = args.scale[0];
+    sc.w = w;
+    sc.h = h;
+    sc.pstride = (long long)w * h;
+    sc.a[0] = in;
+    sc.rows[0] = out;  // the row pass writes out, the column pass then works in place
+    sc.out[0] = out;
+    args.nscales = 1;
+    args.nch = 1;
+    args.nplanes = 1;
+    args.stats = false;
+    memcpy(args.coef, coef, sizeof args.coef);
+    args.scratch = ctx->ss2c_work;
     const vqm::KernelTimer none;
-    hipError_t e = vqm::launch_ss2_rows(&in, &in, &out, 1, 1, w, h, (long long)w * h, coef, ctx->stream, none);
-    if (e == hipSuccess) e = vqm::launch_ss2_cols(&out, 1, 1, w, h, (long long)w * h, coef, ctx->stream, none);
+    const hipError_t e = vqm::launch_ss2_chain(args, ctx->stream, none, none);
     if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
     HIP_TRY(hipStreamSynchronize(ctx->stream));
     return 0;
@@ -1050,14 +1064,15 @@ int ss2_down_plane(const float *in, float *out, int w, int h) {
     return 0;
 }
 
-constexpr int kSs2MaxScales = 6;
+using vqm::kSs2MaxScales;
 
 size_t align64(size_t n) { return (n + 63) & ~(size_t)63; }
 
-// Every scale enqueued on one stream: per scale the downsample (from the
-// second scale on), the row pass with the products, the column pass, and
-// the statistics into the scale's span of the pinned result block; one
-// wait, one read-back.
+// Every scale enqueued on one stream: the pyramid of the two pictures (a
+// downsample launch per later scale), then the row pass of every scale with
+// the products, the column pass of every scale with the statistics, and the
+// sums of each (scale, channel)'s partials into the pinned result block;
+// one wait, one read-back.
 int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, int h, int nscales,
               const float *coef, double *sums) {
     if (!ref || !dis || !sums) return fail(-EINVAL, "NULL plane array or sums pointer");
@@ -1078,20 +1093,25 @@ int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, 
         if ((rc = device_only(ctx, ref[c], "reference plane")) || (rc = device_only(ctx, dis[c], "distorted plane")))
             return rc;
 
-    // sizes; the workspace holds five blurred planes per channel at the
-    // first scale's size, then two images per channel for every later scale
+    // The workspace: the chain's checkpoints and partials, then per scale
+    // the five row-blurred planes of every channel, then the two images of
+    // every channel of every later scale.
     int sw[kSs2MaxScales], sh[kSs2MaxScales];
-    size_t pyr_off[kSs2MaxScales] = {0};
+    size_t ps[kSs2MaxScales], rows_off[kSs2MaxScales], pyr_off[kSs2MaxScales] = {0};
     sw[0] = w;
     sh[0] = h;
-    const size_t ps0 = align64((size_t)w * h);
-    size_t total = 5 * (size_t)nch * ps0;
-    for (int s = 1; s < nscales; ++s) {
-        vqm::ss2_downsampled_dim(sw[s - 1], sh[s - 1], &sw[s], &sh[s]);
-        pyr_off[s] = total;
-        total += 2 * (size_t)nch * align64((size_t)sw[s] * sh[s]);
+    for (int s = 1; s < nscales; ++s) vqm::ss2_downsampled_dim(sw[s - 1], sh[s - 1], &sw[s], &sh[s]);
+    size_t total = align64(vqm::ss2_chain_scratch_floats(nch, 5, sw, sh, nscales));
+    for (int s = 0; s < nscales; ++s) {
+        ps[s] = align64((size_t)sw[s] * sh[s]);
+        rows_off[s] = total;
+        total += 5 * (size_t)nch * ps[s];
     }
-    if ((rc = ss2c_workspace(ctx, total)) || (rc = ss2_buffers(ctx))) return rc;
+    for (int s = 1; s < nscales; ++s) {
+        pyr_off[s] = total;
+        total += 2 * (size_t)nch * ps[s];
+    }
+    if ((rc = ss2c_workspace(ctx, total))) return rc;
     if (!ctx->ss2c_result_host) {
         HIP_TRY_ALLOC(hipHostMalloc(&ctx->ss2c_result_host, 6 * vqm::kSs2MaxChannels * kSs2MaxScales * sizeof(double),
                                     hipHostMallocMapped | hipHostMallocCoherent));
@@ -1100,48 +1120,48 @@ int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, 
     const int nres = 6 * nch * nscales;
     for (int k = 0; k < nres; ++k) ctx->ss2c_result_host[k] = NAN;
 
-    const vqm::KernelTimer none;
     float *const work = ctx->ss2c_work;
-    const float *a[vqm::kSs2MaxChannels], *b[vqm::kSs2MaxChannels];
-    for (int c = 0; c < nch; ++c) {
-        a[c] = ref[c];
-        b[c] = dis[c];
-    }
+    vqm::Ss2ChainArgs args{};
+    args.nscales = nscales;
+    args.nch = nch;
+    args.nplanes = 5;
+    args.stats = true;
+    memcpy(args.coef, coef, sizeof args.coef);
+    args.scratch = work;
+    args.result = ctx->ss2c_result_dev;
     hipError_t e = hipSuccess;
     for (int s = 0; s < nscales && e == hipSuccess; ++s) {
-        const long long n = (long long)sw[s] * sh[s];
-        const size_t ps = align64((size_t)n);
-        if (s > 0) {
+        vqm::Ss2Scale &sc = args.scale[s];
+        sc.w = sw[s];
+        sc.h = sh[s];
+        sc.pstride = (long long)ps[s];
+        for (int c = 0; c < nch; ++c) {
+            sc.rows[c] = work + rows_off[s] + 5 * (size_t)c * ps[s];
+            sc.out[c] = nullptr;
+            if (s == 0) {
+                sc.a[c] = ref[c];
+                sc.b[c] = dis[c];
+            } else {
+                float *na = work + pyr_off[s] + (2 * (size_t)c) * ps[s];
+                float *nb = work + pyr_off[s] + (2 * (size_t)c + 1) * ps[s];
+                sc.a[c] = na;
+                sc.b[c] = nb;
+            }
+        }
+        if (s > 0) {  // the pyramid: this scale's images from the previous scale's
             const float *from[2 * vqm::kSs2MaxChannels];
             float *to[2 * vqm::kSs2MaxChannels];
             for (int c = 0; c < nch; ++c) {
-                from[2 * c] = a[c];
-                from[2 * c + 1] = b[c];
-                to[2 * c] = work + pyr_off[s] + (2 * (size_t)c) * ps;
-                to[2 * c + 1] = work + pyr_off[s] + (2 * (size_t)c + 1) * ps;
+                from[2 * c] = args.scale[s - 1].a[c];
+                from[2 * c + 1] = args.scale[s - 1].b[c];
+                to[2 * c] = const_cast<float *>(sc.a[c]);
+                to[2 * c + 1] = const_cast<float *>(sc.b[c]);
             }
             e = vqm::launch_ss2_down(from, to, 2 * nch, sw[s - 1], sh[s - 1], ctx->stream);
-            for (int c = 0; c < nch; ++c) {
-                a[c] = to[2 * c];
-                b[c] = to[2 * c + 1];
-            }
         }
-        float *blur[vqm::kSs2MaxChannels];
-        for (int c = 0; c < nch; ++c) blur[c] = work + 5 * (size_t)c * ps0;
-        if (e == hipSuccess)
-            e = vqm::launch_ss2_rows(a, b, blur, nch, 5, sw[s], sh[s], (long long)ps, coef, ctx->stream, none);
-        if (e == hipSuccess)
-            e = vqm::launch_ss2_cols(blur, nch, 5, sw[s], sh[s], (long long)ps, coef, ctx->stream, none);
-        const float *planes[7 * vqm::kSs2MaxChannels];
-        for (int c = 0; c < nch; ++c) {
-            planes[7 * c] = a[c];
-            planes[7 * c + 1] = b[c];
-            for (int p = 0; p < 5; ++p) planes[7 * c + 2 + p] = blur[c] + (size_t)p * ps;
-        }
-        if (e == hipSuccess)
-            e = vqm::launch_ss2_sums(planes, nch, n, ctx->ss2_partials, ctx->ss2c_result_dev + 6 * (size_t)nch * s,
-                                     ctx->stream);
     }
+    const vqm::KernelTimer none;
+    if (e == hipSuccess) e = vqm::launch_ss2_chain(args, ctx->stream, none, none);
     if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
     HIP_TRY(hipStreamSynchronize(ctx->stream));  // the one wait
     memcpy(sums, ctx->ss2c_result_host, nres * sizeof(double));
