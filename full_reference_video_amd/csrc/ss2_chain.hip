@@ -69,6 +69,7 @@ struct Shape {
     static constexpr int kLines = NP == 5 ? 51 : 64;
     static constexpr int kThreads = NP == 5 ? 256 : 64;
     static constexpr int kState = 3 * kThreads;  // floats of one checkpoint
+    static constexpr int kRowChunk = NP == 5 ? 64 : 32;  // columns per chunk of the row pass
 };
 
 // One step of the recursion: s1, s2, s3 are the newest, second and third
@@ -138,11 +139,12 @@ __device__ __forceinline__ int scale_of(const Chain &ch, int block, bool cols) {
 template <int NP>
 __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coef k) {
     constexpr int L = Shape<NP>::kLines, NT = Shape<NP>::kThreads, KS = Shape<NP>::kState;
+    constexpr int CH = Shape<NP>::kRowChunk, PT = CH + 1;  // chunk columns, tile pitch
     constexpr int NI = NP == 1 ? 1 : 2;  // image tiles
-    constexpr int RS = NT / kChunk;      // tile rows one pass of the workgroup covers
+    constexpr int RS = NT / CH;      // tile rows one pass of the workgroup covers
     constexpr int KI = (L + RS - 1) / RS;
-    constexpr int TILE = L * kPitch;
-    __shared__ float tin[NI * TILE + kPitch];  // the image tiles, then a row of ones
+    constexpr int TILE = L * PT;
+    __shared__ float tin[NI * TILE + PT];  // the image tiles, then a row of ones
     __shared__ float tout[NP * TILE];
 
     const int s = scale_of(chain, blockIdx.x, false);
@@ -153,25 +155,25 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
     const int t = threadIdx.x;
     const int p = t / L, line = t % L;  // this thread's plane and row
     const bool live = p < NP && line < nrows;
-    const int nchunks = (w + kChunk - 1) / kChunk;
+    const int nchunks = (w + CH - 1) / CH;
     float *const ck = chain.ckpt + d.ckpt_rows0 + (long long)(blk * chain.nch + c) * nchunks * KS;
     const float *img[2] = {d.a[c], NP == 1 ? d.a[c] : d.b[c]};
     // the plane's factors: a = a 1, b = b 1, a a, b b, a b
     const int f0 = (NP == 5 && (p == 1 || p == 3)) ? 1 : 0;
     const int f1 = (NP == 5 && p >= 3) ? 1 : 0;
-    const float *src0 = tin + f0 * TILE + line * kPitch;
-    const float *src1 = (NP == 5 && p >= 2) ? tin + f1 * TILE + line * kPitch : tin + NI * TILE;
-    float *const mine = tout + min(p, NP - 1) * TILE + line * kPitch;
-    const int tcol = t % kChunk, trow = t / kChunk;  // tile share (loads and stores)
+    const float *src0 = tin + f0 * TILE + line * PT;
+    const float *src1 = (NP == 5 && p >= 2) ? tin + f1 * TILE + line * PT : tin + NI * TILE;
+    float *const mine = tout + min(p, NP - 1) * TILE + line * PT;
+    const int tcol = t % CH, trow = t / CH;  // tile share (loads and stores)
 
-    if (t < kPitch) tin[NI * TILE + t] = 1.0f;
+    if (t < PT) tin[NI * TILE + t] = 1.0f;
 
     float pre[kRing][NI][KI];
     const bool full_rows = nrows == L;
     auto fetch = [&](float (&dst)[NI][KI], int ch) {
         if (ch < 0 || ch >= nchunks) return;
-        const int c0 = ch * kChunk, n = min(kChunk, w - c0);
-        if (full_rows && n == kChunk) {  // every sample of the tile exists: no per-load guard
+        const int c0 = ch * CH, n = min(CH, w - c0);
+        if (full_rows && n == CH) {  // every sample of the tile exists: no per-load guard
 #pragma unroll
             for (int q = 0; q < NI; ++q) {
                 const float *src = img[q] + (long long)(r0 + trow) * w + c0 + tcol;
@@ -195,12 +197,12 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
 #pragma unroll
             for (int i = 0; i < KI; ++i) {
                 const int row = trow + i * RS;
-                if (i < KI - 1 || row < L) tin[q * TILE + row * kPitch + tcol] = src[q][i];
+                if (i < KI - 1 || row < L) tin[q * TILE + row * PT + tcol] = src[q][i];
             }
     };
-    auto samples = [&](float (&v)[kChunk]) {
+    auto samples = [&](float (&v)[CH]) {
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) v[j] = src0[j] * src1[j];
+        for (int j = 0; j < CH; ++j) v[j] = src0[j] * src1[j];
     };
 
     // Causal walk over every chunk but the last, keeping each end state.
@@ -214,9 +216,9 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
         __syncthreads();
         fetch(pre[(si + 2) % kRing], ch + 2);
         if (live) {
-            float v[kChunk];
+            float v[CH];
             samples(v);
-            walk_regs<kChunk, false>(k, v, f);
+            walk_regs<CH, false>(k, v, f);
             ck[ch * KS + t] = f.s1;
             ck[ch * KS + NT + t] = f.s2;
             ck[ch * KS + 2 * NT + t] = f.s3;
@@ -247,20 +249,20 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
     auto bbody = [&](auto S, int ch) {
         constexpr int si = decltype(S)::value;
         if (ch < 0) return;
-        const int c0 = ch * kChunk, n = min(kChunk, w - c0);
+        const int c0 = ch * CH, n = min(CH, w - c0);
         stage(pre[si]);
         __syncthreads();
         fetch(pre[(si + 2) % kRing], ch - 2);
         fetch_state(before[(si + 1) % kRing], ch - 1);
         if (live) {
             State r = before[si];
-            if (n == kChunk) {
-                float v[kChunk];
+            if (n == CH) {
+                float v[CH];
                 samples(v);
-                walk_regs<kChunk, false>(k, v, r);
-                walk_regs<kChunk, true>(k, v, g);
+                walk_regs<CH, false>(k, v, r);
+                walk_regs<CH, true>(k, v, g);
 #pragma unroll
-                for (int j = 0; j < kChunk; ++j) mine[j] = v[j];
+                for (int j = 0; j < CH; ++j) mine[j] = v[j];
             } else {  // the row's last chunk: n < 32 samples, walked through LDS
                 for (int j = 0; j < n; ++j) mine[j] = r.step(k, src0[j] * src1[j]);
                 for (int j = n - 1; j >= 0; --j) mine[j] = g.step(k, mine[j]);
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
         if (tcol < n) {
             for (int q = 0; q < NP; ++q) {
                 float *const o = d.rows[c] + (long long)q * d.pstride + (long long)r0 * w + c0 + tcol;
-                for (int i = trow; i < nrows; i += RS) o[(long long)i * w] = tout[q * TILE + i * kPitch + tcol];
+                for (int i = trow; i < nrows; i += RS) o[(long long)i * w] = tout[q * TILE + i * PT + tcol];
             }
         }
     };
@@ -500,7 +502,8 @@ int col_blocks(int w) {
 }
 template <int NP>
 long long rows_ckpt(int w, int h) {
-    return (long long)row_blocks<NP>(h) * ((w + kChunk - 1) / kChunk) * Shape<NP>::kState;
+    return (long long)row_blocks<NP>(h) * ((w + Shape<NP>::kRowChunk - 1) / Shape<NP>::kRowChunk) *
+           Shape<NP>::kState;
 }
 template <int NP>
 long long cols_ckpt(int w, int h) {
