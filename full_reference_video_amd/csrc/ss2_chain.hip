@@ -346,7 +346,6 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_cols(Chain chain, Coe
     // Anticausal walk, last chunk first; each chunk's five blurred planes
     // then meet in LDS for the statistics of its pixels.
     Acc acc[6];
-    int since_norm = 0;
     State g;
     State before[kRing];
     auto fetch_state = [&](State &dst, int ch) {
@@ -406,18 +405,20 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_cols(Chain chain, Coe
         }
         if (NP == 5 && stats) {
             __syncthreads();
+            // branch-free over the thread's pixels (one basic block, so their
+            // long pair-arithmetic chains interleave); a pixel outside the
+            // plane enters as zeros, whose terms are exactly 0
 #pragma unroll
             for (int m = 0; m < KP; ++m) {
                 const int q = t + m * NT, xx = q % L;
-                if (q >= n * L || xx >= ncols) continue;
-                pixel_terms(ia[m], ib[m], tile[q], tile[CT + q], tile[2 * CT + q], tile[3 * CT + q],
-                            tile[4 * CT + q], acc);
-                if (++since_norm == 8) {
-                    since_norm = 0;
-#pragma unroll
-                    for (int u = 0; u < 6; ++u) acc[u].norm();
-                }
+                const bool in = q < n * L && xx < ncols;
+                const int qq = in ? q : 0;
+                pixel_terms(in ? ia[m] : 0.0f, in ? ib[m] : 0.0f, in ? tile[qq] : 0.0f, in ? tile[CT + qq] : 0.0f,
+                            in ? tile[2 * CT + qq] : 0.0f, in ? tile[3 * CT + qq] : 0.0f,
+                            in ? tile[4 * CT + qq] : 0.0f, acc);
             }
+#pragma unroll
+            for (int u = 0; u < 6; ++u) acc[u].norm();
             __syncthreads();
         }
     };
@@ -557,6 +558,7 @@ hipError_t launch_ss2_chain(const Ss2ChainArgs &args, hipStream_t stream, const 
     if (nch < 1 || nch > kSs2MaxChannels || ns < 1 || ns > kSs2MaxScales || (np != 1 && np != 5) || !args.scratch)
         return hipErrorInvalidValue;
     if (np == 1 && (nch != 1 || args.stats)) return hipErrorInvalidValue;
+    if (np == 5 && !args.stats) return hipErrorInvalidValue;  // the five-plane column pass always sums
     if (args.stats && !args.result) return hipErrorInvalidValue;
     Chain ch{};
     ch.nch = nch;
