@@ -22,9 +22,13 @@
 //    first (the pyramid of the two pictures needs no blur), so the short
 //    lines of the small scales run beside the long ones of the first scale
 //    instead of after them.
-//  * A workgroup is four waves holding 51 lines of all five planes (255 of
-//    256 lanes), one wave per SIMD, so no SIMD carries two walkers while the
-//    others wait at a barrier.
+//  * A workgroup is four waves, one per SIMD.  The row pass holds 51 rows of
+//    all five planes in its 256 lanes (255 used), so no SIMD carries two
+//    walkers while the others wait at a barrier.  The column pass holds 32
+//    columns of all five planes (160 lanes walk, all 256 form the
+//    statistics): its loads are then whole 128-byte lines, where 51-column
+//    blocks shared lines with their neighbours and fetched 1.6 times the
+//    bytes they used.
 //  * No pass writes the causal outputs w: the causal walk keeps only its
 //    state (w[i-1], w[i-2], w[i-3]) at the end of every 32-sample chunk, and
 //    the anticausal walk, chunk by chunk from the end, recomputes the
@@ -66,7 +70,8 @@ using Ic = std::integral_constant<int, V>;
 // or one plane of 64 lines in one wave.
 template <int NP>
 struct Shape {
-    static constexpr int kLines = NP == 5 ? 51 : 64;
+    static constexpr int kRowLines = NP == 5 ? 51 : 64;  // rows per row-pass workgroup (5 x 51 of 256 lanes)
+    static constexpr int kColLines = NP == 5 ? 32 : 64;  // columns per column-pass workgroup (128-byte rows)
     static constexpr int kThreads = NP == 5 ? 256 : 64;
     static constexpr int kState = 3 * kThreads;  // floats of one checkpoint
     static constexpr int kRowChunk = NP == 5 ? 64 : 32;  // columns per chunk of the row pass
@@ -138,7 +143,7 @@ __device__ __forceinline__ int scale_of(const Chain &ch, int block, bool cols) {
 
 template <int NP>
 __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coef k) {
-    constexpr int L = Shape<NP>::kLines, NT = Shape<NP>::kThreads, KS = Shape<NP>::kState;
+    constexpr int L = Shape<NP>::kRowLines, NT = Shape<NP>::kThreads, KS = Shape<NP>::kState;
     constexpr int CH = Shape<NP>::kRowChunk, PT = CH + 1;  // chunk columns, tile pitch
     constexpr int NI = NP == 1 ? 1 : 2;  // image tiles
     constexpr int RS = NT / CH;      // tile rows one pass of the workgroup covers
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
 
 template <int NP>
 __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_cols(Chain chain, Coef k) {
-    constexpr int L = Shape<NP>::kLines, NT = Shape<NP>::kThreads, KS = Shape<NP>::kState;
+    constexpr int L = Shape<NP>::kColLines, NT = Shape<NP>::kThreads, KS = Shape<NP>::kState;
     constexpr int CT = kChunk * L;  // pixels of a chunk
     __shared__ float tile[NP * CT];  // [plane][row of the chunk][column]
     __shared__ Pair red[6][NT / 64];
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(kFinishThreads) void ss2_chain_finish(Chain chain) 
     __shared__ Pair red[6][kFinishThreads / 64];
     const int c = blockIdx.x, s = blockIdx.y;
     const ScaleDesc &d = chain.s[s];
-    const int nblk = (d.w + Shape<5>::kLines - 1) / Shape<5>::kLines;
+    const int nblk = (d.w + Shape<5>::kColLines - 1) / Shape<5>::kColLines;
     Pair sum[6];
 #pragma unroll
     for (int m = 0; m < 6; ++m) sum[m] = Pair{0.0f, 0.0f};
@@ -495,11 +500,11 @@ __global__ __launch_bounds__(256) void ss2_down(DownPass d, int w, int h, int ow
 
 template <int NP>
 int row_blocks(int h) {
-    return (h + Shape<NP>::kLines - 1) / Shape<NP>::kLines;
+    return (h + Shape<NP>::kRowLines - 1) / Shape<NP>::kRowLines;
 }
 template <int NP>
 int col_blocks(int w) {
-    return (w + Shape<NP>::kLines - 1) / Shape<NP>::kLines;
+    return (w + Shape<NP>::kColLines - 1) / Shape<NP>::kColLines;
 }
 template <int NP>
 long long rows_ckpt(int w, int h) {
