@@ -144,13 +144,17 @@ __device__ __forceinline__ int scale_of(const Chain &ch, int block, bool cols) {
 template <int NP>
 __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coef k) {
     constexpr int L = Shape<NP>::kRowLines, NT = Shape<NP>::kThreads, KS = Shape<NP>::kState;
-    constexpr int CH = Shape<NP>::kRowChunk, PT = CH + 1;  // chunk columns, tile pitch
+    // chunk columns; tile pitch CH + 4: each lane's row starts 16-byte aligned
+    // (so its 64 samples move as 16-byte LDS accesses) and the rows of 16
+    // consecutive lanes start 4 banks apart, which keeps those accesses free
+    // of bank conflicts
+    constexpr int CH = Shape<NP>::kRowChunk, PT = CH + 4;
     constexpr int NI = NP == 1 ? 1 : 2;  // image tiles
     constexpr int RS = NT / CH;      // tile rows one pass of the workgroup covers
     constexpr int KI = (L + RS - 1) / RS;
     constexpr int TILE = L * PT;
-    __shared__ float tin[NI * TILE + PT];  // the image tiles, then a row of ones
-    __shared__ float tout[NP * TILE];
+    __shared__ __attribute__((aligned(16))) float tin[NI * TILE + PT];  // the image tiles, then a row of ones
+    __shared__ __attribute__((aligned(16))) float tout[NP * TILE];
 
     const int s = scale_of(chain, blockIdx.x, false);
     const ScaleDesc &d = chain.s[s];
@@ -274,7 +278,16 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
             }
         }
         __syncthreads();
-        if (tcol < n) {
+        if (full_rows && n == CH) {  // every output of the tile exists: unrolled, unguarded but the last row
+#pragma unroll
+            for (int q = 0; q < NP; ++q) {
+                float *const o = d.rows[c] + (long long)q * d.pstride + (long long)(r0 + trow) * w + c0 + tcol;
+#pragma unroll
+                for (int i = 0; i < KI; ++i)
+                    if (i < KI - 1 || trow + i * RS < L)
+                        o[(long long)i * RS * w] = tout[q * TILE + (trow + i * RS) * PT + tcol];
+            }
+        } else if (tcol < n) {
             for (int q = 0; q < NP; ++q) {
                 float *const o = d.rows[c] + (long long)q * d.pstride + (long long)r0 * w + c0 + tcol;
                 for (int i = trow; i < nrows; i += RS) o[(long long)i * w] = tout[q * TILE + i * PT + tcol];
