@@ -45,7 +45,7 @@
 //    pixels go straight into the statistics, so the blurred planes are never
 //    written.  One more small launch sums each (scale, channel)'s partials.
 #include "ss2_pairs.h"
-#include "vqm_kernels.h"
+#include "ss2_kernels.h"
 
 #include <algorithm>
 #include <type_traits>

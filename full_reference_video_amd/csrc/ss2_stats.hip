@@ -21,7 +21,7 @@
 //   e = (1 + |r2 - mu2|) / (1 + |r1 - mu1|) - 1, art = max(e, 0),
 //   det = max(-e, 0); the sums of d, d^4, art, art^4, det, det^4.
 #include "ss2_pairs.h"
-#include "vqm_kernels.h"
+#include "ss2_kernels.h"
 
 namespace vqm {
 namespace {

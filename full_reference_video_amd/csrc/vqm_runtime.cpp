@@ -27,6 +27,7 @@
 #include <string>
 #include <vector>
 
+#include "ss2_kernels.h"
 #include "vqm_kernels.h"
 
 static_assert(VQM_MAX_BATCH == vqm::kMaxBatch, "batch limits of the ABI and the kernels differ");
