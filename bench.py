@@ -247,20 +247,39 @@ def run_ss2_chain(args):
     for f in frames:
         vqm.vqm_ss2_scale_sums(*f, nscales, coef)  # warm-up (grows the workspace once)
     n = max(1, args.steps)
+    callers = max(1, args.ss2_callers)
+
+    def caller(k, out):
+        # ctypes releases the GIL for the call, so the callers' frames overlap on the GPU
+        for i in range(k, n, callers):
+            got = vqm.vqm_ss2_scale_sums(*frames[i % sets], nscales, coef)
+            if i % sets == 0:
+                out.append(got)
+
     runs = []
     for _ in range(max(1, args.reps)):
+        outs = [[] for _ in range(callers)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(n):
-            vqm.vqm_ss2_scale_sums(*frames[i % sets], nscales, coef)
+        if callers == 1:
+            caller(0, outs[0])
+        else:
+            import threading
+            th = [threading.Thread(target=caller, args=(k, outs[k])) for k in range(callers)]
+            for x in th:
+                x.start()
+            for x in th:
+                x.join()
         torch.cuda.synchronize()
         runs.append((time.perf_counter() - t0) / n)
-    if not np.array_equal(vqm.vqm_ss2_scale_sums(*frames[0], nscales, coef), first):
-        raise RuntimeError("ssimulacra2 chain sums changed between calls")
+        for o in outs:
+            for got in o:
+                if not np.array_equal(got, first):
+                    raise RuntimeError("ssimulacra2 chain sums changed between calls")
     el = sorted(runs)[len(runs) // 2]
     ops, px, minbytes = ss2_chain_work(sw, sh, nscales, nch)
-    print(json.dumps({"metric": f"ssimulacra2 per-scale chain, {nch} channels of {sw}x{sh}, {nscales} scales, "
-                                "one blocking call per frame",
+    how = "one blocking call per frame" if callers == 1 else f"blocking calls from {callers} host threads"
+    print(json.dumps({"metric": f"ssimulacra2 per-scale chain, {nch} channels of {sw}x{sh}, {nscales} scales, {how}",
                       "value": round(1.0 / el, 1), "unit": "frames/s", "ms_per_frame": round(el * 1e3, 4),
                       "recursion_ops_per_frame": ops, "recursion_Gops": round(ops / el / 1e9, 1),
                       "pixels_all_scales": px, "min_bytes_per_frame": minbytes,
@@ -303,6 +322,9 @@ def main():
                     help="only time the ssimulacra2 per-scale chain (vqm_ss2_scale_sums: six scales of multiplies, "
                          "recursive blur, statistics and downsample) on three channels of WxH seeded planes, one "
                          "blocking call per frame, and exit")
+    ap.add_argument("--ss2-callers", type=int, default=1, metavar="N",
+                    help="with --ss2-chain: N host threads each make the blocking calls, so N frames are in flight "
+                         "on N pooled contexts (streams)")
     ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
                     help="only time the library's streaming 16-byte non-temporal read over MIB MiB of device memory "
                          "(the HBM read ceiling of the decimation's loads) and exit")
