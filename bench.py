@@ -238,10 +238,24 @@ def run_ss2_chain(args):
     coef = vqm.vqm_ss2_cascade_coefficients(1.5)
     # distinct frames, more bytes than the 256 MB last-level cache
     sets = max(2, -(-(300 << 20) // (2 * nch * 4 * sw * sh)))
-    frames = []
-    for k in range(sets):
-        ref, dis = synth.ss2_images(20 + k, sw, sh, nch)
-        frames.append(([torch.from_numpy(p).cuda() for p in ref], [torch.from_numpy(p).cuda() for p in dis]))
+    host = [synth.ss2_images(20 + k, sw, sh, nch) for k in range(sets)]
+    cpu = None
+    if args.cpu_budget > 0:  # the oracle's chain, one thread, before the GPU is touched
+        import oracle
+        log("oracle timing on the host")
+        ocoef = oracle.ss2_cascade_coefficients(1.5)
+        n_cpu, t0 = 0, time.perf_counter()
+        while True:
+            oracle.ss2_chain(*host[n_cpu % sets], nscales, ocoef)
+            n_cpu += 1
+            el_cpu = time.perf_counter() - t0
+            if el_cpu >= args.cpu_budget or n_cpu >= 40 * sets:
+                break
+        cpu = {"value": round(n_cpu / el_cpu, 4), "unit": "frames/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_cpu} frames of the chain ({nch} channels of {sw}x{sh}, {nscales} scales), one thread, "
+                         f"{el_cpu:.1f} s, {cpu_model()}"}
+    frames = [([torch.from_numpy(p).cuda() for p in ref], [torch.from_numpy(p).cuda() for p in dis])
+              for ref, dis in host]
     torch.cuda.synchronize()
     first = vqm.vqm_ss2_scale_sums(*frames[0], nscales, coef)
     for f in frames:
@@ -283,7 +297,7 @@ def run_ss2_chain(args):
                       "value": round(1.0 / el, 1), "unit": "frames/s", "ms_per_frame": round(el * 1e3, 4),
                       "recursion_ops_per_frame": ops, "recursion_Gops": round(ops / el / 1e9, 1),
                       "pixels_all_scales": px, "min_bytes_per_frame": minbytes,
-                      "frames": sets, "reps": len(runs)}), flush=True)
+                      "frames": sets, "reps": len(runs), "cpu_baseline": cpu}), flush=True)
 
 
 def main():
