@@ -1074,9 +1074,14 @@ size_t align64(size_t n) { return (n + 63) & ~(size_t)63; }
 // the products, the column pass of every scale with the statistics, and the
 // sums of each (scale, channel)'s partials into the pinned result block;
 // one wait, one read-back.
+//
+// blurred (inspection only, one scale): per channel a device buffer of five
+// w x h planes that also receives the blurred planes mu1, mu2, s11, s22, s12
+// from the same kernels.
 int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, int h, int nscales,
-              const float *coef, double *sums) {
+              const float *coef, double *sums, float *const *blurred = nullptr) {
     if (!ref || !dis || !sums) return fail(-EINVAL, "NULL plane array or sums pointer");
+    if (blurred && nscales != 1) return fail(-EINVAL, "the blurred planes are returned for one scale only");
     if (nch < 1 || nch > vqm::kSs2MaxChannels)
         return fail(-EINVAL, "%d channels outside 1..%d", nch, vqm::kSs2MaxChannels);
     if (nscales < 1 || nscales > kSs2MaxScales)
@@ -1091,7 +1096,8 @@ int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, 
     if (rc) return rc;
     vqm_ctx *ctx = lease.ctx;
     for (int c = 0; c < nch; ++c)
-        if ((rc = device_only(ctx, ref[c], "reference plane")) || (rc = device_only(ctx, dis[c], "distorted plane")))
+        if ((rc = device_only(ctx, ref[c], "reference plane")) || (rc = device_only(ctx, dis[c], "distorted plane")) ||
+            (blurred && (rc = device_only(ctx, blurred[c], "blurred planes"))))
             return rc;
 
     // The workspace: the chain's checkpoints and partials, then per scale
@@ -1104,7 +1110,7 @@ int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, 
     for (int s = 1; s < nscales; ++s) vqm::ss2_downsampled_dim(sw[s - 1], sh[s - 1], &sw[s], &sh[s]);
     size_t total = align64(vqm::ss2_chain_scratch_floats(nch, 5, sw, sh, nscales));
     for (int s = 0; s < nscales; ++s) {
-        ps[s] = align64((size_t)sw[s] * sh[s]);
+        ps[s] = blurred ? (size_t)sw[s] * sh[s] : align64((size_t)sw[s] * sh[s]);
         rows_off[s] = total;
         total += 5 * (size_t)nch * ps[s];
     }
@@ -1138,7 +1144,7 @@ int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, 
         sc.pstride = (long long)ps[s];
         for (int c = 0; c < nch; ++c) {
             sc.rows[c] = work + rows_off[s] + 5 * (size_t)c * ps[s];
-            sc.out[c] = nullptr;
+            sc.out[c] = blurred ? blurred[c] : nullptr;
             if (s == 0) {
                 sc.a[c] = ref[c];
                 sc.b[c] = dis[c];
@@ -1838,6 +1844,14 @@ int vqm_ss2_scale_sums(const float *const *ref, const float *const *dis, int nch
 }
 
 int vqm_ss2_cascade_coefficients(double sigma, float *coef) { return ss2_cascade(sigma, coef); }
+
+int vqm_debug_ss2_blurred(const float *const *ref, const float *const *dis, int nch, int w, int h,
+                          const float *coef, float *const *blurred, double *sums) {
+    if (!blurred) return fail(-EINVAL, "NULL blurred-plane array");
+    for (int c = 0; c < nch && c < vqm::kSs2MaxChannels; ++c)
+        if (!blurred[c]) return fail(-EINVAL, "NULL blurred planes of channel %d", c);
+    return ss2_chain(ref, dis, nch, w, h, 1, coef, sums, blurred);
+}
 
 int vqm_debug_read_probe(const void *buf, long long bytes, int reps, double *ms) {
     return read_probe(buf, bytes, reps, ms);

@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.vqm_ss2_scale_sums.argtypes = [ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int, c_int, c_int,
                                          c_int, c_void_p, c_double_p]
         L.vqm_ss2_cascade_coefficients.argtypes = [ctypes.c_double, c_void_p]
+        L.vqm_debug_ss2_blurred.argtypes = [ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int, c_int, c_int,
+                                            c_void_p, ctypes.POINTER(c_void_p), c_double_p]
         L.vqm_debug_read_probe.argtypes = [c_void_p, ctypes.c_longlong, c_int, c_double_p]
         L.vqm_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -365,6 +367,29 @@ def vqm_ss2_scale_sums(ref_planes, dis_planes, nscales: int, coef) -> np.ndarray
     _check(lib().vqm_ss2_scale_sums(rp, dp, nch, int(w or 0), int(h or 0), int(nscales), cf.ctypes.data,
                                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))), "vqm_ss2_scale_sums")
     return out
+
+
+def vqm_debug_ss2_blurred(ref_planes, dis_planes, coef):
+    """One scale of the chain: (sums [nch, 6], blurred [nch, 5, h, w] device
+    tensor) where blurred holds mu1, mu2, s11, s22, s12 of each channel."""
+    import torch
+    nch = len(ref_planes)
+    if nch != len(dis_planes) or nch < 1:
+        raise ValueError("one reference and one distorted plane per channel")
+    for t in list(ref_planes) + list(dis_planes):
+        _f32_plane(t, "plane")
+        if t.shape != ref_planes[0].shape:
+            raise ValueError("all planes must have one shape")
+    h, w = ref_planes[0].shape
+    out = torch.empty((nch, 5, h, w), dtype=torch.float32, device=ref_planes[0].device)
+    arr = ctypes.c_void_p * nch
+    rp, dp = arr(*[t.data_ptr() for t in ref_planes]), arr(*[t.data_ptr() for t in dis_planes])
+    op = arr(*[out[c].data_ptr() for c in range(nch)])
+    cf = _coef_array(coef)
+    sums = np.empty((nch, 6), np.float64)
+    _check(lib().vqm_debug_ss2_blurred(rp, dp, nch, int(w), int(h), cf.ctypes.data, op,
+                                       sums.ctypes.data_as(ctypes.POINTER(ctypes.c_double))), "vqm_debug_ss2_blurred")
+    return sums, out
 
 
 def vqm_debug_pair_ops(op: int, a, b) -> np.ndarray:

@@ -486,6 +486,18 @@ VQM_API int vqm_ss2_scale_sums(const float *const *ref, const float *const *dis,
  * sigma outside the range. */
 VQM_API int vqm_ss2_cascade_coefficients(double sigma, float *coef);
 
+/* The first scale of vqm_ss2_scale_sums (nscales 1) that also returns the
+ * five blurred planes its kernels form, for the bit-exactness tests of
+ * "Research-1363: Device-resident ssimulacra2 and a single-wait MS-SSIM on
+ * SYCL", Finding 2 (everything but the sums reproduces the CPU exactly).
+ *   blurred  nch device pointers (the current device), each to 5 * w * h
+ *            floats: blur(a), blur(b), blur(a a), blur(b b), blur(a b) of
+ *            the channel, w x h each, tightly packed, in that order.
+ *   sums     6 * nch doubles (host), as vqm_ss2_scale_sums.
+ * Other arguments and errors as vqm_ss2_scale_sums; blocking. */
+VQM_API int vqm_debug_ss2_blurred(const float *const *ref, const float *const *dis, int nch, int w, int h,
+                                  const float *coef, float *const *blurred, double *sums);
+
 /* A streaming read of `bytes` (>= 16) of device memory `buf` with 16-byte
  * non-temporal loads, one workgroup of 256 threads per 64 KiB, timed
  * with HIP events around each of `reps` launches (after one untimed one);

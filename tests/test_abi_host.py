@@ -250,6 +250,9 @@ def test_ss2_chain_refuses_bad_arguments_before_any_hip_call():
     assert L.vqm_ss2_blur(dummy, dummy, 8, 8, bad.ctypes.data) == -errno.EINVAL
     assert L.vqm_ss2_downsample(dummy, None, 8, 8) == -errno.EINVAL
     assert L.vqm_ss2_downsample(dummy, dummy, 0, 8) == -errno.EINVAL
+    assert L.vqm_debug_ss2_blurred(arr, arr, 1, 64, 64, coef.ctypes.data, None, sp) == -errno.EINVAL
+    assert L.vqm_debug_ss2_blurred(arr, arr, 1, 64, 64, coef.ctypes.data, (ctypes.c_void_p * 1)(None),
+                                   sp) == -errno.EINVAL
     c = np.zeros(4, np.float32)
     assert L.vqm_ss2_cascade_coefficients(0.0, c.ctypes.data) == -errno.EINVAL
     assert L.vqm_ss2_cascade_coefficients(1.5, None) == -errno.EINVAL

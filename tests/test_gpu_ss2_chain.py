@@ -160,3 +160,22 @@ def test_chain_refuses_bad_arguments(torch_cuda):
         vqm.vqm_ss2_scale_sums(dr, dd, 2, np.array([np.nan, 0, 0, 0], np.float32))
     with pytest.raises(vqm.VqmError):
         vqm.vqm_ss2_scale_sums(dr * 4, dd * 4, 2, coef)  # four channels
+
+
+@pytest.mark.parametrize("w,h,nch", [(576, 324, 3), (130, 117, 2), (97, 45, 1), (64, 51, 1), (33, 2, 2),
+                                     (3840, 2160, 1)])
+def test_chain_kernels_blur_bit_exact(torch_cuda, w, h, nch):
+    # The chain's own five-plane row and column kernels (not the one-plane
+    # blur's): every blurred plane equal to the oracle's blur bit for bit, and
+    # the sums of the same launch within the bar.
+    ref, dis = synth.ss2_images(15, w, h, nch)
+    coef = oracle.ss2_cascade_coefficients(1.5)
+    say(f"chain kernels' blurred planes {w}x{h}, {nch} channels")
+    sums, planes = vqm.vqm_debug_ss2_blurred([_dev(torch_cuda, p) for p in ref], [_dev(torch_cuda, p) for p in dis],
+                                             coef)
+    planes = planes.cpu().numpy()
+    for c in range(nch):
+        a, b = ref[c], dis[c]
+        for k, src in enumerate((a, b, a * a, b * b, a * b)):
+            _bits_equal(planes[c, k], oracle.ss2_blur(src, coef))
+    _check_close(sums, oracle.ss2_chain(ref, dis, 1, coef)[0], w * h)
