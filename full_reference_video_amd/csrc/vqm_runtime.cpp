@@ -1142,29 +1142,24 @@ int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, 
         sc.w = sw[s];
         sc.h = sh[s];
         sc.pstride = (long long)ps[s];
+        // images: the caller's at the first scale, the pyramid's after it
+        // (plane 2c the reference, 2c + 1 the distorted one)
+        float *pyr[2 * vqm::kSs2MaxChannels];
         for (int c = 0; c < nch; ++c) {
             sc.rows[c] = work + rows_off[s] + 5 * (size_t)c * ps[s];
             sc.out[c] = blurred ? blurred[c] : nullptr;
-            if (s == 0) {
-                sc.a[c] = ref[c];
-                sc.b[c] = dis[c];
-            } else {
-                float *na = work + pyr_off[s] + (2 * (size_t)c) * ps[s];
-                float *nb = work + pyr_off[s] + (2 * (size_t)c + 1) * ps[s];
-                sc.a[c] = na;
-                sc.b[c] = nb;
-            }
+            pyr[2 * c] = work + pyr_off[s] + (2 * (size_t)c) * ps[s];
+            pyr[2 * c + 1] = work + pyr_off[s] + (2 * (size_t)c + 1) * ps[s];
+            sc.a[c] = s == 0 ? ref[c] : pyr[2 * c];
+            sc.b[c] = s == 0 ? dis[c] : pyr[2 * c + 1];
         }
         if (s > 0) {  // the pyramid: this scale's images from the previous scale's
             const float *from[2 * vqm::kSs2MaxChannels];
-            float *to[2 * vqm::kSs2MaxChannels];
             for (int c = 0; c < nch; ++c) {
                 from[2 * c] = args.scale[s - 1].a[c];
                 from[2 * c + 1] = args.scale[s - 1].b[c];
-                to[2 * c] = const_cast<float *>(sc.a[c]);
-                to[2 * c + 1] = const_cast<float *>(sc.b[c]);
             }
-            e = vqm::launch_ss2_down(from, to, 2 * nch, sw[s - 1], sh[s - 1], ctx->stream);
+            e = vqm::launch_ss2_down(from, pyr, 2 * nch, sw[s - 1], sh[s - 1], ctx->stream);
         }
     }
     const vqm::KernelTimer none;
