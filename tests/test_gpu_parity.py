@@ -347,7 +347,8 @@ def test_msssim_pyramid_bit_exact(ctx, w, h, bpc):
 # (strips of 128 columns with a ragged last one, down to a single valid
 # column at 1931 wide; odd plane sizes; several strip rows); a batch of one
 # frame takes the tile kernel.
-ROWS_CASES = [(2001, 1203, 16), (1921, 1081, 8), (1283, 767, 12), (1931, 1087, 10)]
+# The last case is the MS-SSIM workload's own shape and depth, in its launch batch of 32.
+ROWS_CASES = [(2001, 1203, 16), (1921, 1081, 8), (1283, 767, 12), (1931, 1087, 10), (3840, 2160, 8)]
 
 
 @pytest.mark.parametrize("w,h,bpc", ROWS_CASES)
