@@ -15,6 +15,7 @@ the five synthetic workloads; the default is the 2160p 10-bit float_ssim one.
 from __future__ import annotations
 
 import argparse
+import collections
 import dataclasses
 import json
 import os
@@ -263,6 +264,14 @@ def run_ss2_chain(args):
     n = max(1, args.steps)
     callers = max(1, args.ss2_callers)
 
+    pipelined = args.ss2_pipelined
+    if pipelined and callers != 1:
+        raise SystemExit("--ss2-pipelined is one caller's submit/collect loop: drop --ss2-callers")
+    ctx = vqm.Context(0) if pipelined else None
+    depth = args.ss2_depth or vqm.VQM_SS2_MAX_IN_FLIGHT
+    if not 1 <= depth <= vqm.VQM_SS2_MAX_IN_FLIGHT:
+        raise SystemExit(f"--ss2-depth outside 1..{vqm.VQM_SS2_MAX_IN_FLIGHT}")
+
     def caller(k, out):
         # ctypes releases the GIL for the call, so the callers' frames overlap on the GPU
         for i in range(k, n, callers):
@@ -270,12 +279,32 @@ def run_ss2_chain(args):
             if i % sets == 0:
                 out.append(got)
 
+    def pipeline(out):
+        # one caller, VQM_SS2_MAX_IN_FLIGHT frames in flight on one context
+        order = collections.deque()
+        for i in range(n):
+            if ctx.vqm_ss2_in_flight() == depth:
+                got = ctx.vqm_ss2_collect()
+                if order.popleft() == 0:
+                    out.append(got)
+            ctx.vqm_ss2_submit(*frames[i % sets], nscales, coef)
+            order.append(i % sets)
+        while order:
+            got = ctx.vqm_ss2_collect()
+            if order.popleft() == 0:
+                out.append(got)
+
+    if pipelined:
+        pipeline([])  # warm-up: every slot's workspace and stream
+
     runs = []
     for _ in range(max(1, args.reps)):
         outs = [[] for _ in range(callers)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        if callers == 1:
+        if pipelined:
+            pipeline(outs[0])
+        elif callers == 1:
             caller(0, outs[0])
         else:
             import threading
@@ -292,7 +321,11 @@ def run_ss2_chain(args):
                     raise RuntimeError("ssimulacra2 chain sums changed between calls")
     el = sorted(runs)[len(runs) // 2]
     ops, px, minbytes = ss2_chain_work(sw, sh, nscales, nch)
-    how = "one blocking call per frame" if callers == 1 else f"blocking calls from {callers} host threads"
+    if pipelined:
+        how = f"one caller, {depth} frames in flight on one context"
+        ctx.close()
+    else:
+        how = "one blocking call per frame" if callers == 1 else f"blocking calls from {callers} host threads"
     print(json.dumps({"metric": f"ssimulacra2 per-scale chain, {nch} channels of {sw}x{sh}, {nscales} scales, {how}",
                       "value": round(1.0 / el, 1), "unit": "frames/s", "ms_per_frame": round(el * 1e3, 4),
                       "recursion_ops_per_frame": ops, "recursion_Gops": round(ops / el / 1e9, 1),
@@ -336,6 +369,10 @@ def main():
                     help="only time the ssimulacra2 per-scale chain (vqm_ss2_scale_sums: six scales of multiplies, "
                          "recursive blur, statistics and downsample) on three channels of WxH seeded planes, one "
                          "blocking call per frame, and exit")
+    ap.add_argument("--ss2-pipelined", action="store_true",
+                    help="with --ss2-chain: one caller submitting to one context and collecting in order")
+    ap.add_argument("--ss2-depth", type=int, default=0, metavar="D",
+                    help="with --ss2-pipelined: frames kept in flight (0: VQM_SS2_MAX_IN_FLIGHT)")
     ap.add_argument("--ss2-callers", type=int, default=1, metavar="N",
                     help="with --ss2-chain: N host threads each make the blocking calls, so N frames are in flight "
                          "on N pooled contexts (streams)")

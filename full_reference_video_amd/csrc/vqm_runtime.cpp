@@ -209,6 +209,41 @@ struct TimedLaunch {
 
 }  // namespace
 
+// A ssimulacra2 chain's device workspace and its pinned result block.
+struct Ss2Buffers {
+    float *work = nullptr;
+    size_t work_floats = 0;
+    double *res_host = nullptr, *res_dev = nullptr;
+    void release() {
+        if (work) (void)hipFree(work);
+        if (res_host) (void)hipHostFree(res_host);
+        work = nullptr;
+        res_host = res_dev = nullptr;
+        work_floats = 0;
+    }
+};
+
+// A submitted chain frame: its buffers, its own stream (so frames in flight
+// overlap on the GPU), an event ordering it after the context's stream, and
+// its completion event.
+struct Ss2Slot {
+    Ss2Buffers buf;
+    hipStream_t stream = nullptr;
+    hipEvent_t ready = nullptr, done = nullptr;
+    int nres = 0;
+    void release() {
+        if (stream) {
+            (void)hipStreamSynchronize(stream);
+            (void)hipStreamDestroy(stream);
+        }
+        if (ready) (void)hipEventDestroy(ready);
+        if (done) (void)hipEventDestroy(done);
+        stream = nullptr;
+        ready = done = nullptr;
+        buf.release();
+    }
+};
+
 struct vqm_ctx {
     int device = 0;
     hipStream_t stream = nullptr;
@@ -230,11 +265,12 @@ struct vqm_ctx {
     // ssimulacra2 statistics: workgroup partials and the pinned result block
     void *ss2_partials = nullptr;
     double *ss2_result_host = nullptr, *ss2_result_dev = nullptr;
-    // ssimulacra2 per-scale chain: the five blurred planes per channel and
-    // the downsampled images, and the pinned block of every scale's sums
-    float *ss2c_work = nullptr;
-    size_t ss2c_work_floats = 0;
-    double *ss2c_result_host = nullptr, *ss2c_result_dev = nullptr;
+    // ssimulacra2 per-scale chain of the blocking calls (the workspace and
+    // the pinned block of every scale's sums), and the slots of frames
+    // submitted on this context, each with its own stream
+    Ss2Buffers ss2c;
+    Ss2Slot ss2_slot[VQM_SS2_MAX_IN_FLIGHT];
+    int ss2_head = 0, ss2_count = 0;
 };
 
 namespace {
@@ -741,8 +777,8 @@ void destroy(vqm_ctx *ctx) {
     for (hipEvent_t e : ctx->event_pool) (void)hipEventDestroy(e);
     if (ctx->ss2_partials) (void)hipFree(ctx->ss2_partials);
     if (ctx->ss2_result_host) (void)hipHostFree(ctx->ss2_result_host);
-    if (ctx->ss2c_work) (void)hipFree(ctx->ss2c_work);
-    if (ctx->ss2c_result_host) (void)hipHostFree(ctx->ss2c_result_host);
+    ctx->ss2c.release();
+    for (Ss2Slot &sl : ctx->ss2_slot) sl.release();
     if (ctx->own_stream) (void)hipStreamDestroy(ctx->stream);
     if (cur >= 0) (void)hipSetDevice(cur);
     delete ctx;
@@ -1003,17 +1039,22 @@ int device_only(vqm_ctx *ctx, const void *p, const char *what) {
     return 0;
 }
 
-// Device memory of at least `floats` floats in the context's chain workspace
-// (the context is idle: blocking calls end with a wait).
-int ss2c_workspace(vqm_ctx *ctx, size_t floats) {
-    if (ctx->ss2c_work_floats >= floats) return 0;
-    if (ctx->ss2c_work) {
-        (void)hipFree(ctx->ss2c_work);
-        ctx->ss2c_work = nullptr;
-        ctx->ss2c_work_floats = 0;
+// At least `floats` floats of chain workspace and the pinned result block
+// (the buffers are idle: a blocking call ends with a wait, a slot is reused
+// only after its frame was collected).
+int ss2_buffers(Ss2Buffers &b, size_t floats) {
+    if (b.work_floats < floats) {
+        if (b.work) (void)hipFree(b.work);
+        b.work = nullptr;
+        b.work_floats = 0;
+        HIP_TRY_ALLOC(hipMalloc(&b.work, floats * sizeof(float)));
+        b.work_floats = floats;
     }
-    HIP_TRY_ALLOC(hipMalloc(&ctx->ss2c_work, floats * sizeof(float)));
-    ctx->ss2c_work_floats = floats;
+    if (!b.res_host) {
+        HIP_TRY_ALLOC(hipHostMalloc(&b.res_host, 6 * vqm::kSs2MaxChannels * vqm::kSs2MaxScales * sizeof(double),
+                                    hipHostMallocMapped | hipHostMallocCoherent));
+        HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void **>(&b.res_dev), b.res_host, 0));
+    }
     return 0;
 }
 
@@ -1028,7 +1069,7 @@ int ss2_blur_plane(const float *in, float *out, int w, int h, const float *coef)
     if (rc) return rc;
     vqm_ctx *ctx = lease.ctx;
     if ((rc = device_only(ctx, in, "input plane")) || (rc = device_only(ctx, out, "output plane"))) return rc;
-    if ((rc = ss2c_workspace(ctx, vqm::ss2_chain_scratch_floats(1, 1, &w, &h, 1)))) return rc;
+    if ((rc = ss2_buffers(ctx->ss2c, vqm::ss2_chain_scratch_floats(1, 1, &w, &h, 1)))) return rc;
     vqm::Ss2ChainArgs args{};
     vqm::Ss2Scale &sc = args.scale[0];
     sc.w = w;
@@ -1042,7 +1083,7 @@ int ss2_blur_plane(const float *in, float *out, int w, int h, const float *coef)
     args.nplanes = 1;
     args.stats = false;
     memcpy(args.coef, coef, sizeof args.coef);
-    args.scratch = ctx->ss2c_work;
+    args.scratch = ctx->ss2c.work;
     const vqm::KernelTimer none;
     const hipError_t e = vqm::launch_ss2_chain(args, ctx->stream, none, none);
     if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
@@ -1069,19 +1110,11 @@ using vqm::kSs2MaxScales;
 
 size_t align64(size_t n) { return (n + 63) & ~(size_t)63; }
 
-// Every scale enqueued on one stream: the pyramid of the two pictures (a
-// downsample launch per later scale), then the row pass of every scale with
-// the products, the column pass of every scale with the statistics, and the
-// sums of each (scale, channel)'s partials into the pinned result block;
-// one wait, one read-back.
-//
-// blurred (inspection only, one scale): per channel a device buffer of five
-// w x h planes that also receives the blurred planes mu1, mu2, s11, s22, s12
-// from the same kernels.
-int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, int h, int nscales,
-              const float *coef, double *sums, float *const *blurred = nullptr) {
-    if (!ref || !dis || !sums) return fail(-EINVAL, "NULL plane array or sums pointer");
-    if (blurred && nscales != 1) return fail(-EINVAL, "the blurred planes are returned for one scale only");
+// The arguments of one frame of the chain, checked on the host before any
+// HIP call.
+int ss2_check(const float *const *ref, const float *const *dis, int nch, int w, int h, int nscales,
+              const float *coef) {
+    if (!ref || !dis) return fail(-EINVAL, "NULL plane array");
     if (nch < 1 || nch > vqm::kSs2MaxChannels)
         return fail(-EINVAL, "%d channels outside 1..%d", nch, vqm::kSs2MaxChannels);
     if (nscales < 1 || nscales > kSs2MaxScales)
@@ -1091,15 +1124,21 @@ int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, 
     if (rc) return rc;
     for (int c = 0; c < nch; ++c)
         if (!ref[c] || !dis[c]) return fail(-EINVAL, "NULL plane of channel %d", c);
-    Lease lease;
-    rc = lease_ctx(lease);
-    if (rc) return rc;
-    vqm_ctx *ctx = lease.ctx;
-    for (int c = 0; c < nch; ++c)
-        if ((rc = device_only(ctx, ref[c], "reference plane")) || (rc = device_only(ctx, dis[c], "distorted plane")) ||
-            (blurred && (rc = device_only(ctx, blurred[c], "blurred planes"))))
-            return rc;
+    return 0;
+}
 
+// Every scale of one frame enqueued on `stream`: the pyramid of the two
+// pictures (a downsample launch per later scale), then the row pass of every
+// scale with the products, the column pass of every scale with the
+// statistics, and the sums of each (scale, channel)'s partials into buf's
+// pinned result block (6 * nch * nscales doubles, NaN until written).
+//
+// blurred (inspection only, one scale): per channel a device buffer of five
+// w x h planes that also receives the blurred planes mu1, mu2, s11, s22, s12
+// from the same kernels.
+int ss2_enqueue(hipStream_t stream, Ss2Buffers &buf, const float *const *ref, const float *const *dis, int nch,
+                int w, int h, int nscales, const float *coef, float *const *blurred = nullptr) {
+    int rc = 0;
     // The workspace: the chain's checkpoints and partials, then per scale
     // the five row-blurred planes of every channel, then the two images of
     // every channel of every later scale.
@@ -1118,16 +1157,11 @@ int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, 
         pyr_off[s] = total;
         total += 2 * (size_t)nch * ps[s];
     }
-    if ((rc = ss2c_workspace(ctx, total))) return rc;
-    if (!ctx->ss2c_result_host) {
-        HIP_TRY_ALLOC(hipHostMalloc(&ctx->ss2c_result_host, 6 * vqm::kSs2MaxChannels * kSs2MaxScales * sizeof(double),
-                                    hipHostMallocMapped | hipHostMallocCoherent));
-        HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void **>(&ctx->ss2c_result_dev), ctx->ss2c_result_host, 0));
-    }
+    if ((rc = ss2_buffers(buf, total))) return rc;
     const int nres = 6 * nch * nscales;
-    for (int k = 0; k < nres; ++k) ctx->ss2c_result_host[k] = NAN;
+    for (int k = 0; k < nres; ++k) buf.res_host[k] = NAN;
 
-    float *const work = ctx->ss2c_work;
+    float *const work = buf.work;
     vqm::Ss2ChainArgs args{};
     args.nscales = nscales;
     args.nch = nch;
@@ -1135,7 +1169,7 @@ int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, 
     args.stats = true;
     memcpy(args.coef, coef, sizeof args.coef);
     args.scratch = work;
-    args.result = ctx->ss2c_result_dev;
+    args.result = buf.res_dev;
     hipError_t e = hipSuccess;
     for (int s = 0; s < nscales && e == hipSuccess; ++s) {
         vqm::Ss2Scale &sc = args.scale[s];
@@ -1159,14 +1193,83 @@ int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, 
                 from[2 * c] = args.scale[s - 1].a[c];
                 from[2 * c + 1] = args.scale[s - 1].b[c];
             }
-            e = vqm::launch_ss2_down(from, pyr, 2 * nch, sw[s - 1], sh[s - 1], ctx->stream);
+            e = vqm::launch_ss2_down(from, pyr, 2 * nch, sw[s - 1], sh[s - 1], stream);
         }
     }
     const vqm::KernelTimer none;
-    if (e == hipSuccess) e = vqm::launch_ss2_chain(args, ctx->stream, none, none);
+    if (e == hipSuccess) e = vqm::launch_ss2_chain(args, stream, none, none);
     if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
+    return 0;
+}
+
+// Every plane of a chain frame on the context's device.
+int ss2_device_planes(vqm_ctx *ctx, const float *const *ref, const float *const *dis, int nch,
+                      float *const *blurred = nullptr) {
+    int rc = 0;
+    for (int c = 0; c < nch; ++c)
+        if ((rc = device_only(ctx, ref[c], "reference plane")) || (rc = device_only(ctx, dis[c], "distorted plane")) ||
+            (blurred && (rc = device_only(ctx, blurred[c], "blurred planes"))))
+            return rc;
+    return 0;
+}
+
+// A frame's chain as one blocking call on a leased context: enqueue, one
+// wait, one read-back.
+int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, int h, int nscales,
+              const float *coef, double *sums, float *const *blurred = nullptr) {
+    if (!sums) return fail(-EINVAL, "NULL sums pointer");
+    if (blurred && nscales != 1) return fail(-EINVAL, "the blurred planes are returned for one scale only");
+    int rc = ss2_check(ref, dis, nch, w, h, nscales, coef);
+    if (rc) return rc;
+    Lease lease;
+    rc = lease_ctx(lease);
+    if (rc) return rc;
+    vqm_ctx *ctx = lease.ctx;
+    if ((rc = ss2_device_planes(ctx, ref, dis, nch, blurred))) return rc;
+    rc = ss2_enqueue(ctx->stream, ctx->ss2c, ref, dis, nch, w, h, nscales, coef, blurred);
+    if (rc) return rc;
     HIP_TRY(hipStreamSynchronize(ctx->stream));  // the one wait
-    memcpy(sums, ctx->ss2c_result_host, nres * sizeof(double));
+    memcpy(sums, ctx->ss2c.res_host, 6 * (size_t)nch * nscales * sizeof(double));
+    return 0;
+}
+
+// Submit: the frame goes to the next free slot, on the slot's own stream,
+// after the work already on the context's stream; no wait.
+int ss2_submit(vqm_ctx *ctx, const float *const *ref, const float *const *dis, int nch, int w, int h,
+               int nscales, const float *coef) {
+    if (!ctx) return fail(-EINVAL, "NULL context");
+    int rc = ss2_check(ref, dis, nch, w, h, nscales, coef);
+    if (rc) return rc;
+    if (ctx->ss2_count >= VQM_SS2_MAX_IN_FLIGHT)
+        return fail(-EAGAIN, "%d ssimulacra2 frames already in flight", ctx->ss2_count);
+    if ((rc = ensure_device(ctx)) || (rc = ss2_device_planes(ctx, ref, dis, nch))) return rc;
+    Ss2Slot &sl = ctx->ss2_slot[(ctx->ss2_head + ctx->ss2_count) % VQM_SS2_MAX_IN_FLIGHT];
+    if (!sl.stream) {
+        HIP_TRY_ALLOC(hipStreamCreate(&sl.stream));  // a blocking stream, default priority
+        HIP_TRY_ALLOC(hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming));
+        HIP_TRY_ALLOC(hipEventCreateWithFlags(&sl.done, hipEventDisableTiming));
+    }
+    HIP_TRY(hipEventRecord(sl.ready, ctx->stream));
+    HIP_TRY(hipStreamWaitEvent(sl.stream, sl.ready, 0));
+    rc = ss2_enqueue(sl.stream, sl.buf, ref, dis, nch, w, h, nscales, coef);
+    if (rc) return rc;
+    HIP_TRY(hipEventRecord(sl.done, sl.stream));
+    sl.nres = 6 * nch * nscales;
+    ++ctx->ss2_count;
+    return 0;
+}
+
+// Collect: the oldest submitted frame's one wait and read-back.
+int ss2_collect(vqm_ctx *ctx, double *sums) {
+    if (!ctx || !sums) return fail(-EINVAL, "NULL context or sums pointer");
+    if (ctx->ss2_count == 0) return fail(-EAGAIN, "no ssimulacra2 frame in flight");
+    int rc = ensure_device(ctx);
+    if (rc) return rc;
+    Ss2Slot &sl = ctx->ss2_slot[ctx->ss2_head];
+    HIP_TRY(hipEventSynchronize(sl.done));  // the one wait
+    memcpy(sums, sl.buf.res_host, (size_t)sl.nres * sizeof(double));
+    ctx->ss2_head = (ctx->ss2_head + 1) % VQM_SS2_MAX_IN_FLIGHT;
+    --ctx->ss2_count;
     return 0;
 }
 
@@ -1839,6 +1942,19 @@ int vqm_ss2_scale_sums(const float *const *ref, const float *const *dis, int nch
 }
 
 int vqm_ss2_cascade_coefficients(double sigma, float *coef) { return ss2_cascade(sigma, coef); }
+
+int vqm_ss2_submit(vqm_ctx *ctx, const float *const *ref, const float *const *dis, int nch, int w, int h,
+                   int nscales, const float *coef) {
+    DeviceScope scope;
+    return ss2_submit(ctx, ref, dis, nch, w, h, nscales, coef);
+}
+
+int vqm_ss2_collect(vqm_ctx *ctx, double *sums) {
+    DeviceScope scope;
+    return ss2_collect(ctx, sums);
+}
+
+int vqm_ss2_in_flight(const vqm_ctx *ctx) { return ctx ? ctx->ss2_count : 0; }
 
 int vqm_debug_ss2_blurred(const float *const *ref, const float *const *dis, int nch, int w, int h,
                           const float *coef, float *const *blurred, double *sums) {

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libvqm.so")
 VQM_MAX_IN_FLIGHT = 192
 VQM_MAX_BATCH = 32
 VQM_MSSSIM_LCS = 15
+VQM_SS2_MAX_IN_FLIGHT = 4
 VQM_METRIC_FLOAT_SSIM = 0
 VQM_METRIC_MS_SSIM = 1
 VQM_KERNEL_SSIM_STEP = 0
@@ -104,6 +105,10 @@ def lib() -> ctypes.CDLL:
         L.vqm_ss2_scale_sums.argtypes = [ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int, c_int, c_int,
                                          c_int, c_void_p, c_double_p]
         L.vqm_ss2_cascade_coefficients.argtypes = [ctypes.c_double, c_void_p]
+        L.vqm_ss2_submit.argtypes = [c_void_p, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int, c_int,
+                                     c_int, c_int, c_void_p]
+        L.vqm_ss2_collect.argtypes = [c_void_p, c_double_p]
+        L.vqm_ss2_in_flight.argtypes = [c_void_p]
         L.vqm_debug_ss2_blurred.argtypes = [ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int, c_int, c_int,
                                             c_void_p, ctypes.POINTER(c_void_p), c_double_p]
         L.vqm_debug_read_probe.argtypes = [c_void_p, ctypes.c_longlong, c_int, c_double_p]
@@ -345,10 +350,8 @@ def vqm_ss2_downsample(plane):
     return out
 
 
-def vqm_ss2_scale_sums(ref_planes, dis_planes, nscales: int, coef) -> np.ndarray:
-    """The six sums per channel at every scale of the per-scale chain,
-    array [nscales, nch, 6]; ``ref_planes``/``dis_planes`` hold 1..3 float32
-    device tensors of one (h, w) shape."""
+def _ss2_planes(ref_planes, dis_planes):
+    """(ref pointer array, dis pointer array, nch, w, h) of a chain frame."""
     nch = len(ref_planes)
     if nch != len(dis_planes):
         raise ValueError("one reference and one distorted plane per channel")
@@ -362,9 +365,17 @@ def vqm_ss2_scale_sums(ref_planes, dis_planes, nscales: int, coef) -> np.ndarray
             elif tuple(t.shape) != (h, w):
                 raise ValueError("all planes must have one shape")
             arr[c] = t.data_ptr()
+    return rp, dp, nch, int(w or 0), int(h or 0)
+
+
+def vqm_ss2_scale_sums(ref_planes, dis_planes, nscales: int, coef) -> np.ndarray:
+    """The six sums per channel at every scale of the per-scale chain,
+    array [nscales, nch, 6]; ``ref_planes``/``dis_planes`` hold 1..3 float32
+    device tensors of one (h, w) shape."""
+    rp, dp, nch, w, h = _ss2_planes(ref_planes, dis_planes)
     cf = _coef_array(coef)
     out = np.empty((max(int(nscales), 1), max(nch, 1), 6), np.float64)
-    _check(lib().vqm_ss2_scale_sums(rp, dp, nch, int(w or 0), int(h or 0), int(nscales), cf.ctypes.data,
+    _check(lib().vqm_ss2_scale_sums(rp, dp, nch, w, h, int(nscales), cf.ctypes.data,
                                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))), "vqm_ss2_scale_sums")
     return out
 
@@ -435,12 +446,15 @@ class Context:
         # Inputs of frames in flight stay referenced until collected (pinned
         # or device planes are read after submit returns).
         self._inflight = collections.deque()
+        # ssimulacra2 chain frames in flight: (planes, nscales, nch)
+        self._ss2_inflight = collections.deque()
 
     def close(self):
         if self._h:
             lib().vqm_ctx_destroy(self._h)
             self._h = ctypes.c_void_p()
             self._inflight.clear()
+            self._ss2_inflight.clear()
 
     def __enter__(self):
         return self
@@ -510,6 +524,26 @@ class Context:
 
     def vqm_in_flight(self) -> int:
         return lib().vqm_in_flight(self._h)
+
+    def vqm_ss2_submit(self, ref_planes, dis_planes, nscales: int, coef):
+        """Enqueue one frame of the per-scale chain (planes as
+        vqm_ss2_scale_sums's) on its own slot stream, without waiting."""
+        rp, dp, nch, w, h = _ss2_planes(ref_planes, dis_planes)
+        cf = _coef_array(coef)
+        _check(lib().vqm_ss2_submit(self._h, rp, dp, nch, w, h, int(nscales), cf.ctypes.data), "vqm_ss2_submit")
+        self._ss2_inflight.append((list(ref_planes) + list(dis_planes), int(nscales), nch))
+
+    def vqm_ss2_collect(self) -> np.ndarray:
+        """The oldest chain frame's sums, array [nscales, nch, 6]."""
+        ns, nch = self._ss2_inflight[0][1:] if self._ss2_inflight else (1, 1)
+        out = np.full((ns, nch, 6), np.nan)
+        _check(lib().vqm_ss2_collect(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))),
+               "vqm_ss2_collect")
+        self._ss2_inflight.popleft()
+        return out
+
+    def vqm_ss2_in_flight(self) -> int:
+        return lib().vqm_ss2_in_flight(self._h)
 
     def vqm_ctx_set_timing(self, enable: bool):
         _check(lib().vqm_ctx_set_timing(self._h, 1 if enable else 0), "vqm_ctx_set_timing")

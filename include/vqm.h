@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define VQM_ABI_VERSION 6
+#define VQM_ABI_VERSION 7
 
 /* Exported symbols (the library is built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -106,6 +106,10 @@ extern "C" {
 /* Number of per-level means vqm_msssim_frame_lcs returns: L_1..L_5,
  * C_1..C_5, S_1..S_5 ([R-1363] Finding 6, enable_lcs). */
 #define VQM_MSSSIM_LCS 15
+
+/* ssimulacra2 chain frames a context holds in flight between
+ * vqm_ss2_submit and vqm_ss2_collect, each on a stream of its own. */
+#define VQM_SS2_MAX_IN_FLIGHT 4
 
 /* Device scratch, in bytes (8 MiB), of vqm_ssim_frame_noalloc: one array per GPU the
  * library runs on, held until the process ends. */
@@ -476,6 +480,30 @@ VQM_API int vqm_ss2_downsample(const float *in, float *out, int w, int h);
  * current device; -ENOMEM when the workspace cannot grow. */
 VQM_API int vqm_ss2_scale_sums(const float *const *ref, const float *const *dis, int nch, int w, int h,
                                int nscales, const float *coef, double *sums);
+
+/* vqm_ss2_scale_sums as a submit that does not wait ([R-1363] Finding 6:
+ * submit() enqueues every stage, collect() waits once; Finding 1: the
+ * frame's stages stay on the device).  The frame goes to the context's next
+ * free chain slot (VQM_SS2_MAX_IN_FLIGHT of them), whose own stream waits
+ * for the work already enqueued on the context's stream and then runs the
+ * whole chain: frames in flight on one context overlap on the GPU, which a
+ * lone frame's small later scales leave mostly idle.  Each slot keeps its
+ * own workspace (as vqm_ss2_scale_sums's) and pinned result block, grown on
+ * demand.  ref, dis must stay unchanged until the matching vqm_ss2_collect.
+ * Arguments and errors as vqm_ss2_scale_sums (ref, dis on the context's
+ * device), and -EAGAIN with VQM_SS2_MAX_IN_FLIGHT frames already in flight;
+ * nothing is enqueued on error.  These slots are apart from the float_ssim
+ * and MS-SSIM ones: vqm_collect never returns a chain frame. */
+VQM_API int vqm_ss2_submit(vqm_ctx *ctx, const float *const *ref, const float *const *dis, int nch, int w, int h,
+                           int nscales, const float *coef);
+
+/* Wait for the oldest chain frame of the context (its one wait) and copy
+ * its 6 * nch * nscales sums, laid out as vqm_ss2_scale_sums's, to `sums`
+ * (host memory).  -EAGAIN when no chain frame is in flight. */
+VQM_API int vqm_ss2_collect(vqm_ctx *ctx, double *sums);
+
+/* Number of chain frames in flight on the context (0 for NULL). */
+VQM_API int vqm_ss2_in_flight(const vqm_ctx *ctx);
 
 /* Coefficients {B, a1, a2, a3} for the chain's blur whose impulse response
  * is a Gaussian-like bell of variance sigma^2 (0 < sigma < 1e6): three

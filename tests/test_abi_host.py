@@ -52,7 +52,7 @@ def header_constants():
 
 
 def test_abi_version():
-    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 6
+    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 7
 
 
 def test_graft_entry_check_matches_the_built_library():
@@ -65,7 +65,7 @@ def test_graft_entry_check_matches_the_built_library():
 
 def test_binding_constants_match_the_header():
     consts = header_constants()
-    for name in ("VQM_MAX_IN_FLIGHT", "VQM_MAX_BATCH", "VQM_MSSSIM_LCS"):
+    for name in ("VQM_MAX_IN_FLIGHT", "VQM_MAX_BATCH", "VQM_MSSSIM_LCS", "VQM_SS2_MAX_IN_FLIGHT"):
         assert getattr(vqm, name) == consts[name], name
     # a float_ssim batch passes through three step launches before its
     # frames can be collected; the in-flight limit leaves room for more
@@ -253,6 +253,19 @@ def test_ss2_chain_refuses_bad_arguments_before_any_hip_call():
     assert L.vqm_debug_ss2_blurred(arr, arr, 1, 64, 64, coef.ctypes.data, None, sp) == -errno.EINVAL
     assert L.vqm_debug_ss2_blurred(arr, arr, 1, 64, 64, coef.ctypes.data, (ctypes.c_void_p * 1)(None),
                                    sp) == -errno.EINVAL
+    # submit and collect on a context: the same checks, and NULL context
+    ctx = ctypes.c_void_p(0x2000)  # never dereferenced: every check below fails first
+    g = L.vqm_ss2_submit
+    assert g(None, arr, arr, 1, 64, 64, 2, coef.ctypes.data) == -errno.EINVAL
+    assert g(ctx, None, arr, 1, 64, 64, 2, coef.ctypes.data) == -errno.EINVAL
+    assert g(ctx, arr, arr, 4, 64, 64, 2, coef.ctypes.data) == -errno.EINVAL
+    assert g(ctx, arr, arr, 1, 64, 64, 7, coef.ctypes.data) == -errno.EINVAL
+    assert g(ctx, arr, arr, 1, 64, 0, 2, coef.ctypes.data) == -errno.EINVAL
+    assert g(ctx, arr, arr, 1, 64, 64, 2, bad.ctypes.data) == -errno.EINVAL
+    assert g(ctx, (ctypes.c_void_p * 1)(None), arr, 1, 64, 64, 2, coef.ctypes.data) == -errno.EINVAL
+    assert L.vqm_ss2_collect(None, sp) == -errno.EINVAL
+    assert L.vqm_ss2_collect(ctx, None) == -errno.EINVAL
+    assert L.vqm_ss2_in_flight(None) == 0
     c = np.zeros(4, np.float32)
     assert L.vqm_ss2_cascade_coefficients(0.0, c.ctypes.data) == -errno.EINVAL
     assert L.vqm_ss2_cascade_coefficients(1.5, None) == -errno.EINVAL

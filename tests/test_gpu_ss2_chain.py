@@ -179,3 +179,62 @@ def test_chain_kernels_blur_bit_exact(torch_cuda, w, h, nch):
         for k, src in enumerate((a, b, a * a, b * b, a * b)):
             _bits_equal(planes[c, k], oracle.ss2_blur(src, coef))
     _check_close(sums, oracle.ss2_chain(ref, dis, 1, coef)[0], w * h)
+
+
+def test_submitted_frames_equal_the_blocking_call(torch_cuda):
+    # Frames of different sizes, channel and scale counts in flight together
+    # on one context, each on its own slot stream: collected in submission
+    # order, each equal bit for bit to the blocking call and within the bar
+    # of the oracle; a fourth frame is refused while three are in flight.
+    torch = torch_cuda
+    coef = oracle.ss2_cascade_coefficients(1.5)
+    cases = [(576, 324, 3, 6), (130, 97, 2, 4), (1920, 1080, 1, 5), (33, 17, 3, 6), (853, 481, 3, 6)]
+    frames = []
+    for k, (w, h, nch, ns) in enumerate(cases):
+        ref, dis = synth.ss2_images(20 + k, w, h, nch)
+        frames.append((ref, dis, [_dev(torch, p) for p in ref], [_dev(torch, p) for p in dis], ns))
+    with vqm.Context(0) as ctx:
+        with pytest.raises(vqm.VqmError):
+            ctx.vqm_ss2_collect()  # nothing in flight
+        got = []
+        for k, (_, _, dr, dd, ns) in enumerate(frames):
+            if ctx.vqm_ss2_in_flight() == vqm.VQM_SS2_MAX_IN_FLIGHT:
+                with pytest.raises(vqm.VqmError):
+                    ctx.vqm_ss2_submit(dr, dd, ns, coef)
+                got.append(ctx.vqm_ss2_collect())
+            say(f"submit {cases[k]}")
+            ctx.vqm_ss2_submit(dr, dd, ns, coef)
+        while ctx.vqm_ss2_in_flight():
+            got.append(ctx.vqm_ss2_collect())
+    assert len(got) == len(frames)
+    for (ref, dis, dr, dd, ns), g, (w, h, _, _) in zip(frames, got, cases):
+        assert np.array_equal(g, vqm.vqm_ss2_scale_sums(dr, dd, ns, coef))
+        _check_close(g, oracle.ss2_chain(ref, dis, ns, coef), w * h)
+
+
+def test_submit_orders_after_the_context_stream(torch_cuda):
+    # A context on torch's stream: planes written by torch just before the
+    # submit are the ones the chain reads (the slot stream waits for the
+    # context's stream), and a context closed with frames in flight waits
+    # for them.
+    torch = torch_cuda
+    coef = oracle.ss2_cascade_coefficients(1.5)
+    ref, dis = synth.ss2_images(30, 1280, 720, 3)
+    src_r = [_dev(torch, p) for p in ref]
+    src_d = [_dev(torch, p) for p in dis]
+    want = oracle.ss2_chain(ref, dis, 6, coef)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dr = [torch.zeros_like(t) for t in src_r]
+        dd = [torch.zeros_like(t) for t in src_d]
+        torch.cuda.synchronize()
+        ctx = vqm.Context(0, stream=s)
+        for a, b in zip(dr + dd, src_r + src_d):
+            torch.cuda._sleep(1_000_000)  # the copies land well after the submit returns
+            a.copy_(b)
+        ctx.vqm_ss2_submit(dr, dd, 6, coef)
+        got = ctx.vqm_ss2_collect()
+        ctx.vqm_ss2_submit(dr, dd, 6, coef)
+        ctx.close()  # one frame still in flight
+    _check_close(got, want, 1280 * 720)
+    torch.cuda.synchronize()
