@@ -487,28 +487,92 @@ __global__ __launch_bounds__(kFinishThreads) void ss2_chain_finish(Chain chain) 
     }
 }
 
-// ---------------------------------------------------------------- downsample
+// ---------------------------------------------------------------- pyramid
 
-struct DownPass {
+// Every later scale of the pyramid in one launch.  A workgroup owns a
+// 64 x 64 tile of the first scale: its 32 x 32 downsample, that tile's
+// 16 x 16 downsample and so on are tiles of the later scales, aligned on
+// their own edges, so the pixels a later scale's pixel averages (the
+// replicated last column or row included: it is the pixel just before,
+// inside the same tile) stay in the workgroup, and the scales after the
+// second are formed from LDS.  Each scale's pixel is
+// ((a + b) + (c + d)) * 0.25f over its 2 x 2 block, a and b from the upper
+// row, the last column and row repeated when the size is odd.
+constexpr int kPyrEdge = 32;  // a workgroup's tile edge at the second scale
+
+struct PyrPass {
     const float *in[2 * kSs2MaxChannels];
-    float *out[2 * kSs2MaxChannels];
+    float *out[kSs2MaxScales - 1][2 * kSs2MaxChannels];
+    int w[kSs2MaxScales], h[kSs2MaxScales];
+    int levels, tiles_x;
 };
 
-// ceil(w/2) x ceil(h/2) means of 2x2 blocks, the last column and row
-// repeated when the size is odd: ((a + b) + (c + d)) * 0.25f, a and b from
-// the upper row.
-__global__ __launch_bounds__(256) void ss2_down(DownPass d, int w, int h, int ow, int oh) {
-    const float *in = d.in[blockIdx.y];
-    float *out = d.out[blockIdx.y];
-    const long long n = (long long)ow * oh;
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
-        const int y = (int)(i / ow), x = (int)(i % ow);
-        const int r0 = 2 * y, r1 = min(2 * y + 1, h - 1);
-        const int c0 = 2 * x, c1 = min(2 * x + 1, w - 1);
-        const float a = in[(long long)r0 * w + c0], b = in[(long long)r0 * w + c1];
-        const float cc = in[(long long)r1 * w + c0], dd = in[(long long)r1 * w + c1];
-        out[i] = ((a + b) + (cc + dd)) * 0.25f;
+__device__ inline float mean4(float a, float b, float c, float d) { return ((a + b) + (c + d)) * 0.25f; }
+
+// Scale L (2..5) of the tile from scale L-1's tile in LDS (pitch 2E+1).
+template <int L>
+__device__ void pyramid_level(const PyrPass &p, int plane, int tx, int ty, const float *src, float *dst) {
+    constexpr int E = kPyrEdge >> (L - 1);  // this scale's tile edge
+    constexpr int SP = 2 * E + 1, DP = E + 1;
+    const int t = threadIdx.x;
+    if (t >= E * E) return;
+    const int r = t / E, c = t % E;
+    const int y = ty * E + r, x = tx * E + c;
+    const int ow = p.w[L], oh = p.h[L], pw = p.w[L - 1], ph = p.h[L - 1];
+    if (y >= oh || x >= ow) return;
+    const int r0 = 2 * r, r1 = min(2 * y + 1, ph - 1) - 2 * E * ty;
+    const int c0 = 2 * c, c1 = min(2 * x + 1, pw - 1) - 2 * E * tx;
+    const float v = mean4(src[r0 * SP + c0], src[r0 * SP + c1], src[r1 * SP + c0], src[r1 * SP + c1]);
+    if (dst) dst[r * DP + c] = v;
+    p.out[L - 1][plane][(long long)y * ow + x] = v;
+}
+
+__global__ __launch_bounds__(256) void ss2_pyramid(PyrPass p) {
+    __shared__ float t1[32 * 33], t2[16 * 17], t3[8 * 9], t4[4 * 5];
+    const int plane = blockIdx.y;
+    const int tx = blockIdx.x % p.tiles_x, ty = blockIdx.x / p.tiles_x;
+    {  // the second scale from the caller's plane: four pixels per thread,
+       // every load issued before any sum (the loads of pixels outside the
+       // plane are clamped in, their results dropped)
+        const float *in = p.in[plane];
+        const int w = p.w[0], h = p.h[0], ow = p.w[1], oh = p.h[1];
+        float q[4][4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = threadIdx.x + 256 * k;
+            const int y = min(ty * kPyrEdge + (i >> 5), oh - 1), x = min(tx * kPyrEdge + (i & 31), ow - 1);
+            const long long r0 = (long long)(2 * y) * w, r1 = (long long)min(2 * y + 1, h - 1) * w;
+            const int c0 = 2 * x, c1 = min(2 * x + 1, w - 1);
+            q[k][0] = in[r0 + c0];
+            q[k][1] = in[r0 + c1];
+            q[k][2] = in[r1 + c0];
+            q[k][3] = in[r1 + c1];
+        }
+        float *out = p.out[0][plane];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = threadIdx.x + 256 * k;
+            const int r = i >> 5, c = i & 31;
+            const int y = ty * kPyrEdge + r, x = tx * kPyrEdge + c;
+            if (y < oh && x < ow) {
+                const float v = mean4(q[k][0], q[k][1], q[k][2], q[k][3]);
+                t1[r * 33 + c] = v;
+                out[(long long)y * ow + x] = v;
+            }
+        }
     }
+    if (p.levels < 2) return;
+    __syncthreads();
+    pyramid_level<2>(p, plane, tx, ty, t1, t2);
+    if (p.levels < 3) return;
+    __syncthreads();
+    pyramid_level<3>(p, plane, tx, ty, t2, t3);
+    if (p.levels < 4) return;
+    __syncthreads();
+    pyramid_level<4>(p, plane, tx, ty, t3, t4);
+    if (p.levels < 5) return;
+    __syncthreads();
+    pyramid_level<5>(p, plane, tx, ty, t4, nullptr);
 }
 
 template <int NP>
@@ -627,19 +691,22 @@ void ss2_downsampled_dim(int w, int h, int *ow, int *oh) {
     *oh = (h + 1) / 2;
 }
 
-hipError_t launch_ss2_down(const float *const *in, float *const *out, int nplanes, int w, int h,
-                           hipStream_t stream) {
-    if (nplanes < 1 || nplanes > 2 * kSs2MaxChannels || w < 1 || h < 1) return hipErrorInvalidValue;
-    DownPass d{};
+hipError_t launch_ss2_pyramid(const float *const *in, float *const *out, int nplanes, int w, int h, int levels,
+                              hipStream_t stream) {
+    if (nplanes < 1 || nplanes > 2 * kSs2MaxChannels || w < 1 || h < 1 || levels < 1 || levels > kSs2MaxScales - 1)
+        return hipErrorInvalidValue;
+    PyrPass p{};
+    p.w[0] = w;
+    p.h[0] = h;
+    for (int l = 1; l <= levels; ++l) ss2_downsampled_dim(p.w[l - 1], p.h[l - 1], &p.w[l], &p.h[l]);
     for (int i = 0; i < nplanes; ++i) {
-        d.in[i] = in[i];
-        d.out[i] = out[i];
+        p.in[i] = in[i];
+        for (int l = 0; l < levels; ++l) p.out[l][i] = out[l * nplanes + i];
     }
-    int ow, oh;
-    ss2_downsampled_dim(w, h, &ow, &oh);
-    const long long n = (long long)ow * oh;
-    const long long blocks = std::min<long long>((n + 255) / 256, 4096);
-    hipLaunchKernelGGL(ss2_down, dim3((unsigned)blocks, nplanes), dim3(256), 0, stream, d, w, h, ow, oh);
+    p.levels = levels;
+    p.tiles_x = (p.w[1] + kPyrEdge - 1) / kPyrEdge;
+    const long long tiles = (long long)p.tiles_x * ((p.h[1] + kPyrEdge - 1) / kPyrEdge);
+    hipLaunchKernelGGL(ss2_pyramid, dim3((unsigned)tiles, nplanes), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

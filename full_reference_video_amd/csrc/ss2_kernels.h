@@ -67,8 +67,11 @@ hipError_t launch_ss2_chain(const Ss2ChainArgs &args, hipStream_t stream, const 
 // ceil(w/2) x ceil(h/2).
 void ss2_downsampled_dim(int w, int h, int *ow, int *oh);
 
-// The 2x2 downsample of nplanes (up to 6) w x h planes in[i] into out[i].
-hipError_t launch_ss2_down(const float *const *in, float *const *out, int nplanes, int w, int h,
-                           hipStream_t stream);
+// The pyramid of nplanes (up to 6) w x h planes in[i] in one launch:
+// out[(l - 1) * nplanes + i] receives the 2x2 downsample of scale l - 1 of
+// plane i (scale 0 is in[i]), for l = 1..levels (levels up to 5), each
+// tightly packed.
+hipError_t launch_ss2_pyramid(const float *const *in, float *const *out, int nplanes, int w, int h, int levels,
+                              hipStream_t stream);
 
 }  // namespace vqm

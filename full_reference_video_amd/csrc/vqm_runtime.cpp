@@ -1100,7 +1100,7 @@ int ss2_down_plane(const float *in, float *out, int w, int h) {
     if (rc) return rc;
     vqm_ctx *ctx = lease.ctx;
     if ((rc = device_only(ctx, in, "input plane")) || (rc = device_only(ctx, out, "output plane"))) return rc;
-    const hipError_t e = vqm::launch_ss2_down(&in, &out, 1, w, h, ctx->stream);
+    const hipError_t e = vqm::launch_ss2_pyramid(&in, &out, 1, w, h, 1, ctx->stream);
     if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
     HIP_TRY(hipStreamSynchronize(ctx->stream));
     return 0;
@@ -1133,9 +1133,9 @@ int ss2_check(const float *const *ref, const float *const *dis, int nch, int w, 
 // statistics, and the sums of each (scale, channel)'s partials into buf's
 // pinned result block (6 * nch * nscales doubles, NaN until written).
 //
-// blurred (inspection only, one scale): per channel a device buffer of five
-// w x h planes that also receives the blurred planes mu1, mu2, s11, s22, s12
-// from the same kernels.
+// blurred (inspection only): per channel a device buffer that also receives
+// the blurred planes mu1, mu2, s11, s22, s12 from the same kernels, the five
+// planes of each scale (tightly packed) after those of the scales before it.
 int ss2_enqueue(hipStream_t stream, Ss2Buffers &buf, const float *const *ref, const float *const *dis, int nch,
                 int w, int h, int nscales, const float *coef, float *const *blurred = nullptr) {
     int rc = 0;
@@ -1170,32 +1170,35 @@ int ss2_enqueue(hipStream_t stream, Ss2Buffers &buf, const float *const *ref, co
     memcpy(args.coef, coef, sizeof args.coef);
     args.scratch = work;
     args.result = buf.res_dev;
-    hipError_t e = hipSuccess;
-    for (int s = 0; s < nscales && e == hipSuccess; ++s) {
+    // images: the caller's at the first scale, the pyramid's after it
+    // (plane 2c the reference, 2c + 1 the distorted one; pyr holds scale
+    // s's plane i at (s - 1) * 2 nch + i)
+    const float *img[2 * vqm::kSs2MaxChannels];
+    float *pyr[(kSs2MaxScales - 1) * 2 * vqm::kSs2MaxChannels];
+    size_t blurred_off = 0;  // floats of the earlier scales' blurred planes
+    for (int s = 0; s < nscales; ++s) {
         vqm::Ss2Scale &sc = args.scale[s];
         sc.w = sw[s];
         sc.h = sh[s];
         sc.pstride = (long long)ps[s];
-        // images: the caller's at the first scale, the pyramid's after it
-        // (plane 2c the reference, 2c + 1 the distorted one)
-        float *pyr[2 * vqm::kSs2MaxChannels];
         for (int c = 0; c < nch; ++c) {
             sc.rows[c] = work + rows_off[s] + 5 * (size_t)c * ps[s];
-            sc.out[c] = blurred ? blurred[c] : nullptr;
-            pyr[2 * c] = work + pyr_off[s] + (2 * (size_t)c) * ps[s];
-            pyr[2 * c + 1] = work + pyr_off[s] + (2 * (size_t)c + 1) * ps[s];
-            sc.a[c] = s == 0 ? ref[c] : pyr[2 * c];
-            sc.b[c] = s == 0 ? dis[c] : pyr[2 * c + 1];
-        }
-        if (s > 0) {  // the pyramid: this scale's images from the previous scale's
-            const float *from[2 * vqm::kSs2MaxChannels];
-            for (int c = 0; c < nch; ++c) {
-                from[2 * c] = args.scale[s - 1].a[c];
-                from[2 * c + 1] = args.scale[s - 1].b[c];
+            sc.out[c] = blurred ? blurred[c] + blurred_off : nullptr;
+            if (s == 0) {
+                sc.a[c] = img[2 * c] = ref[c];
+                sc.b[c] = img[2 * c + 1] = dis[c];
+                continue;
             }
-            e = vqm::launch_ss2_down(from, pyr, 2 * nch, sw[s - 1], sh[s - 1], stream);
+            float *const a = work + pyr_off[s] + (2 * (size_t)c) * ps[s], *const b = a + ps[s];
+            pyr[(s - 1) * 2 * nch + 2 * c] = a;
+            pyr[(s - 1) * 2 * nch + 2 * c + 1] = b;
+            sc.a[c] = a;
+            sc.b[c] = b;
         }
+        blurred_off += 5 * (size_t)sw[s] * sh[s];
     }
+    hipError_t e = hipSuccess;
+    if (nscales > 1) e = vqm::launch_ss2_pyramid(img, pyr, 2 * nch, w, h, nscales - 1, stream);
     const vqm::KernelTimer none;
     if (e == hipSuccess) e = vqm::launch_ss2_chain(args, stream, none, none);
     if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
@@ -1218,7 +1221,6 @@ int ss2_device_planes(vqm_ctx *ctx, const float *const *ref, const float *const 
 int ss2_chain(const float *const *ref, const float *const *dis, int nch, int w, int h, int nscales,
               const float *coef, double *sums, float *const *blurred = nullptr) {
     if (!sums) return fail(-EINVAL, "NULL sums pointer");
-    if (blurred && nscales != 1) return fail(-EINVAL, "the blurred planes are returned for one scale only");
     int rc = ss2_check(ref, dis, nch, w, h, nscales, coef);
     if (rc) return rc;
     Lease lease;
@@ -1956,12 +1958,12 @@ int vqm_ss2_collect(vqm_ctx *ctx, double *sums) {
 
 int vqm_ss2_in_flight(const vqm_ctx *ctx) { return ctx ? ctx->ss2_count : 0; }
 
-int vqm_debug_ss2_blurred(const float *const *ref, const float *const *dis, int nch, int w, int h,
+int vqm_debug_ss2_blurred(const float *const *ref, const float *const *dis, int nch, int w, int h, int nscales,
                           const float *coef, float *const *blurred, double *sums) {
     if (!blurred) return fail(-EINVAL, "NULL blurred-plane array");
     for (int c = 0; c < nch && c < vqm::kSs2MaxChannels; ++c)
         if (!blurred[c]) return fail(-EINVAL, "NULL blurred planes of channel %d", c);
-    return ss2_chain(ref, dis, nch, w, h, 1, coef, sums, blurred);
+    return ss2_chain(ref, dis, nch, w, h, nscales, coef, sums, blurred);
 }
 
 int vqm_debug_read_probe(const void *buf, long long bytes, int reps, double *ms) {

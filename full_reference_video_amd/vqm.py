@@ -110,7 +110,7 @@ def lib() -> ctypes.CDLL:
         L.vqm_ss2_collect.argtypes = [c_void_p, c_double_p]
         L.vqm_ss2_in_flight.argtypes = [c_void_p]
         L.vqm_debug_ss2_blurred.argtypes = [ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int, c_int, c_int,
-                                            c_void_p, ctypes.POINTER(c_void_p), c_double_p]
+                                            c_int, c_void_p, ctypes.POINTER(c_void_p), c_double_p]
         L.vqm_debug_read_probe.argtypes = [c_void_p, ctypes.c_longlong, c_int, c_double_p]
         L.vqm_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -380,9 +380,10 @@ def vqm_ss2_scale_sums(ref_planes, dis_planes, nscales: int, coef) -> np.ndarray
     return out
 
 
-def vqm_debug_ss2_blurred(ref_planes, dis_planes, coef):
-    """One scale of the chain: (sums [nch, 6], blurred [nch, 5, h, w] device
-    tensor) where blurred holds mu1, mu2, s11, s22, s12 of each channel."""
+def vqm_debug_ss2_blurred(ref_planes, dis_planes, coef, nscales: int = 1):
+    """The chain with its blurred planes: (sums [nscales, nch, 6], blurred)
+    where blurred[s] is a device tensor [nch, 5, h_s, w_s] holding mu1, mu2,
+    s11, s22, s12 of each channel at scale s."""
     import torch
     nch = len(ref_planes)
     if nch != len(dis_planes) or nch < 1:
@@ -392,15 +393,24 @@ def vqm_debug_ss2_blurred(ref_planes, dis_planes, coef):
         if t.shape != ref_planes[0].shape:
             raise ValueError("all planes must have one shape")
     h, w = ref_planes[0].shape
-    out = torch.empty((nch, 5, h, w), dtype=torch.float32, device=ref_planes[0].device)
+    ns = int(nscales)
+    dims = [(h, w)]
+    for _ in range(1, max(ns, 1)):
+        dims.append(((dims[-1][0] + 1) // 2, (dims[-1][1] + 1) // 2))
+    per_ch = sum(5 * a * b for a, b in dims)
+    flat = torch.empty((nch, per_ch), dtype=torch.float32, device=ref_planes[0].device)
     arr = ctypes.c_void_p * nch
     rp, dp = arr(*[t.data_ptr() for t in ref_planes]), arr(*[t.data_ptr() for t in dis_planes])
-    op = arr(*[out[c].data_ptr() for c in range(nch)])
+    op = arr(*[flat[c].data_ptr() for c in range(nch)])
     cf = _coef_array(coef)
-    sums = np.empty((nch, 6), np.float64)
-    _check(lib().vqm_debug_ss2_blurred(rp, dp, nch, int(w), int(h), cf.ctypes.data, op,
+    sums = np.empty((max(ns, 1), nch, 6), np.float64)
+    _check(lib().vqm_debug_ss2_blurred(rp, dp, nch, int(w), int(h), ns, cf.ctypes.data, op,
                                        sums.ctypes.data_as(ctypes.POINTER(ctypes.c_double))), "vqm_debug_ss2_blurred")
-    return sums, out
+    planes, off = [], 0
+    for a, b in dims:
+        planes.append(flat[:, off:off + 5 * a * b].view(nch, 5, a, b))
+        off += 5 * a * b
+    return sums, planes
 
 
 def vqm_debug_pair_ops(op: int, a, b) -> np.ndarray:

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define VQM_ABI_VERSION 7
+#define VQM_ABI_VERSION 8
 
 /* Exported symbols (the library is built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -474,8 +474,9 @@ VQM_API int vqm_ss2_downsample(const float *in, float *out, int w, int h);
  * about 1e-12 relative of exact and bitwise repeatable.  The library keeps
  * a device workspace of about 5 * nch * w * h floats per blocking context
  * (and the smaller scales' images), grown on demand.  Blocking: four
- * launches per scale (three at the first) on a library-owned blocking
- * stream and one wait.  -EINVAL for NULL pointers, bad counts or sizes,
+ * launches for every scale together (the pyramid, the row pass, the column
+ * pass with the statistics, the sums; three for one scale) on a
+ * library-owned blocking stream and one wait.  -EINVAL for NULL pointers, bad counts or sizes,
  * non-finite coefficients or planes that are not device memory of the
  * current device; -ENOMEM when the workspace cannot grow. */
 VQM_API int vqm_ss2_scale_sums(const float *const *ref, const float *const *dis, int nch, int w, int h,
@@ -514,17 +515,18 @@ VQM_API int vqm_ss2_in_flight(const vqm_ctx *ctx);
  * sigma outside the range. */
 VQM_API int vqm_ss2_cascade_coefficients(double sigma, float *coef);
 
-/* The first scale of vqm_ss2_scale_sums (nscales 1) that also returns the
- * five blurred planes its kernels form, for the bit-exactness tests of
- * "Research-1363: Device-resident ssimulacra2 and a single-wait MS-SSIM on
- * SYCL", Finding 2 (everything but the sums reproduces the CPU exactly).
- *   blurred  nch device pointers (the current device), each to 5 * w * h
- *            floats: blur(a), blur(b), blur(a a), blur(b b), blur(a b) of
- *            the channel, w x h each, tightly packed, in that order.
- *   sums     6 * nch doubles (host), as vqm_ss2_scale_sums.
+/* vqm_ss2_scale_sums that also returns the five blurred planes its kernels
+ * form at every scale, for the bit-exactness tests of "Research-1363:
+ * Device-resident ssimulacra2 and a single-wait MS-SSIM on SYCL", Finding 2
+ * (everything but the sums reproduces the CPU exactly).
+ *   blurred  nch device pointers (the current device), each to
+ *            5 * (w_0 h_0 + ... + w_{n-1} h_{n-1}) floats, w_s x h_s the
+ *            size of scale s: per scale, in order, blur(a), blur(b),
+ *            blur(a a), blur(b b), blur(a b) of the channel, tightly packed.
+ *   sums     6 * nch * nscales doubles (host), as vqm_ss2_scale_sums.
  * Other arguments and errors as vqm_ss2_scale_sums; blocking. */
 VQM_API int vqm_debug_ss2_blurred(const float *const *ref, const float *const *dis, int nch, int w, int h,
-                                  const float *coef, float *const *blurred, double *sums);
+                                  int nscales, const float *coef, float *const *blurred, double *sums);
 
 /* A streaming read of `bytes` (>= 16) of device memory `buf` with 16-byte
  * non-temporal loads, one workgroup of 256 threads per 64 KiB, timed

@@ -52,7 +52,7 @@ def header_constants():
 
 
 def test_abi_version():
-    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 7
+    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 8
 
 
 def test_graft_entry_check_matches_the_built_library():
@@ -250,9 +250,10 @@ def test_ss2_chain_refuses_bad_arguments_before_any_hip_call():
     assert L.vqm_ss2_blur(dummy, dummy, 8, 8, bad.ctypes.data) == -errno.EINVAL
     assert L.vqm_ss2_downsample(dummy, None, 8, 8) == -errno.EINVAL
     assert L.vqm_ss2_downsample(dummy, dummy, 0, 8) == -errno.EINVAL
-    assert L.vqm_debug_ss2_blurred(arr, arr, 1, 64, 64, coef.ctypes.data, None, sp) == -errno.EINVAL
-    assert L.vqm_debug_ss2_blurred(arr, arr, 1, 64, 64, coef.ctypes.data, (ctypes.c_void_p * 1)(None),
+    assert L.vqm_debug_ss2_blurred(arr, arr, 1, 64, 64, 1, coef.ctypes.data, None, sp) == -errno.EINVAL
+    assert L.vqm_debug_ss2_blurred(arr, arr, 1, 64, 64, 1, coef.ctypes.data, (ctypes.c_void_p * 1)(None),
                                    sp) == -errno.EINVAL
+    assert L.vqm_debug_ss2_blurred(arr, arr, 1, 64, 64, 7, coef.ctypes.data, arr, sp) == -errno.EINVAL
     # submit and collect on a context: the same checks, and NULL context
     ctx = ctypes.c_void_p(0x2000)  # never dereferenced: every check below fails first
     g = L.vqm_ss2_submit

@@ -162,23 +162,29 @@ def test_chain_refuses_bad_arguments(torch_cuda):
         vqm.vqm_ss2_scale_sums(dr * 4, dd * 4, 2, coef)  # four channels
 
 
-@pytest.mark.parametrize("w,h,nch", [(576, 324, 3), (130, 117, 2), (97, 45, 1), (64, 51, 1), (33, 2, 2),
-                                     (3840, 2160, 1)])
-def test_chain_kernels_blur_bit_exact(torch_cuda, w, h, nch):
-    # The chain's own five-plane row and column kernels (not the one-plane
-    # blur's): every blurred plane equal to the oracle's blur bit for bit, and
-    # the sums of the same launch within the bar.
+@pytest.mark.parametrize("w,h,nch,nscales", [(576, 324, 3, 6), (130, 117, 2, 6), (97, 45, 1, 1), (64, 51, 1, 3),
+                                             (33, 2, 2, 6), (1, 1, 1, 6), (129, 65, 1, 6), (3840, 2160, 1, 6),
+                                             (1031, 777, 3, 6)])
+def test_chain_kernels_blur_bit_exact(torch_cuda, w, h, nch, nscales):
+    # The chain's own pyramid and five-plane row and column kernels (not the
+    # one-plane blur's or downsample's): every blurred plane of every scale
+    # equal bit for bit to the oracle's blur of the oracle's downsampled
+    # images, and the sums of the same launch within the bar.
     ref, dis = synth.ss2_images(15, w, h, nch)
     coef = oracle.ss2_cascade_coefficients(1.5)
-    say(f"chain kernels' blurred planes {w}x{h}, {nch} channels")
+    say(f"chain kernels' blurred planes {w}x{h}, {nch} channels, {nscales} scales")
     sums, planes = vqm.vqm_debug_ss2_blurred([_dev(torch_cuda, p) for p in ref], [_dev(torch_cuda, p) for p in dis],
-                                             coef)
-    planes = planes.cpu().numpy()
-    for c in range(nch):
-        a, b = ref[c], dis[c]
-        for k, src in enumerate((a, b, a * a, b * b, a * b)):
-            _bits_equal(planes[c, k], oracle.ss2_blur(src, coef))
-    _check_close(sums, oracle.ss2_chain(ref, dis, 1, coef)[0], w * h)
+                                             coef, nscales)
+    a_s, b_s = list(ref), list(dis)
+    for s in range(nscales):
+        got = planes[s].cpu().numpy()
+        for c in range(nch):
+            a, b = a_s[c], b_s[c]
+            for k, src in enumerate((a, b, a * a, b * b, a * b)):
+                _bits_equal(got[c, k], oracle.ss2_blur(src, coef))
+        a_s = [oracle.ss2_downsample(p) for p in a_s]
+        b_s = [oracle.ss2_downsample(p) for p in b_s]
+    _check_close(sums, oracle.ss2_chain(ref, dis, nscales, coef), w * h)
 
 
 def test_submitted_frames_equal_the_blocking_call(torch_cuda):
