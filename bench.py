@@ -27,10 +27,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0                    # MI355X HBM3E, GB/s
-# fp32 VALU peak without packed math: 256 CUs x 4 SIMD x 16 lanes x 2 flops
-# (FMA) x 2.4 GHz.  The published 157.3 TFLOP/s counts packed FMA, which this
-# library does not use (it is compiled with packed fp32 off).
-FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12   # 78.6
+# The published fp32 vector peak: 256 CUs x 4 SIMD x 32 lane-FMAs per clock x
+# 2 flops x 2.4 GHz.  The library's kernels use ordinary (non-packed) FMA
+# instructions, and those reach it too: --valu-probe measures about 127
+# TFLOP/s with plain v_fma_f32 chains at eight waves per SIMD, above the
+# 78.6 that 16 lanes per clock would allow.
+FP32_VALU_PEAK_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12   # 157.3
 
 # Kernel sources whose counters profiles/ssim_step_2160p10_traffic.json holds.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "ssim_step_2160p10_traffic.json")
@@ -376,6 +378,8 @@ def main():
     ap.add_argument("--ss2-callers", type=int, default=1, metavar="N",
                     help="with --ss2-chain: N host threads each make the blocking calls, so N frames are in flight "
                          "on N pooled contexts (streams)")
+    ap.add_argument("--valu-probe", type=int, default=0, metavar="ITERS",
+                    help="time plain fp32 FMA chains (ITERS steps of 16 per lane) at 1-16 waves per SIMD and exit")
     ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
                     help="only time the library's streaming 16-byte non-temporal read over MIB MiB of device memory "
                          "(the HBM read ceiling of the decimation's loads) and exit")
@@ -433,6 +437,14 @@ def main():
 
     if args.ss2_chain:
         run_ss2_chain(args)
+        return
+
+    if args.valu_probe:
+        from full_reference_video_amd import vqm
+        for w in (1, 2, 4, 8, 16):
+            t = vqm.vqm_debug_valu_probe(waves_per_simd=w, iters=args.valu_probe, reps=5)
+            print(json.dumps({"valu_probe_waves_per_simd": w, "iters": args.valu_probe, "TFLOPs": round(t, 1),
+                              "frac_of_peak": round(t / FP32_VALU_PEAK_TFLOPS, 4)}), flush=True)
         return
 
     if args.read_probe:

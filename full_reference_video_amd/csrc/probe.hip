@@ -1,7 +1,10 @@
-// probe.hip — a plain streaming read of device memory, to measure the HBM
-// read ceiling that the decimation's 16-byte non-temporal loads can reach
-// on this GPU (an inspection entry point, not part of the scoring path).
-#include "vqm_kernels.h"
+// probe.hip — two inspection kernels, not part of the scoring path: a plain
+// streaming read of device memory (the HBM read ceiling that the
+// decimation's 16-byte non-temporal loads can reach on this GPU), and a
+// plain fp32 multiply-add loop (the rate the VALU reaches with ordinary,
+// non-packed FMA instructions, against which the arithmetic-bound kernels
+// are measured).
+#include "probe.h"
 
 namespace vqm {
 namespace {
@@ -38,7 +41,34 @@ __global__ __launch_bounds__(256) void read_probe(const u32x4 *__restrict__ p, l
     }
 }
 
+// Each thread runs 16 independent multiply-add chains v = g v + 1 for
+// `iters` steps (16 FMAs per step, none waiting on the one before it), then
+// stores their sum so that none is dead.  One float per thread to out.
+constexpr int kValuChains = 16;
+
+__global__ __launch_bounds__(256) void valu_probe(float *out, int iters, float x) {
+    float v[kValuChains];
+#pragma unroll
+    for (int k = 0; k < kValuChains; ++k) v[k] = x + (float)k + (float)threadIdx.x;
+    const float g = x * 0.25f;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int k = 0; k < kValuChains; ++k) v[k] = __builtin_fmaf(g, v[k], 1.0f);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kValuChains; ++k) s += v[k];
+    out[(long long)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 }  // namespace
+
+long long valu_probe_fmas(int blocks, int iters) { return (long long)blocks * 256 * iters * kValuChains; }
+
+hipError_t launch_valu_probe(float *out, int blocks, int iters, hipStream_t stream, const KernelTimer &timer) {
+    if (blocks < 1 || iters < 1) return hipErrorInvalidValue;
+    return launch_kernel(valu_probe, dim3((unsigned)blocks), dim3(256), stream, timer, out, iters, 0.5f);
+}
 
 long long read_probe_blocks(long long bytes) { return (bytes / 16 + kChunk - 1) / kChunk; }
 

@@ -27,6 +27,7 @@
 #include <string>
 #include <vector>
 
+#include "probe.h"
 #include "ss2_kernels.h"
 #include "vqm_kernels.h"
 
@@ -1331,6 +1332,43 @@ int read_probe(const void *buf, long long bytes, int reps, double *ms) {
     return 0;
 }
 
+int valu_probe(int waves_per_simd, int iters, int reps, double *tflops) {
+    if (!tflops) return fail(-EINVAL, "NULL argument");
+    if (waves_per_simd < 1 || waves_per_simd > 32 || iters < 1 || iters > (1 << 20) || reps < 1)
+        return fail(-EINVAL, "waves per SIMD 1..32, iterations 1..2^20 and one repetition at least");
+    Lease lease;
+    int rc = lease_ctx(lease);
+    if (rc) return rc;
+    vqm_ctx *ctx = lease.ctx;
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, ctx->device));
+    // four waves of 64 per workgroup, four SIMDs per compute unit
+    const int blocks = waves_per_simd * prop.multiProcessorCount;
+    float *out = nullptr;
+    HIP_TRY_ALLOC(hipMalloc(&out, (size_t)blocks * 256 * sizeof(float)));
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    hipError_t e = hipEventCreate(&ev[0]);
+    if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+    double total = 0.0;
+    for (int r = 0; r <= reps && e == hipSuccess; ++r) {  // launch 0 warms up
+        vqm::KernelTimer kt;
+        kt.start = ev[0];
+        kt.stop = ev[1];
+        e = vqm::launch_valu_probe(out, blocks, iters, ctx->stream, kt);
+        if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+        float t = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[0], ev[1]);
+        if (r > 0) total += t;
+    }
+    for (hipEvent_t x : ev)
+        if (x) (void)hipEventDestroy(x);
+    (void)hipFree(out);
+    if (e != hipSuccess) return fail(-EIO, "VALU probe: %s", hipGetErrorString(e));
+    const double ms = total / reps;
+    *tflops = 2.0 * (double)vqm::valu_probe_fmas(blocks, iters) / (ms * 1e-3) / 1e12;
+    return 0;
+}
+
 int pair_ops(int op, const float *a, const float *b, float *out, int n) {
     if (!a || !b || !out) return fail(-EINVAL, "NULL argument");
     if (op < 0 || op > 4) return fail(-EINVAL, "pair operation %d outside 0..4", op);
@@ -1968,6 +2006,10 @@ int vqm_debug_ss2_blurred(const float *const *ref, const float *const *dis, int 
 
 int vqm_debug_read_probe(const void *buf, long long bytes, int reps, double *ms) {
     return read_probe(buf, bytes, reps, ms);
+}
+
+int vqm_debug_valu_probe(int waves_per_simd, int iters, int reps, double *tflops) {
+    return valu_probe(waves_per_simd, iters, reps, tflops);
 }
 
 int vqm_debug_pair_ops(int op, const float *a, const float *b, float *out, int n) {

@@ -112,6 +112,7 @@ def lib() -> ctypes.CDLL:
         L.vqm_debug_ss2_blurred.argtypes = [ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int, c_int, c_int,
                                             c_int, c_void_p, ctypes.POINTER(c_void_p), c_double_p]
         L.vqm_debug_read_probe.argtypes = [c_void_p, ctypes.c_longlong, c_int, c_double_p]
+        L.vqm_debug_valu_probe.argtypes = [c_int, c_int, c_int, c_double_p]
         L.vqm_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -424,6 +425,14 @@ def vqm_debug_pair_ops(op: int, a, b) -> np.ndarray:
     _check(lib().vqm_debug_pair_ops(int(op), a.ctypes.data, b.ctypes.data, out.ctypes.data, a.shape[0]),
            "vqm_debug_pair_ops")
     return out
+
+
+def vqm_debug_valu_probe(waves_per_simd: int = 8, iters: int = 20000, reps: int = 5) -> float:
+    """TFLOP/s of plain (non-packed) fp32 FMA chains on the vector units."""
+    t = ctypes.c_double()
+    _check(lib().vqm_debug_valu_probe(int(waves_per_simd), int(iters), int(reps), ctypes.byref(t)),
+           "vqm_debug_valu_probe")
+    return t.value
 
 
 def vqm_debug_read_probe(buf, reps: int = 20) -> float:

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define VQM_ABI_VERSION 8
+#define VQM_ABI_VERSION 9
 
 /* Exported symbols (the library is built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -535,6 +535,16 @@ VQM_API int vqm_debug_ss2_blurred(const float *const *ref, const float *const *d
  * decimation's loads can reach on this GPU, for the measurements beside the
  * published peak.  Blocking; allocates a small sink. */
 VQM_API int vqm_debug_read_probe(const void *buf, long long bytes, int reps, double *ms);
+
+/* The fp32 multiply-add rate of the GPU's vector units with ordinary
+ * (non-packed) FMA instructions: waves_per_simd (1..32) waves of 64 lanes
+ * per SIMD, each lane running 16 independent FMA chains for `iters`
+ * (1..2^20) steps, timed with HIP events around each of `reps` launches
+ * (after one untimed one); *tflops receives 2 x lane FMAs / mean kernel
+ * time.  The ceiling of the arithmetic-bound kernels, for the measurements
+ * beside the published fp32 vector peak.  Blocking; allocates one float per
+ * thread. */
+VQM_API int vqm_debug_valu_probe(int waves_per_simd, int iters, int reps, double *tflops);
 
 /* Message of the last failed call on this thread ("" if none). */
 VQM_API const char *vqm_last_error(void);

@@ -52,7 +52,7 @@ def header_constants():
 
 
 def test_abi_version():
-    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 8
+    assert vqm.vqm_abi_version() == header_constants()["VQM_ABI_VERSION"] == 9
 
 
 def test_graft_entry_check_matches_the_built_library():
@@ -267,6 +267,12 @@ def test_ss2_chain_refuses_bad_arguments_before_any_hip_call():
     assert L.vqm_ss2_collect(None, sp) == -errno.EINVAL
     assert L.vqm_ss2_collect(ctx, None) == -errno.EINVAL
     assert L.vqm_ss2_in_flight(None) == 0
+    t = ctypes.c_double()
+    assert L.vqm_debug_valu_probe(0, 100, 1, ctypes.byref(t)) == -errno.EINVAL   # waves per SIMD
+    assert L.vqm_debug_valu_probe(33, 100, 1, ctypes.byref(t)) == -errno.EINVAL
+    assert L.vqm_debug_valu_probe(4, 0, 1, ctypes.byref(t)) == -errno.EINVAL     # iterations
+    assert L.vqm_debug_valu_probe(4, 100, 0, ctypes.byref(t)) == -errno.EINVAL   # repetitions
+    assert L.vqm_debug_valu_probe(4, 100, 1, None) == -errno.EINVAL
     c = np.zeros(4, np.float32)
     assert L.vqm_ss2_cascade_coefficients(0.0, c.ctypes.data) == -errno.EINVAL
     assert L.vqm_ss2_cascade_coefficients(1.5, None) == -errno.EINVAL
