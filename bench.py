@@ -120,11 +120,12 @@ def default_streams(metric: str, scale: int) -> int:
     over.  float_ssim with decimation: one; a second one overlapping
     consecutive launches measured slower (the steps contend for HBM and for
     the per-XCD layout: 2160p 164k -> 149k, 1080p 675k -> 634k, 853x481
-    919k -> 843k frames/s).  Work without an HBM-bound part takes two: the
-    compute-bound launches' tails (MS-SSIM's small levels and combine, the
-    scale-1 map's last tiles) leave SIMDs idle, which the other context's
-    batch fills (2160p MS-SSIM 19.4k -> 21.4k, 576x324 1.03M -> 1.15M)."""
-    return 2 if metric == "ms_ssim" or scale == 1 else 1
+    919k -> 843k frames/s).  The scale-1 map takes two: its launches' last
+    tiles leave SIMDs idle, which the other context's batch fills (576x324
+    1.03M -> 1.15M).  MS-SSIM takes one: a context on its own stream already
+    alternates its batches over two streams, which fills the small levels'
+    idle SIMDs the same way (2160p 19.8k -> 21.8k; two such contexts 21.3k)."""
+    return 2 if scale == 1 and metric != "ms_ssim" else 1
 
 
 def cpu_model() -> str:
@@ -344,8 +345,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="workload number 1..5")
     ap.add_argument("--streams", type=int, default=0,
-                    help="contexts/streams batches rotate over (0: the metric's best, 1 for float_ssim, 2 for MS-SSIM)")
+                    help="contexts batches rotate over (0: the metric's best: 1, or 2 for float_ssim at scale 1)")
     ap.add_argument("--batch", type=int, default=32, help="frames per submit (and per kernel launch)")
+    ap.add_argument("--torch-streams", action="store_true",
+                    help="contexts on torch streams instead of library-owned ones")
     ap.add_argument("--lag", type=int, default=0,
                     help="frames submitted after a frame before it is collected (0: 3*batch)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0: skip)")
@@ -515,7 +518,10 @@ def main():
     if args.streams <= 0:
         args.streams = default_streams(wl.metric, s)
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
-    ctxs = [vqm.Context(0, st) for st in streams]
+    # Contexts on library-owned streams by default: such a context alternates
+    # its MS-SSIM batches over two streams of its own (on a caller's stream
+    # every batch stays there).
+    ctxs = [vqm.Context(0, st) if args.torch_streams else vqm.Context(0) for st in streams]
     lag = args.lag if args.lag > 0 else 3 * args.batch
     # The timed run streams the workload's frames K times over without a
     # break, as a video is scored (the pipeline fills once and drains once).

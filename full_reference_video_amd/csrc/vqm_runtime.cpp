@@ -258,6 +258,13 @@ struct vqm_ctx {
     std::deque<PendingBatch> pipeline;
     bool timing = false;
     bool capturing = false;              // launches go into a graph: no completion events
+    // MS-SSIM batches of a context that owns its stream alternate between
+    // that stream and this one (made on first use), so that one batch's
+    // small levels run beside the next batch's first level; `ms_ready`
+    // orders a batch on ms_aux after the uploads on the context's stream.
+    hipStream_t ms_aux = nullptr;
+    hipEvent_t ms_ready = nullptr;
+    bool ms_flip = false;
     std::vector<TimedLaunch> timed;      // recorded, not yet read
     std::vector<hipEvent_t> event_pool;  // free timing events
     double time_ms[4] = {0, 0, 0, 0};
@@ -602,7 +609,8 @@ int drain(vqm_ctx *ctx) {
     return 0;
 }
 
-int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r, const void *const *in_d) {
+int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r, const void *const *in_d,
+                   hipStream_t stream) {
     const Geometry &g = sl[0]->geo;
     const float unit = ldexpf(1.0f, -(g.bpc - 8));
     for (int j = 0; j < kLevels; ++j) {
@@ -621,7 +629,7 @@ int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r
         const int next_pitch = j + 1 < kLevels ? g.lpitch[j + 1] : 0;
         LAUNCH_TIMED(ctx, j == 0 ? VQM_KERNEL_MSSSIM_LEVEL1 : VQM_KERNEL_MSSSIM_COARSE, n,
                      vqm::launch_ms_level(mb, n, kind, g.lpitch[j], g.lw[j], g.lh[j], next_pitch,
-                                          j == 0 ? unit : 1.0f, ctx->taps, ctx->stream, timer_));
+                                          j == 0 ? unit : 1.0f, ctx->taps, stream, timer_));
     }
     vqm::MsFinishBatch fb;
     memset(&fb, 0, sizeof fb);
@@ -636,8 +644,28 @@ int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r
         lv.offset[j] = (long long)sl[0]->span[j];
         lv.count[j] = (double)(g.lw[j] - 10) * (double)(g.lh[j] - 10);
     }
-    const hipError_t e = vqm::launch_ms_finish(fb, n, lv, ctx->stream);
+    const hipError_t e = vqm::launch_ms_finish(fb, n, lv, stream);
     if (e != hipSuccess) return fail(-EIO, "kernel launch: %s", hipGetErrorString(e));
+    return 0;
+}
+
+// The stream an MS-SSIM batch runs on: every other batch of a context that
+// owns its stream goes to ms_aux, after the work already on the context's
+// stream (its uploads).  A caller's stream keeps every batch (the caller
+// orders its own work against it), and so do graph capture and kernel
+// timing (whose events must bracket one launch at a time).
+int msssim_stream(vqm_ctx *ctx, hipStream_t *out) {
+    *out = ctx->stream;
+    if (!ctx->own_stream || ctx->capturing || ctx->timing) return 0;
+    ctx->ms_flip = !ctx->ms_flip;
+    if (!ctx->ms_flip) return 0;
+    if (!ctx->ms_aux) {
+        HIP_TRY_ALLOC(hipEventCreateWithFlags(&ctx->ms_ready, hipEventDisableTiming));
+        HIP_TRY_ALLOC(hipStreamCreate(&ctx->ms_aux));  // blocking, default priority
+    }
+    HIP_TRY(hipEventRecord(ctx->ms_ready, ctx->stream));
+    HIP_TRY(hipStreamWaitEvent(ctx->ms_aux, ctx->ms_ready, 0));
+    *out = ctx->ms_aux;
     return 0;
 }
 
@@ -688,12 +716,14 @@ int submit(vqm_ctx *ctx, int kind, const void *const *refs, const void *const *d
         rc = step(ctx, &p);
         if (rc) return rc;
     } else {
-        rc = enqueue_msssim(ctx, p.sl, n, p.in_r, p.in_d);
+        hipStream_t ms = nullptr;
+        if ((rc = msssim_stream(ctx, &ms))) return rc;
+        rc = enqueue_msssim(ctx, p.sl, n, p.in_r, p.in_d, ms);
         if (rc) return rc;
         BatchEvent *be = nullptr;
         rc = take_batch_event(ctx, &be);
         if (rc) return rc;
-        HIP_TRY(hipEventRecord(be->ev, ctx->stream));
+        HIP_TRY(hipEventRecord(be->ev, ms));
         be->refs = n;
         be->completed = false;
         for (int i = 0; i < n; ++i) p.sl[i]->batch = be;
@@ -769,6 +799,7 @@ void destroy(vqm_ctx *ctx) {
     (void)hipGetDevice(&cur);
     (void)hipSetDevice(ctx->device);
     (void)hipStreamSynchronize(ctx->stream);
+    if (ctx->ms_aux) (void)hipStreamSynchronize(ctx->ms_aux);
     for (Slot &s : ctx->slots) s.release();
     for (auto &be : ctx->batch_events) (void)hipEventDestroy(be->ev);
     for (const TimedLaunch &t : ctx->timed) {
@@ -780,6 +811,8 @@ void destroy(vqm_ctx *ctx) {
     if (ctx->ss2_result_host) (void)hipHostFree(ctx->ss2_result_host);
     ctx->ss2c.release();
     for (Ss2Slot &sl : ctx->ss2_slot) sl.release();
+    if (ctx->ms_aux) (void)hipStreamDestroy(ctx->ms_aux);
+    if (ctx->ms_ready) (void)hipEventDestroy(ctx->ms_ready);
     if (ctx->own_stream) (void)hipStreamDestroy(ctx->stream);
     if (cur >= 0) (void)hipSetDevice(cur);
     delete ctx;
@@ -1453,7 +1486,7 @@ int record_pass(vqm_graph *g, const void *const *refs, const void *const *dis, i
             p.in_r[i] = refs[b0 + i];
             p.in_d[i] = dis[b0 + i];
         }
-        rc = g->kind == KIND_SSIM ? step(ctx, &p) : enqueue_msssim(ctx, p.sl, p.n, p.in_r, p.in_d);
+        rc = g->kind == KIND_SSIM ? step(ctx, &p) : enqueue_msssim(ctx, p.sl, p.n, p.in_r, p.in_d, ctx->stream);
     }
     if (rc == 0 && g->kind == KIND_SSIM) rc = drain(ctx);
     ctx->capturing = false;
@@ -1907,7 +1940,7 @@ int vqm_debug_pyramid(vqm_ctx *ctx, const void *ref, const void *dis, int w, int
     const void *dref = nullptr, *ddis = nullptr;
     rc = debug_slot(ctx, g, ref, dis, &sl, &dref, &ddis);
     if (rc) return rc;
-    rc = enqueue_msssim(ctx, &sl, 1, &dref, &ddis);
+    rc = enqueue_msssim(ctx, &sl, 1, &dref, &ddis, ctx->stream);
     if (rc) return rc;
     const int j = level - 1;
     HIP_TRY(hipMemcpy2DAsync(out_ref, g.lw[j] * sizeof(float), sl->planes + sl->off_ref[j],
@@ -1950,7 +1983,7 @@ int vqm_debug_pyramid_batch(vqm_ctx *ctx, const void *const *refs, const void *c
         if (rc) return rc;
         sl[i] = &s;
     }
-    rc = enqueue_msssim(ctx, sl, n, dref, ddis);
+    rc = enqueue_msssim(ctx, sl, n, dref, ddis, ctx->stream);
     if (rc) return rc;
     const int j = level - 1;
     const size_t plane = (size_t)g.lw[j] * (size_t)g.lh[j];

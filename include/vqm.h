@@ -196,8 +196,12 @@ typedef struct vqm_ctx vqm_ctx;
  * pinned staging and the per-slot scratch such a context owns).  `hip_stream`
  * is a hipStream_t on that device to enqueue on (e.g.
  * torch.cuda.current_stream().cuda_stream), or NULL for a library-owned
- * blocking stream (see "Ordering of device input" above).  The stream must
- * outlive the context.  A context is not thread-safe: use one per thread.
+ * blocking stream (see "Ordering of device input" above).  A context on a
+ * library-owned stream runs every other MS-SSIM batch on a second stream of
+ * its own, after the work already on the first (its uploads), so that one
+ * batch's small levels run beside the next batch's first level; on a
+ * caller's stream, in graph capture and with kernel timing on, every batch
+ * stays on the one stream.  The stream must outlive the context.  A context is not thread-safe: use one per thread.
  * Calls on a context make its device current while they run and restore the
  * calling thread's current device before they return. */
 VQM_API int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out);

@@ -78,7 +78,7 @@ def test_default_streams_per_path():
     assert bench.default_streams("float_ssim", 8) == 1
     assert bench.default_streams("float_ssim", 2) == 1
     assert bench.default_streams("float_ssim", 1) == 2
-    assert bench.default_streams("ms_ssim", 1) == 2
+    assert bench.default_streams("ms_ssim", 1) == 1
 
 
 def test_cpu_baselines_time_the_oracle():

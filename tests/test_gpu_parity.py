@@ -451,6 +451,40 @@ def test_msssim_batched_equals_single(ctx):
     assert abs(single[2][0] - oracle.msssim(*pairs[2], 8)) <= TOL
 
 
+def test_msssim_batches_in_flight_on_both_streams(torch_cuda):
+    # A context on a library-owned stream alternates its MS-SSIM batches over
+    # that stream and a second one: several batches in flight at once (host
+    # and device input, interleaved with float_ssim frames on the first
+    # stream), collected in order, give the blocking calls' scores and level
+    # means bit for bit; so does a context on a caller's stream, which keeps
+    # every batch on that stream.
+    torch = torch_cuda
+    src = synth.FrameSource(5, w=960, h=544)
+    pairs = [src.pair(t) for t in range(12)]
+    single = [vqm.vqm_msssim_frame_lcs(r, d, 8) for r, d in pairs]
+    ssim_src = synth.FrameSource(2)
+    ssim_pair = ssim_src.pair(0)
+    ssim_want = vqm.vqm_ssim_frame(*ssim_pair, ssim_src.bpc)
+    dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
+    torch.cuda.synchronize()
+    for stream in (None, torch.cuda.Stream()):
+        say(f"msssim batches in flight, stream {stream}")
+        with vqm.Context(0, stream) as c:
+            for b0 in range(0, 12, 3):
+                batch = pairs[b0:b0 + 3] if b0 % 6 == 0 else dev[b0:b0 + 3]
+                c.vqm_msssim_submit_batch([r for r, _ in batch], [d for _, d in batch], 8)
+                if b0 == 3:
+                    c.vqm_ssim_submit(*ssim_pair, ssim_src.bpc)
+            got = []
+            for k in range(13):
+                got.append(c.vqm_collect(want_lcs=True))
+        ssim_got = got.pop(6)[0]
+        assert ssim_got == ssim_want
+        for (s1, l1), (s2, l2) in zip(single, got):
+            assert s2 == s1
+            assert np.array_equal(l1, l2)
+
+
 @pytest.mark.parametrize("metric,c", [(0, 2), (0, 4), (1, 5)])
 def test_score_frames_loop_matches_single_frames(torch_cuda, metric, c):
     torch = torch_cuda
