@@ -290,21 +290,24 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
         for (int p = 0; p < 5; ++p) ring[s][p][0] = ring[s][p][1] = 0.0f;
 
     const bool vA = x0 + c < MW, vB = x0 + c + 1 < MW;
-    LcsAcc acc;  // at most 22 pixels (one group of rows) in 32-bit integers
+    LcsAcc acc;  // at most 44 pixels (one group of rows) in 32-bit integers
     double DL = 0.0, DC = 0.0, PS = 0.0;
     float psx = 0.0f, psy = 0.0f;  // the previous row's pair sums
 
     RowPair nm{}, nh{};
     load_row(0, nm);
     load_halo(0, nh);
-    for (int t0 = 0; t0 < in_rows; t0 += 11) {
-        static_steps(std::make_integer_sequence<int, 11>{}, [&](auto uc) __attribute__((always_inline)) {
+    // Groups of 22 rows: the eleven output slots and the row buffer's parity
+    // are compile-time at every step (22 rows unrolled against 11 issue 6 %
+    // fewer VALU instructions; level 1 at 2160p 1093 -> 1080 us per batch).
+    for (int t0 = 0; t0 < in_rows; t0 += 22) {
+        static_steps(std::make_integer_sequence<int, 22>{}, [&](auto uc) __attribute__((always_inline)) {
             constexpr int u = decltype(uc)::value;
             const int t = t0 + u;
             if (t >= in_rows) return;
             // Convert this row, then reuse its registers for the next row's
             // loads (they land while this row is filtered).
-            float *buf = lds + (t & 1) * 5 * P;
+            float *buf = lds + (u & 1) * 5 * P;  // t0 is even
             const float xa = fmaf(Raw::value(nm.ra), unit, -kMomentOffset);
             const float xb = fmaf(Raw::value(nm.rb), unit, -kMomentOffset);
             const float ya = fmaf(Raw::value(nm.da), unit, -kMomentOffset);
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
             }
             psx = sx;
             psy = sy;
-            if ((t & 1) == 0) {
+            if ((u & 1) == 0) {
                 // Row t + 1's halo goes into the buffer the previous row was
                 // read from: those reads come first.
                 __syncthreads();
