@@ -27,6 +27,7 @@
 #include <string>
 #include <vector>
 
+#include "msssim_kernels.h"
 #include "probe.h"
 #include "ss2_kernels.h"
 #include "vqm_kernels.h"
@@ -610,7 +611,7 @@ int drain(vqm_ctx *ctx) {
 }
 
 int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r, const void *const *in_d,
-                   hipStream_t stream) {
+                   hipStream_t stream, bool overlapped = false) {
     const Geometry &g = sl[0]->geo;
     const float unit = ldexpf(1.0f, -(g.bpc - 8));
     for (int j = 0; j < kLevels; ++j) {
@@ -629,7 +630,7 @@ int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r
         const int next_pitch = j + 1 < kLevels ? g.lpitch[j + 1] : 0;
         LAUNCH_TIMED(ctx, j == 0 ? VQM_KERNEL_MSSSIM_LEVEL1 : VQM_KERNEL_MSSSIM_COARSE, n,
                      vqm::launch_ms_level(mb, n, kind, g.lpitch[j], g.lw[j], g.lh[j], next_pitch,
-                                          j == 0 ? unit : 1.0f, ctx->taps, stream, timer_));
+                                          j == 0 ? unit : 1.0f, ctx->taps, overlapped, stream, timer_));
     }
     vqm::MsFinishBatch fb;
     memset(&fb, 0, sizeof fb);
@@ -640,7 +641,7 @@ int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r
     }
     vqm::MsLevels lv;
     for (int j = 0; j < kLevels; ++j) {
-        lv.nb[j] = vqm::ms_partials(g.lw[j], g.lh[j], n);
+        lv.nb[j] = vqm::ms_partials(g.lw[j], g.lh[j], n, overlapped);
         lv.offset[j] = (long long)sl[0]->span[j];
         lv.count[j] = (double)(g.lw[j] - 10) * (double)(g.lh[j] - 10);
     }
@@ -651,12 +652,15 @@ int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r
 
 // The stream an MS-SSIM batch runs on: every other batch of a context that
 // owns its stream goes to ms_aux, after the work already on the context's
-// stream (its uploads).  A caller's stream keeps every batch (the caller
-// orders its own work against it), and so do graph capture and kernel
-// timing (whose events must bracket one launch at a time).
-int msssim_stream(vqm_ctx *ctx, hipStream_t *out) {
+// stream (its uploads); *overlapped tells the level kernels' planner that
+// the batch shares the GPU with the other stream's.  A caller's stream keeps
+// every batch (the caller orders its own work against it), and so do graph
+// capture and kernel timing (whose events must bracket one launch at a time).
+int msssim_stream(vqm_ctx *ctx, hipStream_t *out, bool *overlapped) {
     *out = ctx->stream;
+    *overlapped = false;
     if (!ctx->own_stream || ctx->capturing || ctx->timing) return 0;
+    *overlapped = true;
     ctx->ms_flip = !ctx->ms_flip;
     if (!ctx->ms_flip) return 0;
     if (!ctx->ms_aux) {
@@ -717,8 +721,9 @@ int submit(vqm_ctx *ctx, int kind, const void *const *refs, const void *const *d
         if (rc) return rc;
     } else {
         hipStream_t ms = nullptr;
-        if ((rc = msssim_stream(ctx, &ms))) return rc;
-        rc = enqueue_msssim(ctx, p.sl, n, p.in_r, p.in_d, ms);
+        bool overlapped = false;
+        if ((rc = msssim_stream(ctx, &ms, &overlapped))) return rc;
+        rc = enqueue_msssim(ctx, p.sl, n, p.in_r, p.in_d, ms, overlapped);
         if (rc) return rc;
         BatchEvent *be = nullptr;
         rc = take_batch_event(ctx, &be);
