@@ -1167,7 +1167,7 @@ int ss2_check(const float *const *ref, const float *const *dis, int nch, int w, 
 }
 
 // Every scale of one frame enqueued on `stream`: the pyramid of the two
-// pictures (a downsample launch per later scale), then the row pass of every
+// pictures (one launch for every later scale), then the row pass of every
 // scale with the products, the column pass of every scale with the
 // statistics, and the sums of each (scale, channel)'s partials into buf's
 // pinned result block (6 * nch * nscales doubles, NaN until written).

@@ -201,7 +201,8 @@ typedef struct vqm_ctx vqm_ctx;
  * its own, after the work already on the first (its uploads), so that one
  * batch's small levels run beside the next batch's first level; on a
  * caller's stream, in graph capture and with kernel timing on, every batch
- * stays on the one stream.  The stream must outlive the context.  A context is not thread-safe: use one per thread.
+ * stays on the one stream.  The stream must outlive the context.  A context
+ * is not thread-safe: use one per thread.
  * Calls on a context make its device current while they run and restore the
  * calling thread's current device before they return. */
 VQM_API int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out);
@@ -480,9 +481,10 @@ VQM_API int vqm_ss2_downsample(const float *in, float *out, int w, int h);
  * (and the smaller scales' images), grown on demand.  Blocking: four
  * launches for every scale together (the pyramid, the row pass, the column
  * pass with the statistics, the sums; three for one scale) on a
- * library-owned blocking stream and one wait.  -EINVAL for NULL pointers, bad counts or sizes,
- * non-finite coefficients or planes that are not device memory of the
- * current device; -ENOMEM when the workspace cannot grow. */
+ * library-owned blocking stream and one wait.  -EINVAL for NULL pointers,
+ * bad counts or sizes, non-finite coefficients or planes that are not
+ * device memory of the current device; -ENOMEM when the workspace cannot
+ * grow. */
 VQM_API int vqm_ss2_scale_sums(const float *const *ref, const float *const *dis, int nch, int w, int h,
                                int nscales, const float *coef, double *sums);
 
@@ -497,7 +499,7 @@ VQM_API int vqm_ss2_scale_sums(const float *const *ref, const float *const *dis,
  * demand.  ref, dis must stay unchanged until the matching vqm_ss2_collect.
  * Arguments and errors as vqm_ss2_scale_sums (ref, dis on the context's
  * device), and -EAGAIN with VQM_SS2_MAX_IN_FLIGHT frames already in flight;
- * nothing is enqueued on error.  These slots are apart from the float_ssim
+ * no frame is in flight after an error.  These slots are apart from the float_ssim
  * and MS-SSIM ones: vqm_collect never returns a chain frame. */
 VQM_API int vqm_ss2_submit(vqm_ctx *ctx, const float *const *ref, const float *const *dis, int nch, int w, int h,
                            int nscales, const float *coef);
