@@ -347,8 +347,8 @@ def main():
     ap.add_argument("--streams", type=int, default=0,
                     help="contexts batches rotate over (0: the metric's best: 1, or 2 for float_ssim at scale 1)")
     ap.add_argument("--batch", type=int, default=32, help="frames per submit (and per kernel launch)")
-    ap.add_argument("--torch-streams", action="store_true",
-                    help="contexts on torch streams instead of library-owned ones")
+    ap.add_argument("--ctx-streams", choices=("own", "torch"), default="own",
+                    help="contexts on library-owned streams (default) or on torch streams")
     ap.add_argument("--lag", type=int, default=0,
                     help="frames submitted after a frame before it is collected (0: 3*batch)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0: skip)")
@@ -520,8 +520,8 @@ def main():
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
     # Contexts on library-owned streams by default: such a context alternates
     # its MS-SSIM batches over two streams of its own (on a caller's stream
-    # every batch stays there).
-    ctxs = [vqm.Context(0, st) if args.torch_streams else vqm.Context(0) for st in streams]
+    # every batch stays there); float_ssim measures the same on either.
+    ctxs = [vqm.Context(0, st) if args.ctx_streams == "torch" else vqm.Context(0) for st in streams]
     lag = args.lag if args.lag > 0 else 3 * args.batch
     # The timed run streams the workload's frames K times over without a
     # break, as a video is scored (the pipeline fills once and drains once).

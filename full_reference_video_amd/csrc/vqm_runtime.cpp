@@ -266,6 +266,7 @@ struct vqm_ctx {
     hipStream_t ms_aux = nullptr;
     hipEvent_t ms_ready = nullptr;
     bool ms_flip = false;
+    bool ms_overlap = false;  // a caller's context on a library-owned stream (not the blocking calls' pool)
     std::vector<TimedLaunch> timed;      // recorded, not yet read
     std::vector<hipEvent_t> event_pool;  // free timing events
     double time_ms[4] = {0, 0, 0, 0};
@@ -650,16 +651,18 @@ int enqueue_msssim(vqm_ctx *ctx, Slot *const *sl, int n, const void *const *in_r
     return 0;
 }
 
-// The stream an MS-SSIM batch runs on: every other batch of a context that
-// owns its stream goes to ms_aux, after the work already on the context's
-// stream (its uploads); *overlapped tells the level kernels' planner that
-// the batch shares the GPU with the other stream's.  A caller's stream keeps
-// every batch (the caller orders its own work against it), and so do graph
-// capture and kernel timing (whose events must bracket one launch at a time).
+// The stream an MS-SSIM batch runs on: every other batch of a caller's
+// context on a library-owned stream goes to ms_aux, after the work already
+// on the context's stream (its uploads); *overlapped tells the level
+// kernels' planner that the batch shares the GPU with the other stream's.
+// A caller's stream keeps every batch (the caller orders its own work
+// against it), and so do the blocking calls' contexts (each call waits for
+// its frame), graph capture and kernel timing (whose events must bracket one
+// launch at a time).
 int msssim_stream(vqm_ctx *ctx, hipStream_t *out, bool *overlapped) {
     *out = ctx->stream;
     *overlapped = false;
-    if (!ctx->own_stream || ctx->capturing || ctx->timing) return 0;
+    if (!ctx->ms_overlap || ctx->capturing || ctx->timing) return 0;
     *overlapped = true;
     ctx->ms_flip = !ctx->ms_flip;
     if (!ctx->ms_flip) return 0;
@@ -1786,7 +1789,11 @@ int vqm_msssim_frame_yuv(const void *const *ref, const void *const *dis, int w, 
 
 int vqm_ctx_create(int device, void *hip_stream, vqm_ctx **out) {
     DeviceScope scope;
-    return create(device, hip_stream, out);
+    const int rc = create(device, hip_stream, out);
+    // The blocking calls' pooled contexts wait for each frame, so they have
+    // no second batch to overlap: only a caller's context alternates.
+    if (rc == 0) (*out)->ms_overlap = (*out)->own_stream;
+    return rc;
 }
 
 void vqm_ctx_destroy(vqm_ctx *ctx) {
