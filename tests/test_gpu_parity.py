@@ -529,15 +529,18 @@ def test_mixed_metrics_and_sizes_in_one_context(ctx):
 
 # ------------------------------------------------------------ full workloads, bench launch shape
 
-def _score_stream(torch, pairs, bpc, metric, batch=vqm.VQM_MAX_BATCH, lag=0, n_streams=1, want_lcs=False):
-    """Score device-resident pairs the way bench.py times them: one context
-    per torch stream, batches of VQM_MAX_BATCH frames per launch, each frame
-    collected three batches after its submit (lag 0).  With want_lcs, also
-    the 15 level means per frame (from a second pass that asks for them)."""
+def _score_stream(torch, pairs, bpc, metric, batch=vqm.VQM_MAX_BATCH, lag=0, n_streams=1, want_lcs=False,
+                  own_streams=True):
+    """Score device-resident pairs the way bench.py times them: n_streams
+    contexts on library-owned streams (whose MS-SSIM batches alternate over
+    two streams each, with the overlapped kernel plans), or with
+    own_streams=False on torch streams (every batch on its context's one
+    stream), batches of VQM_MAX_BATCH frames per launch, each frame collected
+    three batches after its submit (lag 0).  With want_lcs, also the 15
+    level means per frame (from a second pass that asks for them)."""
     dev = [(to_dev(torch, r), to_dev(torch, d)) for r, d in pairs]
     fs = vqm.FrameSet([r for r, _ in dev], [d for _, d in dev], bpc)
-    streams = [torch.cuda.Stream() for _ in range(n_streams)]
-    ctxs = [vqm.Context(0, s) for s in streams]
+    ctxs = [vqm.Context(0) if own_streams else vqm.Context(0, torch.cuda.Stream()) for _ in range(n_streams)]
     try:
         first = vqm.vqm_score_frames(ctxs, metric, fs, batch, lag).tolist()
         again = vqm.vqm_score_frames(ctxs, metric, fs, batch, lag).tolist()
@@ -603,8 +606,12 @@ def test_full_msssim_workload_in_bench_launch_shape(torch_cuda):
     for t in range(n):
         assert abs(got[t] - rec[str(t)]["score"]) <= TOL, (t, got[t], rec[str(t)]["score"])
         assert np.all(np.abs(lcs[t] - np.array(rec[str(t)]["lcs"])) <= TOL), t
-    # two contexts on two streams, as bench.py times MS-SSIM
-    say("full MS-SSIM workload: two streams")
+    # every batch on one torch stream (the one-stream kernel plans: 136-row
+    # level-1 strips where the overlapped batches above took 308), and two
+    # contexts of two streams each: the same bits
+    say("full MS-SSIM workload: one torch stream")
+    assert _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_MS_SSIM, own_streams=False) == single
+    say("full MS-SSIM workload: two contexts")
     assert _score_stream(torch_cuda, pairs, src.bpc, vqm.VQM_METRIC_MS_SSIM, n_streams=2) == single
     say("full MS-SSIM workload: oracle frame 23")
     assert abs(got[23] - oracle.msssim(*pairs[23], src.bpc)) <= TOL, got[23]
