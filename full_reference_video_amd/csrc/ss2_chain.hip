@@ -141,7 +141,11 @@ __device__ __forceinline__ int scale_of(const Chain &ch, int block, bool cols) {
 
 // ------------------------------------------------------------------ row pass
 
-template <int NP>
+// V4: every scale's rows are whole 16-byte groups (width and plane stride
+// multiples of four floats, 16-byte aligned planes), so each lane moves
+// four floats per load, store and LDS access (4 loads per image and chunk
+// instead of 13); the arithmetic is the same.
+template <int NP, bool V4>
 __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coef k) {
     constexpr int L = Shape<NP>::kRowLines, NT = Shape<NP>::kThreads, KS = Shape<NP>::kState;
     // chunk columns; tile pitch CH + 4: each lane's row starts 16-byte aligned
@@ -174,10 +178,13 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
     const float *src1 = (NP == 5 && p >= 2) ? tin + f1 * TILE + line * PT : tin + NI * TILE;
     float *const mine = tout + min(p, NP - 1) * TILE + line * PT;
     const int tcol = t % CH, trow = t / CH;  // tile share (loads and stores)
+    constexpr int Q = CH / 4, RS4 = NT / Q, KI4 = (L + RS4 - 1) / RS4;  // the same with float4s
+    const int tq = t % Q, trow4 = t / Q;
 
     if (t < PT) tin[NI * TILE + t] = 1.0f;
 
     float pre[kRing][NI][KI];
+    float4 pre4[kRing][NI][KI4];
     const bool full_rows = nrows == L;
     auto fetch = [&](float (&dst)[NI][KI], int ch) {
         if (ch < 0 || ch >= nchunks) return;
@@ -209,6 +216,32 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
                 if (i < KI - 1 || row < L) tin[q * TILE + row * PT + tcol] = src[q][i];
             }
     };
+    // Four columns per lane: a chunk's columns come in whole float4s (the
+    // width is a multiple of four), so only rows and whole groups are guarded.
+    auto fetch4 = [&](float4 (&dst)[NI][KI4], int ch) {
+        if (ch < 0 || ch >= nchunks) return;
+        const int c0 = ch * CH, n = min(CH, w - c0);
+#pragma unroll
+        for (int q = 0; q < NI; ++q) {
+            const float *src = img[q] + (long long)(r0 + trow4) * w + c0 + 4 * tq;
+#pragma unroll
+            for (int i = 0; i < KI4; ++i) {
+                const int row = trow4 + i * RS4;
+                const bool in = (full_rows && n == CH) ? (i < KI4 - 1 || row < L) : (row < nrows && 4 * tq < n);
+                dst[q][i] = in ? *reinterpret_cast<const float4 *>(src + (long long)i * RS4 * w)
+                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+        }
+    };
+    auto stage4 = [&](const float4 (&src)[NI][KI4]) {
+#pragma unroll
+        for (int q = 0; q < NI; ++q)
+#pragma unroll
+            for (int i = 0; i < KI4; ++i) {
+                const int row = trow4 + i * RS4;
+                if (i < KI4 - 1 || row < L) *reinterpret_cast<float4 *>(tin + q * TILE + row * PT + 4 * tq) = src[q][i];
+            }
+    };
     auto samples = [&](float (&v)[CH]) {
 #pragma unroll
         for (int j = 0; j < CH; ++j) v[j] = src0[j] * src1[j];
@@ -216,14 +249,25 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
 
     // Causal walk over every chunk but the last, keeping each end state.
     State f;
-    fetch(pre[0], 0);
-    fetch(pre[1], 1);
+    if constexpr (V4) {
+        fetch4(pre4[0], 0);
+        fetch4(pre4[1], 1);
+    } else {
+        fetch(pre[0], 0);
+        fetch(pre[1], 1);
+    }
     auto fbody = [&](auto S, int ch) {
         constexpr int si = decltype(S)::value;
         if (ch >= nchunks - 1) return;
-        stage(pre[si]);
+        if constexpr (V4)
+            stage4(pre4[si]);
+        else
+            stage(pre[si]);
         __syncthreads();
-        fetch(pre[(si + 2) % kRing], ch + 2);
+        if constexpr (V4)
+            fetch4(pre4[(si + 2) % kRing], ch + 2);
+        else
+            fetch(pre[(si + 2) % kRing], ch + 2);
         if (live) {
             float v[CH];
             samples(v);
@@ -252,16 +296,27 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
         dst.s2 = ck[(ch - 1) * KS + NT + t];
         dst.s3 = ck[(ch - 1) * KS + 2 * NT + t];
     };
-    fetch(pre[0], nchunks - 1);
-    fetch(pre[1], nchunks - 2);
+    if constexpr (V4) {
+        fetch4(pre4[0], nchunks - 1);
+        fetch4(pre4[1], nchunks - 2);
+    } else {
+        fetch(pre[0], nchunks - 1);
+        fetch(pre[1], nchunks - 2);
+    }
     fetch_state(before[0], nchunks - 1);
     auto bbody = [&](auto S, int ch) {
         constexpr int si = decltype(S)::value;
         if (ch < 0) return;
         const int c0 = ch * CH, n = min(CH, w - c0);
-        stage(pre[si]);
+        if constexpr (V4)
+            stage4(pre4[si]);
+        else
+            stage(pre[si]);
         __syncthreads();
-        fetch(pre[(si + 2) % kRing], ch - 2);
+        if constexpr (V4)
+            fetch4(pre4[(si + 2) % kRing], ch - 2);
+        else
+            fetch(pre[(si + 2) % kRing], ch - 2);
         fetch_state(before[(si + 1) % kRing], ch - 1);
         if (live) {
             State r = before[si];
@@ -278,7 +333,19 @@ __global__ __launch_bounds__(Shape<NP>::kThreads) void ss2_rows(Chain chain, Coe
             }
         }
         __syncthreads();
-        if (full_rows && n == CH) {  // every output of the tile exists: unrolled, unguarded but the last row
+        if constexpr (V4) {  // whole float4 groups: rows and groups past the tile are skipped
+#pragma unroll
+            for (int q = 0; q < NP; ++q) {
+                float *const o = d.rows[c] + (long long)q * d.pstride + (long long)(r0 + trow4) * w + c0 + 4 * tq;
+#pragma unroll
+                for (int i = 0; i < KI4; ++i) {
+                    const int row = trow4 + i * RS4;
+                    if (row < nrows && 4 * tq < n)
+                        *reinterpret_cast<float4 *>(o + (long long)i * RS4 * w) =
+                            *reinterpret_cast<const float4 *>(tout + q * TILE + row * PT + 4 * tq);
+                }
+            }
+        } else if (full_rows && n == CH) {  // every output of the tile exists: unrolled, unguarded but the last row
 #pragma unroll
             for (int q = 0; q < NP; ++q) {
                 float *const o = d.rows[c] + (long long)q * d.pstride + (long long)(r0 + trow) * w + c0 + tcol;
@@ -672,12 +739,23 @@ hipError_t launch_ss2_chain(const Ss2ChainArgs &args, hipStream_t stream, const 
     const int nrow = last.row_block0 + (np == 5 ? row_blocks<5>(last.h) : row_blocks<1>(last.h)) * nch;
     const int ncol = last.col_block0 + (np == 5 ? col_blocks<5>(last.w) : col_blocks<1>(last.w)) * nch;
     hipError_t e;
+    // Whole 16-byte groups at every scale: widths and plane strides multiples
+    // of four floats, images and row planes 16-byte aligned.
+    bool v4 = true;
+    for (int s = 0; s < ns; ++s) {
+        const ScaleDesc &d = ch.s[s];
+        v4 = v4 && d.w % 4 == 0 && d.pstride % 4 == 0;
+        for (int c = 0; c < nch; ++c)
+            v4 = v4 && ((reinterpret_cast<uintptr_t>(d.a[c]) | reinterpret_cast<uintptr_t>(d.b[c]) |
+                         reinterpret_cast<uintptr_t>(d.rows[c])) & 15u) == 0;
+    }
     if (np == 5) {
-        e = launch_kernel(ss2_rows<5>, dim3(nrow), dim3(Shape<5>::kThreads), stream, rows_timer, ch, k);
+        e = v4 ? launch_kernel(ss2_rows<5, true>, dim3(nrow), dim3(Shape<5>::kThreads), stream, rows_timer, ch, k)
+               : launch_kernel(ss2_rows<5, false>, dim3(nrow), dim3(Shape<5>::kThreads), stream, rows_timer, ch, k);
         if (e == hipSuccess)
             e = launch_kernel(ss2_cols<5>, dim3(ncol), dim3(Shape<5>::kThreads), stream, cols_timer, ch, k);
     } else {
-        e = launch_kernel(ss2_rows<1>, dim3(nrow), dim3(Shape<1>::kThreads), stream, rows_timer, ch, k);
+        e = launch_kernel(ss2_rows<1, false>, dim3(nrow), dim3(Shape<1>::kThreads), stream, rows_timer, ch, k);
         if (e == hipSuccess)
             e = launch_kernel(ss2_cols<1>, dim3(ncol), dim3(Shape<1>::kThreads), stream, cols_timer, ch, k);
     }
