@@ -295,6 +295,22 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
     double DL = 0.0, DC = 0.0, PS = 0.0;
     float psx = 0.0f, psy = 0.0f;  // the previous row's pair sums
 
+    // Byte offsets in LDS of the thread's first column in each row buffer
+    // and in that buffer's last plane, kept in registers of their own (the
+    // empty asm hides their values from the compiler): every read and write
+    // of a row then takes a constant below 2040 bytes, which the 8-bit offset
+    // fields of paired LDS accesses hold, instead of an address addition per
+    // access.  plane_at(u & 1, p) is plane p of row t's buffer (t0 is even).
+    int lofs[2][2] = {{4 * c, 4 * (c + 4 * P)}, {4 * (c + 5 * P), 4 * (c + 9 * P)}};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(lofs[i][j]));
+    auto plane_at = [&](int parity, int p) __attribute__((always_inline)) {
+        return p < 4 ? reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + lofs[parity][0]) + p * P
+                     : reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + lofs[parity][1]);
+    };
+
     RowPair nm{}, nh{};
     load_row(0, nm);
     load_halo(0, nh);
@@ -308,16 +324,15 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
             if (t >= in_rows) return;
             // Convert this row, then reuse its registers for the next row's
             // loads (they land while this row is filtered).
-            float *buf = lds + (u & 1) * 5 * P;  // t0 is even
             const float xa = fmaf(Raw::value(nm.ra), unit, -kMomentOffset);
             const float xb = fmaf(Raw::value(nm.rb), unit, -kMomentOffset);
             const float ya = fmaf(Raw::value(nm.da), unit, -kMomentOffset);
             const float yb = fmaf(Raw::value(nm.db), unit, -kMomentOffset);
-            *reinterpret_cast<float2 *>(buf + 0 * P + c) = make_float2(xa, xb);
-            *reinterpret_cast<float2 *>(buf + 1 * P + c) = make_float2(ya, yb);
-            *reinterpret_cast<float2 *>(buf + 2 * P + c) = make_float2(xa * xa, xb * xb);
-            *reinterpret_cast<float2 *>(buf + 3 * P + c) = make_float2(ya * ya, yb * yb);
-            *reinterpret_cast<float2 *>(buf + 4 * P + c) = make_float2(xa * ya, xb * yb);
+            *reinterpret_cast<float2 *>(plane_at(u & 1, 0)) = make_float2(xa, xb);
+            *reinterpret_cast<float2 *>(plane_at(u & 1, 1)) = make_float2(ya, yb);
+            *reinterpret_cast<float2 *>(plane_at(u & 1, 2)) = make_float2(xa * xa, xb * xb);
+            *reinterpret_cast<float2 *>(plane_at(u & 1, 3)) = make_float2(ya * ya, yb * yb);
+            *reinterpret_cast<float2 *>(plane_at(u & 1, 4)) = make_float2(xa * ya, xb * yb);
             // Next level: the block row (t - 1, t) when t is odd.
             const bool block_row = has_next && (t & 1) != 0 && (t - 1 < R || last_y);
             const int so_next = ((y0 + t) / 2) * next_pitch * 4;
@@ -373,7 +388,7 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
                 float v[12];
 #pragma unroll
                 for (int k = 0; k < 6; ++k) {
-                    const float2 w = *reinterpret_cast<const float2 *>(buf + p * P + c + 2 * k);
+                    const float2 w = *reinterpret_cast<const float2 *>(plane_at(u & 1, p) + 2 * k);
                     v[2 * k] = w.x;
                     v[2 * k + 1] = w.y;
                 }
