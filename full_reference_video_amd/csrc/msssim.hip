@@ -79,8 +79,9 @@ __device__ __forceinline__ void ms_pixel(const float (&m)[5], LcsAcc &a) {
     const float d3 = fmaf(sdx, sdy, kC3);
     const float d12 = d1 * d2;
     const float r = rcp(d12 * d3) * 0x1p24f;
-    a.dl += (int)((dm * dm) * ((d2 * d3) * r));
-    a.dc += (int)((ds * ds) * ((d1 * d3) * r));
+    const float d3r = d3 * r;  // 2^24 / (d1 d2), shared by the first two quotients
+    a.dl += (int)(((dm * dm) * d2) * d3r);
+    a.dc += (int)(((ds * ds) * d1) * d3r);
     a.s += (int)((cxy + kC3) * (d12 * r));
 }
 
