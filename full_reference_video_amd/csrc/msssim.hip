@@ -291,8 +291,13 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
 #pragma unroll
         for (int p = 0; p < 5; ++p) ring[s][p][0] = ring[s][p][1] = 0.0f;
 
+    // The terms of both columns are formed and added unconditionally, into
+    // an accumulator per column (at most 22 pixels, one group of rows, in
+    // 32-bit integers), so the two pixels' dependency chains interleave; a
+    // column outside the valid map region (its inputs are clamped, so its
+    // terms are finite) is dropped once per group.
     const bool vA = x0 + c < MW, vB = x0 + c + 1 < MW;
-    LcsAcc acc;  // at most 44 pixels (one group of rows) in 32-bit integers
+    LcsAcc accA, accB;
     double DL = 0.0, DC = 0.0, PS = 0.0;
     float psx = 0.0f, psy = 0.0f;  // the previous row's pair sums
 
@@ -416,22 +421,19 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
             const int j = t - 10;
             if (j >= 0 && j < out_rows) {
                 constexpr int sc = (u + 1) % 11;
-                if (vA) {
-                    const float mm[5] = {ring[sc][0][0], ring[sc][1][0], ring[sc][2][0], ring[sc][3][0],
-                                         ring[sc][4][0]};
-                    ms_pixel(mm, acc);
-                }
-                if (vB) {
-                    const float mm[5] = {ring[sc][0][1], ring[sc][1][1], ring[sc][2][1], ring[sc][3][1],
-                                         ring[sc][4][1]};
-                    ms_pixel(mm, acc);
-                }
+                const float ma[5] = {ring[sc][0][0], ring[sc][1][0], ring[sc][2][0], ring[sc][3][0],
+                                     ring[sc][4][0]};
+                const float mb[5] = {ring[sc][0][1], ring[sc][1][1], ring[sc][2][1], ring[sc][3][1],
+                                     ring[sc][4][1]};
+                ms_pixel(ma, accA);
+                ms_pixel(mb, accB);
             }
         });
-        DL += (double)acc.dl;
-        DC += (double)acc.dc;
-        PS += (double)acc.s;
-        acc = LcsAcc{};
+        DL += (double)(vA ? accA.dl : 0) + (double)(vB ? accB.dl : 0);
+        DC += (double)(vA ? accA.dc : 0) + (double)(vB ? accB.dc : 0);
+        PS += (double)(vA ? accA.s : 0) + (double)(vB ? accB.s : 0);
+        accA = LcsAcc{};
+        accB = LcsAcc{};
     }
 
     const double npx = (double)out_rows * (double)((int)vA + (int)vB) * 0x1p24;
