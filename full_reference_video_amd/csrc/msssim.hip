@@ -171,13 +171,13 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
 // to R map rows (R even, so the strip starts on an even row and the next
 // level's 2x2 blocks do not straddle strips).  The row buffer holds the five
 // per-sample planes x, y, x^2, y^2, xy of the strip's 128 NW + 10 input
-// columns; it is double-buffered, so one barrier per row suffices (a buffer
-// is rewritten two rows later, after every thread has passed the barrier of
-// the row between).  The first five threads also convert the ten columns past
-// the strip.  One wave per workgroup (kRowsWaves) measured fastest: its
-// barrier waits for no other wave, which outweighs the halo columns costing
-// the wave a second conversion pass (2160p MS-SSIM 19.6k frames/s against
-// 19.0k with two waves and 17.0k with three).
+// columns; it is double-buffered (a buffer is rewritten two rows later,
+// after the row between has been read).  The first five threads also convert the ten columns past
+// the strip.  One wave per workgroup (kRowsWaves) measured fastest: it
+// needs no barrier, only its own LDS accesses in order (wave_lds_order),
+// which outweighs the halo columns costing the wave a second conversion pass
+// (2160p MS-SSIM 19.6k frames/s against 19.0k with two waves and 17.0k with
+// three, when each row still took a workgroup barrier).
 //
 // Loads and stores go through buffer resources whose row offset is a scalar,
 // so a row costs no per-lane address arithmetic; columns past the plane are
@@ -211,6 +211,13 @@ template <> struct RowRaw<float> {
 struct RowPair {
     uint32_t ra, rb, da, db;
 };
+
+// Orders a one-wave workgroup's LDS accesses as written.  The LDS performs
+// one wave's accesses in issue order, so a row's reads see the writes issued
+// before them without waiting for those writes to complete (the workgroup
+// barrier's fence would: s_waitcnt lgkmcnt(0)); a wavefront-scope fence only
+// keeps the compiler from moving accesses across it.
+__device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
 template <int... U, typename F>
 __device__ __forceinline__ void static_steps(std::integer_sequence<int, U...>, F &&f) {
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
             if ((u & 1) == 0) {
                 // Row t + 1's halo goes into the buffer the previous row was
                 // read from: those reads come first.
-                __syncthreads();
+                wave_lds_order();
                 if (halo) {
                     const float hxa = fmaf(Raw::value(nh.ra), unit, -kMomentOffset);
                     const float hxb = fmaf(Raw::value(nh.rb), unit, -kMomentOffset);
@@ -385,7 +392,7 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
             }
             if (t + 1 < in_rows) load_row(t + 1, nm);
 
-            __syncthreads();  // the row is in the buffer
+            wave_lds_order();  // the row is in the buffer
 
             // Horizontal 11-tap sums of the thread's two columns, plane by
             // plane, each added at once into the eleven unfinished outputs.
