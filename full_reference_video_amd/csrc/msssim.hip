@@ -186,24 +186,58 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
 constexpr int kRowsWaves = 1;                // waves per workgroup (strips of 128 kRowsWaves columns)
 
+// A thread's two adjacent samples come from one load (load2) when the
+// planes allow it (kPair), else from one load each.  values() gives the two
+// samples' values from the loaded words w0, w1 (one load each: the two
+// samples; one load: the packed pair in w0, or both words for fp32).
 template <typename TIn> struct RowRaw;
 template <> struct RowRaw<uint8_t> {
     __device__ static uint32_t load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
         return __builtin_amdgcn_raw_buffer_load_b8(r, vo, so, 0);
     }
-    __device__ static float value(uint32_t v) { return (float)v; }
+    __device__ static void load2(__amdgpu_buffer_rsrc_t r, int vo, int so, uint32_t &w0, uint32_t &w1) {
+        w0 = __builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
+        w1 = 0;
+    }
+    // Each byte of a pair converts in one instruction: the compiler takes
+    // v_cvt_f32_ubyte0 for the low one, and the high one is written out
+    // (knowing the load cleared bits 16-31, the compiler would shift first).
+    template <bool kPair> __device__ static void values(uint32_t w0, uint32_t w1, float &a, float &b) {
+        if constexpr (kPair) {
+            a = (float)(w0 & 0xffu);
+            asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(b) : "v"(w0));
+        } else {
+            a = (float)w0;
+            b = (float)w1;
+        }
+    }
 };
 template <> struct RowRaw<uint16_t> {
     __device__ static uint32_t load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
         return __builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
     }
-    __device__ static float value(uint32_t v) { return (float)v; }
+    __device__ static void load2(__amdgpu_buffer_rsrc_t r, int vo, int so, uint32_t &w0, uint32_t &w1) {
+        w0 = __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0);
+        w1 = 0;
+    }
+    template <bool kPair> __device__ static void values(uint32_t w0, uint32_t w1, float &a, float &b) {
+        a = kPair ? (float)(w0 & 0xffffu) : (float)w0;
+        b = kPair ? (float)(w0 >> 16) : (float)w1;
+    }
 };
 template <> struct RowRaw<float> {
     __device__ static uint32_t load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
         return __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0);
     }
-    __device__ static float value(uint32_t v) { return __builtin_bit_cast(float, v); }
+    __device__ static void load2(__amdgpu_buffer_rsrc_t r, int vo, int so, uint32_t &w0, uint32_t &w1) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0);
+        w0 = v[0];
+        w1 = v[1];
+    }
+    template <bool kPair> __device__ static void values(uint32_t w0, uint32_t w1, float &a, float &b) {
+        a = __builtin_bit_cast(float, w0);
+        b = __builtin_bit_cast(float, w1);
+    }
 };
 
 // The raw samples of one input row that a thread converts: its two columns
@@ -224,7 +258,7 @@ __device__ __forceinline__ void static_steps(std::integer_sequence<int, U...>, F
     (f(std::integral_constant<int, U>{}), ...);
 }
 
-template <typename TIn, int NW>
+template <typename TIn, int NW, bool kPair>
 __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, int W, int H, int next_pitch,
                                                          float unit, int R, Taps taps) {
     using Raw = RowRaw<TIn>;
@@ -250,6 +284,11 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
                                                                           kRsrcWord3);
     const int row_bytes = pitch * (int)sizeof(TIn);
     const int voA = min(x0 + c, W - 1) * (int)sizeof(TIn), voB = min(x0 + c + 1, W - 1) * (int)sizeof(TIn);
+    // A pair starts on an even column: past the plane it is the last pair
+    // that starts inside it, whose values reach only map columns outside the
+    // valid region (as does a pair's second sample past an odd width).
+    const int last_pair = (W - 1) & ~1;
+    const int voP = min(x0 + c, last_pair) * (int)sizeof(TIn);
     // The ten columns past the strip, for two rows at once: threads 0-4 take
     // the even row t of a pair, threads 5-9 the odd row t + 1, two columns
     // each, so the pass runs every other row.  (One wave: a row's buffer is
@@ -260,23 +299,34 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
     const int hc = S + 2 * hl;  // strip-local first column of the halo thread's pair
     const int hvoA = min(x0 + hc, W - 1) * (int)sizeof(TIn);
     const int hvoB = min(x0 + hc + 1, W - 1) * (int)sizeof(TIn);
+    const int hvoP = min(x0 + hc, last_pair) * (int)sizeof(TIn);
 
     auto load_row = [&](int t, RowPair &m) __attribute__((always_inline)) {
         const int so = (y0 + t) * row_bytes;
-        m.ra = Raw::load(rref, voA, so);
-        m.rb = Raw::load(rref, voB, so);
-        m.da = Raw::load(rdis, voA, so);
-        m.db = Raw::load(rdis, voB, so);
+        if constexpr (kPair) {
+            Raw::load2(rref, voP, so, m.ra, m.rb);
+            Raw::load2(rdis, voP, so, m.da, m.db);
+        } else {
+            m.ra = Raw::load(rref, voA, so);
+            m.rb = Raw::load(rref, voB, so);
+            m.da = Raw::load(rdis, voA, so);
+            m.db = Raw::load(rdis, voB, so);
+        }
     };
     // Halo samples of the row pair (t, t + 1), t even; without a row t + 1
     // the odd threads read row t again (and their values go unused).
     auto load_halo = [&](int t, RowPair &h) __attribute__((always_inline)) {
         const int so = (y0 + t) * row_bytes;
         const int dr = (hr != 0 && t + 1 < in_rows) ? row_bytes : 0;
-        h.ra = Raw::load(rref, hvoA + dr, so);
-        h.rb = Raw::load(rref, hvoB + dr, so);
-        h.da = Raw::load(rdis, hvoA + dr, so);
-        h.db = Raw::load(rdis, hvoB + dr, so);
+        if constexpr (kPair) {
+            Raw::load2(rref, hvoP + dr, so, h.ra, h.rb);
+            Raw::load2(rdis, hvoP + dr, so, h.da, h.db);
+        } else {
+            h.ra = Raw::load(rref, hvoA + dr, so);
+            h.rb = Raw::load(rref, hvoB + dr, so);
+            h.da = Raw::load(rdis, hvoA + dr, so);
+            h.db = Raw::load(rdis, hvoB + dr, so);
+        }
     };
 
     // Next level: this thread's 2x2 block column, and (last strip only) the
@@ -337,10 +387,11 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
             if (t >= in_rows) return;
             // Convert this row, then reuse its registers for the next row's
             // loads (they land while this row is filtered).
-            const float xa = fmaf(Raw::value(nm.ra), unit, -kMomentOffset);
-            const float xb = fmaf(Raw::value(nm.rb), unit, -kMomentOffset);
-            const float ya = fmaf(Raw::value(nm.da), unit, -kMomentOffset);
-            const float yb = fmaf(Raw::value(nm.db), unit, -kMomentOffset);
+            float va, vb, wa, wb;
+            Raw::template values<kPair>(nm.ra, nm.rb, va, vb);
+            Raw::template values<kPair>(nm.da, nm.db, wa, wb);
+            const float xa = fmaf(va, unit, -kMomentOffset), xb = fmaf(vb, unit, -kMomentOffset);
+            const float ya = fmaf(wa, unit, -kMomentOffset), yb = fmaf(wb, unit, -kMomentOffset);
             *reinterpret_cast<float2 *>(plane_at(u & 1, 0)) = make_float2(xa, xb);
             *reinterpret_cast<float2 *>(plane_at(u & 1, 1)) = make_float2(ya, yb);
             *reinterpret_cast<float2 *>(plane_at(u & 1, 2)) = make_float2(xa * xa, xb * xb);
@@ -363,10 +414,11 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
                 // read from: those reads come first.
                 wave_lds_order();
                 if (halo) {
-                    const float hxa = fmaf(Raw::value(nh.ra), unit, -kMomentOffset);
-                    const float hxb = fmaf(Raw::value(nh.rb), unit, -kMomentOffset);
-                    const float hya = fmaf(Raw::value(nh.da), unit, -kMomentOffset);
-                    const float hyb = fmaf(Raw::value(nh.db), unit, -kMomentOffset);
+                    float hva, hvb, hwa, hwb;
+                    Raw::template values<kPair>(nh.ra, nh.rb, hva, hvb);
+                    Raw::template values<kPair>(nh.da, nh.db, hwa, hwb);
+                    const float hxa = fmaf(hva, unit, -kMomentOffset), hxb = fmaf(hvb, unit, -kMomentOffset);
+                    const float hya = fmaf(hwa, unit, -kMomentOffset), hyb = fmaf(hwb, unit, -kMomentOffset);
                     float *hb = lds + ((t + hr) & 1) * 5 * P;  // row t, or row t + 1's buffer
                     *reinterpret_cast<float2 *>(hb + 0 * P + hc) = make_float2(hxa, hxb);
                     *reinterpret_cast<float2 *>(hb + 1 * P + hc) = make_float2(hya, hyb);
@@ -583,8 +635,15 @@ template <typename TIn>
 hipError_t launch_rows(const MsPlan &p, const MsBatch &b, int n, int pitch, int W, int H, int next_pitch,
                        float unit, const Taps &taps, hipStream_t stream, const KernelTimer &timer) {
     const dim3 grid(p.gx, p.gy, n);
-    return launch_kernel(ms_level_rows<TIn, kRowsWaves>, grid, dim3(64 * kRowsWaves), stream, timer, b, pitch, W, H,
-                         next_pitch, unit, p.R, taps);
+    // Pair loads need every row of every plane to start on a pair boundary.
+    bool pair = pitch % 2 == 0;
+    for (int i = 0; i < n; ++i)
+        if (((uintptr_t)b.f[i].ref | (uintptr_t)b.f[i].dis) % (2 * sizeof(TIn)) != 0) pair = false;
+    if (pair)
+        return launch_kernel(ms_level_rows<TIn, kRowsWaves, true>, grid, dim3(64 * kRowsWaves), stream, timer, b,
+                             pitch, W, H, next_pitch, unit, p.R, taps);
+    return launch_kernel(ms_level_rows<TIn, kRowsWaves, false>, grid, dim3(64 * kRowsWaves), stream, timer, b, pitch,
+                         W, H, next_pitch, unit, p.R, taps);
 }
 
 hipError_t launch_ms_level(const MsBatch &b, int n, InKind kind, int pitch, int W, int H, int next_pitch,
