@@ -426,18 +426,23 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
                     *reinterpret_cast<float2 *>(hb + 3 * P + hc) = make_float2(hya * hya, hyb * hyb);
                     *reinterpret_cast<float2 *>(hb + 4 * P + hc) = make_float2(hxa * hya, hxb * hyb);
                     // Next level: the block row (t, t + 1) of the halo
-                    // columns, the odd row's pair sums from thread + 5.
-                    const float hsx = hxa + hxb, hsy = hya + hyb;
-                    const float osx = __builtin_bit_cast(
-                        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hsx), 0x105, 0xF, 0xF, false));
-                    const float osy = __builtin_bit_cast(
-                        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hsy), 0x105, 0xF, 0xF, false));
-                    if (has_next && hown_x && (t < R || last_y) && t + 1 < in_rows) {
-                        const int so_h = ((y0 + t) / 2) * next_pitch * 4;
-                        __builtin_amdgcn_raw_buffer_store_b32(
-                            __builtin_bit_cast(uint32_t, fmaf(hsx + osx, 0.25f, kMomentOffset)), nr, hnbx * 4, so_h, 0);
-                        __builtin_amdgcn_raw_buffer_store_b32(
-                            __builtin_bit_cast(uint32_t, fmaf(hsy + osy, 0.25f, kMomentOffset)), nd, hnbx * 4, so_h, 0);
+                    // columns (the plane's last strip only, a wave-uniform
+                    // test), the odd row's pair sums from thread + 5.
+                    if (has_next && last_x && (t < R || last_y) && t + 1 < in_rows) {
+                        const float hsx = hxa + hxb, hsy = hya + hyb;
+                        const float osx = __builtin_bit_cast(
+                            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hsx), 0x105, 0xF, 0xF, false));
+                        const float osy = __builtin_bit_cast(
+                            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hsy), 0x105, 0xF, 0xF, false));
+                        if (hown_x) {
+                            const int so_h = ((y0 + t) / 2) * next_pitch * 4;
+                            __builtin_amdgcn_raw_buffer_store_b32(
+                                __builtin_bit_cast(uint32_t, fmaf(hsx + osx, 0.25f, kMomentOffset)), nr, hnbx * 4,
+                                so_h, 0);
+                            __builtin_amdgcn_raw_buffer_store_b32(
+                                __builtin_bit_cast(uint32_t, fmaf(hsy + osy, 0.25f, kMomentOffset)), nd, hnbx * 4,
+                                so_h, 0);
+                        }
                     }
                 }
                 if (t + 2 < in_rows) load_halo(t + 2, nh);
