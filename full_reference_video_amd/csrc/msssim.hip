@@ -407,9 +407,9 @@ __global__ __launch_bounds__(64 * NW) void ms_level_rows(MsBatch b, int pitch, i
                 __builtin_amdgcn_raw_buffer_store_b32(
                     __builtin_bit_cast(uint32_t, fmaf(psy + sy, 0.25f, kMomentOffset)), nd, nbx * 4, so_next, 0);
             }
-            psx = sx;
-            psy = sy;
             if ((u & 1) == 0) {
+                psx = sx;  // the next (odd) row's block row pairs with this row
+                psy = sy;
                 // Row t + 1's halo goes into the buffer the previous row was
                 // read from: those reads come first.
                 wave_lds_order();
