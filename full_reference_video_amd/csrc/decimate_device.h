@@ -352,6 +352,21 @@ template <typename T, int S> struct Pow2Shape {
     static constexpr int CPT = G / S;                 // chunks (outputs) per lane
 };
 
+// N 32-bit words to a 4N-byte aligned address in 16-byte (or smaller) stores.
+template <int N>
+__device__ __forceinline__ void store_words(void *p, const uint32_t (&w)[N]) {
+    if constexpr (N == 1) {
+        *static_cast<uint32_t *>(p) = w[0];
+    } else if constexpr (N == 2) {
+        *static_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+    } else {
+        static_assert(N % 4 == 0, "whole 16-byte groups");
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i)
+            static_cast<uint4 *>(p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    }
+}
+
 // The windows of one unit from its half-chunk sums: the high half before a
 // lane's first chunk comes from the previous lane (one cross-lane shift);
 // store them.
@@ -372,6 +387,42 @@ __device__ __forceinline__ void pow2_finish(const DecimateFrame &fr, int wv, int
     const uint32_t pr = __shfl_up(hr[CPT - 1], 1, 64);
     const uint32_t pd = __shfl_up(hd[CPT - 1], 1, 64);
     if (lane == 0) return;
+    if constexpr (CPT >= 2) {
+        // A lane's CPT adjacent outputs in one store per plane where they are
+        // all inside the row (the planes are 16-byte aligned and their pitch
+        // a multiple of 8 outputs), so a unit issues two stores instead of
+        // 2 CPT.
+        const int X0 = g * CPT;
+        if (X0 + CPT <= dec_w) {
+            uint32_t tr[CPT], td[CPT];
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                tr[k] = (k == 0 ? pr : hr[k - 1]) + lr[k];
+                td[k] = (k == 0 ? pd : hd[k - 1]) + ld[k];
+            }
+            const size_t o = (size_t)Y * opitch + X0;
+            if (packed) {
+                uint32_t wr[CPT / 2], wd[CPT / 2];
+#pragma unroll
+                for (int k = 0; k < CPT / 2; ++k) {
+                    wr[k] = tr[2 * k] | (tr[2 * k + 1] << 16);
+                    wd[k] = td[2 * k] | (td[2 * k + 1] << 16);
+                }
+                store_words<CPT / 2>(static_cast<uint16_t *>(fr.out_ref) + o, wr);
+                store_words<CPT / 2>(static_cast<uint16_t *>(fr.out_dis) + o, wd);
+            } else {
+                uint32_t wr[CPT], wd[CPT];
+#pragma unroll
+                for (int k = 0; k < CPT; ++k) {
+                    wr[k] = __builtin_bit_cast(uint32_t, (float)tr[k] * post);
+                    wd[k] = __builtin_bit_cast(uint32_t, (float)td[k] * post);
+                }
+                store_words<CPT>(static_cast<float *>(fr.out_ref) + o, wr);
+                store_words<CPT>(static_cast<float *>(fr.out_dis) + o, wd);
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const int X = g * CPT + k;

@@ -415,7 +415,13 @@ hipError_t launch_ssim_step(const StepRoles &r, const StepGeometry &g, InKind ma
         // The map role reads what the decimation writes: uint16 window sums
         // or fp32 values.
         if (map_kind != (g.packed ? IN_U16 : IN_F32) && r.n_map > 0) return hipErrorInvalidValue;
-        const bool fast = decimate_fast_path(r.dec, r.n_dec, g.w, g.h, g.bpc, g.s);
+        // The vector path stores a lane's outputs as one 16-byte (or smaller)
+        // group: planes 16-byte aligned, pitch a multiple of 8 outputs (the
+        // library's planes are 256-byte aligned with a pitch of 64 k).
+        bool out_aligned = g.dec_pitch % 8 == 0;
+        for (int i = 0; i < r.n_dec; ++i)
+            if (((uintptr_t)r.dec.f[i].out_ref | (uintptr_t)r.dec.f[i].out_dis) & 15u) out_aligned = false;
+        const bool fast = out_aligned && decimate_fast_path(r.dec, r.n_dec, g.w, g.h, g.bpc, g.s);
         if (g.packed) {
             // packed implies s = 2^k: the vector path, else the scalar one
             if (g.bpc == 8) {
