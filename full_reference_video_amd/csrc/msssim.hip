@@ -54,9 +54,11 @@ __constant__ double kBeta[5] = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333};
 // l = 1 - (mx - my)^2 / (mux^2 + muy^2 + C1) and
 // c = 1 - (sx - sy)^2 / (sx^2 + sy^2 + C2) (the mirrored quotients
 // rewritten, so identical planes give deficits of exactly 0),
-// s = (sxy + C3) / (sx sy + C3), with sx^2 = max(var_x, 0); the three
-// quotients share one reciprocal of the product of the denominators (at most
-// ~1e14).  Both level kernels take every pixel through this function and add
+// s = (sxy + C3) / (sx sy + C3), with sx^2 = |var_x| (a variance whose fp32
+// value comes out below zero is a rounding error of a few ulps of the second
+// moment, far below C2; its magnitude costs nothing: the consumers take it as
+// an input modifier); the three quotients share one reciprocal of the product
+// of the denominators (at most ~1e14).  Both level kernels take every pixel through this function and add
 // the integers exactly (a level's sums stay far below 2^53 in fp64), so the
 // sums, and the score, do not depend on which kernel ran, how it split the
 // plane, or how many frames shared the launch.  Truncation moves a mean by
@@ -68,8 +70,8 @@ struct LcsAcc {
 __device__ __forceinline__ void ms_pixel(const float (&m)[5], LcsAcc &a) {
     constexpr float kC3 = kC2 / 2.0f;
     const float mx = m[0], my = m[1], xx = m[2], yy = m[3], xy = m[4];
-    const float vx = fmaxf(fmaf(-mx, mx, xx), 0.0f);
-    const float vy = fmaxf(fmaf(-my, my, yy), 0.0f);
+    const float vx = fabsf(fmaf(-mx, mx, xx));
+    const float vy = fabsf(fmaf(-my, my, yy));
     const float cxy = fmaf(-mx, my, xy);
     const float sdx = hw_sqrt(vx), sdy = hw_sqrt(vy);
     const float ux = mx + kMomentOffset, uy = my + kMomentOffset;
