@@ -174,8 +174,10 @@ __global__ __launch_bounds__(NT) void ms_level(MsBatch b, int pitch, int W, int 
 // level's 2x2 blocks do not straddle strips).  The row buffer holds the five
 // per-sample planes x, y, x^2, y^2, xy of the strip's 128 NW + 10 input
 // columns; it is double-buffered (a buffer is rewritten two rows later,
-// after the row between has been read).  The first five threads also convert the ten columns past
-// the strip.  One wave per workgroup (kRowsWaves) measured fastest: it
+// after the row between has been read).  The first ten threads also convert
+// the ten columns past the strip, for two rows at a time (four row buffers
+// would let them take four, but their base registers cost the kernel its
+// third wave per SIMD).  One wave per workgroup (kRowsWaves) measured fastest: it
 // needs no barrier, only its own LDS accesses in order (wave_lds_order),
 // which outweighs the halo columns costing the wave a second conversion pass
 // (2160p MS-SSIM 19.6k frames/s against 19.0k with two waves and 17.0k with
