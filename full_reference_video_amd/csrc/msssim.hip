@@ -58,11 +58,11 @@ __constant__ double kBeta[5] = {0.0448, 0.2856, 0.3001, 0.2363, 0.1333};
 // value comes out below zero is a rounding error of a few ulps of the second
 // moment, far below C2; its magnitude costs nothing: the consumers take it as
 // an input modifier); the three quotients share one reciprocal of the product
-// of the denominators (at most ~1e14).  Both level kernels take every pixel through this function and add
-// the integers exactly (a level's sums stay far below 2^53 in fp64), so the
-// sums, and the score, do not depend on which kernel ran, how it split the
-// plane, or how many frames shared the launch.  Truncation moves a mean by
-// less than 2^-24.
+// of the denominators (at most ~1e14).  Both level kernels take every pixel
+// through this function and add the integers exactly (a level's sums stay far
+// below 2^53 in fp64), so the sums, and the score, do not depend on which
+// kernel ran, how it split the plane, or how many frames shared the launch.
+// Truncation moves a mean by less than 2^-24.
 struct LcsAcc {
     int dl = 0, dc = 0, s = 0;
 };
