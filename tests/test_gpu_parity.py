@@ -348,7 +348,12 @@ def test_msssim_pyramid_bit_exact(ctx, w, h, bpc):
 # column at 1931 wide; odd plane sizes; several strip rows); a batch of one
 # frame takes the tile kernel.
 # The last case is the MS-SSIM workload's own shape and depth, in its launch batch of 32.
-ROWS_CASES = [(2001, 1203, 16), (1921, 1081, 8), (1283, 767, 12), (1931, 1087, 10), (3840, 2160, 8)]
+# Odd level-1 widths take one load per sample; even ones one load per sample
+# pair (1922 x 1082 at 10 bits: 16-bit pairs), whose odd-width levels (961,
+# 1921) read a pair's second sample from the plane's padding at the last
+# column.
+ROWS_CASES = [(2001, 1203, 16), (1921, 1081, 8), (1283, 767, 12), (1931, 1087, 10), (3840, 2160, 8),
+              (1922, 1082, 10), (3842, 2160, 8)]
 
 
 @pytest.mark.parametrize("w,h,bpc", ROWS_CASES)
